@@ -1,0 +1,207 @@
+"""Benchmark of the fused MoE experts forward on one MI355X.
+
+One step = one full experts forward (route sort, activation quantization,
+gate_up grouped GEMM + SwiGLU + h quantization, down grouped GEMM + routing
+weight, deterministic combine) over one batch of synthetic inputs already
+resident in HBM.  The default workload is the Mixtral-8x7B-shaped layer (4096
+tokens, hidden 4096, intermediate 14336, 8 experts, top-2, FP8 e4m3 with
+128x128 weight scales and dynamic 1x128 activation scales).
+
+Prints one JSON line.  `value` is active-expert TFLOP/s (6*H*I per valid slot);
+`roofline` covers the dominant kernel (the gate_up grouped GEMM) timed with HIP
+events on the stream it runs on; `cpu_baseline` is the CPU oracle on a bounded
+sample of the same tokens.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks (dense)
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_MXFP4_TFLOPS = 10100.0
+PEAK_HBM_GBS = 8000.0
+
+METRIC = "MoE-layer active-expert TFLOP/s + tokens/s at 1 GPU; % of FP8/MXFP4 MFMA peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixtral_8x7b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path has no multi-GPU mode)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_scaled_fp8_sort_amd as moe
+    import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload {wl.name}: generating inputs on the GPU")
+    inp = W.inputs(wl, dev)
+    w = moe.prepare_weights(inp["w13"], inp["s13"], inp["w2"], inp["s2"], fmt=wl.fmt)
+    x, ids, wts = inp["x"], inp["ids"], inp["w"]
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    S = T * k
+
+    ids_h = ids.cpu().numpy()
+    valid = (ids_h >= 0) & (ids_h < E)
+    S_v = int(valid.sum())
+    touched = np.unique(ids_h[valid])
+    flop_l1 = 4.0 * H * I * S_v
+    flop_total = 6.0 * H * I * S_v
+    if wl.fmt == W.FMT_FP8_B128:
+        w13_bytes = 2 * I * H + 4 * (2 * I // 128) * (H // 128)
+        w2_bytes = H * I + 4 * (H // 128) * (I // 128)
+    else:
+        w13_bytes = 2 * I * H // 2 + 2 * I * H // 32
+        w2_bytes = H * I // 2 + H * I // 32
+    alg_bytes = len(touched) * (w13_bytes + w2_bytes) + 2 * T * H * 2 + T * k * 8
+
+    ws = torch.empty(moe.forward_workspace_bytes(T, k, w), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        moe.experts_forward(x, ids, wts, w, swiglu_limit=wl.swiglu_limit, out=out, workspace=ws)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] {ms:.3f} ms/step (wall {1e3 * t_wall / args.steps:.3f} ms/step)")
+
+    # ---- dominant kernel: gate_up grouped GEMM with the SwiGLU + h-quant epilogue,
+    # enqueued through the C ABI in the same configuration as in the forward
+    ss, off, _, _ = moe.route_sort(ids, E, with_slot_pos=False)
+    a_codes, a_scales = moe.quant_act(x, wl.fmt)
+    sdt = torch.float32 if wl.fmt == W.FMT_FP8_B128 else torch.uint8
+    h_codes = torch.empty((S, I), dtype=torch.uint8, device=dev)
+    h_scales = torch.empty((S, I // 128 if wl.fmt == W.FMT_FP8_B128 else I // 32), dtype=sdt, device=dev)
+
+    def l1():
+        moe.grouped_gemm(wl.fmt, a_codes, a_scales, off, inp["w13"], inp["s13"], 2 * I, H, moe.EPI_SWIGLU_QUANT, S,
+                         a_row_index=ss, a_row_divisor=k, h_codes=h_codes, h_scales=h_scales,
+                         swiglu_limit=wl.swiglu_limit)
+
+    for _ in range(2):
+        l1()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        l1()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    l1_ms = ev0.elapsed_time(ev1) / args.steps
+    l1_tflops = flop_l1 / (l1_ms * 1e-3) / 1e12
+    peak = PEAK_FP8_TFLOPS if wl.fmt == W.FMT_FP8_B128 else PEAK_MXFP4_TFLOPS
+    log(f"[bench] gate_up GEMM {l1_ms:.3f} ms = {l1_tflops:.1f} TFLOP/s")
+
+    tflops = flop_total / (ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3" if wl.fmt == W.FMT_FP8_B128 else "fp8e4m3 x fp4e2m1",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "tokens": T, "hidden": H, "intermediate": I, "experts": E, "top_k": k,
+            "format": "fp8 e4m3, fp32 scales 1x128 act / 128x128 weight" if wl.fmt == W.FMT_FP8_B128
+            else "e4m3 act x e2m1 weight, UE8M0 per 1x32",
+            "routing": wl.routing, "skipped_slot_prob": wl.skip, "swiglu_limit": wl.swiglu_limit,
+            "valid_slots": S_v, "active_tflop": round(flop_total / 1e12, 4),
+            "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "pct_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2),
+            "pct_mxfp4_peak": round(100.0 * tflops / PEAK_MXFP4_TFLOPS, 2),
+            "hbm_gbs_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+        },
+        "roofline": {
+            "kernel": "gate_up grouped GEMM + SwiGLU + h quantization (moe_grouped_gemm, MOE_EPI_SWIGLU_QUANT)",
+            "bound": "mfma", "achieved": round(l1_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(l1_tflops / peak, 4), "traffic": None, "ms_per_launch": round(l1_ms, 4),
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, inp, seconds):
+    """The CPU oracle, as it stands, on a seeded sample of the workload's tokens."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    n = {k: W.to_numpy(v) for k, v in inp.items()}
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    # calibrate on a few tokens, then size the sample for about `seconds`
+    probe = W.sample_tokens(wl.T, 2 * threads, wl.seed + 100)
+    t0 = time.perf_counter()
+    oracle.forward(wl.fmt, n["w13"], n["s13"], n["w2"], n["s2"], n["x"], n["ids"], n["w"],
+                   swiglu_limit=wl.swiglu_limit, tokens=probe)
+    dt = time.perf_counter() - t0
+    per_tok = dt / probe.size
+    count = int(max(threads, min(wl.T, seconds / max(per_tok, 1e-9))))
+    sample = W.sample_tokens(wl.T, count, wl.seed + 200)
+    t0 = time.perf_counter()
+    oracle.forward(wl.fmt, n["w13"], n["s13"], n["w2"], n["s2"], n["x"], n["ids"], n["w"],
+                   swiglu_limit=wl.swiglu_limit, tokens=sample)
+    dt = time.perf_counter() - t0
+    ids = n["ids"][sample]
+    s_v = int(((ids >= 0) & (ids < wl.E)).sum())
+    flop = 6.0 * wl.H * wl.I * s_v
+    log(f"[bench] oracle: {sample.size} tokens in {dt:.1f} s on {threads} threads")
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{sample.size} of {wl.T} tokens (seeded), {s_v} valid slots, {dt:.1f} s",
+            "tokens_per_s": round(sample.size / dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

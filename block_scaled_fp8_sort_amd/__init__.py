@@ -1,0 +1,339 @@
+"""MI355X (gfx950) fine-grained-quantized MoE experts forward.
+
+Thin Python face of the C ABI in ``include/moe.h`` (``libmoe.so``, built by
+``block_scaled_fp8_sort_amd.build``).  This module only marshals arguments:
+torch supplies device memory and the current HIP stream, and every step of the
+forward runs in the library's HIP kernels.  There is no CPU fallback: importing
+works without the library, but every call raises if it is missing.
+
+Errors follow the pages' guards: a non-bf16 input raises ValueError, static
+activation scales or a non-int8 FP4 weight raise NotImplementedError, tensors on
+another device raise RuntimeError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "FMT_FP8_B128", "FMT_MXFP8A_MXFP4W", "EPI_STORE_F32", "EPI_SWIGLU_QUANT", "EPI_WEIGHTED_SCATTER",
+    "MoeError", "library_path", "load_library", "route_sort", "quant_act", "prepare_weights", "grouped_gemm",
+    "experts_forward", "forward_workspace_bytes", "Weights",
+]
+
+FMT_FP8_B128 = 0
+FMT_MXFP8A_MXFP4W = 1
+LAYOUT_NT = 0
+LAYOUT_NN = 1
+EPI_STORE_F32 = 0
+EPI_SWIGLU_QUANT = 1
+EPI_WEIGHTED_SCATTER = 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmoe.so")
+_lib = None
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_F32 = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int), ("E", _I32), ("H", _I32), ("I", _I32), ("w13", _P), ("w13_scale", _P),
+                ("w2", _P), ("w2_scale", _P)]
+
+
+class MoeGemmArgs(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int), ("N", _I32), ("K", _I32), ("E", _I32), ("max_rows", _I32),
+                ("a_codes", _P), ("a_scales", _P), ("a_row_index", _P), ("a_row_divisor", _I32),
+                ("expert_offsets", _P), ("b_codes", _P), ("b_scales", _P), ("epilogue", ctypes.c_int),
+                ("c_f32", _P), ("h_codes", _P), ("h_scales", _P), ("has_swiglu_limit", _I32),
+                ("swiglu_limit", _F32), ("slot_out", _P), ("top_k_weights", _P), ("slot_of_row", _P)]
+
+
+class MoeDebug(ctypes.Structure):
+    _fields_ = [("sorted_slot", _P), ("expert_offsets", _P), ("act_codes", _P), ("act_scales", _P)]
+
+
+class MoeOptions(ctypes.Structure):
+    _fields_ = [("has_swiglu_limit", _I32), ("swiglu_limit", _F32), ("expert_begin", _I32),
+                ("static_activation_scales", _I32), ("invalid_count", _P), ("debug", ctypes.POINTER(MoeDebug))]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name}: {detail}")
+        self.status = status
+
+
+_EXC = {3: ValueError, 4: NotImplementedError, 7: RuntimeError}
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libmoe.so (raises if it was not built: there is no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m block_scaled_fp8_sort_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_last_error.restype = ctypes.c_char_p
+    lib.moe_last_error.argtypes = []
+    lib.moe_route_sort_workspace.restype = _SZ
+    lib.moe_route_sort_workspace.argtypes = [_I32, _I32, _I32]
+    lib.moe_route_sort.restype = ctypes.c_int
+    lib.moe_route_sort.argtypes = [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]
+    lib.moe_quant_act.restype = ctypes.c_int
+    lib.moe_quant_act.argtypes = [_P, _I32, _I32, ctypes.c_int, _P, _P, _P]
+    lib.moe_prepared_weights_size.restype = _SZ
+    lib.moe_prepared_weights_size.argtypes = [ctypes.c_int, _I32, _I32, _I32]
+    lib.moe_prepare_weights.restype = ctypes.c_int
+    lib.moe_prepare_weights.argtypes = [ctypes.c_int, ctypes.c_int, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ,
+                                        ctypes.POINTER(MoeWeights), _P]
+    lib.moe_grouped_gemm.restype = ctypes.c_int
+    lib.moe_grouped_gemm.argtypes = [ctypes.POINTER(MoeGemmArgs), _P]
+    lib.moe_experts_forward_workspace.restype = _SZ
+    lib.moe_experts_forward_workspace.argtypes = [_I32, _I32, ctypes.POINTER(MoeWeights)]
+    lib.moe_experts_forward.restype = ctypes.c_int
+    lib.moe_experts_forward.argtypes = [ctypes.POINTER(MoeWeights), _P, _P, _P, _I32, _I32,
+                                        ctypes.POINTER(MoeOptions), _P, _P, _SZ, _P]
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        name = lib.moe_status_string(status).decode()
+        detail = lib.moe_last_error().decode()
+        exc = _EXC.get(status)
+        if exc is not None:
+            raise exc(f"{name}: {detail}")
+        raise MoeError(status, name, detail)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, device=None):
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise RuntimeError(f"{name} is on {t.device}, expected {device} (one device per process)")
+
+
+def _scale_dtype(fmt: int):
+    return torch.float32 if fmt == FMT_FP8_B128 else torch.uint8
+
+
+def _scale_cols(fmt: int, n: int) -> int:
+    return n // 128 if fmt == FMT_FP8_B128 else n // 32
+
+
+# ------------------------------------------------------------------ route sort
+def route_sort(top_k_index: torch.Tensor, num_experts: int, expert_begin: int = 0, with_slot_pos: bool = True):
+    """Stable sort of the flat (token, slot) pairs by local expert id.
+
+    Returns (sorted_slot int32 [T*k], expert_offsets int32 [E+1], slot_pos int32
+    [T*k] or None, invalid_count int32 [1]); all stay on the device.
+    """
+    lib = load_library()
+    dev = top_k_index.device
+    _need(top_k_index, "top_k_index", torch.int32)
+    T, k = top_k_index.shape
+    S = T * k
+    sorted_slot = torch.empty(S, dtype=torch.int32, device=dev)
+    offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+    slot_pos = torch.empty(S, dtype=torch.int32, device=dev) if with_slot_pos else None
+    invalid = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws_bytes = lib.moe_route_sort_workspace(T, k, num_experts)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib.moe_route_sort(_ptr(top_k_index), T, k, num_experts, expert_begin, _ptr(sorted_slot), _ptr(offsets),
+                              _ptr(slot_pos), _ptr(invalid), _ptr(ws), ws_bytes, _stream(dev)))
+    return sorted_slot, offsets, slot_pos, invalid
+
+
+# -------------------------------------------------------------- quantization
+def quant_act(x: torch.Tensor, fmt: int = FMT_FP8_B128):
+    """Dynamic per-block quantization of bf16 rows: (codes uint8 [rows, H], scales)."""
+    lib = load_library()
+    _need(x, "x", torch.bfloat16)
+    rows, H = x.shape
+    codes = torch.empty((rows, H), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, _scale_cols(fmt, H)), dtype=_scale_dtype(fmt), device=x.device)
+    _check(lib.moe_quant_act(_ptr(x), rows, H, fmt, _ptr(codes), _ptr(scales), _stream(x.device)))
+    return codes, scales
+
+
+# ------------------------------------------------------------------- weights
+class Weights:
+    """Prepared expert weights: the C descriptor plus the tensors it points at."""
+
+    def __init__(self, desc: MoeWeights, keep: tuple):
+        self.desc = desc
+        self._keep = keep
+
+    @property
+    def fmt(self):
+        return self.desc.fmt
+
+    @property
+    def E(self):
+        return self.desc.E
+
+    @property
+    def H(self):
+        return self.desc.H
+
+    @property
+    def I(self):
+        return self.desc.I
+
+
+def prepare_weights(gate_up: torch.Tensor, gate_up_scale: torch.Tensor, down: torch.Tensor,
+                    down_scale: torch.Tensor, fmt: int = FMT_FP8_B128, transposed: bool = False,
+                    copy: bool = False) -> Weights:
+    """One-shot weight preparation (nt tensors are used in place unless copy=True).
+
+    FP8_B128: gate_up uint8 [E, 2I, H] (or [E, H, 2I] when transposed), fp32 scales
+    per 128x128 block; down uint8 [E, H, I].  MX: int8/uint8 packed e2m1
+    [E, 2I, H/2] and [E, H, I/2] with uint8 UE8M0 scales per 1x32.
+    """
+    lib = load_library()
+    dev = gate_up.device
+    if fmt == FMT_MXFP8A_MXFP4W and gate_up.dtype not in (torch.int8, torch.uint8):
+        raise NotImplementedError(f"MXFP4 experts need FP4-packed int8 weights, got {gate_up.dtype}")
+    for name, t in (("gate_up", gate_up), ("down", down)):
+        if t.dtype not in (torch.uint8, torch.int8, torch.float8_e4m3fn):
+            raise ValueError(f"{name} must hold 8-bit codes, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    E = gate_up.shape[0]
+    if fmt == FMT_FP8_B128:
+        H, I2 = (gate_up.shape[1], gate_up.shape[2]) if transposed else (gate_up.shape[2], gate_up.shape[1])
+    else:
+        H, I2 = gate_up.shape[2] * 2, gate_up.shape[1]
+    I = I2 // 2
+    desc = MoeWeights()
+    prepared = None
+    nbytes = 0
+    if transposed or copy:
+        nbytes = lib.moe_prepared_weights_size(fmt, E, H, I)
+        prepared = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _check(lib.moe_prepare_weights(fmt, LAYOUT_NN if transposed else LAYOUT_NT, E, H, I, _ptr(gate_up),
+                                   _ptr(gate_up_scale), _ptr(down), _ptr(down_scale), _ptr(prepared), nbytes,
+                                   ctypes.byref(desc), _stream(dev)))
+    keep = (prepared,) if prepared is not None else (gate_up, gate_up_scale, down, down_scale)
+    return Weights(desc, keep)
+
+
+# -------------------------------------------------------------- grouped GEMM
+def grouped_gemm(fmt: int, a_codes, a_scales, expert_offsets, b_codes, b_scales, N: int, K: int, epilogue: int,
+                 max_rows: int, a_row_index=None, a_row_divisor: int = 1, c_f32=None, h_codes=None, h_scales=None,
+                 swiglu_limit: Optional[float] = None, slot_out=None, top_k_weights=None, slot_of_row=None):
+    """Enqueue one grouped GEMM (see moe_grouped_gemm); outputs are caller tensors."""
+    lib = load_library()
+    a = MoeGemmArgs()
+    a.fmt = fmt
+    a.N, a.K, a.E, a.max_rows = N, K, expert_offsets.numel() - 1, max_rows
+    a.a_codes, a.a_scales = _ptr(a_codes), _ptr(a_scales)
+    a.a_row_index, a.a_row_divisor = _ptr(a_row_index), a_row_divisor
+    a.expert_offsets = _ptr(expert_offsets)
+    a.b_codes, a.b_scales = _ptr(b_codes), _ptr(b_scales)
+    a.epilogue = epilogue
+    a.c_f32, a.h_codes, a.h_scales = _ptr(c_f32), _ptr(h_codes), _ptr(h_scales)
+    a.has_swiglu_limit = 0 if swiglu_limit is None else 1
+    a.swiglu_limit = 0.0 if swiglu_limit is None else float(swiglu_limit)
+    a.slot_out, a.top_k_weights, a.slot_of_row = _ptr(slot_out), _ptr(top_k_weights), _ptr(slot_of_row)
+    _check(lib.moe_grouped_gemm(ctypes.byref(a), _stream(a_codes.device)))
+
+
+# ------------------------------------------------------------ fused forward
+_ws_cache: dict = {}
+
+
+def _pow2_tokens(T: int) -> int:
+    # sized for the next power of two, as the pages size their buffers: a batch
+    # that grows reallocates a few times, for at most twice the memory
+    return 1 << (T - 1).bit_length() if T > 0 else 0
+
+
+def forward_workspace_bytes(T: int, k: int, weights: Weights) -> int:
+    return load_library().moe_experts_forward_workspace(T, k, ctypes.byref(weights.desc))
+
+
+def _workspace(T: int, k: int, weights: Weights, device) -> torch.Tensor:
+    need = forward_workspace_bytes(_pow2_tokens(T), k, weights)
+    key = (device, weights.E, weights.H, weights.I, weights.fmt, k)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def experts_forward(hidden_states: torch.Tensor, top_k_index: torch.Tensor, top_k_weights: torch.Tensor,
+                    weights: Weights, swiglu_limit: Optional[float] = None, expert_begin: int = 0,
+                    activation_scheme: str = "dynamic", out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, invalid_count: Optional[torch.Tensor] = None,
+                    debug: Optional[dict] = None) -> torch.Tensor:
+    """The fused experts forward: out[t] = sum_j w[t, j] * expert_{id[t, j]}(hidden_states[t]).
+
+    hidden_states bf16 [T, H]; top_k_index int32 [T, k] (global ids, -1 skips the
+    slot); top_k_weights fp32 [T, k].  Returns bf16 [T, H].
+    """
+    lib = load_library()
+    if hidden_states.dtype != torch.bfloat16:
+        raise ValueError(f"the experts forward requires bfloat16 hidden states, got {hidden_states.dtype}")
+    if activation_scheme == "static":
+        raise NotImplementedError("activations are quantized dynamically per block; static scales are not supported")
+    dev = hidden_states.device
+    _need(hidden_states, "hidden_states", torch.bfloat16, dev)
+    _need(top_k_index, "top_k_index", torch.int32, dev)
+    _need(top_k_weights, "top_k_weights", torch.float32, dev)
+    T, H = hidden_states.shape
+    k = top_k_index.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if T == 0:
+        return out
+    if workspace is None:
+        workspace = _workspace(T, k, weights, dev)
+    opt = MoeOptions()
+    opt.has_swiglu_limit = 0 if swiglu_limit is None else 1
+    opt.swiglu_limit = 0.0 if swiglu_limit is None else float(swiglu_limit)
+    opt.expert_begin = expert_begin
+    opt.static_activation_scales = 0
+    opt.invalid_count = _ptr(invalid_count)
+    dbg = None
+    if debug is not None:
+        S = T * k
+        debug["sorted_slot"] = torch.empty(S, dtype=torch.int32, device=dev)
+        debug["expert_offsets"] = torch.empty(weights.E + 1, dtype=torch.int32, device=dev)
+        debug["act_codes"] = torch.empty((T, H), dtype=torch.uint8, device=dev)
+        debug["act_scales"] = torch.empty((T, _scale_cols(weights.fmt, H)), dtype=_scale_dtype(weights.fmt),
+                                          device=dev)
+        dbg = MoeDebug(_ptr(debug["sorted_slot"]), _ptr(debug["expert_offsets"]), _ptr(debug["act_codes"]),
+                       _ptr(debug["act_scales"]))
+        opt.debug = ctypes.pointer(dbg)
+    _check(lib.moe_experts_forward(ctypes.byref(weights.desc), _ptr(hidden_states), _ptr(top_k_index),
+                                   _ptr(top_k_weights), T, k, ctypes.byref(opt), _ptr(out), _ptr(workspace),
+                                   workspace.numel(), _stream(dev)))
+    return out

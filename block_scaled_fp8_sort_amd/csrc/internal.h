@@ -1,0 +1,51 @@
+// Launchers of the gfx950 kernels, called by the C-ABI layer (moe_api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Parameters of one grouped GEMM launch (see moe_grouped_gemm in include/moe.h).
+struct GemmParams {
+  const uint8_t* a_codes;
+  const void* a_scales;
+  const int32_t* a_row_index;
+  int32_t a_row_div;
+  const int32_t* offsets;
+  int32_t E;
+  const uint8_t* b_codes;
+  const void* b_scales;
+  int32_t N;  // rows of B per expert
+  int32_t K;
+  int32_t max_rows;
+  // epilogues
+  float* c_f32;
+  uint8_t* h_codes;
+  void* h_scales;
+  int32_t has_limit;
+  float limit;
+  uint16_t* slot_out;
+  const float* top_k_weights;
+  const int32_t* slot_of_row;
+};
+
+enum Epilogue { kEpiStoreF32 = 0, kEpiSwiGLUQuant = 1, kEpiWeightedScatter = 2 };
+
+size_t route_sort_lds_bytes(int32_t E);
+hipError_t launch_route_sort(const int32_t* ids, int32_t S, int32_t E, int32_t expert_begin, int32_t* sorted_slot,
+                             int32_t* offsets, int32_t* slot_pos, int32_t* invalid_count, hipStream_t stream);
+hipError_t launch_quant_act(const uint16_t* x, int32_t rows, int32_t H, int fmt, uint8_t* codes, void* scales,
+                            hipStream_t stream);
+// epi: Epilogue; paired: gate/up row pairing of B (used with kEpiSwiGLUQuant and
+// optionally kEpiStoreF32 on the gate_up weight).
+hipError_t launch_gemm_fp8_b128(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream);
+hipError_t launch_gemm_mx(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream);
+hipError_t launch_combine(const uint16_t* slot_out, const int32_t* ids, int32_t T, int32_t k, int32_t H, int32_t E,
+                          int32_t expert_begin, uint16_t* out, hipStream_t stream);
+hipError_t launch_transpose_u8(const uint8_t* in, uint8_t* out, int32_t batch, int32_t rows, int32_t cols,
+                               hipStream_t stream);
+hipError_t launch_transpose_f32(const float* in, float* out, int32_t batch, int32_t rows, int32_t cols,
+                                hipStream_t stream);
+
+}  // namespace moe

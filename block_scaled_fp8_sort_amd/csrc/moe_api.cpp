@@ -1,0 +1,489 @@
+// C ABI of the library (include/moe.h): argument validation, workspace layout
+// and the launch sequence.  Every check that needs no device runs first, so a
+// bad call is refused before the HIP runtime is touched; then the device checks
+// (gfx950, pointers on the stream's device); then the kernels are enqueued.
+//
+// The refusals mirror the pages' guards, which all fire before any kernel work:
+// non-bf16 hidden states (ValueError), static activation scales and non-int8 FP4
+// weights (NotImplementedError), a model spread over several devices in one
+// process (RuntimeError), and a device that cannot serve the dtypes ("DeepGEMM
+// experts selected on a model spanning multiple CUDA devices", the record's
+// source; "DeepGEMM Mega MoE requires FP4-packed expert weights (dtype=int8)",
+// section "Source").
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "internal.h"
+#include "moe.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+moe_status ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool valid_fmt(int f) { return f == MOE_FMT_FP8_B128 || f == MOE_FMT_MXFP8A_MXFP4W; }
+
+constexpr int kMaxE = 512;
+constexpr int kMaxK = 64;
+
+// ------------------------------------------------------------ device checks
+struct DeviceInfo {
+  bool probed = false;
+  bool gfx950 = false;
+  int num_cus = 0;
+};
+std::mutex g_dev_mu;
+DeviceInfo g_dev[64];
+
+moe_status stream_device(hipStream_t stream, int* dev) {
+  hipError_t e = hipStreamGetDevice(stream, dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+moe_status check_device(hipStream_t stream, int* dev_out, int* num_cus) {
+  int dev = 0;
+  moe_status st = stream_device(stream, &dev);
+  if (st != MOE_OK) return st;
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_DEVICE, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.probed) {
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    d.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.num_cus = prop.multiProcessorCount;
+    d.probed = true;
+    if (!d.gfx950) {
+      d.probed = false;
+      return fail(MOE_ERR_ARCH, "device %d is %s; these kernels are built for gfx950 (MI355X)", dev,
+                  prop.gcnArchName);
+    }
+  }
+  *dev_out = dev;
+  *num_cus = d.num_cus;
+  return MOE_OK;
+}
+
+// A pointer must be device memory of `dev` (or host-registered memory mapped on it).
+moe_status check_ptr(const void* p, int dev, const char* name) {
+  if (!p) return MOE_OK;
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MOE_ERR_DEVICE, "%s is not memory known to the HIP runtime", name);
+  }
+  if (attr.type == hipMemoryTypeDevice && attr.device != dev)
+    return fail(MOE_ERR_DEVICE, "%s lives on device %d but the stream is on device %d (one device per process)", name,
+                attr.device, dev);
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------- forward workspace
+struct FwdLayout {
+  size_t sorted_slot, offsets, act_codes, act_scales, h_codes, h_scales, slot_out, total;
+};
+
+FwdLayout fwd_layout(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I, int fmt) {
+  const size_t S = (size_t)T * k;
+  const size_t A = 256;
+  const bool mx = fmt == MOE_FMT_MXFP8A_MXFP4W;
+  FwdLayout L;
+  size_t o = 0;
+  L.sorted_slot = o; o = align_up(o + 4 * S, A);
+  L.offsets = o; o = align_up(o + 4 * (size_t)(E + 1), A);
+  L.act_codes = o; o = align_up(o + (size_t)T * H, A);
+  L.act_scales = o; o = align_up(o + (mx ? (size_t)T * (H / 32) : 4 * (size_t)T * (H / 128)), A);
+  L.h_codes = o; o = align_up(o + S * I, A);
+  L.h_scales = o; o = align_up(o + (mx ? S * (I / 32) : 4 * S * (I / 128)), A);
+  L.slot_out = o; o = align_up(o + 2 * S * H, A);
+  L.total = o;
+  return L;
+}
+
+moe_status validate_weights(const moe_weights* w) {
+  if (!w) return fail(MOE_ERR_NULL, "weights descriptor is NULL");
+  if (!valid_fmt(w->fmt)) return fail(MOE_ERR_UNSUPPORTED, "unknown weight format %d", (int)w->fmt);
+  if (w->E < 1 || w->E > kMaxE) return fail(MOE_ERR_SHAPE, "E=%d outside [1, %d]", w->E, kMaxE);
+  if (w->H <= 0 || w->I <= 0 || w->H % 128 || w->I % 128)
+    return fail(MOE_ERR_SHAPE, "H=%d and I=%d must be positive multiples of 128", w->H, w->I);
+  if ((int64_t)2 * w->I * w->H >= (int64_t)1 << 31 || (int64_t)w->H * w->I >= (int64_t)1 << 31)
+    return fail(MOE_ERR_SHAPE, "one expert's weight must stay below 2^31 elements");
+  if (!w->w13 || !w->w13_scale || !w->w2 || !w->w2_scale) return fail(MOE_ERR_NULL, "weight pointer is NULL");
+  return MOE_OK;
+}
+
+moe_status validate_gemm(const moe_gemm_args* a) {
+  if (!a) return fail(MOE_ERR_NULL, "gemm args are NULL");
+  if (!valid_fmt(a->fmt)) return fail(MOE_ERR_UNSUPPORTED, "unknown format %d", (int)a->fmt);
+  if (a->E < 1 || a->E > kMaxE) return fail(MOE_ERR_SHAPE, "E=%d outside [1, %d]", a->E, kMaxE);
+  if (a->K <= 0 || a->K % 128) return fail(MOE_ERR_SHAPE, "K=%d must be a positive multiple of 128", a->K);
+  if (a->N <= 0 || a->N % 128) return fail(MOE_ERR_SHAPE, "N=%d must be a positive multiple of 128", a->N);
+  if (a->epilogue == MOE_EPI_SWIGLU_QUANT && a->N % 256)
+    return fail(MOE_ERR_SHAPE, "SwiGLU epilogue needs N = 2I with I a multiple of 128 (N=%d)", a->N);
+  if (a->max_rows < 0) return fail(MOE_ERR_SHAPE, "max_rows=%d", a->max_rows);
+  if ((int64_t)a->N * a->K >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "N*K must stay below 2^31");
+  if (a->a_row_index && a->a_row_divisor < 1) return fail(MOE_ERR_SHAPE, "a_row_divisor must be >= 1");
+  if (!a->a_codes || !a->a_scales || !a->expert_offsets || !a->b_codes || !a->b_scales)
+    return fail(MOE_ERR_NULL, "an operand pointer is NULL");
+  switch (a->epilogue) {
+    case MOE_EPI_STORE_F32:
+      if (!a->c_f32) return fail(MOE_ERR_NULL, "c_f32 is NULL");
+      break;
+    case MOE_EPI_SWIGLU_QUANT:
+      if (!a->h_codes || !a->h_scales) return fail(MOE_ERR_NULL, "h_codes / h_scales are NULL");
+      if (a->has_swiglu_limit && !(std::isfinite(a->swiglu_limit) && a->swiglu_limit > 0.0f))
+        return fail(MOE_ERR_SHAPE, "swiglu_limit must be finite and > 0");
+      break;
+    case MOE_EPI_WEIGHTED_SCATTER:
+      if (!a->slot_out || !a->top_k_weights || !a->slot_of_row)
+        return fail(MOE_ERR_NULL, "slot_out / top_k_weights / slot_of_row are NULL");
+      break;
+    default:
+      return fail(MOE_ERR_UNSUPPORTED, "unknown epilogue %d", (int)a->epilogue);
+  }
+  return MOE_OK;
+}
+
+moe::GemmParams to_params(const moe_gemm_args* a) {
+  moe::GemmParams p;
+  p.a_codes = a->a_codes;
+  p.a_scales = a->a_scales;
+  p.a_row_index = a->a_row_index;
+  p.a_row_div = a->a_row_index ? a->a_row_divisor : 1;
+  p.offsets = a->expert_offsets;
+  p.E = a->E;
+  p.b_codes = a->b_codes;
+  p.b_scales = a->b_scales;
+  p.N = a->N;
+  p.K = a->K;
+  p.max_rows = a->max_rows;
+  p.c_f32 = a->c_f32;
+  p.h_codes = a->h_codes;
+  p.h_scales = a->h_scales;
+  p.has_limit = a->has_swiglu_limit ? 1 : 0;
+  p.limit = a->swiglu_limit;
+  p.slot_out = a->slot_out;
+  p.top_k_weights = a->top_k_weights;
+  p.slot_of_row = a->slot_of_row;
+  return p;
+}
+
+hipError_t launch_gemm(const moe::GemmParams& p, int fmt, int epi, bool paired, int num_cus, hipStream_t stream) {
+  if (fmt == MOE_FMT_FP8_B128) return moe::launch_gemm_fp8_b128(p, epi, paired, num_cus, stream);
+  return moe::launch_gemm_mx(p, epi, paired, num_cus, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE";
+    case MOE_ERR_DTYPE: return "MOE_ERR_DTYPE";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_ARCH: return "MOE_ERR_ARCH";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+size_t moe_route_sort_workspace(int32_t T, int32_t k, int32_t E) {
+  (void)T;
+  (void)k;
+  (void)E;
+  return 0;  // the sort runs in one workgroup's LDS
+}
+
+moe_status moe_route_sort(const int32_t* top_k_index, int32_t T, int32_t k, int32_t E, int32_t expert_begin,
+                          int32_t* sorted_slot, int32_t* expert_offsets, int32_t* slot_pos, int32_t* invalid_count,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  if (T < 0) return fail(MOE_ERR_SHAPE, "T=%d < 0", T);
+  if (k < 1 || k > kMaxK) return fail(MOE_ERR_SHAPE, "k=%d outside [1, %d]", k, kMaxK);
+  if (E < 1 || E > kMaxE) return fail(MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, kMaxE);
+  if ((int64_t)T * k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "T*k must stay below 2^31");
+  if (!expert_offsets) return fail(MOE_ERR_NULL, "expert_offsets is NULL");
+  if (T > 0 && (!top_k_index || !sorted_slot)) return fail(MOE_ERR_NULL, "top_k_index / sorted_slot is NULL");
+  if (ws_bytes < moe_route_sort_workspace(T, k, E)) return fail(MOE_ERR_WORKSPACE, "workspace too small");
+  if (T > 0 && ((const void*)top_k_index == (const void*)sorted_slot ||
+                (const void*)top_k_index == (const void*)slot_pos))
+    return fail(MOE_ERR_UNSUPPORTED, "outputs must not alias top_k_index");
+  int dev, cus;
+  moe_status st = check_device(stream, &dev, &cus);
+  if (st != MOE_OK) return st;
+  for (auto pr : {std::make_pair((const void*)top_k_index, "top_k_index"),
+                  std::make_pair((const void*)sorted_slot, "sorted_slot"),
+                  std::make_pair((const void*)expert_offsets, "expert_offsets")})
+    if ((st = check_ptr(pr.first, dev, pr.second)) != MOE_OK) return st;
+  st = hip_status(moe::launch_route_sort(top_k_index, T * k, E, expert_begin, sorted_slot, expert_offsets, slot_pos,
+                                         invalid_count, stream),
+                  "route sort launch");
+  return st == MOE_OK ? ok() : st;
+}
+
+moe_status moe_quant_act(const uint16_t* x, int32_t rows, int32_t H, moe_format fmt, uint8_t* codes, void* scales,
+                         hipStream_t stream) {
+  if (!valid_fmt(fmt)) return fail(MOE_ERR_UNSUPPORTED, "unknown format %d", (int)fmt);
+  if (rows < 0) return fail(MOE_ERR_SHAPE, "rows=%d < 0", rows);
+  if (H <= 0 || H % 128) return fail(MOE_ERR_SHAPE, "H=%d must be a positive multiple of 128", H);
+  if (rows > 0 && (!x || !codes || !scales)) return fail(MOE_ERR_NULL, "x / codes / scales is NULL");
+  if ((const void*)x == (const void*)codes || (const void*)x == scales)
+    return fail(MOE_ERR_UNSUPPORTED, "outputs must not alias x");
+  if (rows == 0) return ok();
+  int dev, cus;
+  moe_status st = check_device(stream, &dev, &cus);
+  if (st != MOE_OK) return st;
+  if ((st = check_ptr(x, dev, "x")) != MOE_OK || (st = check_ptr(codes, dev, "codes")) != MOE_OK) return st;
+  st = hip_status(moe::launch_quant_act(x, rows, H, (int)fmt, codes, scales, stream), "quant launch");
+  return st == MOE_OK ? ok() : st;
+}
+
+size_t moe_prepared_weights_size(moe_format fmt, int32_t E, int32_t H, int32_t I) {
+  if (!valid_fmt(fmt) || E < 1 || H <= 0 || I <= 0 || H % 128 || I % 128) return 0;
+  const size_t A = 256;
+  const size_t e = (size_t)E, h = (size_t)H, i = (size_t)I;
+  if (fmt == MOE_FMT_FP8_B128)
+    return align_up(e * 2 * i * h, A) + align_up(4 * e * (2 * i / 128) * (h / 128), A) + align_up(e * h * i, A) +
+           align_up(4 * e * (h / 128) * (i / 128), A);
+  return align_up(e * 2 * i * h / 2, A) + align_up(e * 2 * i * (h / 32), A) + align_up(e * h * i / 2, A) +
+         align_up(e * h * (i / 32), A);
+}
+
+moe_status moe_prepare_weights(moe_format fmt, moe_layout layout, int32_t E, int32_t H, int32_t I,
+                               const void* gate_up, const void* gate_up_scale, const void* down,
+                               const void* down_scale, void* prepared, size_t prepared_bytes, moe_weights* out,
+                               hipStream_t stream) {
+  if (!out) return fail(MOE_ERR_NULL, "output descriptor is NULL");
+  if (!valid_fmt(fmt)) return fail(MOE_ERR_UNSUPPORTED, "unknown format %d", (int)fmt);
+  if (layout != MOE_LAYOUT_NT && layout != MOE_LAYOUT_NN) return fail(MOE_ERR_UNSUPPORTED, "unknown layout");
+  if (E < 1 || E > kMaxE) return fail(MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, kMaxE);
+  if (H <= 0 || I <= 0 || H % 128 || I % 128)
+    return fail(MOE_ERR_SHAPE, "H=%d and I=%d must be positive multiples of 128", H, I);
+  if (!gate_up || !gate_up_scale || !down || !down_scale) return fail(MOE_ERR_NULL, "a weight pointer is NULL");
+  if (layout == MOE_LAYOUT_NN && fmt != MOE_FMT_FP8_B128)
+    return fail(MOE_ERR_UNSUPPORTED, "the nn layout is accepted for FP8_B128 weights only");
+  const size_t need = moe_prepared_weights_size(fmt, E, H, I);
+  if ((layout == MOE_LAYOUT_NN || prepared) && prepared_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "prepared buffer holds %zu bytes, %zu needed", prepared_bytes, need);
+  if (layout == MOE_LAYOUT_NN && !prepared) return fail(MOE_ERR_NULL, "the nn layout needs a prepared buffer");
+
+  moe_weights w;
+  w.fmt = fmt;
+  w.E = E;
+  w.H = H;
+  w.I = I;
+  if (layout == MOE_LAYOUT_NT && !prepared) {
+    w.w13 = (const uint8_t*)gate_up;
+    w.w13_scale = gate_up_scale;
+    w.w2 = (const uint8_t*)down;
+    w.w2_scale = down_scale;
+    *out = w;
+    return ok();
+  }
+  int dev, cus;
+  moe_status st = check_device(stream, &dev, &cus);
+  if (st != MOE_OK) return st;
+  const size_t A = 256;
+  const size_t e = E, h = H, i = I;
+  const bool mx = fmt == MOE_FMT_MXFP8A_MXFP4W;
+  const size_t b13 = mx ? e * 2 * i * h / 2 : e * 2 * i * h;
+  const size_t b13s = mx ? e * 2 * i * (h / 32) : 4 * e * (2 * i / 128) * (h / 128);
+  const size_t b2 = mx ? e * h * i / 2 : e * h * i;
+  uint8_t* base = (uint8_t*)prepared;
+  uint8_t* p13 = base;
+  uint8_t* p13s = p13 + align_up(b13, A);
+  uint8_t* p2 = p13s + align_up(b13s, A);
+  uint8_t* p2s = p2 + align_up(b2, A);
+  const size_t b2s = mx ? e * h * (i / 32) : 4 * e * (h / 128) * (i / 128);
+  hipError_t he;
+  if (layout == MOE_LAYOUT_NT) {
+    if ((he = hipMemcpyAsync(p13, gate_up, b13, hipMemcpyDeviceToDevice, stream)) != hipSuccess ||
+        (he = hipMemcpyAsync(p13s, gate_up_scale, b13s, hipMemcpyDeviceToDevice, stream)) != hipSuccess ||
+        (he = hipMemcpyAsync(p2, down, b2, hipMemcpyDeviceToDevice, stream)) != hipSuccess ||
+        (he = hipMemcpyAsync(p2s, down_scale, b2s, hipMemcpyDeviceToDevice, stream)) != hipSuccess)
+      return hip_status(he, "weight copy");
+  } else {
+    // nn: gate_up [E, H, 2I] -> [E, 2I, H]; scales [E, H/128, 2I/128] -> [E, 2I/128, H/128];
+    //     down [E, I, H] -> [E, H, I]; scales [E, I/128, H/128] -> [E, H/128, I/128]
+    if ((he = moe::launch_transpose_u8((const uint8_t*)gate_up, p13, E, H, 2 * I, stream)) != hipSuccess ||
+        (he = moe::launch_transpose_f32((const float*)gate_up_scale, (float*)p13s, E, H / 128, 2 * I / 128,
+                                        stream)) != hipSuccess ||
+        (he = moe::launch_transpose_u8((const uint8_t*)down, p2, E, I, H, stream)) != hipSuccess ||
+        (he = moe::launch_transpose_f32((const float*)down_scale, (float*)p2s, E, I / 128, H / 128, stream)) !=
+            hipSuccess)
+      return hip_status(he, "weight transpose");
+  }
+  w.w13 = p13;
+  w.w13_scale = p13s;
+  w.w2 = p2;
+  w.w2_scale = p2s;
+  *out = w;
+  return ok();
+}
+
+moe_status moe_grouped_gemm(const moe_gemm_args* args, hipStream_t stream) {
+  moe_status st = validate_gemm(args);
+  if (st != MOE_OK) return st;
+  if (args->max_rows == 0) return ok();
+  int dev, cus;
+  if ((st = check_device(stream, &dev, &cus)) != MOE_OK) return st;
+  if ((st = check_ptr(args->a_codes, dev, "a_codes")) != MOE_OK ||
+      (st = check_ptr(args->b_codes, dev, "b_codes")) != MOE_OK)
+    return st;
+  const moe::GemmParams p = to_params(args);
+  const bool paired = args->epilogue == MOE_EPI_SWIGLU_QUANT;
+  st = hip_status(launch_gemm(p, args->fmt, (int)args->epilogue, paired, cus, stream), "grouped gemm launch");
+  return st == MOE_OK ? ok() : st;
+}
+
+size_t moe_experts_forward_workspace(int32_t T, int32_t k, const moe_weights* w) {
+  if (!w || T < 0 || k < 1 || !valid_fmt(w->fmt) || w->E < 1 || w->H <= 0 || w->I <= 0) return 0;
+  return fwd_layout(T, k, w->E, w->H, w->I, w->fmt).total;
+}
+
+moe_status moe_experts_forward(const moe_weights* w, const uint16_t* hidden_states, const int32_t* top_k_index,
+                               const float* top_k_weights, int32_t T, int32_t k, const moe_options* opt,
+                               uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = validate_weights(w);
+  if (st != MOE_OK) return st;
+  if (T < 0) return fail(MOE_ERR_SHAPE, "T=%d < 0", T);
+  if (k < 1 || k > kMaxK) return fail(MOE_ERR_SHAPE, "k=%d outside [1, %d]", k, kMaxK);
+  if ((int64_t)T * k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "T*k must stay below 2^31");
+  const bool has_limit = opt && opt->has_swiglu_limit;
+  if (has_limit && !(std::isfinite(opt->swiglu_limit) && opt->swiglu_limit > 0.0f))
+    return fail(MOE_ERR_SHAPE, "swiglu_limit must be finite and > 0");
+  if (opt && opt->static_activation_scales)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "the grouped experts path quantizes activations dynamically per block; static activation scales "
+                "are not supported");
+  if (T == 0) return ok();
+  if (!hidden_states || !top_k_index || !top_k_weights || !out)
+    return fail(MOE_ERR_NULL, "hidden_states / top_k_index / top_k_weights / out is NULL");
+  if ((const void*)out == (const void*)hidden_states) return fail(MOE_ERR_UNSUPPORTED, "out must not alias input");
+  const FwdLayout L = fwd_layout(T, k, w->E, w->H, w->I, w->fmt);
+  if (!ws || ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace holds %zu bytes, %zu needed", ws ? ws_bytes : (size_t)0, L.total);
+  int dev, cus;
+  if ((st = check_device(stream, &dev, &cus)) != MOE_OK) return st;
+  for (auto pr : {std::make_pair((const void*)hidden_states, "hidden_states"),
+                  std::make_pair((const void*)top_k_index, "top_k_index"), std::make_pair((const void*)out, "out"),
+                  std::make_pair((const void*)w->w13, "w13"), std::make_pair((const void*)w->w2, "w2"),
+                  std::make_pair((const void*)ws, "workspace")})
+    if ((st = check_ptr(pr.first, dev, pr.second)) != MOE_OK) return st;
+
+  const int E = w->E, H = w->H, I = w->I;
+  const int32_t S = T * k;
+  uint8_t* base = (uint8_t*)ws;
+  int32_t* sorted_slot = (int32_t*)(base + L.sorted_slot);
+  int32_t* offsets = (int32_t*)(base + L.offsets);
+  uint8_t* act_codes = base + L.act_codes;
+  void* act_scales = base + L.act_scales;
+  uint8_t* h_codes = base + L.h_codes;
+  void* h_scales = base + L.h_scales;
+  uint16_t* slot_out = (uint16_t*)(base + L.slot_out);
+  const int32_t expert_begin = opt ? opt->expert_begin : 0;
+
+  hipError_t he = moe::launch_route_sort(top_k_index, S, E, expert_begin, sorted_slot, offsets, nullptr,
+                                         opt ? opt->invalid_count : nullptr, stream);
+  if (he != hipSuccess) return hip_status(he, "route sort launch");
+  he = moe::launch_quant_act(hidden_states, T, H, w->fmt, act_codes, act_scales, stream);
+  if (he != hipSuccess) return hip_status(he, "quant launch");
+
+  moe::GemmParams p1{};
+  p1.a_codes = act_codes;
+  p1.a_scales = act_scales;
+  p1.a_row_index = sorted_slot;
+  p1.a_row_div = k;
+  p1.offsets = offsets;
+  p1.E = E;
+  p1.b_codes = w->w13;
+  p1.b_scales = w->w13_scale;
+  p1.N = 2 * I;
+  p1.K = H;
+  p1.max_rows = S;
+  p1.h_codes = h_codes;
+  p1.h_scales = h_scales;
+  p1.has_limit = has_limit ? 1 : 0;
+  p1.limit = has_limit ? opt->swiglu_limit : 0.0f;
+  he = launch_gemm(p1, w->fmt, moe::kEpiSwiGLUQuant, true, cus, stream);
+  if (he != hipSuccess) return hip_status(he, "gate_up gemm launch");
+
+  moe::GemmParams p2{};
+  p2.a_codes = h_codes;
+  p2.a_scales = h_scales;
+  p2.a_row_index = nullptr;
+  p2.a_row_div = 1;
+  p2.offsets = offsets;
+  p2.E = E;
+  p2.b_codes = w->w2;
+  p2.b_scales = w->w2_scale;
+  p2.N = H;
+  p2.K = I;
+  p2.max_rows = S;
+  p2.slot_out = slot_out;
+  p2.top_k_weights = top_k_weights;
+  p2.slot_of_row = sorted_slot;
+  he = launch_gemm(p2, w->fmt, moe::kEpiWeightedScatter, false, cus, stream);
+  if (he != hipSuccess) return hip_status(he, "down gemm launch");
+
+  he = moe::launch_combine(slot_out, top_k_index, T, k, H, E, expert_begin, out, stream);
+  if (he != hipSuccess) return hip_status(he, "combine launch");
+
+  if (opt && opt->debug) {
+    const moe_debug* d = opt->debug;
+    const bool mx = w->fmt == MOE_FMT_MXFP8A_MXFP4W;
+    const size_t sc_bytes = mx ? (size_t)T * (H / 32) : 4 * (size_t)T * (H / 128);
+    if ((d->sorted_slot &&
+         (he = hipMemcpyAsync(d->sorted_slot, sorted_slot, 4 * (size_t)S, hipMemcpyDeviceToDevice, stream)) !=
+             hipSuccess) ||
+        (d->expert_offsets &&
+         (he = hipMemcpyAsync(d->expert_offsets, offsets, 4 * (size_t)(E + 1), hipMemcpyDeviceToDevice, stream)) !=
+             hipSuccess) ||
+        (d->act_codes &&
+         (he = hipMemcpyAsync(d->act_codes, act_codes, (size_t)T * H, hipMemcpyDeviceToDevice, stream)) !=
+             hipSuccess) ||
+        (d->act_scales &&
+         (he = hipMemcpyAsync(d->act_scales, act_scales, sc_bytes, hipMemcpyDeviceToDevice, stream)) != hipSuccess))
+      return hip_status(he, "debug copy");
+  }
+  return ok();
+}
+
+}  // extern "C"

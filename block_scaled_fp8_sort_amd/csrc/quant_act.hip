@@ -1,0 +1,85 @@
+// Dynamic per-block activation quantization of bf16 rows.
+//
+// The grouped experts dispatch quantizes activations dynamically per block and
+// cannot take precomputed scales ("grouped_mm experts dispatch does not support
+// activation_scheme='static'", section "What it means").  Block rule:
+//  FP8_B128 (blocks of 128): s = max(amax, 1e-4) / 448 (fp32), code = e4m3(x / s)
+//  with an IEEE fp32 division, so codes match a host implementation bit for bit.
+//  MX (blocks of 32): s = 2^e, e = ceil(log2(max(amax, 1e-4) / 448)) from the
+//  fp32 bits, stored as the byte e + 127; code = e4m3(x * 2^-e), exact scaling.
+//
+// The kernel is HBM-bound (2 bytes in, 1 byte + a scale out per element): each
+// lane reads 16 contiguous bytes (8 bf16), the lanes of one block reduce the
+// amax with xor butterflies, and each lane stores its 8 codes as one 8-byte
+// store.  Quantizing the T token rows once and gathering codes by index later is
+// the same as gathering first (the rule is row-local).
+#include "device_common.h"
+#include "internal.h"
+
+namespace moe {
+
+namespace {
+
+template <int BLOCK>
+__global__ __launch_bounds__(256) void quant_act_kernel(const uint4* __restrict__ x, int64_t n_chunks, int32_t H,
+                                                        uint2* __restrict__ codes, void* __restrict__ scales) {
+  constexpr int kLanesPerBlock = BLOCK / 8;  // 16 (FP8_B128) or 4 (MX)
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  // n_chunks is a multiple of kLanesPerBlock and every lane group stays together
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n_chunks; c += stride) {
+    const uint4 v = x[c];
+    float f[8];
+    f[0] = bf16_bits_to_f32(v.x & 0xFFFF);
+    f[1] = bf16_bits_to_f32(v.x >> 16);
+    f[2] = bf16_bits_to_f32(v.y & 0xFFFF);
+    f[3] = bf16_bits_to_f32(v.y >> 16);
+    f[4] = bf16_bits_to_f32(v.z & 0xFFFF);
+    f[5] = bf16_bits_to_f32(v.z >> 16);
+    f[6] = bf16_bits_to_f32(v.w & 0xFFFF);
+    f[7] = bf16_bits_to_f32(v.w >> 16);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[i]));
+#pragma unroll
+    for (int m = 1; m < kLanesPerBlock; m <<= 1) amax = wave_max_xor(amax, m);
+    uint2 out;
+    if constexpr (BLOCK == 128) {
+      const float s = fp8_block_scale(amax);
+      float q[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = f[i] / s;  // IEEE division
+      out.x = e4m3x4(q[0], q[1], q[2], q[3]);
+      out.y = e4m3x4(q[4], q[5], q[6], q[7]);
+      if ((c % kLanesPerBlock) == 0) ((float*)scales)[c / kLanesPerBlock] = s;
+    } else {
+      const int e = mx_block_exponent(amax);
+      float q[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = __builtin_ldexpf(f[i], -e);
+      out.x = e4m3x4(q[0], q[1], q[2], q[3]);
+      out.y = e4m3x4(q[4], q[5], q[6], q[7]);
+      if ((c % kLanesPerBlock) == 0) ((uint8_t*)scales)[c / kLanesPerBlock] = (uint8_t)(e + 127);
+    }
+    codes[c] = out;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_act(const uint16_t* x, int32_t rows, int32_t H, int fmt, uint8_t* codes, void* scales,
+                            hipStream_t stream) {
+  const int64_t n_chunks = (int64_t)rows * H / 8;
+  if (n_chunks == 0) return hipSuccess;
+  const int threads = 256;
+  const int64_t want = (n_chunks + threads - 1) / threads;
+  const int blocks = (int)(want < 256 * 64 ? want : 256 * 64);
+  if (fmt == 0)
+    hipLaunchKernelGGL(quant_act_kernel<128>, dim3(blocks), dim3(threads), 0, stream, (const uint4*)x, n_chunks, H,
+                       (uint2*)codes, scales);
+  else
+    hipLaunchKernelGGL(quant_act_kernel<32>, dim3(blocks), dim3(threads), 0, stream, (const uint4*)x, n_chunks, H,
+                       (uint2*)codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,240 @@
+/*
+ * moe.h: C ABI of the MI355X (gfx950) fine-grained-quantized MoE experts forward.
+ *
+ * The operation follows these pages (cited by title and section):
+ *  [P-grouped]  "grouped_mm experts dispatch does not support
+ *               activation_scheme='static'", sections "What it means" and
+ *               "Source": the grouped experts forward flattens the (token, slot)
+ *               pairs, sorts them by expert id, gathers each pair's token row,
+ *               quantizes activations dynamically per block, runs the grouped
+ *               GEMMs, then zeroes sentinel rows, weights each slot's output and
+ *               sums the k slots of a token with a deterministic reshape+sum
+ *               (not an atomic index_add_) before casting back to bf16.
+ *  [P-mega]     "DeepGEMM Mega MoE requires a `process_group` for the EP group",
+ *               the forward's docstring: top_k_index holds global expert ids,
+ *               -1 marks a skipped slot; gate_up_proj / down_proj are the L1 / L2
+ *               weights with UE8M0 scale factors, transformed once; an optional
+ *               swiglu_limit clamps the SwiGLU (absent means unclamped).
+ *  [P-fp4]      "DeepGEMM Mega MoE requires FP4-packed expert weights
+ *               (dtype=int8)", section "Source": FP4 weights come packed in int8.
+ *  [P-devices]  "DeepGEMM experts selected on a model spanning multiple CUDA
+ *               devices", the record's source: the forward refuses a multi-device
+ *               model, non-bf16 hidden states and static activation scales before
+ *               any kernel work, and picks the nn or nt weight layout.
+ *
+ * Conventions for every call:
+ *  - Pointers marked "device" are device memory on the device current for
+ *    `stream`; the caller owns every buffer.  Nothing here allocates device
+ *    memory, frees it, or synchronizes the host: every call validates its
+ *    arguments on the host, enqueues its kernels on `stream` and returns.
+ *  - Inputs are read-only.  Outputs must not alias inputs.
+ *  - Validation failures return before anything is enqueued; the text of the
+ *    last failure on the calling thread is available from moe_last_error().
+ *  - T (tokens), k (slots per token), E (local experts), H (hidden size) and
+ *    I (expert intermediate size) are as in the forward; S = T * k slots.
+ *  - Shapes: H and I must be multiples of 128.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t only */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,       /* a size is out of range or not a multiple of the block */
+  MOE_ERR_DTYPE = 3,       /* an argument has the wrong element type (the pages: ValueError on non-bf16 input) */
+  MOE_ERR_UNSUPPORTED = 4, /* a valid request this library does not serve (static activation scales, aliasing) */
+  MOE_ERR_WORKSPACE = 5,   /* workspace missing or smaller than the matching *_workspace() size */
+  MOE_ERR_ARCH = 6,        /* the stream's device is not gfx950 */
+  MOE_ERR_DEVICE = 7,      /* a pointer lives on another device than the stream */
+  MOE_ERR_HIP = 8          /* the HIP runtime reported an error while enqueueing */
+} moe_status;
+
+/* Quantization formats.
+ * MOE_FMT_FP8_B128: activations e4m3 (OCP e4m3fn) with one fp32 scale per 1x128
+ *   block along the row; weights e4m3 with one fp32 scale per 128x128 block.
+ * MOE_FMT_MXFP8A_MXFP4W: activations e4m3 with one UE8M0 scale byte per 1x32
+ *   block; weights e2m1 packed two per byte along K (even k in the low nibble)
+ *   with one UE8M0 byte per 1x32 block along K.  A UE8M0 byte b means 2^(b-127).
+ * In both, a dequantized value is code value times its block scale. */
+typedef enum moe_format { MOE_FMT_FP8_B128 = 0, MOE_FMT_MXFP8A_MXFP4W = 1 } moe_format;
+
+/* Weight layouts accepted by moe_prepare_weights: nt stores each expert's weight
+ * as [N, K] (rows are output features), nn as [K, N]; the pages' forward picks
+ * between the two grouped matmuls by this flag ([P-devices]). */
+typedef enum moe_layout { MOE_LAYOUT_NT = 0, MOE_LAYOUT_NN = 1 } moe_layout;
+
+const char* moe_status_string(moe_status s);
+/* Detail text of the last failed call on this thread ("" when none). */
+const char* moe_last_error(void);
+
+/* ------------------------------------------------------------ route sort --
+ * Sorts the S = T*k flat slots s = t*k + j by expert ([P-grouped], "Source":
+ * the flattened expert ids are sorted and the rows gathered by perm // k).
+ * key(s) = top_k_index[s] - expert_begin when that lies in [0, E), otherwise
+ * the slot is skipped and gets the sentinel key E ([P-mega]: -1 marks a skipped
+ * slot; ids outside this GPU's range are treated the same way).  Sentinels sort
+ * after every valid slot and ties keep ascending s, so the result is unique.
+ *
+ *  top_k_index     device int32 [T*k], global expert ids.
+ *  sorted_slot     device int32 [T*k] out: the flat slot at each sorted row.
+ *  expert_offsets  device int32 [E+1] out: number of slots with key < e;
+ *                  expert e owns sorted rows [offsets[e], offsets[e+1]) and
+ *                  offsets[E] is the number of valid slots.
+ *  slot_pos        device int32 [T*k] out, may be NULL: inverse of sorted_slot.
+ *  invalid_count   device int32 [1] out, may be NULL: number of ids that are
+ *                  neither -1 nor inside [expert_begin, expert_begin + E).
+ *  ws / ws_bytes   device workspace of at least moe_route_sort_workspace() bytes.
+ * Limits: 0 <= T, 1 <= k <= 64, 1 <= E <= 512, T*k < 2^31. */
+size_t moe_route_sort_workspace(int32_t T, int32_t k, int32_t E);
+moe_status moe_route_sort(const int32_t* top_k_index, int32_t T, int32_t k, int32_t E, int32_t expert_begin,
+                          int32_t* sorted_slot, int32_t* expert_offsets, int32_t* slot_pos,
+                          int32_t* invalid_count, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* --------------------------------------------------- activation quantization --
+ * Dynamic per-block quantization of bf16 rows ([P-grouped], "What it means":
+ * activations are quantized dynamically per block; precomputed static scales are
+ * refused).  Per block of B = 128 (FP8_B128) or 32 (MX) elements of a row:
+ * amax = max|x|; FP8_B128: s = max(amax, 1e-4f) / 448 in fp32 and
+ * code = e4m3(x / s) with an IEEE fp32 division; MX: e = ceil(log2(max(amax,
+ * 1e-4f) / 448)) read exactly from the fp32 bits, scale byte e + 127 and
+ * code = e4m3(x * 2^-e).  e4m3() rounds to nearest even and saturates at 448.
+ *
+ *  x       device bf16 bit patterns [rows, H].
+ *  codes   device uint8 [rows, H] out.
+ *  scales  device out: float [rows, H/128] (FP8_B128) or uint8 [rows, H/32] (MX). */
+moe_status moe_quant_act(const uint16_t* x, int32_t rows, int32_t H, moe_format fmt, uint8_t* codes, void* scales,
+                         hipStream_t stream);
+
+/* --------------------------------------------------------- expert weights --
+ * Descriptor of one layer's quantized expert weights in the kernel's layout (nt):
+ *  w13        gate_up_proj codes: FP8_B128 uint8 [E, 2I, H]; MX packed uint8
+ *             [E, 2I, H/2].  Rows [0, I) are the gate, rows [I, 2I) the up
+ *             projection.
+ *  w13_scale  FP8_B128 float [E, 2I/128, H/128]; MX uint8 [E, 2I, H/32].
+ *  w2         down_proj codes: FP8_B128 uint8 [E, H, I]; MX packed [E, H, I/2].
+ *  w2_scale   FP8_B128 float [E, H/128, I/128]; MX uint8 [E, H, I/32].
+ * All four are device pointers that must stay valid while the descriptor is used. */
+typedef struct moe_weights {
+  moe_format fmt;
+  int32_t E, H, I;
+  const uint8_t* w13;
+  const void* w13_scale;
+  const uint8_t* w2;
+  const void* w2_scale;
+} moe_weights;
+
+/* One-shot weight preparation ([P-mega]: both weight pairs are transformed
+ * together once before the first forward).  layout NT: the arrays are already in
+ * the kernel layout; with prepared == NULL the descriptor points at them, else
+ * they are copied into `prepared`.  layout NN: gate_up is [E, H, 2I] and down is
+ * [E, I, H] (codes; FP8_B128 only, scales [E, H/128, 2I/128] and [E, I/128,
+ * H/128]); they are transposed into `prepared`, which must hold
+ * moe_prepared_weights_size() bytes.  Enqueued on `stream`; the descriptor is
+ * filled on the host. */
+size_t moe_prepared_weights_size(moe_format fmt, int32_t E, int32_t H, int32_t I);
+moe_status moe_prepare_weights(moe_format fmt, moe_layout layout, int32_t E, int32_t H, int32_t I,
+                               const void* gate_up, const void* gate_up_scale, const void* down,
+                               const void* down_scale, void* prepared, size_t prepared_bytes, moe_weights* out,
+                               hipStream_t stream);
+
+/* ----------------------------------------------------------- grouped GEMM --
+ * For every expert e and sorted row r in [offsets[e], offsets[e+1]):
+ *   C[r, n] = sum_i A[a_row(r), i] * B[e, n, i]      (n < N, i < K)
+ * with both operands dequantized (code times block scale), products exact and
+ * sums in fp32.  a_row(r) = a_row_index[r] / a_row_divisor, or r when
+ * a_row_index is NULL (the row gather of [P-grouped], "Source").  Then one
+ * epilogue:
+ *  MOE_EPI_STORE_F32         c_f32[r, n] = C[r, n]                (fp32 [max_rows, N])
+ *  MOE_EPI_SWIGLU_QUANT      N = 2I: g = C[r, n], u = C[r, I + n] for n < I; with a
+ *                            limit L, g = min(g, L) and u = clamp(u, -L, L);
+ *                            h = silu(g) * u, quantized per block along I with the
+ *                            activation rule into h_codes [max_rows, I] and
+ *                            h_scales (float [max_rows, I/128] or uint8 [max_rows, I/32]).
+ *  MOE_EPI_WEIGHTED_SCATTER  slot = slot_of_row[r]:
+ *                            slot_out[slot, n] = bf16(top_k_weights[slot] * C[r, n]).
+ * Rows at and beyond offsets[E] are not written.  max_rows bounds offsets[E]
+ * (normally T*k).  A codes are [rowsA, K] uint8 with scales float [rowsA, K/128]
+ * or uint8 [rowsA, K/32]; B is one weight of a moe_weights (nt).  K must be a
+ * multiple of 128, N a multiple of 128 (of 256 for SWIGLU_QUANT). */
+typedef enum moe_epilogue {
+  MOE_EPI_STORE_F32 = 0,
+  MOE_EPI_SWIGLU_QUANT = 1,
+  MOE_EPI_WEIGHTED_SCATTER = 2
+} moe_epilogue;
+
+typedef struct moe_gemm_args {
+  moe_format fmt;
+  int32_t N, K, E;
+  int32_t max_rows;
+  const uint8_t* a_codes;
+  const void* a_scales;
+  const int32_t* a_row_index; /* may be NULL */
+  int32_t a_row_divisor;      /* >= 1 */
+  const int32_t* expert_offsets;
+  const uint8_t* b_codes;
+  const void* b_scales;
+  moe_epilogue epilogue;
+  float* c_f32;
+  uint8_t* h_codes;
+  void* h_scales;
+  int32_t has_swiglu_limit;
+  float swiglu_limit;
+  uint16_t* slot_out;
+  const float* top_k_weights;
+  const int32_t* slot_of_row;
+} moe_gemm_args;
+
+moe_status moe_grouped_gemm(const moe_gemm_args* args, hipStream_t stream);
+
+/* ---------------------------------------------------- fused experts forward --
+ * The whole path in one call ([P-grouped] and [P-mega]): route sort, activation
+ * quantization, gate_up grouped GEMM with the SwiGLU (+ optional clamp) and h
+ * quantization fused into its epilogue, down grouped GEMM with the routing
+ * weight applied in its epilogue, and the deterministic per-token sum over the
+ * k slots in ascending j.  Skipped slots are never computed and contribute
+ * exactly zero whatever their weight (NaN included).
+ *
+ *  w               prepared weights (moe_prepare_weights).
+ *  hidden_states   device bf16 [T, H].
+ *  top_k_index     device int32 [T, k], global expert ids, -1 = skipped.
+ *  top_k_weights   device float [T, k] (unmasked routing weights).
+ *  opt             may be NULL (no clamp, expert_begin 0).
+ *  out             device bf16 [T, H] out.
+ *  ws / ws_bytes   device workspace of at least moe_experts_forward_workspace().
+ * T == 0 returns MOE_OK with nothing enqueued. */
+typedef struct moe_debug {
+  /* Optional device copies of intermediates, for parity checks; each may be NULL. */
+  int32_t* sorted_slot;    /* [T*k] */
+  int32_t* expert_offsets; /* [E+1] */
+  uint8_t* act_codes;      /* [T, H] */
+  void* act_scales;        /* float [T, H/128] or uint8 [T, H/32] */
+} moe_debug;
+
+typedef struct moe_options {
+  int32_t has_swiglu_limit;
+  float swiglu_limit;    /* must be finite and > 0 when has_swiglu_limit */
+  int32_t expert_begin;  /* global id of local expert 0 */
+  int32_t static_activation_scales; /* nonzero requests static scales: refused (MOE_ERR_UNSUPPORTED) */
+  int32_t* invalid_count; /* device int32 [1], may be NULL */
+  moe_debug* debug;       /* may be NULL */
+} moe_options;
+
+size_t moe_experts_forward_workspace(int32_t T, int32_t k, const moe_weights* w);
+moe_status moe_experts_forward(const moe_weights* w, const uint16_t* hidden_states, const int32_t* top_k_index,
+                               const float* top_k_weights, int32_t T, int32_t k, const moe_options* opt,
+                               uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,165 @@
+"""The C-ABI library on the host: it loads, exports every function include/moe.h
+declares, and refuses bad calls before touching the GPU (no GPU here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_sort_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, WS = 0, 1, 2, 3, 4, 5
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.library_path()):
+        import block_scaled_fp8_sort_amd.build as b
+        b.build()
+    return moe.load_library()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = _declared_functions()
+    assert "moe_experts_forward" in names and "moe_grouped_gemm" in names
+    assert len(names) == 10
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.moe_status_string(0) == b"MOE_OK"
+    assert lib.moe_status_string(5) == b"MOE_ERR_WORKSPACE"
+
+
+def test_route_sort_refusals(lib):
+    p = ctypes.c_void_p(16)  # never dereferenced: the calls fail validation first
+    assert lib.moe_route_sort(p, 4, 0, 8, 0, p, p, None, None, None, 0, None) == SHAPE
+    assert lib.moe_route_sort(p, 4, 65, 8, 0, p, p, None, None, None, 0, None) == SHAPE
+    assert lib.moe_route_sort(p, 4, 2, 0, 0, p, p, None, None, None, 0, None) == SHAPE
+    assert lib.moe_route_sort(p, 4, 2, 513, 0, p, p, None, None, None, 0, None) == SHAPE
+    assert lib.moe_route_sort(p, -1, 2, 8, 0, p, p, None, None, None, 0, None) == SHAPE
+    assert lib.moe_route_sort(None, 4, 2, 8, 0, p, p, None, None, None, 0, None) == NULL
+    assert lib.moe_route_sort(p, 4, 2, 8, 0, p, None, None, None, None, 0, None) == NULL
+    assert lib.moe_route_sort(p, 4, 2, 8, 0, p, ctypes.c_void_p(32), None, None, None, 0, None) == UNSUP
+    assert b"alias" in lib.moe_last_error()
+    # an empty batch passes validation even though its (empty) arrays share an address
+
+
+def test_quant_refusals(lib):
+    p = ctypes.c_void_p(16)
+    q = ctypes.c_void_p(48)
+    assert lib.moe_quant_act(p, 4, 100, 0, q, q, None) == SHAPE
+    assert lib.moe_quant_act(p, 4, 128, 7, q, q, None) == UNSUP
+    assert lib.moe_quant_act(None, 4, 128, 0, q, q, None) == NULL
+    assert lib.moe_quant_act(p, 0, 128, 0, q, q, None) == OK  # nothing to do, nothing enqueued
+
+
+def _weights(E=4, H=256, I=128, fmt=0):
+    w = moe.MoeWeights()
+    w.fmt, w.E, w.H, w.I = fmt, E, H, I
+    w.w13 = w.w13_scale = w.w2 = w.w2_scale = 64
+    return w
+
+
+def test_forward_refusals(lib):
+    p = ctypes.c_void_p(16)
+    w = _weights()
+    opt = moe.MoeOptions()
+
+    def fwd(w=w, T=8, k=2, opt=None, out=ctypes.c_void_p(32), ws=ctypes.c_void_p(64), ws_bytes=1 << 40):
+        return lib.moe_experts_forward(ctypes.byref(w), p, p, p, T, k, None if opt is None else ctypes.byref(opt),
+                                       out, ws, ws_bytes, None)
+
+    assert fwd(T=0) == OK
+    assert fwd(k=0) == SHAPE
+    assert fwd(w=_weights(H=200)) == SHAPE
+    assert fwd(w=_weights(I=64)) == SHAPE
+    assert fwd(w=_weights(E=0)) == SHAPE
+    assert fwd(w=_weights(fmt=9)) == UNSUP
+    opt.static_activation_scales = 1
+    assert fwd(opt=opt) == UNSUP
+    assert b"static" in lib.moe_last_error()
+    opt.static_activation_scales = 0
+    opt.has_swiglu_limit, opt.swiglu_limit = 1, float("nan")
+    assert fwd(opt=opt) == SHAPE
+    opt.swiglu_limit = -2.0
+    assert fwd(opt=opt) == SHAPE
+    opt.swiglu_limit = float("inf")
+    assert fwd(opt=opt) == SHAPE
+    assert fwd(ws=None) == WS
+    need = lib.moe_experts_forward_workspace(8, 2, ctypes.byref(w))
+    assert need > 0
+    assert fwd(ws_bytes=need - 1) == WS
+    assert fwd(out=p) == UNSUP  # out aliases hidden_states
+    bad = _weights()
+    bad.w2 = None
+    assert fwd(w=bad) == NULL
+
+
+def test_gemm_refusals(lib):
+    a = moe.MoeGemmArgs()
+    a.fmt, a.N, a.K, a.E, a.max_rows = 0, 256, 256, 4, 64
+    a.a_codes = a.a_scales = a.expert_offsets = a.b_codes = a.b_scales = 16
+    a.epilogue = moe.EPI_STORE_F32
+    assert lib.moe_grouped_gemm(ctypes.byref(a), None) == NULL  # c_f32 missing
+    a.c_f32 = 16
+    a.K = 100
+    assert lib.moe_grouped_gemm(ctypes.byref(a), None) == SHAPE
+    a.K = 256
+    a.epilogue = moe.EPI_SWIGLU_QUANT
+    a.N = 384
+    a.h_codes = a.h_scales = 16
+    assert lib.moe_grouped_gemm(ctypes.byref(a), None) == SHAPE  # N must be 2I with I % 128 == 0
+    a.N = 256
+    a.has_swiglu_limit, a.swiglu_limit = 1, 0.0
+    assert lib.moe_grouped_gemm(ctypes.byref(a), None) == SHAPE
+    a.epilogue = 9
+    assert lib.moe_grouped_gemm(ctypes.byref(a), None) == UNSUP
+    a.epilogue = moe.EPI_STORE_F32
+    a.max_rows = 0
+    assert lib.moe_grouped_gemm(ctypes.byref(a), None) == OK  # nothing to do
+
+
+def test_prepare_weights_host_paths(lib):
+    desc = moe.MoeWeights()
+    p = ctypes.c_void_p(4096)
+    # nt in place: the descriptor points at the caller's arrays, no device work
+    assert lib.moe_prepare_weights(0, 0, 4, 256, 128, p, p, p, p, None, 0, ctypes.byref(desc), None) == OK
+    assert desc.E == 4 and desc.H == 256 and desc.I == 128 and desc.w13 == 4096
+    # nn needs a buffer; MX only comes in nt
+    assert lib.moe_prepare_weights(0, 1, 4, 256, 128, p, p, p, p, None, 0, ctypes.byref(desc), None) == WS
+    assert lib.moe_prepare_weights(1, 1, 4, 256, 128, p, p, p, p, p, 1 << 30, ctypes.byref(desc), None) == UNSUP
+    assert lib.moe_prepared_weights_size(0, 4, 256, 128) == 4 * 256 * 256 + 4 * 4 * 2 * 2 * 4 + 256 * 128 * 4 + 256
+    assert lib.moe_prepared_weights_size(0, 4, 250, 128) == 0
+
+
+def test_python_face_raises_like_the_pages():
+    x = torch.zeros((4, 256), dtype=torch.float32)
+    ids = torch.zeros((4, 2), dtype=torch.int32)
+    w = torch.ones((4, 2), dtype=torch.float32)
+    with pytest.raises(ValueError, match="bfloat16"):
+        moe.experts_forward(x, ids, w, weights=None)
+    with pytest.raises(NotImplementedError, match="static"):
+        moe.experts_forward(x.bfloat16(), ids, w, weights=None, activation_scheme="static")
+    with pytest.raises(NotImplementedError, match="int8"):
+        moe.prepare_weights(torch.zeros(2, 4, dtype=torch.float16), None, None, None, fmt=moe.FMT_MXFP8A_MXFP4W)
+
+
+def test_workspace_sized_for_next_power_of_two():
+    path = os.path.join(ROOT, "tests", "golden", "pow2_buffer_tokens.txt")
+    rows = [tuple(int(v) for v in l.split()) for l in open(path) if l.strip() and not l.startswith("#")]
+    for n, sized in rows:
+        assert moe._pow2_tokens(n) == sized
+        assert sized < 2 * n or n == 1

@@ -1,0 +1,296 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Bit-exact: the route sort (sorted_slot, expert_offsets, slot_pos, invalid
+count) and the activation codes and scales.  Tolerance (bf16 outputs):
+max|err| <= 1e-2 * max|ref| and relative L2 <= 5e-3.  Sizes: the tiny layer and
+mid-size cases that span several tiles with ragged tails run whole through the
+oracle; the full-size layers run whole on the GPU and are checked on a seeded
+sample of tokens.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_sort_amd as moe
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+FP8, MX = W.FMT_FP8_B128, W.FMT_MX
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bits_to_f64(b):
+    return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def assert_out_close(got_bits, ref_bits, what=""):
+    g, r = bits_to_f64(got_bits), bits_to_f64(ref_bits)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    max_ref = np.max(np.abs(r))
+    max_err = np.max(np.abs(g - r))
+    rel_l2 = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
+    say(f"  {what}: max|err| / max|ref| = {max_err / max(max_ref, 1e-30):.2e}, rel L2 = {rel_l2:.2e}")
+    assert max_err <= 1e-2 * max_ref, f"{what}: max|err| {max_err} > 1e-2 * {max_ref}"
+    assert rel_l2 <= 5e-3, f"{what}: rel L2 {rel_l2}"
+
+
+def host(t):
+    return W.to_numpy(t)
+
+
+# ---------------------------------------------------------------- route sort
+def _rand_ids(rng, T, k, E, p_skip, p_bad, lo=0):
+    ids = rng.integers(lo, lo + E, size=(T, k)).astype(np.int32)
+    u = rng.random((T, k))
+    ids[u < p_skip] = -1
+    bad = u > 1 - p_bad
+    ids[bad] = rng.choice(np.array([lo + E, lo + E + 3, -5, lo - 1, 1 << 30], np.int32), size=int(bad.sum()))
+    return ids
+
+
+SORT_CASES = [
+    (1, 1, 1, 0.0, 0.0), (7, 2, 3, 0.2, 0.1), (64, 2, 8, 0.0, 0.0), (64, 8, 128, 0.05, 0.0),
+    (4096, 2, 8, 0.0, 0.0), (8192, 8, 256, 0.05, 0.01), (16384, 8, 256, 0.05, 0.0), (1000, 3, 512, 0.3, 0.05),
+    (333, 64, 5, 0.1, 0.1),
+]
+
+
+@pytest.mark.parametrize("T,k,E,p_skip,p_bad", SORT_CASES)
+def test_route_sort_bit_exact(T, k, E, p_skip, p_bad):
+    say(f"route_sort T={T} k={k} E={E}")
+    rng = np.random.default_rng(T + 7 * k + 13 * E)
+    ids = _rand_ids(rng, T, k, E, p_skip, p_bad, lo=3)
+    ss, off, sp, inv = moe.route_sort(torch.from_numpy(ids).to(DEV), E, expert_begin=3)
+    torch.cuda.synchronize()
+    o_ss, o_off, o_sp, o_inv = oracle.route_sort(ids, E, expert_begin=3)
+    assert np.array_equal(host(off), o_off)
+    assert np.array_equal(host(ss), o_ss)
+    assert np.array_equal(host(sp), o_sp)
+    assert int(host(inv)[0]) == o_inv
+
+
+def test_route_sort_degenerate():
+    for ids in (np.full((50, 4), -1, np.int32), np.full((50, 4), 2, np.int32), np.zeros((0, 4), np.int32)):
+        ss, off, sp, inv = moe.route_sort(torch.from_numpy(ids).to(DEV), 3)
+        torch.cuda.synchronize()
+        o = oracle.route_sort(ids, 3)
+        assert np.array_equal(host(off), o[1])
+        assert np.array_equal(host(ss), o[0])
+
+
+# -------------------------------------------------------------- quantization
+def _bf16(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("fmt", [FP8, MX])
+def test_quant_act_bit_exact_random(fmt):
+    say(f"quant_act random fmt={fmt}")
+    rng = np.random.default_rng(5 + fmt)
+    rows, H = 2048, 1024
+    x = rng.standard_normal((rows, H)) * np.exp(rng.uniform(-12, 12, size=(rows, 1)))
+    x[::17, :128] = 0.0                                  # zero blocks -> floor scale
+    x[5::23, 64] = 3e4                                   # outliers
+    x[7::29] *= 1e-6                                     # tiny rows (below the floor)
+    xb = _bf16(x)
+    codes, scales = moe.quant_act(xb.to(DEV), fmt)
+    torch.cuda.synchronize()
+    o_codes, o_scales = oracle.quant_rows_bf16(xb.view(torch.int16).numpy().view(np.uint16), fmt)
+    g_codes = host(codes)
+    mism = np.argwhere(g_codes != o_codes)
+    assert mism.size == 0, f"{len(mism)} code mismatches, first at {mism[:5]}"
+    assert np.array_equal(host(scales).view(np.uint8), o_scales.view(np.uint8))
+
+
+@pytest.mark.parametrize("fmt", [FP8, MX])
+def test_quant_act_all_bf16_values(fmt):
+    """Every finite bf16 with |x| <= 448 (both signs), in blocks whose scale is 1,
+    then the same values under a random non-power-of-two scale."""
+    say(f"quant_act all-bf16 fmt={fmt}")
+    B = 128 if fmt == FP8 else 32
+    bits = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    vals = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    keep = np.isfinite(vals) & (np.abs(vals) <= 448)
+    v = vals[keep]
+    per = B - 1
+    n_rows = (v.size + per - 1) // per
+    v = np.concatenate([v, np.zeros(n_rows * per - v.size, np.float32)]).reshape(n_rows, per)
+    rng = np.random.default_rng(9)
+    for mult in (1.0, float(np.float32(rng.uniform(1.01, 1.99))) * 2.0 ** -7):
+        block = np.concatenate([np.full((n_rows, 1), 448.0, np.float32), v], axis=1) * np.float32(mult)
+        # pack the blocks into rows of 128 (one FP8 block or four MX blocks per row)
+        flat = block.reshape(-1)
+        pad = (-flat.size) % 128
+        flat = np.concatenate([flat, np.zeros(pad, np.float32)]).reshape(-1, 128)
+        xb = _bf16(flat)
+        codes, scales = moe.quant_act(xb.to(DEV), fmt)
+        torch.cuda.synchronize()
+        o_codes, o_scales = oracle.quant_rows_bf16(xb.view(torch.int16).numpy().view(np.uint16), fmt)
+        assert np.array_equal(host(codes), o_codes)
+        assert np.array_equal(host(scales).view(np.uint8), o_scales.view(np.uint8))
+
+
+# -------------------------------------------------------------- grouped GEMM
+def _gemm_case(fmt, E, N, K, T, k, seed, p_skip=0.1):
+    rng = np.random.default_rng(seed)
+    if fmt == FP8:
+        b, bs = W.fp8_weights(E, N, K, seed, "gemm", DEV)
+    else:
+        b, bs = W.fp4_weights(E, N, K, seed, "gemm", DEV)
+    x = W.hidden_states(T, K, seed, DEV)
+    ids = torch.from_numpy(_rand_ids(rng, T, k, E, p_skip, 0.0)).to(DEV)
+    a, asc = moe.quant_act(x, fmt)
+    ss, off, _, _ = moe.route_sort(ids, E)
+    return b, bs, a, asc, ss, off, ids
+
+
+@pytest.mark.parametrize("fmt", [FP8])
+@pytest.mark.parametrize("E,N,K,T,k", [(3, 256, 256, 40, 2), (5, 640, 384, 700, 3), (2, 384, 1024, 300, 1)])
+def test_grouped_gemm_store_f32(fmt, E, N, K, T, k):
+    say(f"gemm store f32 fmt={fmt} E={E} N={N} K={K} T={T} k={k}")
+    b, bs, a, asc, ss, off, ids = _gemm_case(fmt, E, N, K, T, k, seed=N + K + T)
+    S = T * k
+    c = torch.full((S, N), float("nan"), dtype=torch.float32, device=DEV)
+    moe.grouped_gemm(fmt, a, asc, off, b, bs, N, K, moe.EPI_STORE_F32, S, a_row_index=ss, a_row_divisor=k, c_f32=c)
+    torch.cuda.synchronize()
+    offs = host(off)
+    ref = oracle.grouped_gemm(fmt, host(a), host(asc), offs, host(b), host(bs), N, K, row_index=host(ss), row_div=k)
+    got = host(c)[: offs[-1]].astype(np.float64)
+    assert np.all(np.isnan(host(c)[offs[-1]:]))  # rows past the valid ones are never written
+    err = np.abs(got - ref)
+    scale = np.max(np.abs(ref))
+    say(f"  max err / max ref = {np.max(err) / scale:.2e}")
+    # fp8 products are exact, but the MFMA's internal sum of a 128-long block is
+    # not a sequential fp32 sum: measured ~2e-5 of max|ref| against fp64
+    assert np.max(err) <= 1e-4 * scale + 1e-30
+
+
+# ------------------------------------------------------------- the forward
+def _prepare(inp, fmt):
+    return moe.prepare_weights(inp["w13"], inp["s13"], inp["w2"], inp["s2"], fmt=fmt)
+
+
+def _forward_case(wl, inp, tokens=None, debug=False, limit="workload"):
+    lim = wl.swiglu_limit if limit == "workload" else limit
+    w = _prepare(inp, wl.fmt)
+    dbg = {} if debug else None
+    inv = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w, swiglu_limit=lim, invalid_count=inv, debug=dbg)
+    torch.cuda.synchronize()
+    n = {k_: host(v) for k_, v in inp.items()}
+    ref = oracle.forward(wl.fmt, n["w13"], n["s13"], n["w2"], n["s2"], n["x"], n["ids"], n["w"], swiglu_limit=lim,
+                         tokens=tokens)
+    return host(out), ref, dbg, n, int(host(inv)[0])
+
+
+def _small_workload(name, fmt, T, H, I, E, k, routing="uniform", skip=0.0, limit=None, seed=0):
+    return W.Workload(name, T=T, H=H, I=I, E=E, k=k, fmt=fmt, routing=routing, zipf_s=1.1, skip=skip,
+                      swiglu_limit=limit, seed=seed)
+
+
+SMALL = [
+    W.WORKLOADS["tiny"],
+    _small_workload("ragged_fp8", FP8, T=300, H=512, I=384, E=6, k=3, routing="zipf", skip=0.1, seed=11),
+    _small_workload("ragged_fp8_clamp", FP8, T=517, H=384, I=256, E=12, k=4, routing="zipf", skip=0.05,
+                    limit=0.05, seed=12),
+    _small_workload("k1_one_expert", FP8, T=129, H=256, I=128, E=1, k=1, seed=13),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_forward_parity_small(wl):
+    say(f"forward {wl.name}")
+    inp = W.inputs(wl, DEV)
+    got, ref, dbg, n, inv = _forward_case(wl, inp, debug=True)
+    o_ss, o_off, _, o_inv = oracle.route_sort(n["ids"], wl.E)
+    assert np.array_equal(host(dbg["sorted_slot"]), o_ss)
+    assert np.array_equal(host(dbg["expert_offsets"]), o_off)
+    assert inv == o_inv
+    o_codes, o_scales = oracle.quant_rows_bf16(n["x"], wl.fmt)
+    assert np.array_equal(host(dbg["act_codes"]), o_codes)
+    assert np.array_equal(host(dbg["act_scales"]).view(np.uint8), o_scales.view(np.uint8))
+    assert_out_close(got, ref, wl.name)
+
+
+def test_forward_invariants_tiny():
+    wl = W.WORKLOADS["tiny"]
+    inp = W.inputs(wl, DEV)
+    w = _prepare(inp, wl.fmt)
+    a = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w).clone()
+    b = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w).clone()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "not deterministic"
+    perm = torch.randperm(wl.T, generator=torch.Generator().manual_seed(3)).to(DEV)
+    c = moe.experts_forward(inp["x"][perm].contiguous(), inp["ids"][perm].contiguous(), inp["w"][perm].contiguous(),
+                            w)
+    assert torch.equal(c.view(torch.int16), a[perm].view(torch.int16)), "token permutation changed results"
+    # a NaN-poisoned workspace changes nothing
+    ws = torch.full((moe.forward_workspace_bytes(wl.T, wl.k, w),), 0xFF, dtype=torch.uint8, device=DEV)
+    d = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w, workspace=ws)
+    assert torch.equal(d.view(torch.int16), a.view(torch.int16))
+    # skipped slots with NaN weights contribute exactly nothing
+    ids = inp["ids"].clone()
+    wts = inp["w"].clone()
+    ids[:, 1] = -1
+    wts[:, 1] = float("nan")
+    e = moe.experts_forward(inp["x"], ids, wts, w)
+    ids2 = inp["ids"][:, :1].contiguous()
+    f = moe.experts_forward(inp["x"], ids2, inp["w"][:, :1].contiguous(), w)
+    torch.cuda.synchronize()
+    assert torch.equal(e.view(torch.int16), f.view(torch.int16))
+    # every slot skipped -> exact zeros
+    z = moe.experts_forward(inp["x"], torch.full_like(inp["ids"], -1), torch.full_like(inp["w"], float("nan")), w)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(z.view(torch.int16)).item() == 0
+
+
+def test_forward_empty_and_single_token():
+    wl = W.WORKLOADS["tiny"]
+    inp = W.inputs(wl, DEV)
+    w = _prepare(inp, wl.fmt)
+    out = moe.experts_forward(inp["x"][:0], inp["ids"][:0], inp["w"][:0], w)
+    assert out.shape == (0, wl.H)
+    one = moe.experts_forward(inp["x"][-1:].contiguous(), inp["ids"][-1:].contiguous(), inp["w"][-1:].contiguous(), w)
+    torch.cuda.synchronize()
+    n = {k_: host(v) for k_, v in inp.items()}
+    ref = oracle.forward(wl.fmt, n["w13"], n["s13"], n["w2"], n["s2"], n["x"][-1:], n["ids"][-1:], n["w"][-1:])
+    assert_out_close(host(one), ref, "single token")
+
+
+def test_prepare_weights_nn_layout_matches_nt():
+    wl = _small_workload("nn", FP8, T=96, H=384, I=256, E=3, k=2, seed=21)
+    inp = W.inputs(wl, DEV)
+    w_nt = _prepare(inp, FP8)
+    gate_up_nn = inp["w13"].transpose(1, 2).contiguous()
+    s13_nn = inp["s13"].transpose(1, 2).contiguous()
+    down_nn = inp["w2"].transpose(1, 2).contiguous()
+    s2_nn = inp["s2"].transpose(1, 2).contiguous()
+    w_nn = moe.prepare_weights(gate_up_nn, s13_nn, down_nn, s2_nn, fmt=FP8, transposed=True)
+    a = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w_nt).clone()
+    b = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w_nn)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+FULL = ["qwen3_moe_decode", "mixtral_8x7b", "deepseek_v3"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_forward_parity_full_size_sampled(name):
+    """The full layer on the GPU (the launch configuration the benchmark times);
+    the oracle recomputes a seeded sample of tokens."""
+    wl = W.WORKLOADS[name]
+    say(f"forward full {name}: generating inputs")
+    inp = W.inputs(wl, DEV)
+    tokens = W.sample_tokens(wl.T, 12, wl.seed)
+    say(f"forward full {name}: running GPU + oracle on {tokens.size} tokens")
+    got, ref, _, n, _ = _forward_case(wl, inp, tokens=tokens)
+    assert_out_close(got[tokens], ref[tokens], name)
