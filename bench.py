@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--workload", default="mixtral_8x7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--only", choices=["gate_up", "down"], default=None,
+                    help="time one grouped GEMM alone (for counter runs); prints its own JSON line")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="time a plain device-to-device copy of this many bytes (counter calibration)")
     return ap.parse_args()
 
 
@@ -60,9 +64,11 @@ def main():
     import block_scaled_fp8_sort_amd as moe
     import workloads as W
 
-    wl = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_bytes:
+        return copy_calibration(args, dev)
+    wl = W.WORKLOADS[args.workload]
     log(f"[bench] workload {wl.name}: generating inputs on the GPU")
     inp = W.inputs(wl, dev)
     w = moe.prepare_weights(inp["w13"], inp["s13"], inp["w2"], inp["s2"], fmt=wl.fmt)
@@ -91,6 +97,9 @@ def main():
     def step():
         moe.experts_forward(x, ids, wts, w, swiglu_limit=wl.swiglu_limit, out=out, workspace=ws)
 
+    if args.only:
+        return only_gemm(args, wl, inp, w, dev)
+
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
@@ -111,16 +120,11 @@ def main():
 
     # ---- dominant kernel: gate_up grouped GEMM with the SwiGLU + h-quant epilogue,
     # enqueued through the C ABI in the same configuration as in the forward
-    ss, off, _, _ = moe.route_sort(ids, E, with_slot_pos=False)
-    a_codes, a_scales = moe.quant_act(x, wl.fmt)
-    sdt = torch.float32 if wl.fmt == W.FMT_FP8_B128 else torch.uint8
-    h_codes = torch.empty((S, I), dtype=torch.uint8, device=dev)
-    h_scales = torch.empty((S, I // 128 if wl.fmt == W.FMT_FP8_B128 else I // 32), dtype=sdt, device=dev)
+    ss, off, a_codes, a_scales, h_codes, h_scales = _gemm_inputs(wl, inp, dev)
 
     def l1():
-        moe.grouped_gemm(wl.fmt, a_codes, a_scales, off, inp["w13"], inp["s13"], 2 * I, H, moe.EPI_SWIGLU_QUANT, S,
-                         a_row_index=ss, a_row_divisor=k, h_codes=h_codes, h_scales=h_scales,
-                         swiglu_limit=wl.swiglu_limit)
+        moe.grouped_gemm(w, 0, a_codes, a_scales, T, off, moe.EPI_SWIGLU_QUANT, S, a_row_index=ss, a_row_divisor=k,
+                         h_codes=h_codes, h_scales=h_scales, swiglu_limit=wl.swiglu_limit)
 
     for _ in range(2):
         l1()
@@ -170,6 +174,72 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def _gemm_inputs(wl, inp, dev):
+    import torch
+
+    import block_scaled_fp8_sort_amd as moe
+    import workloads as W
+
+    S, I, H = wl.T * wl.k, wl.I, wl.H
+    ss, off, _, _ = moe.route_sort(inp["ids"], wl.E, with_slot_pos=False)
+    a_codes, a_scales = moe.quant_act(inp["x"], wl.fmt)
+    sdt = torch.float32 if wl.fmt == W.FMT_FP8_B128 else torch.uint8
+    h_codes = torch.zeros((I // 128, S, 128), dtype=torch.uint8, device=dev)
+    h_scales = torch.ones((I // 128 if wl.fmt == W.FMT_FP8_B128 else I // 32, S), dtype=sdt, device=dev)
+    return ss, off, a_codes, a_scales, h_codes, h_scales
+
+
+def only_gemm(args, wl, inp, w, dev):
+    """Time one grouped GEMM alone, as the forward launches it (for counter runs)."""
+    import torch
+
+    import block_scaled_fp8_sort_amd as moe
+
+    S, I, H, k = wl.T * wl.k, wl.I, wl.H, wl.k
+    ss, off, a_codes, a_scales, h_codes, h_scales = _gemm_inputs(wl, inp, dev)
+    slot_out = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
+    if args.only == "gate_up":
+        def run():
+            moe.grouped_gemm(w, 0, a_codes, a_scales, wl.T, off, moe.EPI_SWIGLU_QUANT, S, a_row_index=ss,
+                             a_row_divisor=k, h_codes=h_codes, h_scales=h_scales, swiglu_limit=wl.swiglu_limit)
+    else:
+        def run():
+            moe.grouped_gemm(w, 1, h_codes, h_scales, S, off, moe.EPI_WEIGHTED_SCATTER, S, slot_out=slot_out,
+                             top_k_weights=inp["w"], slot_of_row=ss)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    print(json.dumps({"mode": f"only {args.only}", "workload": wl.name, "ms_per_launch": round(ms, 4)}), flush=True)
+
+
+def copy_calibration(args, dev):
+    """A plain device-to-device copy of known size, for scaling the HBM byte counters."""
+    import torch
+
+    n = args.copy_bytes
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    print(json.dumps({"mode": "copy", "bytes": n, "ms_per_copy": round(ms, 4),
+                      "GB/s (read+write)": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def cpu_baseline(wl, inp, seconds):

@@ -48,9 +48,9 @@ class MoeWeights(ctypes.Structure):
 
 
 class MoeGemmArgs(ctypes.Structure):
-    _fields_ = [("fmt", ctypes.c_int), ("N", _I32), ("K", _I32), ("E", _I32), ("max_rows", _I32),
-                ("a_codes", _P), ("a_scales", _P), ("a_row_index", _P), ("a_row_divisor", _I32),
-                ("expert_offsets", _P), ("b_codes", _P), ("b_scales", _P), ("epilogue", ctypes.c_int),
+    _fields_ = [("weights", ctypes.POINTER(MoeWeights)), ("which", _I32), ("max_rows", _I32),
+                ("a_codes", _P), ("a_scales", _P), ("a_rows", _I32), ("a_row_index", _P), ("a_row_divisor", _I32),
+                ("expert_offsets", _P), ("epilogue", ctypes.c_int),
                 ("c_f32", _P), ("h_codes", _P), ("h_scales", _P), ("has_swiglu_limit", _I32),
                 ("swiglu_limit", _F32), ("slot_out", _P), ("top_k_weights", _P), ("slot_of_row", _P)]
 
@@ -172,12 +172,16 @@ def route_sort(top_k_index: torch.Tensor, num_experts: int, expert_begin: int = 
 
 # -------------------------------------------------------------- quantization
 def quant_act(x: torch.Tensor, fmt: int = FMT_FP8_B128):
-    """Dynamic per-block quantization of bf16 rows: (codes uint8 [rows, H], scales)."""
+    """Dynamic per-block quantization of bf16 rows.
+
+    Returns K-block-major codes uint8 [H/128, rows, 128] and scales [H/128, rows]
+    (fp32, FP8_B128) or [H/32, rows] (uint8, MX).
+    """
     lib = load_library()
     _need(x, "x", torch.bfloat16)
     rows, H = x.shape
-    codes = torch.empty((rows, H), dtype=torch.uint8, device=x.device)
-    scales = torch.empty((rows, _scale_cols(fmt, H)), dtype=_scale_dtype(fmt), device=x.device)
+    codes = torch.empty((H // 128, rows, 128), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((_scale_cols(fmt, H), rows), dtype=_scale_dtype(fmt), device=x.device)
     _check(lib.moe_quant_act(_ptr(x), rows, H, fmt, _ptr(codes), _ptr(scales), _stream(x.device)))
     return codes, scales
 
@@ -208,9 +212,8 @@ class Weights:
 
 
 def prepare_weights(gate_up: torch.Tensor, gate_up_scale: torch.Tensor, down: torch.Tensor,
-                    down_scale: torch.Tensor, fmt: int = FMT_FP8_B128, transposed: bool = False,
-                    copy: bool = False) -> Weights:
-    """One-shot weight preparation (nt tensors are used in place unless copy=True).
+                    down_scale: torch.Tensor, fmt: int = FMT_FP8_B128, transposed: bool = False) -> Weights:
+    """One-shot weight preparation into the library's tiled layout.
 
     FP8_B128: gate_up uint8 [E, 2I, H] (or [E, H, 2I] when transposed), fp32 scales
     per 128x128 block; down uint8 [E, H, I].  MX: int8/uint8 packed e2m1
@@ -232,31 +235,31 @@ def prepare_weights(gate_up: torch.Tensor, gate_up_scale: torch.Tensor, down: to
         H, I2 = gate_up.shape[2] * 2, gate_up.shape[1]
     I = I2 // 2
     desc = MoeWeights()
-    prepared = None
-    nbytes = 0
-    if transposed or copy:
-        nbytes = lib.moe_prepared_weights_size(fmt, E, H, I)
-        prepared = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    nbytes = lib.moe_prepared_weights_size(fmt, E, H, I)
+    prepared = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     _check(lib.moe_prepare_weights(fmt, LAYOUT_NN if transposed else LAYOUT_NT, E, H, I, _ptr(gate_up),
                                    _ptr(gate_up_scale), _ptr(down), _ptr(down_scale), _ptr(prepared), nbytes,
                                    ctypes.byref(desc), _stream(dev)))
-    keep = (prepared,) if prepared is not None else (gate_up, gate_up_scale, down, down_scale)
-    return Weights(desc, keep)
+    return Weights(desc, (prepared,))
 
 
 # -------------------------------------------------------------- grouped GEMM
-def grouped_gemm(fmt: int, a_codes, a_scales, expert_offsets, b_codes, b_scales, N: int, K: int, epilogue: int,
+def grouped_gemm(weights: Weights, which: int, a_codes, a_scales, a_rows: int, expert_offsets, epilogue: int,
                  max_rows: int, a_row_index=None, a_row_divisor: int = 1, c_f32=None, h_codes=None, h_scales=None,
                  swiglu_limit: Optional[float] = None, slot_out=None, top_k_weights=None, slot_of_row=None):
-    """Enqueue one grouped GEMM (see moe_grouped_gemm); outputs are caller tensors."""
+    """Enqueue one grouped GEMM (see moe_grouped_gemm); outputs are caller tensors.
+
+    which = 0 multiplies by the gate_up weight, 1 by the down weight.  A is
+    K-block-major with a_rows rows per plane.
+    """
     lib = load_library()
     a = MoeGemmArgs()
-    a.fmt = fmt
-    a.N, a.K, a.E, a.max_rows = N, K, expert_offsets.numel() - 1, max_rows
-    a.a_codes, a.a_scales = _ptr(a_codes), _ptr(a_scales)
+    a.weights = ctypes.pointer(weights.desc)
+    a.which = which
+    a.max_rows = max_rows
+    a.a_codes, a.a_scales, a.a_rows = _ptr(a_codes), _ptr(a_scales), a_rows
     a.a_row_index, a.a_row_divisor = _ptr(a_row_index), a_row_divisor
     a.expert_offsets = _ptr(expert_offsets)
-    a.b_codes, a.b_scales = _ptr(b_codes), _ptr(b_scales)
     a.epilogue = epilogue
     a.c_f32, a.h_codes, a.h_scales = _ptr(c_f32), _ptr(h_codes), _ptr(h_scales)
     a.has_swiglu_limit = 0 if swiglu_limit is None else 1
@@ -327,8 +330,8 @@ def experts_forward(hidden_states: torch.Tensor, top_k_index: torch.Tensor, top_
         S = T * k
         debug["sorted_slot"] = torch.empty(S, dtype=torch.int32, device=dev)
         debug["expert_offsets"] = torch.empty(weights.E + 1, dtype=torch.int32, device=dev)
-        debug["act_codes"] = torch.empty((T, H), dtype=torch.uint8, device=dev)
-        debug["act_scales"] = torch.empty((T, _scale_cols(weights.fmt, H)), dtype=_scale_dtype(weights.fmt),
+        debug["act_codes"] = torch.empty((H // 128, T, 128), dtype=torch.uint8, device=dev)
+        debug["act_scales"] = torch.empty((_scale_cols(weights.fmt, H), T), dtype=_scale_dtype(weights.fmt),
                                           device=dev)
         dbg = MoeDebug(_ptr(debug["sorted_slot"]), _ptr(debug["expert_offsets"]), _ptr(debug["act_codes"]),
                        _ptr(debug["act_scales"]))

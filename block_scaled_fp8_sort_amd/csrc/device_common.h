@@ -69,6 +69,20 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
       : "v"(g), "s"(lds)
       : "memory");
 }
+// The same 16-byte DMA with a wave-uniform 64-bit base in SGPRs and a 32-bit
+// per-lane byte offset (the saddr form): no per-lane 64-bit address math.
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory");
+}
 __device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds) {
   uint32_t saved;
   asm volatile(

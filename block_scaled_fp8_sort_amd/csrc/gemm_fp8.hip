@@ -17,26 +17,26 @@
 //    one value per 16-row sub-tile.
 //  * fp32 block scales cannot ride the MFMA's E8M0 scale operands, so each
 //    128-wide K block is one MFMA with a zero accumulator (the block's partial
-//    sum P of code products, exact products and fp32 sums) followed by
-//    acc += P * (s_act * s_w) on the VALU (one FMA per output per K block).
-//  * Workgroup tile 256 (n) x BM (tokens) x 128 (K), four waves as 2 x 2, each
-//    128 n x BM/2 tokens.  Operands move global -> LDS by LDS-DMA
-//    (global_load_lds_dwordx4): every lane supplies its own global address, so
-//    the row gather costs nothing; the LDS row layout swizzles 16-byte chunks by
-//    (row >> 1) & 7, which keeps the MFMA fragment reads free of bank conflicts.
-//    Three stages are in flight.
+//    sum of code products) followed by acc += P * (s_act * s_w) on the VALU.
+//    The MFMAs of one n sub-tile and the FMAs of the previous one are
+//    interleaved in program order, so the matrix core and the VALU overlap.
+//  * Workgroup tile 256 (n) x BM (tokens) x 128 (K), eight waves as 2 (n) x 4
+//    (tokens), two per SIMD, each 128 n x BM/4 tokens.  Two LDS stages.
+//  * Operands move global -> LDS by LDS-DMA (global_load_lds_dwordx4, 16 bytes
+//    per lane).  Weights are pre-tiled (tile_layout.h) so each DMA instruction
+//    copies one contiguous 1 KB; activations are stored K-block-major
+//    ([K/128][rows][128 bytes]), so a DMA instruction gathers 8 token rows'
+//    128-byte chunks by per-lane address (the gather is free) without the
+//    same-L2-channel aliasing that 4 KB-strided rows suffer.
 //  * Persistent grid: each workgroup reads the expert offsets, builds the tile
 //    table (experts x n-tiles x m-tiles, m fastest) in LDS, and walks tiles
 //    with a stride of the grid size.  Workgroup ids are remapped so that
 //    consecutive tiles land on the same XCD (dispatch is round-robin over the
 //    8 XCDs), which keeps a weight tile shared by an expert's m-tiles in that
 //    XCD's L2.  Partial m-tiles are masked; no host-visible counts are needed.
-//  * Paired mode (gate_up weight): the 256 rows of an n-tile are 128 gate rows
-//    and the 128 matching up rows, interleaved 16 at a time, so the SwiGLU
-//    epilogue finds g and u of the same output in the same lane, and one tile
-//    owns a whole 128-wide block of h for its quantization.
 #include "device_common.h"
 #include "internal.h"
+#include "tile_layout.h"
 
 namespace moe {
 
@@ -45,24 +45,22 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int BN = 256;
-constexpr int BK = 128;
-constexpr int kThreads = 256;
-constexpr int kStages = 3;
+constexpr int BN = kTileN;
+constexpr int BK = kBlockK;
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
 constexpr int kMaxE = 512;
 
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
-
-// One pipeline stage in LDS: 256 weight rows and BM activation rows of one
-// 128-byte K block, and the activation scales of that block (one 256-byte DMA
-// per wave; wave w's first BM/4 entries are rows [w*BM/4, (w+1)*BM/4)).  Each
-// stage is its own __shared__ object so the compiler can tell a DMA into one
-// stage from the fragment reads of another and does not wait on it.
+// One pipeline stage in LDS: the 256 weight rows and BM activation rows of one
+// 128-wide K block, and the scales of that block (one 256-byte DMA per wave:
+// slots [0, BM) are the activation scales in the order the MFMA lanes read
+// them, slots BM and BM + 1 the two weight-block scales).  Each stage is its
+// own __shared__ object.
 template <int BM>
 struct StageBuf {
   uint8_t w[BN * BK];
   uint8_t a[BM * BK];
-  float s[4 * 64];
+  float s[kWaves * 64];
 };
 
 // Tile table and epilogue exchange.
@@ -74,19 +72,6 @@ struct Misc {
   float amax[2][BM];
 };
 
-// Row of B (within the expert) held by tile row tr of n-tile nt.
-template <bool PAIRED>
-__device__ __forceinline__ int b_row(int nt, int tr, int N) {
-  if constexpr (PAIRED) {
-    const int I = N / 2;
-    const int p = tr >> 5, within = tr & 31;
-    const int h = nt * 128 + 16 * p + (within & 15);
-    return within < 16 ? h : I + h;
-  } else {
-    return min(nt * BN + tr, N - 1);
-  }
-}
-
 // 32 bytes of K (logical chunks 2g and 2g+1 of the 128-byte row) of LDS row tr.
 __device__ __forceinline__ v8i lds_frag(const uint8_t* region, int tr, int g) {
   const int s = swz(tr);
@@ -96,55 +81,54 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* region, int tr, int g) {
 }
 
 // Barrier without a memory fence: the waits before it are explicit (vmcnt for
-// the DMAs this wave issued, lgkmcnt for its LDS writes); the empty asm
-// statements keep the compiler from moving LDS accesses across it.
+// the DMAs this wave issued); the empty asm statements keep the compiler from
+// moving LDS accesses across it.
 __device__ __forceinline__ void raw_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// Per-lane DMA sources of one tile (fixed for the tile; K advances by 128
-// bytes of codes and one float of scales per block).
+// Per-lane DMA sources of one tile.
 template <int BM>
 struct TileSrc {
-  static constexpr int A_LOADS = BM / 32;
-  const uint8_t* wbase;
-  uint32_t w_off[8];
-  const uint8_t* a_src[A_LOADS];
-  const float* s_src;
+  static constexpr int A_LOADS = BM / 64;  // 1 KB activation DMAs per wave per stage
+  const uint8_t* w_tile;   // tiled weights of (expert, n-tile), K block 0 (uniform)
+  const uint8_t* a_codes;  // activation planes (uniform)
+  size_t a_plane;          // bytes of one 128-wide K plane of activation codes
+  uint32_t a_off[A_LOADS]; // per-lane byte offset of the gathered row chunk
+  const float* s_base;     // per-lane scale address of K block 0
+  uint32_t s_stride;       // per-lane scale advance per K block, in floats
 };
 
 template <int BM>
-__device__ __forceinline__ void issue_stage(StageBuf<BM>* st, const TileSrc<BM>& src, int kb, int wave) {
-  // wave-uniform LDS destinations, held in SGPRs
+__device__ __forceinline__ void issue_stage(StageBuf<BM>* st, const TileSrc<BM>& src, int kb, int wave, int lane) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(st));
-  const uint32_t wofs = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t w = __builtin_amdgcn_readfirstlane(wave);
+  // weights: wave w copies the 4 KB of tile rows [32 w, 32 w + 32), contiguous
+  const uint8_t* wsrc = src.w_tile + (size_t)kb * (BN * BK) + w * 4096;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) lds_dma16(src.wbase + src.w_off[q] + (size_t)kb * BK, base + (64 * wofs + 8 * q) * BK);
+  for (int q = 0; q < 4; ++q) lds_dma16_s(wsrc + q * 1024, lane * 16, base + w * 4096 + q * 1024);
+  // activations: wave w gathers rows [w BM/8, (w+1) BM/8) of the tile
+  const uint8_t* plane = src.a_codes + (size_t)kb * src.a_plane;
 #pragma unroll
   for (int q = 0; q < TileSrc<BM>::A_LOADS; ++q)
-    lds_dma16(src.a_src[q] + (size_t)kb * BK, base + BN * BK + (wofs * (BM / 4) + 8 * q) * BK);
-  lds_dma4(src.s_src + kb, base + (BN + BM) * BK + wofs * 256);
+    lds_dma16_s(plane, src.a_off[q], base + BN * BK + (w * (BM / 8) + 8 * q) * BK);
+  lds_dma4(src.s_base + (size_t)kb * src.s_stride, base + (BN + BM) * BK + w * 256);
 }
 
-// One K block: wait for stage `cur`, start the DMA of block kb + 2 into `nxt`
+// One K block: wait for stage `cur`, start the DMA of block kb + 1 into `nxt`
 // (the stage block kb - 1 used), then accumulate the block from `cur`.
 template <int BM, bool PAIRED>
-__device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nxt,
-                                       const TileSrc<BM>& src, int kb, int KB, int wave, int lane,
-                                       v4f (&acc)[8][BM / 32]) {
-  constexpr int WM = BM / 2;
+__device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nxt, const TileSrc<BM>& src, int kb,
+                                       int KB, int wave, int lane, v4f (&acc)[8][BM / 64]) {
+  constexpr int WM = BM / 4;
   constexpr int TS = WM / 16;
-  constexpr int LOADS = 8 + BM / 32 + 1;
   const int wn = wave & 1, wt = wave >> 1;
   const int g = lane >> 4, l16 = lane & 15;
-  // Stage kb is the oldest of the two stages in flight.  Past the last block the
-  // DMA repeats block KB - 1 into a stage nobody reads, which keeps the number of
-  // DMAs in flight, and so this wait, the same on every step.
-  wait_vmcnt<LOADS>();
-  raw_barrier();
-  issue_stage<BM>(nxt, src, min(kb + 2, KB - 1), wave);
+  wait_vmcnt<0>();  // this wave's DMAs of stage kb have landed
+  raw_barrier();    // ... and every other wave's; all waves are done with block kb - 1
+  if (kb + 1 < KB) issue_stage<BM>(nxt, src, kb + 1, wave, lane);
   const float swg = cur->s[PAIRED ? BM : BM + wn];
   const float swu = cur->s[BM + 1];
   typedef float vts __attribute__((ext_vector_type(TS)));
@@ -152,16 +136,33 @@ __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nx
   v8i bf[TS];
 #pragma unroll
   for (int ti = 0; ti < TS; ++ti) bf[ti] = lds_frag(cur->a, wt * WM + ti * 16 + l16, g);
+  float fg[TS], fu[TS];
 #pragma unroll
-  for (int ni = 0; ni < 8; ++ni) {
-    const v8i af = lds_frag(cur->w, wn * 128 + ni * 16 + l16, g);
-    const float swn = (PAIRED && (ni & 1)) ? swu : swg;
+  for (int ti = 0; ti < TS; ++ti) {
+    fg[ti] = sav[ti] * swg;
+    fu[ti] = sav[ti] * swu;
+  }
+  // Software pipeline over the 8 n sub-tiles: the MFMAs of sub-tile ni write
+  // one set of partial registers while the FMAs fold the other set (sub-tile
+  // ni - 1) into the accumulators, and the weight fragment of sub-tile ni + 1 is
+  // read from LDS meanwhile.  sched_barrier(0) keeps this program order.
+  v4f part[2][TS];
+  v8i af = lds_frag(cur->w, wn * 128 + l16, g);
+#pragma unroll
+  for (int ni = 0; ni <= 8; ++ni) {
+    v8i af_next = af;
+    if (ni < 7) af_next = lds_frag(cur->w, wn * 128 + (ni + 1) * 16 + l16, g);
+    const int pn = ni - 1;
+    const bool up = PAIRED && (pn & 1);
 #pragma unroll
     for (int ti = 0; ti < TS; ++ti) {
-      const v4f part =
-          __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[ti], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-      acc[ni][ti] += part * (sav[ti] * swn);
+      if (ni < 8)
+        part[ni & 1][ti] =
+            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[ti], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+      if (ni > 0) acc[pn][ti] += part[pn & 1][ti] * (up ? fu[ti] : fg[ti]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    af = af_next;
   }
 }
 
@@ -169,14 +170,10 @@ template <int BM, int EPI, bool PAIRED>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) StageBuf<BM> st0;
   __shared__ __attribute__((aligned(16))) StageBuf<BM> st1;
-  __shared__ __attribute__((aligned(16))) StageBuf<BM> st2;
   __shared__ __attribute__((aligned(16))) Misc<BM> misc;
-  constexpr int WM = BM / 2;        // tokens per wave
-  constexpr int TS = WM / 16;       // 16-token sub-tiles per wave
-  constexpr int RPW = BM / 4;       // activation rows loaded per wave per stage
-  constexpr int A_LOADS = RPW / 8;  // 1-KB DMAs of activation rows per wave per stage
-  constexpr int W_LOADS = 8;        // 1-KB DMAs of weight rows per wave per stage
-  static_assert(A_LOADS >= 1 && BM + 2 <= 256, "32 <= BM <= 248");
+  constexpr int WM = BM / 4;   // tokens per wave
+  constexpr int TS = WM / 16;  // 16-token sub-tiles per wave
+  static_assert(TS >= 1 && BM + 2 <= kWaves * 64, "64 <= BM <= 256");
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wn = wave & 1, wt = wave >> 1;
@@ -217,14 +214,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p
   const int vb = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
 
   for (int t = vb; t < total; t += G) {
-    // ---- locate the tile: the last expert e with tp[e] <= t
+    // ---- locate the tile: the last expert e with tp[e] <= t (every lane agrees:
+    // make the values scalar)
     int lo = 0, hi = E;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (misc.tp[mid] <= t) lo = mid; else hi = mid;
     }
-    // every lane computed the same values: make them scalar (SGPR) so the
-    // weight-scale reads below are scalar loads
     const int e = __builtin_amdgcn_readfirstlane(lo);
     const int m_begin = __builtin_amdgcn_readfirstlane(misc.off[e]);
     const int m_end = __builtin_amdgcn_readfirstlane(misc.off[e + 1]);
@@ -235,40 +231,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p
 
     // ---- per-lane DMA sources
     TileSrc<BM> src;
-    src.wbase = p.b_codes + (size_t)e * N * K;
+    src.w_tile = p.b_codes + ((size_t)e * NT + n_tile) * (size_t)KB * (BN * BK);
+    src.a_codes = p.a_codes;
+    src.a_plane = (size_t)p.a_rows * BK;
 #pragma unroll
-    for (int q = 0; q < W_LOADS; ++q) {
-      const int tr = 64 * wave + 8 * q + (lane >> 3);
-      src.w_off[q] = (uint32_t)b_row<PAIRED>(n_tile, tr, N) * (uint32_t)K + (uint32_t)(((lane & 7) ^ swz(tr)) << 4);
-    }
-#pragma unroll
-    for (int q = 0; q < A_LOADS; ++q) {
-      const int tr = wave * RPW + 8 * q + (lane >> 3);
+    for (int q = 0; q < TileSrc<BM>::A_LOADS; ++q) {
+      const int tr = wave * (BM / 8) + 8 * q + (lane >> 3);
       const int r = min(m0 + tr, m_end - 1);
       const int arow = p.a_row_index ? p.a_row_index[r] / p.a_row_div : r;
-      src.a_src[q] = p.a_codes + (size_t)arow * K + (((lane & 7) ^ swz(tr)) << 4);
+      src.a_off[q] = (uint32_t)arow * BK + (uint32_t)(((lane & 7) ^ swz(tr)) << 4);
     }
-    // Scale DMA, 4 bytes per lane, lane L of wave w filling scale slot
-    // p = 64 w + L of the stage.  Slots [0, BM) hold the activation scales in
-    // the order the MFMA lanes read them (slot (wt*16 + l16) * TS + ti is token
-    // row wt*WM + ti*16 + l16), so each lane reads its TS scales with one LDS
-    // load.  Slots BM and BM + 1 hold the two weight-block scales of the tile
-    // (gate and up blocks when paired, the blocks of the two n-halves
-    // otherwise).  The remaining lanes repeat slot 0.
     {
       const int slot = 64 * wave + lane;
       if (slot == BM || slot == BM + 1) {
         int nb;
         if constexpr (PAIRED) nb = slot == BM ? n_tile : I / 128 + n_tile;
         else nb = min(n_tile * 2 + (slot - BM), NB - 1);
-        src.s_src = bsc + ((size_t)e * NB + nb) * KB;
+        src.s_base = bsc + ((size_t)e * NB + nb) * KB;
+        src.s_stride = 1;
       } else {
         const int q = slot < BM ? slot / TS : 0;
         const int ti = slot < BM ? slot % TS : 0;
         const int tr = (q / 16) * WM + ti * 16 + (q % 16);
         const int r = min(m0 + tr, m_end - 1);
         const int arow = p.a_row_index ? p.a_row_index[r] / p.a_row_div : r;
-        src.s_src = (const float*)p.a_scales + (size_t)arow * KB;
+        src.s_base = (const float*)p.a_scales + arow;
+        src.s_stride = (uint32_t)p.a_rows;
       }
     }
 
@@ -279,14 +267,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p
       for (int ti = 0; ti < TS; ++ti) acc[ni][ti] = v4f{0.f, 0.f, 0.f, 0.f};
 
     __syncthreads();  // the previous tile's LDS readers are done
-    issue_stage<BM>(&st0, src, 0, wave);
-    issue_stage<BM>(&st1, src, min(1, KB - 1), wave);
-    for (int kb = 0; kb < KB; kb += 3) {
-      k_step<BM, PAIRED>(&st0, &st2, src, kb, KB, wave, lane, acc);
+    issue_stage<BM>(&st0, src, 0, wave, lane);
+    for (int kb = 0; kb < KB; kb += 2) {
+      k_step<BM, PAIRED>(&st0, &st1, src, kb, KB, wave, lane, acc);
       if (kb + 1 < KB) k_step<BM, PAIRED>(&st1, &st0, src, kb + 1, KB, wave, lane, acc);
-      if (kb + 2 < KB) k_step<BM, PAIRED>(&st2, &st1, src, kb + 2, KB, wave, lane, acc);
     }
-    wait_vmcnt<0>();  // the trailing repeat DMAs land before the stages are reused
 
     // ---- epilogues
     if constexpr (EPI == kEpiStoreF32) {
@@ -310,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p
     } else if constexpr (EPI == kEpiSwiGLUQuant) {
       static_assert(PAIRED, "SwiGLU needs the paired gate/up layout");
       // h of pair q, sub-tile ti, element i (recomputed in the second pass
-      // instead of being held across the barrier).
+      // instead of being held across the barrier)
       auto hval = [&](int q, int ti, int i) {
         float gv = acc[2 * q][ti][i];
         float uv = acc[2 * q + 1][ti][i];
@@ -332,6 +317,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p
         if (g == 0) misc.amax[wn][wt * WM + ti * 16 + l16] = m;
       }
       __syncthreads();
+      // h codes go to the K-block-major layout [I/128][max_rows][128] that the
+      // down GEMM reads; the tile's 128 outputs are exactly plane n_tile
+      uint8_t* plane = p.h_codes + (size_t)n_tile * p.max_rows * 128;
 #pragma unroll
       for (int ti = 0; ti < TS; ++ti) {
         const int tt = wt * WM + ti * 16 + l16;
@@ -344,9 +332,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p
           for (int q = 0; q < 4; ++q) {
             const uint32_t code =
                 e4m3x4(hval(q, ti, 0) * inv, hval(q, ti, 1) * inv, hval(q, ti, 2) * inv, hval(q, ti, 3) * inv);
-            *(uint32_t*)(p.h_codes + (size_t)r * I + n_tile * 128 + 16 * (wn * 4 + q) + 4 * g) = code;
+            *(uint32_t*)(plane + (size_t)r * 128 + 16 * (wn * 4 + q) + 4 * g) = code;
           }
-          if (wn == 0 && g == 0) ((float*)p.h_scales)[(size_t)r * (I / 128) + n_tile] = s;
+          if (wn == 0 && g == 0) ((float*)p.h_scales)[(size_t)n_tile * p.max_rows + r] = s;
         }
       }
     } else {  // kEpiWeightedScatter
@@ -397,9 +385,9 @@ hipError_t dispatch_epi(const GemmParams& p, int epi, bool paired, int num_cus, 
 
 hipError_t launch_gemm_fp8_b128(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream) {
   const long avg_rows = p.E > 0 ? (long)p.max_rows / p.E : p.max_rows;
+  if (avg_rows >= 192) return dispatch_epi<256>(p, epi, paired, num_cus, stream);
   if (avg_rows >= 96) return dispatch_epi<128>(p, epi, paired, num_cus, stream);
-  if (avg_rows >= 48) return dispatch_epi<64>(p, epi, paired, num_cus, stream);
-  return dispatch_epi<32>(p, epi, paired, num_cus, stream);
+  return dispatch_epi<64>(p, epi, paired, num_cus, stream);
 }
 
 }  // namespace moe

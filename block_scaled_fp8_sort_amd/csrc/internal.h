@@ -12,10 +12,11 @@ struct GemmParams {
   const void* a_scales;
   const int32_t* a_row_index;
   int32_t a_row_div;
+  int32_t a_rows;  // rows of each K-block plane of A ([K/128][a_rows][128] codes, [K/128][a_rows] scales)
   const int32_t* offsets;
   int32_t E;
-  const uint8_t* b_codes;
-  const void* b_scales;
+  const uint8_t* b_codes;  // tiled weight codes (tile_layout.h)
+  const void* b_scales;     // weight scales, [E][N/128][K/128]
   int32_t N;  // rows of B per expert
   int32_t K;
   int32_t max_rows;
@@ -43,6 +44,10 @@ hipError_t launch_gemm_fp8_b128(const GemmParams& p, int epi, bool paired, int n
 hipError_t launch_gemm_mx(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream);
 hipError_t launch_combine(const uint16_t* slot_out, const int32_t* ids, int32_t T, int32_t k, int32_t H, int32_t E,
                           int32_t expert_begin, uint16_t* out, hipStream_t stream);
+// Tile one weight [E, N, K] (nt, or nn = [E, K, N] when `nn`) into the layout
+// of tile_layout.h; `paired` selects the gate/up pairing (N = 2I).
+hipError_t launch_tile_weight_fp8(const uint8_t* src, bool nn, bool paired, int32_t E, int32_t N, int32_t K,
+                                  uint8_t* dst, hipStream_t stream);
 hipError_t launch_transpose_u8(const uint8_t* in, uint8_t* out, int32_t batch, int32_t rows, int32_t cols,
                                hipStream_t stream);
 hipError_t launch_transpose_f32(const float* in, float* out, int32_t batch, int32_t rows, int32_t cols,

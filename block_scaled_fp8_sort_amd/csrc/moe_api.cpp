@@ -144,22 +144,21 @@ moe_status validate_weights(const moe_weights* w) {
 
 moe_status validate_gemm(const moe_gemm_args* a) {
   if (!a) return fail(MOE_ERR_NULL, "gemm args are NULL");
-  if (!valid_fmt(a->fmt)) return fail(MOE_ERR_UNSUPPORTED, "unknown format %d", (int)a->fmt);
-  if (a->E < 1 || a->E > kMaxE) return fail(MOE_ERR_SHAPE, "E=%d outside [1, %d]", a->E, kMaxE);
-  if (a->K <= 0 || a->K % 128) return fail(MOE_ERR_SHAPE, "K=%d must be a positive multiple of 128", a->K);
-  if (a->N <= 0 || a->N % 128) return fail(MOE_ERR_SHAPE, "N=%d must be a positive multiple of 128", a->N);
-  if (a->epilogue == MOE_EPI_SWIGLU_QUANT && a->N % 256)
-    return fail(MOE_ERR_SHAPE, "SwiGLU epilogue needs N = 2I with I a multiple of 128 (N=%d)", a->N);
+  moe_status st = validate_weights(a->weights);
+  if (st != MOE_OK) return st;
+  if (a->which != 0 && a->which != 1) return fail(MOE_ERR_UNSUPPORTED, "which=%d is neither 0 (gate_up) nor 1 (down)", a->which);
   if (a->max_rows < 0) return fail(MOE_ERR_SHAPE, "max_rows=%d", a->max_rows);
-  if ((int64_t)a->N * a->K >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "N*K must stay below 2^31");
+  if (a->a_rows < 0 || (int64_t)a->a_rows * 128 >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "a_rows=%d", a->a_rows);
+  if (!a->a_row_index && a->a_rows < a->max_rows)
+    return fail(MOE_ERR_SHAPE, "without a row index A needs max_rows=%d rows, has %d", a->max_rows, a->a_rows);
   if (a->a_row_index && a->a_row_divisor < 1) return fail(MOE_ERR_SHAPE, "a_row_divisor must be >= 1");
-  if (!a->a_codes || !a->a_scales || !a->expert_offsets || !a->b_codes || !a->b_scales)
-    return fail(MOE_ERR_NULL, "an operand pointer is NULL");
+  if (!a->a_codes || !a->a_scales || !a->expert_offsets) return fail(MOE_ERR_NULL, "an operand pointer is NULL");
   switch (a->epilogue) {
     case MOE_EPI_STORE_F32:
       if (!a->c_f32) return fail(MOE_ERR_NULL, "c_f32 is NULL");
       break;
     case MOE_EPI_SWIGLU_QUANT:
+      if (a->which != 0) return fail(MOE_ERR_UNSUPPORTED, "the SwiGLU epilogue runs on the gate_up weight (which = 0)");
       if (!a->h_codes || !a->h_scales) return fail(MOE_ERR_NULL, "h_codes / h_scales are NULL");
       if (a->has_swiglu_limit && !(std::isfinite(a->swiglu_limit) && a->swiglu_limit > 0.0f))
         return fail(MOE_ERR_SHAPE, "swiglu_limit must be finite and > 0");
@@ -175,17 +174,19 @@ moe_status validate_gemm(const moe_gemm_args* a) {
 }
 
 moe::GemmParams to_params(const moe_gemm_args* a) {
-  moe::GemmParams p;
+  const moe_weights* w = a->weights;
+  moe::GemmParams p{};
   p.a_codes = a->a_codes;
   p.a_scales = a->a_scales;
   p.a_row_index = a->a_row_index;
   p.a_row_div = a->a_row_index ? a->a_row_divisor : 1;
+  p.a_rows = a->a_rows;
   p.offsets = a->expert_offsets;
-  p.E = a->E;
-  p.b_codes = a->b_codes;
-  p.b_scales = a->b_scales;
-  p.N = a->N;
-  p.K = a->K;
+  p.E = w->E;
+  p.b_codes = a->which == 0 ? w->w13 : w->w2;
+  p.b_scales = a->which == 0 ? w->w13_scale : w->w2_scale;
+  p.N = a->which == 0 ? 2 * w->I : w->H;
+  p.K = a->which == 0 ? w->H : w->I;
   p.max_rows = a->max_rows;
   p.c_f32 = a->c_f32;
   p.h_codes = a->h_codes;
@@ -279,9 +280,11 @@ size_t moe_prepared_weights_size(moe_format fmt, int32_t E, int32_t H, int32_t I
   if (!valid_fmt(fmt) || E < 1 || H <= 0 || I <= 0 || H % 128 || I % 128) return 0;
   const size_t A = 256;
   const size_t e = (size_t)E, h = (size_t)H, i = (size_t)I;
-  if (fmt == MOE_FMT_FP8_B128)
-    return align_up(e * 2 * i * h, A) + align_up(4 * e * (2 * i / 128) * (h / 128), A) + align_up(e * h * i, A) +
-           align_up(4 * e * (h / 128) * (i / 128), A);
+  if (fmt == MOE_FMT_FP8_B128) {
+    const size_t nt2 = (h + 255) / 256;
+    return align_up(e * 2 * i * h, A) + align_up(4 * e * (2 * i / 128) * (h / 128), A) +
+           align_up(e * nt2 * 256 * i, A) + align_up(4 * e * (h / 128) * (i / 128), A);
+  }
   return align_up(e * 2 * i * h / 2, A) + align_up(e * 2 * i * (h / 32), A) + align_up(e * h * i / 2, A) +
          align_up(e * h * (i / 32), A);
 }
@@ -296,27 +299,14 @@ moe_status moe_prepare_weights(moe_format fmt, moe_layout layout, int32_t E, int
   if (E < 1 || E > kMaxE) return fail(MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, kMaxE);
   if (H <= 0 || I <= 0 || H % 128 || I % 128)
     return fail(MOE_ERR_SHAPE, "H=%d and I=%d must be positive multiples of 128", H, I);
+  if ((int64_t)2 * I * H >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "one expert's weight must stay below 2^31");
   if (!gate_up || !gate_up_scale || !down || !down_scale) return fail(MOE_ERR_NULL, "a weight pointer is NULL");
   if (layout == MOE_LAYOUT_NN && fmt != MOE_FMT_FP8_B128)
     return fail(MOE_ERR_UNSUPPORTED, "the nn layout is accepted for FP8_B128 weights only");
+  if (!prepared) return fail(MOE_ERR_NULL, "prepared buffer is NULL");
   const size_t need = moe_prepared_weights_size(fmt, E, H, I);
-  if ((layout == MOE_LAYOUT_NN || prepared) && prepared_bytes < need)
+  if (prepared_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "prepared buffer holds %zu bytes, %zu needed", prepared_bytes, need);
-  if (layout == MOE_LAYOUT_NN && !prepared) return fail(MOE_ERR_NULL, "the nn layout needs a prepared buffer");
-
-  moe_weights w;
-  w.fmt = fmt;
-  w.E = E;
-  w.H = H;
-  w.I = I;
-  if (layout == MOE_LAYOUT_NT && !prepared) {
-    w.w13 = (const uint8_t*)gate_up;
-    w.w13_scale = gate_up_scale;
-    w.w2 = (const uint8_t*)down;
-    w.w2_scale = down_scale;
-    *out = w;
-    return ok();
-  }
   int dev, cus;
   moe_status st = check_device(stream, &dev, &cus);
   if (st != MOE_OK) return st;
@@ -325,31 +315,42 @@ moe_status moe_prepare_weights(moe_format fmt, moe_layout layout, int32_t E, int
   const bool mx = fmt == MOE_FMT_MXFP8A_MXFP4W;
   const size_t b13 = mx ? e * 2 * i * h / 2 : e * 2 * i * h;
   const size_t b13s = mx ? e * 2 * i * (h / 32) : 4 * e * (2 * i / 128) * (h / 128);
-  const size_t b2 = mx ? e * h * i / 2 : e * h * i;
-  uint8_t* base = (uint8_t*)prepared;
-  uint8_t* p13 = base;
+  const size_t b2 = mx ? e * h * i / 2 : e * ((h + 255) / 256) * 256 * i;
+  const size_t b2s = mx ? e * h * (i / 32) : 4 * e * (h / 128) * (i / 128);
+  uint8_t* p13 = (uint8_t*)prepared;
   uint8_t* p13s = p13 + align_up(b13, A);
   uint8_t* p2 = p13s + align_up(b13s, A);
   uint8_t* p2s = p2 + align_up(b2, A);
-  const size_t b2s = mx ? e * h * (i / 32) : 4 * e * (h / 128) * (i / 128);
-  hipError_t he;
-  if (layout == MOE_LAYOUT_NT) {
+  hipError_t he = hipSuccess;
+  if (mx) {
     if ((he = hipMemcpyAsync(p13, gate_up, b13, hipMemcpyDeviceToDevice, stream)) != hipSuccess ||
         (he = hipMemcpyAsync(p13s, gate_up_scale, b13s, hipMemcpyDeviceToDevice, stream)) != hipSuccess ||
         (he = hipMemcpyAsync(p2, down, b2, hipMemcpyDeviceToDevice, stream)) != hipSuccess ||
         (he = hipMemcpyAsync(p2s, down_scale, b2s, hipMemcpyDeviceToDevice, stream)) != hipSuccess)
       return hip_status(he, "weight copy");
   } else {
-    // nn: gate_up [E, H, 2I] -> [E, 2I, H]; scales [E, H/128, 2I/128] -> [E, 2I/128, H/128];
-    //     down [E, I, H] -> [E, H, I]; scales [E, I/128, H/128] -> [E, H/128, I/128]
-    if ((he = moe::launch_transpose_u8((const uint8_t*)gate_up, p13, E, H, 2 * I, stream)) != hipSuccess ||
-        (he = moe::launch_transpose_f32((const float*)gate_up_scale, (float*)p13s, E, H / 128, 2 * I / 128,
-                                        stream)) != hipSuccess ||
-        (he = moe::launch_transpose_u8((const uint8_t*)down, p2, E, I, H, stream)) != hipSuccess ||
-        (he = moe::launch_transpose_f32((const float*)down_scale, (float*)p2s, E, I / 128, H / 128, stream)) !=
-            hipSuccess)
-      return hip_status(he, "weight transpose");
+    const bool nn = layout == MOE_LAYOUT_NN;
+    if ((he = moe::launch_tile_weight_fp8((const uint8_t*)gate_up, nn, true, E, 2 * I, H, p13, stream)) != hipSuccess ||
+        (he = moe::launch_tile_weight_fp8((const uint8_t*)down, nn, false, E, H, I, p2, stream)) != hipSuccess)
+      return hip_status(he, "weight tiling");
+    if (!nn) {
+      if ((he = hipMemcpyAsync(p13s, gate_up_scale, b13s, hipMemcpyDeviceToDevice, stream)) != hipSuccess ||
+          (he = hipMemcpyAsync(p2s, down_scale, b2s, hipMemcpyDeviceToDevice, stream)) != hipSuccess)
+        return hip_status(he, "scale copy");
+    } else {
+      // scales [E, H/128, 2I/128] -> [E, 2I/128, H/128] and [E, I/128, H/128] -> [E, H/128, I/128]
+      if ((he = moe::launch_transpose_f32((const float*)gate_up_scale, (float*)p13s, E, H / 128, 2 * I / 128,
+                                          stream)) != hipSuccess ||
+          (he = moe::launch_transpose_f32((const float*)down_scale, (float*)p2s, E, I / 128, H / 128, stream)) !=
+              hipSuccess)
+        return hip_status(he, "scale transpose");
+    }
   }
+  moe_weights w;
+  w.fmt = fmt;
+  w.E = E;
+  w.H = H;
+  w.I = I;
   w.w13 = p13;
   w.w13_scale = p13s;
   w.w2 = p2;
@@ -365,11 +366,12 @@ moe_status moe_grouped_gemm(const moe_gemm_args* args, hipStream_t stream) {
   int dev, cus;
   if ((st = check_device(stream, &dev, &cus)) != MOE_OK) return st;
   if ((st = check_ptr(args->a_codes, dev, "a_codes")) != MOE_OK ||
-      (st = check_ptr(args->b_codes, dev, "b_codes")) != MOE_OK)
+      (st = check_ptr(args->weights->w13, dev, "weights")) != MOE_OK)
     return st;
   const moe::GemmParams p = to_params(args);
-  const bool paired = args->epilogue == MOE_EPI_SWIGLU_QUANT;
-  st = hip_status(launch_gemm(p, args->fmt, (int)args->epilogue, paired, cus, stream), "grouped gemm launch");
+  const bool paired = args->which == 0;
+  st = hip_status(launch_gemm(p, args->weights->fmt, (int)args->epilogue, paired, cus, stream),
+                  "grouped gemm launch");
   return st == MOE_OK ? ok() : st;
 }
 
@@ -431,6 +433,7 @@ moe_status moe_experts_forward(const moe_weights* w, const uint16_t* hidden_stat
   p1.a_scales = act_scales;
   p1.a_row_index = sorted_slot;
   p1.a_row_div = k;
+  p1.a_rows = T;
   p1.offsets = offsets;
   p1.E = E;
   p1.b_codes = w->w13;
@@ -450,6 +453,7 @@ moe_status moe_experts_forward(const moe_weights* w, const uint16_t* hidden_stat
   p2.a_scales = h_scales;
   p2.a_row_index = nullptr;
   p2.a_row_div = 1;
+  p2.a_rows = S;
   p2.offsets = offsets;
   p2.E = E;
   p2.b_codes = w->w2;
@@ -469,7 +473,7 @@ moe_status moe_experts_forward(const moe_weights* w, const uint16_t* hidden_stat
   if (opt && opt->debug) {
     const moe_debug* d = opt->debug;
     const bool mx = w->fmt == MOE_FMT_MXFP8A_MXFP4W;
-    const size_t sc_bytes = mx ? (size_t)T * (H / 32) : 4 * (size_t)T * (H / 128);
+    const size_t sc_bytes = mx ? (size_t)T * (H / 32) : 4 * (size_t)T * (H / 128);  // same in either layout
     if ((d->sorted_slot &&
          (he = hipMemcpyAsync(d->sorted_slot, sorted_slot, 4 * (size_t)S, hipMemcpyDeviceToDevice, stream)) !=
              hipSuccess) ||

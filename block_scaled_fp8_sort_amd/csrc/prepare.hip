@@ -1,12 +1,13 @@
-// One-shot weight preparation kernels: batched transposes that turn the nn
-// weight layout ([E, K, N] per weight) into the nt layout the GEMMs read
-// ([E, N, K]).  The pages' forward transforms both weight pairs once, before the
+// One-shot weight preparation kernels: the tiling of the FP8 weights into the
+// layout the grouped GEMMs stream (tile_layout.h), from the nt ([E, N, K]) or
+// the nn ([E, K, N]) layout, and batched transposes for the nn scales.  The pages' forward transforms both weight pairs once, before the
 // first forward, and picks the nn or nt grouped matmul by a layout flag ("DeepGEMM
 // Mega MoE requires a `process_group` for the EP group", docstring; "DeepGEMM
 // experts selected on a model spanning multiple CUDA devices", the record's
-// source).  Not on the timed path: a plain 64x64 LDS-tiled transpose.
+// source).  Not on the timed path.
 #include "device_common.h"
 #include "internal.h"
+#include "tile_layout.h"
 
 namespace moe {
 
@@ -31,6 +32,42 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
   }
 }
 
+// One thread per 16-byte chunk of the tiled destination
+// [E][NT][KB][256][128]: find its tile row tr and logical chunk c (physical
+// position p = c ^ swz(tr)), copy the source row's 16 K-bytes there, or zeros
+// for a padding row.
+template <bool PAIRED>
+__global__ __launch_bounds__(256) void tile_weight_kernel(const uint8_t* __restrict__ src, int nn, int32_t N,
+                                                          int32_t K, int32_t NT, int64_t n_chunks,
+                                                          uint8_t* __restrict__ dst) {
+  const int KB = K / kBlockK;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < n_chunks; d += stride) {
+    const int p = (int)(d & 7);
+    int64_t rest = d >> 3;
+    const int tr = (int)(rest % kTileN);
+    rest /= kTileN;
+    const int kb = (int)(rest % KB);
+    rest /= KB;
+    const int nt = (int)(rest % NT);
+    const int64_t e = rest / NT;
+    const int c = p ^ swz(tr);
+    const int row = tile_src_row<PAIRED>(nt, tr, N);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row >= 0) {
+      const int64_t k0 = (int64_t)kb * kBlockK + c * 16;
+      if (!nn) {
+        v = *(const uint4*)(src + (e * N + row) * (int64_t)K + k0);
+      } else {  // [E][K][N]: gather 16 bytes down a column
+        uint8_t b[16];
+        for (int j = 0; j < 16; ++j) b[j] = src[(e * K + k0 + j) * (int64_t)N + row];
+        v = *(const uint4*)b;
+      }
+    }
+    *(uint4*)(dst + d * 16) = v;
+  }
+}
+
 template <typename T>
 hipError_t launch_t(const T* in, T* out, int32_t batch, int32_t rows, int32_t cols, hipStream_t stream) {
   if (batch == 0 || rows == 0 || cols == 0) return hipSuccess;
@@ -40,6 +77,22 @@ hipError_t launch_t(const T* in, T* out, int32_t batch, int32_t rows, int32_t co
 }
 
 }  // namespace
+
+hipError_t launch_tile_weight_fp8(const uint8_t* src, bool nn, bool paired, int32_t E, int32_t N, int32_t K,
+                                  uint8_t* dst, hipStream_t stream) {
+  const int32_t NT = paired ? (N / 2) / 128 : (N + kTileN - 1) / kTileN;
+  const int64_t n_chunks = (int64_t)E * NT * (K / kBlockK) * kTileN * 8;
+  if (n_chunks == 0) return hipSuccess;
+  const int64_t want = (n_chunks + 255) / 256;
+  const int blocks = (int)(want < 65536 ? want : 65536);
+  if (paired)
+    hipLaunchKernelGGL(tile_weight_kernel<true>, dim3(blocks), dim3(256), 0, stream, src, nn ? 1 : 0, N, K, NT,
+                       n_chunks, dst);
+  else
+    hipLaunchKernelGGL(tile_weight_kernel<false>, dim3(blocks), dim3(256), 0, stream, src, nn ? 1 : 0, N, K, NT,
+                       n_chunks, dst);
+  return hipGetLastError();
+}
 
 hipError_t launch_transpose_u8(const uint8_t* in, uint8_t* out, int32_t batch, int32_t rows, int32_t cols,
                                hipStream_t stream) {

@@ -1,0 +1,44 @@
+// Layout of the prepared (tiled) expert weights and of the LDS operand rows,
+// shared by the weight-preparation kernel and the grouped GEMMs.
+//
+// A weight [E, N, K] (N output rows, K = reduction) is stored as
+//   [E][NT = ceil(N / 256)][KB = K / 128][256 tile rows][128 bytes],
+// i.e. every 128-wide K block of a 256-row tile is one contiguous 32 KB piece,
+// and every group of 8 tile rows is one contiguous 1 KB piece: one LDS-DMA
+// wave instruction (64 lanes x 16 bytes) copies it straight into LDS.  Inside a
+// 128-byte row the 16-byte chunks are permuted by swz(tile_row) so that the MFMA
+// fragment reads from LDS are free of bank conflicts.  Rows past N are zero.
+//
+// Paired tiles (the gate_up weight, N = 2I): tile j holds the 128 gate rows
+// [128 j, 128 j + 128) and the 128 matching up rows [I + 128 j, ...), interleaved
+// 16 at a time (tile rows 32 p + [0, 16) gate, 32 p + [16, 32) up), so one tile
+// yields a whole 128-wide block of SwiGLU outputs and g and u of the same output
+// land in the same lane.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace moe {
+
+constexpr int kTileN = 256;  // weight rows per tile
+constexpr int kBlockK = 128; // bytes of K per block row (FP8: 128 elements)
+
+// Physical 16-byte chunk position of logical chunk c in tile row r.  Rows
+// r..r+7 (and with 64 banks r..r+15) put the same logical chunk in distinct banks.
+__host__ __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// Source row (within the expert) of tile row tr of tile nt.  Returns -1 for a
+// padding row (plain tiles past N).
+template <bool PAIRED>
+__host__ __device__ __forceinline__ int tile_src_row(int nt, int tr, int N) {
+  if (PAIRED) {
+    const int I = N / 2;
+    const int p = tr >> 5, within = tr & 31;
+    const int h = nt * 128 + 16 * p + (within & 15);
+    return within < 16 ? h : I + h;
+  }
+  const int r = nt * kTileN + tr;
+  return r < N ? r : -1;
+}
+
+}  // namespace moe

@@ -108,20 +108,25 @@ moe_status moe_route_sort(const int32_t* top_k_index, int32_t T, int32_t k, int3
  * 1e-4f) / 448)) read exactly from the fp32 bits, scale byte e + 127 and
  * code = e4m3(x * 2^-e).  e4m3() rounds to nearest even and saturates at 448.
  *
- *  x       device bf16 bit patterns [rows, H].
- *  codes   device uint8 [rows, H] out.
- *  scales  device out: float [rows, H/128] (FP8_B128) or uint8 [rows, H/32] (MX). */
+ * Activation layout used by this library ("K-block-major"): a [rows, K] matrix
+ * of codes is stored as K/128 planes of [rows][128] bytes, i.e. byte
+ * (row, k) lives at (k / 128) * rows * 128 + row * 128 + k % 128; its scales are
+ * float [K/128][rows] (FP8_B128) or uint8 [K/32][rows] (MX).
+ *
+ *  x       device bf16 bit patterns [rows, H], row-major.
+ *  codes   device uint8 out, K-block-major [H/128][rows][128].
+ *  scales  device out: float [H/128][rows] (FP8_B128) or uint8 [H/32][rows] (MX). */
 moe_status moe_quant_act(const uint16_t* x, int32_t rows, int32_t H, moe_format fmt, uint8_t* codes, void* scales,
                          hipStream_t stream);
 
 /* --------------------------------------------------------- expert weights --
- * Descriptor of one layer's quantized expert weights in the kernel's layout (nt):
- *  w13        gate_up_proj codes: FP8_B128 uint8 [E, 2I, H]; MX packed uint8
- *             [E, 2I, H/2].  Rows [0, I) are the gate, rows [I, 2I) the up
- *             projection.
- *  w13_scale  FP8_B128 float [E, 2I/128, H/128]; MX uint8 [E, 2I, H/32].
- *  w2         down_proj codes: FP8_B128 uint8 [E, H, I]; MX packed [E, H, I/2].
- *  w2_scale   FP8_B128 float [E, H/128, I/128]; MX uint8 [E, H, I/32].
+ * Descriptor of one layer's prepared expert weights (filled by
+ * moe_prepare_weights; the code arrays are in the library's tiled layout and
+ * are not meant to be read by the caller):
+ *  w13 / w13_scale  gate_up weight codes (tiled) and its scales,
+ *                   FP8_B128: float [E, 2I/128, H/128].
+ *  w2 / w2_scale    down weight codes (tiled) and its scales,
+ *                   FP8_B128: float [E, H/128, I/128].
  * All four are device pointers that must stay valid while the descriptor is used. */
 typedef struct moe_weights {
   moe_format fmt;
@@ -133,13 +138,18 @@ typedef struct moe_weights {
 } moe_weights;
 
 /* One-shot weight preparation ([P-mega]: both weight pairs are transformed
- * together once before the first forward).  layout NT: the arrays are already in
- * the kernel layout; with prepared == NULL the descriptor points at them, else
- * they are copied into `prepared`.  layout NN: gate_up is [E, H, 2I] and down is
- * [E, I, H] (codes; FP8_B128 only, scales [E, H/128, 2I/128] and [E, I/128,
- * H/128]); they are transposed into `prepared`, which must hold
- * moe_prepared_weights_size() bytes.  Enqueued on `stream`; the descriptor is
- * filled on the host. */
+ * together once, before the first forward, into the kernel's own layout).
+ * Inputs, device memory, as the checkpoint stores them:
+ *  layout NT: gate_up [E, 2I, H] (rows [0, I) gate, [I, 2I) up), down [E, H, I];
+ *  layout NN: gate_up [E, H, 2I], down [E, I, H] (each expert's weight transposed).
+ *  FP8_B128: uint8 e4m3 codes; scales float per 128x128 block, [E, 2I/128, H/128]
+ *  and [E, H/128, I/128] for NT, transposed ([E, H/128, 2I/128], [E, I/128, H/128])
+ *  for NN.
+ *  MX (NT only): gate_up packed e2m1 [E, 2I, H/2] (even k in the low nibble),
+ *  down packed [E, H, I/2]; UE8M0 scales uint8 [E, 2I, H/32] and [E, H, I/32].
+ * The tiled copy goes to `prepared` (device, at least moe_prepared_weights_size()
+ * bytes, owned by the caller); `out` is filled on the host.  Enqueued on
+ * `stream`.  Weight quantization itself is offline (the checkpoint's). */
 size_t moe_prepared_weights_size(moe_format fmt, int32_t E, int32_t H, int32_t I);
 moe_status moe_prepare_weights(moe_format fmt, moe_layout layout, int32_t E, int32_t H, int32_t I,
                                const void* gate_up, const void* gate_up_scale, const void* down,
@@ -150,21 +160,23 @@ moe_status moe_prepare_weights(moe_format fmt, moe_layout layout, int32_t E, int
  * For every expert e and sorted row r in [offsets[e], offsets[e+1]):
  *   C[r, n] = sum_i A[a_row(r), i] * B[e, n, i]      (n < N, i < K)
  * with both operands dequantized (code times block scale), products exact and
- * sums in fp32.  a_row(r) = a_row_index[r] / a_row_divisor, or r when
- * a_row_index is NULL (the row gather of [P-grouped], "Source").  Then one
- * epilogue:
- *  MOE_EPI_STORE_F32         c_f32[r, n] = C[r, n]                (fp32 [max_rows, N])
- *  MOE_EPI_SWIGLU_QUANT      N = 2I: g = C[r, n], u = C[r, I + n] for n < I; with a
- *                            limit L, g = min(g, L) and u = clamp(u, -L, L);
+ * sums in fp32.  B is one weight of a prepared moe_weights: which = 0 the
+ * gate_up weight (N = 2I, K = H), which = 1 the down weight (N = H, K = I).
+ * a_row(r) = a_row_index[r] / a_row_divisor, or r when a_row_index is NULL (the
+ * row gather of [P-grouped], "Source").  A is K-block-major (see moe_quant_act)
+ * with a_rows rows per plane.  Then one epilogue:
+ *  MOE_EPI_STORE_F32         c_f32[r, n] = C[r, n]           (fp32 [max_rows, N], row-major)
+ *  MOE_EPI_SWIGLU_QUANT      which = 0: g = C[r, n], u = C[r, I + n] for n < I;
+ *                            with a limit L, g = min(g, L), u = clamp(u, -L, L);
  *                            h = silu(g) * u, quantized per block along I with the
- *                            activation rule into h_codes [max_rows, I] and
- *                            h_scales (float [max_rows, I/128] or uint8 [max_rows, I/32]).
+ *                            activation rule into h_codes (K-block-major
+ *                            [I/128][max_rows][128]) and h_scales (float
+ *                            [I/128][max_rows] or uint8 [I/32][max_rows]).
  *  MOE_EPI_WEIGHTED_SCATTER  slot = slot_of_row[r]:
- *                            slot_out[slot, n] = bf16(top_k_weights[slot] * C[r, n]).
+ *                            slot_out[slot, n] = bf16(top_k_weights[slot] * C[r, n])
+ *                            (bf16 [S, N], row-major).
  * Rows at and beyond offsets[E] are not written.  max_rows bounds offsets[E]
- * (normally T*k).  A codes are [rowsA, K] uint8 with scales float [rowsA, K/128]
- * or uint8 [rowsA, K/32]; B is one weight of a moe_weights (nt).  K must be a
- * multiple of 128, N a multiple of 128 (of 256 for SWIGLU_QUANT). */
+ * (normally T*k). */
 typedef enum moe_epilogue {
   MOE_EPI_STORE_F32 = 0,
   MOE_EPI_SWIGLU_QUANT = 1,
@@ -172,16 +184,15 @@ typedef enum moe_epilogue {
 } moe_epilogue;
 
 typedef struct moe_gemm_args {
-  moe_format fmt;
-  int32_t N, K, E;
+  const moe_weights* weights;
+  int32_t which; /* 0 = gate_up, 1 = down */
   int32_t max_rows;
   const uint8_t* a_codes;
   const void* a_scales;
+  int32_t a_rows;             /* rows per K-block plane of A */
   const int32_t* a_row_index; /* may be NULL */
   int32_t a_row_divisor;      /* >= 1 */
-  const int32_t* expert_offsets;
-  const uint8_t* b_codes;
-  const void* b_scales;
+  const int32_t* expert_offsets; /* [E+1] */
   moe_epilogue epilogue;
   float* c_f32;
   uint8_t* h_codes;
@@ -215,8 +226,8 @@ typedef struct moe_debug {
   /* Optional device copies of intermediates, for parity checks; each may be NULL. */
   int32_t* sorted_slot;    /* [T*k] */
   int32_t* expert_offsets; /* [E+1] */
-  uint8_t* act_codes;      /* [T, H] */
-  void* act_scales;        /* float [T, H/128] or uint8 [T, H/32] */
+  uint8_t* act_codes;      /* K-block-major [H/128][T][128] */
+  void* act_scales;        /* float [H/128][T] or uint8 [H/32][T] */
 } moe_debug;
 
 typedef struct moe_options {

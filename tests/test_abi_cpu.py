@@ -109,20 +109,25 @@ def test_forward_refusals(lib):
 
 
 def test_gemm_refusals(lib):
+    w = _weights()
     a = moe.MoeGemmArgs()
-    a.fmt, a.N, a.K, a.E, a.max_rows = 0, 256, 256, 4, 64
-    a.a_codes = a.a_scales = a.expert_offsets = a.b_codes = a.b_scales = 16
+    a.weights = ctypes.pointer(w)
+    a.which, a.max_rows, a.a_rows = 0, 64, 64
+    a.a_codes = a.a_scales = a.expert_offsets = 16
     a.epilogue = moe.EPI_STORE_F32
     assert lib.moe_grouped_gemm(ctypes.byref(a), None) == NULL  # c_f32 missing
     a.c_f32 = 16
-    a.K = 100
+    a.which = 2
+    assert lib.moe_grouped_gemm(ctypes.byref(a), None) == UNSUP
+    a.which = 0
+    a.a_rows = 10  # fewer A rows than max_rows without a row index
     assert lib.moe_grouped_gemm(ctypes.byref(a), None) == SHAPE
-    a.K = 256
+    a.a_rows = 64
     a.epilogue = moe.EPI_SWIGLU_QUANT
-    a.N = 384
     a.h_codes = a.h_scales = 16
-    assert lib.moe_grouped_gemm(ctypes.byref(a), None) == SHAPE  # N must be 2I with I % 128 == 0
-    a.N = 256
+    a.which = 1
+    assert lib.moe_grouped_gemm(ctypes.byref(a), None) == UNSUP  # SwiGLU only on gate_up
+    a.which = 0
     a.has_swiglu_limit, a.swiglu_limit = 1, 0.0
     assert lib.moe_grouped_gemm(ctypes.byref(a), None) == SHAPE
     a.epilogue = 9
@@ -130,18 +135,23 @@ def test_gemm_refusals(lib):
     a.epilogue = moe.EPI_STORE_F32
     a.max_rows = 0
     assert lib.moe_grouped_gemm(ctypes.byref(a), None) == OK  # nothing to do
+    bad = _weights(H=100)
+    a.weights = ctypes.pointer(bad)
+    assert lib.moe_grouped_gemm(ctypes.byref(a), None) == SHAPE
 
 
-def test_prepare_weights_host_paths(lib):
+def test_prepare_weights_refusals_and_sizes(lib):
     desc = moe.MoeWeights()
     p = ctypes.c_void_p(4096)
-    # nt in place: the descriptor points at the caller's arrays, no device work
-    assert lib.moe_prepare_weights(0, 0, 4, 256, 128, p, p, p, p, None, 0, ctypes.byref(desc), None) == OK
-    assert desc.E == 4 and desc.H == 256 and desc.I == 128 and desc.w13 == 4096
-    # nn needs a buffer; MX only comes in nt
-    assert lib.moe_prepare_weights(0, 1, 4, 256, 128, p, p, p, p, None, 0, ctypes.byref(desc), None) == WS
+    assert lib.moe_prepare_weights(0, 0, 4, 256, 128, p, p, p, p, None, 0, ctypes.byref(desc), None) == NULL
+    assert lib.moe_prepare_weights(0, 0, 4, 256, 128, p, p, p, p, p, 10, ctypes.byref(desc), None) == WS
     assert lib.moe_prepare_weights(1, 1, 4, 256, 128, p, p, p, p, p, 1 << 30, ctypes.byref(desc), None) == UNSUP
-    assert lib.moe_prepared_weights_size(0, 4, 256, 128) == 4 * 256 * 256 + 4 * 4 * 2 * 2 * 4 + 256 * 128 * 4 + 256
+    assert lib.moe_prepare_weights(0, 0, 4, 200, 128, p, p, p, p, p, 1 << 30, ctypes.byref(desc), None) == SHAPE
+    # FP8: tiled gate_up 4*256*256, its scales 4*2*2 floats, tiled down (H=256 -> one 256-row tile) 4*256*128,
+    # its scales 4*2*1 floats, each rounded up to 256 bytes
+    assert lib.moe_prepared_weights_size(0, 4, 256, 128) == 4 * 256 * 256 + 256 + 4 * 256 * 128 + 256
+    # H = 384 pads the down weight to two 256-row tiles
+    assert lib.moe_prepared_weights_size(0, 1, 384, 128) == 256 * 384 + 256 + 2 * 256 * 128 + 256
     assert lib.moe_prepared_weights_size(0, 4, 250, 128) == 0
 
 

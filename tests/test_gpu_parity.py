@@ -47,6 +47,18 @@ def host(t):
     return W.to_numpy(t)
 
 
+def rowmajor_codes(codes):
+    """K-block-major codes [K/128, rows, 128] (device) -> row-major [rows, K] (host)."""
+    c = host(codes)
+    kb, rows, _ = c.shape
+    return np.ascontiguousarray(c.transpose(1, 0, 2).reshape(rows, kb * 128))
+
+
+def rowmajor_scales(scales):
+    """[blocks, rows] (device) -> [rows, blocks] (host)."""
+    return np.ascontiguousarray(host(scales).T)
+
+
 # ---------------------------------------------------------------- route sort
 def _rand_ids(rng, T, k, E, p_skip, p_bad, lo=0):
     ids = rng.integers(lo, lo + E, size=(T, k)).astype(np.int32)
@@ -105,10 +117,10 @@ def test_quant_act_bit_exact_random(fmt):
     codes, scales = moe.quant_act(xb.to(DEV), fmt)
     torch.cuda.synchronize()
     o_codes, o_scales = oracle.quant_rows_bf16(xb.view(torch.int16).numpy().view(np.uint16), fmt)
-    g_codes = host(codes)
+    g_codes = rowmajor_codes(codes)
     mism = np.argwhere(g_codes != o_codes)
     assert mism.size == 0, f"{len(mism)} code mismatches, first at {mism[:5]}"
-    assert np.array_equal(host(scales).view(np.uint8), o_scales.view(np.uint8))
+    assert np.array_equal(rowmajor_scales(scales).view(np.uint8), o_scales.view(np.uint8))
 
 
 @pytest.mark.parametrize("fmt", [FP8, MX])
@@ -135,35 +147,36 @@ def test_quant_act_all_bf16_values(fmt):
         codes, scales = moe.quant_act(xb.to(DEV), fmt)
         torch.cuda.synchronize()
         o_codes, o_scales = oracle.quant_rows_bf16(xb.view(torch.int16).numpy().view(np.uint16), fmt)
-        assert np.array_equal(host(codes), o_codes)
-        assert np.array_equal(host(scales).view(np.uint8), o_scales.view(np.uint8))
+        assert np.array_equal(rowmajor_codes(codes), o_codes)
+        assert np.array_equal(rowmajor_scales(scales).view(np.uint8), o_scales.view(np.uint8))
 
 
 # -------------------------------------------------------------- grouped GEMM
-def _gemm_case(fmt, E, N, K, T, k, seed, p_skip=0.1):
+@pytest.mark.parametrize("which", [0, 1])
+@pytest.mark.parametrize("E,H,I,T,k", [(3, 256, 128, 40, 2), (5, 640, 384, 700, 3), (2, 384, 1024, 300, 1)])
+def test_grouped_gemm_store_f32(which, E, H, I, T, k):
+    """Either weight of a prepared layer times gathered rows, against the oracle's
+    grouped GEMM (which = 0: N = 2I over K = H; which = 1: N = H over K = I)."""
+    fmt = FP8
+    say(f"gemm store f32 which={which} E={E} H={H} I={I} T={T} k={k}")
+    seed = H + I + T + which
     rng = np.random.default_rng(seed)
-    if fmt == FP8:
-        b, bs = W.fp8_weights(E, N, K, seed, "gemm", DEV)
-    else:
-        b, bs = W.fp4_weights(E, N, K, seed, "gemm", DEV)
+    w13, s13 = W.fp8_weights(E, 2 * I, H, seed, "w13", DEV)
+    w2, s2 = W.fp8_weights(E, H, I, seed, "w2", DEV)
+    w = moe.prepare_weights(w13, s13, w2, s2, fmt=fmt)
+    N, K = (2 * I, H) if which == 0 else (H, I)
     x = W.hidden_states(T, K, seed, DEV)
-    ids = torch.from_numpy(_rand_ids(rng, T, k, E, p_skip, 0.0)).to(DEV)
+    ids = torch.from_numpy(_rand_ids(rng, T, k, E, 0.1, 0.0)).to(DEV)
     a, asc = moe.quant_act(x, fmt)
     ss, off, _, _ = moe.route_sort(ids, E)
-    return b, bs, a, asc, ss, off, ids
-
-
-@pytest.mark.parametrize("fmt", [FP8])
-@pytest.mark.parametrize("E,N,K,T,k", [(3, 256, 256, 40, 2), (5, 640, 384, 700, 3), (2, 384, 1024, 300, 1)])
-def test_grouped_gemm_store_f32(fmt, E, N, K, T, k):
-    say(f"gemm store f32 fmt={fmt} E={E} N={N} K={K} T={T} k={k}")
-    b, bs, a, asc, ss, off, ids = _gemm_case(fmt, E, N, K, T, k, seed=N + K + T)
     S = T * k
     c = torch.full((S, N), float("nan"), dtype=torch.float32, device=DEV)
-    moe.grouped_gemm(fmt, a, asc, off, b, bs, N, K, moe.EPI_STORE_F32, S, a_row_index=ss, a_row_divisor=k, c_f32=c)
+    moe.grouped_gemm(w, which, a, asc, T, off, moe.EPI_STORE_F32, S, a_row_index=ss, a_row_divisor=k, c_f32=c)
     torch.cuda.synchronize()
     offs = host(off)
-    ref = oracle.grouped_gemm(fmt, host(a), host(asc), offs, host(b), host(bs), N, K, row_index=host(ss), row_div=k)
+    b, bs = (host(w13), host(s13)) if which == 0 else (host(w2), host(s2))
+    ref = oracle.grouped_gemm(fmt, rowmajor_codes(a), rowmajor_scales(asc), offs, b, bs, N, K, row_index=host(ss),
+                              row_div=k)
     got = host(c)[: offs[-1]].astype(np.float64)
     assert np.all(np.isnan(host(c)[offs[-1]:]))  # rows past the valid ones are never written
     err = np.abs(got - ref)
@@ -216,8 +229,8 @@ def test_forward_parity_small(wl):
     assert np.array_equal(host(dbg["expert_offsets"]), o_off)
     assert inv == o_inv
     o_codes, o_scales = oracle.quant_rows_bf16(n["x"], wl.fmt)
-    assert np.array_equal(host(dbg["act_codes"]), o_codes)
-    assert np.array_equal(host(dbg["act_scales"]).view(np.uint8), o_scales.view(np.uint8))
+    assert np.array_equal(rowmajor_codes(dbg["act_codes"]), o_codes)
+    assert np.array_equal(rowmajor_scales(dbg["act_scales"]).view(np.uint8), o_scales.view(np.uint8))
     assert_out_close(got, ref, wl.name)
 
 
