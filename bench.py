@@ -31,6 +31,13 @@ PEAK_HBM_GBS = 8000.0
 
 METRIC = "MoE-layer active-expert TFLOP/s + tokens/s at 1 GPU; % of FP8/MXFP4 MFMA peak"
 
+# sources that define the dominant kernel; its HBM byte counters (profiles/) are
+# reported only while these are unchanged since the counters were taken
+KERNEL_SOURCES = {
+    0: ["block_scaled_fp8_sort_amd/csrc/gemm_fp8.hip", "block_scaled_fp8_sort_amd/csrc/tile_layout.h",
+        "block_scaled_fp8_sort_amd/csrc/device_common.h"],
+}
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -167,13 +174,37 @@ def main():
         "roofline": {
             "kernel": "gate_up grouped GEMM + SwiGLU + h quantization (moe_grouped_gemm, MOE_EPI_SWIGLU_QUANT)",
             "bound": "mfma", "achieved": round(l1_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(l1_tflops / peak, 4), "traffic": None, "ms_per_launch": round(l1_ms, 4),
+            "frac": round(l1_tflops / peak, 4), "traffic": traffic_record(wl), "ms_per_launch": round(l1_ms, 4),
+            "algorithmic_bytes_per_launch": int(len(touched) * w13_bytes + T * H + S_v * I),
         },
     }
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def traffic_record(wl):
+    """Calibrated HBM bytes per launch of the gate_up GEMM from the committed
+    rocprofv3 counter summary, or None when the kernel changed since."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"gate_up_gemm_{'fp8' if wl.fmt == 0 else 'mx'}_{wl.name}_hbm_bytes.md")
+    srcs = KERNEL_SOURCES.get(wl.fmt)
+    if not srcs or not os.path.exists(path):
+        return None
+    rec = None
+    for line in open(path):
+        if line.startswith("traffic-record: "):
+            rec = json.loads(line[len("traffic-record: "):])
+    if rec is None:
+        return None
+    h = hashlib.sha256()
+    for f in srcs:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec.get("kernel_sources_sha256"):
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 def _gemm_inputs(wl, inp, dev):
