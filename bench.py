@@ -218,7 +218,10 @@ def _gemm_inputs(wl, inp, dev):
     a_codes, a_scales = moe.quant_act(inp["x"], wl.fmt)
     sdt = torch.float32 if wl.fmt == W.FMT_FP8_B128 else torch.uint8
     h_codes = torch.zeros((I // 128, S, 128), dtype=torch.uint8, device=dev)
-    h_scales = torch.ones((I // 128 if wl.fmt == W.FMT_FP8_B128 else I // 32, S), dtype=sdt, device=dev)
+    if wl.fmt == W.FMT_FP8_B128:
+        h_scales = torch.ones((I // 128, S), dtype=sdt, device=dev)
+    else:
+        h_scales = torch.full((I // 128, S, 4), 127, dtype=sdt, device=dev)
     return ss, off, a_codes, a_scales, h_codes, h_scales
 
 

@@ -147,6 +147,11 @@ def _scale_cols(fmt: int, n: int) -> int:
     return n // 128 if fmt == FMT_FP8_B128 else n // 32
 
 
+def _scale_shape(fmt: int, K: int, rows: int):
+    """Shape of K-block-major scales: [K/128, rows] fp32, or [K/128, rows, 4] bytes (MX)."""
+    return (K // 128, rows) if fmt == FMT_FP8_B128 else (K // 128, rows, 4)
+
+
 # ------------------------------------------------------------------ route sort
 def route_sort(top_k_index: torch.Tensor, num_experts: int, expert_begin: int = 0, with_slot_pos: bool = True):
     """Stable sort of the flat (token, slot) pairs by local expert id.
@@ -175,13 +180,13 @@ def quant_act(x: torch.Tensor, fmt: int = FMT_FP8_B128):
     """Dynamic per-block quantization of bf16 rows.
 
     Returns K-block-major codes uint8 [H/128, rows, 128] and scales [H/128, rows]
-    (fp32, FP8_B128) or [H/32, rows] (uint8, MX).
+    (fp32, FP8_B128) or [H/128, rows, 4] (uint8 UE8M0, MX).
     """
     lib = load_library()
     _need(x, "x", torch.bfloat16)
     rows, H = x.shape
     codes = torch.empty((H // 128, rows, 128), dtype=torch.uint8, device=x.device)
-    scales = torch.empty((_scale_cols(fmt, H), rows), dtype=_scale_dtype(fmt), device=x.device)
+    scales = torch.empty(_scale_shape(fmt, H, rows), dtype=_scale_dtype(fmt), device=x.device)
     _check(lib.moe_quant_act(_ptr(x), rows, H, fmt, _ptr(codes), _ptr(scales), _stream(x.device)))
     return codes, scales
 
@@ -331,7 +336,7 @@ def experts_forward(hidden_states: torch.Tensor, top_k_index: torch.Tensor, top_
         debug["sorted_slot"] = torch.empty(S, dtype=torch.int32, device=dev)
         debug["expert_offsets"] = torch.empty(weights.E + 1, dtype=torch.int32, device=dev)
         debug["act_codes"] = torch.empty((H // 128, T, 128), dtype=torch.uint8, device=dev)
-        debug["act_scales"] = torch.empty((_scale_cols(weights.fmt, H), T), dtype=_scale_dtype(weights.fmt),
+        debug["act_scales"] = torch.empty(_scale_shape(weights.fmt, H, T), dtype=_scale_dtype(weights.fmt),
                                           device=dev)
         dbg = MoeDebug(_ptr(debug["sorted_slot"]), _ptr(debug["expert_offsets"]), _ptr(debug["act_codes"]),
                        _ptr(debug["act_scales"]))

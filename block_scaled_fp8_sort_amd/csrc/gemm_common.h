@@ -1,0 +1,82 @@
+// Pieces shared by the grouped GEMM kernels: the persistent tile table, the
+// tile lookup and a fence-free barrier.
+#pragma once
+
+#include "device_common.h"
+
+namespace moe {
+
+// Barrier without a memory fence: the waits before it are explicit (vmcnt for
+// the DMAs this wave issued); the empty asm statements keep the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Tile table in LDS: off[e] = expert offsets, tp[e] = first tile of expert e,
+// where expert e has ceil(rows_e / BM) m-tiles times NT n-tiles (m fastest);
+// tp[E] = total.  All threads of the block must call it.
+template <int THREADS>
+__device__ __forceinline__ int build_tile_table(const int32_t* offsets, int E, int BM, int NT, int* off, int* tp,
+                                                int* scan) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e <= E; e += THREADS) off[e] = offsets[e];
+  __syncthreads();
+  const int seg = (E + THREADS - 1) / THREADS;
+  const int e_lo = min(E, tid * seg), e_hi = min(E, tid * seg + seg);
+  int mine = 0;
+  for (int e = e_lo; e < e_hi; ++e) mine += ((off[e + 1] - off[e] + BM - 1) / BM) * NT;
+  scan[tid] = mine;
+  __syncthreads();
+  for (int d = 1; d < THREADS; d <<= 1) {
+    const int v = tid >= d ? scan[tid - d] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  {
+    int run = scan[tid] - mine;
+    for (int e = e_lo; e < e_hi; ++e) {
+      tp[e] = run;
+      run += ((off[e + 1] - off[e] + BM - 1) / BM) * NT;
+    }
+    if (tid == THREADS - 1) tp[E] = scan[THREADS - 1];
+  }
+  __syncthreads();
+  return tp[E];
+}
+
+struct TileCoord {
+  int e, n_tile, m0, m_end;
+};
+
+// Tile t -> (expert, n-tile, first sorted row, end of the expert's rows).  Every
+// lane computes the same values; they are made wave-uniform (scalar).
+__device__ __forceinline__ TileCoord locate_tile(int t, int E, int BM, const int* off, const int* tp) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tp[mid] <= t) lo = mid; else hi = mid;
+  }
+  TileCoord c;
+  c.e = __builtin_amdgcn_readfirstlane(lo);
+  const int m_begin = __builtin_amdgcn_readfirstlane(off[c.e]);
+  c.m_end = __builtin_amdgcn_readfirstlane(off[c.e + 1]);
+  const int mt = (c.m_end - m_begin + BM - 1) / BM;
+  const int loc = t - __builtin_amdgcn_readfirstlane(tp[c.e]);
+  c.n_tile = loc / mt;
+  c.m0 = m_begin + (loc % mt) * BM;
+  return c;
+}
+
+// Workgroup id remap for the persistent tile loop: dispatch places block b on
+// XCD b % 8, so consecutive virtual ids go to one XCD and the tiles that share
+// an expert's weight tile share that XCD's L2.
+__device__ __forceinline__ int xcd_virtual_block() {
+  const int G = gridDim.x;
+  return (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+}
+
+}  // namespace moe

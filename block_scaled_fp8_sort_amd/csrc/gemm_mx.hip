@@ -1,13 +1,299 @@
-// Grouped GEMM for the MX format (e4m3 activations x e2m1 weights with UE8M0
-// per-32 scales).  Not built yet: the launcher reports "not supported".
-#include "device_common.h"
+// Grouped GEMM over expert-sorted rows for the MX format: e4m3 activations
+// with a UE8M0 scale per 1x32 block times e2m1 weights (packed two per byte
+// along K) with a UE8M0 scale per 1x32 block along K, for gfx950.
+//
+// What it computes: the same grouped matmul and epilogues as the FP8 kernel
+// (the pages' grouped experts forward, "grouped_mm experts dispatch does not
+// support activation_scheme='static'", sections "What it means" and "Source";
+// FP4 weights arrive packed in int8, "DeepGEMM Mega MoE requires FP4-packed
+// expert weights (dtype=int8)", section "Source").
+//
+// Design (gfx950): power-of-two block scales ride the MFMA itself:
+// v_mfma_scale_f32_16x16x128_f8f6f4 with A = e2m1 weights (format 4), B = e4m3
+// activations (format 0), and per-lane E8M0 scale bytes, so the accumulators
+// take the MFMA result directly (no VALU promotion).  Operand lane layout, as
+// measured on the chip: an FP4 lane of group g (lane / 16) holds K elements
+// [32 g, 32 g + 32) as 32 nibbles; an FP8 lane of group g holds K elements
+// [16 g, 16 g + 16) in bytes 0-15 and [64 + 16 g, 64 + 16 g + 16) in bytes 16-31;
+// the scale byte of lane group g applies to K elements [32 g, 32 g + 32).
+// Tiles: 256 weight rows x BM tokens x 128 K, eight waves (2 x 4), two LDS stages
+// fed by LDS-DMA from the tiled weights (64-byte rows) and the K-block-major
+// activations; persistent XCD-aware tile walk as in the FP8 kernel.
+#include "gemm_common.h"
 #include "internal.h"
+#include "tile_layout.h"
 
 namespace moe {
 
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int BN = kTileN;
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kMaxE = 512;
+constexpr int kWRow = 64;   // bytes of a 128-wide K block of one FP4 weight row
+constexpr int kARow = 128;  // bytes of a 128-wide K block of one FP8 activation row
+
+template <int BM>
+struct StageBuf {
+  uint8_t w[BN * kWRow];     // FP4 weight rows (swz4 chunk order)
+  uint8_t a[BM * kARow];     // FP8 activation rows (swz chunk order)
+  uint8_t ws[BN * 4];        // weight scale bytes [row][4]
+  uint8_t as[BM * 4];        // activation scale bytes [row][4]
+};
+
+template <int BM>
+struct Misc {
+  int off[kMaxE + 1];
+  int tp[kMaxE + 1];
+  int scan[kThreads];
+};
+
+template <int BM>
+struct TileSrc {
+  static constexpr int A_LOADS = BM / 64;  // 1 KB activation DMAs per wave per stage
+  const uint8_t* w_tile;    // tiled FP4 codes of (expert, n-tile), K block 0
+  const uint8_t* ws_tile;   // tiled weight scales of (expert, n-tile), K block 0
+  const uint8_t* a_codes;
+  size_t a_plane;           // bytes per K-block plane of activation codes
+  uint32_t a_off[A_LOADS];  // per-lane gathered row chunk offset
+  const uint8_t* as_base;   // activation scale planes ([K/128][a_rows][4])
+  size_t as_plane;
+  uint32_t as_off;          // per-lane gathered row offset (waves < BM/64)
+};
+
+template <int BM>
+__device__ __forceinline__ void issue_stage(StageBuf<BM>* st, const TileSrc<BM>& src, int kb, int wave, int lane) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(st));
+  const uint32_t w = __builtin_amdgcn_readfirstlane(wave);
+  constexpr uint32_t oW = 0, oA = BN * kWRow, oWS = oA + BM * kARow, oAS = oWS + BN * 4;
+  // weights: 16 KB per K block, wave w copies 2 KB (32 rows), contiguous
+  const uint8_t* wsrc = src.w_tile + (size_t)kb * (BN * kWRow) + w * 2048;
+  lds_dma16_s(wsrc, lane * 16, base + oW + w * 2048);
+  lds_dma16_s(wsrc + 1024, lane * 16, base + oW + w * 2048 + 1024);
+  const uint8_t* plane = src.a_codes + (size_t)kb * src.a_plane;
+#pragma unroll
+  for (int q = 0; q < TileSrc<BM>::A_LOADS; ++q)
+    lds_dma16_s(plane, src.a_off[q], base + oA + (w * (BM / 8) + 8 * q) * kARow);
+  if (w < BM / 64) {  // activation scales: 64 rows x 4 bytes per wave
+    lds_dma4(src.as_base + (size_t)kb * src.as_plane + src.as_off, base + oAS + w * 256);
+  } else if (w == BM / 64) {  // weight scales: 256 rows x 4 bytes, contiguous
+    lds_dma16_s(src.ws_tile + (size_t)kb * (BN * 4), lane * 16, base + oWS);
+  }
+}
+
+// 16 bytes = 32 FP4 values, K elements [32 g, 32 g + 32) of weight row tr
+__device__ __forceinline__ v8i frag_w(const uint8_t* w, int tr, int g) {
+  const int4 x = *(const int4*)(w + tr * kWRow + ((g ^ swz4(tr)) << 4));
+  return v8i{x.x, x.y, x.z, x.w, 0, 0, 0, 0};
+}
+// 32 bytes = K elements [16 g, 16 g + 16) and [64 + 16 g, 64 + 16 g + 16) of activation row tr
+__device__ __forceinline__ v8i frag_a(const uint8_t* a, int tr, int g) {
+  const int s = swz(tr);
+  const int4 x0 = *(const int4*)(a + tr * kARow + ((g ^ s) << 4));
+  const int4 x1 = *(const int4*)(a + tr * kARow + (((4 + g) ^ s) << 4));
+  return v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+}
+
+template <int BM>
+__device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nxt, const TileSrc<BM>& src, int kb,
+                                       int KB, int wave, int lane, v4f (&acc)[8][BM / 64]) {
+  constexpr int WM = BM / 4;
+  constexpr int TS = WM / 16;
+  const int wn = wave & 1, wt = wave >> 1;
+  const int g = lane >> 4, l16 = lane & 15;
+  wait_vmcnt<0>();
+  raw_barrier();
+  if (kb + 1 < KB) issue_stage<BM>(nxt, src, kb + 1, wave, lane);
+  v8i bf[TS];
+  int sa[TS];
+#pragma unroll
+  for (int ti = 0; ti < TS; ++ti) {
+    const int tr = wt * WM + ti * 16 + l16;
+    bf[ti] = frag_a(cur->a, tr, g);
+    sa[ti] = cur->as[tr * 4 + g];
+  }
+#pragma unroll
+  for (int ni = 0; ni < 8; ++ni) {
+    const int tr = wn * 128 + ni * 16 + l16;
+    const v8i af = frag_w(cur->w, tr, g);
+    const int sw = cur->ws[tr * 4 + g];
+#pragma unroll
+    for (int ti = 0; ti < TS; ++ti)
+      acc[ni][ti] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[ti], acc[ni][ti], 4, 0, 0, sw, 0, sa[ti]);
+  }
+}
+
+template <int BM, int EPI, bool PAIRED>
+__global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) StageBuf<BM> st0;
+  __shared__ __attribute__((aligned(16))) StageBuf<BM> st1;
+  __shared__ __attribute__((aligned(16))) Misc<BM> misc;
+  constexpr int WM = BM / 4;
+  constexpr int TS = WM / 16;
+  static_assert(TS >= 1 && BM <= 256, "64 <= BM <= 256");
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wn = wave & 1, wt = wave >> 1;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int E = p.E, N = p.N, K = p.K, KB = K / 128;
+  const int I = N / 2;
+  const int NT = PAIRED ? I / 128 : (N + BN - 1) / BN;
+
+  const int total = build_tile_table<kThreads>(p.offsets, E, BM, NT, misc.off, misc.tp, misc.scan);
+  const int G = gridDim.x;
+  for (int t = xcd_virtual_block(); t < total; t += G) {
+    const TileCoord tc = locate_tile(t, E, BM, misc.off, misc.tp);
+    const int e = tc.e, n_tile = tc.n_tile, m0 = tc.m0, m_end = tc.m_end;
+
+    TileSrc<BM> src;
+    const size_t tile = (size_t)e * NT + n_tile;
+    src.w_tile = p.b_codes + tile * (size_t)KB * (BN * kWRow);
+    src.ws_tile = (const uint8_t*)p.b_scales + tile * (size_t)KB * (BN * 4);
+    src.a_codes = p.a_codes;
+    src.a_plane = (size_t)p.a_rows * kARow;
+#pragma unroll
+    for (int q = 0; q < TileSrc<BM>::A_LOADS; ++q) {
+      const int tr = wave * (BM / 8) + 8 * q + (lane >> 3);
+      const int r = min(m0 + tr, m_end - 1);
+      const int arow = p.a_row_index ? p.a_row_index[r] / p.a_row_div : r;
+      src.a_off[q] = (uint32_t)arow * kARow + (uint32_t)(((lane & 7) ^ swz(tr)) << 4);
+    }
+    src.as_base = (const uint8_t*)p.a_scales;
+    src.as_plane = (size_t)p.a_rows * 4;
+    {
+      const int tr = (wave % (BM / 64 > 0 ? BM / 64 : 1)) * 64 + lane;  // rows of the waves that load scales
+      const int r = min(m0 + min(tr, BM - 1), m_end - 1);
+      const int arow = p.a_row_index ? p.a_row_index[r] / p.a_row_div : r;
+      src.as_off = (uint32_t)arow * 4;
+    }
+
+    v4f acc[8][TS];
+#pragma unroll
+    for (int ni = 0; ni < 8; ++ni)
+#pragma unroll
+      for (int ti = 0; ti < TS; ++ti) acc[ni][ti] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    __syncthreads();
+    issue_stage<BM>(&st0, src, 0, wave, lane);
+    for (int kb = 0; kb < KB; kb += 2) {
+      k_step<BM>(&st0, &st1, src, kb, KB, wave, lane, acc);
+      if (kb + 1 < KB) k_step<BM>(&st1, &st0, src, kb + 1, KB, wave, lane, acc);
+    }
+
+    if constexpr (EPI == kEpiStoreF32) {
+#pragma unroll
+      for (int ti = 0; ti < TS; ++ti) {
+        const int r = m0 + wt * WM + ti * 16 + l16;
+        if (r < m_end) {
+#pragma unroll
+          for (int ni = 0; ni < 8; ++ni) {
+            int n;
+            if constexpr (PAIRED) {
+              const int h = n_tile * 128 + 16 * (wn * 4 + (ni >> 1)) + 4 * g;
+              n = (ni & 1) ? I + h : h;
+            } else {
+              n = n_tile * BN + wn * 128 + ni * 16 + 4 * g;
+            }
+            if (n < N) *(v4f*)(p.c_f32 + (size_t)r * N + n) = acc[ni][ti];
+          }
+        }
+      }
+    } else if constexpr (EPI == kEpiSwiGLUQuant) {
+      static_assert(PAIRED, "SwiGLU needs the paired gate/up layout");
+      auto hval = [&](int q, int ti, int i) {
+        float gv = acc[2 * q][ti][i];
+        float uv = acc[2 * q + 1][ti][i];
+        if (p.has_limit) {
+          gv = __builtin_fminf(gv, p.limit);
+          uv = __builtin_fminf(__builtin_fmaxf(uv, -p.limit), p.limit);
+        }
+        return gv / (1.0f + __expf(-gv)) * uv;
+      };
+      // this wave's 64 outputs of the tile's 128 are the 32-wide MX blocks 2 wn and
+      // 2 wn + 1, each made of pairs q = 2b and 2b + 1: the block amax needs only
+      // this wave (xor over the four lane groups)
+      uint8_t* plane = p.h_codes + (size_t)n_tile * p.max_rows * 128;
+      uint8_t* splane = (uint8_t*)p.h_scales + (size_t)n_tile * p.max_rows * 4;
+#pragma unroll
+      for (int ti = 0; ti < TS; ++ti) {
+        const int r = m0 + wt * WM + ti * 16 + l16;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          float m = 0.0f;
+#pragma unroll
+          for (int q = 2 * b; q < 2 * b + 2; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(hval(q, ti, i)));
+          m = wave_max_xor(m, 16);
+          m = wave_max_xor(m, 32);
+          const int ex = mx_block_exponent(m);
+          if (r < m_end) {
+#pragma unroll
+            for (int q = 2 * b; q < 2 * b + 2; ++q) {
+              const uint32_t code =
+                  e4m3x4(__builtin_ldexpf(hval(q, ti, 0), -ex), __builtin_ldexpf(hval(q, ti, 1), -ex),
+                         __builtin_ldexpf(hval(q, ti, 2), -ex), __builtin_ldexpf(hval(q, ti, 3), -ex));
+              *(uint32_t*)(plane + (size_t)r * 128 + 16 * (wn * 4 + q) + 4 * g) = code;
+            }
+            if (g == 0) splane[(size_t)r * 4 + wn * 2 + b] = (uint8_t)(ex + 127);
+          }
+        }
+      }
+    } else {  // kEpiWeightedScatter
+#pragma unroll
+      for (int ti = 0; ti < TS; ++ti) {
+        const int r = m0 + wt * WM + ti * 16 + l16;
+        if (r < m_end) {
+          const int slot = p.slot_of_row[r];
+          const float w = p.top_k_weights[slot];
+#pragma unroll
+          for (int ni = 0; ni < 8; ++ni) {
+            const int n = n_tile * BN + wn * 128 + ni * 16 + 4 * g;
+            if (n < N) {
+              const v4f v = acc[ni][ti] * w;
+              uint2 o;
+              o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+              o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+              *(uint2*)(p.slot_out + (size_t)slot * N + n) = o;
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int EPI, bool PAIRED>
+hipError_t launch_one(const GemmParams& p, int num_cus, hipStream_t stream) {
+  auto kern = gemm_mx_kernel<BM, EPI, PAIRED>;
+  const int NT = PAIRED ? (p.N / 2) / 128 : (p.N + BN - 1) / BN;
+  const long bound = ((long)(p.max_rows + BM - 1) / BM + p.E) * NT;
+  long grid = bound < num_cus ? bound : num_cus;
+  if (grid >= 8) grid = grid / 8 * 8;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int BM>
+hipError_t dispatch_epi(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream) {
+  if (epi == kEpiSwiGLUQuant) return launch_one<BM, kEpiSwiGLUQuant, true>(p, num_cus, stream);
+  if (epi == kEpiWeightedScatter) return launch_one<BM, kEpiWeightedScatter, false>(p, num_cus, stream);
+  if (paired) return launch_one<BM, kEpiStoreF32, true>(p, num_cus, stream);
+  return launch_one<BM, kEpiStoreF32, false>(p, num_cus, stream);
+}
+
+}  // namespace
+
 hipError_t launch_gemm_mx(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream) {
-  (void)p; (void)epi; (void)paired; (void)num_cus; (void)stream;
-  return hipErrorNotSupported;
+  const long avg_rows = p.E > 0 ? (long)p.max_rows / p.E : p.max_rows;
+  if (avg_rows >= 192) return dispatch_epi<256>(p, epi, paired, num_cus, stream);
+  if (avg_rows >= 96) return dispatch_epi<128>(p, epi, paired, num_cus, stream);
+  return dispatch_epi<64>(p, epi, paired, num_cus, stream);
 }
 
 }  // namespace moe

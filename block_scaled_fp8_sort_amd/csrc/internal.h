@@ -48,6 +48,10 @@ hipError_t launch_combine(const uint16_t* slot_out, const int32_t* ids, int32_t 
 // of tile_layout.h; `paired` selects the gate/up pairing (N = 2I).
 hipError_t launch_tile_weight_fp8(const uint8_t* src, bool nn, bool paired, int32_t E, int32_t N, int32_t K,
                                   uint8_t* dst, hipStream_t stream);
+// Tile one MX weight (packed codes [E, N, K/2], UE8M0 scales [E, N, K/32]) into
+// the MX layout of tile_layout.h (codes and scales each get their own array).
+hipError_t launch_tile_weight_mx(const uint8_t* codes, const uint8_t* scales, bool paired, int32_t E, int32_t N,
+                                 int32_t K, uint8_t* dst_codes, uint8_t* dst_scales, hipStream_t stream);
 hipError_t launch_transpose_u8(const uint8_t* in, uint8_t* out, int32_t batch, int32_t rows, int32_t cols,
                                hipStream_t stream);
 hipError_t launch_transpose_f32(const float* in, float* out, int32_t batch, int32_t rows, int32_t cols,

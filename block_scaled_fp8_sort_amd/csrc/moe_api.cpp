@@ -285,8 +285,9 @@ size_t moe_prepared_weights_size(moe_format fmt, int32_t E, int32_t H, int32_t I
     return align_up(e * 2 * i * h, A) + align_up(4 * e * (2 * i / 128) * (h / 128), A) +
            align_up(e * nt2 * 256 * i, A) + align_up(4 * e * (h / 128) * (i / 128), A);
   }
-  return align_up(e * 2 * i * h / 2, A) + align_up(e * 2 * i * (h / 32), A) + align_up(e * h * i / 2, A) +
-         align_up(e * h * (i / 32), A);
+  const size_t rows2 = (h + 255) / 256 * 256;  // down weight rows padded to whole tiles
+  return align_up(e * 2 * i * h / 2, A) + align_up(e * 2 * i * (h / 32), A) + align_up(e * rows2 * i / 2, A) +
+         align_up(e * rows2 * (i / 32), A);
 }
 
 moe_status moe_prepare_weights(moe_format fmt, moe_layout layout, int32_t E, int32_t H, int32_t I,
@@ -315,19 +316,20 @@ moe_status moe_prepare_weights(moe_format fmt, moe_layout layout, int32_t E, int
   const bool mx = fmt == MOE_FMT_MXFP8A_MXFP4W;
   const size_t b13 = mx ? e * 2 * i * h / 2 : e * 2 * i * h;
   const size_t b13s = mx ? e * 2 * i * (h / 32) : 4 * e * (2 * i / 128) * (h / 128);
-  const size_t b2 = mx ? e * h * i / 2 : e * ((h + 255) / 256) * 256 * i;
-  const size_t b2s = mx ? e * h * (i / 32) : 4 * e * (h / 128) * (i / 128);
+  const size_t rows2 = (h + 255) / 256 * 256;
+  const size_t b2 = mx ? e * rows2 * i / 2 : e * rows2 * i;
+  const size_t b2s = mx ? e * rows2 * (i / 32) : 4 * e * (h / 128) * (i / 128);
   uint8_t* p13 = (uint8_t*)prepared;
   uint8_t* p13s = p13 + align_up(b13, A);
   uint8_t* p2 = p13s + align_up(b13s, A);
   uint8_t* p2s = p2 + align_up(b2, A);
   hipError_t he = hipSuccess;
   if (mx) {
-    if ((he = hipMemcpyAsync(p13, gate_up, b13, hipMemcpyDeviceToDevice, stream)) != hipSuccess ||
-        (he = hipMemcpyAsync(p13s, gate_up_scale, b13s, hipMemcpyDeviceToDevice, stream)) != hipSuccess ||
-        (he = hipMemcpyAsync(p2, down, b2, hipMemcpyDeviceToDevice, stream)) != hipSuccess ||
-        (he = hipMemcpyAsync(p2s, down_scale, b2s, hipMemcpyDeviceToDevice, stream)) != hipSuccess)
-      return hip_status(he, "weight copy");
+    if ((he = moe::launch_tile_weight_mx((const uint8_t*)gate_up, (const uint8_t*)gate_up_scale, true, E, 2 * I, H,
+                                         p13, p13s, stream)) != hipSuccess ||
+        (he = moe::launch_tile_weight_mx((const uint8_t*)down, (const uint8_t*)down_scale, false, E, H, I, p2, p2s,
+                                         stream)) != hipSuccess)
+      return hip_status(he, "weight tiling");
   } else {
     const bool nn = layout == MOE_LAYOUT_NN;
     if ((he = moe::launch_tile_weight_fp8((const uint8_t*)gate_up, nn, true, E, 2 * I, H, p13, stream)) != hipSuccess ||

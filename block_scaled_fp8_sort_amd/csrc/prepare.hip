@@ -68,6 +68,55 @@ __global__ __launch_bounds__(256) void tile_weight_kernel(const uint8_t* __restr
   }
 }
 
+// MX codes: one thread per 16-byte chunk of [E][NT][KB][256][64]; the source row
+// is packed [E][N][K/2].
+template <bool PAIRED>
+__global__ __launch_bounds__(256) void tile_weight_mx_kernel(const uint8_t* __restrict__ src, int32_t N, int32_t K,
+                                                             int32_t NT, int64_t n_chunks, uint8_t* __restrict__ dst) {
+  const int KB = K / 128;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < n_chunks; d += stride) {
+    const int p = (int)(d & 3);
+    int64_t rest = d >> 2;
+    const int tr = (int)(rest % kTileN);
+    rest /= kTileN;
+    const int kb = (int)(rest % KB);
+    rest /= KB;
+    const int nt = (int)(rest % NT);
+    const int64_t e = rest / NT;
+    const int c = p ^ swz4(tr);
+    const int row = tile_src_row<PAIRED>(nt, tr, N);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row >= 0) v = *(const uint4*)(src + (e * N + row) * (int64_t)(K / 2) + (int64_t)kb * 64 + c * 16);
+    *(uint4*)(dst + d * 16) = v;
+  }
+}
+
+// MX scales: one thread per 4-byte entry of [E][NT][KB][256][4]; the source is
+// [E][N][K/32] bytes.
+template <bool PAIRED>
+__global__ __launch_bounds__(256) void tile_scale_mx_kernel(const uint8_t* __restrict__ src, int32_t N, int32_t K,
+                                                            int32_t NT, int64_t n_entries, uint32_t* __restrict__ dst) {
+  const int KB = K / 128;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < n_entries; d += stride) {
+    int64_t rest = d;
+    const int tr = (int)(rest % kTileN);
+    rest /= kTileN;
+    const int kb = (int)(rest % KB);
+    rest /= KB;
+    const int nt = (int)(rest % NT);
+    const int64_t e = rest / NT;
+    const int row = tile_src_row<PAIRED>(nt, tr, N);
+    uint32_t v = 0x7F7F7F7Fu;  // padding rows: scale 1, codes 0
+    if (row >= 0) {
+      const uint8_t* s = src + (e * N + row) * (int64_t)(K / 32) + kb * 4;
+      v = (uint32_t)s[0] | ((uint32_t)s[1] << 8) | ((uint32_t)s[2] << 16) | ((uint32_t)s[3] << 24);
+    }
+    dst[d] = v;
+  }
+}
+
 template <typename T>
 hipError_t launch_t(const T* in, T* out, int32_t batch, int32_t rows, int32_t cols, hipStream_t stream) {
   if (batch == 0 || rows == 0 || cols == 0) return hipSuccess;
@@ -91,6 +140,31 @@ hipError_t launch_tile_weight_fp8(const uint8_t* src, bool nn, bool paired, int3
   else
     hipLaunchKernelGGL(tile_weight_kernel<false>, dim3(blocks), dim3(256), 0, stream, src, nn ? 1 : 0, N, K, NT,
                        n_chunks, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_weight_mx(const uint8_t* codes, const uint8_t* scales, bool paired, int32_t E, int32_t N,
+                                 int32_t K, uint8_t* dst_codes, uint8_t* dst_scales, hipStream_t stream) {
+  const int32_t NT = paired ? (N / 2) / 128 : (N + kTileN - 1) / kTileN;
+  const int64_t n_entries = (int64_t)E * NT * (K / 128) * kTileN;  // one per (tile row, K block)
+  if (n_entries == 0) return hipSuccess;
+  const int64_t n_chunks = n_entries * 4;
+  int blocks = (int)((n_chunks + 255) / 256 < 65536 ? (n_chunks + 255) / 256 : 65536);
+  if (paired)
+    hipLaunchKernelGGL(tile_weight_mx_kernel<true>, dim3(blocks), dim3(256), 0, stream, codes, N, K, NT, n_chunks,
+                       dst_codes);
+  else
+    hipLaunchKernelGGL(tile_weight_mx_kernel<false>, dim3(blocks), dim3(256), 0, stream, codes, N, K, NT, n_chunks,
+                       dst_codes);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  blocks = (int)((n_entries + 255) / 256 < 65536 ? (n_entries + 255) / 256 : 65536);
+  if (paired)
+    hipLaunchKernelGGL(tile_scale_mx_kernel<true>, dim3(blocks), dim3(256), 0, stream, scales, N, K, NT, n_entries,
+                       (uint32_t*)dst_scales);
+  else
+    hipLaunchKernelGGL(tile_scale_mx_kernel<false>, dim3(blocks), dim3(256), 0, stream, scales, N, K, NT, n_entries,
+                       (uint32_t*)dst_scales);
   return hipGetLastError();
 }
 

@@ -9,8 +9,8 @@
 //  fp32 bits, stored as the byte e + 127; code = e4m3(x * 2^-e), exact scaling.
 //
 // Output layout (the grouped GEMM's operand layout): K-block-major, codes
-// [H/128][rows][128 bytes] and scales [H/128][rows] (FP8_B128) or [H/32][rows]
-// (MX).  One 128-wide block of a row is 128 contiguous bytes, and the blocks of
+// [H/128][rows][128 bytes] and scales [H/128][rows] (FP8_B128) or
+// [H/128][rows][4 bytes] (MX: the four UE8M0 bytes of a row's 128-wide block).  One 128-wide block of a row is 128 contiguous bytes, and the blocks of
 // different rows for the same K range sit side by side.
 //
 // The kernel is HBM-bound (2 bytes in, 1 byte + a scale out per element): each
@@ -70,7 +70,8 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint4* __restrict_
       for (int i = 0; i < 8; ++i) q[i] = __builtin_ldexpf(f[i], -e);
       out.x = e4m3x4(q[0], q[1], q[2], q[3]);
       out.y = e4m3x4(q[4], q[5], q[6], q[7]);
-      if ((col8 % kLanesPerBlock) == 0) ((uint8_t*)scales)[(int64_t)(col8 / 4) * rows + row] = (uint8_t)(e + 127);
+      if ((col8 % kLanesPerBlock) == 0)
+        ((uint8_t*)scales)[(blk128 * rows + row) * 4 + (col8 % 16) / 4] = (uint8_t)(e + 127);
     }
     *dst = out;
   }

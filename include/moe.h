@@ -111,11 +111,12 @@ moe_status moe_route_sort(const int32_t* top_k_index, int32_t T, int32_t k, int3
  * Activation layout used by this library ("K-block-major"): a [rows, K] matrix
  * of codes is stored as K/128 planes of [rows][128] bytes, i.e. byte
  * (row, k) lives at (k / 128) * rows * 128 + row * 128 + k % 128; its scales are
- * float [K/128][rows] (FP8_B128) or uint8 [K/32][rows] (MX).
+ * float [K/128][rows] (FP8_B128) or uint8 [K/128][rows][4] (MX: the four UE8M0
+ * bytes of a row's 128-wide block, in K order).
  *
  *  x       device bf16 bit patterns [rows, H], row-major.
  *  codes   device uint8 out, K-block-major [H/128][rows][128].
- *  scales  device out: float [H/128][rows] (FP8_B128) or uint8 [H/32][rows] (MX). */
+ *  scales  device out: float [H/128][rows] (FP8_B128) or uint8 [H/128][rows][4] (MX). */
 moe_status moe_quant_act(const uint16_t* x, int32_t rows, int32_t H, moe_format fmt, uint8_t* codes, void* scales,
                          hipStream_t stream);
 
@@ -127,6 +128,7 @@ moe_status moe_quant_act(const uint16_t* x, int32_t rows, int32_t H, moe_format 
  *                   FP8_B128: float [E, 2I/128, H/128].
  *  w2 / w2_scale    down weight codes (tiled) and its scales,
  *                   FP8_B128: float [E, H/128, I/128].
+ *                   MX: the scales are tiled like the codes.
  * All four are device pointers that must stay valid while the descriptor is used. */
 typedef struct moe_weights {
   moe_format fmt;
@@ -171,7 +173,7 @@ moe_status moe_prepare_weights(moe_format fmt, moe_layout layout, int32_t E, int
  *                            h = silu(g) * u, quantized per block along I with the
  *                            activation rule into h_codes (K-block-major
  *                            [I/128][max_rows][128]) and h_scales (float
- *                            [I/128][max_rows] or uint8 [I/32][max_rows]).
+ *                            [I/128][max_rows] or uint8 [I/128][max_rows][4]).
  *  MOE_EPI_WEIGHTED_SCATTER  slot = slot_of_row[r]:
  *                            slot_out[slot, n] = bf16(top_k_weights[slot] * C[r, n])
  *                            (bf16 [S, N], row-major).
@@ -227,7 +229,7 @@ typedef struct moe_debug {
   int32_t* sorted_slot;    /* [T*k] */
   int32_t* expert_offsets; /* [E+1] */
   uint8_t* act_codes;      /* K-block-major [H/128][T][128] */
-  void* act_scales;        /* float [H/128][T] or uint8 [H/32][T] */
+  void* act_scales;        /* float [H/128][T] or uint8 [H/128][T][4] */
 } moe_debug;
 
 typedef struct moe_options {

@@ -55,8 +55,13 @@ def rowmajor_codes(codes):
 
 
 def rowmajor_scales(scales):
-    """[blocks, rows] (device) -> [rows, blocks] (host)."""
-    return np.ascontiguousarray(host(scales).T)
+    """K-block-major scales (device) -> row-major [rows, blocks] (host): FP8
+    [K/128, rows] -> [rows, K/128]; MX [K/128, rows, 4] -> [rows, K/32]."""
+    s = host(scales)
+    if s.ndim == 2:
+        return np.ascontiguousarray(s.T)
+    kb, rows, _ = s.shape
+    return np.ascontiguousarray(s.transpose(1, 0, 2).reshape(rows, kb * 4))
 
 
 # ---------------------------------------------------------------- route sort
@@ -152,17 +157,18 @@ def test_quant_act_all_bf16_values(fmt):
 
 
 # -------------------------------------------------------------- grouped GEMM
+@pytest.mark.parametrize("fmt", [FP8, MX])
 @pytest.mark.parametrize("which", [0, 1])
 @pytest.mark.parametrize("E,H,I,T,k", [(3, 256, 128, 40, 2), (5, 640, 384, 700, 3), (2, 384, 1024, 300, 1)])
-def test_grouped_gemm_store_f32(which, E, H, I, T, k):
+def test_grouped_gemm_store_f32(fmt, which, E, H, I, T, k):
     """Either weight of a prepared layer times gathered rows, against the oracle's
     grouped GEMM (which = 0: N = 2I over K = H; which = 1: N = H over K = I)."""
-    fmt = FP8
-    say(f"gemm store f32 which={which} E={E} H={H} I={I} T={T} k={k}")
+    say(f"gemm store f32 fmt={fmt} which={which} E={E} H={H} I={I} T={T} k={k}")
     seed = H + I + T + which
     rng = np.random.default_rng(seed)
-    w13, s13 = W.fp8_weights(E, 2 * I, H, seed, "w13", DEV)
-    w2, s2 = W.fp8_weights(E, H, I, seed, "w2", DEV)
+    gen = W.fp8_weights if fmt == FP8 else W.fp4_weights
+    w13, s13 = gen(E, 2 * I, H, seed, "w13", DEV)
+    w2, s2 = gen(E, H, I, seed, "w2", DEV)
     w = moe.prepare_weights(w13, s13, w2, s2, fmt=fmt)
     N, K = (2 * I, H) if which == 0 else (H, I)
     x = W.hidden_states(T, K, seed, DEV)
@@ -216,6 +222,11 @@ SMALL = [
     _small_workload("ragged_fp8_clamp", FP8, T=517, H=384, I=256, E=12, k=4, routing="zipf", skip=0.05,
                     limit=0.05, seed=12),
     _small_workload("k1_one_expert", FP8, T=129, H=256, I=128, E=1, k=1, seed=13),
+    _small_workload("mx_tiny", MX, T=64, H=256, I=128, E=8, k=2, seed=14),
+    _small_workload("mx_ragged_clamp", MX, T=300, H=384, I=256, E=7, k=4, routing="zipf", skip=0.1, limit=7.0,
+                    seed=15),
+    _small_workload("mx_tight_clamp", MX, T=200, H=512, I=384, E=5, k=3, routing="zipf", skip=0.05, limit=0.05,
+                    seed=16),
 ]
 
 
@@ -293,7 +304,7 @@ def test_prepare_weights_nn_layout_matches_nt():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-FULL = ["qwen3_moe_decode", "mixtral_8x7b", "deepseek_v3"]
+FULL = ["qwen3_moe_decode", "mixtral_8x7b", "deepseek_v3", "megamoe_fp8xfp4"]
 
 
 @pytest.mark.parametrize("name", FULL)
