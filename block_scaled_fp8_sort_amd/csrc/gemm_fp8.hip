@@ -21,7 +21,9 @@
 //    The MFMAs of one n sub-tile and the FMAs of the previous one are
 //    interleaved in program order, so the matrix core and the VALU overlap.
 //  * Workgroup tile 256 (n) x BM (tokens) x 128 (K), eight waves as 2 (n) x 4
-//    (tokens), two per SIMD, each 128 n x BM/4 tokens.  Two LDS stages.
+//    (tokens), two per SIMD, each 128 n x BM/4 tokens.  Two LDS stages at
+//    BM = 256, three at smaller BM (more bytes in flight per CU, which is what
+//    streaming weights at decode sizes needs).
 //  * Operands move global -> LDS by LDS-DMA (global_load_lds_dwordx4, 16 bytes
 //    per lane).  Weights are pre-tiled (tile_layout.h) so each DMA instruction
 //    copies one contiguous 1 KB; activations are stored K-block-major
@@ -117,18 +119,22 @@ __device__ __forceinline__ void issue_stage(StageBuf<BM>* st, const TileSrc<BM>&
   lds_dma4(src.s_base + (size_t)kb * src.s_stride, base + (BN + BM) * BK + w * 256);
 }
 
-// One K block: wait for stage `cur`, start the DMA of block kb + 1 into `nxt`
-// (the stage block kb - 1 used), then accumulate the block from `cur`.
-template <int BM, bool PAIRED>
+// One K block: wait for stage `cur`, start the DMA of block kb + STAGES - 1 into
+// `nxt` (the stage block kb - 1 used), then accumulate the block from `cur`.
+// Past the last block the DMA repeats block KB - 1 into a stage nobody reads,
+// which keeps the number of DMAs in flight, and so this wait, the same on every
+// step.
+template <int BM, bool PAIRED, int STAGES>
 __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nxt, const TileSrc<BM>& src, int kb,
                                        int KB, int wave, int lane, v4f (&acc)[8][BM / 64]) {
   constexpr int WM = BM / 4;
   constexpr int TS = WM / 16;
+  constexpr int LOADS = 4 + BM / 64 + 1;  // DMA instructions per wave per stage
   const int wn = wave & 1, wt = wave >> 1;
   const int g = lane >> 4, l16 = lane & 15;
-  wait_vmcnt<0>();  // this wave's DMAs of stage kb have landed
-  raw_barrier();    // ... and every other wave's; all waves are done with block kb - 1
-  if (kb + 1 < KB) issue_stage<BM>(nxt, src, kb + 1, wave, lane);
+  wait_vmcnt<LOADS * (STAGES - 2)>();  // this wave's DMAs of stage kb have landed
+  raw_barrier();  // ... and every other wave's; all waves are done with block kb - 1
+  issue_stage<BM>(nxt, src, min(kb + STAGES - 1, KB - 1), wave, lane);
   const float swg = cur->s[PAIRED ? BM : BM + wn];
   const float swu = cur->s[BM + 1];
   typedef float vts __attribute__((ext_vector_type(TS)));
@@ -168,8 +174,8 @@ __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nx
 
 template <int BM, int EPI, bool PAIRED>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) StageBuf<BM> st0;
-  __shared__ __attribute__((aligned(16))) StageBuf<BM> st1;
+  constexpr int STAGES = BM == 256 ? 2 : 3;  // as many as the 160 KB of LDS hold
+  __shared__ __attribute__((aligned(16))) StageBuf<BM> st[STAGES];
   __shared__ __attribute__((aligned(16))) Misc<BM> misc;
   constexpr int WM = BM / 4;   // tokens per wave
   constexpr int TS = WM / 16;  // 16-token sub-tiles per wave
@@ -267,11 +273,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p
       for (int ti = 0; ti < TS; ++ti) acc[ni][ti] = v4f{0.f, 0.f, 0.f, 0.f};
 
     __syncthreads();  // the previous tile's LDS readers are done
-    issue_stage<BM>(&st0, src, 0, wave, lane);
-    for (int kb = 0; kb < KB; kb += 2) {
-      k_step<BM, PAIRED>(&st0, &st1, src, kb, KB, wave, lane, acc);
-      if (kb + 1 < KB) k_step<BM, PAIRED>(&st1, &st0, src, kb + 1, KB, wave, lane, acc);
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) issue_stage<BM>(&st[s], src, min(s, KB - 1), wave, lane);
+    for (int kb = 0; kb < KB; kb += STAGES) {
+#pragma unroll
+      for (int j = 0; j < STAGES; ++j)
+        if (kb + j < KB)
+          k_step<BM, PAIRED, STAGES>(&st[j], &st[(j + STAGES - 1) % STAGES], src, kb + j, KB, wave, lane, acc);
     }
+    wait_vmcnt<0>();  // the trailing repeat DMAs land before the stages are reused
 
     // ---- epilogues
     if constexpr (EPI == kEpiStoreF32) {

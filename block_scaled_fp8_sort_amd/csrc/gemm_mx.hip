@@ -16,8 +16,8 @@
 // [32 g, 32 g + 32) as 32 nibbles; an FP8 lane of group g holds K elements
 // [16 g, 16 g + 16) in bytes 0-15 and [64 + 16 g, 64 + 16 g + 16) in bytes 16-31;
 // the scale byte of lane group g applies to K elements [32 g, 32 g + 32).
-// Tiles: 256 weight rows x BM tokens x 128 K, eight waves (2 x 4), two LDS stages
-// fed by LDS-DMA from the tiled weights (64-byte rows) and the K-block-major
+// Tiles: 256 weight rows x BM tokens x 128 K, eight waves (2 x 4), two or four
+// LDS stages fed by LDS-DMA from the tiled weights (64-byte rows) and the K-block-major
 // activations; persistent XCD-aware tile walk as in the FP8 kernel.
 #include "gemm_common.h"
 #include "internal.h"
@@ -43,6 +43,7 @@ struct StageBuf {
   uint8_t a[BM * kARow];     // FP8 activation rows (swz chunk order)
   uint8_t ws[BN * 4];        // weight scale bytes [row][4]
   uint8_t as[BM * 4];        // activation scale bytes [row][4]
+  uint8_t spare[256];        // target of the waves with no scale to fetch
 };
 
 template <int BM>
@@ -78,10 +79,13 @@ __device__ __forceinline__ void issue_stage(StageBuf<BM>* st, const TileSrc<BM>&
 #pragma unroll
   for (int q = 0; q < TileSrc<BM>::A_LOADS; ++q)
     lds_dma16_s(plane, src.a_off[q], base + oA + (w * (BM / 8) + 8 * q) * kARow);
+  // exactly one scale DMA per wave, so every wave has the same DMA count per stage
   if (w < BM / 64) {  // activation scales: 64 rows x 4 bytes per wave
     lds_dma4(src.as_base + (size_t)kb * src.as_plane + src.as_off, base + oAS + w * 256);
   } else if (w == BM / 64) {  // weight scales: 256 rows x 4 bytes, contiguous
     lds_dma16_s(src.ws_tile + (size_t)kb * (BN * 4), lane * 16, base + oWS);
+  } else {
+    lds_dma4(src.as_base + (size_t)kb * src.as_plane + src.as_off, base + oAS + BM * 4);
   }
 }
 
@@ -98,16 +102,19 @@ __device__ __forceinline__ v8i frag_a(const uint8_t* a, int tr, int g) {
   return v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 }
 
-template <int BM>
+// One K block (see the FP8 kernel: the DMA always goes out, repeating block
+// KB - 1 past the end, so the wait count is constant).
+template <int BM, int STAGES>
 __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nxt, const TileSrc<BM>& src, int kb,
                                        int KB, int wave, int lane, v4f (&acc)[8][BM / 64]) {
   constexpr int WM = BM / 4;
   constexpr int TS = WM / 16;
+  constexpr int LOADS = 2 + BM / 64 + 1;  // DMA instructions per wave per stage
   const int wn = wave & 1, wt = wave >> 1;
   const int g = lane >> 4, l16 = lane & 15;
-  wait_vmcnt<0>();
+  wait_vmcnt<LOADS * (STAGES - 2)>();
   raw_barrier();
-  if (kb + 1 < KB) issue_stage<BM>(nxt, src, kb + 1, wave, lane);
+  issue_stage<BM>(nxt, src, min(kb + STAGES - 1, KB - 1), wave, lane);
   v8i bf[TS];
   int sa[TS];
 #pragma unroll
@@ -129,8 +136,8 @@ __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nx
 
 template <int BM, int EPI, bool PAIRED>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) StageBuf<BM> st0;
-  __shared__ __attribute__((aligned(16))) StageBuf<BM> st1;
+  constexpr int STAGES = BM == 256 ? 2 : 4;  // at BM = 256 a third stage would spill registers
+  __shared__ __attribute__((aligned(16))) StageBuf<BM> st[STAGES];
   __shared__ __attribute__((aligned(16))) Misc<BM> misc;
   constexpr int WM = BM / 4;
   constexpr int TS = WM / 16;
@@ -178,11 +185,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmParams p) {
       for (int ti = 0; ti < TS; ++ti) acc[ni][ti] = v4f{0.f, 0.f, 0.f, 0.f};
 
     __syncthreads();
-    issue_stage<BM>(&st0, src, 0, wave, lane);
-    for (int kb = 0; kb < KB; kb += 2) {
-      k_step<BM>(&st0, &st1, src, kb, KB, wave, lane, acc);
-      if (kb + 1 < KB) k_step<BM>(&st1, &st0, src, kb + 1, KB, wave, lane, acc);
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) issue_stage<BM>(&st[s], src, min(s, KB - 1), wave, lane);
+    for (int kb = 0; kb < KB; kb += STAGES) {
+#pragma unroll
+      for (int j = 0; j < STAGES; ++j)
+        if (kb + j < KB) k_step<BM, STAGES>(&st[j], &st[(j + STAGES - 1) % STAGES], src, kb + j, KB, wave, lane, acc);
     }
+    wait_vmcnt<0>();
 
     if constexpr (EPI == kEpiStoreF32) {
 #pragma unroll
