@@ -21,9 +21,10 @@
 //    The MFMAs of one n sub-tile and the FMAs of the previous one are
 //    interleaved in program order, so the matrix core and the VALU overlap.
 //  * Workgroup tile 256 (n) x BM (tokens) x 128 (K), eight waves as 2 (n) x 4
-//    (tokens), two per SIMD, each 128 n x BM/4 tokens.  Two LDS stages at
-//    BM = 256, three at smaller BM (more bytes in flight per CU, which is what
-//    streaming weights at decode sizes needs).
+//    (tokens), two per SIMD, each 128 n x BM/4 tokens.  BM is 256 for full
+//    m-tiles and 64, 128 or 256 for an expert's last, partial one, chosen per
+//    tile.  Two LDS stages at BM = 256, three at smaller BM (more bytes in
+//    flight per CU, which is what streaming weights at decode sizes needs).
 //  * Operands move global -> LDS by LDS-DMA (global_load_lds_dwordx4, 16 bytes
 //    per lane).  Weights are pre-tiled (tile_layout.h) so each DMA instruction
 //    copies one contiguous 1 KB; activations are stored K-block-major
@@ -35,8 +36,10 @@
 //    with a stride of the grid size.  Workgroup ids are remapped so that
 //    consecutive tiles land on the same XCD (dispatch is round-robin over the
 //    8 XCDs), which keeps a weight tile shared by an expert's m-tiles in that
-//    XCD's L2.  Partial m-tiles are masked; no host-visible counts are needed.
+//    XCD's L2.  Rows past the expert's end are masked; no host-visible counts
+//    are needed.
 #include "device_common.h"
+#include "gemm_common.h"
 #include "internal.h"
 #include "tile_layout.h"
 
@@ -65,14 +68,25 @@ struct StageBuf {
   float s[kWaves * 64];
 };
 
+constexpr int kMaxBM = 256;
+
 // Tile table and epilogue exchange.
-template <int BM>
 struct Misc {
   int off[kMaxE + 1];
   int tp[kMaxE + 1];
   int scan[kThreads];
-  float amax[2][BM];
+  float amax[2][kMaxBM];
 };
+
+// LDS shared by the pipeline stages of every tile height: three stages of the
+// 128-row layout, which also hold two of the 256-row one and three of the
+// 64-row one.
+constexpr int kStageArea = 3 * (int)sizeof(StageBuf<128>);
+template <int BM>
+constexpr int stages_for() {
+  return kStageArea / (int)sizeof(StageBuf<BM>) < 4 ? kStageArea / (int)sizeof(StageBuf<BM>) : 4;
+}
+static_assert(stages_for<256>() >= 2 && stages_for<64>() >= 3, "stage area");
 
 // 32 bytes of K (logical chunks 2g and 2g+1 of the 128-byte row) of LDS row tr.
 __device__ __forceinline__ v8i lds_frag(const uint8_t* region, int tr, int g) {
@@ -80,15 +94,6 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* region, int tr, int g) {
   const int4 x0 = *(const int4*)(region + tr * BK + (((2 * g) ^ s) << 4));
   const int4 x1 = *(const int4*)(region + tr * BK + (((2 * g + 1) ^ s) << 4));
   return v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-}
-
-// Barrier without a memory fence: the waits before it are explicit (vmcnt for
-// the DMAs this wave issued); the empty asm statements keep the compiler from
-// moving LDS accesses across it.
-__device__ __forceinline__ void raw_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 // Per-lane DMA sources of one tile.
@@ -172,198 +177,160 @@ __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nx
   }
 }
 
+// One tile of BM sorted rows [m0, min(m0 + BM, m_end)) of expert e against
+// n-tile n_tile: the K loop through a ring of STAGES LDS stages carved out of
+// `area`, then the epilogue.
 template <int BM, int EPI, bool PAIRED>
-__global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p) {
-  constexpr int STAGES = BM == 256 ? 2 : 3;  // as many as the 160 KB of LDS hold
-  __shared__ __attribute__((aligned(16))) StageBuf<BM> st[STAGES];
-  __shared__ __attribute__((aligned(16))) Misc<BM> misc;
+__device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Misc& misc, int e, int n_tile, int m0,
+                                         int m_end) {
+  constexpr int STAGES = stages_for<BM>();
   constexpr int WM = BM / 4;   // tokens per wave
   constexpr int TS = WM / 16;  // 16-token sub-tiles per wave
   static_assert(TS >= 1 && BM + 2 <= kWaves * 64, "64 <= BM <= 256");
+  StageBuf<BM>* st = reinterpret_cast<StageBuf<BM>*>(area);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the thread id is made opaque per tile so that the per-lane address math of
+  // each tile height stays inside its tile instead of being hoisted out of the
+  // tile loop for all heights at once (which would spill registers)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int wave = tid >> 6, lane = tid & 63;
   const int wn = wave & 1, wt = wave >> 1;
   const int g = lane >> 4, l16 = lane & 15;
-  const int E = p.E, N = p.N, K = p.K, KB = K / BK;
+  const int N = p.N, KB = p.K / BK;
   const int I = N / 2;
   const int NB = N / 128;
   const int NT = PAIRED ? I / 128 : (N + BN - 1) / BN;
   const float* bsc = (const float*)p.b_scales;
 
-  // ---- tile table: tiles of expert e = ceil(rows_e / BM) * NT, prefix in misc.tp
-  for (int e = tid; e <= E; e += kThreads) misc.off[e] = p.offsets[e];
-  __syncthreads();
-  const int seg = (E + kThreads - 1) / kThreads;
-  const int e_lo = min(E, tid * seg), e_hi = min(E, tid * seg + seg);
-  int mine = 0;
-  for (int e = e_lo; e < e_hi; ++e) mine += ((misc.off[e + 1] - misc.off[e] + BM - 1) / BM) * NT;
-  misc.scan[tid] = mine;
-  __syncthreads();
-  for (int d = 1; d < kThreads; d <<= 1) {
-    const int v = tid >= d ? misc.scan[tid - d] : 0;
-    __syncthreads();
-    misc.scan[tid] += v;
-    __syncthreads();
+  // ---- per-lane DMA sources
+  TileSrc<BM> src;
+  src.w_tile = p.b_codes + ((size_t)e * NT + n_tile) * (size_t)KB * (BN * BK);
+  src.a_codes = p.a_codes;
+  src.a_plane = (size_t)p.a_rows * BK;
+#pragma unroll
+  for (int q = 0; q < TileSrc<BM>::A_LOADS; ++q) {
+    const int tr = wave * (BM / 8) + 8 * q + (lane >> 3);
+    const int r = min(m0 + tr, m_end - 1);
+    const int arow = p.a_row_index ? p.a_row_index[r] / p.a_row_div : r;
+    src.a_off[q] = (uint32_t)arow * BK + (uint32_t)(((lane & 7) ^ swz(tr)) << 4);
   }
   {
-    int run = misc.scan[tid] - mine;
-    for (int e = e_lo; e < e_hi; ++e) {
-      misc.tp[e] = run;
-      run += ((misc.off[e + 1] - misc.off[e] + BM - 1) / BM) * NT;
-    }
-    if (tid == kThreads - 1) misc.tp[E] = misc.scan[kThreads - 1];
-  }
-  __syncthreads();
-  const int total = misc.tp[E];
-
-  const int G = gridDim.x;
-  const int vb = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
-
-  for (int t = vb; t < total; t += G) {
-    // ---- locate the tile: the last expert e with tp[e] <= t (every lane agrees:
-    // make the values scalar)
-    int lo = 0, hi = E;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (misc.tp[mid] <= t) lo = mid; else hi = mid;
-    }
-    const int e = __builtin_amdgcn_readfirstlane(lo);
-    const int m_begin = __builtin_amdgcn_readfirstlane(misc.off[e]);
-    const int m_end = __builtin_amdgcn_readfirstlane(misc.off[e + 1]);
-    const int mt = (m_end - m_begin + BM - 1) / BM;
-    const int loc = t - __builtin_amdgcn_readfirstlane(misc.tp[e]);
-    const int n_tile = loc / mt;
-    const int m0 = m_begin + (loc % mt) * BM;
-
-    // ---- per-lane DMA sources
-    TileSrc<BM> src;
-    src.w_tile = p.b_codes + ((size_t)e * NT + n_tile) * (size_t)KB * (BN * BK);
-    src.a_codes = p.a_codes;
-    src.a_plane = (size_t)p.a_rows * BK;
-#pragma unroll
-    for (int q = 0; q < TileSrc<BM>::A_LOADS; ++q) {
-      const int tr = wave * (BM / 8) + 8 * q + (lane >> 3);
+    const int slot = 64 * wave + lane;
+    if (slot == BM || slot == BM + 1) {
+      int nb;
+      if constexpr (PAIRED) nb = slot == BM ? n_tile : I / 128 + n_tile;
+      else nb = min(n_tile * 2 + (slot - BM), NB - 1);
+      src.s_base = bsc + ((size_t)e * NB + nb) * KB;
+      src.s_stride = 1;
+    } else {
+      const int q = slot < BM ? slot / TS : 0;
+      const int ti = slot < BM ? slot % TS : 0;
+      const int tr = (q / 16) * WM + ti * 16 + (q % 16);
       const int r = min(m0 + tr, m_end - 1);
       const int arow = p.a_row_index ? p.a_row_index[r] / p.a_row_div : r;
-      src.a_off[q] = (uint32_t)arow * BK + (uint32_t)(((lane & 7) ^ swz(tr)) << 4);
+      src.s_base = (const float*)p.a_scales + arow;
+      src.s_stride = (uint32_t)p.a_rows;
     }
-    {
-      const int slot = 64 * wave + lane;
-      if (slot == BM || slot == BM + 1) {
-        int nb;
-        if constexpr (PAIRED) nb = slot == BM ? n_tile : I / 128 + n_tile;
-        else nb = min(n_tile * 2 + (slot - BM), NB - 1);
-        src.s_base = bsc + ((size_t)e * NB + nb) * KB;
-        src.s_stride = 1;
-      } else {
-        const int q = slot < BM ? slot / TS : 0;
-        const int ti = slot < BM ? slot % TS : 0;
-        const int tr = (q / 16) * WM + ti * 16 + (q % 16);
-        const int r = min(m0 + tr, m_end - 1);
-        const int arow = p.a_row_index ? p.a_row_index[r] / p.a_row_div : r;
-        src.s_base = (const float*)p.a_scales + arow;
-        src.s_stride = (uint32_t)p.a_rows;
-      }
-    }
+  }
 
-    v4f acc[8][TS];
+  v4f acc[8][TS];
 #pragma unroll
-    for (int ni = 0; ni < 8; ++ni)
+  for (int ni = 0; ni < 8; ++ni)
 #pragma unroll
-      for (int ti = 0; ti < TS; ++ti) acc[ni][ti] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int ti = 0; ti < TS; ++ti) acc[ni][ti] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    __syncthreads();  // the previous tile's LDS readers are done
+  __syncthreads();  // the previous tile's LDS readers are done
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) issue_stage<BM>(&st[s], src, min(s, KB - 1), wave, lane);
-    for (int kb = 0; kb < KB; kb += STAGES) {
+  for (int s = 0; s < STAGES - 1; ++s) issue_stage<BM>(&st[s], src, min(s, KB - 1), wave, lane);
+  for (int kb = 0; kb < KB; kb += STAGES) {
 #pragma unroll
-      for (int j = 0; j < STAGES; ++j)
-        if (kb + j < KB)
-          k_step<BM, PAIRED, STAGES>(&st[j], &st[(j + STAGES - 1) % STAGES], src, kb + j, KB, wave, lane, acc);
-    }
-    wait_vmcnt<0>();  // the trailing repeat DMAs land before the stages are reused
+    for (int j = 0; j < STAGES; ++j)
+      if (kb + j < KB)
+        k_step<BM, PAIRED, STAGES>(&st[j], &st[(j + STAGES - 1) % STAGES], src, kb + j, KB, wave, lane, acc);
+  }
+  wait_vmcnt<0>();  // the trailing repeat DMAs land before the stages are reused
 
-    // ---- epilogues
-    if constexpr (EPI == kEpiStoreF32) {
+  // ---- epilogues
+  if constexpr (EPI == kEpiStoreF32) {
 #pragma unroll
-      for (int ti = 0; ti < TS; ++ti) {
-        const int r = m0 + wt * WM + ti * 16 + l16;
-        if (r < m_end) {
+    for (int ti = 0; ti < TS; ++ti) {
+      const int r = m0 + wt * WM + ti * 16 + l16;
+      if (r < m_end) {
 #pragma unroll
-          for (int ni = 0; ni < 8; ++ni) {
-            int n;
-            if constexpr (PAIRED) {
-              const int h = n_tile * 128 + 16 * (wn * 4 + (ni >> 1)) + 4 * g;
-              n = (ni & 1) ? I + h : h;
-            } else {
-              n = n_tile * BN + wn * 128 + ni * 16 + 4 * g;
-            }
-            if (n < N) *(v4f*)(p.c_f32 + (size_t)r * N + n) = acc[ni][ti];
+        for (int ni = 0; ni < 8; ++ni) {
+          int n;
+          if constexpr (PAIRED) {
+            const int h = n_tile * 128 + 16 * (wn * 4 + (ni >> 1)) + 4 * g;
+            n = (ni & 1) ? I + h : h;
+          } else {
+            n = n_tile * BN + wn * 128 + ni * 16 + 4 * g;
           }
+          if (n < N) *(v4f*)(p.c_f32 + (size_t)r * N + n) = acc[ni][ti];
         }
       }
-    } else if constexpr (EPI == kEpiSwiGLUQuant) {
-      static_assert(PAIRED, "SwiGLU needs the paired gate/up layout");
-      // h of pair q, sub-tile ti, element i (recomputed in the second pass
-      // instead of being held across the barrier)
-      auto hval = [&](int q, int ti, int i) {
-        float gv = acc[2 * q][ti][i];
-        float uv = acc[2 * q + 1][ti][i];
-        if (p.has_limit) {
-          gv = __builtin_fminf(gv, p.limit);
-          uv = __builtin_fminf(__builtin_fmaxf(uv, -p.limit), p.limit);
-        }
-        return gv / (1.0f + __expf(-gv)) * uv;
-      };
-#pragma unroll
-      for (int ti = 0; ti < TS; ++ti) {
-        float m = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(hval(q, ti, i)));
-        m = wave_max_xor(m, 16);
-        m = wave_max_xor(m, 32);
-        if (g == 0) misc.amax[wn][wt * WM + ti * 16 + l16] = m;
+    }
+  } else if constexpr (EPI == kEpiSwiGLUQuant) {
+    static_assert(PAIRED, "SwiGLU needs the paired gate/up layout");
+    // h of pair q, sub-tile ti, element i (recomputed in the second pass
+    // instead of being held across the barrier)
+    auto hval = [&](int q, int ti, int i) {
+      float gv = acc[2 * q][ti][i];
+      float uv = acc[2 * q + 1][ti][i];
+      if (p.has_limit) {
+        gv = __builtin_fminf(gv, p.limit);
+        uv = __builtin_fminf(__builtin_fmaxf(uv, -p.limit), p.limit);
       }
-      __syncthreads();
-      // h codes go to the K-block-major layout [I/128][max_rows][128] that the
-      // down GEMM reads; the tile's 128 outputs are exactly plane n_tile
-      uint8_t* plane = p.h_codes + (size_t)n_tile * p.max_rows * 128;
+      return gv / (1.0f + __expf(-gv)) * uv;
+    };
 #pragma unroll
-      for (int ti = 0; ti < TS; ++ti) {
-        const int tt = wt * WM + ti * 16 + l16;
-        const float amax = __builtin_fmaxf(misc.amax[0][tt], misc.amax[1][tt]);
-        const float s = fp8_block_scale(amax);
-        const float inv = 1.0f / s;
-        const int r = m0 + tt;
-        if (r < m_end) {
+    for (int ti = 0; ti < TS; ++ti) {
+      float m = 0.0f;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t code =
-                e4m3x4(hval(q, ti, 0) * inv, hval(q, ti, 1) * inv, hval(q, ti, 2) * inv, hval(q, ti, 3) * inv);
-            *(uint32_t*)(plane + (size_t)r * 128 + 16 * (wn * 4 + q) + 4 * g) = code;
-          }
-          if (wn == 0 && g == 0) ((float*)p.h_scales)[(size_t)n_tile * p.max_rows + r] = s;
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(hval(q, ti, i)));
+      m = wave_max_xor(m, 16);
+      m = wave_max_xor(m, 32);
+      if (g == 0) misc.amax[wn][wt * WM + ti * 16 + l16] = m;
+    }
+    __syncthreads();
+    // h codes go to the K-block-major layout [I/128][max_rows][128] that the
+    // down GEMM reads; the tile's 128 outputs are exactly plane n_tile
+    uint8_t* plane = p.h_codes + (size_t)n_tile * p.max_rows * 128;
+#pragma unroll
+    for (int ti = 0; ti < TS; ++ti) {
+      const int tt = wt * WM + ti * 16 + l16;
+      const float amax = __builtin_fmaxf(misc.amax[0][tt], misc.amax[1][tt]);
+      const float s = fp8_block_scale(amax);
+      const float inv = 1.0f / s;
+      const int r = m0 + tt;
+      if (r < m_end) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t code =
+              e4m3x4(hval(q, ti, 0) * inv, hval(q, ti, 1) * inv, hval(q, ti, 2) * inv, hval(q, ti, 3) * inv);
+          *(uint32_t*)(plane + (size_t)r * 128 + 16 * (wn * 4 + q) + 4 * g) = code;
         }
+        if (wn == 0 && g == 0) ((float*)p.h_scales)[(size_t)n_tile * p.max_rows + r] = s;
       }
-    } else {  // kEpiWeightedScatter
+    }
+  } else {  // kEpiWeightedScatter
 #pragma unroll
-      for (int ti = 0; ti < TS; ++ti) {
-        const int r = m0 + wt * WM + ti * 16 + l16;
-        if (r < m_end) {
-          const int slot = p.slot_of_row[r];
-          const float w = p.top_k_weights[slot];
+    for (int ti = 0; ti < TS; ++ti) {
+      const int r = m0 + wt * WM + ti * 16 + l16;
+      if (r < m_end) {
+        const int slot = p.slot_of_row[r];
+        const float w = p.top_k_weights[slot];
 #pragma unroll
-          for (int ni = 0; ni < 8; ++ni) {
-            const int n = n_tile * BN + wn * 128 + ni * 16 + 4 * g;
-            if (n < N) {
-              const v4f v = acc[ni][ti] * w;
-              uint2 o;
-              o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-              o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-              *(uint2*)(p.slot_out + (size_t)slot * N + n) = o;
-            }
+        for (int ni = 0; ni < 8; ++ni) {
+          const int n = n_tile * BN + wn * 128 + ni * 16 + 4 * g;
+          if (n < N) {
+            const v4f v = acc[ni][ti] * w;
+            uint2 o;
+            o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+            o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+            *(uint2*)(p.slot_out + (size_t)slot * N + n) = o;
           }
         }
       }
@@ -371,11 +338,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p
   }
 }
 
-template <int BM, int EPI, bool PAIRED>
+// Persistent kernel.  An expert's rows are cut into 256-row m-tiles; the last,
+// partial one runs at the smallest height of {64, 128, 256} that covers it, so
+// little MFMA work goes to padding rows while the number of tiles, and so the
+// weight traffic, stays that of 256-row tiles.
+template <int EPI, bool PAIRED>
+__global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t area[kStageArea];
+  __shared__ __attribute__((aligned(16))) Misc misc;
+  const int E = p.E, N = p.N;
+  const int NT = PAIRED ? (N / 2) / 128 : (N + BN - 1) / BN;
+  const int total = build_tile_table<kThreads>(p.offsets, E, kMaxBM, NT, misc.off, misc.tp, misc.scan);
+  const int G = gridDim.x;
+  for (int t = xcd_virtual_block(); t < total; t += G) {
+    const TileCoord tc = locate_tile(t, E, kMaxBM, misc.off, misc.tp);
+    const int left = tc.m_end - tc.m0;
+    if (left > 128)
+      run_tile<256, EPI, PAIRED>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end);
+    else if (left > 64)
+      run_tile<128, EPI, PAIRED>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end);
+    else
+      run_tile<64, EPI, PAIRED>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end);
+  }
+}
+
+template <int EPI, bool PAIRED>
 hipError_t launch_one(const GemmParams& p, int num_cus, hipStream_t stream) {
-  auto kern = gemm_fp8_b128_kernel<BM, EPI, PAIRED>;
+  auto kern = gemm_fp8_b128_kernel<EPI, PAIRED>;
   const int NT = PAIRED ? (p.N / 2) / 128 : (p.N + BN - 1) / BN;
-  const long bound = ((long)(p.max_rows + BM - 1) / BM + p.E) * NT;
+  const long bound = ((long)(p.max_rows + kMaxBM - 1) / kMaxBM + p.E) * NT;
   long grid = bound < num_cus ? bound : num_cus;
   if (grid >= 8) grid = grid / 8 * 8;
   if (grid < 1) grid = 1;
@@ -383,21 +374,13 @@ hipError_t launch_one(const GemmParams& p, int num_cus, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BM>
-hipError_t dispatch_epi(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream) {
-  if (epi == kEpiSwiGLUQuant) return launch_one<BM, kEpiSwiGLUQuant, true>(p, num_cus, stream);
-  if (epi == kEpiWeightedScatter) return launch_one<BM, kEpiWeightedScatter, false>(p, num_cus, stream);
-  if (paired) return launch_one<BM, kEpiStoreF32, true>(p, num_cus, stream);
-  return launch_one<BM, kEpiStoreF32, false>(p, num_cus, stream);
-}
-
 }  // namespace
 
 hipError_t launch_gemm_fp8_b128(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream) {
-  const long avg_rows = p.E > 0 ? (long)p.max_rows / p.E : p.max_rows;
-  if (avg_rows >= 192) return dispatch_epi<256>(p, epi, paired, num_cus, stream);
-  if (avg_rows >= 96) return dispatch_epi<128>(p, epi, paired, num_cus, stream);
-  return dispatch_epi<64>(p, epi, paired, num_cus, stream);
+  if (epi == kEpiSwiGLUQuant) return launch_one<kEpiSwiGLUQuant, true>(p, num_cus, stream);
+  if (epi == kEpiWeightedScatter) return launch_one<kEpiWeightedScatter, false>(p, num_cus, stream);
+  if (paired) return launch_one<kEpiStoreF32, true>(p, num_cus, stream);
+  return launch_one<kEpiStoreF32, false>(p, num_cus, stream);
 }
 
 }  // namespace moe

@@ -16,8 +16,9 @@
 // [32 g, 32 g + 32) as 32 nibbles; an FP8 lane of group g holds K elements
 // [16 g, 16 g + 16) in bytes 0-15 and [64 + 16 g, 64 + 16 g + 16) in bytes 16-31;
 // the scale byte of lane group g applies to K elements [32 g, 32 g + 32).
-// Tiles: 256 weight rows x BM tokens x 128 K, eight waves (2 x 4), two or four
-// LDS stages fed by LDS-DMA from the tiled weights (64-byte rows) and the K-block-major
+// Tiles: 256 weight rows x BM tokens x 128 K (BM = 256, or 64 / 128 / 256 for an
+// expert's last, partial m-tile), eight waves (2 x 4), two or four LDS stages
+// fed by LDS-DMA from the tiled weights (64-byte rows) and the K-block-major
 // activations; persistent XCD-aware tile walk as in the FP8 kernel.
 #include "gemm_common.h"
 #include "internal.h"
@@ -46,12 +47,23 @@ struct StageBuf {
   uint8_t spare[256];        // target of the waves with no scale to fetch
 };
 
-template <int BM>
+constexpr int kMaxBM = 256;
+
 struct Misc {
   int off[kMaxE + 1];
   int tp[kMaxE + 1];
   int scan[kThreads];
 };
+
+// LDS shared by the pipeline stages of every tile height: four stages of the
+// 128-row layout, which also hold two of the 256-row one (a third would spill
+// registers) and four of the 64-row one.
+constexpr int kStageArea = 4 * (int)sizeof(StageBuf<128>);
+template <int BM>
+constexpr int stages_for() {
+  return kStageArea / (int)sizeof(StageBuf<BM>) < 4 ? kStageArea / (int)sizeof(StageBuf<BM>) : 4;
+}
+static_assert(stages_for<256>() == 2 && stages_for<64>() == 4, "stage area");
 
 template <int BM>
 struct TileSrc {
@@ -134,142 +146,141 @@ __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nx
   }
 }
 
+// One tile of BM sorted rows [m0, min(m0 + BM, m_end)) of expert e against
+// n-tile n_tile, through a ring of STAGES LDS stages carved out of `area`.
 template <int BM, int EPI, bool PAIRED>
-__global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmParams p) {
-  constexpr int STAGES = BM == 256 ? 2 : 4;  // at BM = 256 a third stage would spill registers
-  __shared__ __attribute__((aligned(16))) StageBuf<BM> st[STAGES];
-  __shared__ __attribute__((aligned(16))) Misc<BM> misc;
+__device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, int e, int n_tile, int m0, int m_end) {
+  constexpr int STAGES = stages_for<BM>();
   constexpr int WM = BM / 4;
   constexpr int TS = WM / 16;
   static_assert(TS >= 1 && BM <= 256, "64 <= BM <= 256");
+  StageBuf<BM>* st = reinterpret_cast<StageBuf<BM>*>(area);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the thread id is made opaque per tile so that the per-lane address math of
+  // each tile height stays inside its tile instead of being hoisted out of the
+  // tile loop for all heights at once (which would spill registers)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int wave = tid >> 6, lane = tid & 63;
   const int wn = wave & 1, wt = wave >> 1;
   const int g = lane >> 4, l16 = lane & 15;
-  const int E = p.E, N = p.N, K = p.K, KB = K / 128;
+  const int N = p.N, KB = p.K / 128;
   const int I = N / 2;
   const int NT = PAIRED ? I / 128 : (N + BN - 1) / BN;
 
-  const int total = build_tile_table<kThreads>(p.offsets, E, BM, NT, misc.off, misc.tp, misc.scan);
-  const int G = gridDim.x;
-  for (int t = xcd_virtual_block(); t < total; t += G) {
-    const TileCoord tc = locate_tile(t, E, BM, misc.off, misc.tp);
-    const int e = tc.e, n_tile = tc.n_tile, m0 = tc.m0, m_end = tc.m_end;
+  TileSrc<BM> src;
+  const size_t tile = (size_t)e * NT + n_tile;
+  src.w_tile = p.b_codes + tile * (size_t)KB * (BN * kWRow);
+  src.ws_tile = (const uint8_t*)p.b_scales + tile * (size_t)KB * (BN * 4);
+  src.a_codes = p.a_codes;
+  src.a_plane = (size_t)p.a_rows * kARow;
+#pragma unroll
+  for (int q = 0; q < TileSrc<BM>::A_LOADS; ++q) {
+    const int tr = wave * (BM / 8) + 8 * q + (lane >> 3);
+    const int r = min(m0 + tr, m_end - 1);
+    const int arow = p.a_row_index ? p.a_row_index[r] / p.a_row_div : r;
+    src.a_off[q] = (uint32_t)arow * kARow + (uint32_t)(((lane & 7) ^ swz(tr)) << 4);
+  }
+  src.as_base = (const uint8_t*)p.a_scales;
+  src.as_plane = (size_t)p.a_rows * 4;
+  {
+    const int tr = (wave % (BM / 64 > 0 ? BM / 64 : 1)) * 64 + lane;  // rows of the waves that load scales
+    const int r = min(m0 + min(tr, BM - 1), m_end - 1);
+    const int arow = p.a_row_index ? p.a_row_index[r] / p.a_row_div : r;
+    src.as_off = (uint32_t)arow * 4;
+  }
 
-    TileSrc<BM> src;
-    const size_t tile = (size_t)e * NT + n_tile;
-    src.w_tile = p.b_codes + tile * (size_t)KB * (BN * kWRow);
-    src.ws_tile = (const uint8_t*)p.b_scales + tile * (size_t)KB * (BN * 4);
-    src.a_codes = p.a_codes;
-    src.a_plane = (size_t)p.a_rows * kARow;
+  v4f acc[8][TS];
 #pragma unroll
-    for (int q = 0; q < TileSrc<BM>::A_LOADS; ++q) {
-      const int tr = wave * (BM / 8) + 8 * q + (lane >> 3);
-      const int r = min(m0 + tr, m_end - 1);
-      const int arow = p.a_row_index ? p.a_row_index[r] / p.a_row_div : r;
-      src.a_off[q] = (uint32_t)arow * kARow + (uint32_t)(((lane & 7) ^ swz(tr)) << 4);
-    }
-    src.as_base = (const uint8_t*)p.a_scales;
-    src.as_plane = (size_t)p.a_rows * 4;
-    {
-      const int tr = (wave % (BM / 64 > 0 ? BM / 64 : 1)) * 64 + lane;  // rows of the waves that load scales
-      const int r = min(m0 + min(tr, BM - 1), m_end - 1);
-      const int arow = p.a_row_index ? p.a_row_index[r] / p.a_row_div : r;
-      src.as_off = (uint32_t)arow * 4;
-    }
+  for (int ni = 0; ni < 8; ++ni)
+#pragma unroll
+    for (int ti = 0; ti < TS; ++ti) acc[ni][ti] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    v4f acc[8][TS];
+  __syncthreads();
 #pragma unroll
-    for (int ni = 0; ni < 8; ++ni)
+  for (int s = 0; s < STAGES - 1; ++s) issue_stage<BM>(&st[s], src, min(s, KB - 1), wave, lane);
+  for (int kb = 0; kb < KB; kb += STAGES) {
 #pragma unroll
-      for (int ti = 0; ti < TS; ++ti) acc[ni][ti] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < STAGES; ++j)
+      if (kb + j < KB) k_step<BM, STAGES>(&st[j], &st[(j + STAGES - 1) % STAGES], src, kb + j, KB, wave, lane, acc);
+  }
+  wait_vmcnt<0>();
 
-    __syncthreads();
+  if constexpr (EPI == kEpiStoreF32) {
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) issue_stage<BM>(&st[s], src, min(s, KB - 1), wave, lane);
-    for (int kb = 0; kb < KB; kb += STAGES) {
+    for (int ti = 0; ti < TS; ++ti) {
+      const int r = m0 + wt * WM + ti * 16 + l16;
+      if (r < m_end) {
 #pragma unroll
-      for (int j = 0; j < STAGES; ++j)
-        if (kb + j < KB) k_step<BM, STAGES>(&st[j], &st[(j + STAGES - 1) % STAGES], src, kb + j, KB, wave, lane, acc);
-    }
-    wait_vmcnt<0>();
-
-    if constexpr (EPI == kEpiStoreF32) {
-#pragma unroll
-      for (int ti = 0; ti < TS; ++ti) {
-        const int r = m0 + wt * WM + ti * 16 + l16;
-        if (r < m_end) {
-#pragma unroll
-          for (int ni = 0; ni < 8; ++ni) {
-            int n;
-            if constexpr (PAIRED) {
-              const int h = n_tile * 128 + 16 * (wn * 4 + (ni >> 1)) + 4 * g;
-              n = (ni & 1) ? I + h : h;
-            } else {
-              n = n_tile * BN + wn * 128 + ni * 16 + 4 * g;
-            }
-            if (n < N) *(v4f*)(p.c_f32 + (size_t)r * N + n) = acc[ni][ti];
+        for (int ni = 0; ni < 8; ++ni) {
+          int n;
+          if constexpr (PAIRED) {
+            const int h = n_tile * 128 + 16 * (wn * 4 + (ni >> 1)) + 4 * g;
+            n = (ni & 1) ? I + h : h;
+          } else {
+            n = n_tile * BN + wn * 128 + ni * 16 + 4 * g;
           }
+          if (n < N) *(v4f*)(p.c_f32 + (size_t)r * N + n) = acc[ni][ti];
         }
       }
-    } else if constexpr (EPI == kEpiSwiGLUQuant) {
-      static_assert(PAIRED, "SwiGLU needs the paired gate/up layout");
-      auto hval = [&](int q, int ti, int i) {
-        float gv = acc[2 * q][ti][i];
-        float uv = acc[2 * q + 1][ti][i];
-        if (p.has_limit) {
-          gv = __builtin_fminf(gv, p.limit);
-          uv = __builtin_fminf(__builtin_fmaxf(uv, -p.limit), p.limit);
-        }
-        return gv / (1.0f + __expf(-gv)) * uv;
-      };
-      // this wave's 64 outputs of the tile's 128 are the 32-wide MX blocks 2 wn and
-      // 2 wn + 1, each made of pairs q = 2b and 2b + 1: the block amax needs only
-      // this wave (xor over the four lane groups)
-      uint8_t* plane = p.h_codes + (size_t)n_tile * p.max_rows * 128;
-      uint8_t* splane = (uint8_t*)p.h_scales + (size_t)n_tile * p.max_rows * 4;
+    }
+  } else if constexpr (EPI == kEpiSwiGLUQuant) {
+    static_assert(PAIRED, "SwiGLU needs the paired gate/up layout");
+    auto hval = [&](int q, int ti, int i) {
+      float gv = acc[2 * q][ti][i];
+      float uv = acc[2 * q + 1][ti][i];
+      if (p.has_limit) {
+        gv = __builtin_fminf(gv, p.limit);
+        uv = __builtin_fminf(__builtin_fmaxf(uv, -p.limit), p.limit);
+      }
+      return gv / (1.0f + __expf(-gv)) * uv;
+    };
+    // this wave's 64 outputs of the tile's 128 are the 32-wide MX blocks 2 wn and
+    // 2 wn + 1, each made of pairs q = 2b and 2b + 1: the block amax needs only
+    // this wave (xor over the four lane groups)
+    uint8_t* plane = p.h_codes + (size_t)n_tile * p.max_rows * 128;
+    uint8_t* splane = (uint8_t*)p.h_scales + (size_t)n_tile * p.max_rows * 4;
 #pragma unroll
-      for (int ti = 0; ti < TS; ++ti) {
-        const int r = m0 + wt * WM + ti * 16 + l16;
+    for (int ti = 0; ti < TS; ++ti) {
+      const int r = m0 + wt * WM + ti * 16 + l16;
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          float m = 0.0f;
+      for (int b = 0; b < 2; ++b) {
+        float m = 0.0f;
 #pragma unroll
-          for (int q = 2 * b; q < 2 * b + 2; ++q)
+        for (int q = 2 * b; q < 2 * b + 2; ++q)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(hval(q, ti, i)));
-          m = wave_max_xor(m, 16);
-          m = wave_max_xor(m, 32);
-          const int ex = mx_block_exponent(m);
-          if (r < m_end) {
+          for (int i = 0; i < 4; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(hval(q, ti, i)));
+        m = wave_max_xor(m, 16);
+        m = wave_max_xor(m, 32);
+        const int ex = mx_block_exponent(m);
+        if (r < m_end) {
 #pragma unroll
-            for (int q = 2 * b; q < 2 * b + 2; ++q) {
-              const uint32_t code =
-                  e4m3x4(__builtin_ldexpf(hval(q, ti, 0), -ex), __builtin_ldexpf(hval(q, ti, 1), -ex),
-                         __builtin_ldexpf(hval(q, ti, 2), -ex), __builtin_ldexpf(hval(q, ti, 3), -ex));
-              *(uint32_t*)(plane + (size_t)r * 128 + 16 * (wn * 4 + q) + 4 * g) = code;
-            }
-            if (g == 0) splane[(size_t)r * 4 + wn * 2 + b] = (uint8_t)(ex + 127);
+          for (int q = 2 * b; q < 2 * b + 2; ++q) {
+            const uint32_t code =
+                e4m3x4(__builtin_ldexpf(hval(q, ti, 0), -ex), __builtin_ldexpf(hval(q, ti, 1), -ex),
+                       __builtin_ldexpf(hval(q, ti, 2), -ex), __builtin_ldexpf(hval(q, ti, 3), -ex));
+            *(uint32_t*)(plane + (size_t)r * 128 + 16 * (wn * 4 + q) + 4 * g) = code;
           }
+          if (g == 0) splane[(size_t)r * 4 + wn * 2 + b] = (uint8_t)(ex + 127);
         }
       }
-    } else {  // kEpiWeightedScatter
+    }
+  } else {  // kEpiWeightedScatter
 #pragma unroll
-      for (int ti = 0; ti < TS; ++ti) {
-        const int r = m0 + wt * WM + ti * 16 + l16;
-        if (r < m_end) {
-          const int slot = p.slot_of_row[r];
-          const float w = p.top_k_weights[slot];
+    for (int ti = 0; ti < TS; ++ti) {
+      const int r = m0 + wt * WM + ti * 16 + l16;
+      if (r < m_end) {
+        const int slot = p.slot_of_row[r];
+        const float w = p.top_k_weights[slot];
 #pragma unroll
-          for (int ni = 0; ni < 8; ++ni) {
-            const int n = n_tile * BN + wn * 128 + ni * 16 + 4 * g;
-            if (n < N) {
-              const v4f v = acc[ni][ti] * w;
-              uint2 o;
-              o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-              o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-              *(uint2*)(p.slot_out + (size_t)slot * N + n) = o;
-            }
+        for (int ni = 0; ni < 8; ++ni) {
+          const int n = n_tile * BN + wn * 128 + ni * 16 + 4 * g;
+          if (n < N) {
+            const v4f v = acc[ni][ti] * w;
+            uint2 o;
+            o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+            o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+            *(uint2*)(p.slot_out + (size_t)slot * N + n) = o;
           }
         }
       }
@@ -277,11 +288,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmParams p) {
   }
 }
 
-template <int BM, int EPI, bool PAIRED>
+// Persistent kernel; the last, partial m-tile of an expert runs at the
+// smallest height of {64, 128, 256} that covers it (as in the FP8 kernel).
+template <int EPI, bool PAIRED>
+__global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t area[kStageArea];
+  __shared__ __attribute__((aligned(16))) Misc misc;
+  const int E = p.E, N = p.N;
+  const int NT = PAIRED ? (N / 2) / 128 : (N + BN - 1) / BN;
+  const int total = build_tile_table<kThreads>(p.offsets, E, kMaxBM, NT, misc.off, misc.tp, misc.scan);
+  const int G = gridDim.x;
+  for (int t = xcd_virtual_block(); t < total; t += G) {
+    const TileCoord tc = locate_tile(t, E, kMaxBM, misc.off, misc.tp);
+    const int left = tc.m_end - tc.m0;
+    if (left > 128)
+      run_tile<256, EPI, PAIRED>(p, area, tc.e, tc.n_tile, tc.m0, tc.m_end);
+    else if (left > 64)
+      run_tile<128, EPI, PAIRED>(p, area, tc.e, tc.n_tile, tc.m0, tc.m_end);
+    else
+      run_tile<64, EPI, PAIRED>(p, area, tc.e, tc.n_tile, tc.m0, tc.m_end);
+  }
+}
+
+template <int EPI, bool PAIRED>
 hipError_t launch_one(const GemmParams& p, int num_cus, hipStream_t stream) {
-  auto kern = gemm_mx_kernel<BM, EPI, PAIRED>;
+  auto kern = gemm_mx_kernel<EPI, PAIRED>;
   const int NT = PAIRED ? (p.N / 2) / 128 : (p.N + BN - 1) / BN;
-  const long bound = ((long)(p.max_rows + BM - 1) / BM + p.E) * NT;
+  const long bound = ((long)(p.max_rows + kMaxBM - 1) / kMaxBM + p.E) * NT;
   long grid = bound < num_cus ? bound : num_cus;
   if (grid >= 8) grid = grid / 8 * 8;
   if (grid < 1) grid = 1;
@@ -289,21 +322,13 @@ hipError_t launch_one(const GemmParams& p, int num_cus, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BM>
-hipError_t dispatch_epi(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream) {
-  if (epi == kEpiSwiGLUQuant) return launch_one<BM, kEpiSwiGLUQuant, true>(p, num_cus, stream);
-  if (epi == kEpiWeightedScatter) return launch_one<BM, kEpiWeightedScatter, false>(p, num_cus, stream);
-  if (paired) return launch_one<BM, kEpiStoreF32, true>(p, num_cus, stream);
-  return launch_one<BM, kEpiStoreF32, false>(p, num_cus, stream);
-}
-
 }  // namespace
 
 hipError_t launch_gemm_mx(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream) {
-  const long avg_rows = p.E > 0 ? (long)p.max_rows / p.E : p.max_rows;
-  if (avg_rows >= 192) return dispatch_epi<256>(p, epi, paired, num_cus, stream);
-  if (avg_rows >= 96) return dispatch_epi<128>(p, epi, paired, num_cus, stream);
-  return dispatch_epi<64>(p, epi, paired, num_cus, stream);
+  if (epi == kEpiSwiGLUQuant) return launch_one<kEpiSwiGLUQuant, true>(p, num_cus, stream);
+  if (epi == kEpiWeightedScatter) return launch_one<kEpiWeightedScatter, false>(p, num_cus, stream);
+  if (paired) return launch_one<kEpiStoreF32, true>(p, num_cus, stream);
+  return launch_one<kEpiStoreF32, false>(p, num_cus, stream);
 }
 
 }  // namespace moe
