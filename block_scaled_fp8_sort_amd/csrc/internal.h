@@ -34,8 +34,11 @@ struct GemmParams {
 enum Epilogue { kEpiStoreF32 = 0, kEpiSwiGLUQuant = 1, kEpiWeightedScatter = 2 };
 
 size_t route_sort_lds_bytes(int32_t E);
+// Device workspace the sort of S slots needs (0 for the one-workgroup path).
+size_t route_sort_ws_bytes(int32_t S, int32_t E);
 hipError_t launch_route_sort(const int32_t* ids, int32_t S, int32_t E, int32_t expert_begin, int32_t* sorted_slot,
-                             int32_t* offsets, int32_t* slot_pos, int32_t* invalid_count, hipStream_t stream);
+                             int32_t* offsets, int32_t* slot_pos, int32_t* invalid_count, void* ws,
+                             hipStream_t stream);
 hipError_t launch_quant_act(const uint16_t* x, int32_t rows, int32_t H, int fmt, uint8_t* codes, void* scales,
                             hipStream_t stream);
 // epi: Epilogue; paired: gate/up row pairing of B (used with kEpiSwiGLUQuant and

@@ -110,7 +110,7 @@ moe_status hip_status(hipError_t e, const char* what) {
 
 // ---------------------------------------------------------- forward workspace
 struct FwdLayout {
-  size_t sorted_slot, offsets, act_codes, act_scales, h_codes, h_scales, slot_out, total;
+  size_t sorted_slot, offsets, act_codes, act_scales, h_codes, h_scales, slot_out, sort_ws, total;
 };
 
 FwdLayout fwd_layout(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I, int fmt) {
@@ -126,6 +126,7 @@ FwdLayout fwd_layout(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I, int 
   L.h_codes = o; o = align_up(o + S * I, A);
   L.h_scales = o; o = align_up(o + (mx ? S * (I / 32) : 4 * S * (I / 128)), A);
   L.slot_out = o; o = align_up(o + 2 * S * H, A);
+  L.sort_ws = o; o = align_up(o + moe::route_sort_ws_bytes((int32_t)S, E), A);
   L.total = o;
   return L;
 }
@@ -226,23 +227,22 @@ const char* moe_status_string(moe_status s) {
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 size_t moe_route_sort_workspace(int32_t T, int32_t k, int32_t E) {
-  (void)T;
-  (void)k;
-  (void)E;
-  return 0;  // the sort runs in one workgroup's LDS
+  if (T < 0 || k < 1 || k > kMaxK || E < 1 || E > kMaxE || (int64_t)T * k >= (int64_t)1 << 31) return 0;
+  return moe::route_sort_ws_bytes(T * k, E);
 }
 
 moe_status moe_route_sort(const int32_t* top_k_index, int32_t T, int32_t k, int32_t E, int32_t expert_begin,
                           int32_t* sorted_slot, int32_t* expert_offsets, int32_t* slot_pos, int32_t* invalid_count,
                           void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
   if (T < 0) return fail(MOE_ERR_SHAPE, "T=%d < 0", T);
   if (k < 1 || k > kMaxK) return fail(MOE_ERR_SHAPE, "k=%d outside [1, %d]", k, kMaxK);
   if (E < 1 || E > kMaxE) return fail(MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, kMaxE);
   if ((int64_t)T * k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "T*k must stay below 2^31");
   if (!expert_offsets) return fail(MOE_ERR_NULL, "expert_offsets is NULL");
   if (T > 0 && (!top_k_index || !sorted_slot)) return fail(MOE_ERR_NULL, "top_k_index / sorted_slot is NULL");
-  if (ws_bytes < moe_route_sort_workspace(T, k, E)) return fail(MOE_ERR_WORKSPACE, "workspace too small");
+  const size_t ws_need = moe_route_sort_workspace(T, k, E);
+  if (ws_need > 0 && (!ws || ws_bytes < ws_need))
+    return fail(MOE_ERR_WORKSPACE, "workspace holds %zu bytes, %zu needed", ws ? ws_bytes : (size_t)0, ws_need);
   if (T > 0 && ((const void*)top_k_index == (const void*)sorted_slot ||
                 (const void*)top_k_index == (const void*)slot_pos))
     return fail(MOE_ERR_UNSUPPORTED, "outputs must not alias top_k_index");
@@ -253,8 +253,9 @@ moe_status moe_route_sort(const int32_t* top_k_index, int32_t T, int32_t k, int3
                   std::make_pair((const void*)sorted_slot, "sorted_slot"),
                   std::make_pair((const void*)expert_offsets, "expert_offsets")})
     if ((st = check_ptr(pr.first, dev, pr.second)) != MOE_OK) return st;
+  if (ws_need > 0 && (st = check_ptr(ws, dev, "workspace")) != MOE_OK) return st;
   st = hip_status(moe::launch_route_sort(top_k_index, T * k, E, expert_begin, sorted_slot, expert_offsets, slot_pos,
-                                         invalid_count, stream),
+                                         invalid_count, ws, stream),
                   "route sort launch");
   return st == MOE_OK ? ok() : st;
 }
@@ -425,7 +426,7 @@ moe_status moe_experts_forward(const moe_weights* w, const uint16_t* hidden_stat
   const int32_t expert_begin = opt ? opt->expert_begin : 0;
 
   hipError_t he = moe::launch_route_sort(top_k_index, S, E, expert_begin, sorted_slot, offsets, nullptr,
-                                         opt ? opt->invalid_count : nullptr, stream);
+                                         opt ? opt->invalid_count : nullptr, base + L.sort_ws, stream);
   if (he != hipSuccess) return hip_status(he, "route sort launch");
   he = moe::launch_quant_act(hidden_states, T, H, w->fmt, act_codes, act_scales, stream);
   if (he != hipSuccess) return hip_status(he, "quant launch");

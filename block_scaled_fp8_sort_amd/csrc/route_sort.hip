@@ -16,8 +16,15 @@
 //     start[w][key] + (number of lower lanes with its key), and the lowest such
 //     lane then advances start[w][key].  Order inside a key is therefore slot
 //     order, as a stable sort requires.
-// The work is latency-bound (S <= a few hundred thousand int32), so one
-// workgroup is enough and no global synchronization is needed.
+// Small inputs (decode) run all three steps in one workgroup.  Large inputs
+// split the slots over up to kMaxChunks wave-sized chunks in three launches:
+//  A. each wave histograms its chunk and writes it key-major, hist[key][chunk];
+//  B. one workgroup turns hist into its flat exclusive prefix sum, which is
+//     exactly start[key][chunk] (all smaller keys, then the same key in earlier
+//     chunks), and reads offsets[e] off start[e][0]; the chunk count is capped
+//     so that hist fits in LDS, where the scan runs;
+//  C. each wave loads its starts and runs step 3 above on its chunk.
+// The result is the same unique permutation in both cases.
 #include "device_common.h"
 #include "internal.h"
 
@@ -28,9 +35,159 @@ namespace {
 constexpr int kSortWaves = 16;
 constexpr int kSortThreads = kSortWaves * kWave;
 
+constexpr int kMaxChunks = 256;       // chunks (one wave each) of the multi-block path
+constexpr int kScanInts = 32768;      // (E + 1) * chunks, at most: the scan runs in LDS
+constexpr int kMinChunk = 256;        // slots per chunk, at least
+constexpr int kMultiBlockFrom = 16384;  // S at which the multi-block path takes over
+constexpr int kChunkWaves = 4;        // waves per workgroup in steps A and C
+constexpr int kScanThreads = 1024;
+
 __device__ __forceinline__ int sort_key(int32_t id, int32_t E, int32_t expert_begin) {
   const int64_t local = (int64_t)id - expert_begin;
   return (local >= 0 && local < E) ? (int)local : E;
+}
+
+// Stable scatter of slots [c_begin, c_end) by one wave; start[key] is where the
+// wave's next slot of that key goes (advanced in place, in LDS).
+__device__ __forceinline__ void scatter_chunk(const int32_t* __restrict__ ids, int c_begin, int c_end, int32_t E,
+                                              int32_t expert_begin, int32_t* start, int32_t* __restrict__ sorted_slot,
+                                              int32_t* __restrict__ slot_pos) {
+  const int lane = threadIdx.x % kWave;
+  int key_bits = 1;
+  while ((1 << key_bits) <= E) ++key_bits;
+  const uint64_t lower_lanes = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int s0 = c_begin; s0 < c_end; s0 += kWave) {
+    const int s = s0 + lane;
+    const bool active = s < c_end;
+    const int key = active ? sort_key(ids[s], E, expert_begin) : 0;
+    uint64_t peers = __ballot(active);
+    for (int b = 0; b < key_bits; ++b) {
+      const uint64_t m = __ballot(active && ((key >> b) & 1));
+      peers &= ((key >> b) & 1) ? m : ~m;
+    }
+    if (active) {
+      const int st = start[key];
+      const int pos = st + __popcll(peers & lower_lanes);
+      sorted_slot[pos] = s;
+      if (slot_pos) slot_pos[s] = pos;
+      // the lowest lane of each key group advances the start after all lanes read it
+      const bool leader = (peers & lower_lanes) == 0;
+      __builtin_amdgcn_wave_barrier();
+      if (leader) start[key] = st + __popcll(peers);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Step A: hist[key][chunk] for keys 0..E, and the invalid ids of the chunk in
+// row E + 1.
+__global__ __launch_bounds__(kChunkWaves * kWave) void sort_hist_kernel(const int32_t* __restrict__ ids, int32_t S,
+                                                                       int32_t E, int32_t expert_begin, int32_t chunk,
+                                                                       int32_t n_chunks, int32_t* __restrict__ hist) {
+  extern __shared__ int32_t lh[];  // [kChunkWaves][E + 2]
+  const int K2 = E + 2;
+  const int wl = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int c = blockIdx.x * kChunkWaves + wl;
+  for (int i = threadIdx.x; i < kChunkWaves * K2; i += blockDim.x) lh[i] = 0;
+  __syncthreads();
+  if (c < n_chunks) {
+    const int c_begin = min(S, c * chunk), c_end = min(S, c_begin + chunk);
+    int bad = 0;
+    for (int s = c_begin + lane; s < c_end; s += kWave) {
+      const int32_t id = ids[s];
+      const int key = sort_key(id, E, expert_begin);
+      bad += (key == E && id != -1) ? 1 : 0;
+      atomicAdd(&lh[wl * K2 + key], 1);
+    }
+    if (bad) atomicAdd(&lh[wl * K2 + E + 1], bad);
+  }
+  __syncthreads();
+  if (c < n_chunks)
+    for (int e = lane; e < K2; e += kWave) hist[(size_t)e * n_chunks + c] = lh[wl * K2 + e];
+}
+
+// Step B: in-place exclusive prefix sum of hist[0 .. (E+1) n_chunks), offsets,
+// and the invalid total (row E + 1, not part of the scan).  hist moves through
+// LDS with coalesced, unrolled loads and stores.
+__global__ __launch_bounds__(kScanThreads) void sort_scan_kernel(int32_t E, int32_t n_chunks,
+                                                                int32_t* __restrict__ hist,
+                                                                int32_t* __restrict__ offsets,
+                                                                int32_t* __restrict__ invalid_count) {
+  __shared__ int32_t buf[kScanInts];
+  __shared__ int32_t part[kScanThreads];
+  __shared__ int32_t s_bad;
+  constexpr int U = 8;
+  const int tid = threadIdx.x;
+  const int n = (E + 1) * n_chunks;
+  for (int i0 = 0; i0 < n; i0 += U * kScanThreads) {
+    int32_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kScanThreads + tid;
+      v[u] = i < n ? hist[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kScanThreads + tid;
+      if (i < n) buf[i] = v[u];
+    }
+  }
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  const int seg = (n + kScanThreads - 1) / kScanThreads;
+  const int lo = min(n, tid * seg), hi = min(n, lo + seg);
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) sum += buf[i];
+  part[tid] = sum;
+  __syncthreads();
+  for (int d = 1; d < kScanThreads; d <<= 1) {
+    const int add = tid >= d ? part[tid - d] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  int run = part[tid] - sum;
+  for (int i = lo; i < hi; ++i) {
+    const int v = buf[i];
+    buf[i] = run;
+    run += v;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += kScanThreads) {
+    hist[i] = buf[i];
+    if (i % n_chunks == 0) offsets[i / n_chunks] = buf[i];
+  }
+  if (invalid_count) {
+    int bad = 0;
+    for (int c = tid; c < n_chunks; c += kScanThreads) bad += hist[(size_t)(E + 1) * n_chunks + c];
+    if (bad) atomicAdd(&s_bad, bad);
+    __syncthreads();
+    if (tid == 0) invalid_count[0] = s_bad;
+  }
+}
+
+// Step C: each wave scatters its chunk from its row of starts.
+__global__ __launch_bounds__(kChunkWaves * kWave) void sort_scatter_kernel(
+    const int32_t* __restrict__ ids, int32_t S, int32_t E, int32_t expert_begin, int32_t chunk, int32_t n_chunks,
+    const int32_t* __restrict__ start, int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos) {
+  extern __shared__ int32_t ls[];  // [kChunkWaves][E + 1]
+  const int K1 = E + 1;
+  const int wl = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int c = blockIdx.x * kChunkWaves + wl;
+  if (c >= n_chunks) return;  // whole waves only; no workgroup barrier follows
+  for (int e = lane; e < K1; e += kWave) ls[wl * K1 + e] = start[(size_t)e * n_chunks + c];
+  __builtin_amdgcn_wave_barrier();
+  const int c_begin = min(S, c * chunk), c_end = min(S, c_begin + chunk);
+  scatter_chunk(ids, c_begin, c_end, E, expert_begin, ls + wl * K1, sorted_slot, slot_pos);
+}
+
+// Chunk size of the multi-block path: at least kMinChunk, a multiple of the
+// wave size, and few enough chunks that (E + 1) * chunks <= kScanInts.
+int32_t sort_chunk(int32_t S, int32_t E) {
+  const int64_t max_chunks = kScanInts / (E + 1) < kMaxChunks ? kScanInts / (E + 1) : kMaxChunks;
+  int64_t c = ((int64_t)S + max_chunks - 1) / max_chunks;
+  c = (c + kWave - 1) / kWave * kWave;
+  return (int32_t)(c < kMinChunk ? kMinChunk : c);
 }
 
 __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(const int32_t* __restrict__ ids, int32_t S,
@@ -107,40 +264,39 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(const int32_t*
   __syncthreads();
 
   // 3. stable scatter, 64 slots per step, in slot order within each wave
-  int key_bits = 1;
-  while ((1 << key_bits) <= E) ++key_bits;
-  const uint64_t lower_lanes = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int s0 = c_begin; s0 < c_end; s0 += kWave) {
-    const int s = s0 + lane;
-    const bool active = s < c_end;
-    const int key = active ? sort_key(ids[s], E, expert_begin) : 0;
-    uint64_t peers = __ballot(active);
-    for (int b = 0; b < key_bits; ++b) {
-      const uint64_t m = __ballot(active && ((key >> b) & 1));
-      peers &= ((key >> b) & 1) ? m : ~m;
-    }
-    if (active) {
-      const int start = hist[wave * K1 + key];
-      const int pos = start + __popcll(peers & lower_lanes);
-      sorted_slot[pos] = s;
-      if (slot_pos) slot_pos[s] = pos;
-      // the lowest lane of each key group advances the start after all lanes read it
-      const bool leader = (peers & lower_lanes) == 0;
-      __builtin_amdgcn_wave_barrier();
-      if (leader) hist[wave * K1 + key] = start + __popcll(peers);
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
+  scatter_chunk(ids, c_begin, c_end, E, expert_begin, hist + wave * K1, sorted_slot, slot_pos);
 }
 
 }  // namespace
 
 size_t route_sort_lds_bytes(int32_t E) { return sizeof(int32_t) * (size_t)(kSortWaves + 1) * (E + 1); }
 
+size_t route_sort_ws_bytes(int32_t S, int32_t E) {
+  if (S < kMultiBlockFrom) return 0;
+  const int32_t chunk = sort_chunk(S, E);
+  const size_t n_chunks = ((size_t)S + chunk - 1) / chunk;
+  return sizeof(int32_t) * (size_t)(E + 2) * n_chunks;
+}
+
 hipError_t launch_route_sort(const int32_t* ids, int32_t S, int32_t E, int32_t expert_begin, int32_t* sorted_slot,
-                             int32_t* offsets, int32_t* slot_pos, int32_t* invalid_count, hipStream_t stream) {
-  hipLaunchKernelGGL(route_sort_kernel, dim3(1), dim3(kSortThreads), route_sort_lds_bytes(E), stream, ids, S, E,
-                     expert_begin, sorted_slot, offsets, slot_pos, invalid_count);
+                             int32_t* offsets, int32_t* slot_pos, int32_t* invalid_count, void* ws,
+                             hipStream_t stream) {
+  if (S < kMultiBlockFrom) {
+    hipLaunchKernelGGL(route_sort_kernel, dim3(1), dim3(kSortThreads), route_sort_lds_bytes(E), stream, ids, S, E,
+                       expert_begin, sorted_slot, offsets, slot_pos, invalid_count);
+    return hipGetLastError();
+  }
+  const int32_t chunk = sort_chunk(S, E);
+  const int32_t n_chunks = (S + chunk - 1) / chunk;
+  const int blocks = (n_chunks + kChunkWaves - 1) / kChunkWaves;
+  int32_t* hist = (int32_t*)ws;
+  hipLaunchKernelGGL(sort_hist_kernel, dim3(blocks), dim3(kChunkWaves * kWave),
+                     sizeof(int32_t) * kChunkWaves * (E + 2), stream, ids, S, E, expert_begin, chunk, n_chunks, hist);
+  hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, E, n_chunks, hist, offsets,
+                     invalid_count);
+  hipLaunchKernelGGL(sort_scatter_kernel, dim3(blocks), dim3(kChunkWaves * kWave),
+                     sizeof(int32_t) * kChunkWaves * (E + 1), stream, ids, S, E, expert_begin, chunk, n_chunks, hist,
+                     sorted_slot, slot_pos);
   return hipGetLastError();
 }
 

@@ -92,7 +92,9 @@ const char* moe_last_error(void);
  *  slot_pos        device int32 [T*k] out, may be NULL: inverse of sorted_slot.
  *  invalid_count   device int32 [1] out, may be NULL: number of ids that are
  *                  neither -1 nor inside [expert_begin, expert_begin + E).
- *  ws / ws_bytes   device workspace of at least moe_route_sort_workspace() bytes.
+ *  ws / ws_bytes   device workspace of at least moe_route_sort_workspace()
+ *                  bytes (per-chunk histograms; 0 bytes, and ws may be NULL,
+ *                  below 16384 slots).  Its contents are scratch.
  * Limits: 0 <= T, 1 <= k <= 64, 1 <= E <= 512, T*k < 2^31. */
 size_t moe_route_sort_workspace(int32_t T, int32_t k, int32_t E);
 moe_status moe_route_sort(const int32_t* top_k_index, int32_t T, int32_t k, int32_t E, int32_t expert_begin,

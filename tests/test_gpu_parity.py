@@ -78,6 +78,8 @@ SORT_CASES = [
     (1, 1, 1, 0.0, 0.0), (7, 2, 3, 0.2, 0.1), (64, 2, 8, 0.0, 0.0), (64, 8, 128, 0.05, 0.0),
     (4096, 2, 8, 0.0, 0.0), (8192, 8, 256, 0.05, 0.01), (16384, 8, 256, 0.05, 0.0), (1000, 3, 512, 0.3, 0.05),
     (333, 64, 5, 0.1, 0.1),
+    # around and above the size where the sort switches to several workgroups
+    (16383, 1, 7, 0.1, 0.0), (2048, 8, 256, 0.05, 0.01), (20000, 1, 1, 0.3, 0.1), (40000, 8, 512, 0.05, 0.02),
 ]
 
 
@@ -96,7 +98,8 @@ def test_route_sort_bit_exact(T, k, E, p_skip, p_bad):
 
 
 def test_route_sort_degenerate():
-    for ids in (np.full((50, 4), -1, np.int32), np.full((50, 4), 2, np.int32), np.zeros((0, 4), np.int32)):
+    for ids in (np.full((50, 4), -1, np.int32), np.full((50, 4), 2, np.int32), np.zeros((0, 4), np.int32),
+                np.full((5000, 8), -1, np.int32), np.full((5000, 8), 1, np.int32)):
         ss, off, sp, inv = moe.route_sort(torch.from_numpy(ids).to(DEV), 3)
         torch.cuda.synchronize()
         o = oracle.route_sort(ids, 3)
