@@ -28,8 +28,8 @@ FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
-SOURCES = ["route_sort.hip", "quant_act.hip", "gemm_fp8.hip", "gemm_mx.hip", "combine.hip", "prepare.hip",
-           "moe_api.cpp"]
+SOURCES = ["route_sort.hip", "quant_act.hip", "gemm_fp8.hip", "gemm_fp8_skinny.hip", "gemm_mx.hip", "combine.hip",
+           "prepare.hip", "moe_api.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -6,15 +6,54 @@
 // deterministic ("grouped_mm experts dispatch does not support
 // activation_scheme='static'", section "Source").  Here the slot rows of a token
 // (already multiplied by their routing weight in the down GEMM's epilogue) are
-// added in ascending j in fp32 and rounded once to bf16.  Skipped slots are never
-// read: their rows were never written, so whatever they hold (NaN included)
-// cannot reach the sum.  HBM-bound: 16-byte loads and stores, 8 bf16 per lane.
+// added in ascending j in fp32 and rounded once to bf16.  Skipped slots add
+// nothing: their rows were never written, and whatever they hold (NaN included)
+// is dropped by a select before the sum.  HBM-bound at large sizes (16-byte
+// loads and stores, 8 bf16 per lane), latency-bound at decode sizes.
 #include "device_common.h"
 #include "internal.h"
 
 namespace moe {
 
 namespace {
+
+
+// Sum of one token's valid slot rows at 8 columns (one 16-byte chunk).  Every
+// slot's load is issued before any is used (one memory round trip, which is
+// what decode-sized calls are bound by); a skipped slot loads its own row,
+// which exists but holds anything, and is dropped by a select, never scaled.
+template <int KU>
+__device__ __forceinline__ void combine_chunk(const uint4* __restrict__ slot_out, const int32_t* __restrict__ ids,
+                                              int64_t t, int64_t col, int32_t k, int32_t H8, int32_t E,
+                                              int32_t expert_begin, uint4* __restrict__ out, int64_t c) {
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < k; j0 += KU) {
+    uint4 v[KU];
+    bool ok[KU];
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int j = min(j0 + u, k - 1);
+      const int64_t local = (int64_t)ids[t * k + j] - expert_begin;
+      ok[u] = j0 + u < k && local >= 0 && local < E;
+      v[u] = slot_out[(t * k + j) * H8 + col];
+    }
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += ok[u] ? bf16_bits_to_f32(w[i] & 0xFFFF) : 0.0f;
+        acc[2 * i + 1] += ok[u] ? bf16_bits_to_f32(w[i] >> 16) : 0.0f;
+      }
+    }
+  }
+  uint4 o;
+  o.x = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
+  o.y = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
+  o.z = f32_to_bf16_bits(acc[4]) | (f32_to_bf16_bits(acc[5]) << 16);
+  o.w = f32_to_bf16_bits(acc[6]) | (f32_to_bf16_bits(acc[7]) << 16);
+  out[c] = o;
+}
 
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ slot_out,
                                                       const int32_t* __restrict__ ids, int32_t T, int32_t k,
@@ -25,26 +64,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n; c += stride) {
     const int64_t t = c / H8;
     const int64_t col = c - t * H8;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int64_t local = (int64_t)ids[t * k + j] - expert_begin;
-      if (local < 0 || local >= E) continue;
-      const uint4 v = slot_out[(t * k + j) * H8 + col];
-      acc[0] += bf16_bits_to_f32(v.x & 0xFFFF);
-      acc[1] += bf16_bits_to_f32(v.x >> 16);
-      acc[2] += bf16_bits_to_f32(v.y & 0xFFFF);
-      acc[3] += bf16_bits_to_f32(v.y >> 16);
-      acc[4] += bf16_bits_to_f32(v.z & 0xFFFF);
-      acc[5] += bf16_bits_to_f32(v.z >> 16);
-      acc[6] += bf16_bits_to_f32(v.w & 0xFFFF);
-      acc[7] += bf16_bits_to_f32(v.w >> 16);
-    }
-    uint4 o;
-    o.x = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
-    o.y = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
-    o.z = f32_to_bf16_bits(acc[4]) | (f32_to_bf16_bits(acc[5]) << 16);
-    o.w = f32_to_bf16_bits(acc[6]) | (f32_to_bf16_bits(acc[7]) << 16);
-    out[c] = o;
+    // adding +0 for a dropped slot leaves the running sum unchanged: a sum
+    // that starts at +0 is never -0, the one value +0 would change
+    if (k <= 8) combine_chunk<8>(slot_out, ids, t, col, k, H8, E, expert_begin, out, c);
+    else combine_chunk<16>(slot_out, ids, t, col, k, H8, E, expert_begin, out, c);
   }
 }
 

@@ -39,11 +39,20 @@ size_t route_sort_ws_bytes(int32_t S, int32_t E);
 hipError_t launch_route_sort(const int32_t* ids, int32_t S, int32_t E, int32_t expert_begin, int32_t* sorted_slot,
                              int32_t* offsets, int32_t* slot_pos, int32_t* invalid_count, void* ws,
                              hipStream_t stream);
+// The route sort (without slot_pos) and the activation quantization of x
+// [rows, H], in one launch for small batches, else one after the other.
+hipError_t launch_route_sort_and_quant(const int32_t* ids, int32_t S, int32_t E, int32_t expert_begin,
+                                      int32_t* sorted_slot, int32_t* offsets, int32_t* invalid_count, void* sort_ws,
+                                      const uint16_t* x, int32_t rows, int32_t H, int fmt, uint8_t* codes,
+                                      void* scales, hipStream_t stream);
 hipError_t launch_quant_act(const uint16_t* x, int32_t rows, int32_t H, int fmt, uint8_t* codes, void* scales,
                             hipStream_t stream);
 // epi: Epilogue; paired: gate/up row pairing of B (used with kEpiSwiGLUQuant and
 // optionally kEpiStoreF32 on the gate_up weight).
 hipError_t launch_gemm_fp8_b128(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream);
+// The same FP8 grouped GEMM for a few rows per expert: weights stream through
+// registers, 16 rows per tile.
+hipError_t launch_gemm_fp8_skinny(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream);
 hipError_t launch_gemm_mx(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream);
 hipError_t launch_combine(const uint16_t* slot_out, const int32_t* ids, int32_t T, int32_t k, int32_t H, int32_t E,
                           int32_t expert_begin, uint16_t* out, hipStream_t stream);

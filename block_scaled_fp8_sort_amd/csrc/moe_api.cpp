@@ -200,8 +200,16 @@ moe::GemmParams to_params(const moe_gemm_args* a) {
   return p;
 }
 
+// At most this many rows per expert on average (decode batches): the FP8 GEMM
+// streams the weights through registers instead of LDS tiles.
+constexpr int64_t kSkinnyRowsPerExpert = 8;
+
 hipError_t launch_gemm(const moe::GemmParams& p, int fmt, int epi, bool paired, int num_cus, hipStream_t stream) {
-  if (fmt == MOE_FMT_FP8_B128) return moe::launch_gemm_fp8_b128(p, epi, paired, num_cus, stream);
+  if (fmt == MOE_FMT_FP8_B128) {
+    if ((int64_t)p.max_rows <= kSkinnyRowsPerExpert * p.E)
+      return moe::launch_gemm_fp8_skinny(p, epi, paired, num_cus, stream);
+    return moe::launch_gemm_fp8_b128(p, epi, paired, num_cus, stream);
+  }
   return moe::launch_gemm_mx(p, epi, paired, num_cus, stream);
 }
 
@@ -425,11 +433,10 @@ moe_status moe_experts_forward(const moe_weights* w, const uint16_t* hidden_stat
   uint16_t* slot_out = (uint16_t*)(base + L.slot_out);
   const int32_t expert_begin = opt ? opt->expert_begin : 0;
 
-  hipError_t he = moe::launch_route_sort(top_k_index, S, E, expert_begin, sorted_slot, offsets, nullptr,
-                                         opt ? opt->invalid_count : nullptr, base + L.sort_ws, stream);
-  if (he != hipSuccess) return hip_status(he, "route sort launch");
-  he = moe::launch_quant_act(hidden_states, T, H, w->fmt, act_codes, act_scales, stream);
-  if (he != hipSuccess) return hip_status(he, "quant launch");
+  hipError_t he = moe::launch_route_sort_and_quant(top_k_index, S, E, expert_begin, sorted_slot, offsets,
+                                                   opt ? opt->invalid_count : nullptr, base + L.sort_ws, hidden_states,
+                                                   T, H, w->fmt, act_codes, act_scales, stream);
+  if (he != hipSuccess) return hip_status(he, "route sort / quant launch");
 
   moe::GemmParams p1{};
   p1.a_codes = act_codes;

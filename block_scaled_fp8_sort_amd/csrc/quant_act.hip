@@ -21,6 +21,7 @@
 // rule is row-local).
 #include "device_common.h"
 #include "internal.h"
+#include "quant_act.h"
 
 namespace moe {
 
@@ -30,51 +31,11 @@ template <int BLOCK>
 __global__ __launch_bounds__(256) void quant_act_kernel(const uint4* __restrict__ x, int64_t n_chunks, int32_t rows,
                                                         int32_t H, uint8_t* __restrict__ codes,
                                                         void* __restrict__ scales) {
-  constexpr int kLanesPerBlock = BLOCK / 8;  // 16 (FP8_B128) or 4 (MX)
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  // n_chunks is a multiple of kLanesPerBlock and every lane group stays together
-  const int H8 = H / 8;
-  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n_chunks; c += stride) {
-    const uint4 v = x[c];
-    const int64_t row = c / H8;
-    const int col8 = (int)(c - row * H8);
-    const int64_t blk128 = col8 / 16;  // K-block plane
-    uint2* dst = (uint2*)(codes + (blk128 * rows + row) * 128 + (col8 % 16) * 8);
-    float f[8];
-    f[0] = bf16_bits_to_f32(v.x & 0xFFFF);
-    f[1] = bf16_bits_to_f32(v.x >> 16);
-    f[2] = bf16_bits_to_f32(v.y & 0xFFFF);
-    f[3] = bf16_bits_to_f32(v.y >> 16);
-    f[4] = bf16_bits_to_f32(v.z & 0xFFFF);
-    f[5] = bf16_bits_to_f32(v.z >> 16);
-    f[6] = bf16_bits_to_f32(v.w & 0xFFFF);
-    f[7] = bf16_bits_to_f32(v.w >> 16);
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[i]));
-#pragma unroll
-    for (int m = 1; m < kLanesPerBlock; m <<= 1) amax = wave_max_xor(amax, m);
-    uint2 out;
-    if constexpr (BLOCK == 128) {
-      const float s = fp8_block_scale(amax);
-      float q[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = f[i] / s;  // IEEE division
-      out.x = e4m3x4(q[0], q[1], q[2], q[3]);
-      out.y = e4m3x4(q[4], q[5], q[6], q[7]);
-      if ((col8 % kLanesPerBlock) == 0) ((float*)scales)[blk128 * rows + row] = s;
-    } else {
-      const int e = mx_block_exponent(amax);
-      float q[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = __builtin_ldexpf(f[i], -e);
-      out.x = e4m3x4(q[0], q[1], q[2], q[3]);
-      out.y = e4m3x4(q[4], q[5], q[6], q[7]);
-      if ((col8 % kLanesPerBlock) == 0)
-        ((uint8_t*)scales)[(blk128 * rows + row) * 4 + (col8 % 16) / 4] = (uint8_t)(e + 127);
-    }
-    *dst = out;
-  }
+  // n_chunks and the stride are multiples of the lanes of one block, so every
+  // lane group stays together
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n_chunks; c += stride)
+    quant_chunk<BLOCK>(x, c, rows, H, codes, scales);
 }
 
 }  // namespace

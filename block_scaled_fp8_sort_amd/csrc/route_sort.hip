@@ -27,6 +27,7 @@
 // The result is the same unique permutation in both cases.
 #include "device_common.h"
 #include "internal.h"
+#include "quant_act.h"
 
 namespace moe {
 
@@ -190,12 +191,11 @@ int32_t sort_chunk(int32_t S, int32_t E) {
   return (int32_t)(c < kMinChunk ? kMinChunk : c);
 }
 
-__global__ __launch_bounds__(kSortThreads) void route_sort_kernel(const int32_t* __restrict__ ids, int32_t S,
-                                                                   int32_t E, int32_t expert_begin,
-                                                                   int32_t* __restrict__ sorted_slot,
-                                                                   int32_t* __restrict__ offsets,
-                                                                   int32_t* __restrict__ slot_pos,
-                                                                   int32_t* __restrict__ invalid_count) {
+// The whole sort in one workgroup of kSortThreads threads (steps 1-3 above).
+__device__ __forceinline__ void sort_one_workgroup(const int32_t* __restrict__ ids, int32_t S, int32_t E,
+                                                   int32_t expert_begin, int32_t* __restrict__ sorted_slot,
+                                                   int32_t* __restrict__ offsets, int32_t* __restrict__ slot_pos,
+                                                   int32_t* __restrict__ invalid_count) {
   extern __shared__ int32_t hist[];  // [kSortWaves][E + 1], then the key totals [E + 1]
   __shared__ int32_t s_invalid;
   __shared__ int32_t s_scan[kSortThreads];
@@ -267,6 +267,33 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(const int32_t*
   scatter_chunk(ids, c_begin, c_end, E, expert_begin, hist + wave * K1, sorted_slot, slot_pos);
 }
 
+__global__ __launch_bounds__(kSortThreads) void route_sort_kernel(const int32_t* __restrict__ ids, int32_t S,
+                                                                   int32_t E, int32_t expert_begin,
+                                                                   int32_t* __restrict__ sorted_slot,
+                                                                   int32_t* __restrict__ offsets,
+                                                                   int32_t* __restrict__ slot_pos,
+                                                                   int32_t* __restrict__ invalid_count) {
+  sort_one_workgroup(ids, S, E, expert_begin, sorted_slot, offsets, slot_pos, invalid_count);
+}
+
+// Small batches: the sort and the activation quantization are independent and
+// each too small to fill the chip, so one launch runs both: workgroup 0 sorts,
+// the others quantize (a grid-stride loop whose stride is a multiple of the
+// lanes of one quantization block).
+template <int BLOCK>
+__global__ __launch_bounds__(kSortThreads) void route_quant_kernel(
+    const int32_t* __restrict__ ids, int32_t S, int32_t E, int32_t expert_begin, int32_t* __restrict__ sorted_slot,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ invalid_count, const uint4* __restrict__ x,
+    int64_t n_chunks, int32_t rows, int32_t H, uint8_t* __restrict__ codes, void* __restrict__ scales) {
+  if (blockIdx.x == 0) {
+    sort_one_workgroup(ids, S, E, expert_begin, sorted_slot, offsets, nullptr, invalid_count);
+    return;
+  }
+  const int64_t stride = (int64_t)(gridDim.x - 1) * blockDim.x;
+  for (int64_t c = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x; c < n_chunks; c += stride)
+    quant_chunk<BLOCK>(x, c, rows, H, codes, scales);
+}
+
 }  // namespace
 
 size_t route_sort_lds_bytes(int32_t E) { return sizeof(int32_t) * (size_t)(kSortWaves + 1) * (E + 1); }
@@ -297,6 +324,30 @@ hipError_t launch_route_sort(const int32_t* ids, int32_t S, int32_t E, int32_t e
   hipLaunchKernelGGL(sort_scatter_kernel, dim3(blocks), dim3(kChunkWaves * kWave),
                      sizeof(int32_t) * kChunkWaves * (E + 1), stream, ids, S, E, expert_begin, chunk, n_chunks, hist,
                      sorted_slot, slot_pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_sort_and_quant(const int32_t* ids, int32_t S, int32_t E, int32_t expert_begin,
+                                      int32_t* sorted_slot, int32_t* offsets, int32_t* invalid_count, void* sort_ws,
+                                      const uint16_t* x, int32_t rows, int32_t H, int fmt, uint8_t* codes,
+                                      void* scales, hipStream_t stream) {
+  const int64_t n_chunks = (int64_t)rows * H / 8;
+  if (S >= kMultiBlockFrom || n_chunks == 0) {
+    hipError_t e = launch_route_sort(ids, S, E, expert_begin, sorted_slot, offsets, nullptr, invalid_count, sort_ws,
+                                     stream);
+    if (e != hipSuccess) return e;
+    return launch_quant_act(x, rows, H, fmt, codes, scales, stream);
+  }
+  const int64_t want = (n_chunks + kSortThreads - 1) / kSortThreads;
+  const int blocks = 1 + (int)(want < 256 * 16 ? want : 256 * 16);
+  if (fmt == 0)
+    hipLaunchKernelGGL(route_quant_kernel<128>, dim3(blocks), dim3(kSortThreads), route_sort_lds_bytes(E), stream,
+                       ids, S, E, expert_begin, sorted_slot, offsets, invalid_count, (const uint4*)x, n_chunks, rows,
+                       H, codes, scales);
+  else
+    hipLaunchKernelGGL(route_quant_kernel<32>, dim3(blocks), dim3(kSortThreads), route_sort_lds_bytes(E), stream,
+                       ids, S, E, expert_begin, sorted_slot, offsets, invalid_count, (const uint4*)x, n_chunks, rows,
+                       H, codes, scales);
   return hipGetLastError();
 }
 

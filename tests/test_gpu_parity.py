@@ -162,7 +162,12 @@ def test_quant_act_all_bf16_values(fmt):
 # -------------------------------------------------------------- grouped GEMM
 @pytest.mark.parametrize("fmt", [FP8, MX])
 @pytest.mark.parametrize("which", [0, 1])
-@pytest.mark.parametrize("E,H,I,T,k", [(3, 256, 128, 40, 2), (5, 640, 384, 700, 3), (2, 384, 1024, 300, 1)])
+@pytest.mark.parametrize("E,H,I,T,k", [
+    (3, 256, 128, 40, 2), (5, 640, 384, 700, 3), (2, 384, 1024, 300, 1),
+    # at most 8 rows per expert on average: the FP8 path streams weights
+    # through registers; K / 128 = 5, 3, 16, 4, 2 give ring depths 1, 3, 4, 4, 2
+    (12, 640, 384, 10, 3), (16, 2048, 512, 24, 4), (20, 256, 256, 30, 2),
+])
 def test_grouped_gemm_store_f32(fmt, which, E, H, I, T, k):
     """Either weight of a prepared layer times gathered rows, against the oracle's
     grouped GEMM (which = 0: N = 2I over K = H; which = 1: N = H over K = I)."""
@@ -196,6 +201,56 @@ def test_grouped_gemm_store_f32(fmt, which, E, H, I, T, k):
     assert np.max(err) <= 1e-4 * scale + 1e-30
 
 
+def _gemm_vs_oracle(fmt, which, E, H, I, ids_np, k, seed):
+    gen = W.fp8_weights if fmt == FP8 else W.fp4_weights
+    w13, s13 = gen(E, 2 * I, H, seed, "w13", DEV)
+    w2, s2 = gen(E, H, I, seed, "w2", DEV)
+    w = moe.prepare_weights(w13, s13, w2, s2, fmt=fmt)
+    N, K = (2 * I, H) if which == 0 else (H, I)
+    T = ids_np.shape[0]
+    x = W.hidden_states(T, K, seed, DEV)
+    a, asc = moe.quant_act(x, fmt)
+    ss, off, _, _ = moe.route_sort(torch.from_numpy(ids_np).to(DEV), E)
+    S = T * k
+    c = torch.full((S, N), float("nan"), dtype=torch.float32, device=DEV)
+    moe.grouped_gemm(w, which, a, asc, T, off, moe.EPI_STORE_F32, S, a_row_index=ss, a_row_divisor=k, c_f32=c)
+    torch.cuda.synchronize()
+    offs = host(off)
+    b, bs = (host(w13), host(s13)) if which == 0 else (host(w2), host(s2))
+    del w, w13, w2
+    ref = oracle.grouped_gemm(fmt, rowmajor_codes(a), rowmajor_scales(asc), offs, b, bs, N, K, row_index=host(ss),
+                              row_div=k)
+    got = host(c)[: offs[-1]].astype(np.float64)
+    assert np.all(np.isnan(host(c)[offs[-1]:]))
+    scale = np.max(np.abs(ref))
+    err = np.max(np.abs(got - ref))
+    say(f"  max err / max ref = {err / scale:.2e}")
+    assert err <= 1e-4 * scale + 1e-30
+
+
+@pytest.mark.parametrize("which", [0, 1])
+def test_grouped_gemm_few_rows_one_heavy_expert(which):
+    """Few rows per expert on average, but one expert with 40 rows (three
+    16-row tiles) and several experts with none."""
+    say(f"gemm heavy expert which={which}")
+    T, k, E = 40, 2, 16
+    ids = np.full((T, k), -1, np.int32)
+    ids[:20, :] = 3                 # expert 3: 40 slots
+    ids[20:, 0] = np.arange(20) % 5 + 9
+    _gemm_vs_oracle(FP8, which, E, 512, 384, ids, k, seed=77)
+
+
+def test_grouped_gemm_few_rows_many_tiles():
+    """More tiles than a workgroup fetches row data for at once (16 per
+    workgroup on 256 CUs needs over 4096 tiles): 80 experts x 64 paired
+    n-tiles."""
+    say("gemm many tiles")
+    rng = np.random.default_rng(5)
+    T, k, E = 64, 4, 80
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    _gemm_vs_oracle(FP8, 0, E, 256, 8192, ids, k, seed=78)
+
+
 # ------------------------------------------------------------- the forward
 def _prepare(inp, fmt):
     return moe.prepare_weights(inp["w13"], inp["s13"], inp["w2"], inp["s2"], fmt=fmt)
@@ -225,6 +280,10 @@ SMALL = [
     _small_workload("ragged_fp8_clamp", FP8, T=517, H=384, I=256, E=12, k=4, routing="zipf", skip=0.05,
                     limit=0.05, seed=12),
     _small_workload("k1_one_expert", FP8, T=129, H=256, I=128, E=1, k=1, seed=13),
+    # decode-like: at most 8 rows per expert on average
+    _small_workload("decode_fp8", FP8, T=24, H=512, I=256, E=16, k=4, seed=17),
+    _small_workload("decode_fp8_ragged_clamp", FP8, T=16, H=640, I=384, E=32, k=8, routing="zipf", skip=0.1,
+                    limit=0.05, seed=18),
     _small_workload("mx_tiny", MX, T=64, H=256, I=128, E=8, k=2, seed=14),
     _small_workload("mx_ragged_clamp", MX, T=300, H=384, I=256, E=7, k=4, routing="zipf", skip=0.1, limit=7.0,
                     seed=15),
