@@ -33,6 +33,18 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
 }
 
 // Block scale of the FP8_B128 format: max(amax, 1e-4) / 448 with IEEE fp32 division.
+// SwiGLU of one (gate, up) pair ("swiglu_limit" clamp when given: gate capped
+// above at L, up clamped to [-L, L]): silu(g) * u with silu(g) = g / (1 + e^-g),
+// the division done with the hardware reciprocal (about 1 ulp; h is compared by
+// tolerance, not bit for bit).  Very negative g gives e^-g = inf and h = -0 * u.
+__device__ __forceinline__ float swiglu(float g, float u, bool has_limit, float limit) {
+  if (has_limit) {
+    g = __builtin_fminf(g, limit);
+    u = __builtin_fminf(__builtin_fmaxf(u, -limit), limit);
+  }
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 __device__ __forceinline__ float fp8_block_scale(float amax) { return __builtin_fmaxf(amax, 1e-4f) / 448.0f; }
 
 // MX format: e = ceil(log2(max(amax, 1e-4) / 448)) read from the fp32 bits of

@@ -272,24 +272,19 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Mis
     }
   } else if constexpr (EPI == kEpiSwiGLUQuant) {
     static_assert(PAIRED, "SwiGLU needs the paired gate/up layout");
-    // h of pair q, sub-tile ti, element i (recomputed in the second pass
-    // instead of being held across the barrier)
-    auto hval = [&](int q, int ti, int i) {
-      float gv = acc[2 * q][ti][i];
-      float uv = acc[2 * q + 1][ti][i];
-      if (p.has_limit) {
-        gv = __builtin_fminf(gv, p.limit);
-        uv = __builtin_fminf(__builtin_fmaxf(uv, -p.limit), p.limit);
-      }
-      return gv / (1.0f + __expf(-gv)) * uv;
-    };
+    // h of pair q, sub-tile ti, element i, computed once into the gate's
+    // accumulator, and its amax over the tile's 128 outputs of each token
 #pragma unroll
     for (int ti = 0; ti < TS; ++ti) {
       float m = 0.0f;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(hval(q, ti, i)));
+        for (int i = 0; i < 4; ++i) {
+          const float h = swiglu(acc[2 * q][ti][i], acc[2 * q + 1][ti][i], p.has_limit, p.limit);
+          acc[2 * q][ti][i] = h;
+          m = __builtin_fmaxf(m, __builtin_fabsf(h));
+        }
       m = wave_max_xor(m, 16);
       m = wave_max_xor(m, 32);
       if (g == 0) misc.amax[wn][wt * WM + ti * 16 + l16] = m;
@@ -308,8 +303,8 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Mis
       if (r < m_end) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t code =
-              e4m3x4(hval(q, ti, 0) * inv, hval(q, ti, 1) * inv, hval(q, ti, 2) * inv, hval(q, ti, 3) * inv);
+          const v4f h = acc[2 * q][ti];
+          const uint32_t code = e4m3x4(h[0] * inv, h[1] * inv, h[2] * inv, h[3] * inv);
           *(uint32_t*)(plane + (size_t)r * 128 + 16 * (wn * 4 + q) + 4 * g) = code;
         }
         if (wn == 0 && g == 0) ((float*)p.h_scales)[(size_t)n_tile * p.max_rows + r] = s;

@@ -186,12 +186,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, Misc& misc, const 
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float gv = acc0[i], uv = acc1[i];
-      if (p.has_limit) {
-        gv = __builtin_fminf(gv, p.limit);
-        uv = __builtin_fminf(__builtin_fmaxf(uv, -p.limit), p.limit);
-      }
-      h[i] = gv / (1.0f + __expf(-gv)) * uv;
+      h[i] = swiglu(acc0[i], acc1[i], p.has_limit, p.limit);
       m = __builtin_fmaxf(m, __builtin_fabsf(h[i]));
     }
     m = wave_max_xor(m, 16);
@@ -328,7 +323,8 @@ template <int EPI, bool PAIRED>
 hipError_t launch_epi(const GemmParams& p, int num_cus, hipStream_t stream) {
   const int KB = p.K / BK;
   // 8 slots fit in registers except with the SwiGLU epilogue
-  if (EPI != kEpiSwiGLUQuant && KB % 8 == 0) return launch_d<EPI, PAIRED, 8>(p, num_cus, stream);
+  if constexpr (EPI != kEpiSwiGLUQuant)
+    if (KB % 8 == 0) return launch_d<EPI, PAIRED, 8>(p, num_cus, stream);
   if (KB % 6 == 0) return launch_d<EPI, PAIRED, 6>(p, num_cus, stream);
   if (KB % 4 == 0) return launch_d<EPI, PAIRED, 4>(p, num_cus, stream);
   if (KB % 3 == 0) return launch_d<EPI, PAIRED, 3>(p, num_cus, stream);

@@ -226,15 +226,6 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, int
     }
   } else if constexpr (EPI == kEpiSwiGLUQuant) {
     static_assert(PAIRED, "SwiGLU needs the paired gate/up layout");
-    auto hval = [&](int q, int ti, int i) {
-      float gv = acc[2 * q][ti][i];
-      float uv = acc[2 * q + 1][ti][i];
-      if (p.has_limit) {
-        gv = __builtin_fminf(gv, p.limit);
-        uv = __builtin_fminf(__builtin_fmaxf(uv, -p.limit), p.limit);
-      }
-      return gv / (1.0f + __expf(-gv)) * uv;
-    };
     // this wave's 64 outputs of the tile's 128 are the 32-wide MX blocks 2 wn and
     // 2 wn + 1, each made of pairs q = 2b and 2b + 1: the block amax needs only
     // this wave (xor over the four lane groups)
@@ -249,16 +240,20 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, int
 #pragma unroll
         for (int q = 2 * b; q < 2 * b + 2; ++q)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(hval(q, ti, i)));
+          for (int i = 0; i < 4; ++i) {  // h, computed once into the gate's accumulator
+            const float h = swiglu(acc[2 * q][ti][i], acc[2 * q + 1][ti][i], p.has_limit, p.limit);
+            acc[2 * q][ti][i] = h;
+            m = __builtin_fmaxf(m, __builtin_fabsf(h));
+          }
         m = wave_max_xor(m, 16);
         m = wave_max_xor(m, 32);
         const int ex = mx_block_exponent(m);
         if (r < m_end) {
 #pragma unroll
           for (int q = 2 * b; q < 2 * b + 2; ++q) {
-            const uint32_t code =
-                e4m3x4(__builtin_ldexpf(hval(q, ti, 0), -ex), __builtin_ldexpf(hval(q, ti, 1), -ex),
-                       __builtin_ldexpf(hval(q, ti, 2), -ex), __builtin_ldexpf(hval(q, ti, 3), -ex));
+            const v4f h = acc[2 * q][ti];
+            const uint32_t code = e4m3x4(__builtin_ldexpf(h[0], -ex), __builtin_ldexpf(h[1], -ex),
+                                         __builtin_ldexpf(h[2], -ex), __builtin_ldexpf(h[3], -ex));
             *(uint32_t*)(plane + (size_t)r * 128 + 16 * (wn * 4 + q) + 4 * g) = code;
           }
           if (g == 0) splane[(size_t)r * 4 + wn * 2 + b] = (uint8_t)(ex + 127);
