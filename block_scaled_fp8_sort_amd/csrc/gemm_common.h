@@ -16,8 +16,8 @@ __device__ __forceinline__ void raw_barrier() {
 }
 
 // Tile table in LDS: off[e] = expert offsets, tp[e] = first tile of expert e,
-// where expert e has ceil(rows_e / BM) m-tiles times NT n-tiles (m fastest);
-// tp[E] = total.  All threads of the block must call it.
+// where expert e has ceil(rows_e / BM) m-tiles times NT n-tiles (in the order
+// of tile_position); tp[E] = total.  All threads of the block must call it.
 template <int THREADS>
 __device__ __forceinline__ int build_tile_table(const int32_t* offsets, int E, int BM, int NT, int* off, int* tp,
                                                 int* scan) {
@@ -52,9 +52,27 @@ struct TileCoord {
   int e, n_tile, m0, m_end;
 };
 
+// Order of an expert's mt x NT tiles: groups of up to kTileGroupM m-tiles, m
+// fastest inside a group, then n, then the next group.  Consecutive tiles run
+// at the same time (on one XCD), so a group's activation rows stay cached
+// while all n-tiles pass over them and each weight tile is fetched once per
+// group.  With m fastest over a whole large expert instead, its activation rows
+// (more than the last-level cache holds at large token counts) would come back
+// from HBM once per n-tile.
+constexpr int kTileGroupM = 8;
+
+// (m index, n index) of tile loc (0-based within its expert).
+__device__ __forceinline__ void tile_position(int loc, int mt, int NT, int& m_idx, int& n_idx) {
+  const int grp = loc / (kTileGroupM * NT);
+  const int in = loc - grp * (kTileGroupM * NT);
+  const int gm = min(kTileGroupM, mt - grp * kTileGroupM);
+  n_idx = in / gm;
+  m_idx = grp * kTileGroupM + (in - n_idx * gm);
+}
+
 // Tile t -> (expert, n-tile, first sorted row, end of the expert's rows).  Every
 // lane computes the same values; they are made wave-uniform (scalar).
-__device__ __forceinline__ TileCoord locate_tile(int t, int E, int BM, const int* off, const int* tp) {
+__device__ __forceinline__ TileCoord locate_tile(int t, int E, int BM, int NT, const int* off, const int* tp) {
   int lo = 0, hi = E;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -66,8 +84,10 @@ __device__ __forceinline__ TileCoord locate_tile(int t, int E, int BM, const int
   c.m_end = __builtin_amdgcn_readfirstlane(off[c.e + 1]);
   const int mt = (c.m_end - m_begin + BM - 1) / BM;
   const int loc = t - __builtin_amdgcn_readfirstlane(tp[c.e]);
-  c.n_tile = loc / mt;
-  c.m0 = m_begin + (loc % mt) * BM;
+  int m_idx, n_idx;
+  tile_position(loc, mt, NT, m_idx, n_idx);
+  c.n_tile = n_idx;
+  c.m0 = m_begin + m_idx * BM;
   return c;
 }
 

@@ -32,12 +32,13 @@
 //    128-byte chunks by per-lane address (the gather is free) without the
 //    same-L2-channel aliasing that 4 KB-strided rows suffer.
 //  * Persistent grid: each workgroup reads the expert offsets, builds the tile
-//    table (experts x n-tiles x m-tiles, m fastest) in LDS, and walks tiles
-//    with a stride of the grid size.  Workgroup ids are remapped so that
-//    consecutive tiles land on the same XCD (dispatch is round-robin over the
-//    8 XCDs), which keeps a weight tile shared by an expert's m-tiles in that
-//    XCD's L2.  Rows past the expert's end are masked; no host-visible counts
-//    are needed.
+//    table in LDS (per expert, groups of up to 8 m-tiles, m fastest inside a
+//    group, then n), and walks tiles with a stride of the grid size.
+//    Workgroup ids are remapped so that consecutive tiles land on the same XCD
+//    (dispatch is round-robin over the 8 XCDs): a weight tile is shared by the
+//    group's m-tiles in that XCD's L2, and the group's activation rows stay
+//    cached across its n-tiles.  Rows past the expert's end are masked; no
+//    host-visible counts are needed.
 #include "device_common.h"
 #include "gemm_common.h"
 #include "internal.h"
@@ -346,7 +347,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p
   const int total = build_tile_table<kThreads>(p.offsets, E, kMaxBM, NT, misc.off, misc.tp, misc.scan);
   const int G = gridDim.x;
   for (int t = xcd_virtual_block(); t < total; t += G) {
-    const TileCoord tc = locate_tile(t, E, kMaxBM, misc.off, misc.tp);
+    const TileCoord tc = locate_tile(t, E, kMaxBM, NT, misc.off, misc.tp);
     const int left = tc.m_end - tc.m0;
     if (left > 128)
       run_tile<256, EPI, PAIRED>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end);

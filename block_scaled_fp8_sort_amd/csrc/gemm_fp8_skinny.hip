@@ -80,7 +80,7 @@ __device__ __forceinline__ Src make_src(const GemmParams& p, const Misc& misc, i
   Src s;
   s.valid = t < total;
   if (!s.valid) t = 0;
-  const TileCoord tc = locate_tile(t, p.E, BMS, misc.off, misc.tp);
+  const TileCoord tc = locate_tile(t, p.E, BMS, NT, misc.off, misc.tp);
   s.e = tc.e;
   s.n_tile = tc.n_tile;
   s.m0 = tc.m0;
@@ -110,7 +110,7 @@ __device__ __forceinline__ Src make_src(const GemmParams& p, const Misc& misc, i
 // flight would drain it (the wait is by count, in order), so they are all made
 // here, once per batch.
 template <int EPI>
-__device__ __forceinline__ void fetch_rows(const GemmParams& p, Misc& misc, int t, int G, int total) {
+__device__ __forceinline__ void fetch_rows(const GemmParams& p, Misc& misc, int t, int G, int total, int NT) {
   __syncthreads();  // every wave is done reading the previous batch
   const int tid = threadIdx.x;
   if (tid < kRowBatch * BMS) {
@@ -128,7 +128,9 @@ __device__ __forceinline__ void fetch_rows(const GemmParams& p, Misc& misc, int 
       }
       const int m_begin = misc.off[lo], m_end = misc.off[lo + 1];
       const int mt = (m_end - m_begin + BMS - 1) / BMS;
-      const int r = min(m_begin + ((tb - misc.tp[lo]) % mt) * BMS + i, m_end - 1);
+      int m_idx, n_idx;
+      tile_position(tb - misc.tp[lo], mt, NT, m_idx, n_idx);
+      const int r = min(m_begin + m_idx * BMS + i, m_end - 1);
       arow = p.a_row_index ? p.a_row_index[r] / p.a_row_div : r;
       if constexpr (EPI == kEpiWeightedScatter) {
         slot = p.slot_of_row[r];
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_skinny_kernel(GemmParams
     w_off[q] = (uint32_t)tr * BK + (uint32_t)((c ^ swz(tr)) << 4);
   }
 
-  fetch_rows<EPI>(p, misc, t, G, total);
+  fetch_rows<EPI>(p, misc, t, G, total, NT);
   Src cur = make_src(p, misc, t, total, NT, KB, NB, PAIRED, wave, lane, misc.arow[0][l16], zero);
   // the prologue issues the slots in the same order as the loop below: the
   // compiler waits by count and merges the two paths into the loop, so any
@@ -267,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_skinny_kernel(GemmParams
     // the next tile's rows come from the LDS batch; when the next tile starts a
     // new batch it is refetched here (entry 0 = tile i + 1), which waits for the
     // loads in flight once per kRowBatch tiles
-    if ((i + 1) % kRowBatch == 0) fetch_rows<EPI>(p, misc, t + G, G, total);
+    if ((i + 1) % kRowBatch == 0) fetch_rows<EPI>(p, misc, t + G, G, total, NT);
     const Src nxt =
         make_src(p, misc, t + G, total, NT, KB, NB, PAIRED, wave, lane, misc.arow[(i + 1) % kRowBatch][l16], zero);
     v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};

@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmParams p) {
   const int total = build_tile_table<kThreads>(p.offsets, E, kMaxBM, NT, misc.off, misc.tp, misc.scan);
   const int G = gridDim.x;
   for (int t = xcd_virtual_block(); t < total; t += G) {
-    const TileCoord tc = locate_tile(t, E, kMaxBM, misc.off, misc.tp);
+    const TileCoord tc = locate_tile(t, E, kMaxBM, NT, misc.off, misc.tp);
     const int left = tc.m_end - tc.m0;
     if (left > 128)
       run_tile<256, EPI, PAIRED>(p, area, tc.e, tc.n_tile, tc.m0, tc.m_end);
