@@ -109,24 +109,37 @@ struct TileSrc {
   uint32_t s_stride;       // per-lane scale advance per K block, in floats
 };
 
+// DMA instruction idx (0 .. LOADS - 1) of the stage for block kb: 0-3 the
+// weights (wave w copies the 4 KB of tile rows [32 w, 32 w + 32), contiguous),
+// then BM / 64 activation gathers (wave w gathers rows [w BM/8, (w+1) BM/8) of
+// the tile), last the scales.  idx is a compile-time constant after unrolling.
 template <int BM>
-__device__ __forceinline__ void issue_stage(StageBuf<BM>* st, const TileSrc<BM>& src, int kb, int wave, int lane) {
+__device__ __forceinline__ void issue_part(StageBuf<BM>* st, const TileSrc<BM>& src, int kb, int wave, int lane,
+                                           int idx) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(st));
   const uint32_t w = __builtin_amdgcn_readfirstlane(wave);
-  // weights: wave w copies the 4 KB of tile rows [32 w, 32 w + 32), contiguous
-  const uint8_t* wsrc = src.w_tile + (size_t)kb * (BN * BK) + w * 4096;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) lds_dma16_s(wsrc + q * 1024, lane * 16, base + w * 4096 + q * 1024);
-  // activations: wave w gathers rows [w BM/8, (w+1) BM/8) of the tile
-  const uint8_t* plane = src.a_codes + (size_t)kb * src.a_plane;
-#pragma unroll
-  for (int q = 0; q < TileSrc<BM>::A_LOADS; ++q)
+  if (idx < 4) {
+    const uint8_t* wsrc = src.w_tile + (size_t)kb * (BN * BK) + w * 4096;
+    lds_dma16_s(wsrc + idx * 1024, lane * 16, base + w * 4096 + idx * 1024);
+  } else if (idx < 4 + TileSrc<BM>::A_LOADS) {
+    const int q = idx - 4;
+    const uint8_t* plane = src.a_codes + (size_t)kb * src.a_plane;
     lds_dma16_s(plane, src.a_off[q], base + BN * BK + (w * (BM / 8) + 8 * q) * BK);
-  lds_dma4(src.s_base + (size_t)kb * src.s_stride, base + (BN + BM) * BK + w * 256);
+  } else {
+    lds_dma4(src.s_base + (size_t)kb * src.s_stride, base + (BN + BM) * BK + w * 256);
+  }
 }
 
-// One K block: wait for stage `cur`, start the DMA of block kb + STAGES - 1 into
-// `nxt` (the stage block kb - 1 used), then accumulate the block from `cur`.
+template <int BM>
+__device__ __forceinline__ void issue_stage(StageBuf<BM>* st, const TileSrc<BM>& src, int kb, int wave, int lane) {
+  constexpr int LOADS = 4 + BM / 64 + 1;
+#pragma unroll
+  for (int idx = 0; idx < LOADS; ++idx) issue_part<BM>(st, src, kb, wave, lane, idx);
+}
+
+// One K block: wait for stage `cur`, then accumulate the block from `cur` while
+// the DMA of block kb + STAGES - 1 goes out into `nxt` (the stage block kb - 1
+// used).
 // Past the last block the DMA repeats block KB - 1 into a stage nobody reads,
 // which keeps the number of DMAs in flight, and so this wait, the same on every
 // step.
@@ -140,7 +153,7 @@ __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nx
   const int g = lane >> 4, l16 = lane & 15;
   wait_vmcnt<LOADS * (STAGES - 2)>();  // this wave's DMAs of stage kb have landed
   raw_barrier();  // ... and every other wave's; all waves are done with block kb - 1
-  issue_stage<BM>(nxt, src, min(kb + STAGES - 1, KB - 1), wave, lane);
+  const int kb_dma = min(kb + STAGES - 1, KB - 1);
   const float swg = cur->s[PAIRED ? BM : BM + wn];
   const float swu = cur->s[BM + 1];
   typedef float vts __attribute__((ext_vector_type(TS)));
@@ -162,6 +175,12 @@ __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nx
   v8i af = lds_frag(cur->w, wn * 128 + l16, g);
 #pragma unroll
   for (int ni = 0; ni <= 8; ++ni) {
+    // the DMAs of block kb + STAGES - 1 go out spread over the sub-tiles: issued
+    // all at once they queue in the texture addresser and hold every wave back
+    // from its MFMAs; between MFMAs they drain in the background
+#pragma unroll
+    for (int idx = 0; idx < LOADS; ++idx)
+      if (idx * 8 / LOADS == ni) issue_part<BM>(nxt, src, kb_dma, wave, lane, idx);
     v8i af_next = af;
     if (ni < 7) af_next = lds_frag(cur->w, wn * 128 + (ni + 1) * 16 + l16, g);
     const int pn = ni - 1;

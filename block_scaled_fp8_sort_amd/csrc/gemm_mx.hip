@@ -78,27 +78,38 @@ struct TileSrc {
   uint32_t as_off;          // per-lane gathered row offset (waves < BM/64)
 };
 
+// DMA instruction idx (0 .. LOADS - 1) of the stage for block kb: 0-1 the
+// weights (16 KB per K block, wave w copies 2 KB = 32 rows, contiguous), then
+// BM / 64 activation gathers, last exactly one scale DMA per wave, so every wave
+// has the same DMA count per stage.  idx is a compile-time constant after
+// unrolling.
 template <int BM>
-__device__ __forceinline__ void issue_stage(StageBuf<BM>* st, const TileSrc<BM>& src, int kb, int wave, int lane) {
+__device__ __forceinline__ void issue_part(StageBuf<BM>* st, const TileSrc<BM>& src, int kb, int wave, int lane,
+                                           int idx) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(st));
   const uint32_t w = __builtin_amdgcn_readfirstlane(wave);
   constexpr uint32_t oW = 0, oA = BN * kWRow, oWS = oA + BM * kARow, oAS = oWS + BN * 4;
-  // weights: 16 KB per K block, wave w copies 2 KB (32 rows), contiguous
-  const uint8_t* wsrc = src.w_tile + (size_t)kb * (BN * kWRow) + w * 2048;
-  lds_dma16_s(wsrc, lane * 16, base + oW + w * 2048);
-  lds_dma16_s(wsrc + 1024, lane * 16, base + oW + w * 2048 + 1024);
-  const uint8_t* plane = src.a_codes + (size_t)kb * src.a_plane;
-#pragma unroll
-  for (int q = 0; q < TileSrc<BM>::A_LOADS; ++q)
+  if (idx < 2) {
+    const uint8_t* wsrc = src.w_tile + (size_t)kb * (BN * kWRow) + w * 2048;
+    lds_dma16_s(wsrc + idx * 1024, lane * 16, base + oW + w * 2048 + idx * 1024);
+  } else if (idx < 2 + TileSrc<BM>::A_LOADS) {
+    const int q = idx - 2;
+    const uint8_t* plane = src.a_codes + (size_t)kb * src.a_plane;
     lds_dma16_s(plane, src.a_off[q], base + oA + (w * (BM / 8) + 8 * q) * kARow);
-  // exactly one scale DMA per wave, so every wave has the same DMA count per stage
-  if (w < BM / 64) {  // activation scales: 64 rows x 4 bytes per wave
+  } else if (w < BM / 64) {  // activation scales: 64 rows x 4 bytes per wave
     lds_dma4(src.as_base + (size_t)kb * src.as_plane + src.as_off, base + oAS + w * 256);
   } else if (w == BM / 64) {  // weight scales: 256 rows x 4 bytes, contiguous
     lds_dma16_s(src.ws_tile + (size_t)kb * (BN * 4), lane * 16, base + oWS);
   } else {
     lds_dma4(src.as_base + (size_t)kb * src.as_plane + src.as_off, base + oAS + BM * 4);
   }
+}
+
+template <int BM>
+__device__ __forceinline__ void issue_stage(StageBuf<BM>* st, const TileSrc<BM>& src, int kb, int wave, int lane) {
+  constexpr int LOADS = 2 + BM / 64 + 1;
+#pragma unroll
+  for (int idx = 0; idx < LOADS; ++idx) issue_part<BM>(st, src, kb, wave, lane, idx);
 }
 
 // 16 bytes = 32 FP4 values, K elements [32 g, 32 g + 32) of weight row tr
@@ -114,8 +125,9 @@ __device__ __forceinline__ v8i frag_a(const uint8_t* a, int tr, int g) {
   return v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 }
 
-// One K block (see the FP8 kernel: the DMA always goes out, repeating block
-// KB - 1 past the end, so the wait count is constant).
+// One K block (see the FP8 kernel: the DMA always goes out, spread over the
+// sub-tiles, repeating block KB - 1 past the end, so the wait count is
+// constant).
 template <int BM, int STAGES>
 __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nxt, const TileSrc<BM>& src, int kb,
                                        int KB, int wave, int lane, v4f (&acc)[8][BM / 64]) {
@@ -126,7 +138,7 @@ __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nx
   const int g = lane >> 4, l16 = lane & 15;
   wait_vmcnt<LOADS * (STAGES - 2)>();
   raw_barrier();
-  issue_stage<BM>(nxt, src, min(kb + STAGES - 1, KB - 1), wave, lane);
+  const int kb_dma = min(kb + STAGES - 1, KB - 1);
   v8i bf[TS];
   int sa[TS];
 #pragma unroll
@@ -137,6 +149,11 @@ __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nx
   }
 #pragma unroll
   for (int ni = 0; ni < 8; ++ni) {
+    // the DMAs of block kb + STAGES - 1 go out spread over the sub-tiles (all at
+    // once they would queue in the texture addresser ahead of the MFMAs)
+#pragma unroll
+    for (int idx = 0; idx < LOADS; ++idx)
+      if (idx * 8 / LOADS == ni) issue_part<BM>(nxt, src, kb_dma, wave, lane, idx);
     const int tr = wn * 128 + ni * 16 + l16;
     const v8i af = frag_w(cur->w, tr, g);
     const int sw = cur->ws[tr * 4 + g];
