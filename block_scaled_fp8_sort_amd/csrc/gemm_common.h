@@ -91,6 +91,102 @@ __device__ __forceinline__ TileCoord locate_tile(int t, int E, int BM, int NT, c
   return c;
 }
 
+// Two-phase tile table of the tiled GEMMs (256-row m-tiles, an expert's last,
+// partial m-tile run at 64, 128 or 256 rows).  Phase 1 holds the short
+// remainder tiles (at most 128 rows) of experts that also have full m-tiles, NT
+// per such expert; phase 0 holds every other tile, in expert order and
+// tile_position order inside an expert, and comes first.  The long tiles go
+// first, so with round-robin assignment the short remainders fill the last
+// round instead of lengthening it; an expert whose only m-tile is short keeps
+// its place in phase 0, where its weight-streaming tiles interleave with the
+// MFMA-bound ones of the large experts.
+//   off[e]  expert offsets (E + 1)
+//   tp[e]   first phase-0 tile of expert e; tp[E] = phase-0 total
+//   cnt[e]  experts before e that have a phase-1 tile; expert e's phase-1 tiles
+//           are [cnt[e] NT, cnt[e] NT + NT)
+// Returns the total tile count.  All threads of the block must call it.
+__device__ __forceinline__ int has_short_tile(int rows) {
+  return rows > 256 && (rows % 256) > 0 && (rows % 256) <= 128;
+}
+__device__ __forceinline__ int full_m_tiles(int rows) { return (rows + 255) / 256 - has_short_tile(rows); }
+
+template <int THREADS>
+__device__ __forceinline__ int build_tile_table2(const int32_t* offsets, int E, int NT, int* off, int* tp,
+                                                 uint16_t* cnt, int2* scan) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e <= E; e += THREADS) off[e] = offsets[e];
+  __syncthreads();
+  const int seg = (E + THREADS - 1) / THREADS;
+  const int e_lo = min(E, tid * seg), e_hi = min(E, tid * seg + seg);
+  int2 mine = make_int2(0, 0);
+  for (int e = e_lo; e < e_hi; ++e) {
+    const int rows = off[e + 1] - off[e];
+    mine.x += full_m_tiles(rows) * NT;
+    mine.y += has_short_tile(rows);
+  }
+  scan[tid] = mine;
+  __syncthreads();
+  for (int d = 1; d < THREADS; d <<= 1) {
+    const int2 v = tid >= d ? scan[tid - d] : make_int2(0, 0);
+    __syncthreads();
+    scan[tid].x += v.x;
+    scan[tid].y += v.y;
+    __syncthreads();
+  }
+  {
+    int run0 = scan[tid].x - mine.x, run1 = scan[tid].y - mine.y;
+    for (int e = e_lo; e < e_hi; ++e) {
+      const int rows = off[e + 1] - off[e];
+      tp[e] = run0;
+      cnt[e] = (uint16_t)run1;
+      run0 += full_m_tiles(rows) * NT;
+      run1 += has_short_tile(rows);
+    }
+    if (tid == THREADS - 1) {
+      tp[E] = scan[THREADS - 1].x;
+      cnt[E] = (uint16_t)scan[THREADS - 1].y;
+    }
+  }
+  __syncthreads();
+  return tp[E] + (int)cnt[E] * NT;
+}
+
+// Tile t of the two-phase table -> (expert, n-tile, first sorted row, end of
+// the expert's rows), made wave-uniform.
+__device__ __forceinline__ TileCoord locate_tile2(int t, int E, int NT, const int* off, const int* tp,
+                                                  const uint16_t* cnt) {
+  const int total0 = __builtin_amdgcn_readfirstlane(tp[E]);
+  TileCoord c;
+  int lo = 0, hi = E;
+  if (t < total0) {
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tp[mid] <= t) lo = mid; else hi = mid;
+    }
+    c.e = __builtin_amdgcn_readfirstlane(lo);
+    const int m_begin = __builtin_amdgcn_readfirstlane(off[c.e]);
+    c.m_end = __builtin_amdgcn_readfirstlane(off[c.e + 1]);
+    const int loc = t - __builtin_amdgcn_readfirstlane(tp[c.e]);
+    int m_idx, n_idx;
+    tile_position(loc, full_m_tiles(c.m_end - m_begin), NT, m_idx, n_idx);
+    c.n_tile = n_idx;
+    c.m0 = m_begin + m_idx * 256;
+  } else {
+    const int t1 = t - total0;
+    const int j = t1 / NT;  // the j-th expert that has a phase-1 tile
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((int)cnt[mid] <= j) lo = mid; else hi = mid;
+    }
+    c.e = __builtin_amdgcn_readfirstlane(lo);
+    const int m_begin = __builtin_amdgcn_readfirstlane(off[c.e]);
+    c.m_end = __builtin_amdgcn_readfirstlane(off[c.e + 1]);
+    c.n_tile = t1 - j * NT;
+    c.m0 = m_begin + ((c.m_end - m_begin) / 256) * 256;
+  }
+  return c;
+}
+
 // Workgroup id remap for the persistent tile loop: dispatch places block b on
 // XCD b % 8, so consecutive virtual ids go to one XCD and the tiles that share
 // an expert's weight tile share that XCD's L2.

@@ -26,14 +26,17 @@
 //    tile.  Two LDS stages at BM = 256, three at smaller BM (more bytes in
 //    flight per CU, which is what streaming weights at decode sizes needs).
 //  * Operands move global -> LDS by LDS-DMA (global_load_lds_dwordx4, 16 bytes
-//    per lane).  Weights are pre-tiled (tile_layout.h) so each DMA instruction
-//    copies one contiguous 1 KB; activations are stored K-block-major
+//    per lane).  Weights are pre-tiled in MFMA operand order (tile_layout.h), so
+//    each DMA instruction copies one contiguous 1 KB and each fragment read is
+//    linear; activations are stored K-block-major
 //    ([K/128][rows][128 bytes]), so a DMA instruction gathers 8 token rows'
 //    128-byte chunks by per-lane address (the gather is free) without the
 //    same-L2-channel aliasing that 4 KB-strided rows suffer.
 //  * Persistent grid: each workgroup reads the expert offsets, builds the tile
 //    table in LDS (per expert, groups of up to 8 m-tiles, m fastest inside a
-//    group, then n), and walks tiles with a stride of the grid size.
+//    group, then n; the short remainder tiles of large experts after all the
+//    rest, so they fill the last round), and walks tiles with a stride of the
+//    grid size.
 //    Workgroup ids are remapped so that consecutive tiles land on the same XCD
 //    (dispatch is round-robin over the 8 XCDs): a weight tile is shared by the
 //    group's m-tiles in that XCD's L2, and the group's activation rows stay
@@ -75,8 +78,11 @@ constexpr int kMaxBM = 256;
 struct Misc {
   int off[kMaxE + 1];
   int tp[kMaxE + 1];
-  int scan[kThreads];
-  float amax[2][kMaxBM];
+  uint16_t cnt[kMaxE + 2];
+  union {
+    int2 scan[kThreads];     // tile table build (kernel start)
+    float amax[2][kMaxBM];   // SwiGLU epilogue
+  };
 };
 
 // LDS shared by the pipeline stages of every tile height: three stages of the
@@ -89,11 +95,21 @@ constexpr int stages_for() {
 }
 static_assert(stages_for<256>() >= 2 && stages_for<64>() >= 3, "stage area");
 
-// 32 bytes of K (logical chunks 2g and 2g+1 of the 128-byte row) of LDS row tr.
-__device__ __forceinline__ v8i lds_frag(const uint8_t* region, int tr, int g) {
+// The 32 bytes lane group g of an MFMA operand holds: K bytes [16 g, 16 g + 16)
+// and [64 + 16 g, 64 + 16 g + 16) of its row (logical chunks g and 4 + g).
+// Activation row tr of an LDS stage (chunks at their swizzled positions):
+__device__ __forceinline__ v8i lds_frag_a(const uint8_t* region, int tr, int g) {
   const int s = swz(tr);
-  const int4 x0 = *(const int4*)(region + tr * BK + (((2 * g) ^ s) << 4));
-  const int4 x1 = *(const int4*)(region + tr * BK + (((2 * g + 1) ^ s) << 4));
+  const int4 x0 = *(const int4*)(region + tr * BK + ((g ^ s) << 4));
+  const int4 x1 = *(const int4*)(region + tr * BK + (((4 + g) ^ s) << 4));
+  return v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+}
+// 16-row weight group grp of an LDS stage, stored in operand order: lane l's
+// halves at l * 16 and 1024 + l * 16.
+__device__ __forceinline__ v8i lds_frag_w(const uint8_t* region, int grp, int lane) {
+  const uint8_t* b = region + grp * 2048 + lane * 16;
+  const int4 x0 = *(const int4*)b;
+  const int4 x1 = *(const int4*)(b + 1024);
   return v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 }
 
@@ -160,7 +176,7 @@ __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nx
   const vts sav = *(const vts*)(cur->s + (wt * 16 + l16) * TS);
   v8i bf[TS];
 #pragma unroll
-  for (int ti = 0; ti < TS; ++ti) bf[ti] = lds_frag(cur->a, wt * WM + ti * 16 + l16, g);
+  for (int ti = 0; ti < TS; ++ti) bf[ti] = lds_frag_a(cur->a, wt * WM + ti * 16 + l16, g);
   float fg[TS], fu[TS];
 #pragma unroll
   for (int ti = 0; ti < TS; ++ti) {
@@ -172,7 +188,7 @@ __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nx
   // ni - 1) into the accumulators, and the weight fragment of sub-tile ni + 1 is
   // read from LDS meanwhile.  sched_barrier(0) keeps this program order.
   v4f part[2][TS];
-  v8i af = lds_frag(cur->w, wn * 128 + l16, g);
+  v8i af = lds_frag_w(cur->w, wn * 8, lane);
 #pragma unroll
   for (int ni = 0; ni <= 8; ++ni) {
     // the DMAs of block kb + STAGES - 1 go out spread over the sub-tiles: issued
@@ -182,7 +198,7 @@ __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nx
     for (int idx = 0; idx < LOADS; ++idx)
       if (idx * 8 / LOADS == ni) issue_part<BM>(nxt, src, kb_dma, wave, lane, idx);
     v8i af_next = af;
-    if (ni < 7) af_next = lds_frag(cur->w, wn * 128 + (ni + 1) * 16 + l16, g);
+    if (ni < 7) af_next = lds_frag_w(cur->w, wn * 8 + ni + 1, lane);
     const int pn = ni - 1;
     const bool up = PAIRED && (pn & 1);
 #pragma unroll
@@ -355,18 +371,18 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Mis
 
 // Persistent kernel.  An expert's rows are cut into 256-row m-tiles; the last,
 // partial one runs at the smallest height of {64, 128, 256} that covers it, so
-// little MFMA work goes to padding rows while the number of tiles, and so the
-// weight traffic, stays that of 256-row tiles.
+// little MFMA work goes to padding rows while the number of tiles stays that of
+// 256-row tiles.  Tiles come from the two-phase table (longest first).
 template <int EPI, bool PAIRED>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t area[kStageArea];
   __shared__ __attribute__((aligned(16))) Misc misc;
   const int E = p.E, N = p.N;
   const int NT = PAIRED ? (N / 2) / 128 : (N + BN - 1) / BN;
-  const int total = build_tile_table<kThreads>(p.offsets, E, kMaxBM, NT, misc.off, misc.tp, misc.scan);
+  const int total = build_tile_table2<kThreads>(p.offsets, E, NT, misc.off, misc.tp, misc.cnt, misc.scan);
   const int G = gridDim.x;
   for (int t = xcd_virtual_block(); t < total; t += G) {
-    const TileCoord tc = locate_tile(t, E, kMaxBM, NT, misc.off, misc.tp);
+    const TileCoord tc = locate_tile2(t, E, NT, misc.off, misc.tp, misc.cnt);
     const int left = tc.m_end - tc.m0;
     if (left > 128)
       run_tile<256, EPI, PAIRED>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end);

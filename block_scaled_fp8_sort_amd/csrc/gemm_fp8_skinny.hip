@@ -239,15 +239,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_skinny_kernel(GemmParams
   int t = xcd_virtual_block();
   if (t >= total) return;  // whole workgroup: no barrier follows
 
-  // this lane's byte offsets inside a 32 KB K block of the tile: row group q/2,
-  // logical chunk g (q even) or 4 + g (q odd), at its swizzled position
+  // this lane's byte offsets inside a 32 KB K block of the tile: the wave's row
+  // group 2 wave + q / 2, half q % 2 (logical chunk g or 4 + g); the tile stores
+  // groups in operand order, so each load instruction reads 1 KB contiguous
   uint32_t w_off[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int tr = 32 * wave + 16 * (q >> 1) + l16;
-    const int c = (q & 1) ? 4 + g : g;
-    w_off[q] = (uint32_t)tr * BK + (uint32_t)((c ^ swz(tr)) << 4);
-  }
+  for (int q = 0; q < 4; ++q) w_off[q] = (uint32_t)((2 * wave + (q >> 1)) * 2048 + (q & 1) * 1024 + lane * 16);
 
   fetch_rows<EPI>(p, misc, t, G, total, NT);
   Src cur = make_src(p, misc, t, total, NT, KB, NB, PAIRED, wave, lane, misc.arow[0][l16], zero);

@@ -40,7 +40,7 @@ constexpr int kARow = 128;  // bytes of a 128-wide K block of one FP8 activation
 
 template <int BM>
 struct StageBuf {
-  uint8_t w[BN * kWRow];     // FP4 weight rows (swz4 chunk order)
+  uint8_t w[BN * kWRow];     // FP4 weight rows (16-row groups in operand order)
   uint8_t a[BM * kARow];     // FP8 activation rows (swz chunk order)
   uint8_t ws[BN * 4];        // weight scale bytes [row][4]
   uint8_t as[BM * 4];        // activation scale bytes [row][4]
@@ -52,7 +52,8 @@ constexpr int kMaxBM = 256;
 struct Misc {
   int off[kMaxE + 1];
   int tp[kMaxE + 1];
-  int scan[kThreads];
+  uint16_t cnt[kMaxE + 2];
+  int2 scan[kThreads];
 };
 
 // LDS shared by the pipeline stages of every tile height: four stages of the
@@ -112,9 +113,10 @@ __device__ __forceinline__ void issue_stage(StageBuf<BM>* st, const TileSrc<BM>&
   for (int idx = 0; idx < LOADS; ++idx) issue_part<BM>(st, src, kb, wave, lane, idx);
 }
 
-// 16 bytes = 32 FP4 values, K elements [32 g, 32 g + 32) of weight row tr
-__device__ __forceinline__ v8i frag_w(const uint8_t* w, int tr, int g) {
-  const int4 x = *(const int4*)(w + tr * kWRow + ((g ^ swz4(tr)) << 4));
+// 16 bytes = 32 FP4 values, K elements [32 g, 32 g + 32) of row l % 16 of the
+// 16-row weight group grp, stored in operand order (lane l at l * 16)
+__device__ __forceinline__ v8i frag_w(const uint8_t* w, int grp, int lane) {
+  const int4 x = *(const int4*)(w + grp * 1024 + lane * 16);
   return v8i{x.x, x.y, x.z, x.w, 0, 0, 0, 0};
 }
 // 32 bytes = K elements [16 g, 16 g + 16) and [64 + 16 g, 64 + 16 g + 16) of activation row tr
@@ -155,7 +157,7 @@ __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nx
     for (int idx = 0; idx < LOADS; ++idx)
       if (idx * 8 / LOADS == ni) issue_part<BM>(nxt, src, kb_dma, wave, lane, idx);
     const int tr = wn * 128 + ni * 16 + l16;
-    const v8i af = frag_w(cur->w, tr, g);
+    const v8i af = frag_w(cur->w, wn * 8 + ni, lane);
     const int sw = cur->ws[tr * 4 + g];
 #pragma unroll
     for (int ti = 0; ti < TS; ++ti)
@@ -301,17 +303,18 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, int
 }
 
 // Persistent kernel; the last, partial m-tile of an expert runs at the
-// smallest height of {64, 128, 256} that covers it (as in the FP8 kernel).
+// smallest height of {64, 128, 256} that covers it, and tiles come from the
+// two-phase, longest-first table (as in the FP8 kernel).
 template <int EPI, bool PAIRED>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t area[kStageArea];
   __shared__ __attribute__((aligned(16))) Misc misc;
   const int E = p.E, N = p.N;
   const int NT = PAIRED ? (N / 2) / 128 : (N + BN - 1) / BN;
-  const int total = build_tile_table<kThreads>(p.offsets, E, kMaxBM, NT, misc.off, misc.tp, misc.scan);
+  const int total = build_tile_table2<kThreads>(p.offsets, E, NT, misc.off, misc.tp, misc.cnt, misc.scan);
   const int G = gridDim.x;
   for (int t = xcd_virtual_block(); t < total; t += G) {
-    const TileCoord tc = locate_tile(t, E, kMaxBM, NT, misc.off, misc.tp);
+    const TileCoord tc = locate_tile2(t, E, NT, misc.off, misc.tp, misc.cnt);
     const int left = tc.m_end - tc.m0;
     if (left > 128)
       run_tile<256, EPI, PAIRED>(p, area, tc.e, tc.n_tile, tc.m0, tc.m_end);

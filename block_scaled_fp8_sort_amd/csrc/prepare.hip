@@ -32,10 +32,10 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
   }
 }
 
-// One thread per 16-byte chunk of the tiled destination
-// [E][NT][KB][256][128]: find its tile row tr and logical chunk c (physical
-// position p = c ^ swz(tr)), copy the source row's 16 K-bytes there, or zeros
-// for a padding row.
+// One thread per 16-byte piece of the tiled destination [E][NT][KB][32 KB]:
+// find the tile row tr and logical chunk c the piece holds (the MFMA operand
+// order of tile_layout.h), copy the source row's 16 K-bytes there, or zeros for
+// a padding row.
 template <bool PAIRED>
 __global__ __launch_bounds__(256) void tile_weight_kernel(const uint8_t* __restrict__ src, int nn, int32_t N,
                                                           int32_t K, int32_t NT, int64_t n_chunks,
@@ -43,15 +43,15 @@ __global__ __launch_bounds__(256) void tile_weight_kernel(const uint8_t* __restr
   const int KB = K / kBlockK;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < n_chunks; d += stride) {
-    const int p = (int)(d & 7);
-    int64_t rest = d >> 3;
-    const int tr = (int)(rest % kTileN);
-    rest /= kTileN;
+    const int piece = (int)(d & 2047);  // 16-byte piece inside the 32 KB block
+    int64_t rest = d >> 11;
     const int kb = (int)(rest % KB);
     rest /= KB;
     const int nt = (int)(rest % NT);
     const int64_t e = rest / NT;
-    const int c = p ^ swz(tr);
+    const int grp = piece >> 7, h = (piece >> 6) & 1, l = piece & 63;
+    const int tr = grp * 16 + (l & 15);
+    const int c = 4 * h + (l >> 4);
     const int row = tile_src_row<PAIRED>(nt, tr, N);
     uint4 v = make_uint4(0, 0, 0, 0);
     if (row >= 0) {
@@ -68,23 +68,23 @@ __global__ __launch_bounds__(256) void tile_weight_kernel(const uint8_t* __restr
   }
 }
 
-// MX codes: one thread per 16-byte chunk of [E][NT][KB][256][64]; the source row
-// is packed [E][N][K/2].
+// MX codes: one thread per 16-byte piece of [E][NT][KB][16 KB] (the FP4 MFMA
+// operand order of tile_layout.h); the source row is packed [E][N][K/2].
 template <bool PAIRED>
 __global__ __launch_bounds__(256) void tile_weight_mx_kernel(const uint8_t* __restrict__ src, int32_t N, int32_t K,
                                                              int32_t NT, int64_t n_chunks, uint8_t* __restrict__ dst) {
   const int KB = K / 128;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < n_chunks; d += stride) {
-    const int p = (int)(d & 3);
-    int64_t rest = d >> 2;
-    const int tr = (int)(rest % kTileN);
-    rest /= kTileN;
+    const int piece = (int)(d & 1023);  // 16-byte piece inside the 16 KB block
+    int64_t rest = d >> 10;
     const int kb = (int)(rest % KB);
     rest /= KB;
     const int nt = (int)(rest % NT);
     const int64_t e = rest / NT;
-    const int c = p ^ swz4(tr);
+    const int grp = piece >> 6, l = piece & 63;
+    const int tr = grp * 16 + (l & 15);
+    const int c = l >> 4;
     const int row = tile_src_row<PAIRED>(nt, tr, N);
     uint4 v = make_uint4(0, 0, 0, 0);
     if (row >= 0) v = *(const uint4*)(src + (e * N + row) * (int64_t)(K / 2) + (int64_t)kb * 64 + c * 16);

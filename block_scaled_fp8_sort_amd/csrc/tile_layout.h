@@ -2,12 +2,15 @@
 // shared by the weight-preparation kernel and the grouped GEMMs.
 //
 // A weight [E, N, K] (N output rows, K = reduction) is stored as
-//   [E][NT = ceil(N / 256)][KB = K / 128][256 tile rows][128 bytes],
+//   [E][NT = ceil(N / 256)][KB = K / 128][16 row groups][2048 bytes],
 // i.e. every 128-wide K block of a 256-row tile is one contiguous 32 KB piece,
-// and every group of 8 tile rows is one contiguous 1 KB piece: one LDS-DMA
-// wave instruction (64 lanes x 16 bytes) copies it straight into LDS.  Inside a
-// 128-byte row the 16-byte chunks are permuted by swz(tile_row) so that the MFMA
-// fragment reads from LDS are free of bank conflicts.  Rows past N are zero.
+// and every group of 16 tile rows is one contiguous 2 KB piece in the order
+// the MFMA A operand wants it: [half h][lane l][16 bytes], where lane l holds
+// tile row 16 * group + l % 16 and logical 16-byte chunk c = 4 h + l / 16 of its
+// 128-byte row (K bytes [16 c, 16 c + 16)).  So a wave's fragment of a 16-row
+// group is two contiguous 1 KB reads (lane l at l * 16 and 1024 + l * 16): one
+// coalesced global load each, one LDS-DMA wave instruction each, and LDS reads
+// with no bank conflicts and no address swizzle.  Rows past N are zero.
 //
 // Paired tiles (the gate_up weight, N = 2I): tile j holds the 128 gate rows
 // [128 j, 128 j + 128) and the 128 matching up rows [I + 128 j, ...), interleaved
@@ -17,7 +20,9 @@
 //
 // MX weights (e2m1 packed two per byte along K, even k in the low nibble, a
 // UE8M0 byte per 32 K) use the same tiling with 64-byte rows (128 K elements):
-//   codes  [E][NT][K/128][256 tile rows][64 bytes], chunks permuted by swz4(row),
+//   codes  [E][NT][K/128][16 row groups][1024 bytes], a group stored as
+//          [lane l][16 bytes] = tile row 16 * group + l % 16, chunk l / 16 (K
+//          elements [32 c, 32 c + 32)), the FP4 MFMA operand order,
 //   scales [E][NT][K/128][256 tile rows][4 bytes]  (the 4 scale bytes of the row's
 //                                                   128-wide K block, in order).
 // MX activation / h scales are [K/128][rows][4 bytes] for the same reason: one
@@ -31,14 +36,10 @@ namespace moe {
 constexpr int kTileN = 256;  // weight rows per tile
 constexpr int kBlockK = 128; // bytes of K per block row (FP8: 128 elements)
 
-// Physical 16-byte chunk position of logical chunk c in tile row r.  Rows
-// r..r+7 (and with 64 banks r..r+15) put the same logical chunk in distinct banks.
+// Physical 16-byte chunk position of logical chunk c in row r of an LDS
+// activation stage (128-byte rows gathered by LDS-DMA): rows r..r+7 (and with
+// 64 banks r..r+15) put the same logical chunk in distinct banks.
 __host__ __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-
-// Chunk permutation of a 64-byte (MX weight) row: rows r..r+7 with the same
-// parity, and rows r..r+15 with the same r mod 4, get distinct chunks, which
-// keeps 16-byte fragment reads free of bank conflicts with 32 or 64 banks.
-__host__ __device__ __forceinline__ int swz4(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
 
 // Source row (within the expert) of tile row tr of tile nt.  Returns -1 for a
 // padding row (plain tiles past N).
