@@ -52,7 +52,8 @@ class MoeGemmArgs(ctypes.Structure):
                 ("a_codes", _P), ("a_scales", _P), ("a_rows", _I32), ("a_row_index", _P), ("a_row_divisor", _I32),
                 ("expert_offsets", _P), ("epilogue", ctypes.c_int),
                 ("c_f32", _P), ("h_codes", _P), ("h_scales", _P), ("has_swiglu_limit", _I32),
-                ("swiglu_limit", _F32), ("slot_out", _P), ("top_k_weights", _P), ("slot_of_row", _P)]
+                ("swiglu_limit", _F32), ("slot_out", _P), ("top_k_weights", _P), ("slot_of_row", _P),
+                ("tile_counters", _P)]
 
 
 class MoeDebug(ctypes.Structure):
@@ -249,13 +250,21 @@ def prepare_weights(gate_up: torch.Tensor, gate_up_scale: torch.Tensor, down: to
 
 
 # -------------------------------------------------------------- grouped GEMM
+TILE_COUNTERS_INTS = 256  # MOE_TILE_COUNTERS_BYTES / 4
+
+
 def grouped_gemm(weights: Weights, which: int, a_codes, a_scales, a_rows: int, expert_offsets, epilogue: int,
                  max_rows: int, a_row_index=None, a_row_divisor: int = 1, c_f32=None, h_codes=None, h_scales=None,
-                 swiglu_limit: Optional[float] = None, slot_out=None, top_k_weights=None, slot_of_row=None):
+                 swiglu_limit: Optional[float] = None, slot_out=None, top_k_weights=None, slot_of_row=None,
+                 tile_counters="new"):
     """Enqueue one grouped GEMM (see moe_grouped_gemm); outputs are caller tensors.
 
     which = 0 multiplies by the gate_up weight, 1 by the down weight.  A is
-    K-block-major with a_rows rows per plane.
+    K-block-major with a_rows rows per plane.  tile_counters: "new" (default)
+    allocates zeroed counters for dynamic tile dispensing, as the fused forward
+    uses; a caller's int32 tensor of TILE_COUNTERS_INTS zeros may be reused
+    across launches that do not overlap (each launch leaves it zero); None takes
+    tiles in the fixed round-robin order.
     """
     lib = load_library()
     a = MoeGemmArgs()
@@ -270,6 +279,13 @@ def grouped_gemm(weights: Weights, which: int, a_codes, a_scales, a_rows: int, e
     a.has_swiglu_limit = 0 if swiglu_limit is None else 1
     a.swiglu_limit = 0.0 if swiglu_limit is None else float(swiglu_limit)
     a.slot_out, a.top_k_weights, a.slot_of_row = _ptr(slot_out), _ptr(top_k_weights), _ptr(slot_of_row)
+    if isinstance(tile_counters, str):
+        tile_counters = torch.zeros(TILE_COUNTERS_INTS, dtype=torch.int32, device=a_codes.device)
+    elif tile_counters is not None:
+        _need(tile_counters, "tile_counters", torch.int32)
+        if tile_counters.numel() < TILE_COUNTERS_INTS:
+            raise ValueError(f"tile_counters needs {TILE_COUNTERS_INTS} int32")
+    a.tile_counters = _ptr(tile_counters)
     _check(lib.moe_grouped_gemm(ctypes.byref(a), _stream(a_codes.device)))
 
 

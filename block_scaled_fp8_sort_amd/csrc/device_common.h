@@ -83,7 +83,13 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
 }
 // The same 16-byte DMA with a wave-uniform 64-bit base in SGPRs and a 32-bit
 // per-lane byte offset (the saddr form): no per-lane 64-bit address math.
-__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
+__device__ __forceinline__ void lds_dma16_s(const void* sbase_any, uint32_t voff, uint32_t lds) {
+  // the base is wave-uniform; under register pressure the compiler may compute
+  // it in VGPRs, so move it to SGPRs explicitly (a no-op when it already is)
+  const uint64_t a = (uint64_t)(uintptr_t)sbase_any;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const void* sbase = (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"

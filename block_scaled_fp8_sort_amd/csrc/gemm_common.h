@@ -187,6 +187,64 @@ __device__ __forceinline__ TileCoord locate_tile2(int t, int E, int NT, const in
   return c;
 }
 
+// Dynamic tile dispensing, one dispenser per XCD.  The tile sequence is cut
+// into windows of kWindow consecutive tiles and window w belongs to dispenser
+// w % 8, so each XCD gets a fair slice of the whole sequence (its short tail
+// included) while the tiles that share a weight or activation tile still run
+// together on one XCD, whose workgroups (dispatch puts block b on XCD b % 8)
+// take them in order from an atomic counter.  Counter x lives at
+// counters[x * 32] (own 128-byte line).  Each workgroup makes exactly one failed
+// grab, so the grab that returns count + workgroups - 1 is the dispenser's last;
+// it resets the counter to 0, and the counters are zero again when the launch
+// ends.  With a grid that is not a multiple of 8, one dispenser hands out the
+// plain sequence.
+constexpr int kWindow = 32;
+constexpr int kCounterStride = 32;  // ints between counters: 128 bytes
+
+struct Dispenser {
+  int32_t* ctr;  // this workgroup's counter
+  int x, nd;     // dispenser index, number of dispensers
+  int count;     // tiles it hands out
+  int last;      // value of its final grab
+};
+
+__device__ __forceinline__ Dispenser make_dispenser(int32_t* counters, int total, int G) {
+  Dispenser d;
+  d.nd = (G % 8 == 0) ? 8 : 1;
+  d.x = (int)blockIdx.x % d.nd;
+  if (d.nd == 1) {
+    d.count = total;
+  } else {
+    const int nwin = (total + kWindow - 1) / kWindow;
+    const int owned = d.x < nwin ? (nwin - 1 - d.x) / 8 + 1 : 0;
+    d.count = owned * kWindow;
+    if (nwin > 0 && (nwin - 1) % 8 == d.x) d.count -= nwin * kWindow - total;
+  }
+  d.last = d.count + G / d.nd - 1;
+  d.ctr = counters + d.x * kCounterStride;
+  return d;
+}
+
+// The tile of the dispenser's v-th grab (>= total once it is exhausted).
+__device__ __forceinline__ int dispensed_tile(const Dispenser& d, int v) {
+  if (d.nd == 1) return v;
+  return ((v / kWindow) * 8 + d.x) * kWindow + (v % kWindow);
+}
+
+// One grab (call from a single thread).  The counter address is taken through
+// a VGPR so the atomic is a vector memory atomic.
+__device__ __forceinline__ int grab_tile(const Dispenser& d) {
+  int zero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+  return atomicAdd(d.ctr + zero, 1);
+}
+
+__device__ __forceinline__ void reset_dispenser(const Dispenser& d) {
+  int zero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+  atomicExch(d.ctr + zero, 0);
+}
+
 // Workgroup id remap for the persistent tile loop: dispatch places block b on
 // XCD b % 8, so consecutive virtual ids go to one XCD and the tiles that share
 // an expert's weight tile share that XCD's L2.

@@ -53,6 +53,7 @@ struct Misc {
   int off[kMaxE + 1];
   int tp[kMaxE + 1];
   uint16_t cnt[kMaxE + 2];
+  int next[2];  // dispensed tile values, alternating per tile
   int2 scan[kThreads];
 };
 
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmParams p) {
   const int NT = PAIRED ? (N / 2) / 128 : (N + BN - 1) / BN;
   const int total = build_tile_table2<kThreads>(p.offsets, E, NT, misc.off, misc.tp, misc.cnt, misc.scan);
   const int G = gridDim.x;
-  for (int t = xcd_virtual_block(); t < total; t += G) {
+  auto run = [&](int t) {
     const TileCoord tc = locate_tile2(t, E, NT, misc.off, misc.tp, misc.cnt);
     const int left = tc.m_end - tc.m0;
     if (left > 128)
@@ -322,6 +323,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmParams p) {
       run_tile<128, EPI, PAIRED>(p, area, tc.e, tc.n_tile, tc.m0, tc.m_end);
     else
       run_tile<64, EPI, PAIRED>(p, area, tc.e, tc.n_tile, tc.m0, tc.m_end);
+  };
+  // tiles come from the per-XCD dispensers when counters are given (the next
+  // tile is grabbed at the start of the current one and handed to every wave
+  // through LDS after it), else in the fixed round-robin order
+  const bool dyn = p.sched != nullptr;
+  const int tid = threadIdx.x;
+  Dispenser d{};
+  int v = 0;
+  if (dyn) {
+    d = make_dispenser(p.sched, total, G);
+    if (tid == 0) misc.next[0] = grab_tile(d);
+    __syncthreads();
+    v = __builtin_amdgcn_readfirstlane(misc.next[0]);  // the same in every lane
+  }
+  const int vb = xcd_virtual_block();
+  for (int i = 1;; ++i) {
+    const int t = dyn ? dispensed_tile(d, v) : vb + (i - 1) * G;
+    if (t < 0 || t >= total) {  // (t < 0 only from counters that were not zeroed)
+      if (dyn && tid == 0 && v == d.last) reset_dispenser(d);
+      break;
+    }
+    int v_next = 0;
+    if (dyn && tid == 0) v_next = grab_tile(d);
+    run(t);
+    if (dyn) {
+      if (tid == 0) misc.next[i & 1] = v_next;
+      __syncthreads();
+      v = __builtin_amdgcn_readfirstlane(misc.next[i & 1]);
+    }
   }
 }
 

@@ -29,6 +29,8 @@ struct GemmParams {
   uint16_t* slot_out;
   const float* top_k_weights;
   const int32_t* slot_of_row;
+  // tile dispensing: NULL = static order, else 8 zeroed counters 128 bytes apart
+  int32_t* sched;
 };
 
 enum Epilogue { kEpiStoreF32 = 0, kEpiSwiGLUQuant = 1, kEpiWeightedScatter = 2 };
@@ -39,12 +41,17 @@ size_t route_sort_ws_bytes(int32_t S, int32_t E);
 hipError_t launch_route_sort(const int32_t* ids, int32_t S, int32_t E, int32_t expert_begin, int32_t* sorted_slot,
                              int32_t* offsets, int32_t* slot_pos, int32_t* invalid_count, void* ws,
                              hipStream_t stream);
+// The route sort, also setting zero[0 .. n_zero) to 0.
+hipError_t launch_route_sort_zero(const int32_t* ids, int32_t S, int32_t E, int32_t expert_begin,
+                                  int32_t* sorted_slot, int32_t* offsets, int32_t* slot_pos, int32_t* invalid_count,
+                                  void* ws, int32_t* zero, int32_t n_zero, hipStream_t stream);
 // The route sort (without slot_pos) and the activation quantization of x
-// [rows, H], in one launch for small batches, else one after the other.
+// [rows, H], in one launch for small batches, else one after the other; the
+// first kernel also sets zero[0 .. n_zero) to 0 (the GEMMs' tile counters).
 hipError_t launch_route_sort_and_quant(const int32_t* ids, int32_t S, int32_t E, int32_t expert_begin,
                                       int32_t* sorted_slot, int32_t* offsets, int32_t* invalid_count, void* sort_ws,
                                       const uint16_t* x, int32_t rows, int32_t H, int fmt, uint8_t* codes,
-                                      void* scales, hipStream_t stream);
+                                      void* scales, int32_t* zero, int32_t n_zero, hipStream_t stream);
 hipError_t launch_quant_act(const uint16_t* x, int32_t rows, int32_t H, int fmt, uint8_t* codes, void* scales,
                             hipStream_t stream);
 // epi: Epilogue; paired: gate/up row pairing of B (used with kEpiSwiGLUQuant and

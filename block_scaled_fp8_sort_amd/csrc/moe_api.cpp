@@ -110,7 +110,7 @@ moe_status hip_status(hipError_t e, const char* what) {
 
 // ---------------------------------------------------------- forward workspace
 struct FwdLayout {
-  size_t sorted_slot, offsets, act_codes, act_scales, h_codes, h_scales, slot_out, sort_ws, total;
+  size_t sorted_slot, offsets, act_codes, act_scales, h_codes, h_scales, slot_out, sort_ws, sched, total;
 };
 
 FwdLayout fwd_layout(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I, int fmt) {
@@ -127,6 +127,7 @@ FwdLayout fwd_layout(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I, int 
   L.h_scales = o; o = align_up(o + (mx ? S * (I / 32) : 4 * S * (I / 128)), A);
   L.slot_out = o; o = align_up(o + 2 * S * H, A);
   L.sort_ws = o; o = align_up(o + moe::route_sort_ws_bytes((int32_t)S, E), A);
+  L.sched = o; o = align_up(o + 2 * MOE_TILE_COUNTERS_BYTES, A);  // gate_up's and down's tile counters
   L.total = o;
   return L;
 }
@@ -190,6 +191,7 @@ moe::GemmParams to_params(const moe_gemm_args* a) {
   p.K = a->which == 0 ? w->H : w->I;
   p.max_rows = a->max_rows;
   p.c_f32 = a->c_f32;
+  p.sched = a->tile_counters;
   p.h_codes = a->h_codes;
   p.h_scales = a->h_scales;
   p.has_limit = a->has_swiglu_limit ? 1 : 0;
@@ -379,6 +381,7 @@ moe_status moe_grouped_gemm(const moe_gemm_args* args, hipStream_t stream) {
   if ((st = check_ptr(args->a_codes, dev, "a_codes")) != MOE_OK ||
       (st = check_ptr(args->weights->w13, dev, "weights")) != MOE_OK)
     return st;
+  if (args->tile_counters && (st = check_ptr(args->tile_counters, dev, "tile_counters")) != MOE_OK) return st;
   const moe::GemmParams p = to_params(args);
   const bool paired = args->which == 0;
   st = hip_status(launch_gemm(p, args->weights->fmt, (int)args->epilogue, paired, cus, stream),
@@ -433,9 +436,11 @@ moe_status moe_experts_forward(const moe_weights* w, const uint16_t* hidden_stat
   uint16_t* slot_out = (uint16_t*)(base + L.slot_out);
   const int32_t expert_begin = opt ? opt->expert_begin : 0;
 
+  int32_t* sched = (int32_t*)(base + L.sched);
   hipError_t he = moe::launch_route_sort_and_quant(top_k_index, S, E, expert_begin, sorted_slot, offsets,
                                                    opt ? opt->invalid_count : nullptr, base + L.sort_ws, hidden_states,
-                                                   T, H, w->fmt, act_codes, act_scales, stream);
+                                                   T, H, w->fmt, act_codes, act_scales, sched,
+                                                   2 * MOE_TILE_COUNTERS_BYTES / 4, stream);
   if (he != hipSuccess) return hip_status(he, "route sort / quant launch");
 
   moe::GemmParams p1{};
@@ -452,6 +457,7 @@ moe_status moe_experts_forward(const moe_weights* w, const uint16_t* hidden_stat
   p1.K = H;
   p1.max_rows = S;
   p1.h_codes = h_codes;
+  p1.sched = sched;
   p1.h_scales = h_scales;
   p1.has_limit = has_limit ? 1 : 0;
   p1.limit = has_limit ? opt->swiglu_limit : 0.0f;
@@ -474,6 +480,7 @@ moe_status moe_experts_forward(const moe_weights* w, const uint16_t* hidden_stat
   p2.slot_out = slot_out;
   p2.top_k_weights = top_k_weights;
   p2.slot_of_row = sorted_slot;
+  p2.sched = sched + MOE_TILE_COUNTERS_BYTES / 4;
   he = launch_gemm(p2, w->fmt, moe::kEpiWeightedScatter, false, cus, stream);
   if (he != hipSuccess) return hip_status(he, "down gemm launch");
 

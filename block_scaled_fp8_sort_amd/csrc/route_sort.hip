@@ -84,7 +84,10 @@ __device__ __forceinline__ void scatter_chunk(const int32_t* __restrict__ ids, i
 // row E + 1.
 __global__ __launch_bounds__(kChunkWaves * kWave) void sort_hist_kernel(const int32_t* __restrict__ ids, int32_t S,
                                                                        int32_t E, int32_t expert_begin, int32_t chunk,
-                                                                       int32_t n_chunks, int32_t* __restrict__ hist) {
+                                                                       int32_t n_chunks, int32_t* __restrict__ hist,
+                                                                       int32_t* __restrict__ zero, int32_t n_zero) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < n_zero; i += blockDim.x) zero[i] = 0;
   extern __shared__ int32_t lh[];  // [kChunkWaves][E + 2]
   const int K2 = E + 2;
   const int wl = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -272,7 +275,9 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(const int32_t*
                                                                    int32_t* __restrict__ sorted_slot,
                                                                    int32_t* __restrict__ offsets,
                                                                    int32_t* __restrict__ slot_pos,
-                                                                   int32_t* __restrict__ invalid_count) {
+                                                                   int32_t* __restrict__ invalid_count,
+                                                                   int32_t* __restrict__ zero, int32_t n_zero) {
+  for (int i = threadIdx.x; i < n_zero; i += blockDim.x) zero[i] = 0;
   sort_one_workgroup(ids, S, E, expert_begin, sorted_slot, offsets, slot_pos, invalid_count);
 }
 
@@ -284,7 +289,10 @@ template <int BLOCK>
 __global__ __launch_bounds__(kSortThreads) void route_quant_kernel(
     const int32_t* __restrict__ ids, int32_t S, int32_t E, int32_t expert_begin, int32_t* __restrict__ sorted_slot,
     int32_t* __restrict__ offsets, int32_t* __restrict__ invalid_count, const uint4* __restrict__ x,
-    int64_t n_chunks, int32_t rows, int32_t H, uint8_t* __restrict__ codes, void* __restrict__ scales) {
+    int64_t n_chunks, int32_t rows, int32_t H, uint8_t* __restrict__ codes, void* __restrict__ scales,
+    int32_t* __restrict__ zero, int32_t n_zero) {
+  if (blockIdx.x == 1 || gridDim.x == 1)
+    for (int i = threadIdx.x; i < n_zero; i += blockDim.x) zero[i] = 0;
   if (blockIdx.x == 0) {
     sort_one_workgroup(ids, S, E, expert_begin, sorted_slot, offsets, nullptr, invalid_count);
     return;
@@ -308,9 +316,16 @@ size_t route_sort_ws_bytes(int32_t S, int32_t E) {
 hipError_t launch_route_sort(const int32_t* ids, int32_t S, int32_t E, int32_t expert_begin, int32_t* sorted_slot,
                              int32_t* offsets, int32_t* slot_pos, int32_t* invalid_count, void* ws,
                              hipStream_t stream) {
+  return launch_route_sort_zero(ids, S, E, expert_begin, sorted_slot, offsets, slot_pos, invalid_count, ws, nullptr, 0,
+                                stream);
+}
+
+hipError_t launch_route_sort_zero(const int32_t* ids, int32_t S, int32_t E, int32_t expert_begin,
+                                  int32_t* sorted_slot, int32_t* offsets, int32_t* slot_pos, int32_t* invalid_count,
+                                  void* ws, int32_t* zero, int32_t n_zero, hipStream_t stream) {
   if (S < kMultiBlockFrom) {
     hipLaunchKernelGGL(route_sort_kernel, dim3(1), dim3(kSortThreads), route_sort_lds_bytes(E), stream, ids, S, E,
-                       expert_begin, sorted_slot, offsets, slot_pos, invalid_count);
+                       expert_begin, sorted_slot, offsets, slot_pos, invalid_count, zero, n_zero);
     return hipGetLastError();
   }
   const int32_t chunk = sort_chunk(S, E);
@@ -318,7 +333,8 @@ hipError_t launch_route_sort(const int32_t* ids, int32_t S, int32_t E, int32_t e
   const int blocks = (n_chunks + kChunkWaves - 1) / kChunkWaves;
   int32_t* hist = (int32_t*)ws;
   hipLaunchKernelGGL(sort_hist_kernel, dim3(blocks), dim3(kChunkWaves * kWave),
-                     sizeof(int32_t) * kChunkWaves * (E + 2), stream, ids, S, E, expert_begin, chunk, n_chunks, hist);
+                     sizeof(int32_t) * kChunkWaves * (E + 2), stream, ids, S, E, expert_begin, chunk, n_chunks, hist,
+                     zero, n_zero);
   hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, E, n_chunks, hist, offsets,
                      invalid_count);
   hipLaunchKernelGGL(sort_scatter_kernel, dim3(blocks), dim3(kChunkWaves * kWave),
@@ -330,11 +346,11 @@ hipError_t launch_route_sort(const int32_t* ids, int32_t S, int32_t E, int32_t e
 hipError_t launch_route_sort_and_quant(const int32_t* ids, int32_t S, int32_t E, int32_t expert_begin,
                                       int32_t* sorted_slot, int32_t* offsets, int32_t* invalid_count, void* sort_ws,
                                       const uint16_t* x, int32_t rows, int32_t H, int fmt, uint8_t* codes,
-                                      void* scales, hipStream_t stream) {
+                                      void* scales, int32_t* zero, int32_t n_zero, hipStream_t stream) {
   const int64_t n_chunks = (int64_t)rows * H / 8;
   if (S >= kMultiBlockFrom || n_chunks == 0) {
-    hipError_t e = launch_route_sort(ids, S, E, expert_begin, sorted_slot, offsets, nullptr, invalid_count, sort_ws,
-                                     stream);
+    hipError_t e = launch_route_sort_zero(ids, S, E, expert_begin, sorted_slot, offsets, nullptr, invalid_count,
+                                          sort_ws, zero, n_zero, stream);
     if (e != hipSuccess) return e;
     return launch_quant_act(x, rows, H, fmt, codes, scales, stream);
   }
@@ -343,11 +359,11 @@ hipError_t launch_route_sort_and_quant(const int32_t* ids, int32_t S, int32_t E,
   if (fmt == 0)
     hipLaunchKernelGGL(route_quant_kernel<128>, dim3(blocks), dim3(kSortThreads), route_sort_lds_bytes(E), stream,
                        ids, S, E, expert_begin, sorted_slot, offsets, invalid_count, (const uint4*)x, n_chunks, rows,
-                       H, codes, scales);
+                       H, codes, scales, zero, n_zero);
   else
     hipLaunchKernelGGL(route_quant_kernel<32>, dim3(blocks), dim3(kSortThreads), route_sort_lds_bytes(E), stream,
                        ids, S, E, expert_begin, sorted_slot, offsets, invalid_count, (const uint4*)x, n_chunks, rows,
-                       H, codes, scales);
+                       H, codes, scales, zero, n_zero);
   return hipGetLastError();
 }
 

@@ -206,7 +206,15 @@ typedef struct moe_gemm_args {
   uint16_t* slot_out;
   const float* top_k_weights;
   const int32_t* slot_of_row;
+  /* May be NULL (tiles are then taken in a fixed round-robin order).  Else
+   * device memory of MOE_TILE_COUNTERS_BYTES, all zero before the launch:
+   * workgroups then take tiles dynamically from atomic counters in it, and the
+   * launch leaves it zero again.  Two launches in flight at once must not share
+   * it. */
+  int32_t* tile_counters;
 } moe_gemm_args;
+
+#define MOE_TILE_COUNTERS_BYTES 1024
 
 moe_status moe_grouped_gemm(const moe_gemm_args* args, hipStream_t stream);
 
