@@ -143,9 +143,12 @@ def main():
     # enqueued through the C ABI in the same configuration as in the forward
     ss, off, a_codes, a_scales, h_codes, h_scales = _gemm_inputs(wl, inp, dev)
 
+    # zeroed tile counters, reused: each launch leaves them zero (as in the forward)
+    counters = torch.zeros(moe.TILE_COUNTERS_INTS, dtype=torch.int32, device=dev)
+
     def l1():
         moe.grouped_gemm(w, 0, a_codes, a_scales, T, off, moe.EPI_SWIGLU_QUANT, S, a_row_index=ss, a_row_divisor=k,
-                         h_codes=h_codes, h_scales=h_scales, swiglu_limit=wl.swiglu_limit)
+                         h_codes=h_codes, h_scales=h_scales, swiglu_limit=wl.swiglu_limit, tile_counters=counters)
 
     for _ in range(2):
         l1()
@@ -264,14 +267,16 @@ def only_gemm(args, wl, inp, w, dev):
     S, I, H, k = wl.T * wl.k, wl.I, wl.H, wl.k
     ss, off, a_codes, a_scales, h_codes, h_scales = _gemm_inputs(wl, inp, dev)
     slot_out = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
+    counters = torch.zeros(moe.TILE_COUNTERS_INTS, dtype=torch.int32, device=dev)
     if args.only == "gate_up":
         def run():
             moe.grouped_gemm(w, 0, a_codes, a_scales, wl.T, off, moe.EPI_SWIGLU_QUANT, S, a_row_index=ss,
-                             a_row_divisor=k, h_codes=h_codes, h_scales=h_scales, swiglu_limit=wl.swiglu_limit)
+                             a_row_divisor=k, h_codes=h_codes, h_scales=h_scales, swiglu_limit=wl.swiglu_limit,
+                             tile_counters=counters)
     else:
         def run():
             moe.grouped_gemm(w, 1, h_codes, h_scales, S, off, moe.EPI_WEIGHTED_SCATTER, S, slot_out=slot_out,
-                             top_k_weights=inp["w"], slot_of_row=ss)
+                             top_k_weights=inp["w"], slot_of_row=ss, tile_counters=counters)
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()

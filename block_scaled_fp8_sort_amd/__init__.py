@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "FMT_FP8_B128", "FMT_MXFP8A_MXFP4W", "EPI_STORE_F32", "EPI_SWIGLU_QUANT", "EPI_WEIGHTED_SCATTER",
     "MoeError", "library_path", "load_library", "route_sort", "quant_act", "prepare_weights", "grouped_gemm",
-    "experts_forward", "forward_workspace_bytes", "Weights",
+    "experts_forward", "forward_workspace_bytes", "Weights", "TILE_COUNTERS_INTS",
 ]
 
 FMT_FP8_B128 = 0
