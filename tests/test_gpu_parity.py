@@ -240,6 +240,38 @@ def test_grouped_gemm_few_rows_one_heavy_expert(which):
     _gemm_vs_oracle(FP8, which, E, 512, 384, ids, k, seed=77)
 
 
+@pytest.mark.parametrize("fmt", [FP8, MX])
+def test_grouped_gemm_tile_order_and_counters(fmt):
+    """The fixed round-robin tile order (no counters) and the dynamic dispensers
+    give the same result bit for bit (each output tile is computed by one
+    workgroup in the same way), and a launch leaves its counters zero, so they
+    can be reused."""
+    say(f"gemm tile order fmt={fmt}")
+    E, H, I, T, k = 6, 512, 384, 900, 3
+    rng = np.random.default_rng(41)
+    gen = W.fp8_weights if fmt == FP8 else W.fp4_weights
+    w13, s13 = gen(E, 2 * I, H, 41, "w13", DEV)
+    w2, s2 = gen(E, H, I, 41, "w2", DEV)
+    w = moe.prepare_weights(w13, s13, w2, s2, fmt=fmt)
+    x = W.hidden_states(T, H, 41, DEV)
+    ids = torch.from_numpy(_rand_ids(rng, T, k, E, 0.1, 0.0)).to(DEV)
+    a, asc = moe.quant_act(x, fmt)
+    ss, off, _, _ = moe.route_sort(ids, E)
+    S = T * k
+    counters = torch.zeros(moe.TILE_COUNTERS_INTS, dtype=torch.int32, device=DEV)
+    outs = []
+    for tc in (None, counters, counters):  # static, dynamic, dynamic reusing the counters
+        c = torch.full((S, 2 * I), float("nan"), dtype=torch.float32, device=DEV)
+        moe.grouped_gemm(w, 0, a, asc, T, off, moe.EPI_STORE_F32, S, a_row_index=ss, a_row_divisor=k, c_f32=c,
+                         tile_counters=tc)
+        torch.cuda.synchronize()
+        outs.append(host(c))
+        assert int(host(counters).astype(np.int64).sum()) == 0
+    n = host(off)[-1]
+    for o in outs[1:]:
+        assert np.array_equal(o[:n].view(np.uint32), outs[0][:n].view(np.uint32))
+
+
 def test_grouped_gemm_few_rows_many_tiles():
     """More tiles than a workgroup fetches row data for at once (16 per
     workgroup on 256 CUs needs over 4096 tiles): 80 experts x 64 paired
