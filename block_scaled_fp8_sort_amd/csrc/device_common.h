@@ -20,31 +20,35 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 
 // Four fp32 values -> four OCP e4m3fn codes packed little-endian (a in the low
 // byte).  The hardware conversion rounds to nearest even; clamping to +-448
-// first makes every out-of-range magnitude saturate to 448 (the rule's
-// "round, then saturate" gives the same code for every input above 448).
+// first (one v_med3 per value) makes every out-of-range magnitude saturate to
+// 448 (the rule's "round, then saturate" gives the same code for every input
+// above 448).
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  a = __builtin_fminf(__builtin_fmaxf(a, -448.0f), 448.0f);
-  b = __builtin_fminf(__builtin_fmaxf(b, -448.0f), 448.0f);
-  c = __builtin_fminf(__builtin_fmaxf(c, -448.0f), 448.0f);
-  d = __builtin_fminf(__builtin_fmaxf(d, -448.0f), 448.0f);
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+  d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
   int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
   return (uint32_t)v;
 }
 
-// Block scale of the FP8_B128 format: max(amax, 1e-4) / 448 with IEEE fp32 division.
-// SwiGLU of one (gate, up) pair ("swiglu_limit" clamp when given: gate capped
-// above at L, up clamped to [-L, L]): silu(g) * u with silu(g) = g / (1 + e^-g),
-// the division done with the hardware reciprocal (about 1 ulp; h is compared by
-// tolerance, not bit for bit).  Very negative g gives e^-g = inf and h = -0 * u.
-__device__ __forceinline__ float swiglu(float g, float u, bool has_limit, float limit) {
-  if (has_limit) {
-    g = __builtin_fminf(g, limit);
-    u = __builtin_fminf(__builtin_fmaxf(u, -limit), limit);
+// SwiGLU of one (gate, up) pair, silu(g) * u with silu(g) = g / (1 + e^-g);
+// with the "swiglu_limit" clamp (LIMIT) the gate is first capped above at L and
+// up clamped to [-L, L] (one v_med3 each).  The division is the hardware
+// reciprocal (about 1 ulp; h is compared by tolerance, not bit for bit).  Very
+// negative g gives e^-g = inf and h = -0 * u.  The limit is a compile-time
+// choice so the unclamped form carries no selects.
+template <bool LIMIT>
+__device__ __forceinline__ float swiglu(float g, float u, float limit) {
+  if constexpr (LIMIT) {
+    g = __builtin_amdgcn_fmed3f(g, -__builtin_inff(), limit);
+    u = __builtin_amdgcn_fmed3f(u, -limit, limit);
   }
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
+// Block scale of the FP8_B128 format: max(amax, 1e-4) / 448 with IEEE fp32 division.
 __device__ __forceinline__ float fp8_block_scale(float amax) { return __builtin_fmaxf(amax, 1e-4f) / 448.0f; }
 
 // MX format: e = ceil(log2(max(amax, 1e-4) / 448)) read from the fp32 bits of

@@ -3,6 +3,7 @@
 #pragma once
 
 #include "device_common.h"
+#include "internal.h"
 
 namespace moe {
 
@@ -251,6 +252,55 @@ __device__ __forceinline__ void reset_dispenser(const Dispenser& d) {
 __device__ __forceinline__ int xcd_virtual_block() {
   const int G = gridDim.x;
   return (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+}
+
+// Epilogue of the down GEMM (weighted scatter) shared by the tiled kernels,
+// whose 8 waves each hold 128 columns x BM/4 rows of the 256 x BM tile (lane:
+// 4 consecutive columns of one row per 16-column sub-tile ni, sub-tile ti of
+// 16 rows).  Row r of the tile is scaled by its slot's routing weight, rounded
+// to bf16 and written to slot_out[slot][256 n_tile ...].  The rows are staged in
+// the stage area (free once every wave is past the K loop) at a padded pitch
+// and leave as whole 512-byte row segments, 16 bytes per lane: stored straight
+// from the accumulators, each lane's 8-byte pieces would reach memory as
+// partial lines.  srow: BM ints of LDS scratch.
+constexpr int kOutPitch = 528;  // bytes per staged row: 512 + 16 (fewer bank conflicts)
+
+template <int BM, typename V>
+__device__ __forceinline__ void scatter_rows_staged(const GemmParams& p, uint8_t* area, int* srow,
+                                                    const V (&acc)[8][BM / 64], int n_tile, int m0, int m_end,
+                                                    int tid) {
+  constexpr int WM = BM / 4, TS = WM / 16;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wn = wave & 1, wt = wave >> 1, g = lane >> 4, l16 = lane & 15;
+  const int N = p.N;
+  __syncthreads();  // every wave is done reading the stages
+  if (tid < BM) srow[tid] = m0 + tid < m_end ? p.slot_of_row[m0 + tid] : -1;
+#pragma unroll
+  for (int ti = 0; ti < TS; ++ti) {
+    const int tr = wt * WM + ti * 16 + l16;
+    const int r = m0 + tr;
+    const float w = r < m_end ? p.top_k_weights[p.slot_of_row[r]] : 0.0f;
+#pragma unroll
+    for (int ni = 0; ni < 8; ++ni) {
+      const V v = acc[ni][ti] * w;
+      uint2 o;
+      o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+      o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+      *(uint2*)(area + tr * kOutPitch + (wn * 128 + ni * 16 + 4 * g) * 2) = o;
+    }
+  }
+  __syncthreads();
+  // wave w, pass j: tile row 16 j + 2 w + (lane / 32), 8 columns per lane
+  const int n0 = n_tile * 256 + (lane & 31) * 8;
+#pragma unroll 4
+  for (int j = 0; j < BM / 16; ++j) {
+    const int tr = 16 * j + 2 * wave + (lane >> 5);
+    const int slot = srow[tr];
+    if (slot >= 0 && n0 < N) {
+      const int4 v = *(const int4*)(area + tr * kOutPitch + (lane & 31) * 16);
+      *(int4*)(p.slot_out + (size_t)slot * N + n0) = v;
+    }
+  }
 }
 
 }  // namespace moe

@@ -42,6 +42,8 @@
 //    group's m-tiles in that XCD's L2, and the group's activation rows stay
 //    cached across its n-tiles.  Rows past the expert's end are masked; no
 //    host-visible counts are needed.
+#include <type_traits>
+
 #include "device_common.h"
 #include "gemm_common.h"
 #include "internal.h"
@@ -311,21 +313,26 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Mis
     static_assert(PAIRED, "SwiGLU needs the paired gate/up layout");
     // h of pair q, sub-tile ti, element i, computed once into the gate's
     // accumulator, and its amax over the tile's 128 outputs of each token
+    auto swiglu_rows = [&](auto lim) {
+      constexpr bool LIM = decltype(lim)::value;
 #pragma unroll
-    for (int ti = 0; ti < TS; ++ti) {
-      float m = 0.0f;
+      for (int ti = 0; ti < TS; ++ti) {
+        float m = 0.0f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float h = swiglu(acc[2 * q][ti][i], acc[2 * q + 1][ti][i], p.has_limit, p.limit);
-          acc[2 * q][ti][i] = h;
-          m = __builtin_fmaxf(m, __builtin_fabsf(h));
-        }
-      m = wave_max_xor(m, 16);
-      m = wave_max_xor(m, 32);
-      if (g == 0) misc.amax[wn][wt * WM + ti * 16 + l16] = m;
-    }
+          for (int i = 0; i < 4; ++i) {
+            const float h = swiglu<LIM>(acc[2 * q][ti][i], acc[2 * q + 1][ti][i], p.limit);
+            acc[2 * q][ti][i] = h;
+            m = __builtin_fmaxf(m, __builtin_fabsf(h));
+          }
+        m = wave_max_xor(m, 16);
+        m = wave_max_xor(m, 32);
+        if (g == 0) misc.amax[wn][wt * WM + ti * 16 + l16] = m;
+      }
+    };
+    if (p.has_limit) swiglu_rows(std::true_type{});
+    else swiglu_rows(std::false_type{});
     __syncthreads();
     // h codes go to the K-block-major layout [I/128][max_rows][128] that the
     // down GEMM reads; the tile's 128 outputs are exactly plane n_tile
@@ -348,25 +355,8 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Mis
       }
     }
   } else {  // kEpiWeightedScatter
-#pragma unroll
-    for (int ti = 0; ti < TS; ++ti) {
-      const int r = m0 + wt * WM + ti * 16 + l16;
-      if (r < m_end) {
-        const int slot = p.slot_of_row[r];
-        const float w = p.top_k_weights[slot];
-#pragma unroll
-        for (int ni = 0; ni < 8; ++ni) {
-          const int n = n_tile * BN + wn * 128 + ni * 16 + 4 * g;
-          if (n < N) {
-            const v4f v = acc[ni][ti] * w;
-            uint2 o;
-            o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-            o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-            *(uint2*)(p.slot_out + (size_t)slot * N + n) = o;
-          }
-        }
-      }
-    }
+    static_assert(BM * kOutPitch <= kStageArea, "output staging");
+    scatter_rows_staged<BM>(p, area, reinterpret_cast<int*>(&misc.amax[0][0]), acc, n_tile, m0, m_end, tid);
   }
 }
 

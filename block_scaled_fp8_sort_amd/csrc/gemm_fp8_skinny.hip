@@ -188,7 +188,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, Misc& misc, const 
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      h[i] = swiglu(acc0[i], acc1[i], p.has_limit, p.limit);
+      h[i] = p.has_limit ? swiglu<true>(acc0[i], acc1[i], p.limit) : swiglu<false>(acc0[i], acc1[i], p.limit);
       m = __builtin_fmaxf(m, __builtin_fabsf(h[i]));
     }
     m = wave_max_xor(m, 16);

@@ -169,7 +169,8 @@ __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nx
 // One tile of BM sorted rows [m0, min(m0 + BM, m_end)) of expert e against
 // n-tile n_tile, through a ring of STAGES LDS stages carved out of `area`.
 template <int BM, int EPI, bool PAIRED>
-__device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, int e, int n_tile, int m0, int m_end) {
+__device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, int* srow, int e, int n_tile, int m0,
+                                         int m_end) {
   constexpr int STAGES = stages_for<BM>();
   constexpr int WM = BM / 4;
   constexpr int TS = WM / 16;
@@ -251,6 +252,18 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, int
     // this wave (xor over the four lane groups)
     uint8_t* plane = p.h_codes + (size_t)n_tile * p.max_rows * 128;
     uint8_t* splane = (uint8_t*)p.h_scales + (size_t)n_tile * p.max_rows * 4;
+    // h, computed once into the gate's accumulators
+    auto swiglu_all = [&](auto lim) {
+      constexpr bool LIM = decltype(lim)::value;
+#pragma unroll
+      for (int ti = 0; ti < TS; ++ti)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[2 * q][ti][i] = swiglu<LIM>(acc[2 * q][ti][i], acc[2 * q + 1][ti][i], p.limit);
+    };
+    if (p.has_limit) swiglu_all(std::true_type{});
+    else swiglu_all(std::false_type{});
 #pragma unroll
     for (int ti = 0; ti < TS; ++ti) {
       const int r = m0 + wt * WM + ti * 16 + l16;
@@ -260,11 +273,7 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, int
 #pragma unroll
         for (int q = 2 * b; q < 2 * b + 2; ++q)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {  // h, computed once into the gate's accumulator
-            const float h = swiglu(acc[2 * q][ti][i], acc[2 * q + 1][ti][i], p.has_limit, p.limit);
-            acc[2 * q][ti][i] = h;
-            m = __builtin_fmaxf(m, __builtin_fabsf(h));
-          }
+          for (int i = 0; i < 4; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(acc[2 * q][ti][i]));
         m = wave_max_xor(m, 16);
         m = wave_max_xor(m, 32);
         const int ex = mx_block_exponent(m);
@@ -281,25 +290,8 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, int
       }
     }
   } else {  // kEpiWeightedScatter
-#pragma unroll
-    for (int ti = 0; ti < TS; ++ti) {
-      const int r = m0 + wt * WM + ti * 16 + l16;
-      if (r < m_end) {
-        const int slot = p.slot_of_row[r];
-        const float w = p.top_k_weights[slot];
-#pragma unroll
-        for (int ni = 0; ni < 8; ++ni) {
-          const int n = n_tile * BN + wn * 128 + ni * 16 + 4 * g;
-          if (n < N) {
-            const v4f v = acc[ni][ti] * w;
-            uint2 o;
-            o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-            o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-            *(uint2*)(p.slot_out + (size_t)slot * N + n) = o;
-          }
-        }
-      }
-    }
+    static_assert(BM * kOutPitch <= kStageArea, "output staging");
+    scatter_rows_staged<BM>(p, area, srow, acc, n_tile, m0, m_end, tid);
   }
 }
 
@@ -310,6 +302,7 @@ template <int EPI, bool PAIRED>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t area[kStageArea];
   __shared__ __attribute__((aligned(16))) Misc misc;
+  int* const srow = reinterpret_cast<int*>(misc.scan);  // scatter epilogue scratch (scan is free after the table)
   const int E = p.E, N = p.N;
   const int NT = PAIRED ? (N / 2) / 128 : (N + BN - 1) / BN;
   const int total = build_tile_table2<kThreads>(p.offsets, E, NT, misc.off, misc.tp, misc.cnt, misc.scan);
@@ -318,11 +311,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmParams p) {
     const TileCoord tc = locate_tile2(t, E, NT, misc.off, misc.tp, misc.cnt);
     const int left = tc.m_end - tc.m0;
     if (left > 128)
-      run_tile<256, EPI, PAIRED>(p, area, tc.e, tc.n_tile, tc.m0, tc.m_end);
+      run_tile<256, EPI, PAIRED>(p, area, srow, tc.e, tc.n_tile, tc.m0, tc.m_end);
     else if (left > 64)
-      run_tile<128, EPI, PAIRED>(p, area, tc.e, tc.n_tile, tc.m0, tc.m_end);
+      run_tile<128, EPI, PAIRED>(p, area, srow, tc.e, tc.n_tile, tc.m0, tc.m_end);
     else
-      run_tile<64, EPI, PAIRED>(p, area, tc.e, tc.n_tile, tc.m0, tc.m_end);
+      run_tile<64, EPI, PAIRED>(p, area, srow, tc.e, tc.n_tile, tc.m0, tc.m_end);
   };
   // tiles come from the per-XCD dispensers when counters are given (the next
   // tile is grabbed at the start of the current one and handed to every wave
