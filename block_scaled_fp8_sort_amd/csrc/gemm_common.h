@@ -265,6 +265,27 @@ __device__ __forceinline__ int xcd_virtual_block() {
 // partial lines.  srow: BM ints of LDS scratch.
 constexpr int kOutPitch = 528;  // bytes per staged row: 512 + 16 (fewer bank conflicts)
 
+// Second half of the staged scatter: ROWS staged rows (bf16, pitch
+// kOutPitch) leave as 512-byte row segments to slot_out[srow[r]][256 n_tile ...];
+// rows with srow < 0 are skipped.  Staging must be complete (barrier) on entry.
+template <int ROWS>
+__device__ __forceinline__ void copy_out_staged_rows(const GemmParams& p, const uint8_t* area, const int* srow,
+                                                     int n_tile, int tid) {
+  const int wave = tid >> 6, lane = tid & 63;
+  const int N = p.N;
+  // wave w, pass j: tile row 16 j + 2 w + (lane / 32), 8 columns per lane
+  const int n0 = n_tile * 256 + (lane & 31) * 8;
+#pragma unroll 4
+  for (int j = 0; j < ROWS / 16; ++j) {
+    const int tr = 16 * j + 2 * wave + (lane >> 5);
+    const int slot = srow[tr];
+    if (slot >= 0 && n0 < N) {
+      const int4 v = *(const int4*)(area + tr * kOutPitch + (lane & 31) * 16);
+      *(int4*)(p.slot_out + (size_t)slot * N + n0) = v;
+    }
+  }
+}
+
 template <int BM, typename V>
 __device__ __forceinline__ void scatter_rows_staged(const GemmParams& p, uint8_t* area, int* srow,
                                                     const V (&acc)[8][BM / 64], int n_tile, int m0, int m_end,
@@ -272,7 +293,6 @@ __device__ __forceinline__ void scatter_rows_staged(const GemmParams& p, uint8_t
   constexpr int WM = BM / 4, TS = WM / 16;
   const int wave = tid >> 6, lane = tid & 63;
   const int wn = wave & 1, wt = wave >> 1, g = lane >> 4, l16 = lane & 15;
-  const int N = p.N;
   __syncthreads();  // every wave is done reading the stages
   if (tid < BM) srow[tid] = m0 + tid < m_end ? p.slot_of_row[m0 + tid] : -1;
 #pragma unroll
@@ -290,17 +310,7 @@ __device__ __forceinline__ void scatter_rows_staged(const GemmParams& p, uint8_t
     }
   }
   __syncthreads();
-  // wave w, pass j: tile row 16 j + 2 w + (lane / 32), 8 columns per lane
-  const int n0 = n_tile * 256 + (lane & 31) * 8;
-#pragma unroll 4
-  for (int j = 0; j < BM / 16; ++j) {
-    const int tr = 16 * j + 2 * wave + (lane >> 5);
-    const int slot = srow[tr];
-    if (slot >= 0 && n0 < N) {
-      const int4 v = *(const int4*)(area + tr * kOutPitch + (lane & 31) * 16);
-      *(int4*)(p.slot_out + (size_t)slot * N + n0) = v;
-    }
-  }
+  copy_out_staged_rows<BM>(p, area, srow, n_tile, tid);
 }
 
 }  // namespace moe

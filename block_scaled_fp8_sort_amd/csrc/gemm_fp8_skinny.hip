@@ -60,9 +60,9 @@ struct Src {
   bool valid;
   int e, n_tile, m0, m_end;
   const uint8_t* w;   // this tile's K block 0
-  const float* swa;   // weight scales of row group 0 (stride 1 per K block)
-  const float* swb;   // weight scales of row group 1
-  const float* sa;    // this lane's activation scale at K block 0 (stride a_rows)
+  uint32_t swa;       // index of row group 0's weight scale at K block 0 (stride 1 per K block)
+  uint32_t swb;       // the same for row group 1
+  uint32_t sa;        // index of this lane's activation scale at K block 0 (stride a_rows)
   uint32_t a_off;     // this lane's activation row chunk offset in a K-block plane
 };
 
@@ -93,13 +93,12 @@ __device__ __forceinline__ Src make_src(const GemmParams& p, const Misc& misc, i
   } else {
     nba = nbb = min(tc.n_tile * 2 + (wave >= 4 ? 1 : 0), NB - 1);
   }
-  // the zero keeps the (uniform) scale addresses in VGPRs: vector loads are
-  // tracked in order, scalar ones are not, and waiting on a scalar load would
-  // wait for every prefetched one
-  const float* bsc = (const float*)p.b_scales + zero;
-  s.swa = bsc + ((size_t)tc.e * NB + nba) * KB;
-  s.swb = bsc + ((size_t)tc.e * NB + nbb) * KB;
-  s.sa = (const float*)p.a_scales + arow;
+  // the zero keeps the (uniform) scale indices in VGPRs, so the scale loads are
+  // vector loads: those are tracked in order, scalar ones are not, and waiting
+  // on a scalar load would wait for every prefetched one
+  s.swa = (uint32_t)(((size_t)tc.e * NB + nba) * KB) + (uint32_t)zero;
+  s.swb = (uint32_t)(((size_t)tc.e * NB + nbb) * KB) + (uint32_t)zero;
+  s.sa = (uint32_t)arow;
   s.a_off = (uint32_t)arow * BK + (uint32_t)((lane >> 4) << 4);
   return s;
 }
@@ -154,9 +153,9 @@ __device__ __forceinline__ void load_slot_a(Slot& sl, const GemmParams& p, const
   const uint8_t* ak = p.a_codes + (size_t)kb * p.a_rows * BK + s.a_off;
   sl.a[0] = *(const int4*)ak;
   sl.a[1] = *(const int4*)(ak + 64);
-  sl.sa = s.sa[(size_t)kb * p.a_rows];
-  sl.swa = s.swa[kb];
-  sl.swb = s.swb[kb];
+  sl.sa = ((const float*)p.a_scales)[s.sa + (uint32_t)kb * (uint32_t)p.a_rows];
+  sl.swa = ((const float*)p.b_scales)[s.swa + (uint32_t)kb];
+  sl.swb = ((const float*)p.b_scales)[s.swb + (uint32_t)kb];
 }
 
 __device__ __forceinline__ void load_slot(Slot& sl, const GemmParams& p, const Src& s, int kb, const uint32_t (&w_off)[4]) {
@@ -226,7 +225,8 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, Misc& misc, const 
 template <int EPI, bool PAIRED, int D>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_skinny_kernel(GemmParams p) {
   __shared__ Misc misc;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave offsets in SGPRs
   const int g = lane >> 4, l16 = lane & 15;
   const int E = p.E, N = p.N, KB = p.K / BK;
   const int NB = N / 128;
@@ -321,7 +321,8 @@ hipError_t launch_d(const GemmParams& p, int num_cus, hipStream_t stream) {
 template <int EPI, bool PAIRED>
 hipError_t launch_epi(const GemmParams& p, int num_cus, hipStream_t stream) {
   const int KB = p.K / BK;
-  // 8 slots fit in registers except with the SwiGLU epilogue
+  // 8 slots fit in registers with the SwiGLU epilogue too, but measured slower
+  // there (the wave's 72 loads in flight exceed what vmcnt counts)
   if constexpr (EPI != kEpiSwiGLUQuant)
     if (KB % 8 == 0) return launch_d<EPI, PAIRED, 8>(p, num_cus, stream);
   if (KB % 6 == 0) return launch_d<EPI, PAIRED, 6>(p, num_cus, stream);
