@@ -313,4 +313,24 @@ __device__ __forceinline__ void scatter_rows_staged(const GemmParams& p, uint8_t
   copy_out_staged_rows<BM>(p, area, srow, n_tile, tid);
 }
 
+// SwiGLU epilogues: a tile's h codes are BM sorted rows x 128 bytes of one
+// K-block plane of the down GEMM's operand ([I/128][rows][128]), so they form
+// one contiguous block in memory.  They are staged in the stage area (free
+// once every wave is past the K loop) at a padded pitch and leave 16 bytes per
+// lane, in whole 128-byte rows; rows at or past m_end are not written (they
+// belong to the next expert).  Staging must be complete (barrier) on entry.
+constexpr int kHPitch = 144;  // bytes per staged code row: 128 + 16 (no bank conflicts)
+
+template <int BM>
+__device__ __forceinline__ void copy_out_h_codes(const GemmParams& p, const uint8_t* area, int n_tile, int m0,
+                                                 int m_end, int tid) {
+  uint8_t* plane = p.h_codes + (size_t)n_tile * p.max_rows * 128;
+#pragma unroll
+  for (int i = tid; i < BM * 8; i += 512) {
+    const int tr = i >> 3, c = i & 7;
+    if (m0 + tr < m_end)
+      *(int4*)(plane + (size_t)(m0 + tr) * 128 + c * 16) = *(const int4*)(area + tr * kHPitch + c * 16);
+  }
+}
+
 }  // namespace moe

@@ -335,25 +335,26 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Mis
     else swiglu_rows(std::false_type{});
     __syncthreads();
     // h codes go to the K-block-major layout [I/128][max_rows][128] that the
-    // down GEMM reads; the tile's 128 outputs are exactly plane n_tile
-    uint8_t* plane = p.h_codes + (size_t)n_tile * p.max_rows * 128;
+    // down GEMM reads; the tile's 128 outputs are exactly plane n_tile, staged
+    // here (every wave is past the K loop) and stored as whole rows
+    static_assert(BM * kHPitch <= kStageArea, "h staging");
 #pragma unroll
     for (int ti = 0; ti < TS; ++ti) {
       const int tt = wt * WM + ti * 16 + l16;
       const float amax = __builtin_fmaxf(misc.amax[0][tt], misc.amax[1][tt]);
       const float s = fp8_block_scale(amax);
       const float inv = 1.0f / s;
-      const int r = m0 + tt;
-      if (r < m_end) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const v4f h = acc[2 * q][ti];
-          const uint32_t code = e4m3x4(h[0] * inv, h[1] * inv, h[2] * inv, h[3] * inv);
-          *(uint32_t*)(plane + (size_t)r * 128 + 16 * (wn * 4 + q) + 4 * g) = code;
-        }
-        if (wn == 0 && g == 0) ((float*)p.h_scales)[(size_t)n_tile * p.max_rows + r] = s;
+      for (int q = 0; q < 4; ++q) {
+        const v4f h = acc[2 * q][ti];
+        *(uint32_t*)(area + tt * kHPitch + 16 * (wn * 4 + q) + 4 * g) =
+            e4m3x4(h[0] * inv, h[1] * inv, h[2] * inv, h[3] * inv);
       }
+      const int r = m0 + tt;
+      if (r < m_end && wn == 0 && g == 0) ((float*)p.h_scales)[(size_t)n_tile * p.max_rows + r] = s;
     }
+    __syncthreads();
+    copy_out_h_codes<BM>(p, area, n_tile, m0, m_end, tid);
   } else {  // kEpiWeightedScatter
     static_assert(BM * kOutPitch <= kStageArea, "output staging");
     scatter_rows_staged<BM>(p, area, reinterpret_cast<int*>(&misc.amax[0][0]), acc, n_tile, m0, m_end, tid);

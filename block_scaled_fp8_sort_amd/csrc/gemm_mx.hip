@@ -250,8 +250,11 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, int
     // this wave's 64 outputs of the tile's 128 are the 32-wide MX blocks 2 wn and
     // 2 wn + 1, each made of pairs q = 2b and 2b + 1: the block amax needs only
     // this wave (xor over the four lane groups)
-    uint8_t* plane = p.h_codes + (size_t)n_tile * p.max_rows * 128;
-    uint8_t* splane = (uint8_t*)p.h_scales + (size_t)n_tile * p.max_rows * 4;
+    // codes and scale bytes are staged (after this barrier every wave is past
+    // the K loop) and stored as whole rows
+    static_assert(BM * (kHPitch + 4) <= kStageArea, "h staging");
+    uint8_t* sstage = area + BM * kHPitch;  // [BM][4] scale bytes
+    __syncthreads();
     // h, computed once into the gate's accumulators
     auto swiglu_all = [&](auto lim) {
       constexpr bool LIM = decltype(lim)::value;
@@ -266,7 +269,7 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, int
     else swiglu_all(std::false_type{});
 #pragma unroll
     for (int ti = 0; ti < TS; ++ti) {
-      const int r = m0 + wt * WM + ti * 16 + l16;
+      const int tt = wt * WM + ti * 16 + l16;
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         float m = 0.0f;
@@ -277,18 +280,21 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, int
         m = wave_max_xor(m, 16);
         m = wave_max_xor(m, 32);
         const int ex = mx_block_exponent(m);
-        if (r < m_end) {
 #pragma unroll
-          for (int q = 2 * b; q < 2 * b + 2; ++q) {
-            const v4f h = acc[2 * q][ti];
-            const uint32_t code = e4m3x4(__builtin_ldexpf(h[0], -ex), __builtin_ldexpf(h[1], -ex),
-                                         __builtin_ldexpf(h[2], -ex), __builtin_ldexpf(h[3], -ex));
-            *(uint32_t*)(plane + (size_t)r * 128 + 16 * (wn * 4 + q) + 4 * g) = code;
-          }
-          if (g == 0) splane[(size_t)r * 4 + wn * 2 + b] = (uint8_t)(ex + 127);
+        for (int q = 2 * b; q < 2 * b + 2; ++q) {
+          const v4f h = acc[2 * q][ti];
+          *(uint32_t*)(area + tt * kHPitch + 16 * (wn * 4 + q) + 4 * g) =
+              e4m3x4(__builtin_ldexpf(h[0], -ex), __builtin_ldexpf(h[1], -ex), __builtin_ldexpf(h[2], -ex),
+                     __builtin_ldexpf(h[3], -ex));
         }
+        if (g == 0) sstage[tt * 4 + wn * 2 + b] = (uint8_t)(ex + 127);
       }
     }
+    __syncthreads();
+    copy_out_h_codes<BM>(p, area, n_tile, m0, m_end, tid);
+    if (tid < BM && m0 + tid < m_end)
+      *(uint32_t*)((uint8_t*)p.h_scales + ((size_t)n_tile * p.max_rows + m0 + tid) * 4) =
+          *(const uint32_t*)(sstage + tid * 4);
   } else {  // kEpiWeightedScatter
     static_assert(BM * kOutPitch <= kStageArea, "output staging");
     scatter_rows_staged<BM>(p, area, srow, acc, n_tile, m0, m_end, tid);
