@@ -42,6 +42,9 @@
 //    group's m-tiles in that XCD's L2, and the group's activation rows stay
 //    cached across its n-tiles.  Rows past the expert's end are masked; no
 //    host-visible counts are needed.
+//  * The epilogues stage their outputs (the SwiGLU's h codes, the down GEMM's
+//    weighted bf16 rows) in the stage area, free once every wave is past the K
+//    loop, and store them as whole rows, 16 bytes per lane.
 #include <type_traits>
 
 #include "device_common.h"

@@ -19,7 +19,8 @@
 // Tiles: 256 weight rows x BM tokens x 128 K (BM = 256, or 64 / 128 / 256 for an
 // expert's last, partial m-tile), eight waves (2 x 4), two or four LDS stages
 // fed by LDS-DMA from the tiled weights (64-byte rows) and the K-block-major
-// activations; persistent XCD-aware tile walk as in the FP8 kernel.
+// activations; persistent XCD-aware tile walk and staged, whole-row epilogue
+// stores as in the FP8 kernel.
 #include "gemm_common.h"
 #include "internal.h"
 #include "tile_layout.h"
