@@ -37,9 +37,12 @@ constexpr int kTileN = 256;  // weight rows per tile
 constexpr int kBlockK = 128; // bytes of K per block row (FP8: 128 elements)
 
 // Physical 16-byte chunk position of logical chunk c in row r of an LDS
-// activation stage (128-byte rows gathered by LDS-DMA): rows r..r+7 (and with
-// 64 banks r..r+15) put the same logical chunk in distinct banks.
-__host__ __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// activation stage (128-byte rows gathered by LDS-DMA) is c ^ swz(r).  An
+// MFMA operand read has 16 lanes on 16 consecutive rows reading the same
+// logical chunk; with this XOR their 16-byte reads are conflict-free on gfx950
+// (measured with the LDS bank-conflict counter, which also showed that adding
+// row bit 3 to the XOR makes every such read two-way conflicted).
+__host__ __device__ __forceinline__ int swz(int row) { return row & 7; }
 
 // Source row (within the expert) of tile row tr of tile nt.  Returns -1 for a
 // padding row (plain tiles past N).
