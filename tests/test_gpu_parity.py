@@ -383,6 +383,38 @@ def test_forward_empty_and_single_token():
     assert_out_close(host(one), ref, "single token")
 
 
+@pytest.mark.parametrize("wl", [SMALL[1], SMALL[5], SMALL[7]], ids=[SMALL[1].name, SMALL[5].name, SMALL[7].name])
+def test_forward_graph_replay(wl):
+    """The forward allocates nothing and records no memset, so it can be captured
+    in a HIP graph: every replay, with the program's own eager work and
+    synchronizations in between, reproduces the eager result bit for bit."""
+    say(f"graph replay {wl.name}")
+    inp = W.inputs(wl, DEV)
+    w = _prepare(inp, wl.fmt)
+    lim = wl.swiglu_limit
+    ref = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w, swiglu_limit=lim)  # also caches the workspace
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe.experts_forward(inp["x"], inp["ids"], inp["w"], w, swiglu_limit=lim)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w, swiglu_limit=lim)
+    torch.cuda.synchronize()
+    ref_bits = host(ref).view(np.uint16)
+    for rep in range(4):
+        junk = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w, swiglu_limit=lim)  # eager work between replays
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out).view(np.uint16), ref_bits), f"replay {rep}"
+        assert np.array_equal(host(junk).view(np.uint16), ref_bits)
+
+
 def test_prepare_weights_nn_layout_matches_nt():
     wl = _small_workload("nn", FP8, T=96, H=384, I=256, E=3, k=2, seed=21)
     inp = W.inputs(wl, DEV)
