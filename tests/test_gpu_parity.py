@@ -321,6 +321,10 @@ SMALL = [
                     seed=15),
     _small_workload("mx_tight_clamp", MX, T=200, H=512, I=384, E=5, k=3, routing="zipf", skip=0.05, limit=0.05,
                     seed=16),
+    # the largest expert count the tile tables hold (512), on both FP8 paths and MX
+    _small_workload("e512_fp8_few_rows", FP8, T=160, H=256, I=128, E=512, k=8, routing="zipf", skip=0.05, seed=19),
+    _small_workload("e512_fp8_tiled", FP8, T=1500, H=256, I=256, E=512, k=6, routing="zipf", skip=0.05, seed=20),
+    _small_workload("e512_mx", MX, T=1200, H=256, I=128, E=512, k=4, routing="zipf", skip=0.05, limit=7.0, seed=22),
 ]
 
 
