@@ -50,6 +50,8 @@ def _load():
     lib.oracle_e8m0_decode.argtypes = [P, i64, P]
     lib.oracle_route_sort.argtypes = [P, i32, i32, i32, i32, P, P, P, P]
     lib.oracle_route_sort.restype = ctypes.c_int
+    lib.oracle_router_topk.argtypes = [P, i32, i32, i32, i32, P, P]
+    lib.oracle_router_topk.restype = ctypes.c_int
     lib.oracle_quant_rows_bf16.argtypes = [P, i32, i32, i32, P, P]
     lib.oracle_quant_rows_bf16.restype = ctypes.c_int
     lib.oracle_quant_rows_f32.argtypes = [P, i32, i32, i32, P, P]
@@ -120,6 +122,17 @@ def route_sort(ids, E: int, expert_begin: int = 0):
     _check(_load().oracle_route_sort(_ptr(ids), T, k, E, expert_begin, _ptr(sorted_slot),
                                      _ptr(offsets), _ptr(slot_pos), _ptr(inv)))
     return sorted_slot, offsets, slot_pos, int(inv[0])
+
+
+def router_topk(logits, k: int, renormalize: bool = True):
+    """logits: float32 [T, E].  Returns (ids int32 [T, k], weights float32 [T, k]):
+    softmax, the k largest (lower id first among equal logits), renormalised."""
+    lg = _c(logits, np.float32)
+    T, E = lg.shape
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    _check(_load().oracle_router_topk(_ptr(lg), T, E, k, 1 if renormalize else 0, _ptr(ids), _ptr(w)))
+    return ids, w
 
 
 def _scale_shape(fmt, rows, H):

@@ -293,6 +293,48 @@ int oracle_route_sort(const int32_t* ids, int32_t T, int32_t k, int32_t E, int32
   return OK;
 }
 
+// Router top-k: the step just before the experts forward, which produces its
+// top_k_index / top_k_weights.  The pages pass the router's output to the
+// experts untouched, as global ids with unmasked weights (PR #49606, "How it
+// runs" and the parallel-style table); the router of the layers the forward is
+// shaped on (Mixtral, Qwen3-MoE) is: softmax over the E logits of a token, the
+// k most probable experts, and (when `renormalize`) their probabilities divided
+// by the sum of the k selected.
+//  - Selection: softmax is strictly increasing in the logit, so the k most
+//    probable experts are the k largest logits, compared as fp32 values;
+//    among equal logits the lower id comes first.  ids[t][j] lists them in
+//    that order (j = 0 is the largest).
+//  - Weights in fp64: p_e = exp(l_e - m) / sum_e' exp(l_e' - m) with m the
+//    row maximum; w_j = p_{ids[j]}, divided by sum_j p_{ids[j]} when
+//    renormalizing; rounded once to fp32.
+// Logits must be finite (not checked).
+int oracle_router_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t renormalize, int32_t* ids,
+                       float* weights) {
+  if (T < 0 || E < 1 || k < 1 || k > E) return ERR_SHAPE;
+  if (T > 0 && (!logits || !ids || !weights)) return ERR_NULL;
+  std::vector<int32_t> order(E);
+  std::vector<double> p(E);
+  for (int64_t t = 0; t < T; ++t) {
+    const float* l = logits + t * E;
+    for (int32_t e = 0; e < E; ++e) order[e] = e;
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return l[a] > l[b]; });
+    const double m = (double)l[order[0]];
+    double z = 0.0;
+    for (int32_t e = 0; e < E; ++e) {
+      p[e] = std::exp((double)l[e] - m);
+      z += p[e];
+    }
+    for (int32_t e = 0; e < E; ++e) p[e] /= z;
+    double sel = 0.0;
+    for (int32_t j = 0; j < k; ++j) sel += p[order[j]];
+    for (int32_t j = 0; j < k; ++j) {
+      ids[t * k + j] = order[j];
+      weights[t * k + j] = (float)(renormalize ? p[order[j]] / sel : p[order[j]]);
+    }
+  }
+  return OK;
+}
+
 // Dynamic per-block quantization of bf16 rows [rows, H].
 int oracle_quant_rows_bf16(const uint16_t* x, int32_t rows, int32_t H, int32_t fmt, uint8_t* codes,
                            void* scales) {

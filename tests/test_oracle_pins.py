@@ -166,6 +166,85 @@ def test_route_sort_degenerate():
     assert list(off) == [0] * 5 and ss.size == 0
 
 
+# ------------------------------------------------------------------ router --
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (50, 8, 2), (64, 128, 8), (40, 256, 8), (9, 512, 64), (30, 5, 5)])
+@pytest.mark.parametrize("renorm", [True, False])
+def test_router_matches_torch_softmax_topk(T, E, k, renorm):
+    # distinct logits (N(0,1) draws): the selection is unique, so torch.topk of
+    # the float64 softmax fixes ids and their order; weights are that softmax
+    # (renormalised over the k), rounded once to fp32
+    rng = np.random.default_rng(T * 7 + E * 3 + k)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    ids, w = oracle.router_topk(lg, k, renorm)
+    p = torch.softmax(torch.from_numpy(lg).double(), dim=-1)
+    pv, pi = torch.topk(p, k, dim=-1)
+    if renorm:
+        pv = pv / pv.sum(dim=-1, keepdim=True)
+    assert np.array_equal(ids, pi.numpy().astype(np.int32))
+    np.testing.assert_allclose(w, pv.float().numpy(), rtol=2.0 ** -23, atol=0)
+
+
+def test_router_ties_take_the_lower_id():
+    # many equal logits: torch's stable descending sort and a brute force both
+    # put the lower id first among equals
+    rng = np.random.default_rng(11)
+    lg = rng.integers(0, 4, size=(64, 32)).astype(np.float32)
+    lg[:, 5] = -0.0
+    lg[:, 6] = 0.0  # -0 and +0 are equal logits
+    ids, _ = oracle.router_topk(lg, 6)
+    _, perm = torch.sort(torch.from_numpy(lg), dim=-1, descending=True, stable=True)
+    assert np.array_equal(ids, perm[:, :6].numpy().astype(np.int32))
+    for t in range(4):
+        brute = sorted(range(32), key=lambda e: (-float(lg[t, e]), e))[:6]
+        assert list(ids[t]) == brute
+
+
+def test_router_closed_forms():
+    # all logits equal: ids 0..k-1, weights exactly 1/k (renormalised) or 1/E
+    lg = np.full((3, 16), 0.75, np.float32)
+    ids, w = oracle.router_topk(lg, 4)
+    assert (ids == np.arange(4)).all() and (w == np.float32(0.25)).all()
+    ids, w = oracle.router_topk(lg, 4, renormalize=False)
+    assert (w == np.float32(1.0 / 16)).all()
+    # two experts, top-1: renormalised weight 1; otherwise the logistic
+    # function of the logit gap
+    lg = np.array([[2.0, -1.0], [0.5, 3.0]], np.float32)
+    ids, w = oracle.router_topk(lg, 1)
+    assert list(ids[:, 0]) == [0, 1] and (w == 1.0).all()
+    ids, w = oracle.router_topk(lg, 1, renormalize=False)
+    assert w[0, 0] == np.float32(1.0 / (1.0 + math.exp(-3.0)))
+    assert w[1, 0] == np.float32(1.0 / (1.0 + math.exp(-2.5)))
+    # k = E with renormalisation: the whole softmax, sorted
+    rng = np.random.default_rng(2)
+    lg = rng.standard_normal((5, 7)).astype(np.float32)
+    ids, w = oracle.router_topk(lg, 7)
+    assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=4e-7)
+    assert (np.diff(w, axis=1) <= 0).all()
+
+
+def test_router_shift_invariance_large_logits():
+    # adding a constant to every logit of a token changes nothing; the shifted
+    # logits are exact in fp32 (multiples of 1/64, |l| < 4, shift 1000), and
+    # exp(1000) would overflow, so the row maximum must be taken out first
+    rng = np.random.default_rng(3)
+    lg = (rng.integers(-256, 256, size=(20, 64)) / 64.0).astype(np.float32)
+    a = oracle.router_topk(lg, 6)
+    for c in (1000.0, -1000.0):
+        sh = (lg + np.float32(c)).astype(np.float32)
+        assert np.array_equal(sh - np.float32(c), lg)
+        b = oracle.router_topk(sh, 6)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert np.isfinite(a[1]).all()
+
+
+def test_router_rejects_bad_arguments():
+    with pytest.raises(oracle.OracleError):
+        oracle.router_topk(np.zeros((2, 4), np.float32), 5)
+    ids, w = oracle.router_topk(np.zeros((0, 4), np.float32), 2)
+    assert ids.shape == (0, 2) and w.shape == (0, 2)
+
+
 # ---------------------------------------------------- activation quantization --
 
 def _bf16_bits(x):
