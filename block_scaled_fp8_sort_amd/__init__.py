@@ -20,8 +20,9 @@ import torch
 
 __all__ = [
     "FMT_FP8_B128", "FMT_MXFP8A_MXFP4W", "EPI_STORE_F32", "EPI_SWIGLU_QUANT", "EPI_WEIGHTED_SCATTER",
-    "MoeError", "library_path", "load_library", "route_sort", "quant_act", "prepare_weights", "grouped_gemm",
-    "experts_forward", "forward_workspace_bytes", "Weights", "TILE_COUNTERS_INTS",
+    "MoeError", "library_path", "load_library", "route_sort", "route_topk", "quant_act", "prepare_weights",
+    "grouped_gemm", "experts_forward", "experts_forward_from_logits", "forward_workspace_bytes", "Weights",
+    "TILE_COUNTERS_INTS",
 ]
 
 FMT_FP8_B128 = 0
@@ -94,6 +95,10 @@ def load_library():
     lib.moe_route_sort_workspace.argtypes = [_I32, _I32, _I32]
     lib.moe_route_sort.restype = ctypes.c_int
     lib.moe_route_sort.argtypes = [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]
+    lib.moe_route_topk_workspace.restype = _SZ
+    lib.moe_route_topk_workspace.argtypes = [_I32, _I32, _I32]
+    lib.moe_route_topk.restype = ctypes.c_int
+    lib.moe_route_topk.argtypes = [_P, _I32, _I32, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]
     lib.moe_quant_act.restype = ctypes.c_int
     lib.moe_quant_act.argtypes = [_P, _I32, _I32, ctypes.c_int, _P, _P, _P]
     lib.moe_prepared_weights_size.restype = _SZ
@@ -108,6 +113,9 @@ def load_library():
     lib.moe_experts_forward.restype = ctypes.c_int
     lib.moe_experts_forward.argtypes = [ctypes.POINTER(MoeWeights), _P, _P, _P, _I32, _I32,
                                         ctypes.POINTER(MoeOptions), _P, _P, _SZ, _P]
+    lib.moe_experts_forward_from_logits.restype = ctypes.c_int
+    lib.moe_experts_forward_from_logits.argtypes = [ctypes.POINTER(MoeWeights), _P, _P, _I32, _I32, _I32, _I32,
+                                                    ctypes.POINTER(MoeOptions), _P, _P, _P, _P, _SZ, _P]
     _lib = lib
     return lib
 
@@ -174,6 +182,39 @@ def route_sort(top_k_index: torch.Tensor, num_experts: int, expert_begin: int = 
     _check(lib.moe_route_sort(_ptr(top_k_index), T, k, num_experts, expert_begin, _ptr(sorted_slot), _ptr(offsets),
                               _ptr(slot_pos), _ptr(invalid), _ptr(ws), ws_bytes, _stream(dev)))
     return sorted_slot, offsets, slot_pos, invalid
+
+
+# ------------------------------------------------------- router + route sort
+def route_topk(router_logits: torch.Tensor, k: int, renormalize: bool = True, num_experts: Optional[int] = None,
+               expert_begin: int = 0, sort: bool = True, with_slot_pos: bool = True):
+    """Router top-k (softmax over the logits, the k largest, optionally
+    renormalised) fused with the route sort.
+
+    router_logits fp32 [T, n_experts].  Returns (top_k_index int32 [T, k],
+    top_k_weights fp32 [T, k], sorted_slot, expert_offsets, slot_pos,
+    invalid_count); the last four are None when ``sort`` is False.  The sort
+    covers ``num_experts`` local experts from ``expert_begin`` (default: all).
+    """
+    lib = load_library()
+    dev = router_logits.device
+    _need(router_logits, "router_logits", torch.float32)
+    T, n = router_logits.shape
+    E = n if num_experts is None else num_experts
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    sorted_slot = offsets = slot_pos = invalid = ws = None
+    ws_bytes = 0
+    if sort:
+        sorted_slot = torch.empty(T * k, dtype=torch.int32, device=dev)
+        offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        slot_pos = torch.empty(T * k, dtype=torch.int32, device=dev) if with_slot_pos else None
+        invalid = torch.zeros(1, dtype=torch.int32, device=dev)
+        ws_bytes = lib.moe_route_topk_workspace(T, k, E)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib.moe_route_topk(_ptr(router_logits), T, n, k, 1 if renormalize else 0, _ptr(ids), _ptr(w), E,
+                              expert_begin, _ptr(sorted_slot), _ptr(offsets), _ptr(slot_pos), _ptr(invalid), _ptr(ws),
+                              ws_bytes, _stream(dev)))
+    return ids, w, sorted_slot, offsets, slot_pos, invalid
 
 
 # -------------------------------------------------------------- quantization
@@ -313,6 +354,53 @@ def _workspace(T: int, k: int, weights: Weights, device) -> torch.Tensor:
     return ws
 
 
+def _options(swiglu_limit, expert_begin, invalid_count):
+    opt = MoeOptions()
+    opt.has_swiglu_limit = 0 if swiglu_limit is None else 1
+    opt.swiglu_limit = 0.0 if swiglu_limit is None else float(swiglu_limit)
+    opt.expert_begin = expert_begin
+    opt.static_activation_scales = 0
+    opt.invalid_count = _ptr(invalid_count)
+    return opt
+
+
+def experts_forward_from_logits(hidden_states: torch.Tensor, router_logits: torch.Tensor, k: int,
+                                weights: Weights, renormalize: bool = True, swiglu_limit: Optional[float] = None,
+                                expert_begin: int = 0, out: Optional[torch.Tensor] = None,
+                                top_k_index: Optional[torch.Tensor] = None,
+                                top_k_weights: Optional[torch.Tensor] = None,
+                                workspace: Optional[torch.Tensor] = None,
+                                invalid_count: Optional[torch.Tensor] = None):
+    """The experts forward from the router's logits (see route_topk): returns
+    (out bf16 [T, H], top_k_index int32 [T, k], top_k_weights fp32 [T, k])."""
+    lib = load_library()
+    if hidden_states.dtype != torch.bfloat16:
+        raise ValueError(f"the experts forward requires bfloat16 hidden states, got {hidden_states.dtype}")
+    dev = hidden_states.device
+    _need(hidden_states, "hidden_states", torch.bfloat16, dev)
+    _need(router_logits, "router_logits", torch.float32, dev)
+    T, H = hidden_states.shape
+    n = router_logits.shape[1]
+    if router_logits.shape[0] != T:
+        raise ValueError(f"router_logits has {router_logits.shape[0]} rows for {T} tokens")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if top_k_index is None:
+        top_k_index = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if top_k_weights is None:
+        top_k_weights = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _need(top_k_index, "top_k_index", torch.int32, dev)
+    _need(top_k_weights, "top_k_weights", torch.float32, dev)
+    if T > 0 and workspace is None:
+        workspace = _workspace(T, k, weights, dev)
+    opt = _options(swiglu_limit, expert_begin, invalid_count)
+    _check(lib.moe_experts_forward_from_logits(ctypes.byref(weights.desc), _ptr(hidden_states), _ptr(router_logits), T,
+                                               n, k, 1 if renormalize else 0, ctypes.byref(opt), _ptr(top_k_index),
+                                               _ptr(top_k_weights), _ptr(out), _ptr(workspace),
+                                               0 if workspace is None else workspace.numel(), _stream(dev)))
+    return out, top_k_index, top_k_weights
+
+
 def experts_forward(hidden_states: torch.Tensor, top_k_index: torch.Tensor, top_k_weights: torch.Tensor,
                     weights: Weights, swiglu_limit: Optional[float] = None, expert_begin: int = 0,
                     activation_scheme: str = "dynamic", out: Optional[torch.Tensor] = None,
@@ -340,12 +428,7 @@ def experts_forward(hidden_states: torch.Tensor, top_k_index: torch.Tensor, top_
         return out
     if workspace is None:
         workspace = _workspace(T, k, weights, dev)
-    opt = MoeOptions()
-    opt.has_swiglu_limit = 0 if swiglu_limit is None else 1
-    opt.swiglu_limit = 0.0 if swiglu_limit is None else float(swiglu_limit)
-    opt.expert_begin = expert_begin
-    opt.static_activation_scales = 0
-    opt.invalid_count = _ptr(invalid_count)
+    opt = _options(swiglu_limit, expert_begin, invalid_count)
     dbg = None
     if debug is not None:
         S = T * k

@@ -35,23 +35,42 @@ struct GemmParams {
 
 enum Epilogue { kEpiStoreF32 = 0, kEpiSwiGLUQuant = 1, kEpiWeightedScatter = 2 };
 
+// Router in front of the route sort (see moe_route_topk in include/moe.h): the
+// softmax top-k of each token's logits is written to ids / weights, and ids is
+// then what the sort reads.  A launcher given a NULL RouterArgs* (or logits ==
+// NULL) sorts the caller's ids as they are.
+struct RouterArgs {
+  const float* logits;  // [T, n_experts]
+  int32_t n_experts;    // 1 .. 512
+  int32_t renormalize;
+  int32_t* ids;         // [T, k] out
+  float* weights;       // [T, k] out
+};
+
 size_t route_sort_lds_bytes(int32_t E);
 // Device workspace the sort of S slots needs (0 for the one-workgroup path).
 size_t route_sort_ws_bytes(int32_t S, int32_t E);
-hipError_t launch_route_sort(const int32_t* ids, int32_t S, int32_t E, int32_t expert_begin, int32_t* sorted_slot,
-                             int32_t* offsets, int32_t* slot_pos, int32_t* invalid_count, void* ws,
-                             hipStream_t stream);
-// The route sort, also setting zero[0 .. n_zero) to 0.
-hipError_t launch_route_sort_zero(const int32_t* ids, int32_t S, int32_t E, int32_t expert_begin,
-                                  int32_t* sorted_slot, int32_t* offsets, int32_t* slot_pos, int32_t* invalid_count,
-                                  void* ws, int32_t* zero, int32_t n_zero, hipStream_t stream);
-// The route sort (without slot_pos) and the activation quantization of x
-// [rows, H], in one launch for small batches, else one after the other; the
-// first kernel also sets zero[0 .. n_zero) to 0 (the GEMMs' tile counters).
-hipError_t launch_route_sort_and_quant(const int32_t* ids, int32_t S, int32_t E, int32_t expert_begin,
-                                      int32_t* sorted_slot, int32_t* offsets, int32_t* invalid_count, void* sort_ws,
-                                      const uint16_t* x, int32_t rows, int32_t H, int fmt, uint8_t* codes,
-                                      void* scales, int32_t* zero, int32_t n_zero, hipStream_t stream);
+// The route sort of ids [T, k] (S = T * k slots), preceded by the router when
+// `router` is non-NULL (ids must then be router->ids).  slot_pos may be NULL.
+hipError_t launch_route_sort(const RouterArgs* router, const int32_t* ids, int32_t T, int32_t k, int32_t E,
+                             int32_t expert_begin, int32_t* sorted_slot, int32_t* offsets, int32_t* slot_pos,
+                             int32_t* invalid_count, void* ws, hipStream_t stream);
+// The same, also setting zero[0 .. n_zero) to 0.
+hipError_t launch_route_sort_zero(const RouterArgs* router, const int32_t* ids, int32_t T, int32_t k, int32_t E,
+                                  int32_t expert_begin, int32_t* sorted_slot, int32_t* offsets, int32_t* slot_pos,
+                                  int32_t* invalid_count, void* ws, int32_t* zero, int32_t n_zero,
+                                  hipStream_t stream);
+// The (router and) route sort, without slot_pos, and the activation
+// quantization of x [rows, H], in one launch for small batches, else one after
+// the other; the first kernel also sets zero[0 .. n_zero) to 0 (the GEMMs'
+// tile counters).
+hipError_t launch_route_sort_and_quant(const RouterArgs* router, const int32_t* ids, int32_t T, int32_t k, int32_t E,
+                                      int32_t expert_begin, int32_t* sorted_slot, int32_t* offsets,
+                                      int32_t* invalid_count, void* sort_ws, const uint16_t* x, int32_t rows,
+                                      int32_t H, int fmt, uint8_t* codes, void* scales, int32_t* zero,
+                                      int32_t n_zero, hipStream_t stream);
+// The router alone (no sort).
+hipError_t launch_router_only(const RouterArgs& router, int32_t T, int32_t k, hipStream_t stream);
 hipError_t launch_quant_act(const uint16_t* x, int32_t rows, int32_t H, int fmt, uint8_t* codes, void* scales,
                             hipStream_t stream);
 // epi: Epilogue; paired: gate/up row pairing of B (used with kEpiSwiGLUQuant and

@@ -215,6 +215,136 @@ hipError_t launch_gemm(const moe::GemmParams& p, int fmt, int epi, bool paired, 
   return moe::launch_gemm_mx(p, epi, paired, num_cus, stream);
 }
 
+// The forward behind both entry points; with a router, top_k_index and
+// top_k_weights are outputs that the router fills before the sort reads them.
+moe_status forward_impl(const moe_weights* w, const uint16_t* hidden_states, const moe::RouterArgs* router,
+                        const int32_t* top_k_index, const float* top_k_weights, int32_t T, int32_t k,
+                        const moe_options* opt, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = validate_weights(w);
+  if (st != MOE_OK) return st;
+  if (T < 0) return fail(MOE_ERR_SHAPE, "T=%d < 0", T);
+  if (k < 1 || k > kMaxK) return fail(MOE_ERR_SHAPE, "k=%d outside [1, %d]", k, kMaxK);
+  if ((int64_t)T * k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "T*k must stay below 2^31");
+  const bool has_limit = opt && opt->has_swiglu_limit;
+  if (has_limit && !(std::isfinite(opt->swiglu_limit) && opt->swiglu_limit > 0.0f))
+    return fail(MOE_ERR_SHAPE, "swiglu_limit must be finite and > 0");
+  if (opt && opt->static_activation_scales)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "the grouped experts path quantizes activations dynamically per block; static activation scales "
+                "are not supported");
+  if (router) {
+    if (router->n_experts < 1 || router->n_experts > kMaxE)
+      return fail(MOE_ERR_SHAPE, "n_experts=%d outside [1, %d]", router->n_experts, kMaxE);
+    if (k > router->n_experts) return fail(MOE_ERR_SHAPE, "k=%d exceeds n_experts=%d", k, router->n_experts);
+  }
+  if (T == 0) return ok();
+  if (!hidden_states || !top_k_index || !top_k_weights || !out || (router && !router->logits))
+    return fail(MOE_ERR_NULL, "hidden_states / router_logits / top_k_index / top_k_weights / out is NULL");
+  if ((const void*)out == (const void*)hidden_states) return fail(MOE_ERR_UNSUPPORTED, "out must not alias input");
+  if (router) {
+    const void* o[] = {top_k_index, top_k_weights, out};
+    for (const void* q : o)
+      if (q == (const void*)router->logits || q == (const void*)hidden_states)
+        return fail(MOE_ERR_UNSUPPORTED, "outputs must not alias inputs");
+    if ((const void*)top_k_index == (const void*)top_k_weights || (const void*)top_k_index == (const void*)out ||
+        (const void*)top_k_weights == (const void*)out)
+      return fail(MOE_ERR_UNSUPPORTED, "outputs must not alias one another");
+  }
+  const FwdLayout L = fwd_layout(T, k, w->E, w->H, w->I, w->fmt);
+  if (!ws || ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace holds %zu bytes, %zu needed", ws ? ws_bytes : (size_t)0, L.total);
+  int dev, cus;
+  if ((st = check_device(stream, &dev, &cus)) != MOE_OK) return st;
+  for (auto pr : {std::make_pair((const void*)hidden_states, "hidden_states"),
+                  std::make_pair((const void*)top_k_index, "top_k_index"), std::make_pair((const void*)out, "out"),
+                  std::make_pair((const void*)w->w13, "w13"), std::make_pair((const void*)w->w2, "w2"),
+                  std::make_pair((const void*)ws, "workspace")})
+    if ((st = check_ptr(pr.first, dev, pr.second)) != MOE_OK) return st;
+
+  const int E = w->E, H = w->H, I = w->I;
+  const int32_t S = T * k;
+  uint8_t* base = (uint8_t*)ws;
+  int32_t* sorted_slot = (int32_t*)(base + L.sorted_slot);
+  int32_t* offsets = (int32_t*)(base + L.offsets);
+  uint8_t* act_codes = base + L.act_codes;
+  void* act_scales = base + L.act_scales;
+  uint8_t* h_codes = base + L.h_codes;
+  void* h_scales = base + L.h_scales;
+  uint16_t* slot_out = (uint16_t*)(base + L.slot_out);
+  const int32_t expert_begin = opt ? opt->expert_begin : 0;
+
+  int32_t* sched = (int32_t*)(base + L.sched);
+  if (router && (st = check_ptr(router->logits, dev, "router_logits")) != MOE_OK) return st;
+  hipError_t he = moe::launch_route_sort_and_quant(router, top_k_index, T, k, E, expert_begin, sorted_slot, offsets,
+                                                   opt ? opt->invalid_count : nullptr, base + L.sort_ws, hidden_states,
+                                                   T, H, w->fmt, act_codes, act_scales, sched,
+                                                   2 * MOE_TILE_COUNTERS_BYTES / 4, stream);
+  if (he != hipSuccess) return hip_status(he, "route sort / quant launch");
+
+  moe::GemmParams p1{};
+  p1.a_codes = act_codes;
+  p1.a_scales = act_scales;
+  p1.a_row_index = sorted_slot;
+  p1.a_row_div = k;
+  p1.a_rows = T;
+  p1.offsets = offsets;
+  p1.E = E;
+  p1.b_codes = w->w13;
+  p1.b_scales = w->w13_scale;
+  p1.N = 2 * I;
+  p1.K = H;
+  p1.max_rows = S;
+  p1.h_codes = h_codes;
+  p1.sched = sched;
+  p1.h_scales = h_scales;
+  p1.has_limit = has_limit ? 1 : 0;
+  p1.limit = has_limit ? opt->swiglu_limit : 0.0f;
+  he = launch_gemm(p1, w->fmt, moe::kEpiSwiGLUQuant, true, cus, stream);
+  if (he != hipSuccess) return hip_status(he, "gate_up gemm launch");
+
+  moe::GemmParams p2{};
+  p2.a_codes = h_codes;
+  p2.a_scales = h_scales;
+  p2.a_row_index = nullptr;
+  p2.a_row_div = 1;
+  p2.a_rows = S;
+  p2.offsets = offsets;
+  p2.E = E;
+  p2.b_codes = w->w2;
+  p2.b_scales = w->w2_scale;
+  p2.N = H;
+  p2.K = I;
+  p2.max_rows = S;
+  p2.slot_out = slot_out;
+  p2.top_k_weights = top_k_weights;
+  p2.slot_of_row = sorted_slot;
+  p2.sched = sched + MOE_TILE_COUNTERS_BYTES / 4;
+  he = launch_gemm(p2, w->fmt, moe::kEpiWeightedScatter, false, cus, stream);
+  if (he != hipSuccess) return hip_status(he, "down gemm launch");
+
+  he = moe::launch_combine(slot_out, top_k_index, T, k, H, E, expert_begin, out, stream);
+  if (he != hipSuccess) return hip_status(he, "combine launch");
+
+  if (opt && opt->debug) {
+    const moe_debug* d = opt->debug;
+    const bool mx = w->fmt == MOE_FMT_MXFP8A_MXFP4W;
+    const size_t sc_bytes = mx ? (size_t)T * (H / 32) : 4 * (size_t)T * (H / 128);  // same in either layout
+    if ((d->sorted_slot &&
+         (he = hipMemcpyAsync(d->sorted_slot, sorted_slot, 4 * (size_t)S, hipMemcpyDeviceToDevice, stream)) !=
+             hipSuccess) ||
+        (d->expert_offsets &&
+         (he = hipMemcpyAsync(d->expert_offsets, offsets, 4 * (size_t)(E + 1), hipMemcpyDeviceToDevice, stream)) !=
+             hipSuccess) ||
+        (d->act_codes &&
+         (he = hipMemcpyAsync(d->act_codes, act_codes, (size_t)T * H, hipMemcpyDeviceToDevice, stream)) !=
+             hipSuccess) ||
+        (d->act_scales &&
+         (he = hipMemcpyAsync(d->act_scales, act_scales, sc_bytes, hipMemcpyDeviceToDevice, stream)) != hipSuccess))
+      return hip_status(he, "debug copy");
+  }
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -264,9 +394,62 @@ moe_status moe_route_sort(const int32_t* top_k_index, int32_t T, int32_t k, int3
                   std::make_pair((const void*)expert_offsets, "expert_offsets")})
     if ((st = check_ptr(pr.first, dev, pr.second)) != MOE_OK) return st;
   if (ws_need > 0 && (st = check_ptr(ws, dev, "workspace")) != MOE_OK) return st;
-  st = hip_status(moe::launch_route_sort(top_k_index, T * k, E, expert_begin, sorted_slot, expert_offsets, slot_pos,
-                                         invalid_count, ws, stream),
+  st = hip_status(moe::launch_route_sort(nullptr, top_k_index, T, k, E, expert_begin, sorted_slot, expert_offsets,
+                                         slot_pos, invalid_count, ws, stream),
                   "route sort launch");
+  return st == MOE_OK ? ok() : st;
+}
+
+size_t moe_route_topk_workspace(int32_t T, int32_t k, int32_t E) { return moe_route_sort_workspace(T, k, E); }
+
+moe_status moe_route_topk(const float* router_logits, int32_t T, int32_t n_experts, int32_t k, int32_t renormalize,
+                          int32_t* top_k_index, float* top_k_weights, int32_t E, int32_t expert_begin,
+                          int32_t* sorted_slot, int32_t* expert_offsets, int32_t* slot_pos, int32_t* invalid_count,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (T < 0) return fail(MOE_ERR_SHAPE, "T=%d < 0", T);
+  if (n_experts < 1 || n_experts > kMaxE) return fail(MOE_ERR_SHAPE, "n_experts=%d outside [1, %d]", n_experts, kMaxE);
+  if (k < 1 || k > kMaxK || k > n_experts)
+    return fail(MOE_ERR_SHAPE, "k=%d outside [1, min(%d, n_experts=%d)]", k, kMaxK, n_experts);
+  if ((int64_t)T * k >= (int64_t)1 << 31 || (int64_t)T * n_experts >= (int64_t)1 << 40)
+    return fail(MOE_ERR_SHAPE, "T*k must stay below 2^31");
+  const bool sort = expert_offsets != nullptr;
+  if (!sort && (sorted_slot || slot_pos))
+    return fail(MOE_ERR_NULL, "sorted_slot / slot_pos given without expert_offsets");
+  if (sort && T > 0 && !sorted_slot) return fail(MOE_ERR_NULL, "sorted_slot is NULL");
+  if (sort && (E < 1 || E > kMaxE)) return fail(MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, kMaxE);
+  if (T == 0) {
+    if (!sort) return ok();
+  } else if (!router_logits || !top_k_index || !top_k_weights) {
+    return fail(MOE_ERR_NULL, "router_logits / top_k_index / top_k_weights is NULL");
+  }
+  const size_t ws_need = sort ? moe_route_sort_workspace(T, k, E) : 0;
+  if (ws_need > 0 && (!ws || ws_bytes < ws_need))
+    return fail(MOE_ERR_WORKSPACE, "workspace holds %zu bytes, %zu needed", ws ? ws_bytes : (size_t)0, ws_need);
+  const void* outs[] = {top_k_index, top_k_weights, sorted_slot, expert_offsets, slot_pos, invalid_count};
+  for (const void* o : outs)
+    if (o && T > 0 && o == (const void*)router_logits) return fail(MOE_ERR_UNSUPPORTED, "outputs must not alias router_logits");
+  if (T > 0 && ((const void*)top_k_index == (const void*)top_k_weights ||
+                (sort && ((const void*)sorted_slot == (const void*)top_k_index ||
+                          (const void*)slot_pos == (const void*)top_k_index))))
+    return fail(MOE_ERR_UNSUPPORTED, "outputs must not alias one another");
+  int dev, cus;
+  moe_status st = check_device(stream, &dev, &cus);
+  if (st != MOE_OK) return st;
+  for (auto pr : {std::make_pair((const void*)router_logits, "router_logits"),
+                  std::make_pair((const void*)top_k_index, "top_k_index"),
+                  std::make_pair((const void*)top_k_weights, "top_k_weights"),
+                  std::make_pair((const void*)sorted_slot, "sorted_slot"),
+                  std::make_pair((const void*)expert_offsets, "expert_offsets")})
+    if ((st = check_ptr(pr.first, dev, pr.second)) != MOE_OK) return st;
+  if (ws_need > 0 && (st = check_ptr(ws, dev, "workspace")) != MOE_OK) return st;
+  const moe::RouterArgs r{router_logits, n_experts, renormalize ? 1 : 0, top_k_index, top_k_weights};
+  hipError_t he;
+  if (sort)
+    he = moe::launch_route_sort(T > 0 ? &r : nullptr, top_k_index, T, k, E, expert_begin, sorted_slot, expert_offsets,
+                                slot_pos, invalid_count, ws, stream);
+  else
+    he = moe::launch_router_only(r, T, k, stream);
+  st = hip_status(he, "router / route sort launch");
   return st == MOE_OK ? ok() : st;
 }
 
@@ -397,114 +580,16 @@ size_t moe_experts_forward_workspace(int32_t T, int32_t k, const moe_weights* w)
 moe_status moe_experts_forward(const moe_weights* w, const uint16_t* hidden_states, const int32_t* top_k_index,
                                const float* top_k_weights, int32_t T, int32_t k, const moe_options* opt,
                                uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  moe_status st = validate_weights(w);
-  if (st != MOE_OK) return st;
-  if (T < 0) return fail(MOE_ERR_SHAPE, "T=%d < 0", T);
-  if (k < 1 || k > kMaxK) return fail(MOE_ERR_SHAPE, "k=%d outside [1, %d]", k, kMaxK);
-  if ((int64_t)T * k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "T*k must stay below 2^31");
-  const bool has_limit = opt && opt->has_swiglu_limit;
-  if (has_limit && !(std::isfinite(opt->swiglu_limit) && opt->swiglu_limit > 0.0f))
-    return fail(MOE_ERR_SHAPE, "swiglu_limit must be finite and > 0");
-  if (opt && opt->static_activation_scales)
-    return fail(MOE_ERR_UNSUPPORTED,
-                "the grouped experts path quantizes activations dynamically per block; static activation scales "
-                "are not supported");
-  if (T == 0) return ok();
-  if (!hidden_states || !top_k_index || !top_k_weights || !out)
-    return fail(MOE_ERR_NULL, "hidden_states / top_k_index / top_k_weights / out is NULL");
-  if ((const void*)out == (const void*)hidden_states) return fail(MOE_ERR_UNSUPPORTED, "out must not alias input");
-  const FwdLayout L = fwd_layout(T, k, w->E, w->H, w->I, w->fmt);
-  if (!ws || ws_bytes < L.total)
-    return fail(MOE_ERR_WORKSPACE, "workspace holds %zu bytes, %zu needed", ws ? ws_bytes : (size_t)0, L.total);
-  int dev, cus;
-  if ((st = check_device(stream, &dev, &cus)) != MOE_OK) return st;
-  for (auto pr : {std::make_pair((const void*)hidden_states, "hidden_states"),
-                  std::make_pair((const void*)top_k_index, "top_k_index"), std::make_pair((const void*)out, "out"),
-                  std::make_pair((const void*)w->w13, "w13"), std::make_pair((const void*)w->w2, "w2"),
-                  std::make_pair((const void*)ws, "workspace")})
-    if ((st = check_ptr(pr.first, dev, pr.second)) != MOE_OK) return st;
+  return forward_impl(w, hidden_states, nullptr, top_k_index, top_k_weights, T, k, opt, out, ws, ws_bytes, stream);
+}
 
-  const int E = w->E, H = w->H, I = w->I;
-  const int32_t S = T * k;
-  uint8_t* base = (uint8_t*)ws;
-  int32_t* sorted_slot = (int32_t*)(base + L.sorted_slot);
-  int32_t* offsets = (int32_t*)(base + L.offsets);
-  uint8_t* act_codes = base + L.act_codes;
-  void* act_scales = base + L.act_scales;
-  uint8_t* h_codes = base + L.h_codes;
-  void* h_scales = base + L.h_scales;
-  uint16_t* slot_out = (uint16_t*)(base + L.slot_out);
-  const int32_t expert_begin = opt ? opt->expert_begin : 0;
-
-  int32_t* sched = (int32_t*)(base + L.sched);
-  hipError_t he = moe::launch_route_sort_and_quant(top_k_index, S, E, expert_begin, sorted_slot, offsets,
-                                                   opt ? opt->invalid_count : nullptr, base + L.sort_ws, hidden_states,
-                                                   T, H, w->fmt, act_codes, act_scales, sched,
-                                                   2 * MOE_TILE_COUNTERS_BYTES / 4, stream);
-  if (he != hipSuccess) return hip_status(he, "route sort / quant launch");
-
-  moe::GemmParams p1{};
-  p1.a_codes = act_codes;
-  p1.a_scales = act_scales;
-  p1.a_row_index = sorted_slot;
-  p1.a_row_div = k;
-  p1.a_rows = T;
-  p1.offsets = offsets;
-  p1.E = E;
-  p1.b_codes = w->w13;
-  p1.b_scales = w->w13_scale;
-  p1.N = 2 * I;
-  p1.K = H;
-  p1.max_rows = S;
-  p1.h_codes = h_codes;
-  p1.sched = sched;
-  p1.h_scales = h_scales;
-  p1.has_limit = has_limit ? 1 : 0;
-  p1.limit = has_limit ? opt->swiglu_limit : 0.0f;
-  he = launch_gemm(p1, w->fmt, moe::kEpiSwiGLUQuant, true, cus, stream);
-  if (he != hipSuccess) return hip_status(he, "gate_up gemm launch");
-
-  moe::GemmParams p2{};
-  p2.a_codes = h_codes;
-  p2.a_scales = h_scales;
-  p2.a_row_index = nullptr;
-  p2.a_row_div = 1;
-  p2.a_rows = S;
-  p2.offsets = offsets;
-  p2.E = E;
-  p2.b_codes = w->w2;
-  p2.b_scales = w->w2_scale;
-  p2.N = H;
-  p2.K = I;
-  p2.max_rows = S;
-  p2.slot_out = slot_out;
-  p2.top_k_weights = top_k_weights;
-  p2.slot_of_row = sorted_slot;
-  p2.sched = sched + MOE_TILE_COUNTERS_BYTES / 4;
-  he = launch_gemm(p2, w->fmt, moe::kEpiWeightedScatter, false, cus, stream);
-  if (he != hipSuccess) return hip_status(he, "down gemm launch");
-
-  he = moe::launch_combine(slot_out, top_k_index, T, k, H, E, expert_begin, out, stream);
-  if (he != hipSuccess) return hip_status(he, "combine launch");
-
-  if (opt && opt->debug) {
-    const moe_debug* d = opt->debug;
-    const bool mx = w->fmt == MOE_FMT_MXFP8A_MXFP4W;
-    const size_t sc_bytes = mx ? (size_t)T * (H / 32) : 4 * (size_t)T * (H / 128);  // same in either layout
-    if ((d->sorted_slot &&
-         (he = hipMemcpyAsync(d->sorted_slot, sorted_slot, 4 * (size_t)S, hipMemcpyDeviceToDevice, stream)) !=
-             hipSuccess) ||
-        (d->expert_offsets &&
-         (he = hipMemcpyAsync(d->expert_offsets, offsets, 4 * (size_t)(E + 1), hipMemcpyDeviceToDevice, stream)) !=
-             hipSuccess) ||
-        (d->act_codes &&
-         (he = hipMemcpyAsync(d->act_codes, act_codes, (size_t)T * H, hipMemcpyDeviceToDevice, stream)) !=
-             hipSuccess) ||
-        (d->act_scales &&
-         (he = hipMemcpyAsync(d->act_scales, act_scales, sc_bytes, hipMemcpyDeviceToDevice, stream)) != hipSuccess))
-      return hip_status(he, "debug copy");
-  }
-  return ok();
+moe_status moe_experts_forward_from_logits(const moe_weights* w, const uint16_t* hidden_states,
+                                           const float* router_logits, int32_t T, int32_t n_experts, int32_t k,
+                                           int32_t renormalize, const moe_options* opt, int32_t* top_k_index,
+                                           float* top_k_weights, uint16_t* out, void* ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+  const moe::RouterArgs r{router_logits, n_experts, renormalize ? 1 : 0, top_k_index, top_k_weights};
+  return forward_impl(w, hidden_states, &r, top_k_index, top_k_weights, T, k, opt, out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

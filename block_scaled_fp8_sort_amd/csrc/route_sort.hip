@@ -25,6 +25,16 @@
 //     so that hist fits in LDS, where the scan runs;
 //  C. each wave loads its starts and runs step 3 above on its chunk.
 // The result is the same unique permutation in both cases.
+//
+// Router (optional, in front of the sort): each token's top-k is taken by a
+// group of G lanes, G the next power of two >= E capped at 64, each lane
+// holding up to 8 of the token's logits (expert e in lane e % G).  Softmax is
+// increasing in the logit, so the k most probable experts are the k largest
+// logits; k rounds of an in-group (value, id) max-reduction, lower id on equal
+// values, pick them in descending order.  Weights are exp(l - max) over the sum
+// of the same terms, taken over all E (plain softmax) or over the k chosen
+// (renormalised), in fp32.  Small batches run the router in the sort's own
+// workgroup before it sorts; large ones run it as a launch of its own.
 #include "device_common.h"
 #include "internal.h"
 #include "quant_act.h"
@@ -46,6 +56,89 @@ constexpr int kScanThreads = 1024;
 __device__ __forceinline__ int sort_key(int32_t id, int32_t E, int32_t expert_begin) {
   const int64_t local = (int64_t)id - expert_begin;
   return (local >= 0 && local < E) ? (int)local : E;
+}
+
+constexpr int kRouterThreads = 256;
+constexpr int kRouterFusedLogits = 65536;  // T * E up to which the sort's workgroup runs the router itself
+
+// Top-k of tokens wave_id * (64 / G) + lane / G, stepping by n_waves * (64 / G)
+// tokens, as described at the top of the file.  All lanes of a group take the
+// same path, so the in-group shuffles never read an idle lane.
+__device__ __forceinline__ void router_tokens(const RouterArgs r, int32_t T, int32_t k, int wave_id, int n_waves) {
+  const int E = r.n_experts;
+  int lg = 0;
+  while ((1 << lg) < E && lg < 6) ++lg;
+  const int G = 1 << lg;
+  const int lane = threadIdx.x % kWave;
+  const int lig = lane & (G - 1);
+  const int per_wave = kWave >> lg;
+  constexpr int kNone = 0x7FFFFFFF;
+  for (int64_t t = (int64_t)wave_id * per_wave + (lane >> lg); t < T; t += (int64_t)n_waves * per_wave) {
+    const float* row = r.logits + t * E;
+    float vals[8];
+    uint32_t avail = 0;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int e = lig + (v << lg);
+      vals[v] = 0.0f;
+      if (e < E) {
+        vals[v] = row[e];
+        avail |= 1u << v;
+      }
+    }
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int v = 0; v < 8; ++v)
+      if ((avail >> v) & 1) m = __builtin_fmaxf(m, vals[v]);
+    for (int x = 1; x < G; x <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, x, kWave));
+    float z = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 8; ++v)
+      if ((avail >> v) & 1) z += expf(vals[v] - m);
+    for (int x = 1; x < G; x <<= 1) z += __shfl_xor(z, x, kWave);
+
+    int my_id = 0;
+    float my_val = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      // the lane's best remaining logit (v, hence e, ascending: lowest e among equals)
+      float bv = 0.0f;
+      int be = kNone;
+#pragma unroll
+      for (int v = 0; v < 8; ++v)
+        if (((avail >> v) & 1) && (be == kNone || vals[v] > bv)) {
+          bv = vals[v];
+          be = lig + (v << lg);
+        }
+      for (int x = 1; x < G; x <<= 1) {
+        const float ov = __shfl_xor(bv, x, kWave);
+        const int oe = __shfl_xor(be, x, kWave);
+        if (oe != kNone && (be == kNone || ov > bv || (ov == bv && oe < be))) {
+          bv = ov;
+          be = oe;
+        }
+      }
+      if ((be & (G - 1)) == lig) avail &= ~(1u << (be >> lg));
+      if (lig == j) {
+        my_id = be;
+        my_val = bv;
+      }
+    }
+    const float ex = lig < k ? expf(my_val - m) : 0.0f;
+    float denom = z;
+    if (r.renormalize) {
+      denom = ex;
+      for (int x = 1; x < G; x <<= 1) denom += __shfl_xor(denom, x, kWave);
+    }
+    if (lig < k) {
+      r.ids[t * k + lig] = my_id;
+      r.weights[t * k + lig] = ex / denom;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(const RouterArgs r, int32_t T, int32_t k) {
+  const int wave = (int)((blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / kWave);
+  router_tokens(r, T, k, wave, (int)(gridDim.x * blockDim.x / kWave));
 }
 
 // Stable scatter of slots [c_begin, c_end) by one wave; start[key] is where the
@@ -270,7 +363,17 @@ __device__ __forceinline__ void sort_one_workgroup(const int32_t* __restrict__ i
   scatter_chunk(ids, c_begin, c_end, E, expert_begin, hist + wave * K1, sorted_slot, slot_pos);
 }
 
-__global__ __launch_bounds__(kSortThreads) void route_sort_kernel(const int32_t* __restrict__ ids, int32_t S,
+// The router's writes of ids reach the sort's reads through the workgroup
+// barrier (workgroup-scope release/acquire covers global memory too).
+__device__ __forceinline__ void router_in_workgroup(const RouterArgs& router, int32_t T, int32_t k) {
+  if (router.logits) {
+    router_tokens(router, T, k, threadIdx.x / kWave, kSortWaves);
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kSortThreads) void route_sort_kernel(const RouterArgs router,
+                                                                   const int32_t* ids, int32_t T, int32_t k,
                                                                    int32_t E, int32_t expert_begin,
                                                                    int32_t* __restrict__ sorted_slot,
                                                                    int32_t* __restrict__ offsets,
@@ -278,7 +381,8 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(const int32_t*
                                                                    int32_t* __restrict__ invalid_count,
                                                                    int32_t* __restrict__ zero, int32_t n_zero) {
   for (int i = threadIdx.x; i < n_zero; i += blockDim.x) zero[i] = 0;
-  sort_one_workgroup(ids, S, E, expert_begin, sorted_slot, offsets, slot_pos, invalid_count);
+  router_in_workgroup(router, T, k);
+  sort_one_workgroup(ids, T * k, E, expert_begin, sorted_slot, offsets, slot_pos, invalid_count);
 }
 
 // Small batches: the sort and the activation quantization are independent and
@@ -287,14 +391,16 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(const int32_t*
 // lanes of one quantization block).
 template <int BLOCK>
 __global__ __launch_bounds__(kSortThreads) void route_quant_kernel(
-    const int32_t* __restrict__ ids, int32_t S, int32_t E, int32_t expert_begin, int32_t* __restrict__ sorted_slot,
+    const RouterArgs router, const int32_t* ids, int32_t T, int32_t k, int32_t E, int32_t expert_begin,
+    int32_t* __restrict__ sorted_slot,
     int32_t* __restrict__ offsets, int32_t* __restrict__ invalid_count, const uint4* __restrict__ x,
     int64_t n_chunks, int32_t rows, int32_t H, uint8_t* __restrict__ codes, void* __restrict__ scales,
     int32_t* __restrict__ zero, int32_t n_zero) {
   if (blockIdx.x == 1 || gridDim.x == 1)
     for (int i = threadIdx.x; i < n_zero; i += blockDim.x) zero[i] = 0;
   if (blockIdx.x == 0) {
-    sort_one_workgroup(ids, S, E, expert_begin, sorted_slot, offsets, nullptr, invalid_count);
+    router_in_workgroup(router, T, k);
+    sort_one_workgroup(ids, T * k, E, expert_begin, sorted_slot, offsets, nullptr, invalid_count);
     return;
   }
   const int64_t stride = (int64_t)(gridDim.x - 1) * blockDim.x;
@@ -313,20 +419,59 @@ size_t route_sort_ws_bytes(int32_t S, int32_t E) {
   return sizeof(int32_t) * (size_t)(E + 2) * n_chunks;
 }
 
-hipError_t launch_route_sort(const int32_t* ids, int32_t S, int32_t E, int32_t expert_begin, int32_t* sorted_slot,
-                             int32_t* offsets, int32_t* slot_pos, int32_t* invalid_count, void* ws,
-                             hipStream_t stream) {
-  return launch_route_sort_zero(ids, S, E, expert_begin, sorted_slot, offsets, slot_pos, invalid_count, ws, nullptr, 0,
-                                stream);
+namespace {
+
+const RouterArgs kNoRouter{nullptr, 0, 0, nullptr, nullptr};
+
+// Whether the sort's one workgroup runs the router itself.
+bool router_fused(const RouterArgs* router, int32_t T, int32_t k) {
+  return (int64_t)T * k < kMultiBlockFrom && (int64_t)T * router->n_experts <= kRouterFusedLogits;
 }
 
-hipError_t launch_route_sort_zero(const int32_t* ids, int32_t S, int32_t E, int32_t expert_begin,
-                                  int32_t* sorted_slot, int32_t* offsets, int32_t* slot_pos, int32_t* invalid_count,
-                                  void* ws, int32_t* zero, int32_t n_zero, hipStream_t stream) {
+hipError_t launch_router(const RouterArgs& r, int32_t T, int32_t k, hipStream_t stream) {
+  int lg = 0;
+  while ((1 << lg) < r.n_experts && lg < 6) ++lg;
+  const int64_t per_block = (int64_t)(kRouterThreads / kWave) * (kWave >> lg);
+  int64_t blocks = (T + per_block - 1) / per_block;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(router_topk_kernel, dim3((unsigned)blocks), dim3(kRouterThreads), 0, stream, r, T, k);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_router_only(const RouterArgs& router, int32_t T, int32_t k, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  return launch_router(router, T, k, stream);
+}
+
+hipError_t launch_route_sort(const RouterArgs* router, const int32_t* ids, int32_t T, int32_t k, int32_t E,
+                             int32_t expert_begin, int32_t* sorted_slot, int32_t* offsets, int32_t* slot_pos,
+                             int32_t* invalid_count, void* ws, hipStream_t stream) {
+  return launch_route_sort_zero(router, ids, T, k, E, expert_begin, sorted_slot, offsets, slot_pos, invalid_count,
+                                ws, nullptr, 0, stream);
+}
+
+hipError_t launch_route_sort_zero(const RouterArgs* router, const int32_t* ids, int32_t T, int32_t k, int32_t E,
+                                  int32_t expert_begin, int32_t* sorted_slot, int32_t* offsets, int32_t* slot_pos,
+                                  int32_t* invalid_count, void* ws, int32_t* zero, int32_t n_zero,
+                                  hipStream_t stream) {
+  if (router && !router->logits) router = nullptr;
+  const int32_t S = T * k;
   if (S < kMultiBlockFrom) {
-    hipLaunchKernelGGL(route_sort_kernel, dim3(1), dim3(kSortThreads), route_sort_lds_bytes(E), stream, ids, S, E,
-                       expert_begin, sorted_slot, offsets, slot_pos, invalid_count, zero, n_zero);
+    const bool fuse = router && router_fused(router, T, k);
+    if (router && !fuse) {
+      hipError_t e = launch_router(*router, T, k, stream);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(route_sort_kernel, dim3(1), dim3(kSortThreads), route_sort_lds_bytes(E), stream,
+                       fuse ? *router : kNoRouter, ids, T, k, E, expert_begin, sorted_slot, offsets, slot_pos,
+                       invalid_count, zero, n_zero);
     return hipGetLastError();
+  }
+  if (router) {
+    hipError_t e = launch_router(*router, T, k, stream);
+    if (e != hipSuccess) return e;
   }
   const int32_t chunk = sort_chunk(S, E);
   const int32_t n_chunks = (S + chunk - 1) / chunk;
@@ -343,27 +488,36 @@ hipError_t launch_route_sort_zero(const int32_t* ids, int32_t S, int32_t E, int3
   return hipGetLastError();
 }
 
-hipError_t launch_route_sort_and_quant(const int32_t* ids, int32_t S, int32_t E, int32_t expert_begin,
-                                      int32_t* sorted_slot, int32_t* offsets, int32_t* invalid_count, void* sort_ws,
-                                      const uint16_t* x, int32_t rows, int32_t H, int fmt, uint8_t* codes,
-                                      void* scales, int32_t* zero, int32_t n_zero, hipStream_t stream) {
+hipError_t launch_route_sort_and_quant(const RouterArgs* router, const int32_t* ids, int32_t T, int32_t k, int32_t E,
+                                      int32_t expert_begin, int32_t* sorted_slot, int32_t* offsets,
+                                      int32_t* invalid_count, void* sort_ws, const uint16_t* x, int32_t rows,
+                                      int32_t H, int fmt, uint8_t* codes, void* scales, int32_t* zero,
+                                      int32_t n_zero, hipStream_t stream) {
+  if (router && !router->logits) router = nullptr;
+  const int32_t S = T * k;
   const int64_t n_chunks = (int64_t)rows * H / 8;
   if (S >= kMultiBlockFrom || n_chunks == 0) {
-    hipError_t e = launch_route_sort_zero(ids, S, E, expert_begin, sorted_slot, offsets, nullptr, invalid_count,
-                                          sort_ws, zero, n_zero, stream);
+    hipError_t e = launch_route_sort_zero(router, ids, T, k, E, expert_begin, sorted_slot, offsets, nullptr,
+                                          invalid_count, sort_ws, zero, n_zero, stream);
     if (e != hipSuccess) return e;
     return launch_quant_act(x, rows, H, fmt, codes, scales, stream);
   }
+  const bool fuse = router && router_fused(router, T, k);
+  if (router && !fuse) {
+    hipError_t e = launch_router(*router, T, k, stream);
+    if (e != hipSuccess) return e;
+  }
+  const RouterArgs r = fuse ? *router : kNoRouter;
   const int64_t want = (n_chunks + kSortThreads - 1) / kSortThreads;
   const int blocks = 1 + (int)(want < 256 * 16 ? want : 256 * 16);
   if (fmt == 0)
     hipLaunchKernelGGL(route_quant_kernel<128>, dim3(blocks), dim3(kSortThreads), route_sort_lds_bytes(E), stream,
-                       ids, S, E, expert_begin, sorted_slot, offsets, invalid_count, (const uint4*)x, n_chunks, rows,
-                       H, codes, scales, zero, n_zero);
+                       r, ids, T, k, E, expert_begin, sorted_slot, offsets, invalid_count, (const uint4*)x, n_chunks,
+                       rows, H, codes, scales, zero, n_zero);
   else
     hipLaunchKernelGGL(route_quant_kernel<32>, dim3(blocks), dim3(kSortThreads), route_sort_lds_bytes(E), stream,
-                       ids, S, E, expert_begin, sorted_slot, offsets, invalid_count, (const uint4*)x, n_chunks, rows,
-                       H, codes, scales, zero, n_zero);
+                       r, ids, T, k, E, expert_begin, sorted_slot, offsets, invalid_count, (const uint4*)x, n_chunks,
+                       rows, H, codes, scales, zero, n_zero);
   return hipGetLastError();
 }
 

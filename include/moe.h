@@ -101,6 +101,44 @@ moe_status moe_route_sort(const int32_t* top_k_index, int32_t T, int32_t k, int3
                           int32_t* sorted_slot, int32_t* expert_offsets, int32_t* slot_pos,
                           int32_t* invalid_count, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------- router + route sort --
+ * The router step in front of the experts forward, fused with the route sort.
+ * The pages hand the router's output to the experts untouched, as global
+ * expert ids with unmasked weights ("deepgemm_megamoe EP implementation for
+ * DeepGEMM Mega MoE", PR #49606: "How it runs" and the parallel-style table);
+ * the router of the layers this forward is shaped on (Mixtral, Qwen3-MoE) is a
+ * softmax over the expert logits, the k most probable experts, and their
+ * probabilities renormalised to sum 1.  Per token t:
+ *   ids:     the k largest of router_logits[t, 0..n_experts), compared as fp32
+ *            values, in descending order, the lower id first among equal
+ *            logits (softmax is increasing, so these are the k most probable);
+ *   weights: p_e = exp(l_e - max_e' l_e') / sum over all e' of the same terms;
+ *            top_k_weights[t, j] = p of ids[t, j], divided by the sum of the k
+ *            selected p when `renormalize` is nonzero.  Computed in fp32 (the
+ *            difference l - max rounded once, exp accurate to about 1 ulp,
+ *            sums in lane order): a weight agrees with an exact computation
+ *            to a relative (n_experts + 4 + 2 (max - min of the token's
+ *            logits)) * 2^-24; the ids agree exactly.
+ * Logits must be finite (not checked).
+ *
+ *  router_logits   device float [T, n_experts], row-major.
+ *  top_k_index     device int32 [T, k] out: the chosen global ids.
+ *  top_k_weights   device float [T, k] out.
+ *  E, expert_begin, sorted_slot, expert_offsets, slot_pos, invalid_count, ws:
+ *                  as in moe_route_sort, applied to the chosen ids (ids
+ *                  outside [expert_begin, expert_begin + E) are sentinels).
+ *                  expert_offsets NULL runs the router alone (sorted_slot
+ *                  and slot_pos must then be NULL too; E and ws are unused).
+ * Small batches (T * k < 16384 and T * n_experts <= 65536) run the router and
+ * the sort in one launch.
+ * Limits: 1 <= n_experts <= 512, 1 <= k <= min(64, n_experts); the rest as in
+ * moe_route_sort. */
+size_t moe_route_topk_workspace(int32_t T, int32_t k, int32_t E);
+moe_status moe_route_topk(const float* router_logits, int32_t T, int32_t n_experts, int32_t k, int32_t renormalize,
+                          int32_t* top_k_index, float* top_k_weights, int32_t E, int32_t expert_begin,
+                          int32_t* sorted_slot, int32_t* expert_offsets, int32_t* slot_pos, int32_t* invalid_count,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* --------------------------------------------------- activation quantization --
  * Dynamic per-block quantization of bf16 rows ([P-grouped], "What it means":
  * activations are quantized dynamically per block; precomputed static scales are
@@ -255,6 +293,19 @@ size_t moe_experts_forward_workspace(int32_t T, int32_t k, const moe_weights* w)
 moe_status moe_experts_forward(const moe_weights* w, const uint16_t* hidden_states, const int32_t* top_k_index,
                                const float* top_k_weights, int32_t T, int32_t k, const moe_options* opt,
                                uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The same forward starting one step earlier, from the router's logits: the
+ * router of moe_route_topk chooses each token's k experts among n_experts
+ * (global ids) and their weights, writes them to top_k_index / top_k_weights
+ * (device int32 / float [T, k], outputs owned by the caller), and the forward
+ * above then runs on them.  Small batches route, sort and quantize in one
+ * launch.  The workspace is moe_experts_forward_workspace(T, k, w).  The
+ * outputs must not alias each other or the inputs. */
+moe_status moe_experts_forward_from_logits(const moe_weights* w, const uint16_t* hidden_states,
+                                           const float* router_logits, int32_t T, int32_t n_experts, int32_t k,
+                                           int32_t renormalize, const moe_options* opt, int32_t* top_k_index,
+                                           float* top_k_weights, uint16_t* out, void* ws, size_t ws_bytes,
+                                           hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,7 @@ def lib():
 def test_library_exports_every_declared_function(lib):
     names = _declared_functions()
     assert "moe_experts_forward" in names and "moe_grouped_gemm" in names
-    assert len(names) == 10
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
 
@@ -70,6 +70,53 @@ def test_route_sort_workspace(lib):
     p = ctypes.c_void_p(16)
     assert lib.moe_route_sort(p, 2048, 8, 256, 0, ctypes.c_void_p(64), p, None, None, None, 0, None) == WS
     assert lib.moe_route_sort(p, 2048, 8, 256, 0, ctypes.c_void_p(64), p, None, None, p, 100, None) == WS
+
+
+def test_route_topk_refusals(lib):
+    p = ctypes.c_void_p(16)
+    q, r, u = ctypes.c_void_p(48), ctypes.c_void_p(80), ctypes.c_void_p(112)
+
+    def call(T=4, n=8, k=2, ids=q, w=r, E=8, ss=u, off=ctypes.c_void_p(144), ws=None, ws_bytes=0, logits=p):
+        return lib.moe_route_topk(logits, T, n, k, 1, ids, w, E, 0, ss, off, None, None, ws, ws_bytes, None)
+
+    assert call(k=9) == SHAPE  # k > n_experts
+    assert call(k=0) == SHAPE
+    assert call(n=0) == SHAPE
+    assert call(n=513, k=2) == SHAPE
+    assert call(T=-1) == SHAPE
+    assert call(E=0) == SHAPE
+    assert call(logits=None) == NULL
+    assert call(ids=None) == NULL
+    assert call(off=None) == NULL  # sorted_slot without expert_offsets
+    assert call(ss=None) == NULL  # the sort needs sorted_slot when T > 0
+    assert call(ids=p) == UNSUP  # top_k_index aliases the logits
+    assert b"alias" in lib.moe_last_error()
+    assert call(w=q) == UNSUP
+    assert call(ss=q) == UNSUP
+    assert call(T=2048, n=256, k=8, E=256) == WS  # multi-workgroup sort needs its histograms
+    assert call(T=0, ss=None, off=None, ids=None, w=None, logits=None) == OK  # router alone, nothing to do
+    assert lib.moe_route_topk_workspace(2048, 8, 256) == lib.moe_route_sort_workspace(2048, 8, 256)
+
+
+def test_forward_from_logits_refusals(lib):
+    p = ctypes.c_void_p(16)
+    w = _weights()
+
+    def fwd(T=8, n=8, k=2, logits=ctypes.c_void_p(24), ids=ctypes.c_void_p(48), wts=ctypes.c_void_p(80),
+            out=ctypes.c_void_p(112), ws=ctypes.c_void_p(64), ws_bytes=1 << 40):
+        return lib.moe_experts_forward_from_logits(ctypes.byref(w), p, logits, T, n, k, 1, None, ids, wts, out, ws,
+                                                   ws_bytes, None)
+
+    assert fwd(k=9) == SHAPE
+    assert fwd(n=0) == SHAPE
+    assert fwd(n=600) == SHAPE
+    assert fwd(T=0) == OK
+    assert fwd(logits=None) == NULL
+    assert fwd(ids=None) == NULL
+    assert fwd(ids=ctypes.c_void_p(24)) == UNSUP  # top_k_index aliases the logits
+    assert fwd(wts=ctypes.c_void_p(48)) == UNSUP  # the two routing outputs alias
+    assert fwd(out=ctypes.c_void_p(80)) == UNSUP
+    assert fwd(ws=None) == WS
 
 
 def test_quant_refusals(lib):

@@ -1,8 +1,8 @@
 """Seeded synthetic inputs for the MoE experts forward.
 
-This module generates inputs only: hidden states, top-k routing (the router
-itself is not part of the experts forward; its outputs are inputs here) and
-offline-quantized expert weights.  It holds none of the forward's arithmetic:
+This module generates inputs only: hidden states, top-k routing (the experts
+forward takes the router's outputs as inputs), router logits (the input of the
+router step in front of it) and offline-quantized expert weights.  It holds none of the forward's arithmetic:
 weights are quantized with torch's own float8 cast (FP8) or a nearest-grid
 lookup (FP4), which stands for the checkpoint's offline quantization.  Both the
 HIP path and the CPU oracle receive the same arrays from here.
@@ -75,6 +75,15 @@ def hidden_states(T: int, H: int, seed: int, device="cpu") -> torch.Tensor:
     """bf16 [T, H], entries N(0, 1) rounded to bf16."""
     g = _gen(device, seed, "x")
     return torch.randn((T, H), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+
+def router_logits(T: int, E: int, seed: int, device="cpu", ties: bool = False) -> torch.Tensor:
+    """fp32 [T, E] router logits, N(0, 1); with ``ties`` drawn from the eight
+    integers -4..3 instead, so that many logits of a token are equal."""
+    g = _gen(device, seed, "logits")
+    if ties:
+        return torch.randint(-4, 4, (T, E), generator=g, device=device).to(torch.float32)
+    return torch.randn((T, E), generator=g, device=device, dtype=torch.float32)
 
 
 def routing(T: int, E: int, k: int, kind: str, seed: int, zipf_s: float = 0.0, skip: float = 0.0,
