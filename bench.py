@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--only", choices=["gate_up", "down"], default=None,
                     help="time one grouped GEMM alone (for counter runs); prints its own JSON line")
+    ap.add_argument("--router", action="store_true",
+                    help="start each step from fp32 router logits: softmax top-k + route sort + the forward "
+                         "(workloads with softmax routing only)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="time a plain device-to-device copy of this many bytes (counter calibration)")
     return ap.parse_args()
@@ -93,9 +96,19 @@ def main():
     log(f"[bench] workload {wl.name}: generating inputs on the GPU")
     inp = W.inputs(wl, dev)
     w = moe.prepare_weights(inp["w13"], inp["s13"], inp["w2"], inp["s2"], fmt=wl.fmt)
-    x, ids, wts = inp["x"], inp["ids"], inp["w"]
     T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
     S = T * k
+    logits = None
+    if args.router:
+        if wl.routing != "uniform":
+            print(f"--router needs a workload routed by a softmax over logits; {wl.name} is {wl.routing}",
+                  file=sys.stderr)
+            sys.exit(2)
+        # the router's own routing replaces the generated one everywhere below
+        logits = W.router_logits(T, E, wl.seed, device=dev)
+        inp["ids"], inp["w"], _, _, _, _ = moe.route_topk(logits, k, sort=False)
+        torch.cuda.synchronize()
+    x, ids, wts = inp["x"], inp["ids"], inp["w"]
 
     ids_h = ids.cpu().numpy()
     valid = (ids_h >= 0) & (ids_h < E)
@@ -115,8 +128,15 @@ def main():
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        moe.experts_forward(x, ids, wts, w, swiglu_limit=wl.swiglu_limit, out=out, workspace=ws)
+    if logits is None:
+        def step():
+            moe.experts_forward(x, ids, wts, w, swiglu_limit=wl.swiglu_limit, out=out, workspace=ws)
+    else:
+        r_ids, r_w = torch.empty_like(ids), torch.empty_like(wts)
+
+        def step():
+            moe.experts_forward_from_logits(x, logits, k, w, swiglu_limit=wl.swiglu_limit, out=out,
+                                            top_k_index=r_ids, top_k_weights=r_w, workspace=ws)
 
     if args.only:
         return only_gemm(args, wl, inp, w, dev)
@@ -138,6 +158,30 @@ def main():
     t_wall = time.perf_counter() - t_wall
     ms = ev0.elapsed_time(ev1) / args.steps
     log(f"[bench] {ms:.3f} ms/step (wall {1e3 * t_wall / args.steps:.3f} ms/step)")
+    router_us = None
+    if logits is not None:
+        # the router + route sort launch(es) alone, as moe_route_topk enqueues them
+        rt = [torch.empty_like(ids), torch.empty_like(wts)]
+        ss_b = torch.empty(S, dtype=torch.int32, device=dev)
+        off_b = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        r_ws = torch.empty(max(1, moe.load_library().moe_route_topk_workspace(T, k, E)), dtype=torch.uint8,
+                           device=dev)
+
+        def route():
+            moe.load_library().moe_route_topk(logits.data_ptr(), T, E, k, 1, rt[0].data_ptr(), rt[1].data_ptr(), E,
+                                              0, ss_b.data_ptr(), off_b.data_ptr(), None, None, r_ws.data_ptr(),
+                                              r_ws.numel(), stream.cuda_stream)
+
+        for _ in range(3):
+            route()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            route()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        router_us = ev0.elapsed_time(ev1) / args.steps * 1e3
+        log(f"[bench] router + route sort {router_us:.1f} us")
 
     # ---- dominant kernel: gate_up grouped GEMM with the SwiGLU + h-quant epilogue,
     # enqueued through the C ABI in the same configuration as in the forward
@@ -211,6 +255,9 @@ def main():
         }),
     }
 
+    if logits is not None:
+        result["config"]["router"] = "fp32 logits N(0,1): softmax, top-k (lower id on ties), renormalised"
+        result["config"]["router_sort_us"] = round(router_us, 2)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -59,86 +59,114 @@ __device__ __forceinline__ int sort_key(int32_t id, int32_t E, int32_t expert_be
 }
 
 constexpr int kRouterThreads = 256;
-constexpr int kRouterFusedLogits = 65536;  // T * E up to which the sort's workgroup runs the router itself
+// The sort's workgroup runs the router itself up to this many tokens (two per
+// DPP row: each row works through its tokens one after another) and experts.
+constexpr int kRouterFusedMaxT = 128;
+constexpr int kRouterFusedMaxE = 128;
+constexpr int kRouterLanes = 16;           // lanes per token: one DPP row
 
-// Top-k of tokens wave_id * (64 / G) + lane / G, stepping by n_waves * (64 / G)
-// tokens, as described at the top of the file.  All lanes of a group take the
-// same path, so the in-group shuffles never read an idle lane.
+// All-reduce step s (0..3) of a DPP row: exchange with lane i ^ 1, i ^ 2, then
+// the mirrored lane in the half row (i ^ 7) and in the row (i ^ 15).  After the
+// four steps every lane of the row holds the combination of all 16; the
+// partners are symmetric, so every lane computes the same bits.
+__device__ __forceinline__ int dpp_step(int v, int s) {
+  switch (s) {
+    case 0: return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    case 1: return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    case 2: return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    default: return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+  }
+}
+__device__ __forceinline__ float dpp_step_f(float v, int s) { return __int_as_float(dpp_step(__float_as_int(v), s)); }
+
+// Top-k of tokens, one DPP row of 16 lanes per token: lane i of the row holds
+// logits e = i + 16 v, v < NV (NV >= ceil(E / 16)).  Rows of a wave take tokens
+// wave_id * 4 + row, stepping by n_waves * 4.  All lanes of a row take the same
+// path, so the row never reads an idle lane.
+template <int NV>
 __device__ __forceinline__ void router_tokens(const RouterArgs r, int32_t T, int32_t k, int wave_id, int n_waves) {
   const int E = r.n_experts;
-  int lg = 0;
-  while ((1 << lg) < E && lg < 6) ++lg;
-  const int G = 1 << lg;
   const int lane = threadIdx.x % kWave;
-  const int lig = lane & (G - 1);
-  const int per_wave = kWave >> lg;
+  const int lig = lane & (kRouterLanes - 1);
+  constexpr int kPerWave = kWave / kRouterLanes;
   constexpr int kNone = 0x7FFFFFFF;
-  for (int64_t t = (int64_t)wave_id * per_wave + (lane >> lg); t < T; t += (int64_t)n_waves * per_wave) {
+  const float ninf = -__builtin_inff();
+  for (int64_t t = (int64_t)wave_id * kPerWave + lane / kRouterLanes; t < T; t += (int64_t)n_waves * kPerWave) {
     const float* row = r.logits + t * E;
-    float vals[8];
+    float vals[NV];
     uint32_t avail = 0;
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int e = lig + (v << lg);
-      vals[v] = 0.0f;
+    for (int v = 0; v < NV; ++v) {
+      const int e = lig + v * kRouterLanes;
+      vals[v] = ninf;
       if (e < E) {
         vals[v] = row[e];
         avail |= 1u << v;
       }
     }
-    float m = -__builtin_inff();
+    float m = ninf;
 #pragma unroll
-    for (int v = 0; v < 8; ++v)
-      if ((avail >> v) & 1) m = __builtin_fmaxf(m, vals[v]);
-    for (int x = 1; x < G; x <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, x, kWave));
+    for (int v = 0; v < NV; ++v) m = __builtin_fmaxf(m, vals[v]);  // absent values are -inf
+#pragma unroll
+    for (int st = 0; st < 4; ++st) m = __builtin_fmaxf(m, dpp_step_f(m, st));
     float z = 0.0f;
 #pragma unroll
-    for (int v = 0; v < 8; ++v)
+    for (int v = 0; v < NV; ++v)
       if ((avail >> v) & 1) z += expf(vals[v] - m);
-    for (int x = 1; x < G; x <<= 1) z += __shfl_xor(z, x, kWave);
-
-    int my_id = 0;
-    float my_val = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      // the lane's best remaining logit (v, hence e, ascending: lowest e among equals)
-      float bv = 0.0f;
-      int be = kNone;
 #pragma unroll
-      for (int v = 0; v < 8; ++v)
-        if (((avail >> v) & 1) && (be == kNone || vals[v] > bv)) {
-          bv = vals[v];
-          be = lig + (v << lg);
+    for (int st = 0; st < 4; ++st) z += dpp_step_f(z, st);
+
+    // k rounds; pick j = 16 c + i is kept by lane i of the row in slot c
+    int pick_id[4] = {0, 0, 0, 0};
+    float pick_val[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float sel = 0.0f;  // sum of exp(pick - m) over the picks, in pick order
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (c * kRouterLanes >= k) break;
+      const int jn = min(k - c * kRouterLanes, kRouterLanes);
+      for (int jj = 0; jj < jn; ++jj) {
+        // the lane's best remaining logit (v, hence e, ascending: lowest e
+        // among equals); a lane with none left offers (-inf, kNone), which
+        // loses to any real logit (logits are finite)
+        float bv = ninf;
+        int be = kNone;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          const bool take = ((avail >> v) & 1) && (be == kNone || vals[v] > bv);
+          bv = take ? vals[v] : bv;
+          be = take ? lig + v * kRouterLanes : be;
         }
-      for (int x = 1; x < G; x <<= 1) {
-        const float ov = __shfl_xor(bv, x, kWave);
-        const int oe = __shfl_xor(be, x, kWave);
-        if (oe != kNone && (be == kNone || ov > bv || (ov == bv && oe < be))) {
-          bv = ov;
-          be = oe;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const float ov = dpp_step_f(bv, st);
+          const int oe = dpp_step(be, st);
+          const bool take = ov > bv || (ov == bv && oe < be);
+          bv = take ? ov : bv;
+          be = take ? oe : be;
+        }
+        if ((be & (kRouterLanes - 1)) == lig) avail &= ~(1u << (be / kRouterLanes));
+        sel += expf(bv - m);
+        if (lig == jj) {
+          pick_id[c] = be;
+          pick_val[c] = bv;
         }
       }
-      if ((be & (G - 1)) == lig) avail &= ~(1u << (be >> lg));
-      if (lig == j) {
-        my_id = be;
-        my_val = bv;
+    }
+    const float denom = r.renormalize ? sel : z;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = c * kRouterLanes + lig;
+      if (j < k) {
+        r.ids[t * k + j] = pick_id[c];
+        r.weights[t * k + j] = expf(pick_val[c] - m) / denom;
       }
-    }
-    const float ex = lig < k ? expf(my_val - m) : 0.0f;
-    float denom = z;
-    if (r.renormalize) {
-      denom = ex;
-      for (int x = 1; x < G; x <<= 1) denom += __shfl_xor(denom, x, kWave);
-    }
-    if (lig < k) {
-      r.ids[t * k + lig] = my_id;
-      r.weights[t * k + lig] = ex / denom;
     }
   }
 }
-
+template <int NV>
 __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(const RouterArgs r, int32_t T, int32_t k) {
   const int wave = (int)((blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / kWave);
-  router_tokens(r, T, k, wave, (int)(gridDim.x * blockDim.x / kWave));
+  router_tokens<NV>(r, T, k, wave, (int)(gridDim.x * blockDim.x / kWave));
 }
 
 // Stable scatter of slots [c_begin, c_end) by one wave; start[key] is where the
@@ -367,7 +395,7 @@ __device__ __forceinline__ void sort_one_workgroup(const int32_t* __restrict__ i
 // barrier (workgroup-scope release/acquire covers global memory too).
 __device__ __forceinline__ void router_in_workgroup(const RouterArgs& router, int32_t T, int32_t k) {
   if (router.logits) {
-    router_tokens(router, T, k, threadIdx.x / kWave, kSortWaves);
+    router_tokens<kRouterFusedMaxE / kRouterLanes>(router, T, k, threadIdx.x / kWave, kSortWaves);
     __syncthreads();
   }
 }
@@ -425,16 +453,27 @@ const RouterArgs kNoRouter{nullptr, 0, 0, nullptr, nullptr};
 
 // Whether the sort's one workgroup runs the router itself.
 bool router_fused(const RouterArgs* router, int32_t T, int32_t k) {
-  return (int64_t)T * k < kMultiBlockFrom && (int64_t)T * router->n_experts <= kRouterFusedLogits;
+  return (int64_t)T * k < kMultiBlockFrom && T <= kRouterFusedMaxT && router->n_experts <= kRouterFusedMaxE;
 }
 
 hipError_t launch_router(const RouterArgs& r, int32_t T, int32_t k, hipStream_t stream) {
-  int lg = 0;
-  while ((1 << lg) < r.n_experts && lg < 6) ++lg;
-  const int64_t per_block = (int64_t)(kRouterThreads / kWave) * (kWave >> lg);
+  const int64_t per_block = kRouterThreads / kRouterLanes;  // one token per DPP row
   int64_t blocks = (T + per_block - 1) / per_block;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(router_topk_kernel, dim3((unsigned)blocks), dim3(kRouterThreads), 0, stream, r, T, k);
+  if (blocks > 8192) blocks = 8192;
+  const int v = (r.n_experts + kRouterLanes - 1) / kRouterLanes;
+  const dim3 g((unsigned)blocks), b(kRouterThreads);
+  if (v <= 1)
+    hipLaunchKernelGGL(router_topk_kernel<1>, g, b, 0, stream, r, T, k);
+  else if (v <= 2)
+    hipLaunchKernelGGL(router_topk_kernel<2>, g, b, 0, stream, r, T, k);
+  else if (v <= 4)
+    hipLaunchKernelGGL(router_topk_kernel<4>, g, b, 0, stream, r, T, k);
+  else if (v <= 8)
+    hipLaunchKernelGGL(router_topk_kernel<8>, g, b, 0, stream, r, T, k);
+  else if (v <= 16)
+    hipLaunchKernelGGL(router_topk_kernel<16>, g, b, 0, stream, r, T, k);
+  else
+    hipLaunchKernelGGL(router_topk_kernel<32>, g, b, 0, stream, r, T, k);
   return hipGetLastError();
 }
 
