@@ -185,3 +185,82 @@ def test_forward_from_logits_graph_replay():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(host(out).view(np.uint16), host(ref).view(np.uint16)), f"replay {rep}"
+
+
+# ------------------------------------------------ one GPU's share under EP
+EP_CASES = [
+    _workload("ep_fp8_tiled", FP8, T=333, H=512, I=256, E=12, k=4, seed=41),
+    _workload("ep_fp8_few_rows", FP8, T=40, H=512, I=256, E=32, k=4, seed=42),
+    _workload("ep_mx_clamp", MX, T=250, H=256, I=256, E=8, k=3, limit=7.0, seed=43),
+]
+
+
+@pytest.mark.parametrize("wl", EP_CASES, ids=[w.name for w in EP_CASES])
+@pytest.mark.parametrize("world", [2, 3])
+def test_ep_equal_token_slices_gather_to_the_full_batch(wl, world):
+    """The Mega MoE EP implementation hands each rank an equal slice of the
+    batch, pads the last slice with skipped slots and all-gathers the outputs
+    ("deepgemm_megamoe EP implementation for DeepGEMM Mega MoE", "How it runs").
+    Each slice is one call here; tokens are independent, so the gathered
+    slices equal the whole-batch forward on every real token, and padded rows
+    are exact zeros."""
+    inp = W.inputs(wl, DEV)
+    w = moe.prepare_weights(inp["w13"], inp["s13"], inp["w2"], inp["s2"], fmt=wl.fmt)
+    full = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w, swiglu_limit=wl.swiglu_limit).clone()
+    per = -(-wl.T // world)
+    pad = per * world - wl.T
+    x = torch.cat([inp["x"], torch.zeros((pad, wl.H), dtype=torch.bfloat16, device=DEV)])
+    ids = torch.cat([inp["ids"], torch.full((pad, wl.k), -1, dtype=torch.int32, device=DEV)])
+    wts = torch.cat([inp["w"], torch.full((pad, wl.k), float("nan"), dtype=torch.float32, device=DEV)])
+    outs = [moe.experts_forward(x[r * per:(r + 1) * per].contiguous(), ids[r * per:(r + 1) * per].contiguous(),
+                                wts[r * per:(r + 1) * per].contiguous(), w, swiglu_limit=wl.swiglu_limit).clone()
+            for r in range(world)]
+    gathered = torch.cat(outs)
+    torch.cuda.synchronize()
+    g, f = host(gathered).view(np.uint16), host(full).view(np.uint16)
+    ref = oracle.forward(wl.fmt, *(host(inp[n]) for n in ("w13", "s13", "w2", "s2", "x", "ids", "w")),
+                         swiglu_limit=wl.swiglu_limit)
+    ga = torch.from_numpy(g[:wl.T].view(np.int16)).view(torch.bfloat16).double().numpy()
+    ra = torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert np.max(np.abs(ga - ra)) <= 1e-2 * np.max(np.abs(ra))
+    assert np.linalg.norm(ga - ra) / np.linalg.norm(ra) <= 5e-3
+    assert not np.any(g[wl.T:]), "padded slots must give exact zeros"
+    # a slice that runs the same GEMM path as the whole batch gives the same bits
+    if (per * wl.k <= 8 * wl.E) == (wl.T * wl.k <= 8 * wl.E):
+        assert np.array_equal(g[:wl.T], f)
+
+
+@pytest.mark.parametrize("wl", EP_CASES, ids=[w.name for w in EP_CASES])
+def test_ep_expert_groups_sum_to_the_full_layer(wl):
+    """Expert parallelism without moving tokens ("all_reduce" in the pages' EP
+    table): each rank holds E / G experts (expert_begin), runs them over the
+    whole batch with global ids, and the partial outputs are summed.  Ids of
+    other ranks' experts are skipped there and counted as out of range."""
+    G = 4 if wl.E % 4 == 0 else 2
+    inp = W.inputs(wl, DEV)
+    n = {k_: host(v) for k_, v in inp.items()}
+    Eg = wl.E // G
+    parts = []
+    for r in range(G):
+        sl = slice(r * Eg, (r + 1) * Eg)
+        w = moe.prepare_weights(inp["w13"][sl].contiguous(), inp["s13"][sl].contiguous(), inp["w2"][sl].contiguous(),
+                                inp["s2"][sl].contiguous(), fmt=wl.fmt)
+        inv = torch.zeros(1, dtype=torch.int32, device=DEV)
+        out = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w, swiglu_limit=wl.swiglu_limit, expert_begin=r * Eg,
+                                  invalid_count=inv)
+        torch.cuda.synchronize()
+        ids = n["ids"]
+        assert int(host(inv)[0]) == int(((ids >= 0) & ((ids < r * Eg) | (ids >= (r + 1) * Eg))).sum())
+        # this rank's partial against the oracle run on the same share
+        ref_r = oracle.forward(wl.fmt, n["w13"][sl], n["s13"][sl], n["w2"][sl], n["s2"][sl], n["x"], ids, n["w"],
+                               swiglu_limit=wl.swiglu_limit, expert_begin=r * Eg)
+        p = torch.from_numpy(host(out).view(np.int16)).view(torch.bfloat16).double().numpy()
+        rr = torch.from_numpy(ref_r.view(np.int16)).view(torch.bfloat16).double().numpy()
+        assert np.max(np.abs(p - rr)) <= 1e-2 * np.max(np.abs(rr))
+        parts.append(p)
+    full = oracle.forward(wl.fmt, n["w13"], n["s13"], n["w2"], n["s2"], n["x"], n["ids"], n["w"],
+                          swiglu_limit=wl.swiglu_limit)
+    fr = torch.from_numpy(full.view(np.int16)).view(torch.bfloat16).double().numpy()
+    total = np.sum(parts, axis=0)
+    assert np.max(np.abs(total - fr)) <= 1e-2 * np.max(np.abs(fr))
+    assert np.linalg.norm(total - fr) / np.linalg.norm(fr) <= 5e-3
