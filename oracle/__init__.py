@@ -20,6 +20,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 FMT_FP8_B128 = 0
 FMT_MX = 1
+FMT_BF16 = 2
 
 _lib = None
 
@@ -163,12 +164,14 @@ def quant_rows_f32(x, fmt: int):
 
 
 def grouped_gemm(fmt, a_codes, a_scales, offsets, b_codes, b_scales, N, K, row_index=None, row_div=1):
-    """C[r, n] over expert-sorted rows, fp64.  Rows = offsets[E]."""
-    a_codes = _c(a_codes, np.uint8)
-    a_scales = _c(a_scales, np.float32 if fmt == FMT_FP8_B128 else np.uint8)
+    """C[r, n] over expert-sorted rows, fp64.  Rows = offsets[E].  BF16: A and B
+    are bf16 bit patterns (uint16) and the scales are None."""
+    bf = fmt == FMT_BF16
+    a_codes = _c(a_codes, np.uint16 if bf else np.uint8)
+    a_scales = None if bf else _c(a_scales, np.float32 if fmt == FMT_FP8_B128 else np.uint8)
     offsets = _c(offsets, np.int32)
-    b_codes = _c(b_codes, np.uint8)
-    b_scales = _c(b_scales, np.float32 if fmt == FMT_FP8_B128 else np.uint8)
+    b_codes = _c(b_codes, np.uint16 if bf else np.uint8)
+    b_scales = None if bf else _c(b_scales, np.float32 if fmt == FMT_FP8_B128 else np.uint8)
     E = offsets.size - 1
     ri = None if row_index is None else _c(row_index, np.int32)
     out = np.zeros((int(offsets[E]), N), np.float64)
@@ -181,15 +184,17 @@ def forward(fmt, w13, w13_scale, w2, w2_scale, x_bits, ids, wts, swiglu_limit=No
             tokens=None, debug=False):
     """The experts forward on the host.
 
-    Weights in the nt layout (see ``moe_oracle.cpp``).  Returns the bf16 bit
+    Weights in the nt layout (see ``moe_oracle.cpp``); BF16: bf16 bit patterns
+    (uint16) [E, 2I, H] and [E, H, I], scales None.  Returns the bf16 bit
     patterns uint16 [T, H] (rows of tokens not listed in ``tokens`` stay 0) and,
     when ``debug`` is set, a dict of per-slot intermediates.
     """
-    w13 = _c(w13, np.uint8)
-    w2 = _c(w2, np.uint8)
+    bf = fmt == FMT_BF16
+    w13 = _c(w13, np.uint16 if bf else np.uint8)
+    w2 = _c(w2, np.uint16 if bf else np.uint8)
     sdt = np.float32 if fmt == FMT_FP8_B128 else np.uint8
-    w13_scale = _c(w13_scale, sdt)
-    w2_scale = _c(w2_scale, sdt)
+    w13_scale = None if bf else _c(w13_scale, sdt)
+    w2_scale = None if bf else _c(w2_scale, sdt)
     x = _c(x_bits, np.uint16)
     ids = _c(ids, np.int32)
     wts = _c(wts, np.float32)

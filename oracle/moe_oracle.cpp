@@ -56,7 +56,7 @@
 
 namespace {
 
-enum { FMT_FP8_B128 = 0, FMT_MX = 1 };
+enum { FMT_FP8_B128 = 0, FMT_MX = 1, FMT_BF16 = 2 };
 enum { OK = 0, ERR_NULL = 1, ERR_SHAPE = 2, ERR_FMT = 3 };
 
 // ---------------------------------------------------------------- codecs --
@@ -202,6 +202,7 @@ void quant_row(const float* x, int64_t n, int fmt, uint8_t* codes, float* sc_f32
 // code array: code value times its block scale.
 inline double act_value(int fmt, const uint8_t* codes, const void* scales, int64_t row, int64_t K,
                         int64_t i) {
+  if (fmt == FMT_BF16) return (double)bf16_to_f32(((const uint16_t*)codes)[row * K + i]);
   const double q = e4m3_table()[codes[row * K + i]];
   if (fmt == FMT_FP8_B128) return q * (double)((const float*)scales)[row * (K / 128) + i / 128];
   return q * e8m0_table()[((const uint8_t*)scales)[row * (K / 32) + i / 32]];
@@ -210,6 +211,11 @@ inline double act_value(int fmt, const uint8_t* codes, const void* scales, int64
 // Decoded weight row n of expert e (N rows of K columns), written to out[K].
 void weight_row(int fmt, const uint8_t* w, const void* ws, int64_t e, int64_t N, int64_t K, int64_t n,
                 double* out) {
+  if (fmt == FMT_BF16) {  // plain bf16 values, no scales
+    const uint16_t* row = (const uint16_t*)w + (e * N + n) * K;
+    for (int64_t i = 0; i < K; ++i) out[i] = (double)bf16_to_f32(row[i]);
+    return;
+  }
   if (fmt == FMT_FP8_B128) {
     const double* dec = e4m3_table();
     const uint8_t* code = w + (e * N + n) * K;
@@ -369,12 +375,14 @@ int oracle_quant_rows_f32(const float* x, int32_t rows, int32_t H, int32_t fmt, 
 // [offsets[e], offsets[e+1]), C[r][n] = sum_i A[a_row(r)][i] * B[e][n][i] with
 // both operands decoded to values (code times scale) and summed in fp64.
 // a_row(r) = row_index[r] / row_div when row_index is given, else r.
+// BF16 format: A and B hold bf16 bit patterns (uint16) and no scales.
 int oracle_grouped_gemm(int32_t fmt, const uint8_t* a_codes, const void* a_scales, const int32_t* row_index,
                         int32_t row_div, const int32_t* offsets, int32_t E, const uint8_t* b_codes,
                         const void* b_scales, int32_t N, int32_t K, double* out) {
-  if (fmt != FMT_FP8_B128 && fmt != FMT_MX) return ERR_FMT;
+  if (fmt != FMT_FP8_B128 && fmt != FMT_MX && fmt != FMT_BF16) return ERR_FMT;
   if (E < 1 || N <= 0 || K <= 0 || K % 128 || N % (fmt == FMT_FP8_B128 ? 128 : 1)) return ERR_SHAPE;
-  if (!a_codes || !a_scales || !offsets || !b_codes || !b_scales || !out) return ERR_NULL;
+  if (!a_codes || !offsets || !b_codes || !out) return ERR_NULL;
+  if (fmt != FMT_BF16 && (!a_scales || !b_scales)) return ERR_NULL;
   const int64_t rows = offsets[E];
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t r = 0; r < rows; ++r) {
@@ -397,6 +405,11 @@ int oracle_grouped_gemm(int32_t fmt, const uint8_t* a_codes, const void* a_scale
 // [E, 2I/128, H/128]; w2 u8 [E, H, I] with fp32 scales [E, H/128, I/128].
 // MX format: w13 packed [E, 2I, H/2] with u8 scales [E, 2I, H/32]; w2 packed
 // [E, H, I/2] with u8 scales [E, H, I/32].
+// BF16 format (the unquantized grouped_mm experts the pages fall back to, "DeepGEMM
+// experts selected on a model spanning multiple CUDA devices", the record's
+// source): w13 bf16 [E, 2I, H], w2 bf16 [E, H, I], no scales; activations are
+// used as they are, and h is rounded once to bf16 (through fp32, the precision
+// of the GPU's accumulators) to be the down projection's operand.
 //
 // Only the tokens listed in `tokens` (all tokens when NULL) are computed; their
 // rows of `out` are written.  Optional per-slot debug outputs (indexed by the
@@ -409,11 +422,13 @@ int oracle_forward(int32_t fmt, int32_t E, int32_t H, int32_t I, const uint8_t* 
                    const float* wts, int32_t T, int32_t k, int32_t expert_begin, int32_t has_limit, float limit,
                    const int32_t* tokens, int32_t n_tokens, uint16_t* out, float* dbg_gu, uint8_t* dbg_h_codes,
                    void* dbg_h_scales, float* dbg_y) {
-  if (fmt != FMT_FP8_B128 && fmt != FMT_MX) return ERR_FMT;
+  if (fmt != FMT_FP8_B128 && fmt != FMT_MX && fmt != FMT_BF16) return ERR_FMT;
   if (E < 1 || T < 0 || k < 1 || H <= 0 || I <= 0 || H % 128 || I % 128) return ERR_SHAPE;
   if (has_limit && !(std::isfinite(limit) && limit > 0.0f)) return ERR_SHAPE;
   if (T == 0) return OK;
-  if (!w13 || !w13_scale || !w2 || !w2_scale || !x || !ids || !wts || !out) return ERR_NULL;
+  if (!w13 || !w2 || !x || !ids || !wts || !out) return ERR_NULL;
+  if (fmt != FMT_BF16 && (!w13_scale || !w2_scale)) return ERR_NULL;
+  const bool bf = fmt == FMT_BF16;
   const int64_t n_list = tokens ? n_tokens : T;
   const int64_t Bh = fmt == FMT_FP8_B128 ? 128 : 32;
 
@@ -424,13 +439,17 @@ int oracle_forward(int32_t fmt, int32_t E, int32_t H, int32_t I, const uint8_t* 
     // Activation quantization of the token's row (dynamic, per block).
     std::vector<float> xr(H);
     for (int64_t i = 0; i < H; ++i) xr[i] = bf16_to_f32(x[t * H + i]);
-    std::vector<uint8_t> xq(H);
-    std::vector<float> xs_f(H / 128);
-    std::vector<uint8_t> xs_u(H / 32);
-    quant_row(xr.data(), H, fmt, xq.data(), xs_f.data(), xs_u.data());
-    const void* xs = fmt == FMT_FP8_B128 ? (const void*)xs_f.data() : (const void*)xs_u.data();
     std::vector<double> a(H);
-    for (int64_t i = 0; i < H; ++i) a[i] = act_value(fmt, xq.data(), xs, 0, H, i);
+    if (bf) {
+      for (int64_t i = 0; i < H; ++i) a[i] = (double)xr[i];
+    } else {
+      std::vector<uint8_t> xq(H);
+      std::vector<float> xs_f(H / 128);
+      std::vector<uint8_t> xs_u(H / 32);
+      quant_row(xr.data(), H, fmt, xq.data(), xs_f.data(), xs_u.data());
+      const void* xs = fmt == FMT_FP8_B128 ? (const void*)xs_f.data() : (const void*)xs_u.data();
+      for (int64_t i = 0; i < H; ++i) a[i] = act_value(fmt, xq.data(), xs, 0, H, i);
+    }
 
     std::vector<double> acc(H, 0.0);
     std::vector<double> gu(2 * (int64_t)I);
@@ -460,6 +479,10 @@ int oracle_forward(int32_t fmt, int32_t E, int32_t H, int32_t I, const uint8_t* 
         }
         h[n] = (float)(g / (1.0 + std::exp(-g)) * u);
       }
+      if (bf) {
+        // BF16: h rounded to bf16 is the down projection's operand.
+        for (int64_t i = 0; i < I; ++i) hd[i] = (double)bf16_to_f32(f32_to_bf16(h[i]));
+      } else {
       // Re-quantize h with the activation rule, blocks along I.
       quant_row(h.data(), I, fmt, hq.data(), hs_f.data(), hs_u.data());
       const void* hs = fmt == FMT_FP8_B128 ? (const void*)hs_f.data() : (const void*)hs_u.data();
@@ -471,6 +494,7 @@ int oracle_forward(int32_t fmt, int32_t E, int32_t H, int32_t I, const uint8_t* 
           std::memcpy((uint8_t*)dbg_h_scales + s * (I / Bh), hs_u.data(), I / Bh);
       }
       for (int64_t i = 0; i < I; ++i) hd[i] = act_value(fmt, hq.data(), hs, 0, I, i);
+      }
       // L2: down projection, then the routing weight, summed over ascending j.
       const double wj = (double)wts[s];
       for (int64_t c = 0; c < H; ++c) {

@@ -17,7 +17,7 @@ import oracle
 import workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-FP8, MX = oracle.FMT_FP8_B128, oracle.FMT_MX
+FP8, MX, BF16 = oracle.FMT_FP8_B128, oracle.FMT_MX, oracle.FMT_BF16
 
 
 def _golden(name):
@@ -642,3 +642,94 @@ def test_forward_rejects_bad_arguments():
         _run(FP8, d, limit=-1.0)
     with pytest.raises(oracle.OracleError):
         oracle.quant_rows_f32(np.zeros((2, 100), np.float32), FP8)
+
+
+# ------------------------------------------------------- bf16 experts --
+
+def _bf16_t(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).double()
+
+
+def _bf16_inputs(T=24, H=256, I=256, E=4, k=3, seed=0, skip=0.15):
+    x = W.hidden_states(T, H, seed)
+    ids, w = W.routing(T, E, k, "uniform", seed, skip=skip)
+    w13 = W.bf16_weights(E, 2 * I, H, seed, "w13")
+    w2 = W.bf16_weights(E, H, I, seed, "w2")
+    return {n: W.to_numpy(t) for n, t in dict(x=x, ids=ids, w=w, w13=w13, w2=w2).items()}
+
+
+def test_bf16_grouped_gemm_matches_torch_matmul():
+    rng = np.random.default_rng(8)
+    E, N, K, T, k = 3, 256, 384, 20, 2
+    b = W.to_numpy(W.bf16_weights(E, N, K, seed=9, tag="g"))
+    a = W.to_numpy(W.hidden_states(T, K, 4))
+    ids = _rand_ids(rng, T, k, E, p_skip=0.2, p_bad=0.0)
+    ss, off, _, _ = oracle.route_sort(ids, E)
+    got = oracle.grouped_gemm(BF16, a, None, off, b, None, N, K, row_index=ss, row_div=k)
+    A, B = _bf16_t(a), _bf16_t(b)
+    for e in range(E):
+        rows = torch.from_numpy((ss[off[e]:off[e + 1]] // k).astype(np.int64))
+        np.testing.assert_allclose(got[off[e]:off[e + 1]], (A[rows] @ B[e].T).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def _bf16_brute_force(d, limit=None):
+    """Every expert for every token with torch float64 matmuls (h rounded to
+    bf16 through fp32), then the routed ones picked and weighted."""
+    X, W13, W2 = _bf16_t(d["x"]), _bf16_t(d["w13"]), _bf16_t(d["w2"])
+    E, I = W13.shape[0], W13.shape[1] // 2
+    T, k = d["ids"].shape
+    GU = torch.einsum("th,enh->etn", X, W13)
+    g, u = GU[..., :I], GU[..., I:]
+    if limit is not None:
+        g = torch.clamp(g, max=limit)
+        u = torch.clamp(u, -limit, limit)
+    h = (torch.nn.functional.silu(g) * u).float().to(torch.bfloat16).double()
+    Y = torch.einsum("eti,ehi->eth", h, W2).numpy()
+    out = np.zeros((T, X.shape[1]), np.float64)
+    for t in range(T):
+        for j in range(k):
+            e = d["ids"][t, j]
+            if 0 <= e < E:
+                out[t] += float(d["w"][t, j]) * Y[e, t]
+    return torch.from_numpy(out).float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("limit", [None, 0.05])
+def test_bf16_forward_matches_dense_brute_force(limit):
+    d = _bf16_inputs()
+    out = oracle.forward(BF16, d["w13"], None, d["w2"], None, d["x"], d["ids"], d["w"], swiglu_limit=limit)
+    ref = _bf16_brute_force(d, limit)
+    o, r = _bits_to_f64(out), _bits_to_f64(ref)
+    assert np.all(np.abs(o - r) <= np.abs(r) * 2 ** -7 + 1e-30)
+    assert np.mean(out == ref) > 0.99
+    assert np.any(o != 0)
+
+
+def test_bf16_forward_textbook_swiglu_mlp():
+    """k = 1, E = 1, weight 1: y = W2 bf16(silu(W1 x) * (W3 x)) with
+    torch.nn.functional.silu and float64 matmuls."""
+    d = _bf16_inputs(T=16, E=1, k=1, skip=0.0)
+    d["w"] = np.ones_like(d["w"])
+    out = oracle.forward(BF16, d["w13"], None, d["w2"], None, d["x"], d["ids"], d["w"])
+    X, W13, W2 = _bf16_t(d["x"]), _bf16_t(d["w13"])[0], _bf16_t(d["w2"])[0]
+    I = W13.shape[0] // 2
+    h = (torch.nn.functional.silu(X @ W13[:I].T) * (X @ W13[I:].T)).float().to(torch.bfloat16).double()
+    ref = (h @ W2.T).float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.mean(out == ref) > 0.99
+    assert np.allclose(_bits_to_f64(out), _bits_to_f64(ref), rtol=2 ** -7, atol=0)
+
+
+def test_bf16_forward_skips_and_weights():
+    d = _bf16_inputs(seed=3)
+    base = oracle.forward(BF16, d["w13"], None, d["w2"], None, d["x"], d["ids"], d["w"])
+    # every slot skipped, NaN weights: exact zeros
+    ids = np.full_like(d["ids"], -1)
+    z = oracle.forward(BF16, d["w13"], None, d["w2"], None, d["x"], ids, np.full_like(d["w"], np.nan))
+    assert not np.any(z)
+    # all weights doubled: outputs doubled exactly
+    two = oracle.forward(BF16, d["w13"], None, d["w2"], None, d["x"], d["ids"], 2 * d["w"])
+    assert np.array_equal(_bits_to_f64(two), 2 * _bits_to_f64(base))
+    # the gate is the first half of gate_up: swapping the halves changes the result
+    sw = np.concatenate([d["w13"][:, 256:], d["w13"][:, :256]], axis=1)
+    other = oracle.forward(BF16, sw, None, d["w2"], None, d["x"], d["ids"], d["w"])
+    assert not np.array_equal(other, base)

@@ -22,6 +22,7 @@ import torch
 
 FMT_FP8_B128 = 0
 FMT_MX = 1
+FMT_BF16 = 2
 
 
 @dataclasses.dataclass(frozen=True)
@@ -32,7 +33,7 @@ class Workload:
     I: int          # expert intermediate size
     E: int          # experts on this GPU
     k: int          # slots per token (top-k)
-    fmt: int        # FMT_FP8_B128 or FMT_MX
+    fmt: int        # FMT_FP8_B128, FMT_MX or FMT_BF16
     routing: str    # "uniform" (softmax top-k of N(0,1) logits) or "zipf"
     zipf_s: float = 0.0
     skip: float = 0.0               # probability that a slot is set to -1
@@ -171,8 +172,19 @@ def fp4_weights(E: int, N: int, K: int, seed: int, tag: str, device="cpu", std: 
     return packed, scales
 
 
+def bf16_weights(E: int, N: int, K: int, seed: int, tag: str, device="cpu", std: float = 0.02):
+    """Unquantized bf16 weights [E, N, K]: N(0, std) rounded to bf16."""
+    g = _gen(device, seed, tag)
+    return (torch.randn((E, N, K), generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
+
+
 def expert_weights(wl: Workload, device="cpu"):
-    """(w13, w13_scale, w2, w2_scale) in the nt layout: gate_up [E, 2I, H], down [E, H, I]."""
+    """(w13, w13_scale, w2, w2_scale) in the nt layout: gate_up [E, 2I, H], down [E, H, I].
+    The bf16 format has no scales (empty tensors stand in for them)."""
+    if wl.fmt == FMT_BF16:
+        none = torch.empty(0, dtype=torch.float32, device=device)
+        return (bf16_weights(wl.E, 2 * wl.I, wl.H, wl.seed, "w13", device), none,
+                bf16_weights(wl.E, wl.H, wl.I, wl.seed, "w2", device), none)
     if wl.fmt == FMT_FP8_B128:
         w13, s13 = fp8_weights(wl.E, 2 * wl.I, wl.H, wl.seed, "w13", device)
         w2, s2 = fp8_weights(wl.E, wl.H, wl.I, wl.seed, "w2", device)
