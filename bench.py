@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 # MI355X published peaks (dense)
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_MXFP4_TFLOPS = 10100.0
+PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
 METRIC = "MoE-layer active-expert TFLOP/s + tokens/s at 1 GPU; % of FP8/MXFP4 MFMA peak"
@@ -42,12 +43,15 @@ GATE_UP_KERNELS = {
     "fp8_tiled": ("gemm_fp8_b128_kernel", [_CSRC + "gemm_fp8.hip"] + _COMMON),
     "fp8_skinny": ("gemm_fp8_skinny_kernel", [_CSRC + "gemm_fp8_skinny.hip"] + _COMMON),
     "mx": ("gemm_mx_kernel", [_CSRC + "gemm_mx.hip"] + _COMMON),
+    "bf16": ("gemm_bf16_kernel", [_CSRC + "gemm_bf16.hip"] + _COMMON),
 }
 
 
 def gate_up_kernel(wl):
     """Key into GATE_UP_KERNELS; its sources define the dominant kernel, and its
     HBM byte counters (profiles/) are reported only while they are unchanged."""
+    if wl.fmt == 2:
+        return "bf16"
     if wl.fmt != 0:
         return "mx"
     return "fp8_skinny" if wl.T * wl.k <= SKINNY_ROWS_PER_EXPERT * wl.E else "fp8_tiled"
@@ -116,7 +120,10 @@ def main():
     touched = np.unique(ids_h[valid])
     flop_l1 = 4.0 * H * I * S_v
     flop_total = 6.0 * H * I * S_v
-    if wl.fmt == W.FMT_FP8_B128:
+    if wl.fmt == W.FMT_BF16:
+        w13_bytes = 2 * I * H * 2
+        w2_bytes = H * I * 2
+    elif wl.fmt == W.FMT_FP8_B128:
         w13_bytes = 2 * I * H + 4 * (2 * I // 128) * (H // 128)
         w2_bytes = H * I + 4 * (H // 128) * (I // 128)
     else:
@@ -204,12 +211,13 @@ def main():
     torch.cuda.synchronize()
     l1_ms = ev0.elapsed_time(ev1) / args.steps
     l1_tflops = flop_l1 / (l1_ms * 1e-3) / 1e12
-    l1_bytes = int(len(touched) * w13_bytes + T * H + S_v * I)  # weights + A codes in + h codes out
+    act_b = 2 if wl.fmt == W.FMT_BF16 else 1  # bytes per activation / h element
+    l1_bytes = int(len(touched) * w13_bytes + (T * H + S_v * I) * act_b)  # weights + A in + h out
     l1_gbs = l1_bytes / (l1_ms * 1e-3) / 1e9
     log(f"[bench] gate_up GEMM {l1_ms:.3f} ms = {l1_tflops:.1f} TFLOP/s, {l1_gbs:.0f} GB/s algorithmic")
     # e4m3 x e2m1 MFMAs issue at the FP8 rate on gfx950 (measured), so the MX
     # contraction is priced against the FP8 peak; its MXFP4 fraction is given too
-    peak_flops = PEAK_FP8_TFLOPS
+    peak_flops = PEAK_BF16_TFLOPS if wl.fmt == W.FMT_BF16 else PEAK_FP8_TFLOPS
     # binding roofline from the kernel's arithmetic intensity (flop per HBM byte)
     mfma_bound = flop_l1 / l1_bytes >= peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
     kname, _ = GATE_UP_KERNELS[gate_up_kernel(wl)]
@@ -232,17 +240,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3" if wl.fmt == W.FMT_FP8_B128 else "fp8e4m3 x fp4e2m1",
+        "dtype": {W.FMT_FP8_B128: "fp8e4m3", W.FMT_MX: "fp8e4m3 x fp4e2m1", W.FMT_BF16: "bf16"}[wl.fmt],
         "data": "synthetic",
         "config": {
             "workload": wl.name, "tokens": T, "hidden": H, "intermediate": I, "experts": E, "top_k": k,
-            "format": "fp8 e4m3, fp32 scales 1x128 act / 128x128 weight" if wl.fmt == W.FMT_FP8_B128
-            else "e4m3 act x e2m1 weight, UE8M0 per 1x32",
+            "format": {W.FMT_FP8_B128: "fp8 e4m3, fp32 scales 1x128 act / 128x128 weight",
+                       W.FMT_MX: "e4m3 act x e2m1 weight, UE8M0 per 1x32",
+                       W.FMT_BF16: "bf16 act x bf16 weight, no quantization"}[wl.fmt],
             "routing": wl.routing, "skipped_slot_prob": wl.skip, "swiglu_limit": wl.swiglu_limit,
             "valid_slots": S_v, "active_tflop": round(flop_total / 1e12, 4),
             "tokens_per_s": round(T / (ms * 1e-3), 1),
             "pct_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2),
             "pct_mxfp4_peak": round(100.0 * tflops / PEAK_MXFP4_TFLOPS, 2),
+            "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
             "hbm_gbs_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
         },
         "roofline": dict(roof, **{
@@ -295,6 +305,8 @@ def _gemm_inputs(wl, inp, dev):
 
     S, I, H = wl.T * wl.k, wl.I, wl.H
     ss, off, _, _ = moe.route_sort(inp["ids"], wl.E, with_slot_pos=False)
+    if wl.fmt == W.FMT_BF16:  # the bf16 GEMMs read bf16 rows as they are
+        return ss, off, inp["x"], None, torch.zeros((S, I), dtype=torch.bfloat16, device=dev), None
     a_codes, a_scales = moe.quant_act(inp["x"], wl.fmt)
     sdt = torch.float32 if wl.fmt == W.FMT_FP8_B128 else torch.uint8
     h_codes = torch.zeros((I // 128, S, 128), dtype=torch.uint8, device=dev)

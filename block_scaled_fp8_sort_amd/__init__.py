@@ -19,7 +19,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "FMT_FP8_B128", "FMT_MXFP8A_MXFP4W", "EPI_STORE_F32", "EPI_SWIGLU_QUANT", "EPI_WEIGHTED_SCATTER",
+    "FMT_FP8_B128", "FMT_MXFP8A_MXFP4W", "FMT_BF16", "EPI_STORE_F32", "EPI_SWIGLU_QUANT", "EPI_WEIGHTED_SCATTER",
     "MoeError", "library_path", "load_library", "route_sort", "route_topk", "quant_act", "prepare_weights",
     "grouped_gemm", "experts_forward", "experts_forward_from_logits", "forward_workspace_bytes", "Weights",
     "TILE_COUNTERS_INTS",
@@ -27,6 +27,7 @@ __all__ = [
 
 FMT_FP8_B128 = 0
 FMT_MXFP8A_MXFP4W = 1
+FMT_BF16 = 2
 LAYOUT_NT = 0
 LAYOUT_NN = 1
 EPI_STORE_F32 = 0
@@ -264,19 +265,25 @@ def prepare_weights(gate_up: torch.Tensor, gate_up_scale: torch.Tensor, down: to
 
     FP8_B128: gate_up uint8 [E, 2I, H] (or [E, H, 2I] when transposed), fp32 scales
     per 128x128 block; down uint8 [E, H, I].  MX: int8/uint8 packed e2m1
-    [E, 2I, H/2] and [E, H, I/2] with uint8 UE8M0 scales per 1x32.
+    [E, 2I, H/2] and [E, H, I/2] with uint8 UE8M0 scales per 1x32.  BF16:
+    bfloat16 [E, 2I, H] and [E, H, I], no scales (pass None).
     """
     lib = load_library()
     dev = gate_up.device
     if fmt == FMT_MXFP8A_MXFP4W and gate_up.dtype not in (torch.int8, torch.uint8):
         raise NotImplementedError(f"MXFP4 experts need FP4-packed int8 weights, got {gate_up.dtype}")
     for name, t in (("gate_up", gate_up), ("down", down)):
-        if t.dtype not in (torch.uint8, torch.int8, torch.float8_e4m3fn):
+        if fmt == FMT_BF16:
+            if t.dtype != torch.bfloat16:
+                raise ValueError(f"{name} must be bfloat16 for the bf16 experts, got {t.dtype}")
+        elif t.dtype not in (torch.uint8, torch.int8, torch.float8_e4m3fn):
             raise ValueError(f"{name} must hold 8-bit codes, got {t.dtype}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     E = gate_up.shape[0]
-    if fmt == FMT_FP8_B128:
+    if fmt == FMT_BF16:
+        H, I2 = gate_up.shape[2], gate_up.shape[1]
+    elif fmt == FMT_FP8_B128:
         H, I2 = (gate_up.shape[1], gate_up.shape[2]) if transposed else (gate_up.shape[2], gate_up.shape[1])
     else:
         H, I2 = gate_up.shape[2] * 2, gate_up.shape[1]

@@ -1,0 +1,216 @@
+// Grouped GEMM of the unquantized bf16 experts, for gfx950.
+//
+// What it computes: the grouped matmuls of the pages' bf16 grouped_mm experts,
+// the path the FP8 dispatch falls back to ("DeepGEMM experts selected on a
+// model spanning multiple CUDA devices", the record's source: use
+// experts_implementation='grouped_mm'), with the same sorted rows, row gather
+// and epilogues as the quantized kernels: C[r, n] = sum_k A[a_row(r), k] *
+// B[e, n, k] over bf16 operands with fp32 accumulation; then fp32 stores, the
+// SwiGLU (h rounded once to bf16, the down projection's operand) or the
+// routing-weighted bf16 scatter into the slot buffer.
+//
+// Layout: B is the expert weight as stored, [E, N, K] bf16 row-major (nt); A
+// rows are bf16 [rows, K] row-major, gathered through a_row_index / divisor.
+//
+// Tile: 128 weight rows x 128 sorted rows, 4 waves.  Wave w owns 32 weight rows
+// (two 16-row groups) and all 128 rows of A (eight 16-row groups), so each lane
+// ends with 4 consecutive weight rows of one A row per (group, A group) pair,
+// from v_mfma_f32_16x16x32_bf16 with the weights as operand A.  In a paired
+// (gate_up) tile, group 0 of wave w is gate rows h0 + 16 w .. + 16 and group 1
+// the matching up rows I + h0 + 16 w .., so g and u of an output meet in one
+// lane.  Per K stage of 64 elements the 128 gathered A rows (16 KB) are loaded
+// once by the workgroup into registers and stored to a double-buffered LDS
+// stage (16-byte chunks XOR-swizzled by row & 7, so the 16 rows a fragment read
+// touches spread over the banks); weights go straight from global memory to
+// registers, one stage ahead, each byte read by exactly one wave.
+#include "device_common.h"
+#include "gemm_common.h"
+#include "internal.h"
+
+namespace moe {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in registers
+
+constexpr int kWavesB = 4;
+constexpr int kThreadsB = kWavesB * kWave;
+constexpr int BMB = 128;            // sorted rows per tile
+constexpr int BNB = 128;            // weight rows per tile
+constexpr int kStageK = 64;         // K elements per stage (128 bytes of a row)
+constexpr int kStageBytes = BMB * kStageK * 2;
+constexpr int kMaxEB = 512;
+
+struct SmemB {
+  u32x4 stage[2][BMB * 8];  // [buffer][row * 8 + swizzled 16-byte chunk]
+  int off[kMaxEB + 1];
+  int tp[kMaxEB + 1];
+  int scan[kThreadsB];
+};
+static_assert(sizeof(u32x4) * BMB * 8 == kStageBytes, "stage size");
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+template <int EPI, bool PAIRED>
+__global__ __launch_bounds__(kThreadsB) void gemm_bf16_kernel(GemmParams p) {
+  __shared__ SmemB sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, l16 = lane & 15;
+  const int E = p.E, N = p.N, K = p.K;
+  const int NT = PAIRED ? (N / 2) / (BNB / 2) : (N + BNB - 1) / BNB;
+  const int KS = K / kStageK;
+  const size_t row_bytes = (size_t)K * 2;
+
+  const int total = build_tile_table<kThreadsB>(p.offsets, E, BMB, NT, sm.off, sm.tp, sm.scan);
+  const uint8_t* A = p.a_codes;
+  const uint8_t* B = p.b_codes;
+
+  // cooperative A load: thread tid covers row tid / 2, chunks 4 (tid % 2) .. + 4
+  const int ld_row = tid >> 1, ld_c0 = (tid & 1) * 4;
+
+  for (int t = xcd_virtual_block(); t < total; t += gridDim.x) {
+    const TileCoord tc = locate_tile(t, E, BMB, NT, sm.off, sm.tp);
+    // this thread's gathered A row (rows past the expert's end repeat its last
+    // row; their results are never stored)
+    const int r_ld = min(tc.m0 + ld_row, tc.m_end - 1);
+    const int arow = p.a_row_index ? p.a_row_index[r_ld] / p.a_row_div : r_ld;
+    const uint8_t* a_src = A + (size_t)arow * row_bytes + ld_c0 * 16;
+    // this lane's weight rows, group 0 and 1
+    int wr0, wr1;
+    if (PAIRED) {
+      const int I = N / 2;
+      wr0 = tc.n_tile * (BNB / 2) + 16 * wave + l16;
+      wr1 = I + wr0;
+    } else {
+      wr0 = min(tc.n_tile * BNB + 32 * wave + l16, N - 1);
+      wr1 = min(tc.n_tile * BNB + 32 * wave + 16 + l16, N - 1);
+    }
+    const uint8_t* w0 = B + ((size_t)tc.e * N + wr0) * row_bytes + g * 16;
+    const uint8_t* w1 = B + ((size_t)tc.e * N + wr1) * row_bytes + g * 16;
+
+    v4f acc[2][8];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[q][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 a_reg[4], w_reg[4], a_nxt[4], w_nxt[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) a_reg[c] = *(const u32x4*)(a_src + c * 16);
+    // weights: [substep ks][group] at bytes ks * 64 + g * 16 of the stage
+    w_reg[0] = *(const u32x4*)(w0);
+    w_reg[1] = *(const u32x4*)(w1);
+    w_reg[2] = *(const u32x4*)(w0 + 64);
+    w_reg[3] = *(const u32x4*)(w1 + 64);
+    __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sm.stage[0][ld_row * 8 + ((ld_c0 + c) ^ (ld_row & 7))] = a_reg[c];
+    __syncthreads();
+
+    for (int s = 0; s < KS; ++s) {
+      const int cur = s & 1;
+      const bool more = s + 1 < KS;
+      if (more) {
+        const size_t o = (size_t)(s + 1) * 128;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) a_nxt[c] = *(const u32x4*)(a_src + o + c * 16);
+        w_nxt[0] = *(const u32x4*)(w0 + o);
+        w_nxt[1] = *(const u32x4*)(w1 + o);
+        w_nxt[2] = *(const u32x4*)(w0 + o + 64);
+        w_nxt[3] = *(const u32x4*)(w1 + o + 64);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 wa = as_bf16x8(w_reg[2 * ks]);
+        const bf16x8 wb = as_bf16x8(w_reg[2 * ks + 1]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int row = 16 * j + l16;
+          const int chunk = (ks * 4 + g) ^ (row & 7);
+          const bf16x8 b = as_bf16x8(sm.stage[cur][row * 8 + chunk]);
+          acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, b, acc[0][j], 0, 0, 0);
+          acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, b, acc[1][j], 0, 0, 0);
+        }
+      }
+      if (more) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sm.stage[cur ^ 1][ld_row * 8 + ((ld_c0 + c) ^ (ld_row & 7))] = a_nxt[c];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) w_reg[c] = w_nxt[c];
+        __syncthreads();
+      }
+    }
+
+    // epilogue: lane holds weight rows 4 g .. 4 g + 3 of each group, A row 16 j + l16
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = tc.m0 + 16 * j + l16;
+      if (r >= tc.m_end) continue;
+      if constexpr (EPI == kEpiStoreF32) {
+        if constexpr (PAIRED) {
+          const int I = N / 2;
+          const int h = tc.n_tile * (BNB / 2) + 16 * wave + 4 * g;
+          *(v4f*)(p.c_f32 + (size_t)r * N + h) = acc[0][j];
+          *(v4f*)(p.c_f32 + (size_t)r * N + I + h) = acc[1][j];
+        } else {
+          const int n = tc.n_tile * BNB + 32 * wave + 4 * g;
+          if (n < N) *(v4f*)(p.c_f32 + (size_t)r * N + n) = acc[0][j];
+          if (n + 16 < N) *(v4f*)(p.c_f32 + (size_t)r * N + n + 16) = acc[1][j];
+        }
+      } else if constexpr (EPI == kEpiSwiGLUQuant) {
+        static_assert(PAIRED, "SwiGLU needs the paired gate/up tile");
+        const int I = N / 2;
+        const int h = tc.n_tile * (BNB / 2) + 16 * wave + 4 * g;
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[i] = p.has_limit ? swiglu<true>(acc[0][j][i], acc[1][j][i], p.limit)
+                             : swiglu<false>(acc[0][j][i], acc[1][j][i], p.limit);
+        uint2 o;
+        o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+        o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+        *(uint2*)((uint16_t*)p.h_codes + (size_t)r * I + h) = o;
+      } else {  // kEpiWeightedScatter
+        const int slot = p.slot_of_row[r];
+        const float wt = p.top_k_weights[slot];
+        const int n = tc.n_tile * BNB + 32 * wave + 4 * g;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          if (n + 16 * q < N) {
+            const v4f y = acc[q][j] * wt;
+            uint2 o;
+            o.x = f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16);
+            o.y = f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16);
+            *(uint2*)(p.slot_out + (size_t)slot * N + n + 16 * q) = o;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int EPI, bool PAIRED>
+hipError_t launch_bf16_epi(const GemmParams& p, int num_cus, hipStream_t stream) {
+  const int NT = PAIRED ? (p.N / 2) / (BNB / 2) : (p.N + BNB - 1) / BNB;
+  const long bound = ((long)(p.max_rows + BMB - 1) / BMB + p.E) * NT;
+  long grid = 2L * num_cus;
+  if (bound < grid) grid = bound;
+  if (grid >= 8) grid = grid / 8 * 8;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, PAIRED>), dim3((unsigned)grid), dim3(kThreadsB), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream) {
+  if (epi == kEpiSwiGLUQuant) return launch_bf16_epi<kEpiSwiGLUQuant, true>(p, num_cus, stream);
+  if (epi == kEpiWeightedScatter) return launch_bf16_epi<kEpiWeightedScatter, false>(p, num_cus, stream);
+  if (paired) return launch_bf16_epi<kEpiStoreF32, true>(p, num_cus, stream);
+  return launch_bf16_epi<kEpiStoreF32, false>(p, num_cus, stream);
+}
+
+}  // namespace moe

@@ -80,6 +80,9 @@ hipError_t launch_gemm_fp8_b128(const GemmParams& p, int epi, bool paired, int n
 // registers, 16 rows per tile.
 hipError_t launch_gemm_fp8_skinny(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream);
 hipError_t launch_gemm_mx(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream);
+// The unquantized bf16 grouped GEMM (A and B bf16, B stored [E, N, K]; the
+// SwiGLU epilogue writes h as bf16 [max_rows, N/2] into h_codes).
+hipError_t launch_gemm_bf16(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream);
 hipError_t launch_combine(const uint16_t* slot_out, const int32_t* ids, int32_t T, int32_t k, int32_t H, int32_t E,
                           int32_t expert_begin, uint16_t* out, hipStream_t stream);
 // Tile one weight [E, N, K] (nt, or nn = [E, K, N] when `nn`) into the layout

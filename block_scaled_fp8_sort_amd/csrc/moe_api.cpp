@@ -43,7 +43,7 @@ moe_status ok() {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-bool valid_fmt(int f) { return f == MOE_FMT_FP8_B128 || f == MOE_FMT_MXFP8A_MXFP4W; }
+bool valid_fmt(int f) { return f == MOE_FMT_FP8_B128 || f == MOE_FMT_MXFP8A_MXFP4W || f == MOE_FMT_BF16; }
 
 constexpr int kMaxE = 512;
 constexpr int kMaxK = 64;
@@ -117,14 +117,15 @@ FwdLayout fwd_layout(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I, int 
   const size_t S = (size_t)T * k;
   const size_t A = 256;
   const bool mx = fmt == MOE_FMT_MXFP8A_MXFP4W;
+  const bool bf = fmt == MOE_FMT_BF16;  // activations used as they are; h kept in bf16
   FwdLayout L;
   size_t o = 0;
   L.sorted_slot = o; o = align_up(o + 4 * S, A);
   L.offsets = o; o = align_up(o + 4 * (size_t)(E + 1), A);
-  L.act_codes = o; o = align_up(o + (size_t)T * H, A);
-  L.act_scales = o; o = align_up(o + (mx ? (size_t)T * (H / 32) : 4 * (size_t)T * (H / 128)), A);
-  L.h_codes = o; o = align_up(o + S * I, A);
-  L.h_scales = o; o = align_up(o + (mx ? S * (I / 32) : 4 * S * (I / 128)), A);
+  L.act_codes = o; o = align_up(o + (bf ? 0 : (size_t)T * H), A);
+  L.act_scales = o; o = align_up(o + (bf ? 0 : mx ? (size_t)T * (H / 32) : 4 * (size_t)T * (H / 128)), A);
+  L.h_codes = o; o = align_up(o + S * I * (bf ? 2 : 1), A);
+  L.h_scales = o; o = align_up(o + (bf ? 0 : mx ? S * (I / 32) : 4 * S * (I / 128)), A);
   L.slot_out = o; o = align_up(o + 2 * S * H, A);
   L.sort_ws = o; o = align_up(o + moe::route_sort_ws_bytes((int32_t)S, E), A);
   L.sched = o; o = align_up(o + 2 * MOE_TILE_COUNTERS_BYTES, A);  // gate_up's and down's tile counters
@@ -140,7 +141,8 @@ moe_status validate_weights(const moe_weights* w) {
     return fail(MOE_ERR_SHAPE, "H=%d and I=%d must be positive multiples of 128", w->H, w->I);
   if ((int64_t)2 * w->I * w->H >= (int64_t)1 << 31 || (int64_t)w->H * w->I >= (int64_t)1 << 31)
     return fail(MOE_ERR_SHAPE, "one expert's weight must stay below 2^31 elements");
-  if (!w->w13 || !w->w13_scale || !w->w2 || !w->w2_scale) return fail(MOE_ERR_NULL, "weight pointer is NULL");
+  if (!w->w13 || !w->w2) return fail(MOE_ERR_NULL, "weight pointer is NULL");
+  if (w->fmt != MOE_FMT_BF16 && (!w->w13_scale || !w->w2_scale)) return fail(MOE_ERR_NULL, "weight scale is NULL");
   return MOE_OK;
 }
 
@@ -154,14 +156,16 @@ moe_status validate_gemm(const moe_gemm_args* a) {
   if (!a->a_row_index && a->a_rows < a->max_rows)
     return fail(MOE_ERR_SHAPE, "without a row index A needs max_rows=%d rows, has %d", a->max_rows, a->a_rows);
   if (a->a_row_index && a->a_row_divisor < 1) return fail(MOE_ERR_SHAPE, "a_row_divisor must be >= 1");
-  if (!a->a_codes || !a->a_scales || !a->expert_offsets) return fail(MOE_ERR_NULL, "an operand pointer is NULL");
+  if (!a->a_codes || !a->expert_offsets || (a->weights->fmt != MOE_FMT_BF16 && !a->a_scales))
+    return fail(MOE_ERR_NULL, "an operand pointer is NULL");
   switch (a->epilogue) {
     case MOE_EPI_STORE_F32:
       if (!a->c_f32) return fail(MOE_ERR_NULL, "c_f32 is NULL");
       break;
     case MOE_EPI_SWIGLU_QUANT:
       if (a->which != 0) return fail(MOE_ERR_UNSUPPORTED, "the SwiGLU epilogue runs on the gate_up weight (which = 0)");
-      if (!a->h_codes || !a->h_scales) return fail(MOE_ERR_NULL, "h_codes / h_scales are NULL");
+      if (!a->h_codes || (a->weights->fmt != MOE_FMT_BF16 && !a->h_scales))
+        return fail(MOE_ERR_NULL, "h_codes / h_scales are NULL");
       if (a->has_swiglu_limit && !(std::isfinite(a->swiglu_limit) && a->swiglu_limit > 0.0f))
         return fail(MOE_ERR_SHAPE, "swiglu_limit must be finite and > 0");
       break;
@@ -207,6 +211,7 @@ moe::GemmParams to_params(const moe_gemm_args* a) {
 constexpr int64_t kSkinnyRowsPerExpert = 8;
 
 hipError_t launch_gemm(const moe::GemmParams& p, int fmt, int epi, bool paired, int num_cus, hipStream_t stream) {
+  if (fmt == MOE_FMT_BF16) return moe::launch_gemm_bf16(p, epi, paired, num_cus, stream);
   if (fmt == MOE_FMT_FP8_B128) {
     if ((int64_t)p.max_rows <= kSkinnyRowsPerExpert * p.E)
       return moe::launch_gemm_fp8_skinny(p, epi, paired, num_cus, stream);
@@ -275,15 +280,22 @@ moe_status forward_impl(const moe_weights* w, const uint16_t* hidden_states, con
 
   int32_t* sched = (int32_t*)(base + L.sched);
   if (router && (st = check_ptr(router->logits, dev, "router_logits")) != MOE_OK) return st;
-  hipError_t he = moe::launch_route_sort_and_quant(router, top_k_index, T, k, E, expert_begin, sorted_slot, offsets,
-                                                   opt ? opt->invalid_count : nullptr, base + L.sort_ws, hidden_states,
-                                                   T, H, w->fmt, act_codes, act_scales, sched,
-                                                   2 * MOE_TILE_COUNTERS_BYTES / 4, stream);
+  const bool bf = w->fmt == MOE_FMT_BF16;
+  hipError_t he;
+  if (bf)  // nothing to quantize: the gate_up GEMM gathers bf16 rows of hidden_states
+    he = moe::launch_route_sort_zero(router, top_k_index, T, k, E, expert_begin, sorted_slot, offsets, nullptr,
+                                     opt ? opt->invalid_count : nullptr, base + L.sort_ws, sched,
+                                     2 * MOE_TILE_COUNTERS_BYTES / 4, stream);
+  else
+    he = moe::launch_route_sort_and_quant(router, top_k_index, T, k, E, expert_begin, sorted_slot, offsets,
+                                          opt ? opt->invalid_count : nullptr, base + L.sort_ws, hidden_states, T, H,
+                                          w->fmt, act_codes, act_scales, sched, 2 * MOE_TILE_COUNTERS_BYTES / 4,
+                                          stream);
   if (he != hipSuccess) return hip_status(he, "route sort / quant launch");
 
   moe::GemmParams p1{};
-  p1.a_codes = act_codes;
-  p1.a_scales = act_scales;
+  p1.a_codes = bf ? (const uint8_t*)hidden_states : act_codes;
+  p1.a_scales = bf ? nullptr : act_scales;
   p1.a_row_index = sorted_slot;
   p1.a_row_div = k;
   p1.a_rows = T;
@@ -335,10 +347,10 @@ moe_status forward_impl(const moe_weights* w, const uint16_t* hidden_states, con
         (d->expert_offsets &&
          (he = hipMemcpyAsync(d->expert_offsets, offsets, 4 * (size_t)(E + 1), hipMemcpyDeviceToDevice, stream)) !=
              hipSuccess) ||
-        (d->act_codes &&
+        (d->act_codes && !bf &&
          (he = hipMemcpyAsync(d->act_codes, act_codes, (size_t)T * H, hipMemcpyDeviceToDevice, stream)) !=
              hipSuccess) ||
-        (d->act_scales &&
+        (d->act_scales && !bf &&
          (he = hipMemcpyAsync(d->act_scales, act_scales, sc_bytes, hipMemcpyDeviceToDevice, stream)) != hipSuccess))
       return hip_status(he, "debug copy");
   }
@@ -474,6 +486,7 @@ size_t moe_prepared_weights_size(moe_format fmt, int32_t E, int32_t H, int32_t I
   if (!valid_fmt(fmt) || E < 1 || H <= 0 || I <= 0 || H % 128 || I % 128) return 0;
   const size_t A = 256;
   const size_t e = (size_t)E, h = (size_t)H, i = (size_t)I;
+  if (fmt == MOE_FMT_BF16) return align_up(e * 2 * i * h * 2, A) + align_up(e * h * i * 2, A);
   if (fmt == MOE_FMT_FP8_B128) {
     const size_t nt2 = (h + 255) / 256;
     return align_up(e * 2 * i * h, A) + align_up(4 * e * (2 * i / 128) * (h / 128), A) +
@@ -495,7 +508,9 @@ moe_status moe_prepare_weights(moe_format fmt, moe_layout layout, int32_t E, int
   if (H <= 0 || I <= 0 || H % 128 || I % 128)
     return fail(MOE_ERR_SHAPE, "H=%d and I=%d must be positive multiples of 128", H, I);
   if ((int64_t)2 * I * H >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "one expert's weight must stay below 2^31");
-  if (!gate_up || !gate_up_scale || !down || !down_scale) return fail(MOE_ERR_NULL, "a weight pointer is NULL");
+  const bool bf = fmt == MOE_FMT_BF16;
+  if (!gate_up || !down || (!bf && (!gate_up_scale || !down_scale)))
+    return fail(MOE_ERR_NULL, "a weight pointer is NULL");
   if (layout == MOE_LAYOUT_NN && fmt != MOE_FMT_FP8_B128)
     return fail(MOE_ERR_UNSUPPORTED, "the nn layout is accepted for FP8_B128 weights only");
   if (!prepared) return fail(MOE_ERR_NULL, "prepared buffer is NULL");
@@ -507,6 +522,26 @@ moe_status moe_prepare_weights(moe_format fmt, moe_layout layout, int32_t E, int
   if (st != MOE_OK) return st;
   const size_t A = 256;
   const size_t e = E, h = H, i = I;
+  if (bf) {
+    // the kernel reads bf16 weights as stored ([E, N, K]): a plain copy
+    uint8_t* q13 = (uint8_t*)prepared;
+    uint8_t* q2 = q13 + align_up(e * 2 * i * h * 2, A);
+    hipError_t he;
+    if ((he = hipMemcpyAsync(q13, gate_up, e * 2 * i * h * 2, hipMemcpyDeviceToDevice, stream)) != hipSuccess ||
+        (he = hipMemcpyAsync(q2, down, e * h * i * 2, hipMemcpyDeviceToDevice, stream)) != hipSuccess)
+      return hip_status(he, "weight copy");
+    moe_weights w{};
+    w.fmt = fmt;
+    w.E = E;
+    w.H = H;
+    w.I = I;
+    w.w13 = q13;
+    w.w13_scale = nullptr;
+    w.w2 = q2;
+    w.w2_scale = nullptr;
+    *out = w;
+    return ok();
+  }
   const bool mx = fmt == MOE_FMT_MXFP8A_MXFP4W;
   const size_t b13 = mx ? e * 2 * i * h / 2 : e * 2 * i * h;
   const size_t b13s = mx ? e * 2 * i * (h / 32) : 4 * e * (2 * i / 128) * (h / 128);

@@ -64,8 +64,12 @@ typedef enum moe_status {
  * MOE_FMT_MXFP8A_MXFP4W: activations e4m3 with one UE8M0 scale byte per 1x32
  *   block; weights e2m1 packed two per byte along K (even k in the low nibble)
  *   with one UE8M0 byte per 1x32 block along K.  A UE8M0 byte b means 2^(b-127).
- * In both, a dequantized value is code value times its block scale. */
-typedef enum moe_format { MOE_FMT_FP8_B128 = 0, MOE_FMT_MXFP8A_MXFP4W = 1 } moe_format;
+ * In both, a dequantized value is code value times its block scale.
+ * MOE_FMT_BF16: the unquantized experts the pages fall back to ([P-devices]:
+ *   experts_implementation='grouped_mm'): bf16 activations and bf16 weights,
+ *   no scales, fp32 accumulation; h = SwiGLU(g, u) is rounded once to bf16 and
+ *   is the down projection's operand. */
+typedef enum moe_format { MOE_FMT_FP8_B128 = 0, MOE_FMT_MXFP8A_MXFP4W = 1, MOE_FMT_BF16 = 2 } moe_format;
 
 /* Weight layouts accepted by moe_prepare_weights: nt stores each expert's weight
  * as [N, K] (rows are output features), nn as [K, N]; the pages' forward picks
@@ -189,6 +193,8 @@ typedef struct moe_weights {
  *  for NN.
  *  MX (NT only): gate_up packed e2m1 [E, 2I, H/2] (even k in the low nibble),
  *  down packed [E, H, I/2]; UE8M0 scales uint8 [E, 2I, H/32] and [E, H, I/32].
+ *  BF16 (NT only): gate_up bf16 [E, 2I, H], down bf16 [E, H, I]; both scale
+ *  pointers are ignored and may be NULL (the descriptor's are NULL).
  * The tiled copy goes to `prepared` (device, at least moe_prepared_weights_size()
  * bytes, owned by the caller); `out` is filled on the host.  Enqueued on
  * `stream`.  Weight quantization itself is offline (the checkpoint's). */
@@ -218,7 +224,10 @@ moe_status moe_prepare_weights(moe_format fmt, moe_layout layout, int32_t E, int
  *                            slot_out[slot, n] = bf16(top_k_weights[slot] * C[r, n])
  *                            (bf16 [S, N], row-major).
  * Rows at and beyond offsets[E] are not written.  max_rows bounds offsets[E]
- * (normally T*k). */
+ * (normally T*k).
+ * MOE_FMT_BF16 weights: A is bf16 [a_rows, K] row-major (not K-block-major) and
+ * a_scales is ignored; the SwiGLU epilogue writes h as bf16 [max_rows, I]
+ * row-major into h_codes (h_scales ignored). */
 typedef enum moe_epilogue {
   MOE_EPI_STORE_F32 = 0,
   MOE_EPI_SWIGLU_QUANT = 1,

@@ -57,6 +57,9 @@ WORKLOADS = {
                  zipf_s=1.1, skip=0.05, seed=3),
         Workload("megamoe_fp8xfp4", T=16384, H=7168, I=2048, E=256, k=8, fmt=FMT_MX, routing="zipf",
                  zipf_s=1.1, skip=0.05, swiglu_limit=7.0, seed=4),
+        # the unquantized bf16 experts (the pages' grouped_mm fallback) on the Mixtral-shaped layer
+        Workload("mixtral_8x7b_bf16", T=4096, H=4096, I=14336, E=8, k=2, fmt=FMT_BF16, routing="uniform",
+                 seed=1),
     ]
 }
 
