@@ -12,13 +12,13 @@
 // Layout: B is the expert weight as stored, [E, N, K] bf16 row-major (nt); A
 // rows are bf16 [rows, K] row-major, gathered through a_row_index / divisor.
 //
-// Tile: 128 weight rows x 128 sorted rows, 4 waves.  Wave w owns 32 weight rows
-// (two 16-row groups) and all 128 rows of A (eight 16-row groups), so each lane
+// Tile: 256 weight rows x 128 sorted rows, 4 waves.  Wave w owns 64 weight rows
+// (four 16-row groups) and all 128 rows of A (eight 16-row groups), so each lane
 // ends with 4 consecutive weight rows of one A row per (group, A group) pair,
-// from v_mfma_f32_16x16x32_bf16 with the weights as operand A.  In a paired
-// (gate_up) tile, group 0 of wave w is gate rows h0 + 16 w .. + 16 and group 1
-// the matching up rows I + h0 + 16 w .., so g and u of an output meet in one
-// lane.  Per K stage of 64 elements the 128 gathered A rows (16 KB) are loaded
+// from v_mfma_f32_16x16x32_bf16 with the weights as operand A; each A fragment
+// read from LDS feeds four MFMAs.  In a paired (gate_up) tile, groups 2q and
+// 2q + 1 of wave w are gate rows h0 + 32 w + 16 q .. + 16 and the matching up
+// rows I + h0 + 32 w + 16 q .., so g and u of an output meet in one lane.  Per K stage of 64 elements the 128 gathered A rows (16 KB) are loaded
 // once by the workgroup into registers and stored to a double-buffered LDS
 // stage (16-byte chunks XOR-swizzled by row & 7, so the 16 rows a fragment read
 // touches spread over the banks); weights go straight from global memory to
@@ -38,7 +38,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // native vecto
 constexpr int kWavesB = 4;
 constexpr int kThreadsB = kWavesB * kWave;
 constexpr int BMB = 128;            // sorted rows per tile
-constexpr int BNB = 128;            // weight rows per tile
+constexpr int BNB = 256;            // weight rows per tile
 constexpr int kStageK = 64;         // K elements per stage (128 bytes of a row)
 constexpr int kStageBytes = BMB * kStageK * 2;
 constexpr int kMaxEB = 512;
@@ -78,33 +78,33 @@ __global__ __launch_bounds__(kThreadsB) void gemm_bf16_kernel(GemmParams p) {
     const int r_ld = min(tc.m0 + ld_row, tc.m_end - 1);
     const int arow = p.a_row_index ? p.a_row_index[r_ld] / p.a_row_div : r_ld;
     const uint8_t* a_src = A + (size_t)arow * row_bytes + ld_c0 * 16;
-    // this lane's weight rows, group 0 and 1
-    int wr0, wr1;
-    if (PAIRED) {
-      const int I = N / 2;
-      wr0 = tc.n_tile * (BNB / 2) + 16 * wave + l16;
-      wr1 = I + wr0;
-    } else {
-      wr0 = min(tc.n_tile * BNB + 32 * wave + l16, N - 1);
-      wr1 = min(tc.n_tile * BNB + 32 * wave + 16 + l16, N - 1);
-    }
-    const uint8_t* w0 = B + ((size_t)tc.e * N + wr0) * row_bytes + g * 16;
-    const uint8_t* w1 = B + ((size_t)tc.e * N + wr1) * row_bytes + g * 16;
-
-    v4f acc[2][8];
+    // this lane's weight rows, groups 0..3
+    const uint8_t* wp[4];
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < 4; ++q) {
+      int wr;
+      if (PAIRED)
+        wr = (q & 1) * (N / 2) + tc.n_tile * (BNB / 2) + 32 * wave + 16 * (q >> 1) + l16;
+      else
+        wr = min(tc.n_tile * BNB + 64 * wave + 16 * q + l16, N - 1);
+      wp[q] = B + ((size_t)tc.e * N + wr) * row_bytes + g * 16;
+    }
+
+    v4f acc[4][8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[q][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 a_reg[4], w_reg[4], a_nxt[4], w_nxt[4];
+    u32x4 a_reg[4], w_reg[8], a_nxt[4], w_nxt[8];
 #pragma unroll
     for (int c = 0; c < 4; ++c) a_reg[c] = *(const u32x4*)(a_src + c * 16);
-    // weights: [substep ks][group] at bytes ks * 64 + g * 16 of the stage
-    w_reg[0] = *(const u32x4*)(w0);
-    w_reg[1] = *(const u32x4*)(w1);
-    w_reg[2] = *(const u32x4*)(w0 + 64);
-    w_reg[3] = *(const u32x4*)(w1 + 64);
+    // weights: [substep ks][group q] at bytes ks * 64 + g * 16 of the stage
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      w_reg[q] = *(const u32x4*)(wp[q]);
+      w_reg[4 + q] = *(const u32x4*)(wp[q] + 64);
+    }
     __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
     for (int c = 0; c < 4; ++c) sm.stage[0][ld_row * 8 + ((ld_c0 + c) ^ (ld_row & 7))] = a_reg[c];
@@ -117,29 +117,29 @@ __global__ __launch_bounds__(kThreadsB) void gemm_bf16_kernel(GemmParams p) {
         const size_t o = (size_t)(s + 1) * 128;
 #pragma unroll
         for (int c = 0; c < 4; ++c) a_nxt[c] = *(const u32x4*)(a_src + o + c * 16);
-        w_nxt[0] = *(const u32x4*)(w0 + o);
-        w_nxt[1] = *(const u32x4*)(w1 + o);
-        w_nxt[2] = *(const u32x4*)(w0 + o + 64);
-        w_nxt[3] = *(const u32x4*)(w1 + o + 64);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          w_nxt[q] = *(const u32x4*)(wp[q] + o);
+          w_nxt[4 + q] = *(const u32x4*)(wp[q] + o + 64);
+        }
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 wa = as_bf16x8(w_reg[2 * ks]);
-        const bf16x8 wb = as_bf16x8(w_reg[2 * ks + 1]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int row = 16 * j + l16;
           const int chunk = (ks * 4 + g) ^ (row & 7);
           const bf16x8 b = as_bf16x8(sm.stage[cur][row * 8 + chunk]);
-          acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, b, acc[0][j], 0, 0, 0);
-          acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, b, acc[1][j], 0, 0, 0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[q][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w_reg[4 * ks + q]), b, acc[q][j], 0, 0, 0);
         }
       }
       if (more) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) sm.stage[cur ^ 1][ld_row * 8 + ((ld_c0 + c) ^ (ld_row & 7))] = a_nxt[c];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) w_reg[c] = w_nxt[c];
+        for (int c = 0; c < 8; ++c) w_reg[c] = w_nxt[c];
         __syncthreads();
       }
     }
@@ -152,39 +152,47 @@ __global__ __launch_bounds__(kThreadsB) void gemm_bf16_kernel(GemmParams p) {
       if constexpr (EPI == kEpiStoreF32) {
         if constexpr (PAIRED) {
           const int I = N / 2;
-          const int h = tc.n_tile * (BNB / 2) + 16 * wave + 4 * g;
-          *(v4f*)(p.c_f32 + (size_t)r * N + h) = acc[0][j];
-          *(v4f*)(p.c_f32 + (size_t)r * N + I + h) = acc[1][j];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int h = tc.n_tile * (BNB / 2) + 32 * wave + 16 * q + 4 * g;
+            *(v4f*)(p.c_f32 + (size_t)r * N + h) = acc[2 * q][j];
+            *(v4f*)(p.c_f32 + (size_t)r * N + I + h) = acc[2 * q + 1][j];
+          }
         } else {
-          const int n = tc.n_tile * BNB + 32 * wave + 4 * g;
-          if (n < N) *(v4f*)(p.c_f32 + (size_t)r * N + n) = acc[0][j];
-          if (n + 16 < N) *(v4f*)(p.c_f32 + (size_t)r * N + n + 16) = acc[1][j];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = tc.n_tile * BNB + 64 * wave + 16 * q + 4 * g;
+            if (n < N) *(v4f*)(p.c_f32 + (size_t)r * N + n) = acc[q][j];
+          }
         }
       } else if constexpr (EPI == kEpiSwiGLUQuant) {
         static_assert(PAIRED, "SwiGLU needs the paired gate/up tile");
         const int I = N / 2;
-        const int h = tc.n_tile * (BNB / 2) + 16 * wave + 4 * g;
-        float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          v[i] = p.has_limit ? swiglu<true>(acc[0][j][i], acc[1][j][i], p.limit)
-                             : swiglu<false>(acc[0][j][i], acc[1][j][i], p.limit);
-        uint2 o;
-        o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-        o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-        *(uint2*)((uint16_t*)p.h_codes + (size_t)r * I + h) = o;
+        for (int q = 0; q < 2; ++q) {
+          const int h = tc.n_tile * (BNB / 2) + 32 * wave + 16 * q + 4 * g;
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            v[i] = p.has_limit ? swiglu<true>(acc[2 * q][j][i], acc[2 * q + 1][j][i], p.limit)
+                               : swiglu<false>(acc[2 * q][j][i], acc[2 * q + 1][j][i], p.limit);
+          uint2 o;
+          o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+          o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+          *(uint2*)((uint16_t*)p.h_codes + (size_t)r * I + h) = o;
+        }
       } else {  // kEpiWeightedScatter
         const int slot = p.slot_of_row[r];
         const float wt = p.top_k_weights[slot];
-        const int n = tc.n_tile * BNB + 32 * wave + 4 * g;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          if (n + 16 * q < N) {
+        for (int q = 0; q < 4; ++q) {
+          const int n = tc.n_tile * BNB + 64 * wave + 16 * q + 4 * g;
+          if (n < N) {
             const v4f y = acc[q][j] * wt;
             uint2 o;
             o.x = f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16);
             o.y = f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16);
-            *(uint2*)(p.slot_out + (size_t)slot * N + n + 16 * q) = o;
+            *(uint2*)(p.slot_out + (size_t)slot * N + n) = o;
           }
         }
       }
