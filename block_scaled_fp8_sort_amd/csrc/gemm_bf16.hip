@@ -9,8 +9,11 @@
 // SwiGLU (h rounded once to bf16, the down projection's operand) or the
 // routing-weighted bf16 scatter into the slot buffer.
 //
-// Layout: B is the expert weight as stored, [E, N, K] bf16 row-major (nt); A
-// rows are bf16 [rows, K] row-major, gathered through a_row_index / divisor.
+// Layout: B is the expert weight [E, N, K] in operand order (prepare.hip): per
+// 16-row group and 64-element K stage a 2 KB block of two 1 KB sub-steps, each
+// the 64 lanes' 16-byte fragments in lane order, so a wave's weight load is 1 KB
+// contiguous.  A rows are bf16 [rows, K] row-major, gathered through
+// a_row_index / divisor.
 //
 // Tile: 256 weight rows x 128 sorted rows, 4 waves.  Wave w owns 64 weight rows
 // (four 16-row groups) and all 128 rows of A (eight 16-row groups), so each lane
@@ -78,16 +81,18 @@ __global__ __launch_bounds__(kThreadsB) void gemm_bf16_kernel(GemmParams p) {
     const int r_ld = min(tc.m0 + ld_row, tc.m_end - 1);
     const int arow = p.a_row_index ? p.a_row_index[r_ld] / p.a_row_div : r_ld;
     const uint8_t* a_src = A + (size_t)arow * row_bytes + ld_c0 * 16;
-    // this lane's weight rows, groups 0..3
+    // this wave's 16-row weight groups 0..3 (a group past N, in the last tile of
+    // an N that is not a multiple of 256, repeats the last group; its results
+    // are never stored); the lane's fragment is 16 bytes at lane * 16
     const uint8_t* wp[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      int wr;
+      int grp;
       if (PAIRED)
-        wr = (q & 1) * (N / 2) + tc.n_tile * (BNB / 2) + 32 * wave + 16 * (q >> 1) + l16;
+        grp = ((q & 1) * (N / 2) + tc.n_tile * (BNB / 2) + 32 * wave + 16 * (q >> 1)) / 16;
       else
-        wr = min(tc.n_tile * BNB + 64 * wave + 16 * q + l16, N - 1);
-      wp[q] = B + ((size_t)tc.e * N + wr) * row_bytes + g * 16;
+        grp = min((tc.n_tile * BNB + 64 * wave + 16 * q) / 16, N / 16 - 1);
+      wp[q] = B + (((size_t)tc.e * (N / 16) + grp) * KS) * 2048 + lane * 16;
     }
 
     v4f acc[4][8];
@@ -103,7 +108,7 @@ __global__ __launch_bounds__(kThreadsB) void gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       w_reg[q] = *(const u32x4*)(wp[q]);
-      w_reg[4 + q] = *(const u32x4*)(wp[q] + 64);
+      w_reg[4 + q] = *(const u32x4*)(wp[q] + 1024);
     }
     __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
@@ -117,10 +122,11 @@ __global__ __launch_bounds__(kThreadsB) void gemm_bf16_kernel(GemmParams p) {
         const size_t o = (size_t)(s + 1) * 128;
 #pragma unroll
         for (int c = 0; c < 4; ++c) a_nxt[c] = *(const u32x4*)(a_src + o + c * 16);
+        const size_t ow = (size_t)(s + 1) * 2048;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          w_nxt[q] = *(const u32x4*)(wp[q] + o);
-          w_nxt[4 + q] = *(const u32x4*)(wp[q] + o + 64);
+          w_nxt[q] = *(const u32x4*)(wp[q] + ow);
+          w_nxt[4 + q] = *(const u32x4*)(wp[q] + ow + 1024);
         }
       }
 #pragma unroll

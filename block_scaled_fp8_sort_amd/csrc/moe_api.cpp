@@ -523,13 +523,14 @@ moe_status moe_prepare_weights(moe_format fmt, moe_layout layout, int32_t E, int
   const size_t A = 256;
   const size_t e = E, h = H, i = I;
   if (bf) {
-    // the kernel reads bf16 weights as stored ([E, N, K]): a plain copy
+    // bf16 weights in the bf16 GEMM's operand order
     uint8_t* q13 = (uint8_t*)prepared;
     uint8_t* q2 = q13 + align_up(e * 2 * i * h * 2, A);
     hipError_t he;
-    if ((he = hipMemcpyAsync(q13, gate_up, e * 2 * i * h * 2, hipMemcpyDeviceToDevice, stream)) != hipSuccess ||
-        (he = hipMemcpyAsync(q2, down, e * h * i * 2, hipMemcpyDeviceToDevice, stream)) != hipSuccess)
-      return hip_status(he, "weight copy");
+    if ((he = moe::launch_tile_weight_bf16((const uint16_t*)gate_up, E, 2 * I, H, (uint16_t*)q13, stream)) !=
+            hipSuccess ||
+        (he = moe::launch_tile_weight_bf16((const uint16_t*)down, E, H, I, (uint16_t*)q2, stream)) != hipSuccess)
+      return hip_status(he, "weight tiling");
     moe_weights w{};
     w.fmt = fmt;
     w.E = E;

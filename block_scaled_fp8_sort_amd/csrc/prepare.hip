@@ -168,6 +168,39 @@ hipError_t launch_tile_weight_mx(const uint8_t* codes, const uint8_t* scales, bo
   return hipGetLastError();
 }
 
+namespace {
+
+// bf16 weights [E, N, K] -> MFMA operand order for the bf16 grouped GEMM: for
+// each 16-row group and 64-element K stage, a 2 KB block holding the two
+// 32-element sub-steps, each as the 64 lanes' 16-byte fragments in lane order
+// (lane = 16 * (k % 32 / 8) + row % 16), so one wave-wide load reads 1 KB
+// contiguous.  One thread moves one 16-byte chunk (8 elements).
+__global__ __launch_bounds__(256) void tile_weight_bf16_kernel(const uint4* __restrict__ src, int32_t N, int32_t K,
+                                                               int64_t chunks, uint4* __restrict__ dst) {
+  const int64_t kc = K / 8;  // chunks per row
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks; c += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = c / kc;  // e * N + n
+    const int k0 = (int)(c - row * kc) * 8;
+    const int64_t e = row / N;
+    const int n = (int)(row - e * N);
+    const int stage = k0 / 64, ks = (k0 % 64) / 32, g = (k0 % 32) / 8;
+    const int64_t block = (e * (N / 16) + n / 16) * (K / 64) + stage;
+    dst[block * 128 + ks * 64 + g * 16 + n % 16] = src[c];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tile_weight_bf16(const uint16_t* src, int32_t E, int32_t N, int32_t K, uint16_t* dst,
+                                   hipStream_t stream) {
+  const int64_t chunks = (int64_t)E * N * (K / 8);
+  int64_t blocks = (chunks + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(tile_weight_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const uint4*)src, N, K,
+                     chunks, (uint4*)dst);
+  return hipGetLastError();
+}
+
 hipError_t launch_transpose_u8(const uint8_t* in, uint8_t* out, int32_t batch, int32_t rows, int32_t cols,
                                hipStream_t stream) {
   return launch_t<uint8_t>(in, out, batch, rows, cols, stream);
