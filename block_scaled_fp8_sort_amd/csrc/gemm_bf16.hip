@@ -71,16 +71,21 @@ __global__ __launch_bounds__(kThreadsB) void gemm_bf16_kernel(GemmParams p) {
   const uint8_t* A = p.a_codes;
   const uint8_t* B = p.b_codes;
 
-  // cooperative A load: thread tid covers row tid / 2, chunks 4 (tid % 2) .. + 4
-  const int ld_row = tid >> 1, ld_c0 = (tid & 1) * 4;
+  // cooperative A load: thread tid covers chunk tid % 8 of rows tid / 8 + 32 i
+  // (i < 4), so 8 consecutive lanes read one row's whole 128-byte stage segment
+  const int ld_r0 = tid >> 3, ld_c = tid & 7;
 
   for (int t = xcd_virtual_block(); t < total; t += gridDim.x) {
     const TileCoord tc = locate_tile(t, E, BMB, NT, sm.off, sm.tp);
-    // this thread's gathered A row (rows past the expert's end repeat its last
+    // this thread's gathered A rows (rows past the expert's end repeat its last
     // row; their results are never stored)
-    const int r_ld = min(tc.m0 + ld_row, tc.m_end - 1);
-    const int arow = p.a_row_index ? p.a_row_index[r_ld] / p.a_row_div : r_ld;
-    const uint8_t* a_src = A + (size_t)arow * row_bytes + ld_c0 * 16;
+    const uint8_t* a_src[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r_ld = min(tc.m0 + ld_r0 + 32 * i, tc.m_end - 1);
+      const int arow = p.a_row_index ? p.a_row_index[r_ld] / p.a_row_div : r_ld;
+      a_src[i] = A + (size_t)arow * row_bytes + ld_c * 16;
+    }
     // this wave's 16-row weight groups 0..3 (a group past N, in the last tile of
     // an N that is not a multiple of 256, repeats the last group; its results
     // are never stored); the lane's fragment is 16 bytes at lane * 16
@@ -103,7 +108,7 @@ __global__ __launch_bounds__(kThreadsB) void gemm_bf16_kernel(GemmParams p) {
 
     u32x4 a_reg[4], w_reg[8], a_nxt[4], w_nxt[8];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) a_reg[c] = *(const u32x4*)(a_src + c * 16);
+    for (int i = 0; i < 4; ++i) a_reg[i] = *(const u32x4*)(a_src[i]);
     // weights: [substep ks][group q] at bytes ks * 64 + g * 16 of the stage
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -112,7 +117,10 @@ __global__ __launch_bounds__(kThreadsB) void gemm_bf16_kernel(GemmParams p) {
     }
     __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
-    for (int c = 0; c < 4; ++c) sm.stage[0][ld_row * 8 + ((ld_c0 + c) ^ (ld_row & 7))] = a_reg[c];
+    for (int i = 0; i < 4; ++i) {
+      const int row = ld_r0 + 32 * i;
+      sm.stage[0][row * 8 + (ld_c ^ (row & 7))] = a_reg[i];
+    }
     __syncthreads();
 
     for (int s = 0; s < KS; ++s) {
@@ -121,7 +129,7 @@ __global__ __launch_bounds__(kThreadsB) void gemm_bf16_kernel(GemmParams p) {
       if (more) {
         const size_t o = (size_t)(s + 1) * 128;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) a_nxt[c] = *(const u32x4*)(a_src + o + c * 16);
+        for (int i = 0; i < 4; ++i) a_nxt[i] = *(const u32x4*)(a_src[i] + o);
         const size_t ow = (size_t)(s + 1) * 2048;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -143,7 +151,10 @@ __global__ __launch_bounds__(kThreadsB) void gemm_bf16_kernel(GemmParams p) {
       }
       if (more) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) sm.stage[cur ^ 1][ld_row * 8 + ((ld_c0 + c) ^ (ld_row & 7))] = a_nxt[c];
+        for (int i = 0; i < 4; ++i) {
+          const int row = ld_r0 + 32 * i;
+          sm.stage[cur ^ 1][row * 8 + (ld_c ^ (row & 7))] = a_nxt[i];
+        }
 #pragma unroll
         for (int c = 0; c < 8; ++c) w_reg[c] = w_nxt[c];
         __syncthreads();
