@@ -158,3 +158,57 @@ def test_bf16_forward_full_size_sampled():
     n = {k_: host(v) for k_, v in inp.items()}
     ref = oracle.forward(BF16, n["w13"], None, n["w2"], None, n["x"], n["ids"], n["w"], tokens=tokens)
     assert_out_close(host(out)[tokens], ref[tokens], wl.name)
+
+
+def test_bf16_forward_edge_cases():
+    """Empty batch, a single token, k = E = 1, and a batch large enough for the
+    multi-workgroup sort (T * k >= 16384 slots)."""
+    wl = SMALL[0]
+    inp = W.inputs(wl, DEV)
+    w = moe.prepare_weights(inp["w13"], None, inp["w2"], None, fmt=BF16)
+    out = moe.experts_forward(inp["x"][:0], inp["ids"][:0], inp["w"][:0], w)
+    assert out.shape == (0, wl.H)
+    one = moe.experts_forward(inp["x"][-1:].contiguous(), inp["ids"][-1:].contiguous(), inp["w"][-1:].contiguous(), w)
+    torch.cuda.synchronize()
+    n = {k_: host(v) for k_, v in inp.items()}
+    ref = oracle.forward(BF16, n["w13"], None, n["w2"], None, n["x"][-1:], n["ids"][-1:], n["w"][-1:])
+    assert_out_close(host(one), ref, "single token")
+    for case in (_wl("bf16_k1_e1", T=130, H=256, I=128, E=1, k=1, seed=56),
+                 _wl("bf16_multiblock_sort", T=2100, H=256, I=128, E=64, k=8, routing="zipf", skip=0.05, seed=57)):
+        say(f"bf16 forward {case.name}")
+        inp = W.inputs(case, DEV)
+        w = moe.prepare_weights(inp["w13"], None, inp["w2"], None, fmt=BF16)
+        out = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w)
+        torch.cuda.synchronize()
+        n = {k_: host(v) for k_, v in inp.items()}
+        ref = oracle.forward(BF16, n["w13"], None, n["w2"], None, n["x"], n["ids"], n["w"])
+        assert_out_close(host(out), ref, case.name)
+
+
+def test_bf16_forward_graph_replay():
+    """Captured in a HIP graph, the bf16 forward replays bit-exactly, with eager
+    work and synchronizations between the replays."""
+    wl = SMALL[1]
+    inp = W.inputs(wl, DEV)
+    w = moe.prepare_weights(inp["w13"], None, inp["w2"], None, fmt=BF16)
+    ref = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w).clone()
+    torch.cuda.synchronize()
+    out = torch.empty_like(ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe.experts_forward(inp["x"], inp["ids"], inp["w"], w, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.experts_forward(inp["x"], inp["ids"], inp["w"], w, out=out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        junk = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out).view(np.uint16), host(ref).view(np.uint16)), f"replay {rep}"
+        assert np.array_equal(host(junk).view(np.uint16), host(ref).view(np.uint16))
