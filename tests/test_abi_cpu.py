@@ -235,3 +235,32 @@ def test_workspace_sized_for_next_power_of_two():
     for n, sized in rows:
         assert moe._pow2_tokens(n) == sized
         assert sized < 2 * n or n == 1
+
+
+def test_bf16_format_on_the_host(lib):
+    # prepared size: the two bf16 weights in operand order, each rounded up to 256 bytes
+    assert lib.moe_prepared_weights_size(2, 4, 256, 128) == 4 * 256 * 256 * 2 + 4 * 256 * 128 * 2
+    assert lib.moe_prepared_weights_size(2, 3, 384, 128) == 3 * 256 * 384 * 2 + 3 * 384 * 128 * 2
+    desc = moe.MoeWeights()
+    p = ctypes.c_void_p(4096)
+    # the nn layout is refused for bf16, like MX; scale pointers may be NULL
+    assert lib.moe_prepare_weights(2, 1, 4, 256, 128, p, None, p, None, p, 1 << 30, ctypes.byref(desc), None) == UNSUP
+    assert lib.moe_prepare_weights(0, 0, 4, 256, 128, p, None, p, None, p, 1 << 30, ctypes.byref(desc), None) == NULL
+    # the forward's workspace holds no activation codes for bf16 but h in bf16
+    w8, wb = _weights(fmt=0), _weights(fmt=2)
+    assert lib.moe_experts_forward_workspace(64, 2, ctypes.byref(wb)) > 0
+    assert lib.moe_experts_forward_workspace(64, 2, ctypes.byref(wb)) != lib.moe_experts_forward_workspace(
+        64, 2, ctypes.byref(w8))
+    # a bf16 GEMM needs no scales: with a_scales NULL it fails only on the missing output
+    a = moe.MoeGemmArgs()
+    wb.w13_scale = wb.w2_scale = None
+    a.weights = ctypes.pointer(wb)
+    a.which, a.max_rows, a.a_rows = 0, 64, 64
+    a.a_codes = a.expert_offsets = 16
+    a.epilogue = moe.EPI_STORE_F32
+    assert lib.moe_grouped_gemm(ctypes.byref(a), None) == NULL
+    assert b"c_f32" in lib.moe_last_error()
+    w8.w13_scale = None
+    a.weights = ctypes.pointer(w8)
+    assert lib.moe_grouped_gemm(ctypes.byref(a), None) == NULL
+    assert b"scale" in lib.moe_last_error()
