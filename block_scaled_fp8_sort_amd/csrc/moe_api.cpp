@@ -422,8 +422,7 @@ moe_status moe_route_topk(const float* router_logits, int32_t T, int32_t n_exper
   if (n_experts < 1 || n_experts > kMaxE) return fail(MOE_ERR_SHAPE, "n_experts=%d outside [1, %d]", n_experts, kMaxE);
   if (k < 1 || k > kMaxK || k > n_experts)
     return fail(MOE_ERR_SHAPE, "k=%d outside [1, min(%d, n_experts=%d)]", k, kMaxK, n_experts);
-  if ((int64_t)T * k >= (int64_t)1 << 31 || (int64_t)T * n_experts >= (int64_t)1 << 40)
-    return fail(MOE_ERR_SHAPE, "T*k must stay below 2^31");
+  if ((int64_t)T * k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "T*k must stay below 2^31");
   const bool sort = expert_offsets != nullptr;
   if (!sort && (sorted_slot || slot_pos))
     return fail(MOE_ERR_NULL, "sorted_slot / slot_pos given without expert_offsets");
