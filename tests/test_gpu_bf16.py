@@ -94,6 +94,7 @@ SMALL = [
     _wl("bf16_clamp", T=517, H=384, I=256, E=12, k=4, routing="zipf", skip=0.05, limit=0.05, seed=52),
     _wl("bf16_few_rows", T=16, H=640, I=384, E=32, k=8, routing="zipf", skip=0.1, seed=53),
     _wl("bf16_e512", T=600, H=256, I=128, E=512, k=6, routing="zipf", skip=0.05, seed=54),
+    _wl("bf16_k64", T=20, H=256, I=128, E=128, k=64, routing="zipf", skip=0.1, seed=58),
 ]
 
 

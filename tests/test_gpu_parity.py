@@ -325,6 +325,10 @@ SMALL = [
     _small_workload("e512_fp8_few_rows", FP8, T=160, H=256, I=128, E=512, k=8, routing="zipf", skip=0.05, seed=19),
     _small_workload("e512_fp8_tiled", FP8, T=1500, H=256, I=256, E=512, k=6, routing="zipf", skip=0.05, seed=20),
     _small_workload("e512_mx", MX, T=1200, H=256, I=128, E=512, k=4, routing="zipf", skip=0.05, limit=7.0, seed=22),
+    # more than 8 slots per token (the combine's wide path), up to the largest k
+    _small_workload("k16_fp8", FP8, T=96, H=256, I=128, E=32, k=16, routing="zipf", skip=0.1, seed=24),
+    _small_workload("k64_fp8", FP8, T=20, H=256, I=128, E=128, k=64, routing="zipf", skip=0.1, seed=25),
+    _small_workload("k24_mx", MX, T=40, H=256, I=128, E=48, k=24, routing="zipf", skip=0.1, limit=7.0, seed=26),
 ]
 
 
