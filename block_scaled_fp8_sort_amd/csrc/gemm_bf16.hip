@@ -46,8 +46,10 @@ constexpr int kStageK = 64;         // K elements per stage (128 bytes of a row)
 constexpr int kStageBytes = BMB * kStageK * 2;
 constexpr int kMaxEB = 512;
 
+constexpr int kRing = 3;            // A stages in LDS, weight stages in registers
+
 struct SmemB {
-  u32x4 stage[2][BMB * 8];  // [buffer][row * 8 + swizzled 16-byte chunk]
+  u32x4 stage[kRing][BMB * 8];  // [buffer][row * 8 + swizzled 16-byte chunk]
   int off[kMaxEB + 1];
   int tp[kMaxEB + 1];
   int scan[kThreadsB];
@@ -57,7 +59,7 @@ static_assert(sizeof(u32x4) * BMB * 8 == kStageBytes, "stage size");
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 template <int EPI, bool PAIRED>
-__global__ __launch_bounds__(kThreadsB) void gemm_bf16_kernel(GemmParams p) {
+__global__ __launch_bounds__(kThreadsB, 2) void gemm_bf16_kernel(GemmParams p) {
   __shared__ SmemB sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -71,24 +73,28 @@ __global__ __launch_bounds__(kThreadsB) void gemm_bf16_kernel(GemmParams p) {
   const uint8_t* A = p.a_codes;
   const uint8_t* B = p.b_codes;
 
-  // cooperative A load: thread tid covers chunk tid % 8 of rows tid / 8 + 32 i
-  // (i < 4), so 8 consecutive lanes read one row's whole 128-byte stage segment
-  const int ld_r0 = tid >> 3, ld_c = tid & 7;
+  // A by LDS-DMA: DMA instruction q (< 4) of wave w copies rows 32 w + 8 q ..
+  // + 8 of the stage, lane l taking row 32 w + 8 q + l / 8 into chunk position
+  // l % 8; it reads logical chunk (l % 8) ^ (l / 8), so position c of row r
+  // holds chunk c ^ (r & 7), the swizzle the fragment reads undo
+  const int dma_rr = lane >> 3, dma_chunk = (lane & 7) ^ dma_rr;
 
   for (int t = xcd_virtual_block(); t < total; t += gridDim.x) {
     const TileCoord tc = locate_tile(t, E, BMB, NT, sm.off, sm.tp);
-    // this thread's gathered A rows (rows past the expert's end repeat its last
+    // this lane's gathered A rows (rows past the expert's end repeat its last
     // row; their results are never stored)
-    const uint8_t* a_src[4];
+    // (byte offsets from A, 32-bit: the host keeps A under 4 GiB)
+    uint32_t a_off[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r_ld = min(tc.m0 + ld_r0 + 32 * i, tc.m_end - 1);
+    for (int q = 0; q < 4; ++q) {
+      const int r_ld = min(tc.m0 + 32 * wave + 8 * q + dma_rr, tc.m_end - 1);
       const int arow = p.a_row_index ? p.a_row_index[r_ld] / p.a_row_div : r_ld;
-      a_src[i] = A + (size_t)arow * row_bytes + ld_c * 16;
+      a_off[q] = (uint32_t)arow * (uint32_t)row_bytes + (uint32_t)dma_chunk * 16;
     }
     // this wave's 16-row weight groups 0..3 (a group past N, in the last tile of
     // an N that is not a multiple of 256, repeats the last group; its results
     // are never stored); the lane's fragment is 16 bytes at lane * 16
+    // (group bases are wave-uniform, in scalar registers; the lane adds lane * 16)
     const uint8_t* wp[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -97,8 +103,10 @@ __global__ __launch_bounds__(kThreadsB) void gemm_bf16_kernel(GemmParams p) {
         grp = ((q & 1) * (N / 2) + tc.n_tile * (BNB / 2) + 32 * wave + 16 * (q >> 1)) / 16;
       else
         grp = min((tc.n_tile * BNB + 64 * wave + 16 * q) / 16, N / 16 - 1);
-      wp[q] = B + (((size_t)tc.e * (N / 16) + grp) * KS) * 2048 + lane * 16;
+      grp = __builtin_amdgcn_readfirstlane(grp);
+      wp[q] = B + (((size_t)tc.e * (N / 16) + grp) * KS) * 2048;
     }
+    const uint32_t wl = (uint32_t)lane * 16;
 
     v4f acc[4][8];
 #pragma unroll
@@ -106,60 +114,57 @@ __global__ __launch_bounds__(kThreadsB) void gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[q][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 a_reg[4], w_reg[8], a_nxt[4], w_nxt[8];
+    // stage s: 4 A DMAs into LDS buffer s % 3 and 8 weight loads into register
+    // slot s % 3 (weights [substep ks][group q] at ks * 1024 of the stage block),
+    // 12 vector-memory instructions per wave, issued two stages ahead
+    u32x4 wr[kRing][8];
+    auto issue = [&](int st, int b, u32x4(&w)[8]) {
+      const uint32_t lds = lds_addr(&sm.stage[b][0]) + (uint32_t)(32 * wave) * 128;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a_reg[i] = *(const u32x4*)(a_src[i]);
-    // weights: [substep ks][group q] at bytes ks * 64 + g * 16 of the stage
+      for (int q = 0; q < 4; ++q) lds_dma16_s(A, a_off[q] + (uint32_t)st * 128, lds + q * 1024);
+      const size_t ow = (size_t)st * 2048;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      w_reg[q] = *(const u32x4*)(wp[q]);
-      w_reg[4 + q] = *(const u32x4*)(wp[q] + 1024);
-    }
+      for (int q = 0; q < 4; ++q) {
+        w[q] = *(const u32x4*)(wp[q] + ow + wl);
+        w[4 + q] = *(const u32x4*)(wp[q] + ow + 1024 + wl);
+      }
+    };
     __syncthreads();  // the previous tile's LDS reads are done
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = ld_r0 + 32 * i;
-      sm.stage[0][row * 8 + (ld_c ^ (row & 7))] = a_reg[i];
-    }
-    __syncthreads();
+    issue(0, 0, wr[0]);
+    issue(1, 1, wr[1]);
 
-    for (int s = 0; s < KS; ++s) {
-      const int cur = s & 1;
-      const bool more = s + 1 < KS;
-      if (more) {
-        const size_t o = (size_t)(s + 1) * 128;
+    // Every step issues (past the last stage it repeats stage KS - 1 into a
+    // buffer and a register slot nobody reads again), so the same 12
+    // instructions are in flight at every wait and the compiler's own waits for
+    // the weight registers stay exact; only the MFMAs are skipped past KS.
+    for (int s0 = 0; s0 < KS; s0 += kRing) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a_nxt[i] = *(const u32x4*)(a_src[i] + o);
-        const size_t ow = (size_t)(s + 1) * 2048;
+      for (int j = 0; j < kRing; ++j) {
+        const int st = s0 + j;
+        // stage st has landed once only stage st + 1's instructions are still in
+        // flight (the compiler's waits for the weight registers never wait less:
+        // it does not count the DMAs)
+        wait_vmcnt<12>();
+        __syncthreads();  // every wave's part landed; every wave is done with stage st - 1
+        issue(min(st + 2, KS - 1), (j + 2) % kRing, wr[(j + 2) % kRing]);
+        if (st < KS) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          w_nxt[q] = *(const u32x4*)(wp[q] + ow);
-          w_nxt[4 + q] = *(const u32x4*)(wp[q] + ow + 1024);
+          for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+              const int row = 16 * jj + l16;
+              const int chunk = (ks * 4 + g) ^ (row & 7);
+              const bf16x8 b = as_bf16x8(sm.stage[j][row * 8 + chunk]);
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                acc[q][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wr[j][4 * ks + q]), b, acc[q][jj], 0, 0,
+                                                                    0);
+            }
+          }
         }
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int row = 16 * j + l16;
-          const int chunk = (ks * 4 + g) ^ (row & 7);
-          const bf16x8 b = as_bf16x8(sm.stage[cur][row * 8 + chunk]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            acc[q][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w_reg[4 * ks + q]), b, acc[q][j], 0, 0, 0);
-        }
-      }
-      if (more) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = ld_r0 + 32 * i;
-          sm.stage[cur ^ 1][row * 8 + (ld_c ^ (row & 7))] = a_nxt[i];
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) w_reg[c] = w_nxt[c];
-        __syncthreads();
       }
     }
+    wait_vmcnt<0>();  // the trailing repeats land before the next tile reuses the buffers
 
     // epilogue: lane holds weight rows 4 g .. 4 g + 3 of each group, A row 16 j + l16
 #pragma unroll

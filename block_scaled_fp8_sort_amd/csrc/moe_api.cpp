@@ -158,6 +158,9 @@ moe_status validate_gemm(const moe_gemm_args* a) {
   if (a->a_row_index && a->a_row_divisor < 1) return fail(MOE_ERR_SHAPE, "a_row_divisor must be >= 1");
   if (!a->a_codes || !a->expert_offsets || (a->weights->fmt != MOE_FMT_BF16 && !a->a_scales))
     return fail(MOE_ERR_NULL, "an operand pointer is NULL");
+  if (a->weights->fmt == MOE_FMT_BF16 &&
+      (int64_t)a->a_rows * (a->which == 0 ? a->weights->H : a->weights->I) * 2 >= (int64_t)1 << 32)
+    return fail(MOE_ERR_SHAPE, "the bf16 A operand must stay below 4 GiB");
   switch (a->epilogue) {
     case MOE_EPI_STORE_F32:
       if (!a->c_f32) return fail(MOE_ERR_NULL, "c_f32 is NULL");
@@ -242,6 +245,9 @@ moe_status forward_impl(const moe_weights* w, const uint16_t* hidden_states, con
       return fail(MOE_ERR_SHAPE, "n_experts=%d outside [1, %d]", router->n_experts, kMaxE);
     if (k > router->n_experts) return fail(MOE_ERR_SHAPE, "k=%d exceeds n_experts=%d", k, router->n_experts);
   }
+  if (w->fmt == MOE_FMT_BF16 && ((int64_t)T * w->H * 2 >= (int64_t)1 << 32 ||
+                                 (int64_t)T * k * w->I * 2 >= (int64_t)1 << 32))
+    return fail(MOE_ERR_SHAPE, "bf16 experts: hidden_states and h must each stay below 4 GiB");
   if (T == 0) return ok();
   if (!hidden_states || !top_k_index || !top_k_weights || !out || (router && !router->logits))
     return fail(MOE_ERR_NULL, "hidden_states / router_logits / top_k_index / top_k_weights / out is NULL");

@@ -68,7 +68,8 @@ typedef enum moe_status {
  * MOE_FMT_BF16: the unquantized experts the pages fall back to ([P-devices]:
  *   experts_implementation='grouped_mm'): bf16 activations and bf16 weights,
  *   no scales, fp32 accumulation; h = SwiGLU(g, u) is rounded once to bf16 and
- *   is the down projection's operand. */
+ *   is the down projection's operand.  The forward needs T*H and T*k*I below
+ *   2^31 elements (MOE_ERR_SHAPE otherwise). */
 typedef enum moe_format { MOE_FMT_FP8_B128 = 0, MOE_FMT_MXFP8A_MXFP4W = 1, MOE_FMT_BF16 = 2 } moe_format;
 
 /* Weight layouts accepted by moe_prepare_weights: nt stores each expert's weight
@@ -225,9 +226,9 @@ moe_status moe_prepare_weights(moe_format fmt, moe_layout layout, int32_t E, int
  *                            (bf16 [S, N], row-major).
  * Rows at and beyond offsets[E] are not written.  max_rows bounds offsets[E]
  * (normally T*k).
- * MOE_FMT_BF16 weights: A is bf16 [a_rows, K] row-major (not K-block-major) and
- * a_scales is ignored; the SwiGLU epilogue writes h as bf16 [max_rows, I]
- * row-major into h_codes (h_scales ignored). */
+ * MOE_FMT_BF16 weights: A is bf16 [a_rows, K] row-major (not K-block-major),
+ * below 4 GiB, and a_scales is ignored; the SwiGLU epilogue writes h as bf16
+ * [max_rows, I] row-major into h_codes (h_scales ignored). */
 typedef enum moe_epilogue {
   MOE_EPI_STORE_F32 = 0,
   MOE_EPI_SWIGLU_QUANT = 1,
