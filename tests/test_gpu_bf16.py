@@ -154,7 +154,7 @@ def test_bf16_forward_full_size_sampled():
     w = moe.prepare_weights(inp["w13"], None, inp["w2"], None, fmt=BF16)
     out = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w)
     torch.cuda.synchronize()
-    tokens = W.sample_tokens(wl.T, 12, wl.seed)
+    tokens = W.sample_tokens(wl.T, 48, wl.seed)
     say(f"bf16 forward full {wl.name}: oracle on {tokens.size} tokens")
     n = {k_: host(v) for k_, v in inp.items()}
     ref = oracle.forward(BF16, n["w13"], None, n["w2"], None, n["x"], n["ids"], n["w"], tokens=tokens)

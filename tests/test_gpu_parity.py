@@ -448,7 +448,7 @@ def test_forward_parity_full_size_sampled(name):
     wl = W.WORKLOADS[name]
     say(f"forward full {name}: generating inputs")
     inp = W.inputs(wl, DEV)
-    tokens = W.sample_tokens(wl.T, 12, wl.seed)
+    tokens = W.sample_tokens(wl.T, 48, wl.seed)
     say(f"forward full {name}: running GPU + oracle on {tokens.size} tokens")
     got, ref, _, n, _ = _forward_case(wl, inp, tokens=tokens)
     assert_out_close(got[tokens], ref[tokens], name)

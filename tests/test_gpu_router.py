@@ -147,7 +147,7 @@ def test_forward_from_logits_full_decode_sampled():
     torch.cuda.synchronize()
     o_ids, o_w = oracle.router_topk(host(lg), wl.k)
     assert np.array_equal(host(ids), o_ids)
-    tokens = W.sample_tokens(wl.T, 12, wl.seed)
+    tokens = W.sample_tokens(wl.T, 48, wl.seed)
     n = {k_: host(v) for k_, v in inp.items()}
     ref = oracle.forward(wl.fmt, n["w13"], n["s13"], n["w2"], n["s2"], n["x"], o_ids, o_w, tokens=tokens)
     g = torch.from_numpy(host(out)[tokens].view(np.int16)).view(torch.bfloat16).double().numpy()
