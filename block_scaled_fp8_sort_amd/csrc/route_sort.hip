@@ -322,7 +322,6 @@ __device__ __forceinline__ void sort_one_workgroup(const int32_t* __restrict__ i
                                                    int32_t* __restrict__ invalid_count) {
   extern __shared__ int32_t hist[];  // [kSortWaves][E + 1], then the key totals [E + 1]
   __shared__ int32_t s_invalid;
-  __shared__ int32_t s_scan[kSortThreads];
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
@@ -355,24 +354,27 @@ __device__ __forceinline__ void sort_one_workgroup(const int32_t* __restrict__ i
     total[e] = t;
   }
   __syncthreads();
-  // exclusive scan of total[0..K1) in blocks of kSortThreads
-  int carry = 0;
-  for (int base = 0; base < K1; base += kSortThreads) {
-    const int e = base + tid;
-    const int v = e < K1 ? total[e] : 0;
-    s_scan[tid] = v;
-    __syncthreads();
-    for (int d = 1; d < kSortThreads; d <<= 1) {
-      const int add = tid >= d ? s_scan[tid - d] : 0;
-      __syncthreads();
-      s_scan[tid] += add;
-      __syncthreads();
+  // exclusive scan of total[0..K1) by wave 0 alone (K1 <= 513: at most 9
+  // entries per lane, then a shuffle scan of the lane sums), with no workgroup
+  // barrier inside
+  if (wave == 0) {
+    const int per = (K1 + kWave - 1) / kWave;
+    const int e0 = lane * per;
+    int lsum = 0;
+    for (int i = 0; i < per; ++i)
+      if (e0 + i < K1) lsum += total[e0 + i];
+    int incl = lsum;
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int o = __shfl_up(incl, d, kWave);
+      if (lane >= d) incl += o;
     }
-    const int incl = s_scan[tid];
-    const int block_sum = s_scan[kSortThreads - 1];
-    __syncthreads();
-    if (e < K1) total[e] = carry + incl - v;  // exclusive prefix
-    carry += block_sum;
+    int run = incl - lsum;
+    for (int i = 0; i < per; ++i)
+      if (e0 + i < K1) {
+        const int v = total[e0 + i];
+        total[e0 + i] = run;
+        run += v;
+      }
   }
   __syncthreads();
   for (int e = tid; e < K1; e += kSortThreads) {
