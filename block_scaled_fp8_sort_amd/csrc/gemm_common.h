@@ -16,6 +16,44 @@ __device__ __forceinline__ void raw_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Exclusive prefix sums over the block of one (x, y) pair per thread, and the
+// block totals: a shuffle scan inside each wave, the wave totals through LDS
+// (wsum, 2 * THREADS / 64 ints), one barrier.  wsum may be reused after the
+// caller's next barrier.
+template <int THREADS>
+__device__ __forceinline__ void block_scan2(int x, int y, int* wsum, int& ex_x, int& ex_y, int& tot_x,
+                                            int& tot_y) {
+  constexpr int W = THREADS / 64;
+  const int lane = threadIdx.x % 64, w = threadIdx.x / 64;
+  int ix = x, iy = y;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int ox = __shfl_up(ix, d, 64);
+    const int oy = __shfl_up(iy, d, 64);
+    if (lane >= d) {
+      ix += ox;
+      iy += oy;
+    }
+  }
+  if (lane == 63) {
+    wsum[w] = ix;
+    wsum[W + w] = iy;
+  }
+  __syncthreads();
+  int bx = 0, by = 0, tx = 0, ty = 0;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    const int sx = wsum[i], sy = wsum[W + i];
+    bx += i < w ? sx : 0;
+    by += i < w ? sy : 0;
+    tx += sx;
+    ty += sy;
+  }
+  ex_x = bx + ix - x;
+  ex_y = by + iy - y;
+  tot_x = tx;
+  tot_y = ty;
+}
+
 // Tile table in LDS: off[e] = expert offsets, tp[e] = first tile of expert e,
 // where expert e has ceil(rows_e / BM) m-tiles times NT n-tiles (in the order
 // of tile_position); tp[E] = total.  All threads of the block must call it.
@@ -29,22 +67,13 @@ __device__ __forceinline__ int build_tile_table(const int32_t* offsets, int E, i
   const int e_lo = min(E, tid * seg), e_hi = min(E, tid * seg + seg);
   int mine = 0;
   for (int e = e_lo; e < e_hi; ++e) mine += ((off[e + 1] - off[e] + BM - 1) / BM) * NT;
-  scan[tid] = mine;
-  __syncthreads();
-  for (int d = 1; d < THREADS; d <<= 1) {
-    const int v = tid >= d ? scan[tid - d] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
+  int run, unused, total, unused_t;
+  block_scan2<THREADS>(mine, 0, scan, run, unused, total, unused_t);
+  for (int e = e_lo; e < e_hi; ++e) {
+    tp[e] = run;
+    run += ((off[e + 1] - off[e] + BM - 1) / BM) * NT;
   }
-  {
-    int run = scan[tid] - mine;
-    for (int e = e_lo; e < e_hi; ++e) {
-      tp[e] = run;
-      run += ((off[e + 1] - off[e] + BM - 1) / BM) * NT;
-    }
-    if (tid == THREADS - 1) tp[E] = scan[THREADS - 1];
-  }
+  if (tid == 0) tp[E] = total;
   __syncthreads();
   return tp[E];
 }
@@ -125,28 +154,18 @@ __device__ __forceinline__ int build_tile_table2(const int32_t* offsets, int E, 
     mine.x += full_m_tiles(rows) * NT;
     mine.y += has_short_tile(rows);
   }
-  scan[tid] = mine;
-  __syncthreads();
-  for (int d = 1; d < THREADS; d <<= 1) {
-    const int2 v = tid >= d ? scan[tid - d] : make_int2(0, 0);
-    __syncthreads();
-    scan[tid].x += v.x;
-    scan[tid].y += v.y;
-    __syncthreads();
+  int run0, run1, tot0, tot1;
+  block_scan2<THREADS>(mine.x, mine.y, reinterpret_cast<int*>(scan), run0, run1, tot0, tot1);
+  for (int e = e_lo; e < e_hi; ++e) {
+    const int rows = off[e + 1] - off[e];
+    tp[e] = run0;
+    cnt[e] = (uint16_t)run1;
+    run0 += full_m_tiles(rows) * NT;
+    run1 += has_short_tile(rows);
   }
-  {
-    int run0 = scan[tid].x - mine.x, run1 = scan[tid].y - mine.y;
-    for (int e = e_lo; e < e_hi; ++e) {
-      const int rows = off[e + 1] - off[e];
-      tp[e] = run0;
-      cnt[e] = (uint16_t)run1;
-      run0 += full_m_tiles(rows) * NT;
-      run1 += has_short_tile(rows);
-    }
-    if (tid == THREADS - 1) {
-      tp[E] = scan[THREADS - 1].x;
-      cnt[E] = (uint16_t)scan[THREADS - 1].y;
-    }
+  if (tid == 0) {
+    tp[E] = tot0;
+    cnt[E] = (uint16_t)tot1;
   }
   __syncthreads();
   return tp[E] + (int)cnt[E] * NT;
