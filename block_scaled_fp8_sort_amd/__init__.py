@@ -265,8 +265,9 @@ def prepare_weights(gate_up: torch.Tensor, gate_up_scale: torch.Tensor, down: to
 
     FP8_B128: gate_up uint8 [E, 2I, H] (or [E, H, 2I] when transposed), fp32 scales
     per 128x128 block; down uint8 [E, H, I].  MX: int8/uint8 packed e2m1
-    [E, 2I, H/2] and [E, H, I/2] with uint8 UE8M0 scales per 1x32.  BF16:
-    bfloat16 [E, 2I, H] and [E, H, I], no scales (pass None).
+    [E, 2I, H/2] and [E, H, I/2] with uint8 UE8M0 scales per 1x32 (nt only).
+    BF16: bfloat16 [E, 2I, H] and [E, H, I] (or [E, H, 2I] and [E, I, H] when
+    transposed), no scales (pass None).
     """
     lib = load_library()
     dev = gate_up.device
@@ -281,9 +282,7 @@ def prepare_weights(gate_up: torch.Tensor, gate_up_scale: torch.Tensor, down: to
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     E = gate_up.shape[0]
-    if fmt == FMT_BF16:
-        H, I2 = gate_up.shape[2], gate_up.shape[1]
-    elif fmt == FMT_FP8_B128:
+    if fmt in (FMT_BF16, FMT_FP8_B128):
         H, I2 = (gate_up.shape[1], gate_up.shape[2]) if transposed else (gate_up.shape[2], gate_up.shape[1])
     else:
         H, I2 = gate_up.shape[2] * 2, gate_up.shape[1]

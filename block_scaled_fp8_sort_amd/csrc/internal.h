@@ -95,7 +95,7 @@ hipError_t launch_tile_weight_mx(const uint8_t* codes, const uint8_t* scales, bo
                                  int32_t K, uint8_t* dst_codes, uint8_t* dst_scales, hipStream_t stream);
 // bf16 weights [E, N, K] (N % 16 == 0, K % 64 == 0) into the operand order of
 // the bf16 grouped GEMM (see gemm_bf16.hip).
-hipError_t launch_tile_weight_bf16(const uint16_t* src, int32_t E, int32_t N, int32_t K, uint16_t* dst,
+hipError_t launch_tile_weight_bf16(const uint16_t* src, bool nn, int32_t E, int32_t N, int32_t K, uint16_t* dst,
                                    hipStream_t stream);
 hipError_t launch_transpose_u8(const uint8_t* in, uint8_t* out, int32_t batch, int32_t rows, int32_t cols,
                                hipStream_t stream);

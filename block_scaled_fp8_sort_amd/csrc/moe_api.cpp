@@ -516,8 +516,8 @@ moe_status moe_prepare_weights(moe_format fmt, moe_layout layout, int32_t E, int
   const bool bf = fmt == MOE_FMT_BF16;
   if (!gate_up || !down || (!bf && (!gate_up_scale || !down_scale)))
     return fail(MOE_ERR_NULL, "a weight pointer is NULL");
-  if (layout == MOE_LAYOUT_NN && fmt != MOE_FMT_FP8_B128)
-    return fail(MOE_ERR_UNSUPPORTED, "the nn layout is accepted for FP8_B128 weights only");
+  if (layout == MOE_LAYOUT_NN && fmt == MOE_FMT_MXFP8A_MXFP4W)
+    return fail(MOE_ERR_UNSUPPORTED, "the nn layout is accepted for FP8_B128 and BF16 weights only");
   if (!prepared) return fail(MOE_ERR_NULL, "prepared buffer is NULL");
   const size_t need = moe_prepared_weights_size(fmt, E, H, I);
   if (prepared_bytes < need)
@@ -532,9 +532,10 @@ moe_status moe_prepare_weights(moe_format fmt, moe_layout layout, int32_t E, int
     uint8_t* q13 = (uint8_t*)prepared;
     uint8_t* q2 = q13 + align_up(e * 2 * i * h * 2, A);
     hipError_t he;
-    if ((he = moe::launch_tile_weight_bf16((const uint16_t*)gate_up, E, 2 * I, H, (uint16_t*)q13, stream)) !=
+    const bool nn = layout == MOE_LAYOUT_NN;
+    if ((he = moe::launch_tile_weight_bf16((const uint16_t*)gate_up, nn, E, 2 * I, H, (uint16_t*)q13, stream)) !=
             hipSuccess ||
-        (he = moe::launch_tile_weight_bf16((const uint16_t*)down, E, H, I, (uint16_t*)q2, stream)) != hipSuccess)
+        (he = moe::launch_tile_weight_bf16((const uint16_t*)down, nn, E, H, I, (uint16_t*)q2, stream)) != hipSuccess)
       return hip_status(he, "weight tiling");
     moe_weights w{};
     w.fmt = fmt;

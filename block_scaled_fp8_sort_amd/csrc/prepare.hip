@@ -170,13 +170,14 @@ hipError_t launch_tile_weight_mx(const uint8_t* codes, const uint8_t* scales, bo
 
 namespace {
 
-// bf16 weights [E, N, K] -> MFMA operand order for the bf16 grouped GEMM: for
-// each 16-row group and 64-element K stage, a 2 KB block holding the two
-// 32-element sub-steps, each as the 64 lanes' 16-byte fragments in lane order
-// (lane = 16 * (k % 32 / 8) + row % 16), so one wave-wide load reads 1 KB
-// contiguous.  One thread moves one 16-byte chunk (8 elements).
-__global__ __launch_bounds__(256) void tile_weight_bf16_kernel(const uint4* __restrict__ src, int32_t N, int32_t K,
-                                                               int64_t chunks, uint4* __restrict__ dst) {
+// bf16 weights [E, N, K] (nt) or [E, K, N] (nn) -> MFMA operand order for the
+// bf16 grouped GEMM: for each 16-row group and 64-element K stage, a 2 KB block
+// holding the two 32-element sub-steps, each as the 64 lanes' 16-byte fragments
+// in lane order (lane = 16 * (k % 32 / 8) + row % 16), so one wave-wide load
+// reads 1 KB contiguous.  One thread fills one 16-byte chunk (8 consecutive k of
+// one row n): one load from an nt row, eight 2-byte loads down an nn column.
+__global__ __launch_bounds__(256) void tile_weight_bf16_kernel(const uint16_t* __restrict__ src, int nn, int32_t N,
+                                                               int32_t K, int64_t chunks, uint4* __restrict__ dst) {
   const int64_t kc = K / 8;  // chunks per row
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks; c += (int64_t)gridDim.x * blockDim.x) {
     const int64_t row = c / kc;  // e * N + n
@@ -185,18 +186,27 @@ __global__ __launch_bounds__(256) void tile_weight_bf16_kernel(const uint4* __re
     const int n = (int)(row - e * N);
     const int stage = k0 / 64, ks = (k0 % 64) / 32, g = (k0 % 32) / 8;
     const int64_t block = (e * (N / 16) + n / 16) * (K / 64) + stage;
-    dst[block * 128 + ks * 64 + g * 16 + n % 16] = src[c];
+    uint4 v;
+    if (!nn) {
+      v = reinterpret_cast<const uint4*>(src)[c];
+    } else {
+      const uint16_t* col = src + (e * K + k0) * (int64_t)N + n;
+      uint32_t w[4];
+      for (int j = 0; j < 4; ++j) w[j] = (uint32_t)col[(2 * j) * (int64_t)N] | ((uint32_t)col[(2 * j + 1) * (int64_t)N] << 16);
+      v = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    dst[block * 128 + ks * 64 + g * 16 + n % 16] = v;
   }
 }
 
 }  // namespace
 
-hipError_t launch_tile_weight_bf16(const uint16_t* src, int32_t E, int32_t N, int32_t K, uint16_t* dst,
+hipError_t launch_tile_weight_bf16(const uint16_t* src, bool nn, int32_t E, int32_t N, int32_t K, uint16_t* dst,
                                    hipStream_t stream) {
   const int64_t chunks = (int64_t)E * N * (K / 8);
   int64_t blocks = (chunks + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(tile_weight_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const uint4*)src, N, K,
+  hipLaunchKernelGGL(tile_weight_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src, nn ? 1 : 0, N, K,
                      chunks, (uint4*)dst);
   return hipGetLastError();
 }

@@ -194,8 +194,9 @@ typedef struct moe_weights {
  *  for NN.
  *  MX (NT only): gate_up packed e2m1 [E, 2I, H/2] (even k in the low nibble),
  *  down packed [E, H, I/2]; UE8M0 scales uint8 [E, 2I, H/32] and [E, H, I/32].
- *  BF16 (NT only): gate_up bf16 [E, 2I, H], down bf16 [E, H, I]; both scale
- *  pointers are ignored and may be NULL (the descriptor's are NULL).
+ *  BF16: bf16 values, gate_up [E, 2I, H] and down [E, H, I] for NT, [E, H, 2I]
+ *  and [E, I, H] for NN; both scale pointers are ignored and may be NULL (the
+ *  descriptor's are NULL).
  * The tiled copy goes to `prepared` (device, at least moe_prepared_weights_size()
  * bytes, owned by the caller); `out` is filled on the host.  Enqueued on
  * `stream`.  Weight quantization itself is offline (the checkpoint's). */

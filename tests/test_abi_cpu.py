@@ -243,8 +243,12 @@ def test_bf16_format_on_the_host(lib):
     assert lib.moe_prepared_weights_size(2, 3, 384, 128) == 3 * 256 * 384 * 2 + 3 * 384 * 128 * 2
     desc = moe.MoeWeights()
     p = ctypes.c_void_p(4096)
-    # the nn layout is refused for bf16, like MX; scale pointers may be NULL
-    assert lib.moe_prepare_weights(2, 1, 4, 256, 128, p, None, p, None, p, 1 << 30, ctypes.byref(desc), None) == UNSUP
+    # the nn layout is refused for MX only; bf16 scale pointers may be NULL (with
+    # no GPU here, both bf16 layouts get as far as the device check)
+    assert lib.moe_prepare_weights(1, 1, 4, 256, 128, p, p, p, p, p, 1 << 30, ctypes.byref(desc), None) == UNSUP
+    for layout in (0, 1):
+        assert lib.moe_prepare_weights(2, layout, 4, 256, 128, p, None, p, None, p, 1 << 30, ctypes.byref(desc),
+                                       None) not in (UNSUP, NULL)
     assert lib.moe_prepare_weights(0, 0, 4, 256, 128, p, None, p, None, p, 1 << 30, ctypes.byref(desc), None) == NULL
     # the forward's workspace holds no activation codes for bf16 but h in bf16
     w8, wb = _weights(fmt=0), _weights(fmt=2)

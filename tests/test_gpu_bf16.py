@@ -130,6 +130,22 @@ def test_bf16_forward_invariants():
     assert torch.count_nonzero(z.view(torch.int16)).item() == 0
 
 
+def test_bf16_prepare_nn_layout_matches_nt():
+    """bf16 weights given transposed ([E, H, 2I] and [E, I, H]) prepare to the
+    same bytes as the nt layout, so the forward is bit-identical."""
+    wl = _wl("bf16_nn", T=96, H=384, I=256, E=3, k=2, seed=59)
+    inp = W.inputs(wl, DEV)
+    w_nt = moe.prepare_weights(inp["w13"], None, inp["w2"], None, fmt=BF16)
+    w_nn = moe.prepare_weights(inp["w13"].transpose(1, 2).contiguous(), None, inp["w2"].transpose(1, 2).contiguous(),
+                               None, fmt=BF16, transposed=True)
+    torch.cuda.synchronize()
+    assert torch.equal(w_nt._keep[0], w_nn._keep[0])
+    a = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w_nt).clone()
+    b = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w_nn)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 def test_bf16_forward_from_logits():
     wl = _wl("bf16_logits", T=96, H=512, I=256, E=16, k=4, seed=55)
     inp = W.inputs(wl, DEV)
