@@ -4,7 +4,8 @@
 // cannot take precomputed scales ("grouped_mm experts dispatch does not support
 // activation_scheme='static'", section "What it means").  Block rule:
 //  FP8_B128 (blocks of 128): s = max(amax, 1e-4) / 448 (fp32), code = e4m3(x / s)
-//  with an IEEE fp32 division, so codes match a host implementation bit for bit.
+//  with x / s the IEEE fp32 quotient, so codes match a host implementation bit
+//  for bit (computed from one reciprocal per block, see quant_chunk).
 //  MX (blocks of 32): s = 2^e, e = ceil(log2(max(amax, 1e-4) / 448)) from the
 //  fp32 bits, stored as the byte e + 127; code = e4m3(x * 2^-e), exact scaling.
 //

@@ -17,24 +17,24 @@
 //     lane then advances start[w][key].  Order inside a key is therefore slot
 //     order, as a stable sort requires.
 // Small inputs (decode) run all three steps in one workgroup.  Large inputs
-// split the slots over up to kMaxChunks wave-sized chunks in three launches:
+// split the slots over up to kMaxChunks chunks of at least 256 slots, one wave
+// each, in three launches:
 //  A. each wave histograms its chunk and writes it key-major, hist[key][chunk];
-//  B. one workgroup turns hist into its flat exclusive prefix sum, which is
-//     exactly start[key][chunk] (all smaller keys, then the same key in earlier
-//     chunks), and reads offsets[e] off start[e][0]; the chunk count is capped
-//     so that hist fits in LDS, where the scan runs;
-//  C. each wave loads its starts and runs step 3 above on its chunk.
+//  B. one wave per key turns its row into the exclusive prefix over the chunks
+//     and writes the row total;
+//  C. each wave scans the E + 1 totals into offsets[key], so that its start is
+//     offsets[key] + hist[key][chunk] (all smaller keys, then the same key in
+//     earlier chunks), and runs step 3 above on its chunk.
 // The result is the same unique permutation in both cases.
 //
-// Router (optional, in front of the sort): each token's top-k is taken by a
-// group of G lanes, G the next power of two >= E capped at 64, each lane
-// holding up to 8 of the token's logits (expert e in lane e % G).  Softmax is
-// increasing in the logit, so the k most probable experts are the k largest
-// logits; k rounds of an in-group (value, id) max-reduction, lower id on equal
-// values, pick them in descending order.  Weights are exp(l - max) over the sum
-// of the same terms, taken over all E (plain softmax) or over the k chosen
-// (renormalised), in fp32.  Small batches run the router in the sort's own
-// workgroup before it sorts; large ones run it as a launch of its own.
+// Router (optional, in front of the sort): each token's top-k is taken by one
+// DPP row of 16 lanes, lane i holding the token's logits i, i + 16, ...
+// Softmax is increasing in the logit, so the k most probable experts are the k
+// largest logits; k rounds of an in-row (value, id) max-reduction, lower id on
+// equal values, pick them in descending order.  Weights are exp(l - max) over
+// the sum of the same terms, taken over all E (plain softmax) or over the k
+// chosen (renormalised), in fp32.  Small batches run the router in the sort's
+// own workgroup before it sorts; large ones run it as a launch of its own.
 #include "device_common.h"
 #include "internal.h"
 #include "quant_act.h"
@@ -46,12 +46,10 @@ namespace {
 constexpr int kSortWaves = 16;
 constexpr int kSortThreads = kSortWaves * kWave;
 
-constexpr int kMaxChunks = 256;       // chunks (one wave each) of the multi-block path
-constexpr int kScanInts = 32768;      // (E + 1) * chunks, at most: the scan runs in LDS
+constexpr int kMaxChunks = 2048;      // chunks (one wave each) of the multi-block path, at most
 constexpr int kMinChunk = 256;        // slots per chunk, at least
 constexpr int kMultiBlockFrom = 16384;  // S at which the multi-block path takes over
-constexpr int kChunkWaves = 4;        // waves per workgroup in steps A and C
-constexpr int kScanThreads = 1024;
+constexpr int kChunkWaves = 4;        // waves per workgroup in the three steps
 
 __device__ __forceinline__ int sort_key(int32_t id, int32_t E, int32_t expert_begin) {
   const int64_t local = (int64_t)id - expert_begin;
@@ -231,86 +229,83 @@ __global__ __launch_bounds__(kChunkWaves * kWave) void sort_hist_kernel(const in
     for (int e = lane; e < K2; e += kWave) hist[(size_t)e * n_chunks + c] = lh[wl * K2 + e];
 }
 
-// Step B: in-place exclusive prefix sum of hist[0 .. (E+1) n_chunks), offsets,
-// and the invalid total (row E + 1, not part of the scan).  hist moves through
-// LDS with coalesced, unrolled loads and stores.
-__global__ __launch_bounds__(kScanThreads) void sort_scan_kernel(int32_t E, int32_t n_chunks,
-                                                                int32_t* __restrict__ hist,
-                                                                int32_t* __restrict__ offsets,
-                                                                int32_t* __restrict__ invalid_count) {
-  __shared__ int32_t buf[kScanInts];
-  __shared__ int32_t part[kScanThreads];
-  __shared__ int32_t s_bad;
-  constexpr int U = 8;
-  const int tid = threadIdx.x;
-  const int n = (E + 1) * n_chunks;
-  for (int i0 = 0; i0 < n; i0 += U * kScanThreads) {
-    int32_t v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * kScanThreads + tid;
-      v[u] = i < n ? hist[i] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * kScanThreads + tid;
-      if (i < n) buf[i] = v[u];
-    }
+// Exclusive prefix sum over the wave of one value per lane, and the wave total.
+__device__ __forceinline__ int wave_exclusive_scan(int v, int lane, int& total) {
+  int incl = v;
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += o;
   }
-  if (tid == 0) s_bad = 0;
-  __syncthreads();
-  const int seg = (n + kScanThreads - 1) / kScanThreads;
-  const int lo = min(n, tid * seg), hi = min(n, lo + seg);
-  int sum = 0;
-  for (int i = lo; i < hi; ++i) sum += buf[i];
-  part[tid] = sum;
-  __syncthreads();
-  for (int d = 1; d < kScanThreads; d <<= 1) {
-    const int add = tid >= d ? part[tid - d] : 0;
-    __syncthreads();
-    part[tid] += add;
-    __syncthreads();
-  }
-  int run = part[tid] - sum;
-  for (int i = lo; i < hi; ++i) {
-    const int v = buf[i];
-    buf[i] = run;
-    run += v;
-  }
-  __syncthreads();
-  for (int i = tid; i < n; i += kScanThreads) {
-    hist[i] = buf[i];
-    if (i % n_chunks == 0) offsets[i / n_chunks] = buf[i];
-  }
-  if (invalid_count) {
-    int bad = 0;
-    for (int c = tid; c < n_chunks; c += kScanThreads) bad += hist[(size_t)(E + 1) * n_chunks + c];
-    if (bad) atomicAdd(&s_bad, bad);
-    __syncthreads();
-    if (tid == 0) invalid_count[0] = s_bad;
-  }
+  total = __shfl(incl, kWave - 1, kWave);
+  return incl - v;
 }
 
-// Step C: each wave scatters its chunk from its row of starts.
+// Step B: one wave per row e of hist (keys 0..E and the invalid row E + 1):
+// the row becomes its exclusive prefix sum over the chunks, in place, and its
+// total goes to totals[e].
+__global__ __launch_bounds__(kChunkWaves * kWave) void sort_rowscan_kernel(int32_t E, int32_t n_chunks,
+                                                                          int32_t* __restrict__ hist,
+                                                                          int32_t* __restrict__ totals) {
+  const int lane = threadIdx.x % kWave;
+  const int e = blockIdx.x * kChunkWaves + threadIdx.x / kWave;
+  if (e > E + 1) return;  // whole waves only; no workgroup barrier here
+  int32_t* row = hist + (size_t)e * n_chunks;
+  int run = 0;
+  for (int c0 = 0; c0 < n_chunks; c0 += kWave) {
+    const int c = c0 + lane;
+    const int v = c < n_chunks ? row[c] : 0;
+    int sum;
+    const int ex = wave_exclusive_scan(v, lane, sum);
+    if (c < n_chunks) row[c] = run + ex;
+    run += sum;
+  }
+  if (lane == 0) totals[e] = run;
+}
+
+// Step C: each wave scans the key totals itself (E + 1 values: a few per lane,
+// then a shuffle scan), adds its chunk's row prefix to get its start per key,
+// and scatters its chunk.  Chunk 0's wave also writes the offsets and the
+// invalid count.
 __global__ __launch_bounds__(kChunkWaves * kWave) void sort_scatter_kernel(
     const int32_t* __restrict__ ids, int32_t S, int32_t E, int32_t expert_begin, int32_t chunk, int32_t n_chunks,
-    const int32_t* __restrict__ start, int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos) {
+    const int32_t* __restrict__ start, const int32_t* __restrict__ totals, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ invalid_count, int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos) {
   extern __shared__ int32_t ls[];  // [kChunkWaves][E + 1]
   const int K1 = E + 1;
   const int wl = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int c = blockIdx.x * kChunkWaves + wl;
   if (c >= n_chunks) return;  // whole waves only; no workgroup barrier follows
-  for (int e = lane; e < K1; e += kWave) ls[wl * K1 + e] = start[(size_t)e * n_chunks + c];
+  int32_t* my = ls + wl * K1;
+  const int per = (K1 + kWave - 1) / kWave;
+  const int e0 = lane * per;
+  int lsum = 0;
+  for (int i = 0; i < per; ++i)
+    if (e0 + i < K1) {
+      const int t = totals[e0 + i];
+      my[e0 + i] = t;
+      lsum += t;
+    }
+  int unused;
+  int run = wave_exclusive_scan(lsum, lane, unused);
+  for (int i = 0; i < per; ++i)
+    if (e0 + i < K1) {
+      const int t = my[e0 + i];
+      my[e0 + i] = run;
+      if (c == 0) offsets[e0 + i] = run;
+      run += t;
+    }
+  if (c == 0 && lane == 0 && invalid_count) invalid_count[0] = totals[K1];
+  __builtin_amdgcn_wave_barrier();
+  for (int e = lane; e < K1; e += kWave) my[e] += start[(size_t)e * n_chunks + c];
   __builtin_amdgcn_wave_barrier();
   const int c_begin = min(S, c * chunk), c_end = min(S, c_begin + chunk);
-  scatter_chunk(ids, c_begin, c_end, E, expert_begin, ls + wl * K1, sorted_slot, slot_pos);
+  scatter_chunk(ids, c_begin, c_end, E, expert_begin, my, sorted_slot, slot_pos);
 }
 
 // Chunk size of the multi-block path: at least kMinChunk, a multiple of the
-// wave size, and few enough chunks that (E + 1) * chunks <= kScanInts.
-int32_t sort_chunk(int32_t S, int32_t E) {
-  const int64_t max_chunks = kScanInts / (E + 1) < kMaxChunks ? kScanInts / (E + 1) : kMaxChunks;
-  int64_t c = ((int64_t)S + max_chunks - 1) / max_chunks;
+// wave size, and at most kMaxChunks chunks.
+int32_t sort_chunk(int32_t S) {
+  int64_t c = ((int64_t)S + kMaxChunks - 1) / kMaxChunks;
   c = (c + kWave - 1) / kWave * kWave;
   return (int32_t)(c < kMinChunk ? kMinChunk : c);
 }
@@ -444,9 +439,9 @@ size_t route_sort_lds_bytes(int32_t E) { return sizeof(int32_t) * (size_t)(kSort
 
 size_t route_sort_ws_bytes(int32_t S, int32_t E) {
   if (S < kMultiBlockFrom) return 0;
-  const int32_t chunk = sort_chunk(S, E);
+  const int32_t chunk = sort_chunk(S);
   const size_t n_chunks = ((size_t)S + chunk - 1) / chunk;
-  return sizeof(int32_t) * (size_t)(E + 2) * n_chunks;
+  return sizeof(int32_t) * (size_t)(E + 2) * (n_chunks + 1);  // hist rows, then the row totals
 }
 
 namespace {
@@ -514,18 +509,19 @@ hipError_t launch_route_sort_zero(const RouterArgs* router, const int32_t* ids, 
     hipError_t e = launch_router(*router, T, k, stream);
     if (e != hipSuccess) return e;
   }
-  const int32_t chunk = sort_chunk(S, E);
+  const int32_t chunk = sort_chunk(S);
   const int32_t n_chunks = (S + chunk - 1) / chunk;
   const int blocks = (n_chunks + kChunkWaves - 1) / kChunkWaves;
-  int32_t* hist = (int32_t*)ws;
+  int32_t* hist = (int32_t*)ws;                         // [E + 2][n_chunks]
+  int32_t* totals = hist + (size_t)(E + 2) * n_chunks;  // [E + 2]
   hipLaunchKernelGGL(sort_hist_kernel, dim3(blocks), dim3(kChunkWaves * kWave),
                      sizeof(int32_t) * kChunkWaves * (E + 2), stream, ids, S, E, expert_begin, chunk, n_chunks, hist,
                      zero, n_zero);
-  hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, E, n_chunks, hist, offsets,
-                     invalid_count);
+  hipLaunchKernelGGL(sort_rowscan_kernel, dim3((E + 2 + kChunkWaves - 1) / kChunkWaves), dim3(kChunkWaves * kWave), 0,
+                     stream, E, n_chunks, hist, totals);
   hipLaunchKernelGGL(sort_scatter_kernel, dim3(blocks), dim3(kChunkWaves * kWave),
                      sizeof(int32_t) * kChunkWaves * (E + 1), stream, ids, S, E, expert_begin, chunk, n_chunks, hist,
-                     sorted_slot, slot_pos);
+                     totals, offsets, invalid_count, sorted_slot, slot_pos);
   return hipGetLastError();
 }
 

@@ -59,13 +59,16 @@ def test_route_sort_refusals(lib):
 
 def test_route_sort_workspace(lib):
     # one workgroup below 16384 slots (no workspace); above, per-chunk
-    # histograms of E + 2 rows over at most 256 chunks
+    # histograms of E + 2 rows over at most 2048 chunks of at least 256 slots,
+    # and the E + 2 row totals
     assert lib.moe_route_sort_workspace(64, 8, 128) == 0
     assert lib.moe_route_sort_workspace(16383, 1, 8) == 0
-    assert lib.moe_route_sort_workspace(2048, 8, 256) == 4 * 258 * 64  # 64 chunks of 256 slots
-    for T, k, E in [(8192, 8, 256), (16384, 8, 256), (40000, 8, 512), (1 << 26, 16, 512)]:
+    assert lib.moe_route_sort_workspace(2048, 8, 256) == 4 * 258 * (64 + 1)  # 64 chunks of 256 slots
+    assert lib.moe_route_sort_workspace(8192, 8, 256) == 4 * 258 * (256 + 1)
+    assert lib.moe_route_sort_workspace(65536, 8, 256) == 4 * 258 * (2048 + 1)  # 2048 chunks of 256
+    for T, k, E in [(16384, 8, 256), (40000, 8, 512), (1 << 26, 16, 512)]:
         ws = lib.moe_route_sort_workspace(T, k, E)
-        assert 0 < ws <= 4 * (E + 2) * 256
+        assert 0 < ws <= 4 * (E + 2) * (2048 + 1)
     assert lib.moe_route_sort_workspace(-1, 8, 8) == 0
     p = ctypes.c_void_p(16)
     assert lib.moe_route_sort(p, 2048, 8, 256, 0, ctypes.c_void_p(64), p, None, None, None, 0, None) == WS
