@@ -17,7 +17,7 @@
 // [16 g, 16 g + 16) in bytes 0-15 and [64 + 16 g, 64 + 16 g + 16) in bytes 16-31;
 // the scale byte of lane group g applies to K elements [32 g, 32 g + 32).
 // Tiles: 256 weight rows x BM tokens x 128 K (BM = 256, or 64 / 128 / 256 for an
-// expert's last, partial m-tile), eight waves (2 x 4), two or four LDS stages
+// expert's last, partial m-tile), eight waves (2 x 4), three or four LDS stages
 // fed by LDS-DMA from the tiled weights (64-byte rows) and the K-block-major
 // activations; persistent XCD-aware tile walk and staged, whole-row epilogue
 // stores as in the FP8 kernel.
@@ -58,15 +58,16 @@ struct Misc {
   int2 scan[kThreads];
 };
 
-// LDS shared by the pipeline stages of every tile height: four stages of the
-// 128-row layout, which also hold two of the 256-row one (a third would spill
-// registers) and four of the 64-row one.
-constexpr int kStageArea = 4 * (int)sizeof(StageBuf<128>);
+// LDS shared by the pipeline stages of every tile height: three stages of the
+// 256-row layout (with the tile table, 159.8 of the 160 KiB), which also
+// hold four of the 128-row and of the 64-row one.  A third 256-row stage (two
+// before) took Mega-MoE's gate_up GEMM from 3.32 to 3.28 ms.
+constexpr int kStageArea = 3 * (int)sizeof(StageBuf<256>);
 template <int BM>
 constexpr int stages_for() {
   return kStageArea / (int)sizeof(StageBuf<BM>) < 4 ? kStageArea / (int)sizeof(StageBuf<BM>) : 4;
 }
-static_assert(stages_for<256>() == 2 && stages_for<64>() == 4, "stage area");
+static_assert(stages_for<256>() == 3 && stages_for<64>() == 4, "stage area");
 
 template <int BM>
 struct TileSrc {

@@ -80,6 +80,9 @@ SORT_CASES = [
     (333, 64, 5, 0.1, 0.1),
     # around and above the size where the sort switches to several workgroups
     (16383, 1, 7, 0.1, 0.0), (2048, 8, 256, 0.05, 0.01), (20000, 1, 1, 0.3, 0.1), (40000, 8, 512, 0.05, 0.02),
+    # past 2048 chunks of 256 slots: longer chunks (320 and 448 slots), a chunk
+    # count that is not a multiple of the four waves of a workgroup
+    (70000, 8, 256, 0.05, 0.01), (100000, 9, 512, 0.1, 0.01),
 ]
 
 
