@@ -245,6 +245,8 @@ moe_status forward_impl(const moe_weights* w, const uint16_t* hidden_states, con
       return fail(MOE_ERR_SHAPE, "n_experts=%d outside [1, %d]", router->n_experts, kMaxE);
     if (k > router->n_experts) return fail(MOE_ERR_SHAPE, "k=%d exceeds n_experts=%d", k, router->n_experts);
   }
+  if (w->fmt != MOE_FMT_BF16 && (int64_t)T * k * 128 >= (int64_t)1 << 31)
+    return fail(MOE_ERR_SHAPE, "T*k*128 must stay below 2^31 (32-bit row offsets in a K plane)");
   if (w->fmt == MOE_FMT_BF16 && ((int64_t)T * w->H * 2 >= (int64_t)1 << 32 ||
                                  (int64_t)T * k * w->I * 2 >= (int64_t)1 << 32))
     return fail(MOE_ERR_SHAPE, "bf16 experts: hidden_states and h must each stay below 4 GiB");

@@ -282,7 +282,10 @@ moe_status moe_grouped_gemm(const moe_gemm_args* args, hipStream_t stream);
  *  opt             may be NULL (no clamp, expert_begin 0).
  *  out             device bf16 [T, H] out.
  *  ws / ws_bytes   device workspace of at least moe_experts_forward_workspace().
- * T == 0 returns MOE_OK with nothing enqueued. */
+ * T == 0 returns MOE_OK with nothing enqueued.  Limits: 1 <= k <= 64 and, for
+ * the quantized formats, T*k*128 < 2^31 (the GEMMs address each 128-wide K
+ * plane of their row operands with 32-bit offsets; the bf16 limits are given
+ * with MOE_FMT_BF16); MOE_ERR_SHAPE otherwise. */
 typedef struct moe_debug {
   /* Optional device copies of intermediates, for parity checks; each may be NULL. */
   int32_t* sorted_slot;    /* [T*k] */

@@ -149,6 +149,11 @@ def test_forward_refusals(lib):
 
     assert fwd(T=0) == OK
     assert fwd(k=0) == SHAPE
+    # quantized formats: the rows of a 128-wide K plane are addressed with
+    # 32-bit offsets, so T*k*128 must stay below 2^31
+    assert fwd(T=1 << 21, k=8) == SHAPE
+    assert b"2^31" in lib.moe_last_error()
+    assert fwd(T=(1 << 21) - 1, k=8, ws=None) == WS  # one slot under the bound gets past the shape checks
     assert fwd(w=_weights(H=200)) == SHAPE
     assert fwd(w=_weights(I=64)) == SHAPE
     assert fwd(w=_weights(E=0)) == SHAPE
