@@ -47,7 +47,9 @@ def assert_weights_close(got, ref, logits, n_experts):
 # T, n_experts, k, renormalize, ties, local experts (E, expert_begin) or None = all
 ROUTER_CASES = [
     (1, 1, 1, True, False, None),
-    (64, 128, 8, True, False, None),        # decode: router inside the sort's workgroup
+    (16, 128, 8, True, True, None),         # small decode: router inside the sort's workgroup
+    (11, 100, 6, False, False, None),
+    (64, 128, 8, True, False, None),        # decode: router launch, then the one-workgroup sort
     (64, 128, 8, False, True, None),
     (4096, 8, 2, True, False, None),        # T * n_experts = 32768: still one workgroup
     (700, 100, 3, True, True, None),        # 70000 logits: router launch of its own, one-workgroup sort
@@ -98,7 +100,8 @@ def _workload(name, fmt, T, H, I, E, k, limit=None, seed=0):
 
 
 FWD_CASES = [
-    _workload("logits_decode_fp8", FP8, T=24, H=512, I=256, E=16, k=4, seed=31),       # fused route+sort+quant
+    _workload("logits_small_decode_fp8", FP8, T=16, H=512, I=256, E=16, k=4, seed=30),  # router+sort+quant in one launch
+    _workload("logits_decode_fp8", FP8, T=24, H=512, I=256, E=16, k=4, seed=31),       # router launch, fused sort+quant
     _workload("logits_ragged_fp8", FP8, T=300, H=384, I=256, E=6, k=3, seed=32),
     # 70000 logits: the router runs as a launch of its own (I = 256: with a single 128-wide h block a lone h-code
     # rounding flip, which the tolerance allows for, can exceed the max-norm bar at 21 rows per expert)
