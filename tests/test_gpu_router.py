@@ -195,6 +195,9 @@ EP_CASES = [
     _workload("ep_fp8_tiled", FP8, T=333, H=512, I=256, E=12, k=4, seed=41),
     _workload("ep_fp8_few_rows", FP8, T=40, H=512, I=256, E=32, k=4, seed=42),
     _workload("ep_mx_clamp", MX, T=250, H=256, I=256, E=8, k=3, limit=7.0, seed=43),
+    # 16800 slots: the whole batch takes the multi-workgroup sort (with a nonzero
+    # expert_begin in the expert-group test), the token slices the one-workgroup sort
+    _workload("ep_fp8_multiblock_sort", FP8, T=4200, H=256, I=128, E=16, k=4, seed=44),
 ]
 
 
