@@ -270,9 +270,14 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Mis
       const int ti = slot < BM ? slot % TS : 0;
       const int tr = (q / 16) * WM + ti * 16 + (q % 16);
       const int r = min(m0 + tr, m_end - 1);
-      const int arow = p.a_row_index ? p.a_row_index[r] / p.a_row_div : r;
-      src.s_base = (const float*)p.a_scales + arow;
-      src.s_stride = (uint32_t)p.a_rows;
+      if (p.a_scales_sorted) {  // by sorted row: the tile's scales are contiguous
+        src.s_base = (const float*)p.a_scales_sorted + r;
+        src.s_stride = (uint32_t)p.max_rows;
+      } else {
+        const int arow = p.a_row_index ? p.a_row_index[r] / p.a_row_div : r;
+        src.s_base = (const float*)p.a_scales + arow;
+        src.s_stride = (uint32_t)p.a_rows;
+      }
     }
   }
 

@@ -204,13 +204,19 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, int
     const int arow = p.a_row_index ? p.a_row_index[r] / p.a_row_div : r;
     src.a_off[q] = (uint32_t)arow * kARow + (uint32_t)(((lane & 7) ^ swz(tr)) << 4);
   }
-  src.as_base = (const uint8_t*)p.a_scales;
-  src.as_plane = (size_t)p.a_rows * 4;
   {
     const int tr = (wave % (BM / 64 > 0 ? BM / 64 : 1)) * 64 + lane;  // rows of the waves that load scales
     const int r = min(m0 + min(tr, BM - 1), m_end - 1);
-    const int arow = p.a_row_index ? p.a_row_index[r] / p.a_row_div : r;
-    src.as_off = (uint32_t)arow * 4;
+    if (p.a_scales_sorted) {  // by sorted row: the tile's scales are contiguous
+      src.as_base = (const uint8_t*)p.a_scales_sorted;
+      src.as_plane = (size_t)p.max_rows * 4;
+      src.as_off = (uint32_t)r * 4;
+    } else {
+      const int arow = p.a_row_index ? p.a_row_index[r] / p.a_row_div : r;
+      src.as_base = (const uint8_t*)p.a_scales;
+      src.as_plane = (size_t)p.a_rows * 4;
+      src.as_off = (uint32_t)arow * 4;
+    }
   }
 
   v4f acc[8][TS];

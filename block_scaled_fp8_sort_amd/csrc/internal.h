@@ -31,6 +31,10 @@ struct GemmParams {
   const int32_t* slot_of_row;
   // tile dispensing: NULL = static order, else 8 zeroed counters 128 bytes apart
   int32_t* sched;
+  // non-NULL: the activation scales by sorted row, [K/128][max_rows] floats
+  // (FP8) or [K/128][max_rows][4] bytes (MX), read instead of a_scales at the
+  // gathered rows (tiled FP8 and MX kernels)
+  const void* a_scales_sorted;
 };
 
 enum Epilogue { kEpiStoreF32 = 0, kEpiSwiGLUQuant = 1, kEpiWeightedScatter = 2 };
@@ -60,19 +64,28 @@ hipError_t launch_route_sort_zero(const RouterArgs* router, const int32_t* ids, 
                                   int32_t expert_begin, int32_t* sorted_slot, int32_t* offsets, int32_t* slot_pos,
                                   int32_t* invalid_count, void* ws, int32_t* zero, int32_t n_zero,
                                   hipStream_t stream);
-// The (router and) route sort, without slot_pos, and the activation
-// quantization of x [rows, H], in one launch for small batches, else one after
-// the other; the first kernel also sets zero[0 .. n_zero) to 0 (the GEMMs'
-// tile counters).
+// Whether S slots take the multi-workgroup sort (three launches, then the
+// quantization as a launch of its own).
+bool route_sort_multiblock(int32_t S);
+// The (router and) route sort and the activation quantization of x [rows, H],
+// in one launch for small batches, else one after the other; the first kernel
+// also sets zero[0 .. n_zero) to 0 (the GEMMs' tile counters).  With the
+// multi-workgroup sort and sorted_scales non-NULL, the scales are then also
+// copied by sorted row into sorted_scales (launch_gather_scales).
 hipError_t launch_route_sort_and_quant(const RouterArgs* router, const int32_t* ids, int32_t T, int32_t k, int32_t E,
                                       int32_t expert_begin, int32_t* sorted_slot, int32_t* offsets,
                                       int32_t* invalid_count, void* sort_ws, const uint16_t* x, int32_t rows,
                                       int32_t H, int fmt, uint8_t* codes, void* scales, int32_t* zero,
-                                      int32_t n_zero, hipStream_t stream);
+                                      int32_t n_zero, hipStream_t stream, void* sorted_scales = nullptr);
 // The router alone (no sort).
 hipError_t launch_router_only(const RouterArgs& router, int32_t T, int32_t k, hipStream_t stream);
 hipError_t launch_quant_act(const uint16_t* x, int32_t rows, int32_t H, int fmt, uint8_t* codes, void* scales,
                             hipStream_t stream);
+// The activation scales of T token rows ([H/128][T] fp32, or [H/128][T][4]
+// UE8M0 bytes) copied by sorted row: dst [H/128][T * k], row r taking token
+// sorted_slot[r] / k.
+hipError_t launch_gather_scales(const void* scales, const int32_t* sorted_slot, int32_t k, int32_t T, int32_t H,
+                                void* dst, hipStream_t stream);
 // epi: Epilogue; paired: gate/up row pairing of B (used with kEpiSwiGLUQuant and
 // optionally kEpiStoreF32 on the gate_up weight).
 hipError_t launch_gemm_fp8_b128(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream);

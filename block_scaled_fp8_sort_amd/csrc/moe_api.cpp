@@ -110,7 +110,11 @@ moe_status hip_status(hipError_t e, const char* what) {
 
 // ---------------------------------------------------------- forward workspace
 struct FwdLayout {
-  size_t sorted_slot, offsets, act_codes, act_scales, h_codes, h_scales, slot_out, sort_ws, sched, total;
+  size_t sorted_slot, offsets, act_codes, act_scales, h_codes, h_scales, slot_out, sort_ws, sched;
+  // with the multi-workgroup sort (quantized formats): the activation scales
+  // by sorted row, which the gate_up GEMM reads contiguously
+  bool sorted_scales;
+  size_t act_scales_sorted, total;
 };
 
 FwdLayout fwd_layout(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I, int fmt) {
@@ -129,6 +133,9 @@ FwdLayout fwd_layout(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I, int 
   L.slot_out = o; o = align_up(o + 2 * S * H, A);
   L.sort_ws = o; o = align_up(o + moe::route_sort_ws_bytes((int32_t)S, E), A);
   L.sched = o; o = align_up(o + 2 * MOE_TILE_COUNTERS_BYTES, A);  // gate_up's and down's tile counters
+  L.sorted_scales = !bf && moe::route_sort_multiblock((int32_t)S);
+  L.act_scales_sorted = o;
+  o = align_up(o + (!L.sorted_scales ? 0 : mx ? S * (H / 32) : 4 * S * (H / 128)), A);
   L.total = o;
   return L;
 }
@@ -298,7 +305,7 @@ moe_status forward_impl(const moe_weights* w, const uint16_t* hidden_states, con
     he = moe::launch_route_sort_and_quant(router, top_k_index, T, k, E, expert_begin, sorted_slot, offsets,
                                           opt ? opt->invalid_count : nullptr, base + L.sort_ws, hidden_states, T, H,
                                           w->fmt, act_codes, act_scales, sched, 2 * MOE_TILE_COUNTERS_BYTES / 4,
-                                          stream);
+                                          stream, L.sorted_scales ? base + L.act_scales_sorted : nullptr);
   if (he != hipSuccess) return hip_status(he, "route sort / quant launch");
 
   moe::GemmParams p1{};
@@ -319,6 +326,7 @@ moe_status forward_impl(const moe_weights* w, const uint16_t* hidden_states, con
   p1.h_scales = h_scales;
   p1.has_limit = has_limit ? 1 : 0;
   p1.limit = has_limit ? opt->swiglu_limit : 0.0f;
+  p1.a_scales_sorted = L.sorted_scales ? base + L.act_scales_sorted : nullptr;
   he = launch_gemm(p1, w->fmt, moe::kEpiSwiGLUQuant, true, cus, stream);
   if (he != hipSuccess) return hip_status(he, "gate_up gemm launch");
 

@@ -39,7 +39,35 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint4* __restrict_
     quant_chunk<BLOCK>(x, c, rows, H, codes, scales);
 }
 
+// The activation scales by sorted row: dst[kb][r] = scales[kb][sorted_slot[r] / k]
+// for every K block kb and sorted row r < S (fp32 scales, or the four UE8M0
+// bytes of a row's 128-wide block as one word).  Writes are contiguous over r;
+// the reads gather from the token scales, which stay in the L2.
+__global__ __launch_bounds__(256) void gather_scales_kernel(const uint32_t* __restrict__ scales,
+                                                            const int32_t* __restrict__ sorted_slot, int32_t k,
+                                                            int32_t T, int32_t S, int64_t n,
+                                                            uint32_t* __restrict__ dst) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const int64_t kb = i / S;
+    const int32_t r = (int32_t)(i - kb * S);
+    dst[i] = scales[kb * T + sorted_slot[r] / k];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gather_scales(const void* scales, const int32_t* sorted_slot, int32_t k, int32_t T, int32_t H,
+                                void* dst, hipStream_t stream) {
+  const int32_t S = T * k;
+  const int64_t n = (int64_t)(H / 128) * S;
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 256 * 32) blocks = 256 * 32;
+  hipLaunchKernelGGL(gather_scales_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const uint32_t*)scales,
+                     sorted_slot, k, T, S, n, (uint32_t*)dst);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_act(const uint16_t* x, int32_t rows, int32_t H, int fmt, uint8_t* codes, void* scales,
                             hipStream_t stream) {

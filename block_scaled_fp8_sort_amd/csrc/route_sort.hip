@@ -440,6 +440,8 @@ __global__ __launch_bounds__(kSortThreads) void route_quant_kernel(
 
 size_t route_sort_lds_bytes(int32_t E) { return sizeof(int32_t) * (size_t)(kSortWaves + 1) * (E + 1); }
 
+bool route_sort_multiblock(int32_t S) { return S >= kMultiBlockFrom; }
+
 size_t route_sort_ws_bytes(int32_t S, int32_t E) {
   if (S < kMultiBlockFrom) return 0;
   const int32_t chunk = sort_chunk(S);
@@ -532,7 +534,7 @@ hipError_t launch_route_sort_and_quant(const RouterArgs* router, const int32_t* 
                                       int32_t expert_begin, int32_t* sorted_slot, int32_t* offsets,
                                       int32_t* invalid_count, void* sort_ws, const uint16_t* x, int32_t rows,
                                       int32_t H, int fmt, uint8_t* codes, void* scales, int32_t* zero,
-                                      int32_t n_zero, hipStream_t stream) {
+                                      int32_t n_zero, hipStream_t stream, void* sorted_scales) {
   if (router && !router->logits) router = nullptr;
   const int32_t S = T * k;
   const int64_t n_chunks = (int64_t)rows * H / 8;
@@ -540,7 +542,10 @@ hipError_t launch_route_sort_and_quant(const RouterArgs* router, const int32_t* 
     hipError_t e = launch_route_sort_zero(router, ids, T, k, E, expert_begin, sorted_slot, offsets, nullptr,
                                           invalid_count, sort_ws, zero, n_zero, stream);
     if (e != hipSuccess) return e;
-    return launch_quant_act(x, rows, H, fmt, codes, scales, stream);
+    if ((e = launch_quant_act(x, rows, H, fmt, codes, scales, stream)) != hipSuccess) return e;
+    if (S >= kMultiBlockFrom && sorted_scales && rows == T)
+      e = launch_gather_scales(scales, sorted_slot, k, T, H, sorted_scales, stream);
+    return e;
   }
   const bool fuse = router && router_fused(router, T, k);
   if (router && !fuse) {

@@ -332,6 +332,14 @@ SMALL = [
     _small_workload("k16_fp8", FP8, T=96, H=256, I=128, E=32, k=16, routing="zipf", skip=0.1, seed=24),
     _small_workload("k64_fp8", FP8, T=20, H=256, I=128, E=128, k=64, routing="zipf", skip=0.1, seed=25),
     _small_workload("k24_mx", MX, T=40, H=256, I=128, E=48, k=24, routing="zipf", skip=0.1, limit=7.0, seed=26),
+    # 16384 slots and more: the multi-workgroup sort, whose slot_pos places each
+    # block scale at the token's sorted rows for the gate_up GEMM.  (I = 256: at
+    # I = 128 a row of h is one scale block, and a single h code that the GPU's
+    # and the oracle's sum orders round to neighbouring e4m3 values moves an
+    # output by about 1% of max|ref|.)
+    _small_workload("multiblock_fp8", FP8, T=2100, H=384, I=256, E=64, k=8, routing="zipf", skip=0.05, seed=27),
+    _small_workload("multiblock_mx", MX, T=4100, H=256, I=128, E=24, k=4, routing="zipf", skip=0.05, limit=7.0,
+                    seed=28),
 ]
 
 
