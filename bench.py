@@ -192,14 +192,15 @@ def main():
 
     # ---- dominant kernel: gate_up grouped GEMM with the SwiGLU + h-quant epilogue,
     # enqueued through the C ABI in the same configuration as in the forward
-    ss, off, a_codes, a_scales, h_codes, h_scales = _gemm_inputs(wl, inp, dev)
+    ss, off, a_codes, a_scales, h_codes, h_scales, a_sorted = _gemm_inputs(wl, inp, dev)
 
     # zeroed tile counters, reused: each launch leaves them zero (as in the forward)
     counters = torch.zeros(moe.TILE_COUNTERS_INTS, dtype=torch.int32, device=dev)
 
     def l1():
         moe.grouped_gemm(w, 0, a_codes, a_scales, T, off, moe.EPI_SWIGLU_QUANT, S, a_row_index=ss, a_row_divisor=k,
-                         h_codes=h_codes, h_scales=h_scales, swiglu_limit=wl.swiglu_limit, tile_counters=counters)
+                         h_codes=h_codes, h_scales=h_scales, swiglu_limit=wl.swiglu_limit, tile_counters=counters,
+                         a_scales_sorted=a_sorted)
 
     for _ in range(2):
         l1()
@@ -306,15 +307,21 @@ def _gemm_inputs(wl, inp, dev):
     S, I, H = wl.T * wl.k, wl.I, wl.H
     ss, off, _, _ = moe.route_sort(inp["ids"], wl.E, with_slot_pos=False)
     if wl.fmt == W.FMT_BF16:  # the bf16 GEMMs read bf16 rows as they are
-        return ss, off, inp["x"], None, torch.zeros((S, I), dtype=torch.bfloat16, device=dev), None
+        return ss, off, inp["x"], None, torch.zeros((S, I), dtype=torch.bfloat16, device=dev), None, None
     a_codes, a_scales = moe.quant_act(inp["x"], wl.fmt)
+    if moe.forward_sorts_scales(wl.T, wl.k, wl.fmt):
+        # as the forward launches it: the scales by sorted row ([H/128][S] or
+        # [H/128][S][4]), prepared here outside the timed region
+        a_scales_sorted = a_scales[:, (ss.long() // wl.k)].contiguous()
+    else:
+        a_scales_sorted = None
     sdt = torch.float32 if wl.fmt == W.FMT_FP8_B128 else torch.uint8
     h_codes = torch.zeros((I // 128, S, 128), dtype=torch.uint8, device=dev)
     if wl.fmt == W.FMT_FP8_B128:
         h_scales = torch.ones((I // 128, S), dtype=sdt, device=dev)
     else:
         h_scales = torch.full((I // 128, S, 4), 127, dtype=sdt, device=dev)
-    return ss, off, a_codes, a_scales, h_codes, h_scales
+    return ss, off, a_codes, a_scales, h_codes, h_scales, a_scales_sorted
 
 
 def only_gemm(args, wl, inp, w, dev):
@@ -324,14 +331,14 @@ def only_gemm(args, wl, inp, w, dev):
     import block_scaled_fp8_sort_amd as moe
 
     S, I, H, k = wl.T * wl.k, wl.I, wl.H, wl.k
-    ss, off, a_codes, a_scales, h_codes, h_scales = _gemm_inputs(wl, inp, dev)
+    ss, off, a_codes, a_scales, h_codes, h_scales, a_sorted = _gemm_inputs(wl, inp, dev)
     slot_out = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
     counters = torch.zeros(moe.TILE_COUNTERS_INTS, dtype=torch.int32, device=dev)
     if args.only == "gate_up":
         def run():
             moe.grouped_gemm(w, 0, a_codes, a_scales, wl.T, off, moe.EPI_SWIGLU_QUANT, S, a_row_index=ss,
                              a_row_divisor=k, h_codes=h_codes, h_scales=h_scales, swiglu_limit=wl.swiglu_limit,
-                             tile_counters=counters)
+                             tile_counters=counters, a_scales_sorted=a_sorted)
     else:
         def run():
             moe.grouped_gemm(w, 1, h_codes, h_scales, S, off, moe.EPI_WEIGHTED_SCATTER, S, slot_out=slot_out,

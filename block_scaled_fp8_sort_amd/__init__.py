@@ -55,7 +55,7 @@ class MoeGemmArgs(ctypes.Structure):
                 ("expert_offsets", _P), ("epilogue", ctypes.c_int),
                 ("c_f32", _P), ("h_codes", _P), ("h_scales", _P), ("has_swiglu_limit", _I32),
                 ("swiglu_limit", _F32), ("slot_out", _P), ("top_k_weights", _P), ("slot_of_row", _P),
-                ("tile_counters", _P)]
+                ("tile_counters", _P), ("a_scales_sorted", _P)]
 
 
 class MoeDebug(ctypes.Structure):
@@ -109,6 +109,8 @@ def load_library():
                                         ctypes.POINTER(MoeWeights), _P]
     lib.moe_grouped_gemm.restype = ctypes.c_int
     lib.moe_grouped_gemm.argtypes = [ctypes.POINTER(MoeGemmArgs), _P]
+    lib.moe_forward_sorts_scales.restype = _I32
+    lib.moe_forward_sorts_scales.argtypes = [_I32, _I32, ctypes.c_int]
     lib.moe_experts_forward_workspace.restype = _SZ
     lib.moe_experts_forward_workspace.argtypes = [_I32, _I32, ctypes.POINTER(MoeWeights)]
     lib.moe_experts_forward.restype = ctypes.c_int
@@ -303,8 +305,12 @@ TILE_COUNTERS_INTS = 256  # MOE_TILE_COUNTERS_BYTES / 4
 def grouped_gemm(weights: Weights, which: int, a_codes, a_scales, a_rows: int, expert_offsets, epilogue: int,
                  max_rows: int, a_row_index=None, a_row_divisor: int = 1, c_f32=None, h_codes=None, h_scales=None,
                  swiglu_limit: Optional[float] = None, slot_out=None, top_k_weights=None, slot_of_row=None,
-                 tile_counters="new"):
+                 tile_counters="new", a_scales_sorted=None):
     """Enqueue one grouped GEMM (see moe_grouped_gemm); outputs are caller tensors.
+
+    a_scales_sorted: optional copy of the activation scales by sorted row (as
+    the forward builds for large batches, see forward_sorts_scales), read by the
+    256-row tiled paths instead of a_scales at the gathered rows.
 
     which = 0 multiplies by the gate_up weight, 1 by the down weight.  A is
     K-block-major with a_rows rows per plane.  tile_counters: "new" (default)
@@ -333,10 +339,17 @@ def grouped_gemm(weights: Weights, which: int, a_codes, a_scales, a_rows: int, e
         if tile_counters.numel() < TILE_COUNTERS_INTS:
             raise ValueError(f"tile_counters needs {TILE_COUNTERS_INTS} int32")
     a.tile_counters = _ptr(tile_counters)
+    a.a_scales_sorted = _ptr(a_scales_sorted)
     _check(lib.moe_grouped_gemm(ctypes.byref(a), _stream(a_codes.device)))
 
 
 # ------------------------------------------------------------ fused forward
+def forward_sorts_scales(T: int, k: int, fmt: int) -> bool:
+    """Whether the forward hands its gate_up GEMM a copy of the activation
+    scales by sorted row (moe_forward_sorts_scales)."""
+    return bool(load_library().moe_forward_sorts_scales(T, k, fmt))
+
+
 _ws_cache: dict = {}
 
 

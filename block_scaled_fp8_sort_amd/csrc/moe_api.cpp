@@ -204,6 +204,7 @@ moe::GemmParams to_params(const moe_gemm_args* a) {
   p.N = a->which == 0 ? 2 * w->I : w->H;
   p.K = a->which == 0 ? w->H : w->I;
   p.max_rows = a->max_rows;
+  p.a_scales_sorted = w->fmt == MOE_FMT_BF16 ? nullptr : a->a_scales_sorted;
   p.c_f32 = a->c_f32;
   p.sched = a->tile_counters;
   p.h_codes = a->h_codes;
@@ -393,6 +394,11 @@ const char* moe_status_string(moe_status s) {
 }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int32_t moe_forward_sorts_scales(int32_t T, int32_t k, moe_format fmt) {
+  if (T <= 0 || k < 1 || k > kMaxK || (int64_t)T * k >= (int64_t)1 << 31) return 0;
+  return fmt != MOE_FMT_BF16 && valid_fmt(fmt) && moe::route_sort_multiblock(T * k) ? 1 : 0;
+}
 
 size_t moe_route_sort_workspace(int32_t T, int32_t k, int32_t E) {
   if (T < 0 || k < 1 || k > kMaxK || E < 1 || E > kMaxE || (int64_t)T * k >= (int64_t)1 << 31) return 0;

@@ -227,6 +227,12 @@ moe_status moe_prepare_weights(moe_format fmt, moe_layout layout, int32_t E, int
  *                            (bf16 [S, N], row-major).
  * Rows at and beyond offsets[E] are not written.  max_rows bounds offsets[E]
  * (normally T*k).
+ * a_scales_sorted (optional, may be NULL): the same activation scales laid out
+ * by sorted row, [K/128][max_rows] floats or [K/128][max_rows][4] UE8M0 bytes,
+ * row r holding the scales of A row a_row(r).  The 256-row tiled paths then read
+ * it instead of a_scales (consecutive addresses instead of a gather); a_scales
+ * stays required, and the few-rows FP8 path reads it.  The forward builds such
+ * a copy when moe_forward_sorts_scales() says so.
  * MOE_FMT_BF16 weights: A is bf16 [a_rows, K] row-major (not K-block-major),
  * below 4 GiB, and a_scales is ignored; the SwiGLU epilogue writes h as bf16
  * [max_rows, I] row-major into h_codes (h_scales ignored). */
@@ -261,6 +267,7 @@ typedef struct moe_gemm_args {
    * launch leaves it zero again.  Two launches in flight at once must not share
    * it. */
   int32_t* tile_counters;
+  const void* a_scales_sorted; /* may be NULL, see above */
 } moe_gemm_args;
 
 #define MOE_TILE_COUNTERS_BYTES 1024
@@ -268,6 +275,13 @@ typedef struct moe_gemm_args {
 moe_status moe_grouped_gemm(const moe_gemm_args* args, hipStream_t stream);
 
 /* ---------------------------------------------------- fused experts forward --
+ * Whether moe_experts_forward, for T tokens of k slots in format fmt, copies
+ * the activation scales by sorted row and hands that copy to its gate_up GEMM
+ * (a_scales_sorted): 1 or 0, no side effects.  A caller timing that GEMM alone
+ * uses it to launch it the way the forward does. */
+int32_t moe_forward_sorts_scales(int32_t T, int32_t k, moe_format fmt);
+
+/*
  * The whole path in one call ([P-grouped] and [P-mega]): route sort, activation
  * quantization, gate_up grouped GEMM with the SwiGLU (+ optional clamp) and h
  * quantization fused into its epilogue, down grouped GEMM with the routing

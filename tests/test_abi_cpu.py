@@ -33,9 +33,22 @@ def lib():
 def test_library_exports_every_declared_function(lib):
     names = _declared_functions()
     assert "moe_experts_forward" in names and "moe_grouped_gemm" in names
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_forward_sorts_scales(lib):
+    # the forward copies the activation scales by sorted row exactly where it
+    # takes the multi-workgroup sort (16384 slots and more), quantized formats only
+    assert lib.moe_forward_sorts_scales(2048, 8, 0) == 1
+    assert lib.moe_forward_sorts_scales(2047, 8, 0) == 0
+    assert lib.moe_forward_sorts_scales(16384, 8, 1) == 1
+    assert lib.moe_forward_sorts_scales(4096, 8, 2) == 0  # bf16: no scales
+    assert lib.moe_forward_sorts_scales(0, 8, 0) == 0
+    assert lib.moe_forward_sorts_scales(4096, 8, 9) == 0
+    assert lib.moe_forward_sorts_scales(4096, 0, 0) == 0
+    assert moe.forward_sorts_scales(8192, 8, moe.FMT_FP8_B128) and not moe.forward_sorts_scales(64, 8, 0)
 
 
 def test_status_strings(lib):
