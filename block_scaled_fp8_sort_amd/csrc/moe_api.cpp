@@ -241,6 +241,7 @@ moe_status forward_impl(const moe_weights* w, const uint16_t* hidden_states, con
   if (T < 0) return fail(MOE_ERR_SHAPE, "T=%d < 0", T);
   if (k < 1 || k > kMaxK) return fail(MOE_ERR_SHAPE, "k=%d outside [1, %d]", k, kMaxK);
   if ((int64_t)T * k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "T*k must stay below 2^31");
+  if (opt && opt->expert_begin < 0) return fail(MOE_ERR_SHAPE, "expert_begin=%d < 0", opt->expert_begin);
   const bool has_limit = opt && opt->has_swiglu_limit;
   if (has_limit && !(std::isfinite(opt->swiglu_limit) && opt->swiglu_limit > 0.0f))
     return fail(MOE_ERR_SHAPE, "swiglu_limit must be finite and > 0");
@@ -412,6 +413,7 @@ moe_status moe_route_sort(const int32_t* top_k_index, int32_t T, int32_t k, int3
   if (k < 1 || k > kMaxK) return fail(MOE_ERR_SHAPE, "k=%d outside [1, %d]", k, kMaxK);
   if (E < 1 || E > kMaxE) return fail(MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, kMaxE);
   if ((int64_t)T * k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "T*k must stay below 2^31");
+  if (expert_begin < 0) return fail(MOE_ERR_SHAPE, "expert_begin=%d < 0", expert_begin);
   if (!expert_offsets) return fail(MOE_ERR_NULL, "expert_offsets is NULL");
   if (T > 0 && (!top_k_index || !sorted_slot)) return fail(MOE_ERR_NULL, "top_k_index / sorted_slot is NULL");
   const size_t ws_need = moe_route_sort_workspace(T, k, E);
@@ -450,6 +452,7 @@ moe_status moe_route_topk(const float* router_logits, int32_t T, int32_t n_exper
     return fail(MOE_ERR_NULL, "sorted_slot / slot_pos given without expert_offsets");
   if (sort && T > 0 && !sorted_slot) return fail(MOE_ERR_NULL, "sorted_slot is NULL");
   if (sort && (E < 1 || E > kMaxE)) return fail(MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, kMaxE);
+  if (sort && expert_begin < 0) return fail(MOE_ERR_SHAPE, "expert_begin=%d < 0", expert_begin);
   if (T == 0) {
     if (!sort) return ok();
   } else if (!router_logits || !top_k_index || !top_k_weights) {

@@ -170,35 +170,48 @@ __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(const Route
   router_tokens<NV>(r, T, k, wave, (int)(gridDim.x * blockDim.x / kWave));
 }
 
-// Stable scatter of slots [c_begin, c_end) by one wave; start[key] is where the
-// wave's next slot of that key goes (advanced in place, in LDS).
+// One 64-slot step of a wave's stable scatter: lane i holds slot s (valid if
+// active) with its key; start[key] is where the wave's next slot of that key
+// goes (advanced in place, in LDS).
+__device__ __forceinline__ void scatter_step(int s, bool active, int key, int key_bits, int32_t* start,
+                                             int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos) {
+  const int lane = threadIdx.x % kWave;
+  const uint64_t lower_lanes = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint64_t peers = __ballot(active);
+  for (int b = 0; b < key_bits; ++b) {
+    const uint64_t m = __ballot(active && ((key >> b) & 1));
+    peers &= ((key >> b) & 1) ? m : ~m;
+  }
+  if (active) {
+    const int st = start[key];
+    const int pos = st + __popcll(peers & lower_lanes);
+    sorted_slot[pos] = s;
+    if (slot_pos) slot_pos[s] = pos;
+    // the lowest lane of each key group advances the start after all lanes read it
+    const bool leader = (peers & lower_lanes) == 0;
+    __builtin_amdgcn_wave_barrier();
+    if (leader) start[key] = st + __popcll(peers);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ int key_bits_for(int32_t E) {
+  int key_bits = 1;
+  while ((1 << key_bits) <= E) ++key_bits;
+  return key_bits;
+}
+
+// Stable scatter of slots [c_begin, c_end) by one wave.
 __device__ __forceinline__ void scatter_chunk(const int32_t* __restrict__ ids, int c_begin, int c_end, int32_t E,
                                               int32_t expert_begin, int32_t* start, int32_t* __restrict__ sorted_slot,
                                               int32_t* __restrict__ slot_pos) {
   const int lane = threadIdx.x % kWave;
-  int key_bits = 1;
-  while ((1 << key_bits) <= E) ++key_bits;
-  const uint64_t lower_lanes = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int key_bits = key_bits_for(E);
   for (int s0 = c_begin; s0 < c_end; s0 += kWave) {
     const int s = s0 + lane;
     const bool active = s < c_end;
     const int key = active ? sort_key(ids[s], E, expert_begin) : 0;
-    uint64_t peers = __ballot(active);
-    for (int b = 0; b < key_bits; ++b) {
-      const uint64_t m = __ballot(active && ((key >> b) & 1));
-      peers &= ((key >> b) & 1) ? m : ~m;
-    }
-    if (active) {
-      const int st = start[key];
-      const int pos = st + __popcll(peers & lower_lanes);
-      sorted_slot[pos] = s;
-      if (slot_pos) slot_pos[s] = pos;
-      // the lowest lane of each key group advances the start after all lanes read it
-      const bool leader = (peers & lower_lanes) == 0;
-      __builtin_amdgcn_wave_barrier();
-      if (leader) start[key] = st + __popcll(peers);
-    }
-    __builtin_amdgcn_wave_barrier();
+    scatter_step(s, active, key, key_bits, start, sorted_slot, slot_pos);
   }
 }
 
@@ -334,14 +347,23 @@ __device__ __forceinline__ void sort_one_workgroup(const int32_t* __restrict__ i
   const int c_begin = min(S, wave * chunk);
   const int c_end = min(S, c_begin + chunk);
 
-  // 1. per-wave histogram
+  // the wave's keys, all loads in flight at once (at most kSteps per lane, as
+  // S < kMultiBlockFrom), kept in registers for both passes
+  constexpr int kSteps = (kMultiBlockFrom / kSortWaves + kWave - 1) / kWave;
+  int keys[kSteps];
   int my_invalid = 0;
-  for (int s = c_begin + lane; s < c_end; s += kWave) {
-    const int32_t id = ids[s];
-    const int key = sort_key(id, E, expert_begin);
-    my_invalid += (key == E && id != -1) ? 1 : 0;
-    atomicAdd(&hist[wave * K1 + key], 1);
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int s = c_begin + lane + i * kWave;
+    const int32_t id = s < c_end ? ids[s] : -1;
+    keys[i] = sort_key(id, E, expert_begin);
+    my_invalid += (keys[i] == E && id != -1) ? 1 : 0;
   }
+
+  // 1. per-wave histogram
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i)
+    if (c_begin + lane + i * kWave < c_end) atomicAdd(&hist[wave * K1 + keys[i]], 1);
   if (my_invalid) atomicAdd(&s_invalid, my_invalid);
   __syncthreads();
 
@@ -388,7 +410,13 @@ __device__ __forceinline__ void sort_one_workgroup(const int32_t* __restrict__ i
   __syncthreads();
 
   // 3. stable scatter, 64 slots per step, in slot order within each wave
-  scatter_chunk(ids, c_begin, c_end, E, expert_begin, hist + wave * K1, sorted_slot, slot_pos);
+  const int key_bits = key_bits_for(E);
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int s0 = c_begin + i * kWave;
+    if (s0 < c_end)  // wave-uniform
+      scatter_step(s0 + lane, s0 + lane < c_end, keys[i], key_bits, hist + wave * K1, sorted_slot, slot_pos);
+  }
 }
 
 // The router's writes of ids reach the sort's reads through the workgroup

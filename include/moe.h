@@ -100,7 +100,8 @@ const char* moe_last_error(void);
  *  ws / ws_bytes   device workspace of at least moe_route_sort_workspace()
  *                  bytes (per-chunk histograms; 0 bytes, and ws may be NULL,
  *                  below 16384 slots).  Its contents are scratch.
- * Limits: 0 <= T, 1 <= k <= 64, 1 <= E <= 512, T*k < 2^31. */
+ * Limits: 0 <= T, 1 <= k <= 64, 1 <= E <= 512, T*k < 2^31, expert_begin >= 0
+ * (global ids are non-negative, so -1 is never a local expert). */
 size_t moe_route_sort_workspace(int32_t T, int32_t k, int32_t E);
 moe_status moe_route_sort(const int32_t* top_k_index, int32_t T, int32_t k, int32_t E, int32_t expert_begin,
                           int32_t* sorted_slot, int32_t* expert_offsets, int32_t* slot_pos,
@@ -311,7 +312,7 @@ typedef struct moe_debug {
 typedef struct moe_options {
   int32_t has_swiglu_limit;
   float swiglu_limit;    /* must be finite and > 0 when has_swiglu_limit */
-  int32_t expert_begin;  /* global id of local expert 0 */
+  int32_t expert_begin;  /* global id of local expert 0, >= 0 */
   int32_t static_activation_scales; /* nonzero requests static scales: refused (MOE_ERR_UNSUPPORTED) */
   int32_t* invalid_count; /* device int32 [1], may be NULL */
   moe_debug* debug;       /* may be NULL */

@@ -63,6 +63,7 @@ def test_route_sort_refusals(lib):
     assert lib.moe_route_sort(p, 4, 2, 0, 0, p, p, None, None, None, 0, None) == SHAPE
     assert lib.moe_route_sort(p, 4, 2, 513, 0, p, p, None, None, None, 0, None) == SHAPE
     assert lib.moe_route_sort(p, -1, 2, 8, 0, p, p, None, None, None, 0, None) == SHAPE
+    assert lib.moe_route_sort(p, 4, 2, 8, -1, p, p, None, None, None, 0, None) == SHAPE  # -1 must stay skipped
     assert lib.moe_route_sort(None, 4, 2, 8, 0, p, p, None, None, None, 0, None) == NULL
     assert lib.moe_route_sort(p, 4, 2, 8, 0, p, None, None, None, None, 0, None) == NULL
     assert lib.moe_route_sort(p, 4, 2, 8, 0, p, ctypes.c_void_p(32), None, None, None, 0, None) == UNSUP
@@ -92,8 +93,10 @@ def test_route_topk_refusals(lib):
     p = ctypes.c_void_p(16)
     q, r, u = ctypes.c_void_p(48), ctypes.c_void_p(80), ctypes.c_void_p(112)
 
-    def call(T=4, n=8, k=2, ids=q, w=r, E=8, ss=u, off=ctypes.c_void_p(144), ws=None, ws_bytes=0, logits=p):
-        return lib.moe_route_topk(logits, T, n, k, 1, ids, w, E, 0, ss, off, None, None, ws, ws_bytes, None)
+    def call(T=4, n=8, k=2, ids=q, w=r, E=8, ss=u, off=ctypes.c_void_p(144), ws=None, ws_bytes=0, logits=p, begin=0):
+        return lib.moe_route_topk(logits, T, n, k, 1, ids, w, E, begin, ss, off, None, None, ws, ws_bytes, None)
+
+    assert call(begin=-1) == SHAPE
 
     assert call(k=9) == SHAPE  # k > n_experts
     assert call(k=0) == SHAPE
@@ -171,6 +174,9 @@ def test_forward_refusals(lib):
     assert fwd(w=_weights(I=64)) == SHAPE
     assert fwd(w=_weights(E=0)) == SHAPE
     assert fwd(w=_weights(fmt=9)) == UNSUP
+    opt.expert_begin = -1
+    assert fwd(opt=opt) == SHAPE
+    opt.expert_begin = 0
     opt.static_activation_scales = 1
     assert fwd(opt=opt) == UNSUP
     assert b"static" in lib.moe_last_error()
