@@ -66,7 +66,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
     const int64_t col = c - t * H8;
     // adding +0 for a dropped slot leaves the running sum unchanged: a sum
     // that starts at +0 is never -0, the one value +0 would change
-    if (k <= 8) combine_chunk<8>(slot_out, ids, t, col, k, H8, E, expert_begin, out, c);
+    // loads in flight per round: the smallest of 2, 4, 8, 16 that covers k
+    // (a round past k repeats the last slot's load, which the select drops)
+    if (k <= 2) combine_chunk<2>(slot_out, ids, t, col, k, H8, E, expert_begin, out, c);
+    else if (k <= 4) combine_chunk<4>(slot_out, ids, t, col, k, H8, E, expert_begin, out, c);
+    else if (k <= 8) combine_chunk<8>(slot_out, ids, t, col, k, H8, E, expert_begin, out, c);
     else combine_chunk<16>(slot_out, ids, t, col, k, H8, E, expert_begin, out, c);
   }
 }
