@@ -626,6 +626,7 @@ moe_status moe_grouped_gemm(const moe_gemm_args* args, hipStream_t stream) {
       (st = check_ptr(args->weights->w13, dev, "weights")) != MOE_OK)
     return st;
   if (args->tile_counters && (st = check_ptr(args->tile_counters, dev, "tile_counters")) != MOE_OK) return st;
+  if (args->a_scales_sorted && (st = check_ptr(args->a_scales_sorted, dev, "a_scales_sorted")) != MOE_OK) return st;
   const moe::GemmParams p = to_params(args);
   const bool paired = args->which == 0;
   st = hip_status(launch_gemm(p, args->weights->fmt, (int)args->epilogue, paired, cus, stream),
