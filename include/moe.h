@@ -135,8 +135,9 @@ moe_status moe_route_sort(const int32_t* top_k_index, int32_t T, int32_t k, int3
  *                  outside [expert_begin, expert_begin + E) are sentinels).
  *                  expert_offsets NULL runs the router alone (sorted_slot
  *                  and slot_pos must then be NULL too; E and ws are unused).
- * Small batches (T * k < 16384 and T * n_experts <= 65536) run the router and
- * the sort in one launch.
+ * Up to 16 tokens of at most 128 experts (and fewer than 16384 slots), the
+ * router and the sort run in one launch; otherwise the router is a launch of
+ * its own.
  * Limits: 1 <= n_experts <= 512, 1 <= k <= min(64, n_experts); the rest as in
  * moe_route_sort. */
 size_t moe_route_topk_workspace(int32_t T, int32_t k, int32_t E);
