@@ -191,7 +191,8 @@ def route_sort(top_k_index: torch.Tensor, num_experts: int, expert_begin: int = 
 def route_topk(router_logits: torch.Tensor, k: int, renormalize: bool = True, num_experts: Optional[int] = None,
                expert_begin: int = 0, sort: bool = True, with_slot_pos: bool = True):
     """Router top-k (softmax over the logits, the k largest, optionally
-    renormalised) fused with the route sort.
+    renormalised) and the route sort of its ids, in one call (one launch up to
+    16 tokens of at most 128 experts).
 
     router_logits fp32 [T, n_experts].  Returns (top_k_index int32 [T, k],
     top_k_weights fp32 [T, k], sorted_slot, expert_offsets, slot_pos,
