@@ -422,6 +422,23 @@ def test_forward_invariants_tiny():
     assert torch.count_nonzero(z.view(torch.int16)).item() == 0
 
 
+@pytest.mark.parametrize("name", ["multiblock_fp8", "multiblock_mx"])
+def test_forward_poisoned_workspace_large_batch(name):
+    """With the multi-workgroup sort the forward also builds the activation
+    scales by sorted row in its workspace; a workspace filled with 0xFF (NaN
+    patterns) beforehand changes no output bit, so every scale the gate_up GEMM
+    reads was written first."""
+    wl = next(w for w in SMALL if w.name == name)
+    assert moe.forward_sorts_scales(wl.T, wl.k, wl.fmt)
+    inp = W.inputs(wl, DEV)
+    w = _prepare(inp, wl.fmt)
+    a = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w, swiglu_limit=wl.swiglu_limit).clone()
+    ws = torch.full((moe.forward_workspace_bytes(wl.T, wl.k, w),), 0xFF, dtype=torch.uint8, device=DEV)
+    b = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w, swiglu_limit=wl.swiglu_limit, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 def test_forward_empty_and_single_token():
     wl = W.WORKLOADS["tiny"]
     inp = W.inputs(wl, DEV)
