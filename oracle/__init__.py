@@ -55,12 +55,14 @@ def _load():
     lib.oracle_router_topk.restype = ctypes.c_int
     lib.oracle_quant_rows_bf16.argtypes = [P, i32, i32, i32, P, P]
     lib.oracle_quant_rows_bf16.restype = ctypes.c_int
+    lib.oracle_quant_rows_bf16_static.argtypes = [P, i32, i32, i32, P, i32, P]
+    lib.oracle_quant_rows_bf16_static.restype = ctypes.c_int
     lib.oracle_quant_rows_f32.argtypes = [P, i32, i32, i32, P, P]
     lib.oracle_quant_rows_f32.restype = ctypes.c_int
     lib.oracle_grouped_gemm.argtypes = [i32, P, P, P, i32, P, i32, P, P, i32, i32, P]
     lib.oracle_grouped_gemm.restype = ctypes.c_int
     lib.oracle_forward.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, i32, i32, i32, i32,
-                                   ctypes.c_float, P, i32, P, P, P, P, P]
+                                   ctypes.c_float, P, i32, P, P, P, P, P, P, i32]
     lib.oracle_forward.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -153,6 +155,22 @@ def quant_rows_bf16(x_bits, fmt: int):
     return codes, scales
 
 
+def quant_rows_bf16_static(x_bits, fmt: int, scales, row_stride=None):
+    """Static per-block quantization: x_bits uint16 [rows, H] (bf16 bit
+    patterns) with the caller's block scales (FP8: float32, MX: uint8 UE8M0
+    bytes).  ``scales`` is [rows, H/B] (row_stride None: H/B) or one row [H/B]
+    for every token (row_stride 0).  Returns the codes u8 [rows, H]."""
+    x = _c(x_bits, np.uint16)
+    rows, H = x.shape
+    nb = H // (128 if fmt == FMT_FP8_B128 else 32)
+    sc = _c(scales, np.float32 if fmt == FMT_FP8_B128 else np.uint8)
+    if row_stride is None:
+        row_stride = 0 if sc.ndim == 1 else nb
+    codes = np.empty((rows, H), np.uint8)
+    _check(_load().oracle_quant_rows_bf16_static(_ptr(x), rows, H, fmt, _ptr(sc), int(row_stride), _ptr(codes)))
+    return codes
+
+
 def quant_rows_f32(x, fmt: int):
     x = _c(x, np.float32)
     rows, H = x.shape
@@ -181,13 +199,15 @@ def grouped_gemm(fmt, a_codes, a_scales, offsets, b_codes, b_scales, N, K, row_i
 
 
 def forward(fmt, w13, w13_scale, w2, w2_scale, x_bits, ids, wts, swiglu_limit=None, expert_begin=0,
-            tokens=None, debug=False):
+            tokens=None, debug=False, act_scales=None, act_scales_row_stride=None):
     """The experts forward on the host.
 
     Weights in the nt layout (see ``moe_oracle.cpp``); BF16: bf16 bit patterns
     (uint16) [E, 2I, H] and [E, H, I], scales None.  Returns the bf16 bit
     patterns uint16 [T, H] (rows of tokens not listed in ``tokens`` stay 0) and,
-    when ``debug`` is set, a dict of per-slot intermediates.
+    when ``debug`` is set, a dict of per-slot intermediates.  ``act_scales``
+    (static activation scheme): the layer input's precomputed block scales, as
+    in quant_rows_bf16_static; None quantizes dynamically.
     """
     bf = fmt == FMT_BF16
     w13 = _c(w13, np.uint16 if bf else np.uint8)
@@ -214,9 +234,15 @@ def forward(fmt, w13, w13_scale, w2, w2_scale, x_bits, ids, wts, swiglu_limit=No
         dbg["y"] = np.full((S, H), np.nan, np.float32)
     has = 0 if swiglu_limit is None else 1
     lim = 0.0 if swiglu_limit is None else float(swiglu_limit)
+    asc = None
+    stride = 0
+    if act_scales is not None:
+        asc = _c(act_scales, np.float32 if fmt == FMT_FP8_B128 else np.uint8)
+        nb = H // (128 if fmt == FMT_FP8_B128 else 32)
+        stride = act_scales_row_stride if act_scales_row_stride is not None else (0 if asc.ndim == 1 else nb)
     _check(_load().oracle_forward(fmt, E, H, I, _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(x),
                                   _ptr(ids), _ptr(wts), T, k, expert_begin, has, lim, _ptr(tok),
                                   0 if tok is None else tok.size, _ptr(out),
                                   _ptr(dbg.get("gu")), _ptr(dbg.get("h_codes")), _ptr(dbg.get("h_scales")),
-                                  _ptr(dbg.get("y"))))
+                                  _ptr(dbg.get("y")), _ptr(asc), int(stride)))
     return (out, dbg) if debug else out

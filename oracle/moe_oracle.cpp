@@ -172,6 +172,23 @@ int ceil_log2_f32(float r) {
 }
 
 // -------------------------------------------------- activation quantization --
+// Encoding of one block of B values once its scale is known.  FP8 format: the
+// fp32 scale s, code = e4m3(x / s) with an IEEE fp32 division.  MX format: the
+// UE8M0 byte b, code = e4m3(x * 2^-(b-127)) computed exactly in fp64.  e4m3()
+// rounds to nearest even and saturates at 448, so values past 448 s give the
+// largest code of their sign.
+void encode_block(const float* x, int64_t B, int fmt, float s_f32, uint8_t s_u8, uint8_t* codes) {
+  if (fmt == FMT_FP8_B128) {
+    for (int64_t i = 0; i < B; ++i) {
+      const float q = x[i] / s_f32;  // IEEE fp32 division
+      codes[i] = e4m3_encode(q);
+    }
+  } else {
+    const int e = (int)s_u8 - 127;
+    for (int64_t i = 0; i < B; ++i) codes[i] = e4m3_encode(std::ldexp((double)x[i], -e));
+  }
+}
+
 // Dynamic per-block quantization of one row of fp32 values (bf16 input is
 // widened exactly first).  Block length 128 with an fp32 scale (FP8 format) or
 // 32 with a UE8M0 byte (MX format).
@@ -183,19 +200,34 @@ void quant_row(const float* x, int64_t n, int fmt, uint8_t* codes, float* sc_f32
     const float r = std::max(amax, 1e-4f) / 448.0f;
     if (fmt == FMT_FP8_B128) {
       sc_f32[b] = r;
-      for (int64_t i = 0; i < B; ++i) {
-        const float q = x[b * B + i] / r;  // IEEE fp32 division
-        codes[b * B + i] = e4m3_encode(q);
-      }
+      encode_block(x + b * B, B, fmt, r, 0, codes + b * B);
     } else {
       const int e = ceil_log2_f32(r);
       sc_u8[b] = (uint8_t)(e + 127);
-      for (int64_t i = 0; i < B; ++i) {
-        // x * 2^-e computed exactly in fp64, then encoded
-        codes[b * B + i] = e4m3_encode(std::ldexp((double)x[b * B + i], -e));
-      }
+      encode_block(x + b * B, B, fmt, 0.0f, sc_u8[b], codes + b * B);
     }
   }
+}
+
+// Static per-block quantization of one row: the caller's precomputed block
+// scales (fp32 per 1x128 for the FP8 format, UE8M0 bytes per 1x32 for MX)
+// replace the amax pass; the encoding is the dynamic rule's.
+void quant_row_static(const float* x, int64_t n, int fmt, const void* row_scales, uint8_t* codes) {
+  const int64_t B = fmt == FMT_FP8_B128 ? 128 : 32;
+  for (int64_t b = 0; b < n / B; ++b) {
+    if (fmt == FMT_FP8_B128)
+      encode_block(x + b * B, B, fmt, ((const float*)row_scales)[b], 0, codes + b * B);
+    else
+      encode_block(x + b * B, B, fmt, 0.0f, ((const uint8_t*)row_scales)[b], codes + b * B);
+  }
+}
+
+// Element size and row address of a caller's static scale array: token t's
+// row of H/B scales starts `row_stride` elements after token t - 1's (0: the
+// one row serves every token).
+inline const void* static_row(int fmt, const void* scales, int64_t row_stride, int64_t t) {
+  if (fmt == FMT_FP8_B128) return (const float*)scales + t * row_stride;
+  return (const uint8_t*)scales + t * row_stride;
 }
 
 // Decoded (dequantized) activation element i of row `row` of a [rows, K]
@@ -358,6 +390,29 @@ int oracle_quant_rows_bf16(const uint16_t* x, int32_t rows, int32_t H, int32_t f
   return OK;
 }
 
+// Static quantization of bf16 rows [rows, H] with the caller's block scales:
+// row t uses scales[t * row_stride ...] (fp32 [.., H/128] for the FP8 format,
+// UE8M0 bytes [.., H/32] for MX); row_stride 0 broadcasts one row of scales.
+// The scales are the static activation scheme's precomputed per-block scales
+// ("grouped_mm experts dispatch does not support activation_scheme='static'",
+// sections "What it means" and "Example fix": the eager path consumes them, the
+// grouped one quantized dynamically instead).  FP8 scales must be finite and
+// positive, MX bytes below 255.
+int oracle_quant_rows_bf16_static(const uint16_t* x, int32_t rows, int32_t H, int32_t fmt, const void* scales,
+                                  int32_t row_stride, uint8_t* codes) {
+  if (fmt != FMT_FP8_B128 && fmt != FMT_MX) return ERR_FMT;
+  const int32_t nb = H / (fmt == FMT_FP8_B128 ? 128 : 32);
+  if (rows < 0 || H <= 0 || H % 128 || row_stride < 0 || (row_stride > 0 && row_stride < nb)) return ERR_SHAPE;
+  if (rows > 0 && (!x || !codes || !scales)) return ERR_NULL;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    std::vector<float> row(H);
+    for (int64_t i = 0; i < H; ++i) row[i] = bf16_to_f32(x[r * H + i]);
+    quant_row_static(row.data(), H, fmt, static_row(fmt, scales, row_stride, r), codes + r * H);
+  }
+  return OK;
+}
+
 // The same rule applied to fp32 rows (the rule the forward uses for h).
 int oracle_quant_rows_f32(const float* x, int32_t rows, int32_t H, int32_t fmt, uint8_t* codes, void* scales) {
   if (fmt != FMT_FP8_B128 && fmt != FMT_MX) return ERR_FMT;
@@ -421,9 +476,15 @@ int oracle_forward(int32_t fmt, int32_t E, int32_t H, int32_t I, const uint8_t* 
                    const uint8_t* w2, const void* w2_scale, const uint16_t* x, const int32_t* ids,
                    const float* wts, int32_t T, int32_t k, int32_t expert_begin, int32_t has_limit, float limit,
                    const int32_t* tokens, int32_t n_tokens, uint16_t* out, float* dbg_gu, uint8_t* dbg_h_codes,
-                   void* dbg_h_scales, float* dbg_y) {
+                   void* dbg_h_scales, float* dbg_y, const void* act_scales, int32_t act_row_stride) {
   if (fmt != FMT_FP8_B128 && fmt != FMT_MX && fmt != FMT_BF16) return ERR_FMT;
   if (E < 1 || T < 0 || k < 1 || H <= 0 || I <= 0 || H % 128 || I % 128) return ERR_SHAPE;
+  // static activation scales (act_scales non-NULL): the layer input is
+  // quantized with them instead of its own block amax; h stays dynamic (the
+  // scheme names the input's scales only)
+  if (act_scales && (fmt == FMT_BF16 || act_row_stride < 0 ||
+                     (act_row_stride > 0 && act_row_stride < H / (fmt == FMT_FP8_B128 ? 128 : 32))))
+    return ERR_SHAPE;
   if (has_limit && !(std::isfinite(limit) && limit > 0.0f)) return ERR_SHAPE;
   if (T == 0) return OK;
   if (!w13 || !w2 || !x || !ids || !wts || !out) return ERR_NULL;
@@ -446,8 +507,14 @@ int oracle_forward(int32_t fmt, int32_t E, int32_t H, int32_t I, const uint8_t* 
       std::vector<uint8_t> xq(H);
       std::vector<float> xs_f(H / 128);
       std::vector<uint8_t> xs_u(H / 32);
-      quant_row(xr.data(), H, fmt, xq.data(), xs_f.data(), xs_u.data());
-      const void* xs = fmt == FMT_FP8_B128 ? (const void*)xs_f.data() : (const void*)xs_u.data();
+      const void* xs;
+      if (act_scales) {
+        xs = static_row(fmt, act_scales, act_row_stride, t);
+        quant_row_static(xr.data(), H, fmt, xs, xq.data());
+      } else {
+        quant_row(xr.data(), H, fmt, xq.data(), xs_f.data(), xs_u.data());
+        xs = fmt == FMT_FP8_B128 ? (const void*)xs_f.data() : (const void*)xs_u.data();
+      }
       for (int64_t i = 0; i < H; ++i) a[i] = act_value(fmt, xq.data(), xs, 0, H, i);
     }
 

@@ -389,6 +389,141 @@ def test_quant_error_bound_and_bf16_entry(fmt):
         assert np.all((blk > 224) & (blk <= 448))
 
 
+# ------------------------------------------------- static activation scales --
+# The static scheme hands the layer its activation scales precomputed, per
+# block (the same blocks and scale types as the dynamic rule); only the amax
+# pass goes away, the encoding is unchanged.
+
+
+def _torch_static_codes(x_bits, fmt, scales):
+    """Independent encoding with torch: FP8, torch's fp32 division by the block
+    scale, clamped to +-448 and cast to float8_e4m3fn; MX, exact scaling by
+    2^-(b-127) in float64 and the same clamp and cast."""
+    x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).view(torch.bfloat16)
+    rows, H = x.shape
+    B = 128 if fmt == FP8 else 32
+    xb = x.float().view(rows, H // B, B)
+    if fmt == FP8:
+        q = torch.div(xb, torch.from_numpy(np.ascontiguousarray(scales, np.float32)).view(rows, H // B, 1))
+    else:
+        e = torch.from_numpy(np.ascontiguousarray(scales).astype(np.int64) - 127).view(rows, H // B, 1)
+        q = xb.double() * torch.exp2(-e.double())
+    return q.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).view(rows, H).numpy()
+
+
+@pytest.mark.parametrize("fmt", [FP8, MX])
+def test_static_scales_equal_to_dynamic_give_the_dynamic_codes(fmt):
+    """Static scales that happen to equal the dynamic ones give bit-identical codes."""
+    rng = np.random.default_rng(31 + fmt)
+    x = (rng.standard_normal((64, 512)) * np.exp(rng.uniform(-10, 10, size=(64, 1)))).astype(np.float32)
+    x[::7, :128] = 0.0
+    x[3::11] *= 1e-7
+    xb = _bf16_bits(x)
+    codes, sc = oracle.quant_rows_bf16(xb, fmt)
+    assert np.array_equal(oracle.quant_rows_bf16_static(xb, fmt, sc), codes)
+
+
+@pytest.mark.parametrize("fmt", [FP8, MX])
+@pytest.mark.parametrize("p", [-30, -4, 0, 3, 60])
+def test_static_power_of_two_scale_reproduces_codes(fmt, p):
+    """x = c * 2^p for e4m3 codes c, with the static scale 2^p: the codes are c
+    (as values), whatever the block's amax (no code needs to reach 448)."""
+    rng = np.random.default_rng(40 + p + 5 * fmt)
+    B = 128 if fmt == FP8 else 32
+    rows, H = 4, 2 * 128
+    c = rng.integers(0, 0x77, size=(rows, H)).astype(np.uint8)  # magnitudes up to 240
+    c |= (rng.random((rows, H)) < 0.5).astype(np.uint8) << 7
+    vals = torch.from_numpy(c).view(torch.float8_e4m3fn).double().numpy() * 2.0 ** p
+    xb = _bf16_bits(vals)
+    assert np.array_equal(_bits_to_f64(xb), vals)
+    sc = np.full((rows, H // B), np.float32(2.0 ** p), np.float32) if fmt == FP8 else \
+        np.full((rows, H // B), 127 + p, np.uint8)
+    codes = oracle.quant_rows_bf16_static(xb, fmt, sc)
+    got = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(got, torch.from_numpy(c).view(torch.float8_e4m3fn).double().numpy())
+
+
+@pytest.mark.parametrize("fmt", [FP8, MX])
+def test_static_values_past_448_s_saturate(fmt):
+    """|x| >= 448 s gives the largest code of x's sign (0x7E / 0xFE), and so does
+    anything that rounds up past 448 (464 s would be the next binade's first
+    value); just below the midpoint 448 s < |x| < 464 s stays 448 too."""
+    B = 128 if fmt == FP8 else 32
+    s32 = np.float32(0.75) if fmt == FP8 else None
+    s = 0.75 if fmt == FP8 else 2.0 ** -3
+    vals = np.array([448.0, 449.0, 460.0, 464.0, 500.0, 1e4, 3e38 / 1e30, 1e30], np.float64) * s
+    x = np.zeros((2, 128), np.float64)
+    x[0, :vals.size] = vals
+    x[1, :vals.size] = -vals
+    xb = _bf16_bits(x)
+    xv = _bits_to_f64(xb)
+    assert np.all(np.abs(xv[:, :vals.size]) >= 440 * s)  # bf16 rounding keeps them at or past 448 s (within bf16)
+    sc = np.full((2, 128 // B), s32, np.float32) if fmt == FP8 else np.full((2, 128 // B), 124, np.uint8)
+    codes = oracle.quant_rows_bf16_static(xb, fmt, sc)
+    big = np.abs(xv[0, :vals.size]) >= 448 * s
+    assert np.all(codes[0, :vals.size][big] == 0x7E) and np.all(codes[1, :vals.size][big] == 0xFE)
+    assert np.array_equal(codes, _torch_static_codes(xb, fmt, sc))
+
+
+@pytest.mark.parametrize("fmt", [FP8, MX])
+def test_static_codes_equal_torch_division_and_cast(fmt):
+    """Arbitrary (non-power-of-two, FP8) static scales, values well past and
+    well under them, and values at e4m3 rounding midpoints of x / s (one fp32
+    ulp either side): torch's fp32 division and float8 cast give the same codes
+    (this pins a division, not a product with 1 / s)."""
+    rng = np.random.default_rng(77 + fmt)
+    B = 128 if fmt == FP8 else 32
+    rows, H = 256, 512
+    if fmt == FP8:
+        sc = np.exp(rng.uniform(-12, 6, size=(rows, H // B))).astype(np.float32)
+        s_full = np.repeat(sc.astype(np.float64), B, axis=1)
+    else:
+        sc = rng.integers(100, 140, size=(rows, H // B)).astype(np.uint8)
+        s_full = np.repeat(2.0 ** (sc.astype(np.float64) - 127), B, axis=1)
+    x = rng.standard_normal((rows, H)) * s_full * np.exp(rng.uniform(-4, 7, size=(rows, 1)))
+    if fmt == FP8:
+        # half the rows: per block a bf16 value x0 and a midpoint m0 between
+        # neighbouring e4m3 values, the block scale s = fp32(x0 / m0), and the
+        # block's entries x0 * 2^-j, so that every x / s lies within an fp32 ulp
+        # of an e4m3 rounding midpoint
+        v = _e4m3_values()
+        mids = ((v[1:] + v[:-1]) / 2)[16:]
+        for r in range(rows // 2):
+            for b in range(H // B):
+                x0 = float(_bits_to_f64(_bf16_bits([rng.uniform(0.5, 4.0)]))[0])
+                m0 = float(rng.choice(mids[mids > 16]))
+                sc[r, b] = np.float32(x0 / m0)
+                j = rng.integers(0, 4, size=B)
+                x[r, b * B:(b + 1) * B] = x0 * 2.0 ** -j * np.where(rng.random(B) < 0.5, -1, 1)
+    xb = _bf16_bits(x)
+    codes = oracle.quant_rows_bf16_static(xb, fmt, sc)
+    assert np.array_equal(codes, _torch_static_codes(xb, fmt, sc))
+    if fmt == FP8:
+        # the midpoint rows do hold quotients whose reciprocal product rounds
+        # differently (else this test could not tell the two apart)
+        xs = _bits_to_f64(xb)[: rows // 2].astype(np.float32)
+        s_rep = np.repeat(sc[: rows // 2], B, axis=1)
+        by_recip = torch.from_numpy((xs * (np.float32(1) / s_rep)).astype(np.float32)).clamp(-448, 448)
+        c_recip = by_recip.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.count_nonzero(c_recip != codes[: rows // 2]) > 0
+
+
+@pytest.mark.parametrize("fmt", [FP8, MX])
+def test_static_one_row_broadcasts(fmt):
+    """Row stride 0: one row of block scales serves every token, the same as
+    repeating it per token."""
+    rng = np.random.default_rng(90 + fmt)
+    B = 128 if fmt == FP8 else 32
+    xb = _bf16_bits(rng.standard_normal((9, 384)))
+    row = np.exp(rng.uniform(-3, 0, size=384 // B)).astype(np.float32) if fmt == FP8 else \
+        rng.integers(120, 127, size=384 // B).astype(np.uint8)
+    a = oracle.quant_rows_bf16_static(xb, fmt, row, row_stride=0)
+    b = oracle.quant_rows_bf16_static(xb, fmt, np.tile(row, (9, 1)))
+    assert np.array_equal(a, b)
+    with pytest.raises(oracle.OracleError):
+        oracle.quant_rows_bf16_static(xb, fmt, np.tile(row, (9, 1)), row_stride=1)  # shorter than a row
+
+
 # ----------------------------------------------------------- grouped GEMM --
 
 def _fp8_decode_t(codes):
@@ -467,13 +602,15 @@ def _bits_to_f64(b):
     return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).double().numpy()
 
 
-def _brute_force(fmt, d, limit=None):
-    """Every expert for every token with torch float64 matmuls, then the routed ones are picked."""
+def _brute_force(fmt, d, limit=None, act=None):
+    """Every expert for every token with torch float64 matmuls, then the routed
+    ones are picked.  act: (codes, scales) of the layer input, else the oracle's
+    dynamic quantization."""
     T, H = d["x"].shape
     E = d["w13"].shape[0]
     I = d["w13"].shape[1] // 2
     k = d["ids"].shape[1]
-    a, asc = oracle.quant_rows_bf16(d["x"], fmt)
+    a, asc = oracle.quant_rows_bf16(d["x"], fmt) if act is None else act
     A = _dequant_act(a, asc, fmt)
     if fmt == FP8:
         W13, W2 = _dequant_w_fp8(d["w13"], d["s13"]), _dequant_w_fp8(d["w2"], d["s2"])
@@ -520,6 +657,33 @@ def test_forward_matches_dense_brute_force(fmt, limit):
                 np.testing.assert_allclose(dbg["gu"][t * k + j], GU[e, t], rtol=1e-6, atol=1e-9)
             else:
                 assert np.all(np.isnan(dbg["gu"][t * k + j]))
+
+
+@pytest.mark.parametrize("fmt", [FP8, MX])
+def test_forward_static_scales(fmt):
+    """Static activation scales: equal to the dynamic ones, the forward is the
+    dynamic forward bit for bit; other scales (per token, and one broadcast row)
+    match a dense brute force whose activation codes come from torch's division
+    and float8 cast (h stays dynamic)."""
+    d = _small_inputs(fmt)
+    _, dyn_sc = oracle.quant_rows_bf16(d["x"], fmt)
+    assert np.array_equal(_run(fmt, d, act_scales=dyn_sc), _run(fmt, d))
+    rng = np.random.default_rng(5 + fmt)
+    T, H = d["x"].shape
+    B = 128 if fmt == FP8 else 32
+    if fmt == FP8:
+        per_tok = (dyn_sc * np.exp(rng.uniform(-0.7, 0.7, size=dyn_sc.shape))).astype(np.float32)
+        row = np.full(H // B, np.float32(3.1 / 448), np.float32)  # saturates the largest activations
+    else:
+        per_tok = (dyn_sc.astype(np.int64) + rng.integers(-1, 2, size=dyn_sc.shape)).astype(np.uint8)
+        row = np.full(H // B, 125, np.uint8)
+    for sc, stride in ((per_tok, None), (row, 0)):
+        out = _run(fmt, d, act_scales=sc, act_scales_row_stride=stride)
+        full = sc if sc.ndim == 2 else np.tile(sc, (T, 1))
+        ref, _ = _brute_force(fmt, d, None, act=(_torch_static_codes(d["x"], fmt, full), full))
+        o, r = _bits_to_f64(out), _bits_to_f64(ref)
+        assert np.all(np.abs(o - r) <= np.abs(r) * 2 ** -7 + 1e-30)
+        assert np.mean(out == ref) > 0.99
 
 
 def test_forward_textbook_reduction_k1_e1():
