@@ -6,9 +6,10 @@ torch supplies device memory and the current HIP stream, and every step of the
 forward runs in the library's HIP kernels.  There is no CPU fallback: importing
 works without the library, but every call raises if it is missing.
 
-Errors follow the pages' guards: a non-bf16 input raises ValueError, static
-activation scales or a non-int8 FP4 weight raise NotImplementedError, tensors on
-another device raise RuntimeError.
+Errors follow the pages' guards: a non-bf16 input raises ValueError, a
+non-int8 FP4 weight raises NotImplementedError, tensors on another device raise
+RuntimeError.  Both activation schemes are served: dynamic (per-block amax) and
+static (the caller's precomputed per-block scales).
 """
 from __future__ import annotations
 
@@ -20,7 +21,8 @@ import torch
 
 __all__ = [
     "FMT_FP8_B128", "FMT_MXFP8A_MXFP4W", "FMT_BF16", "EPI_STORE_F32", "EPI_SWIGLU_QUANT", "EPI_WEIGHTED_SCATTER",
-    "MoeError", "library_path", "load_library", "route_sort", "route_topk", "quant_act", "prepare_weights",
+    "MoeError", "library_path", "load_library", "route_sort", "route_topk", "quant_act", "quant_act_static",
+    "prepare_weights",
     "grouped_gemm", "experts_forward", "experts_forward_from_logits", "forward_workspace_bytes", "Weights",
     "TILE_COUNTERS_INTS",
 ]
@@ -59,12 +61,14 @@ class MoeGemmArgs(ctypes.Structure):
 
 
 class MoeDebug(ctypes.Structure):
-    _fields_ = [("sorted_slot", _P), ("expert_offsets", _P), ("act_codes", _P), ("act_scales", _P)]
+    _fields_ = [("sorted_slot", _P), ("expert_offsets", _P), ("act_codes", _P), ("act_scales", _P),
+                ("h_codes", _P), ("h_scales", _P)]
 
 
 class MoeOptions(ctypes.Structure):
     _fields_ = [("has_swiglu_limit", _I32), ("swiglu_limit", _F32), ("expert_begin", _I32),
-                ("static_activation_scales", _I32), ("invalid_count", _P), ("debug", ctypes.POINTER(MoeDebug))]
+                ("static_activation_scales", _I32), ("invalid_count", _P), ("debug", ctypes.POINTER(MoeDebug)),
+                ("act_scales", _P), ("act_scales_row_stride", _I32)]
 
 
 class MoeError(RuntimeError):
@@ -102,6 +106,8 @@ def load_library():
     lib.moe_route_topk.argtypes = [_P, _I32, _I32, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]
     lib.moe_quant_act.restype = ctypes.c_int
     lib.moe_quant_act.argtypes = [_P, _I32, _I32, ctypes.c_int, _P, _P, _P]
+    lib.moe_quant_act_static.restype = ctypes.c_int
+    lib.moe_quant_act_static.argtypes = [_P, _I32, _I32, ctypes.c_int, _P, _I32, _P, _P, _P]
     lib.moe_prepared_weights_size.restype = _SZ
     lib.moe_prepared_weights_size.argtypes = [ctypes.c_int, _I32, _I32, _I32]
     lib.moe_prepare_weights.restype = ctypes.c_int
@@ -149,6 +155,27 @@ def _need(t: torch.Tensor, name: str, dtype, device=None):
         raise ValueError(f"{name} must be contiguous")
     if device is not None and t.device != device:
         raise RuntimeError(f"{name} is on {t.device}, expected {device} (one device per process)")
+
+
+def _shape(t: torch.Tensor, name: str, shape: tuple):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_forward_shapes(hidden_states, top_k_index, top_k_weights, weights, out):
+    """The shapes the C call takes on trust (it sees bare pointers and uses
+    weights.H): refuse any mismatch before the library is called."""
+    if hidden_states.dim() != 2:
+        raise ValueError(f"hidden_states must be [T, H], got shape {tuple(hidden_states.shape)}")
+    T, H = hidden_states.shape
+    if H != weights.H:
+        raise ValueError(f"hidden_states has H={H} but the weights have H={weights.H}")
+    if top_k_index.dim() != 2 or top_k_index.shape[0] != T:
+        raise ValueError(f"top_k_index must be [T={T}, k], got shape {tuple(top_k_index.shape)}")
+    if top_k_weights is not None:
+        _shape(top_k_weights, "top_k_weights", top_k_index.shape)
+    if out is not None:
+        _shape(out, "out", (T, weights.H))
 
 
 def _scale_dtype(fmt: int):
@@ -237,6 +264,37 @@ def quant_act(x: torch.Tensor, fmt: int = FMT_FP8_B128):
     return codes, scales
 
 
+def _static_scales(act_scales: torch.Tensor, fmt: int, rows: int, H: int, device):
+    """Checks a static scale tensor ([rows, H/B] per token, or [H/B] for every
+    token) and returns its row stride in elements."""
+    if fmt not in (FMT_FP8_B128, FMT_MXFP8A_MXFP4W):
+        raise NotImplementedError("static activation scales need a quantized format (FP8_B128 or MX)")
+    nb = H // 128 if fmt == FMT_FP8_B128 else H // 32
+    dt = torch.float32 if fmt == FMT_FP8_B128 else torch.uint8
+    _need(act_scales, "act_scales", dt, device)
+    if act_scales.dim() == 1:
+        _shape(act_scales, "act_scales", (nb,))
+        return 0
+    _shape(act_scales, "act_scales", (rows, nb))
+    return nb
+
+
+def quant_act_static(x: torch.Tensor, act_scales: torch.Tensor, fmt: int = FMT_FP8_B128):
+    """Static per-block quantization of bf16 rows with the caller's block scales
+    (act_scales: fp32 [rows, H/128] for FP8_B128 or uint8 UE8M0 [rows, H/32]
+    for MX; a 1-D [H/B] tensor serves every row).  Returns (codes, scales) as
+    quant_act does."""
+    lib = load_library()
+    _need(x, "x", torch.bfloat16)
+    rows, H = x.shape
+    stride = _static_scales(act_scales, fmt, rows, H, x.device)
+    codes = torch.empty((H // 128, rows, 128), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(_scale_shape(fmt, H, rows), dtype=_scale_dtype(fmt), device=x.device)
+    _check(lib.moe_quant_act_static(_ptr(x), rows, H, fmt, _ptr(act_scales), stride, _ptr(codes), _ptr(scales),
+                                    _stream(x.device)))
+    return codes, scales
+
+
 # ------------------------------------------------------------------- weights
 class Weights:
     """Prepared expert weights: the C descriptor plus the tensors it points at."""
@@ -284,12 +342,42 @@ def prepare_weights(gate_up: torch.Tensor, gate_up_scale: torch.Tensor, down: to
             raise ValueError(f"{name} must hold 8-bit codes, got {t.dtype}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+    if gate_up.dim() != 3 or down.dim() != 3:
+        raise ValueError("gate_up and down must be 3-D [E, rows, cols]")
     E = gate_up.shape[0]
     if fmt in (FMT_BF16, FMT_FP8_B128):
         H, I2 = (gate_up.shape[1], gate_up.shape[2]) if transposed else (gate_up.shape[2], gate_up.shape[1])
     else:
+        if transposed:
+            raise ValueError("MX weights are accepted in the nt layout only")
         H, I2 = gate_up.shape[2] * 2, gate_up.shape[1]
     I = I2 // 2
+    if I2 % 2:
+        raise ValueError(f"gate_up has {I2} gate+up rows, which is odd")
+    # every array the C call reads, at the shape it assumes for (fmt, layout, E, H, I)
+    if fmt == FMT_FP8_B128:
+        _shape(down, "down", (E, I, H) if transposed else (E, H, I))
+        for name, t in (("gate_up_scale", gate_up_scale), ("down_scale", down_scale)):
+            if t is None or t.dtype != torch.float32 or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous float32 tensor")
+        _shape(gate_up_scale, "gate_up_scale",
+               (E, H // 128, I2 // 128) if transposed else (E, I2 // 128, H // 128))
+        _shape(down_scale, "down_scale", (E, I // 128, H // 128) if transposed else (E, H // 128, I // 128))
+    elif fmt == FMT_MXFP8A_MXFP4W:
+        _shape(down, "down", (E, H, I // 2))
+        for name, t in (("gate_up_scale", gate_up_scale), ("down_scale", down_scale)):
+            if t is None or t.dtype not in (torch.uint8, torch.int8) or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous uint8 tensor of UE8M0 bytes")
+        _shape(gate_up_scale, "gate_up_scale", (E, I2, H // 32))
+        _shape(down_scale, "down_scale", (E, H, I // 32))
+    else:
+        _shape(down, "down", (E, I, H) if transposed else (E, H, I))
+    read = [("gate_up", gate_up), ("down", down)]
+    if fmt != FMT_BF16:
+        read += [("gate_up_scale", gate_up_scale), ("down_scale", down_scale)]
+    for name, t in read:
+        if t.device != dev:
+            raise RuntimeError(f"{name} is on {t.device}, expected {dev} (one device per process)")
     desc = MoeWeights()
     nbytes = lib.moe_prepared_weights_size(fmt, E, H, I)
     prepared = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
@@ -365,8 +453,11 @@ def forward_workspace_bytes(T: int, k: int, weights: Weights) -> int:
 
 
 def _workspace(T: int, k: int, weights: Weights, device) -> torch.Tensor:
+    # one cached workspace per (device, stream, layer shape): two forwards on
+    # different streams must not share scratch while both run, and forwards on
+    # one stream run one after the other
     need = forward_workspace_bytes(_pow2_tokens(T), k, weights)
-    key = (device, weights.E, weights.H, weights.I, weights.fmt, k)
+    key = (device, _stream(device), weights.E, weights.H, weights.I, weights.fmt, k)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < need:
         ws = torch.empty(need, dtype=torch.uint8, device=device)
@@ -374,14 +465,29 @@ def _workspace(T: int, k: int, weights: Weights, device) -> torch.Tensor:
     return ws
 
 
-def _options(swiglu_limit, expert_begin, invalid_count):
+def _options(swiglu_limit, expert_begin, invalid_count, act_scales=None, act_stride=0):
     opt = MoeOptions()
     opt.has_swiglu_limit = 0 if swiglu_limit is None else 1
     opt.swiglu_limit = 0.0 if swiglu_limit is None else float(swiglu_limit)
     opt.expert_begin = expert_begin
-    opt.static_activation_scales = 0
+    opt.static_activation_scales = 0 if act_scales is None else 1
     opt.invalid_count = _ptr(invalid_count)
+    opt.act_scales = _ptr(act_scales)
+    opt.act_scales_row_stride = act_stride
     return opt
+
+
+def _scheme(activation_scheme: str, act_scales, weights, T, H, device):
+    """Static scales (and their row stride) for the forward, or (None, 0)."""
+    if activation_scheme not in ("dynamic", "static"):
+        raise ValueError(f"activation_scheme must be 'dynamic' or 'static', got {activation_scheme!r}")
+    if activation_scheme == "dynamic":
+        if act_scales is not None:
+            raise ValueError("act_scales are the static scheme's; pass activation_scheme='static'")
+        return None, 0
+    if act_scales is None:
+        raise ValueError("activation_scheme='static' needs the precomputed per-block act_scales")
+    return act_scales, _static_scales(act_scales, weights.fmt, T, H, device)
 
 
 def experts_forward_from_logits(hidden_states: torch.Tensor, router_logits: torch.Tensor, k: int,
@@ -390,7 +496,8 @@ def experts_forward_from_logits(hidden_states: torch.Tensor, router_logits: torc
                                 top_k_index: Optional[torch.Tensor] = None,
                                 top_k_weights: Optional[torch.Tensor] = None,
                                 workspace: Optional[torch.Tensor] = None,
-                                invalid_count: Optional[torch.Tensor] = None):
+                                invalid_count: Optional[torch.Tensor] = None,
+                                activation_scheme: str = "dynamic", act_scales: Optional[torch.Tensor] = None):
     """The experts forward from the router's logits (see route_topk): returns
     (out bf16 [T, H], top_k_index int32 [T, k], top_k_weights fp32 [T, k])."""
     lib = load_library()
@@ -399,21 +506,27 @@ def experts_forward_from_logits(hidden_states: torch.Tensor, router_logits: torc
     dev = hidden_states.device
     _need(hidden_states, "hidden_states", torch.bfloat16, dev)
     _need(router_logits, "router_logits", torch.float32, dev)
+    if hidden_states.dim() != 2 or router_logits.dim() != 2:
+        raise ValueError("hidden_states and router_logits must be 2-D")
     T, H = hidden_states.shape
     n = router_logits.shape[1]
     if router_logits.shape[0] != T:
         raise ValueError(f"router_logits has {router_logits.shape[0]} rows for {T} tokens")
     if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((T, weights.H), dtype=torch.bfloat16, device=dev)
     if top_k_index is None:
         top_k_index = torch.empty((T, k), dtype=torch.int32, device=dev)
     if top_k_weights is None:
         top_k_weights = torch.empty((T, k), dtype=torch.float32, device=dev)
     _need(top_k_index, "top_k_index", torch.int32, dev)
     _need(top_k_weights, "top_k_weights", torch.float32, dev)
+    _need(out, "out", torch.bfloat16, dev)
+    _shape(top_k_index, "top_k_index", (T, k))
+    _check_forward_shapes(hidden_states, top_k_index, top_k_weights, weights, out)
+    asc, astride = _scheme(activation_scheme, act_scales, weights, T, H, dev)
     if T > 0 and workspace is None:
         workspace = _workspace(T, k, weights, dev)
-    opt = _options(swiglu_limit, expert_begin, invalid_count)
+    opt = _options(swiglu_limit, expert_begin, invalid_count, asc, astride)
     _check(lib.moe_experts_forward_from_logits(ctypes.byref(weights.desc), _ptr(hidden_states), _ptr(router_logits), T,
                                                n, k, 1 if renormalize else 0, ctypes.byref(opt), _ptr(top_k_index),
                                                _ptr(top_k_weights), _ptr(out), _ptr(workspace),
@@ -425,30 +538,35 @@ def experts_forward(hidden_states: torch.Tensor, top_k_index: torch.Tensor, top_
                     weights: Weights, swiglu_limit: Optional[float] = None, expert_begin: int = 0,
                     activation_scheme: str = "dynamic", out: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, invalid_count: Optional[torch.Tensor] = None,
-                    debug: Optional[dict] = None) -> torch.Tensor:
+                    debug: Optional[dict] = None, act_scales: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The fused experts forward: out[t] = sum_j w[t, j] * expert_{id[t, j]}(hidden_states[t]).
 
     hidden_states bf16 [T, H]; top_k_index int32 [T, k] (global ids, -1 skips the
     slot); top_k_weights fp32 [T, k].  Returns bf16 [T, H].
+    activation_scheme "dynamic" quantizes hidden_states per block from its own
+    amax; "static" uses act_scales, the precomputed block scales (fp32
+    [T, H/128] for FP8_B128, uint8 UE8M0 [T, H/32] for MX, or one [H/B] row
+    for every token).
     """
     lib = load_library()
     if hidden_states.dtype != torch.bfloat16:
         raise ValueError(f"the experts forward requires bfloat16 hidden states, got {hidden_states.dtype}")
-    if activation_scheme == "static":
-        raise NotImplementedError("activations are quantized dynamically per block; static scales are not supported")
     dev = hidden_states.device
     _need(hidden_states, "hidden_states", torch.bfloat16, dev)
     _need(top_k_index, "top_k_index", torch.int32, dev)
     _need(top_k_weights, "top_k_weights", torch.float32, dev)
+    _check_forward_shapes(hidden_states, top_k_index, top_k_weights, weights, out)
     T, H = hidden_states.shape
     k = top_k_index.shape[1]
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    asc, astride = _scheme(activation_scheme, act_scales, weights, T, H, dev)
     if T == 0:
         return out
     if workspace is None:
         workspace = _workspace(T, k, weights, dev)
-    opt = _options(swiglu_limit, expert_begin, invalid_count)
+    opt = _options(swiglu_limit, expert_begin, invalid_count, asc, astride)
     dbg = None
     if debug is not None:
         S = T * k
@@ -457,8 +575,13 @@ def experts_forward(hidden_states: torch.Tensor, top_k_index: torch.Tensor, top_
         debug["act_codes"] = torch.empty((H // 128, T, 128), dtype=torch.uint8, device=dev)
         debug["act_scales"] = torch.empty(_scale_shape(weights.fmt, H, T), dtype=_scale_dtype(weights.fmt),
                                           device=dev)
+        if weights.fmt != FMT_BF16:
+            I = weights.I
+            debug["h_codes"] = torch.empty((I // 128, S, 128), dtype=torch.uint8, device=dev)
+            debug["h_scales"] = torch.empty(_scale_shape(weights.fmt, I, S), dtype=_scale_dtype(weights.fmt),
+                                            device=dev)
         dbg = MoeDebug(_ptr(debug["sorted_slot"]), _ptr(debug["expert_offsets"]), _ptr(debug["act_codes"]),
-                       _ptr(debug["act_scales"]))
+                       _ptr(debug["act_scales"]), _ptr(debug.get("h_codes")), _ptr(debug.get("h_scales")))
         opt.debug = ctypes.pointer(dbg)
     _check(lib.moe_experts_forward(ctypes.byref(weights.desc), _ptr(hidden_states), _ptr(top_k_index),
                                    _ptr(top_k_weights), T, k, ctypes.byref(opt), _ptr(out), _ptr(workspace),

@@ -51,6 +51,19 @@ __device__ __forceinline__ float swiglu(float g, float u, float limit) {
 // Block scale of the FP8_B128 format: max(amax, 1e-4) / 448 with IEEE fp32 division.
 __device__ __forceinline__ float fp8_block_scale(float amax) { return __builtin_fmaxf(amax, 1e-4f) / 448.0f; }
 
+// x / s as the FP8_B128 rule writes it (an IEEE fp32 quotient), from r = 1 / s
+// (one IEEE reciprocal per block): the product q0 = x r, its exact residual
+// x - s q0 (one fma) and one correction step (Markstein's division by
+// reciprocal), which is the correctly rounded quotient wherever nothing
+// underflows; the copysign keeps -0.  Where |x / s| is below 2^-10 the result
+// may differ from the quotient, but both encode to the same signed e4m3 zero.
+// Checked on the host against the IEEE quotient: exhaustively for bf16 x and
+// every scale the rule gives, and on seeded fp32 x (the SwiGLU output h).
+__device__ __forceinline__ float div_by_scale(float x, float s, float r) {
+  const float q0 = __fmul_rn(x, r);
+  return __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-s, q0, x), r, q0), x);
+}
+
 // MX format: e = ceil(log2(max(amax, 1e-4) / 448)) read from the fp32 bits of
 // the (always normal) ratio: the exponent, plus one when a mantissa bit is set.
 __device__ __forceinline__ int mx_block_exponent(float amax) {

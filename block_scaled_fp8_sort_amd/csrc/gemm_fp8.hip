@@ -352,11 +352,13 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Mis
       const float amax = __builtin_fmaxf(misc.amax[0][tt], misc.amax[1][tt]);
       const float s = fp8_block_scale(amax);
       const float inv = 1.0f / s;
+      // h / s as the activation rule's IEEE quotient (div_by_scale)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const v4f h = acc[2 * q][ti];
         *(uint32_t*)(area + tt * kHPitch + 16 * (wn * 4 + q) + 4 * g) =
-            e4m3x4(h[0] * inv, h[1] * inv, h[2] * inv, h[3] * inv);
+            e4m3x4(div_by_scale(h[0], s, inv), div_by_scale(h[1], s, inv), div_by_scale(h[2], s, inv),
+                   div_by_scale(h[3], s, inv));
       }
       const int r = m0 + tt;
       if (r < m_end && wn == 0 && g == 0) ((float*)p.h_scales)[(size_t)n_tile * p.max_rows + r] = s;

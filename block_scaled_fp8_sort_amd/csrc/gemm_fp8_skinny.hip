@@ -202,7 +202,10 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, Misc& misc, const 
     const float inv = 1.0f / sc;
     if (r < s.m_end) {
       uint8_t* plane = p.h_codes + (size_t)s.n_tile * p.max_rows * 128;
-      *(uint32_t*)(plane + (size_t)r * 128 + 16 * wave + 4 * g) = e4m3x4(h[0] * inv, h[1] * inv, h[2] * inv, h[3] * inv);
+      // h / sc as the activation rule's IEEE quotient (div_by_scale)
+      *(uint32_t*)(plane + (size_t)r * 128 + 16 * wave + 4 * g) =
+          e4m3x4(div_by_scale(h[0], sc, inv), div_by_scale(h[1], sc, inv), div_by_scale(h[2], sc, inv),
+                 div_by_scale(h[3], sc, inv));
       if (wave == 0 && g == 0) ((float*)p.h_scales)[(size_t)s.n_tile * p.max_rows + r] = sc;
     }
   } else {  // kEpiWeightedScatter

@@ -51,6 +51,15 @@ struct RouterArgs {
   float* weights;       // [T, k] out
 };
 
+// Precomputed activation scales of the static scheme: row t's block scales
+// (fp32 per 1x128 block, or UE8M0 bytes per 1x32 block) start `stride`
+// elements after row t - 1's; stride 0 gives every row the same scales.  A
+// launcher given a NULL StaticScales* quantizes dynamically.
+struct StaticScales {
+  const void* p;
+  int32_t stride;
+};
+
 size_t route_sort_lds_bytes(int32_t E);
 // Device workspace the sort of S slots needs (0 for the one-workgroup path).
 size_t route_sort_ws_bytes(int32_t S, int32_t E);
@@ -76,11 +85,13 @@ hipError_t launch_route_sort_and_quant(const RouterArgs* router, const int32_t* 
                                       int32_t expert_begin, int32_t* sorted_slot, int32_t* offsets,
                                       int32_t* invalid_count, void* sort_ws, const uint16_t* x, int32_t rows,
                                       int32_t H, int fmt, uint8_t* codes, void* scales, int32_t* zero,
-                                      int32_t n_zero, hipStream_t stream, void* sorted_scales = nullptr);
+                                      int32_t n_zero, hipStream_t stream, void* sorted_scales = nullptr,
+                                      const StaticScales* static_scales = nullptr);
 // The router alone (no sort).
 hipError_t launch_router_only(const RouterArgs& router, int32_t T, int32_t k, hipStream_t stream);
+// static_scales non-NULL: the caller's block scales instead of the amax rule.
 hipError_t launch_quant_act(const uint16_t* x, int32_t rows, int32_t H, int fmt, uint8_t* codes, void* scales,
-                            hipStream_t stream);
+                            hipStream_t stream, const StaticScales* static_scales = nullptr);
 // The activation scales of T token rows ([H/128][T] fp32, or [H/128][T][4]
 // UE8M0 bytes) copied by sorted row: dst [H/128][T * k], row r taking token
 // sorted_slot[r] / k.

@@ -4,9 +4,9 @@
 // (gfx950, pointers on the stream's device); then the kernels are enqueued.
 //
 // The refusals mirror the pages' guards, which all fire before any kernel work:
-// non-bf16 hidden states (ValueError), static activation scales and non-int8 FP4
-// weights (NotImplementedError), a model spread over several devices in one
-// process (RuntimeError), and a device that cannot serve the dtypes ("DeepGEMM
+// non-bf16 hidden states (ValueError), non-int8 FP4 weights
+// (NotImplementedError), a model spread over several devices in one process
+// (RuntimeError), and a device that cannot serve the dtypes ("DeepGEMM
 // experts selected on a model spanning multiple CUDA devices", the record's
 // source; "DeepGEMM Mega MoE requires FP4-packed expert weights (dtype=int8)",
 // section "Source").
@@ -16,7 +16,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
+#include <utility>
 #include <string>
 
 #include "internal.h"
@@ -103,6 +105,15 @@ moe_status check_ptr(const void* p, int dev, const char* name) {
   return MOE_OK;
 }
 
+// Every non-NULL pointer of the list must pass check_ptr.
+moe_status check_ptrs(int dev, std::initializer_list<std::pair<const void*, const char*>> ptrs) {
+  for (const auto& pr : ptrs) {
+    const moe_status st = check_ptr(pr.first, dev, pr.second);
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
 moe_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return MOE_OK;
   return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -186,6 +197,16 @@ moe_status validate_gemm(const moe_gemm_args* a) {
     default:
       return fail(MOE_ERR_UNSUPPORTED, "unknown epilogue %d", (int)a->epilogue);
   }
+  // the epilogue's outputs must not alias what the launch reads
+  const void* outs[] = {a->epilogue == MOE_EPI_STORE_F32 ? (const void*)a->c_f32 : nullptr,
+                        a->epilogue == MOE_EPI_SWIGLU_QUANT ? (const void*)a->h_codes : nullptr,
+                        a->epilogue == MOE_EPI_SWIGLU_QUANT ? (const void*)a->h_scales : nullptr,
+                        a->epilogue == MOE_EPI_WEIGHTED_SCATTER ? (const void*)a->slot_out : nullptr};
+  const void* ins[] = {a->a_codes, a->a_scales, a->a_row_index, a->expert_offsets, a->a_scales_sorted,
+                       a->top_k_weights, a->slot_of_row, a->tile_counters};
+  for (const void* o : outs)
+    for (const void* i : ins)
+      if (o && o == i) return fail(MOE_ERR_UNSUPPORTED, "an epilogue output aliases an input of the launch");
   return MOE_OK;
 }
 
@@ -245,10 +266,15 @@ moe_status forward_impl(const moe_weights* w, const uint16_t* hidden_states, con
   const bool has_limit = opt && opt->has_swiglu_limit;
   if (has_limit && !(std::isfinite(opt->swiglu_limit) && opt->swiglu_limit > 0.0f))
     return fail(MOE_ERR_SHAPE, "swiglu_limit must be finite and > 0");
-  if (opt && opt->static_activation_scales)
-    return fail(MOE_ERR_UNSUPPORTED,
-                "the grouped experts path quantizes activations dynamically per block; static activation scales "
-                "are not supported");
+  const bool stat = opt && opt->static_activation_scales;
+  if (stat) {
+    if (w->fmt == MOE_FMT_BF16)
+      return fail(MOE_ERR_UNSUPPORTED, "static activation scales need a quantized format (the bf16 experts quantize nothing)");
+    const int32_t nb = w->H / (w->fmt == MOE_FMT_FP8_B128 ? 128 : 32);
+    if (opt->act_scales_row_stride < 0 || (opt->act_scales_row_stride > 0 && opt->act_scales_row_stride < nb))
+      return fail(MOE_ERR_SHAPE, "act_scales_row_stride=%d: 0 or at least one row of %d block scales",
+                  opt->act_scales_row_stride, nb);
+  }
   if (router) {
     if (router->n_experts < 1 || router->n_experts > kMaxE)
       return fail(MOE_ERR_SHAPE, "n_experts=%d outside [1, %d]", router->n_experts, kMaxE);
@@ -262,7 +288,11 @@ moe_status forward_impl(const moe_weights* w, const uint16_t* hidden_states, con
   if (T == 0) return ok();
   if (!hidden_states || !top_k_index || !top_k_weights || !out || (router && !router->logits))
     return fail(MOE_ERR_NULL, "hidden_states / router_logits / top_k_index / top_k_weights / out is NULL");
-  if ((const void*)out == (const void*)hidden_states) return fail(MOE_ERR_UNSUPPORTED, "out must not alias input");
+  if (stat && !opt->act_scales) return fail(MOE_ERR_NULL, "static activation scales requested but act_scales is NULL");
+  if (stat && (const void*)out == opt->act_scales) return fail(MOE_ERR_UNSUPPORTED, "out must not alias an input");
+  if ((const void*)out == (const void*)hidden_states || (const void*)out == (const void*)top_k_index ||
+      (const void*)out == (const void*)top_k_weights)
+    return fail(MOE_ERR_UNSUPPORTED, "out must not alias an input");
   if (router) {
     const void* o[] = {top_k_index, top_k_weights, out};
     for (const void* q : o)
@@ -277,11 +307,25 @@ moe_status forward_impl(const moe_weights* w, const uint16_t* hidden_states, con
     return fail(MOE_ERR_WORKSPACE, "workspace holds %zu bytes, %zu needed", ws ? ws_bytes : (size_t)0, L.total);
   int dev, cus;
   if ((st = check_device(stream, &dev, &cus)) != MOE_OK) return st;
-  for (auto pr : {std::make_pair((const void*)hidden_states, "hidden_states"),
-                  std::make_pair((const void*)top_k_index, "top_k_index"), std::make_pair((const void*)out, "out"),
-                  std::make_pair((const void*)w->w13, "w13"), std::make_pair((const void*)w->w2, "w2"),
-                  std::make_pair((const void*)ws, "workspace")})
-    if ((st = check_ptr(pr.first, dev, pr.second)) != MOE_OK) return st;
+  const moe_debug* dbg = opt ? opt->debug : nullptr;
+  if ((st = check_ptrs(dev, {{hidden_states, "hidden_states"},
+                             {top_k_index, "top_k_index"},
+                             {top_k_weights, "top_k_weights"},
+                             {out, "out"},
+                             {w->w13, "w13"},
+                             {w->w13_scale, "w13_scale"},
+                             {w->w2, "w2"},
+                             {w->w2_scale, "w2_scale"},
+                             {ws, "workspace"},
+                             {opt ? opt->invalid_count : nullptr, "invalid_count"},
+                             {stat ? opt->act_scales : nullptr, "act_scales"},
+                             {dbg ? dbg->sorted_slot : nullptr, "debug.sorted_slot"},
+                             {dbg ? dbg->expert_offsets : nullptr, "debug.expert_offsets"},
+                             {dbg ? dbg->act_codes : nullptr, "debug.act_codes"},
+                             {dbg ? dbg->act_scales : nullptr, "debug.act_scales"},
+                             {dbg ? dbg->h_codes : nullptr, "debug.h_codes"},
+                             {dbg ? dbg->h_scales : nullptr, "debug.h_scales"}})) != MOE_OK)
+    return st;
 
   const int E = w->E, H = w->H, I = w->I;
   const int32_t S = T * k;
@@ -303,11 +347,14 @@ moe_status forward_impl(const moe_weights* w, const uint16_t* hidden_states, con
     he = moe::launch_route_sort_zero(router, top_k_index, T, k, E, expert_begin, sorted_slot, offsets, nullptr,
                                      opt ? opt->invalid_count : nullptr, base + L.sort_ws, sched,
                                      2 * MOE_TILE_COUNTERS_BYTES / 4, stream);
-  else
+  else {
+    const moe::StaticScales sts{stat ? opt->act_scales : nullptr, stat ? opt->act_scales_row_stride : 0};
     he = moe::launch_route_sort_and_quant(router, top_k_index, T, k, E, expert_begin, sorted_slot, offsets,
                                           opt ? opt->invalid_count : nullptr, base + L.sort_ws, hidden_states, T, H,
                                           w->fmt, act_codes, act_scales, sched, 2 * MOE_TILE_COUNTERS_BYTES / 4,
-                                          stream, L.sorted_scales ? base + L.act_scales_sorted : nullptr);
+                                          stream, L.sorted_scales ? base + L.act_scales_sorted : nullptr,
+                                          stat ? &sts : nullptr);
+  }
   if (he != hipSuccess) return hip_status(he, "route sort / quant launch");
 
   moe::GemmParams p1{};
@@ -369,7 +416,12 @@ moe_status forward_impl(const moe_weights* w, const uint16_t* hidden_states, con
          (he = hipMemcpyAsync(d->act_codes, act_codes, (size_t)T * H, hipMemcpyDeviceToDevice, stream)) !=
              hipSuccess) ||
         (d->act_scales && !bf &&
-         (he = hipMemcpyAsync(d->act_scales, act_scales, sc_bytes, hipMemcpyDeviceToDevice, stream)) != hipSuccess))
+         (he = hipMemcpyAsync(d->act_scales, act_scales, sc_bytes, hipMemcpyDeviceToDevice, stream)) != hipSuccess) ||
+        (d->h_codes && !bf &&
+         (he = hipMemcpyAsync(d->h_codes, h_codes, (size_t)S * I, hipMemcpyDeviceToDevice, stream)) != hipSuccess) ||
+        (d->h_scales && !bf &&
+         (he = hipMemcpyAsync(d->h_scales, h_scales, mx ? (size_t)S * (I / 32) : 4 * (size_t)S * (I / 128),
+                              hipMemcpyDeviceToDevice, stream)) != hipSuccess))
       return hip_status(he, "debug copy");
   }
   return ok();
@@ -425,10 +477,12 @@ moe_status moe_route_sort(const int32_t* top_k_index, int32_t T, int32_t k, int3
   int dev, cus;
   moe_status st = check_device(stream, &dev, &cus);
   if (st != MOE_OK) return st;
-  for (auto pr : {std::make_pair((const void*)top_k_index, "top_k_index"),
-                  std::make_pair((const void*)sorted_slot, "sorted_slot"),
-                  std::make_pair((const void*)expert_offsets, "expert_offsets")})
-    if ((st = check_ptr(pr.first, dev, pr.second)) != MOE_OK) return st;
+  if ((st = check_ptrs(dev, {{top_k_index, "top_k_index"},
+                             {sorted_slot, "sorted_slot"},
+                             {expert_offsets, "expert_offsets"},
+                             {slot_pos, "slot_pos"},
+                             {invalid_count, "invalid_count"}})) != MOE_OK)
+    return st;
   if (ws_need > 0 && (st = check_ptr(ws, dev, "workspace")) != MOE_OK) return st;
   st = hip_status(moe::launch_route_sort(nullptr, top_k_index, T, k, E, expert_begin, sorted_slot, expert_offsets,
                                          slot_pos, invalid_count, ws, stream),
@@ -471,12 +525,14 @@ moe_status moe_route_topk(const float* router_logits, int32_t T, int32_t n_exper
   int dev, cus;
   moe_status st = check_device(stream, &dev, &cus);
   if (st != MOE_OK) return st;
-  for (auto pr : {std::make_pair((const void*)router_logits, "router_logits"),
-                  std::make_pair((const void*)top_k_index, "top_k_index"),
-                  std::make_pair((const void*)top_k_weights, "top_k_weights"),
-                  std::make_pair((const void*)sorted_slot, "sorted_slot"),
-                  std::make_pair((const void*)expert_offsets, "expert_offsets")})
-    if ((st = check_ptr(pr.first, dev, pr.second)) != MOE_OK) return st;
+  if ((st = check_ptrs(dev, {{router_logits, "router_logits"},
+                             {top_k_index, "top_k_index"},
+                             {top_k_weights, "top_k_weights"},
+                             {sorted_slot, "sorted_slot"},
+                             {expert_offsets, "expert_offsets"},
+                             {slot_pos, "slot_pos"},
+                             {invalid_count, "invalid_count"}})) != MOE_OK)
+    return st;
   if (ws_need > 0 && (st = check_ptr(ws, dev, "workspace")) != MOE_OK) return st;
   const moe::RouterArgs r{router_logits, n_experts, renormalize ? 1 : 0, top_k_index, top_k_weights};
   hipError_t he;
@@ -501,8 +557,32 @@ moe_status moe_quant_act(const uint16_t* x, int32_t rows, int32_t H, moe_format 
   int dev, cus;
   moe_status st = check_device(stream, &dev, &cus);
   if (st != MOE_OK) return st;
-  if ((st = check_ptr(x, dev, "x")) != MOE_OK || (st = check_ptr(codes, dev, "codes")) != MOE_OK) return st;
+  if ((st = check_ptrs(dev, {{x, "x"}, {codes, "codes"}, {scales, "scales"}})) != MOE_OK) return st;
   st = hip_status(moe::launch_quant_act(x, rows, H, (int)fmt, codes, scales, stream), "quant launch");
+  return st == MOE_OK ? ok() : st;
+}
+
+moe_status moe_quant_act_static(const uint16_t* x, int32_t rows, int32_t H, moe_format fmt, const void* act_scales,
+                                int32_t row_stride, uint8_t* codes, void* scales, hipStream_t stream) {
+  if (!valid_fmt(fmt)) return fail(MOE_ERR_UNSUPPORTED, "unknown format %d", (int)fmt);
+  if (fmt == MOE_FMT_BF16) return fail(MOE_ERR_UNSUPPORTED, "MOE_FMT_BF16 has no activation quantization");
+  if (rows < 0) return fail(MOE_ERR_SHAPE, "rows=%d < 0", rows);
+  if (H <= 0 || H % 128) return fail(MOE_ERR_SHAPE, "H=%d must be a positive multiple of 128", H);
+  const int32_t nb = H / (fmt == MOE_FMT_FP8_B128 ? 128 : 32);
+  if (row_stride < 0 || (row_stride > 0 && row_stride < nb))
+    return fail(MOE_ERR_SHAPE, "row_stride=%d: 0 or at least one row of %d block scales", row_stride, nb);
+  if (rows > 0 && (!x || !codes || !scales || !act_scales)) return fail(MOE_ERR_NULL, "x / act_scales / codes / scales is NULL");
+  if ((const void*)x == (const void*)codes || (const void*)x == scales || act_scales == (const void*)codes ||
+      act_scales == scales)
+    return fail(MOE_ERR_UNSUPPORTED, "outputs must not alias the inputs");
+  if (rows == 0) return ok();
+  int dev, cus;
+  moe_status st = check_device(stream, &dev, &cus);
+  if (st != MOE_OK) return st;
+  if ((st = check_ptrs(dev, {{x, "x"}, {act_scales, "act_scales"}, {codes, "codes"}, {scales, "scales"}})) != MOE_OK)
+    return st;
+  const moe::StaticScales sts{act_scales, row_stride};
+  st = hip_status(moe::launch_quant_act(x, rows, H, (int)fmt, codes, scales, stream, &sts), "quant launch");
   return st == MOE_OK ? ok() : st;
 }
 
@@ -544,6 +624,12 @@ moe_status moe_prepare_weights(moe_format fmt, moe_layout layout, int32_t E, int
   int dev, cus;
   moe_status st = check_device(stream, &dev, &cus);
   if (st != MOE_OK) return st;
+  if ((st = check_ptrs(dev, {{gate_up, "gate_up"},
+                             {bf ? nullptr : gate_up_scale, "gate_up_scale"},
+                             {down, "down"},
+                             {bf ? nullptr : down_scale, "down_scale"},
+                             {prepared, "prepared"}})) != MOE_OK)
+    return st;
   const size_t A = 256;
   const size_t e = E, h = H, i = I;
   if (bf) {
@@ -622,11 +708,27 @@ moe_status moe_grouped_gemm(const moe_gemm_args* args, hipStream_t stream) {
   if (args->max_rows == 0) return ok();
   int dev, cus;
   if ((st = check_device(stream, &dev, &cus)) != MOE_OK) return st;
-  if ((st = check_ptr(args->a_codes, dev, "a_codes")) != MOE_OK ||
-      (st = check_ptr(args->weights->w13, dev, "weights")) != MOE_OK)
+  // every pointer this launch dereferences: the weight it multiplies by, the
+  // operand and the outputs and inputs of its epilogue
+  const moe_weights* wt = args->weights;
+  const bool bf = wt->fmt == MOE_FMT_BF16;
+  const moe_epilogue epi = args->epilogue;
+  if ((st = check_ptrs(dev, {{args->which == 0 ? wt->w13 : wt->w2, args->which == 0 ? "weights.w13" : "weights.w2"},
+                             {bf ? nullptr : (args->which == 0 ? wt->w13_scale : wt->w2_scale),
+                              args->which == 0 ? "weights.w13_scale" : "weights.w2_scale"},
+                             {args->a_codes, "a_codes"},
+                             {bf ? nullptr : args->a_scales, "a_scales"},
+                             {args->a_row_index, "a_row_index"},
+                             {args->expert_offsets, "expert_offsets"},
+                             {epi == MOE_EPI_STORE_F32 ? args->c_f32 : nullptr, "c_f32"},
+                             {epi == MOE_EPI_SWIGLU_QUANT ? args->h_codes : nullptr, "h_codes"},
+                             {epi == MOE_EPI_SWIGLU_QUANT && !bf ? args->h_scales : nullptr, "h_scales"},
+                             {epi == MOE_EPI_WEIGHTED_SCATTER ? args->slot_out : nullptr, "slot_out"},
+                             {epi == MOE_EPI_WEIGHTED_SCATTER ? args->top_k_weights : nullptr, "top_k_weights"},
+                             {epi == MOE_EPI_WEIGHTED_SCATTER ? args->slot_of_row : nullptr, "slot_of_row"},
+                             {args->tile_counters, "tile_counters"},
+                             {bf ? nullptr : args->a_scales_sorted, "a_scales_sorted"}})) != MOE_OK)
     return st;
-  if (args->tile_counters && (st = check_ptr(args->tile_counters, dev, "tile_counters")) != MOE_OK) return st;
-  if (args->a_scales_sorted && (st = check_ptr(args->a_scales_sorted, dev, "a_scales_sorted")) != MOE_OK) return st;
   const moe::GemmParams p = to_params(args);
   const bool paired = args->which == 0;
   st = hip_status(launch_gemm(p, args->weights->fmt, (int)args->epilogue, paired, cus, stream),

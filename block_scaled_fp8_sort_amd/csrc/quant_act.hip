@@ -1,8 +1,11 @@
-// Dynamic per-block activation quantization of bf16 rows.
+// Per-block activation quantization of bf16 rows.
 //
-// The grouped experts dispatch quantizes activations dynamically per block and
-// cannot take precomputed scales ("grouped_mm experts dispatch does not support
-// activation_scheme='static'", section "What it means").  Block rule:
+// The pages' grouped experts dispatch quantizes activations dynamically per
+// block, and the eager one also takes the static scheme's precomputed scales
+// ("grouped_mm experts dispatch does not support activation_scheme='static'",
+// sections "What it means" and "Example fix"); both are served here, the
+// static one by reading the caller's block scales instead of the amax.  Block
+// rule:
 //  FP8_B128 (blocks of 128): s = max(amax, 1e-4) / 448 (fp32), code = e4m3(x / s)
 //  with x / s the IEEE fp32 quotient, so codes match a host implementation bit
 //  for bit (computed from one reciprocal per block, see quant_chunk).
@@ -28,15 +31,15 @@ namespace moe {
 
 namespace {
 
-template <int BLOCK>
+template <int BLOCK, bool STATIC>
 __global__ __launch_bounds__(256) void quant_act_kernel(const uint4* __restrict__ x, int64_t n_chunks, int32_t rows,
                                                         int32_t H, uint8_t* __restrict__ codes,
-                                                        void* __restrict__ scales) {
+                                                        void* __restrict__ scales, StaticScales st) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   // n_chunks and the stride are multiples of the lanes of one block, so every
   // lane group stays together
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n_chunks; c += stride)
-    quant_chunk<BLOCK>(x, c, rows, H, codes, scales);
+    quant_chunk<BLOCK, STATIC>(x, c, rows, H, codes, scales, st);
 }
 
 // The activation scales by sorted row: dst[kb][r] = scales[kb][sorted_slot[r] / k]
@@ -70,18 +73,29 @@ hipError_t launch_gather_scales(const void* scales, const int32_t* sorted_slot, 
 }
 
 hipError_t launch_quant_act(const uint16_t* x, int32_t rows, int32_t H, int fmt, uint8_t* codes, void* scales,
-                            hipStream_t stream) {
+                            hipStream_t stream, const StaticScales* st) {
   const int64_t n_chunks = (int64_t)rows * H / 8;
   if (n_chunks == 0) return hipSuccess;
   const int threads = 256;
   const int64_t want = (n_chunks + threads - 1) / threads;
   const int blocks = (int)(want < 256 * 64 ? want : 256 * 64);
-  if (fmt == 0)
-    hipLaunchKernelGGL(quant_act_kernel<128>, dim3(blocks), dim3(threads), 0, stream, (const uint4*)x, n_chunks,
-                       rows, H, codes, scales);
-  else
-    hipLaunchKernelGGL(quant_act_kernel<32>, dim3(blocks), dim3(threads), 0, stream, (const uint4*)x, n_chunks, rows,
-                       H, codes, scales);
+  const dim3 g(blocks), b(threads);
+  const StaticScales none{nullptr, 0};
+  if (fmt == 0) {
+    if (st)
+      hipLaunchKernelGGL((quant_act_kernel<128, true>), g, b, 0, stream, (const uint4*)x, n_chunks, rows, H, codes,
+                         scales, *st);
+    else
+      hipLaunchKernelGGL((quant_act_kernel<128, false>), g, b, 0, stream, (const uint4*)x, n_chunks, rows, H, codes,
+                         scales, none);
+  } else {
+    if (st)
+      hipLaunchKernelGGL((quant_act_kernel<32, true>), g, b, 0, stream, (const uint4*)x, n_chunks, rows, H, codes,
+                         scales, *st);
+    else
+      hipLaunchKernelGGL((quant_act_kernel<32, false>), g, b, 0, stream, (const uint4*)x, n_chunks, rows, H, codes,
+                         scales, none);
+  }
   return hipGetLastError();
 }
 

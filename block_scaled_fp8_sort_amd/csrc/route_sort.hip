@@ -445,13 +445,13 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(const RouterAr
 // each too small to fill the chip, so one launch runs both: workgroup 0 sorts,
 // the others quantize (a grid-stride loop whose stride is a multiple of the
 // lanes of one quantization block).
-template <int BLOCK>
+template <int BLOCK, bool STATIC>
 __global__ __launch_bounds__(kSortThreads) void route_quant_kernel(
     const RouterArgs router, const int32_t* ids, int32_t T, int32_t k, int32_t E, int32_t expert_begin,
     int32_t* __restrict__ sorted_slot,
     int32_t* __restrict__ offsets, int32_t* __restrict__ invalid_count, const uint4* __restrict__ x,
     int64_t n_chunks, int32_t rows, int32_t H, uint8_t* __restrict__ codes, void* __restrict__ scales,
-    int32_t* __restrict__ zero, int32_t n_zero) {
+    int32_t* __restrict__ zero, int32_t n_zero, StaticScales st) {
   if (blockIdx.x == 1 || gridDim.x == 1)
     for (int i = threadIdx.x; i < n_zero; i += blockDim.x) zero[i] = 0;
   if (blockIdx.x == 0) {
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(kSortThreads) void route_quant_kernel(
   }
   const int64_t stride = (int64_t)(gridDim.x - 1) * blockDim.x;
   for (int64_t c = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x; c < n_chunks; c += stride)
-    quant_chunk<BLOCK>(x, c, rows, H, codes, scales);
+    quant_chunk<BLOCK, STATIC>(x, c, rows, H, codes, scales, st);
 }
 
 }  // namespace
@@ -562,7 +562,8 @@ hipError_t launch_route_sort_and_quant(const RouterArgs* router, const int32_t* 
                                       int32_t expert_begin, int32_t* sorted_slot, int32_t* offsets,
                                       int32_t* invalid_count, void* sort_ws, const uint16_t* x, int32_t rows,
                                       int32_t H, int fmt, uint8_t* codes, void* scales, int32_t* zero,
-                                      int32_t n_zero, hipStream_t stream, void* sorted_scales) {
+                                      int32_t n_zero, hipStream_t stream, void* sorted_scales,
+                                      const StaticScales* static_scales) {
   if (router && !router->logits) router = nullptr;
   const int32_t S = T * k;
   const int64_t n_chunks = (int64_t)rows * H / 8;
@@ -570,7 +571,7 @@ hipError_t launch_route_sort_and_quant(const RouterArgs* router, const int32_t* 
     hipError_t e = launch_route_sort_zero(router, ids, T, k, E, expert_begin, sorted_slot, offsets, nullptr,
                                           invalid_count, sort_ws, zero, n_zero, stream);
     if (e != hipSuccess) return e;
-    if ((e = launch_quant_act(x, rows, H, fmt, codes, scales, stream)) != hipSuccess) return e;
+    if ((e = launch_quant_act(x, rows, H, fmt, codes, scales, stream, static_scales)) != hipSuccess) return e;
     if (S >= kMultiBlockFrom && sorted_scales && rows == T)
       e = launch_gather_scales(scales, sorted_slot, k, T, H, sorted_scales, stream);
     return e;
@@ -583,14 +584,12 @@ hipError_t launch_route_sort_and_quant(const RouterArgs* router, const int32_t* 
   const RouterArgs r = fuse ? *router : kNoRouter;
   const int64_t want = (n_chunks + kSortThreads - 1) / kSortThreads;
   const int blocks = 1 + (int)(want < 256 * 16 ? want : 256 * 16);
-  if (fmt == 0)
-    hipLaunchKernelGGL(route_quant_kernel<128>, dim3(blocks), dim3(kSortThreads), route_sort_lds_bytes(E), stream,
-                       r, ids, T, k, E, expert_begin, sorted_slot, offsets, invalid_count, (const uint4*)x, n_chunks,
-                       rows, H, codes, scales, zero, n_zero);
-  else
-    hipLaunchKernelGGL(route_quant_kernel<32>, dim3(blocks), dim3(kSortThreads), route_sort_lds_bytes(E), stream,
-                       r, ids, T, k, E, expert_begin, sorted_slot, offsets, invalid_count, (const uint4*)x, n_chunks,
-                       rows, H, codes, scales, zero, n_zero);
+  const StaticScales st = static_scales ? *static_scales : StaticScales{nullptr, 0};
+  auto kern = fmt == 0 ? (static_scales ? route_quant_kernel<128, true> : route_quant_kernel<128, false>)
+                       : (static_scales ? route_quant_kernel<32, true> : route_quant_kernel<32, false>);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kSortThreads), route_sort_lds_bytes(E), stream, r, ids, T, k, E,
+                     expert_begin, sorted_slot, offsets, invalid_count, (const uint4*)x, n_chunks, rows, H, codes,
+                     scales, zero, n_zero, st);
   return hipGetLastError();
 }
 

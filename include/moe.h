@@ -19,8 +19,12 @@
  *               (dtype=int8)", section "Source": FP4 weights come packed in int8.
  *  [P-devices]  "DeepGEMM experts selected on a model spanning multiple CUDA
  *               devices", the record's source: the forward refuses a multi-device
- *               model, non-bf16 hidden states and static activation scales before
- *               any kernel work, and picks the nn or nt weight layout.
+ *               model and non-bf16 hidden states before any kernel work, and
+ *               picks the nn or nt weight layout.
+ *  [P-grouped] also names the static activation scheme: precomputed activation
+ *               scales that the pages' eager path consumes and their grouped
+ *               path refuses ("What it means", "Example fix"); this library
+ *               serves it (moe_quant_act_static, moe_options.act_scales).
  *
  * Conventions for every call:
  *  - Pointers marked "device" are device memory on the device current for
@@ -51,7 +55,7 @@ typedef enum moe_status {
   MOE_ERR_NULL = 1,        /* a required pointer is NULL */
   MOE_ERR_SHAPE = 2,       /* a size is out of range or not a multiple of the block */
   MOE_ERR_DTYPE = 3,       /* an argument has the wrong element type (the pages: ValueError on non-bf16 input) */
-  MOE_ERR_UNSUPPORTED = 4, /* a valid request this library does not serve (static activation scales, aliasing) */
+  MOE_ERR_UNSUPPORTED = 4, /* a request this library does not serve (aliasing, static scales on bf16 experts) */
   MOE_ERR_WORKSPACE = 5,   /* workspace missing or smaller than the matching *_workspace() size */
   MOE_ERR_ARCH = 6,        /* the stream's device is not gfx950 */
   MOE_ERR_DEVICE = 7,      /* a pointer lives on another device than the stream */
@@ -148,8 +152,8 @@ moe_status moe_route_topk(const float* router_logits, int32_t T, int32_t n_exper
 
 /* --------------------------------------------------- activation quantization --
  * Dynamic per-block quantization of bf16 rows ([P-grouped], "What it means":
- * activations are quantized dynamically per block; precomputed static scales are
- * refused).  Per block of B = 128 (FP8_B128) or 32 (MX) elements of a row:
+ * activations are quantized dynamically per block).  Per block of B = 128
+ * (FP8_B128) or 32 (MX) elements of a row:
  * amax = max|x|; FP8_B128: s = max(amax, 1e-4f) / 448 in fp32 and
  * code = e4m3(x / s) with an IEEE fp32 division; MX: e = ceil(log2(max(amax,
  * 1e-4f) / 448)) read exactly from the fp32 bits, scale byte e + 127 and
@@ -166,6 +170,26 @@ moe_status moe_route_topk(const float* router_logits, int32_t T, int32_t n_exper
  *  scales  device out: float [H/128][rows] (FP8_B128) or uint8 [H/128][rows][4] (MX). */
 moe_status moe_quant_act(const uint16_t* x, int32_t rows, int32_t H, moe_format fmt, uint8_t* codes, void* scales,
                          hipStream_t stream);
+
+/* Static per-block quantization: the activation scheme whose scales are
+ * precomputed ([P-grouped], "What it means" and "Example fix": the static
+ * scheme implies pre-computed activation scales, which the pages' eager path
+ * consumes).  The caller's block scales replace the amax pass; the encoding is
+ * moe_quant_act's: FP8_B128 code = e4m3(x / s) with an IEEE fp32 division, MX
+ * code = e4m3(x * 2^-(b - 127)); e4m3() rounds to nearest even and saturates
+ * at 448, so |x| >= 448 s gives the largest code of x's sign.
+ *
+ *  act_scales  device, read-only: FP8_B128 float, MX uint8 UE8M0 bytes; row t's
+ *              H/128 (FP8_B128) or H/32 (MX) block scales start at element
+ *              t * row_stride.  row_stride 0 gives every row the same scales
+ *              (one row of block scales, e.g. a per-tensor scale repeated);
+ *              otherwise row_stride >= H/128 (H/32).  FP8 scales must be
+ *              finite and > 0 and MX bytes < 255 (not checked: a zero or
+ *              non-finite scale gives unspecified codes).
+ *  codes, scales  out, as moe_quant_act (the scales are the caller's, copied
+ *              into the K-block-major layout the grouped GEMM reads). */
+moe_status moe_quant_act_static(const uint16_t* x, int32_t rows, int32_t H, moe_format fmt, const void* act_scales,
+                                int32_t row_stride, uint8_t* codes, void* scales, hipStream_t stream);
 
 /* --------------------------------------------------------- expert weights --
  * Descriptor of one layer's prepared expert weights (filled by
@@ -308,15 +332,31 @@ typedef struct moe_debug {
   int32_t* expert_offsets; /* [E+1] */
   uint8_t* act_codes;      /* K-block-major [H/128][T][128] */
   void* act_scales;        /* float [H/128][T] or uint8 [H/128][T][4] */
+  /* The quantized SwiGLU output h (the down projection's operand), by sorted
+   * row: K-block-major codes [I/128][T*k][128] and scales float [I/128][T*k]
+   * or uint8 [I/128][T*k][4].  Only rows [0, expert_offsets[E]) are defined;
+   * sorted row r belongs to flat slot sorted_slot[r].  Not written for
+   * MOE_FMT_BF16. */
+  uint8_t* h_codes;
+  void* h_scales;
 } moe_debug;
 
 typedef struct moe_options {
   int32_t has_swiglu_limit;
   float swiglu_limit;    /* must be finite and > 0 when has_swiglu_limit */
   int32_t expert_begin;  /* global id of local expert 0, >= 0 */
-  int32_t static_activation_scales; /* nonzero requests static scales: refused (MOE_ERR_UNSUPPORTED) */
+  /* Nonzero: the static activation scheme.  hidden_states is quantized with
+   * the caller's block scales act_scales (laid out as in moe_quant_act_static,
+   * row t = token t, stride act_scales_row_stride) instead of its own block
+   * amax; h, the down projection's operand, stays dynamic (the scheme gives
+   * scales for the layer's input only).  Quantized formats only:
+   * MOE_ERR_UNSUPPORTED for MOE_FMT_BF16, MOE_ERR_NULL without act_scales,
+   * MOE_ERR_SHAPE for a stride below one row. */
+  int32_t static_activation_scales;
   int32_t* invalid_count; /* device int32 [1], may be NULL */
   moe_debug* debug;       /* may be NULL */
+  const void* act_scales;        /* device: float (FP8_B128) or uint8 (MX) block scales */
+  int32_t act_scales_row_stride; /* elements between consecutive tokens' rows; 0 = one row for all */
 } moe_options;
 
 size_t moe_experts_forward_workspace(int32_t T, int32_t k, const moe_weights* w);

@@ -33,7 +33,7 @@ def lib():
 def test_library_exports_every_declared_function(lib):
     names = _declared_functions()
     assert "moe_experts_forward" in names and "moe_grouped_gemm" in names
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
 
@@ -177,10 +177,25 @@ def test_forward_refusals(lib):
     opt.expert_begin = -1
     assert fwd(opt=opt) == SHAPE
     opt.expert_begin = 0
+    # the static activation scheme: needs its scales, a quantized format and a
+    # row stride of 0 or at least one row of block scales
     opt.static_activation_scales = 1
-    assert fwd(opt=opt) == UNSUP
+    assert fwd(opt=opt) == NULL
+    assert b"act_scales" in lib.moe_last_error()
+    opt.act_scales = 48
+    opt.act_scales_row_stride = 1  # H = 256: two FP8 block scales per row
+    assert fwd(opt=opt) == SHAPE
+    opt.act_scales_row_stride = -2
+    assert fwd(opt=opt) == SHAPE
+    opt.act_scales_row_stride = 2
+    assert fwd(opt=opt, ws=None) == WS  # past every static check
+    opt.act_scales_row_stride = 0
+    assert fwd(opt=opt, ws=None) == WS
+    assert fwd(w=_weights(fmt=2), opt=opt) == UNSUP  # bf16 experts quantize nothing
     assert b"static" in lib.moe_last_error()
+    assert fwd(opt=opt, out=ctypes.c_void_p(48)) == UNSUP  # out aliases act_scales
     opt.static_activation_scales = 0
+    opt.act_scales = None
     opt.has_swiglu_limit, opt.swiglu_limit = 1, float("nan")
     assert fwd(opt=opt) == SHAPE
     opt.swiglu_limit = -2.0
@@ -192,6 +207,15 @@ def test_forward_refusals(lib):
     assert need > 0
     assert fwd(ws_bytes=need - 1) == WS
     assert fwd(out=p) == UNSUP  # out aliases hidden_states
+
+    def fwd3(x, ids, wts, out):
+        return lib.moe_experts_forward(ctypes.byref(w), ctypes.c_void_p(x), ctypes.c_void_p(ids),
+                                       ctypes.c_void_p(wts), 8, 2, None, ctypes.c_void_p(out), ctypes.c_void_p(64),
+                                       1 << 40, None)
+
+    assert fwd3(16, 24, 40, 24) == UNSUP  # out aliases top_k_index (the combine reads it while writing out)
+    assert fwd3(16, 24, 40, 40) == UNSUP  # out aliases top_k_weights
+    assert b"alias" in lib.moe_last_error()
     bad = _weights()
     bad.w2 = None
     assert fwd(w=bad) == NULL
@@ -202,10 +226,13 @@ def test_gemm_refusals(lib):
     a = moe.MoeGemmArgs()
     a.weights = ctypes.pointer(w)
     a.which, a.max_rows, a.a_rows = 0, 64, 64
-    a.a_codes = a.a_scales = a.expert_offsets = 16
+    a.a_codes, a.a_scales, a.expert_offsets = 16, 24, 32
     a.epilogue = moe.EPI_STORE_F32
     assert lib.moe_grouped_gemm(ctypes.byref(a), None) == NULL  # c_f32 missing
-    a.c_f32 = 16
+    for alias in (16, 24, 32):  # an output may not alias an input of the launch
+        a.c_f32 = alias
+        assert lib.moe_grouped_gemm(ctypes.byref(a), None) == UNSUP
+    a.c_f32 = 40
     a.which = 2
     assert lib.moe_grouped_gemm(ctypes.byref(a), None) == UNSUP
     a.which = 0
@@ -213,7 +240,7 @@ def test_gemm_refusals(lib):
     assert lib.moe_grouped_gemm(ctypes.byref(a), None) == SHAPE
     a.a_rows = 64
     a.epilogue = moe.EPI_SWIGLU_QUANT
-    a.h_codes = a.h_scales = 16
+    a.h_codes, a.h_scales = 48, 56
     a.which = 1
     assert lib.moe_grouped_gemm(ctypes.byref(a), None) == UNSUP  # SwiGLU only on gate_up
     a.which = 0
@@ -250,10 +277,116 @@ def test_python_face_raises_like_the_pages():
     w = torch.ones((4, 2), dtype=torch.float32)
     with pytest.raises(ValueError, match="bfloat16"):
         moe.experts_forward(x, ids, w, weights=None)
-    with pytest.raises(NotImplementedError, match="static"):
-        moe.experts_forward(x.bfloat16(), ids, w, weights=None, activation_scheme="static")
     with pytest.raises(NotImplementedError, match="int8"):
         moe.prepare_weights(torch.zeros(2, 4, dtype=torch.float16), None, None, None, fmt=moe.FMT_MXFP8A_MXFP4W)
+
+
+def _fake_weights(E=4, H=256, I=128, fmt=0):
+    return moe.Weights(_weights(E, H, I, fmt), ())
+
+
+def test_python_forward_shape_refusals():
+    """Shapes the C call takes on trust (bare pointers, sizes from the weight
+    descriptor) are refused in Python before the library is called: a mismatch
+    would otherwise become an out-of-bounds device access."""
+    wt = _fake_weights()  # H = 256
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    ids = torch.zeros((4, 2), dtype=torch.int32)
+    w = torch.ones((4, 2), dtype=torch.float32)
+    cases = [
+        (dict(hidden_states=torch.zeros((4, 384), dtype=torch.bfloat16)), "H=384"),
+        (dict(hidden_states=torch.zeros((4, 2, 128), dtype=torch.bfloat16)), r"\[T, H\]"),
+        (dict(top_k_index=torch.zeros((5, 2), dtype=torch.int32)), "top_k_index"),
+        (dict(top_k_index=torch.zeros(8, dtype=torch.int32)), "top_k_index"),
+        (dict(top_k_weights=torch.ones((4, 3), dtype=torch.float32)), "top_k_weights"),
+        (dict(out=torch.empty((4, 128), dtype=torch.bfloat16)), "out"),
+    ]
+    for over, msg in cases:
+        a = dict(hidden_states=x, top_k_index=ids, top_k_weights=w)
+        a.update(over)
+        with pytest.raises(ValueError, match=msg):
+            moe.experts_forward(a["hidden_states"], a["top_k_index"], a["top_k_weights"], wt, out=a.get("out"))
+    with pytest.raises(ValueError, match="out"):
+        moe.experts_forward(x, ids, w, wt, out=torch.empty((4, 256), dtype=torch.float32))
+    logits = torch.zeros((4, 8), dtype=torch.float32)
+    with pytest.raises(ValueError, match="rows"):
+        moe.experts_forward_from_logits(x, torch.zeros((5, 8)), 2, wt)
+    with pytest.raises(ValueError, match="H=384"):
+        moe.experts_forward_from_logits(torch.zeros((4, 384), dtype=torch.bfloat16), logits, 2, wt)
+    with pytest.raises(ValueError, match="top_k_index"):
+        moe.experts_forward_from_logits(x, logits, 2, wt, top_k_index=torch.zeros((4, 3), dtype=torch.int32))
+    with pytest.raises(ValueError, match="out"):
+        moe.experts_forward_from_logits(x, logits, 2, wt, out=torch.empty((4, 512), dtype=torch.bfloat16))
+
+
+def test_python_static_scheme_refusals():
+    wt = _fake_weights()  # FP8, H = 256: two block scales per token
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    ids = torch.zeros((4, 2), dtype=torch.int32)
+    w = torch.ones((4, 2), dtype=torch.float32)
+    with pytest.raises(ValueError, match="act_scales"):
+        moe.experts_forward(x, ids, w, wt, activation_scheme="static")
+    with pytest.raises(ValueError, match="static"):
+        moe.experts_forward(x, ids, w, wt, act_scales=torch.ones((4, 2)))
+    with pytest.raises(ValueError, match="activation_scheme"):
+        moe.experts_forward(x, ids, w, wt, activation_scheme="per_tensor")
+    with pytest.raises(ValueError, match="act_scales"):
+        moe.experts_forward(x, ids, w, wt, activation_scheme="static", act_scales=torch.ones((4, 3)))
+    with pytest.raises(ValueError, match="act_scales"):
+        moe.experts_forward(x, ids, w, wt, activation_scheme="static", act_scales=torch.ones(2, dtype=torch.float64))
+    with pytest.raises(NotImplementedError, match="quantized"):
+        moe.experts_forward(x, ids, w, _fake_weights(fmt=2), activation_scheme="static", act_scales=torch.ones(2))
+    with pytest.raises(ValueError, match="act_scales"):  # MX: one UE8M0 byte per 32 columns
+        moe.quant_act_static(x, torch.ones((4, 2), dtype=torch.uint8), fmt=moe.FMT_MXFP8A_MXFP4W)
+
+
+def test_quant_static_refusals(lib):
+    p = ctypes.c_void_p(16)
+    q = lambda **kw: lib.moe_quant_act_static(kw.get("x", p), kw.get("rows", 4), kw.get("H", 256), kw.get("fmt", 0),
+                                              kw.get("sc", ctypes.c_void_p(24)), kw.get("stride", 2),
+                                              kw.get("codes", ctypes.c_void_p(32)), kw.get("scales", ctypes.c_void_p(40)),
+                                              None)
+    assert q(rows=0) == OK
+    assert q(fmt=2) == UNSUP
+    assert q(fmt=7) == UNSUP
+    assert q(H=200) == SHAPE
+    assert q(stride=1) == SHAPE
+    assert q(stride=-1) == SHAPE
+    assert q(fmt=1, stride=4) == SHAPE  # MX: 8 block scales per row of 256
+    assert q(sc=None) == NULL
+    assert q(codes=ctypes.c_void_p(24)) == UNSUP  # codes alias the input scales
+    assert q(scales=p) == UNSUP  # scales alias x
+
+
+def test_python_prepare_weights_shape_refusals():
+    E, H, I = 2, 384, 128
+    u8 = lambda *s: torch.zeros(s, dtype=torch.uint8)
+    f32 = lambda *s: torch.ones(s, dtype=torch.float32)
+    good = dict(gate_up=u8(E, 2 * I, H), gate_up_scale=f32(E, 2 * I // 128, H // 128), down=u8(E, H, I),
+                down_scale=f32(E, H // 128, I // 128))
+    bad = [
+        ("down", u8(E, H, 2 * I)), ("down", u8(E + 1, H, I)), ("gate_up_scale", f32(E, H // 128, 2 * I // 128)),
+        ("down_scale", f32(E, I // 128, H // 128)), ("gate_up_scale", torch.ones((E, 2, 2), dtype=torch.float64)),
+        ("gate_up", u8(E, 2 * I + 1, H)),
+    ]
+    for name, t in bad:
+        a = dict(good)
+        a[name] = t
+        with pytest.raises(ValueError):
+            moe.prepare_weights(a["gate_up"], a["gate_up_scale"], a["down"], a["down_scale"], fmt=moe.FMT_FP8_B128)
+    # MX: packed codes [E, 2I, H/2] and [E, H, I/2], UE8M0 bytes [E, 2I, H/32] and [E, H, I/32]
+    mx = dict(gate_up=u8(E, 2 * I, H // 2), gate_up_scale=u8(E, 2 * I, H // 32), down=u8(E, H, I // 2),
+              down_scale=u8(E, H, I // 32))
+    for name, t in (("down", u8(E, H, I)), ("down_scale", u8(E, H, I // 128)), ("gate_up_scale", u8(E, 2 * I, H // 128)),
+                    ("down_scale", f32(E, H, I // 32))):
+        a = dict(mx)
+        a[name] = t
+        with pytest.raises(ValueError):
+            moe.prepare_weights(a["gate_up"], a["gate_up_scale"], a["down"], a["down_scale"],
+                                fmt=moe.FMT_MXFP8A_MXFP4W)
+    with pytest.raises(ValueError, match="nt"):
+        moe.prepare_weights(mx["gate_up"], mx["gate_up_scale"], mx["down"], mx["down_scale"],
+                            fmt=moe.FMT_MXFP8A_MXFP4W, transposed=True)
 
 
 def test_workspace_sized_for_next_power_of_two():

@@ -16,6 +16,8 @@ import torch
 import block_scaled_fp8_sort_amd as moe
 import oracle
 import workloads as W
+from parity_checks import (assert_forward_parity, bits_to_f64, check_down_half, check_h_codes, flip_explainer,
+                           host, rowmajor_codes, rowmajor_scales, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -23,16 +25,8 @@ FP8, MX = W.FMT_FP8_B128, W.FMT_MX
 DEV = "cuda:0"
 
 
-def say(*a):
-    print(*a, flush=True)
-    sys.stdout.flush()
-
-
-def bits_to_f64(b):
-    return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).double().numpy()
-
-
 def assert_out_close(got_bits, ref_bits, what=""):
+    """The forward's tolerance with no exception path (outputs without debug data)."""
     g, r = bits_to_f64(got_bits), bits_to_f64(ref_bits)
     assert np.all(np.isfinite(g)), f"{what}: non-finite output"
     max_ref = np.max(np.abs(r))
@@ -41,27 +35,6 @@ def assert_out_close(got_bits, ref_bits, what=""):
     say(f"  {what}: max|err| / max|ref| = {max_err / max(max_ref, 1e-30):.2e}, rel L2 = {rel_l2:.2e}")
     assert max_err <= 1e-2 * max_ref, f"{what}: max|err| {max_err} > 1e-2 * {max_ref}"
     assert rel_l2 <= 5e-3, f"{what}: rel L2 {rel_l2}"
-
-
-def host(t):
-    return W.to_numpy(t)
-
-
-def rowmajor_codes(codes):
-    """K-block-major codes [K/128, rows, 128] (device) -> row-major [rows, K] (host)."""
-    c = host(codes)
-    kb, rows, _ = c.shape
-    return np.ascontiguousarray(c.transpose(1, 0, 2).reshape(rows, kb * 128))
-
-
-def rowmajor_scales(scales):
-    """K-block-major scales (device) -> row-major [rows, blocks] (host): FP8
-    [K/128, rows] -> [rows, K/128]; MX [K/128, rows, 4] -> [rows, K/32]."""
-    s = host(scales)
-    if s.ndim == 2:
-        return np.ascontiguousarray(s.T)
-    kb, rows, _ = s.shape
-    return np.ascontiguousarray(s.transpose(1, 0, 2).reshape(rows, kb * 4))
 
 
 # ---------------------------------------------------------------- route sort
@@ -365,12 +338,11 @@ SMALL = [
     _small_workload("k16_fp8", FP8, T=96, H=256, I=128, E=32, k=16, routing="zipf", skip=0.1, seed=24),
     _small_workload("k64_fp8", FP8, T=20, H=256, I=128, E=128, k=64, routing="zipf", skip=0.1, seed=25),
     _small_workload("k24_mx", MX, T=40, H=256, I=128, E=48, k=24, routing="zipf", skip=0.1, limit=7.0, seed=26),
-    # 16384 slots and more: the multi-workgroup sort, whose slot_pos places each
-    # block scale at the token's sorted rows for the gate_up GEMM.  (I = 256: at
-    # I = 128 a row of h is one scale block, and a single h code that the GPU's
-    # and the oracle's sum orders round to neighbouring e4m3 values moves an
-    # output by about 1% of max|ref|.)
+    # 16384 slots and more: the multi-workgroup sort; the activation scales are
+    # then copied by sorted row (sorted_slot / k) for the gate_up GEMM
     _small_workload("multiblock_fp8", FP8, T=2100, H=384, I=256, E=64, k=8, routing="zipf", skip=0.05, seed=27),
+    _small_workload("multiblock_fp8_i128", FP8, T=2100, H=384, I=128, E=64, k=8, routing="zipf", skip=0.05,
+                    seed=27),
     _small_workload("multiblock_mx", MX, T=4100, H=256, I=128, E=24, k=4, routing="zipf", skip=0.05, limit=7.0,
                     seed=28),
 ]
@@ -388,7 +360,80 @@ def test_forward_parity_small(wl):
     o_codes, o_scales = oracle.quant_rows_bf16(n["x"], wl.fmt)
     assert np.array_equal(rowmajor_codes(dbg["act_codes"]), o_codes)
     assert np.array_equal(rowmajor_scales(dbg["act_scales"]).view(np.uint8), o_scales.view(np.uint8))
-    assert_out_close(got, ref, wl.name)
+    assert_forward_parity(wl.name, got, ref,
+                          flip_explainer(wl.fmt, wl.T, wl.k, wl.H, wl.I, n, got, dbg, swiglu_limit=wl.swiglu_limit))
+
+
+H_CASES = ["tiny", "ragged_fp8_clamp", "decode_fp8_ragged_clamp", "multiblock_fp8_i128", "mx_ragged_clamp",
+           "e512_fp8_tiled"]
+
+
+@pytest.mark.parametrize("name", H_CASES)
+def test_forward_down_half_from_the_gpus_own_h(name):
+    """The down projection, routing weight and combine, checked on their own
+    (parity_checks.check_down_half): the oracle's grouped GEMM on the GPU's own
+    quantized h, the weighted per-token sum in fp64, and the GPU's output within
+    the rounding the GPU path does after h.  A wrong h scale, a misplaced h row
+    or a wrong weight would be far outside that bound.  The GPU's h codes
+    against the oracle's: neighbouring e4m3 values at most (they follow fp32
+    sums in another order)."""
+    wl = W.WORKLOADS.get(name) or next(w for w in SMALL if w.name == name)
+    say(f"down half from GPU h: {name}")
+    inp = W.inputs(wl, DEV)
+    w = _prepare(inp, wl.fmt)
+    dbg = {}
+    out = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w, swiglu_limit=wl.swiglu_limit, debug=dbg)
+    torch.cuda.synchronize()
+    n = {k_: host(v) for k_, v in inp.items()}
+    hq, hs, slots = check_down_half(wl.fmt, wl.T, wl.k, wl.H, wl.I, n, host(out), dbg)
+    _, odbg = oracle.forward(wl.fmt, n["w13"], n["s13"], n["w2"], n["s2"], n["x"], n["ids"], n["w"],
+                             swiglu_limit=wl.swiglu_limit, debug=True)
+    check_h_codes(wl.fmt, hq, hs, slots, odbg["h_codes"], odbg["h_scales"], wl.I)
+
+DUP_CASES = [
+    _small_workload("dup_garbage_fp8", FP8, T=200, H=384, I=256, E=10, k=4, seed=40),
+    _small_workload("dup_garbage_decode_fp8", FP8, T=12, H=512, I=256, E=16, k=4, seed=41),
+    _small_workload("dup_garbage_mx", MX, T=150, H=256, I=128, E=6, k=3, limit=7.0, seed=42),
+    _small_workload("dup_garbage_multiblock", FP8, T=2100, H=256, I=256, E=24, k=8, seed=43),
+]
+
+
+@pytest.mark.parametrize("wl", DUP_CASES, ids=[w.name for w in DUP_CASES])
+@pytest.mark.parametrize("begin", [0, 7])
+def test_forward_duplicate_and_out_of_range_ids(wl, begin):
+    """The same expert twice in one token counts twice (two independent slots),
+    and ids outside [begin, begin + E) other than -1 (-5, 1 << 30, begin + E,
+    begin + E + 3, and begin - 1 when begin > 0) are skipped and counted."""
+    say(f"forward duplicate / garbage ids {wl.name} begin={begin}")
+    inp = W.inputs(wl, DEV)
+    ids = host(inp["ids"]).astype(np.int64)
+    ids = np.where(ids >= 0, ids + begin, ids)
+    ids[::3, 1] = ids[::3, 0]
+    ids[1::7, 2 % wl.k] = -5
+    ids[2::11, 0] = 1 << 30
+    ids[3::13, wl.k - 1] = begin + wl.E
+    ids[4::17, 1] = begin + wl.E + 3
+    if begin > 0:
+        ids[5::19, 0] = begin - 1
+    ids = ids.astype(np.int32)
+    assert np.any((ids[:, 0] == ids[:, 1]) & (ids[:, 0] >= begin))
+    inp["ids"] = torch.from_numpy(ids).to(DEV)
+    w = _prepare(inp, wl.fmt)
+    inv = torch.zeros(1, dtype=torch.int32, device=DEV)
+    dbg = {}
+    out = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w, swiglu_limit=wl.swiglu_limit, expert_begin=begin,
+                              invalid_count=inv, debug=dbg)
+    torch.cuda.synchronize()
+    n = {k_: host(v) for k_, v in inp.items()}
+    ref = oracle.forward(wl.fmt, n["w13"], n["s13"], n["w2"], n["s2"], n["x"], ids, n["w"],
+                         swiglu_limit=wl.swiglu_limit, expert_begin=begin)
+    o_ss, o_off, _, o_inv = oracle.route_sort(ids, wl.E, expert_begin=begin)
+    assert int(host(inv)[0]) == o_inv > 0
+    assert np.array_equal(host(dbg["sorted_slot"]), o_ss) and np.array_equal(host(dbg["expert_offsets"]), o_off)
+    got = host(out)
+    assert_forward_parity(f"{wl.name} begin={begin}", got, ref,
+                          flip_explainer(wl.fmt, wl.T, wl.k, wl.H, wl.I, n, got, dbg, swiglu_limit=wl.swiglu_limit,
+                                         expert_begin=begin))
 
 
 def test_forward_invariants_tiny():

@@ -19,6 +19,7 @@ import torch
 import block_scaled_fp8_sort_amd as moe
 import oracle
 import workloads as W
+from parity_checks import assert_forward_parity, flip_explainer
 
 pytestmark = pytest.mark.gpu
 
@@ -103,9 +104,9 @@ FWD_CASES = [
     _workload("logits_small_decode_fp8", FP8, T=16, H=512, I=256, E=16, k=4, seed=30),  # router+sort+quant in one launch
     _workload("logits_decode_fp8", FP8, T=24, H=512, I=256, E=16, k=4, seed=31),       # router launch, fused sort+quant
     _workload("logits_ragged_fp8", FP8, T=300, H=384, I=256, E=6, k=3, seed=32),
-    # 70000 logits: the router runs as a launch of its own (I = 256: with a single 128-wide h block a lone h-code
-    # rounding flip, which the tolerance allows for, can exceed the max-norm bar at 21 rows per expert)
+    # 70000 logits: the router runs as a launch of its own
     _workload("logits_router_launch", FP8, T=700, H=512, I=256, E=100, k=3, seed=33),
+    _workload("logits_router_launch_i128", FP8, T=700, H=512, I=128, E=100, k=3, seed=33),
     _workload("logits_mx_clamp", MX, T=200, H=256, I=256, E=8, k=2, limit=7.0, seed=34),
 ]
 
@@ -124,18 +125,19 @@ def test_forward_from_logits_parity(wl):
     assert np.array_equal(host(ids), o_ids)
     assert_weights_close(host(wts), o_w, lg_h, wl.E)
     # the same kernels as the forward given this routing: identical bits
-    same = moe.experts_forward(inp["x"], ids, wts, w, swiglu_limit=wl.swiglu_limit)
+    dbg = {}
+    same = moe.experts_forward(inp["x"], ids, wts, w, swiglu_limit=wl.swiglu_limit, debug=dbg)
     torch.cuda.synchronize()
     assert np.array_equal(host(out).view(np.uint16), host(same).view(np.uint16))
     n = {k_: host(v) for k_, v in inp.items()}
     ref = oracle.forward(wl.fmt, n["w13"], n["s13"], n["w2"], n["s2"], n["x"], o_ids, o_w,
                          swiglu_limit=wl.swiglu_limit)
-    g = torch.from_numpy(host(out).view(np.int16)).view(torch.bfloat16).double().numpy()
-    r = torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).double().numpy()
-    max_err, max_ref = np.max(np.abs(g - r)), np.max(np.abs(r))
-    rel_l2 = np.linalg.norm(g - r) / np.linalg.norm(r)
-    say(f"  max|err| / max|ref| = {max_err / max_ref:.2e}, rel L2 = {rel_l2:.2e}")
-    assert max_err <= 1e-2 * max_ref and rel_l2 <= 5e-3
+    got = host(out)
+    # the explanation path runs on the router's own choice (the same ids and
+    # weights the GPU used, equal to the oracle's ids, weights to 1 fp32 rounding)
+    n_gpu = dict(n, ids=host(ids), w=host(wts))
+    assert_forward_parity(wl.name, got, ref,
+                          flip_explainer(wl.fmt, wl.T, wl.k, wl.H, wl.I, n_gpu, got, dbg, swiglu_limit=wl.swiglu_limit))
 
 
 def test_forward_from_logits_full_decode_sampled():
