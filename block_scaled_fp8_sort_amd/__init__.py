@@ -23,7 +23,8 @@ __all__ = [
     "FMT_FP8_B128", "FMT_MXFP8A_MXFP4W", "FMT_BF16", "EPI_STORE_F32", "EPI_SWIGLU_QUANT", "EPI_WEIGHTED_SCATTER",
     "MoeError", "library_path", "load_library", "route_sort", "route_topk", "quant_act", "quant_act_static",
     "prepare_weights",
-    "grouped_gemm", "experts_forward", "experts_forward_from_logits", "forward_workspace_bytes", "Weights",
+    "grouped_gemm", "experts_forward", "experts_forward_from_logits", "experts_forward_noalloc",
+    "forward_workspace_bytes", "NOALLOC_SCRATCH_BYTES", "Weights",
     "TILE_COUNTERS_INTS",
 ]
 
@@ -122,6 +123,9 @@ def load_library():
     lib.moe_experts_forward.restype = ctypes.c_int
     lib.moe_experts_forward.argtypes = [ctypes.POINTER(MoeWeights), _P, _P, _P, _I32, _I32,
                                         ctypes.POINTER(MoeOptions), _P, _P, _SZ, _P]
+    lib.moe_experts_forward_noalloc.restype = ctypes.c_int
+    lib.moe_experts_forward_noalloc.argtypes = [ctypes.POINTER(MoeWeights), _P, _P, _P, _I32, _I32,
+                                                ctypes.POINTER(MoeOptions), _P, _P]
     lib.moe_experts_forward_from_logits.restype = ctypes.c_int
     lib.moe_experts_forward_from_logits.argtypes = [ctypes.POINTER(MoeWeights), _P, _P, _I32, _I32, _I32, _I32,
                                                     ctypes.POINTER(MoeOptions), _P, _P, _P, _P, _SZ, _P]
@@ -439,6 +443,8 @@ def forward_sorts_scales(T: int, k: int, fmt: int) -> bool:
     return bool(load_library().moe_forward_sorts_scales(T, k, fmt))
 
 
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+
 _ws_cache: dict = {}
 
 
@@ -586,4 +592,33 @@ def experts_forward(hidden_states: torch.Tensor, top_k_index: torch.Tensor, top_
     _check(lib.moe_experts_forward(ctypes.byref(weights.desc), _ptr(hidden_states), _ptr(top_k_index),
                                    _ptr(top_k_weights), T, k, ctypes.byref(opt), _ptr(out), _ptr(workspace),
                                    workspace.numel(), _stream(dev)))
+    return out
+
+
+def experts_forward_noalloc(hidden_states: torch.Tensor, top_k_index: torch.Tensor, top_k_weights: torch.Tensor,
+                            weights: Weights, swiglu_limit: Optional[float] = None, expert_begin: int = 0,
+                            out: Optional[torch.Tensor] = None, invalid_count: Optional[torch.Tensor] = None,
+                            activation_scheme: str = "dynamic",
+                            act_scales: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """experts_forward through moe_experts_forward_noalloc: the library's own
+    per-GPU scratch (NOALLOC_SCRATCH_BYTES) replaces the workspace, so the C call
+    allocates nothing (pass ``out`` to allocate nothing here either).  Calls
+    that overlap on one GPU share that scratch and must not run concurrently."""
+    lib = load_library()
+    if hidden_states.dtype != torch.bfloat16:
+        raise ValueError(f"the experts forward requires bfloat16 hidden states, got {hidden_states.dtype}")
+    dev = hidden_states.device
+    _need(hidden_states, "hidden_states", torch.bfloat16, dev)
+    _need(top_k_index, "top_k_index", torch.int32, dev)
+    _need(top_k_weights, "top_k_weights", torch.float32, dev)
+    _check_forward_shapes(hidden_states, top_k_index, top_k_weights, weights, out)
+    T, H = hidden_states.shape
+    k = top_k_index.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    asc, astride = _scheme(activation_scheme, act_scales, weights, T, H, dev)
+    opt = _options(swiglu_limit, expert_begin, invalid_count, asc, astride)
+    _check(lib.moe_experts_forward_noalloc(ctypes.byref(weights.desc), _ptr(hidden_states), _ptr(top_k_index),
+                                           _ptr(top_k_weights), T, k, ctypes.byref(opt), _ptr(out), _stream(dev)))
     return out

@@ -254,9 +254,42 @@ hipError_t launch_gemm(const moe::GemmParams& p, int fmt, int epi, bool paired, 
 
 // The forward behind both entry points; with a router, top_k_index and
 // top_k_weights are outputs that the router fills before the sort reads them.
+// The scratch of moe_experts_forward_noalloc: one array per GPU, in device
+// memory for the life of the process.  Host code never uses its name as an
+// address (on the host it is only a stand-in): its device address, per device,
+// comes from hipGetSymbolAddress with that device current.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+// Device address of `scratch` on device dev (looked up once per device).
+moe_status scratch_address(int dev, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(MOE_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+// ws_is_scratch: ws is the library's own scratch array (whose address the
+// runtime's pointer query need not know), so it is not checked as a caller
+// pointer.
 moe_status forward_impl(const moe_weights* w, const uint16_t* hidden_states, const moe::RouterArgs* router,
                         const int32_t* top_k_index, const float* top_k_weights, int32_t T, int32_t k,
-                        const moe_options* opt, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+                        const moe_options* opt, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream,
+                        bool ws_is_scratch = false) {
   moe_status st = validate_weights(w);
   if (st != MOE_OK) return st;
   if (T < 0) return fail(MOE_ERR_SHAPE, "T=%d < 0", T);
@@ -316,7 +349,7 @@ moe_status forward_impl(const moe_weights* w, const uint16_t* hidden_states, con
                              {w->w13_scale, "w13_scale"},
                              {w->w2, "w2"},
                              {w->w2_scale, "w2_scale"},
-                             {ws, "workspace"},
+                             {ws_is_scratch ? nullptr : ws, "workspace"},
                              {opt ? opt->invalid_count : nullptr, "invalid_count"},
                              {stat ? opt->act_scales : nullptr, "act_scales"},
                              {dbg ? dbg->sorted_slot : nullptr, "debug.sorted_slot"},
@@ -745,6 +778,31 @@ moe_status moe_experts_forward(const moe_weights* w, const uint16_t* hidden_stat
                                const float* top_k_weights, int32_t T, int32_t k, const moe_options* opt,
                                uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
   return forward_impl(w, hidden_states, nullptr, top_k_index, top_k_weights, T, k, opt, out, ws, ws_bytes, stream);
+}
+
+moe_status moe_experts_forward_noalloc(const moe_weights* w, const uint16_t* hidden_states,
+                                       const int32_t* top_k_index, const float* top_k_weights, int32_t T, int32_t k,
+                                       const moe_options* opt, uint16_t* out, hipStream_t stream) {
+  // host-only checks first, so a refused call touches no device state
+  moe_status st = validate_weights(w);
+  if (st != MOE_OK) return st;
+  if (T < 0) return fail(MOE_ERR_SHAPE, "T=%d < 0", T);
+  if (k < 1 || k > kMaxK) return fail(MOE_ERR_SHAPE, "k=%d outside [1, %d]", k, kMaxK);
+  if ((int64_t)T * k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "T*k must stay below 2^31");
+  if (T == 0) return forward_impl(w, hidden_states, nullptr, top_k_index, top_k_weights, T, k, opt, out, nullptr, 0,
+                                  stream);
+  const size_t need = fwd_layout(T, k, w->E, w->H, w->I, w->fmt).total;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "this forward needs %zu bytes of workspace; the no-allocation entry point holds %zu per GPU (use "
+                "moe_experts_forward with a caller workspace)",
+                need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  int dev, cus;
+  if ((st = check_device(stream, &dev, &cus)) != MOE_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_address(dev, &ws)) != MOE_OK) return st;
+  return forward_impl(w, hidden_states, nullptr, top_k_index, top_k_weights, T, k, opt, out, ws,
+                      MOE_NOALLOC_SCRATCH_BYTES, stream, true);
 }
 
 moe_status moe_experts_forward_from_logits(const moe_weights* w, const uint16_t* hidden_states,

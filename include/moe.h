@@ -364,6 +364,25 @@ moe_status moe_experts_forward(const moe_weights* w, const uint16_t* hidden_stat
                                const float* top_k_weights, int32_t T, int32_t k, const moe_options* opt,
                                uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------ forward without allocation --
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the fused
+ * forward above, with its workspace taken from a scratch array the library
+ * holds in device memory, MOE_NOALLOC_SCRATCH_BYTES per GPU, for the life of
+ * the process (each GPU the library runs on holds its own copy).  The caller
+ * still passes the inputs and the output; the call allocates and frees
+ * nothing.  A forward whose moe_experts_forward_workspace() exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES is refused with MOE_ERR_WORKSPACE (64 MiB holds,
+ * for example, a 64-token Qwen3-MoE-shaped decode batch or 256 tokens of a
+ * DeepSeek-V3-shaped layer).  Every call on a GPU shares that GPU's scratch:
+ * calls that overlap on one GPU (on different streams) race and corrupt each
+ * other's results; calls on one stream are ordered and safe.  Arguments,
+ * results and errors are those of moe_experts_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_experts_forward_noalloc(const moe_weights* w, const uint16_t* hidden_states,
+                                       const int32_t* top_k_index, const float* top_k_weights, int32_t T, int32_t k,
+                                       const moe_options* opt, uint16_t* out, hipStream_t stream);
+
 /* The same forward starting one step earlier, from the router's logits: the
  * router of moe_route_topk chooses each token's k experts among n_experts
  * (global ids) and their weights, writes them to top_k_index / top_k_weights

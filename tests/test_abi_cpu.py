@@ -33,7 +33,7 @@ def lib():
 def test_library_exports_every_declared_function(lib):
     names = _declared_functions()
     assert "moe_experts_forward" in names and "moe_grouped_gemm" in names
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
 
@@ -428,3 +428,18 @@ def test_bf16_format_on_the_host(lib):
     a.weights = ctypes.pointer(w8)
     assert lib.moe_grouped_gemm(ctypes.byref(a), None) == NULL
     assert b"scale" in lib.moe_last_error()
+
+
+def test_noalloc_forward_host_refusals(lib):
+    """The forward without allocation refuses, on the host, anything its scratch
+    cannot hold (and the usual bad arguments) before touching the GPU."""
+    p = ctypes.c_void_p(16)
+    big = _weights(E=8, H=4096, I=14336)
+    assert lib.moe_experts_forward_workspace(4096, 2, ctypes.byref(big)) > moe.NOALLOC_SCRATCH_BYTES
+    assert lib.moe_experts_forward_noalloc(ctypes.byref(big), p, p, p, 4096, 2, None, ctypes.c_void_p(32), None) == WS
+    assert b"no-allocation" in lib.moe_last_error()
+    small = _weights()
+    assert lib.moe_experts_forward_noalloc(ctypes.byref(small), p, p, p, 0, 2, None, ctypes.c_void_p(32), None) == OK
+    assert lib.moe_experts_forward_noalloc(ctypes.byref(small), p, p, p, 8, 0, None, ctypes.c_void_p(32), None) == SHAPE
+    assert lib.moe_experts_forward_noalloc(ctypes.byref(_weights(H=100)), p, p, p, 8, 2, None, ctypes.c_void_p(32),
+                                           None) == SHAPE
