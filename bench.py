@@ -3,15 +3,20 @@
 One step = one full experts forward (route sort, activation quantization,
 gate_up grouped GEMM + SwiGLU + h quantization, down grouped GEMM + routing
 weight, deterministic combine) over one batch of synthetic inputs already
-resident in HBM.  The default workload is the Mixtral-8x7B-shaped layer (4096
+resident in HBM.  The headline workload is the Mixtral-8x7B-shaped layer (4096
 tokens, hidden 4096, intermediate 14336, 8 experts, top-2, FP8 e4m3 with
 128x128 weight scales and dynamic 1x128 activation scales).
 
-Prints one JSON line.  `value` is active-expert TFLOP/s (6*H*I per valid slot);
-`roofline` covers the dominant kernel (the gate_up grouped GEMM) timed with HIP
-events on the stream it runs on, against the roofline its arithmetic intensity
-binds (MFMA at the FP8 peak, or HBM); `cpu_baseline` is the CPU oracle on a
-bounded sample of the same tokens.
+Prints one JSON line.  `value` is active-expert TFLOP/s (6*H*I per valid slot)
+of the headline workload; `roofline` covers its dominant kernel (the gate_up
+grouped GEMM) timed with HIP events on the stream it runs on, against the
+roofline its arithmetic intensity binds (MFMA at the FP8 peak, or HBM);
+`cpu_baseline` is the CPU oracle on a bounded sample of the same tokens.
+`per_config` repeats the measurement for the other workloads (the tiny layer,
+the Qwen3-MoE-shaped decode batch, the DeepSeek-V3-shaped layer and the
+Mega-MoE-style FP8 x FP4 layer), each with its own roofline and oracle sample;
+the decode batch is also timed cold (a 1 GiB write between forwards evicts the
+256 MB last-level cache) and warm, per forward.
 """
 from __future__ import annotations
 
@@ -69,6 +74,10 @@ def parse():
     ap.add_argument("--workload", default="mixtral_8x7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--per-config-cpu-seconds", type=float, default=5.0,
+                    help="target CPU time of the oracle sample of each per_config workload")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="measure the chosen workload only (no per_config block)")
     ap.add_argument("--only", choices=["gate_up", "down"], default=None,
                     help="time one grouped GEMM alone (for counter runs); prints its own JSON line")
     ap.add_argument("--router", action="store_true",
@@ -79,6 +88,10 @@ def parse():
     return ap.parse_args()
 
 
+PER_CONFIG = ["tiny", "qwen3_moe_decode", "deepseek_v3", "megamoe_fp8xfp4"]
+DECODE = "qwen3_moe_decode"
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -86,24 +99,79 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_bytes:
+        return copy_calibration(args, dev)
+    if args.only:
+        import block_scaled_fp8_sort_amd as moe
+        import workloads as W
+
+        wl = W.WORKLOADS[args.workload]
+        inp = W.inputs(wl, dev)
+        w = moe.prepare_weights(inp["w13"], inp["s13"], inp["w2"], inp["s2"], fmt=wl.fmt)
+        return only_gemm(args, wl, inp, w, dev)
+
+    result = measure(args.workload, args, dev, args.steps, args.warmup, args.cpu_seconds, router=args.router)
+    line = {
+        "metric": METRIC,
+        "value": result.pop("tflops"),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": result.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": result.pop("dtype"),
+        "data": "synthetic",
+        "config": result.pop("config"),
+        "roofline": result.pop("roofline"),
+    }
+    if "cpu_baseline" in result:
+        line["cpu_baseline"] = result.pop("cpu_baseline")
+    if not args.no_per_config and args.workload == "mixtral_8x7b" and not args.router:
+        # the other workloads, measured the same way after the headline (outside
+        # its timed region); each drops its inputs before the next is generated
+        torch.cuda.empty_cache()
+        per = {}
+        for name in PER_CONFIG:
+            r = measure(name, args, dev, max(args.steps, 10), args.warmup, args.per_config_cpu_seconds,
+                        cold=name == DECODE)
+            per[name] = r
+            torch.cuda.empty_cache()
+        line["per_config"] = per
+    print(json.dumps(line), flush=True)
+
+
+def _percentiles(xs):
+    import numpy as np
+
+    a = np.asarray(xs)
+    return {"median_us": round(float(np.median(a)) * 1e3, 2), "p90_us": round(float(np.percentile(a, 90)) * 1e3, 2),
+            "min_us": round(float(a.min()) * 1e3, 2), "iterations": int(a.size)}
+
+
+def measure(name, args, dev, steps, warmup, cpu_seconds, router=False, cold=False):
+    """Time the forward of one workload (steps back to back, after warmup) and
+    its gate_up GEMM alone; returns the numbers of one JSON record."""
     import numpy as np
     import torch
 
     import block_scaled_fp8_sort_amd as moe
     import workloads as W
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.copy_bytes:
-        return copy_calibration(args, dev)
-    wl = W.WORKLOADS[args.workload]
+    wl = W.WORKLOADS[name]
     log(f"[bench] workload {wl.name}: generating inputs on the GPU")
     inp = W.inputs(wl, dev)
     w = moe.prepare_weights(inp["w13"], inp["s13"], inp["w2"], inp["s2"], fmt=wl.fmt)
     T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
     S = T * k
     logits = None
-    if args.router:
+    if router:
         if wl.routing != "uniform":
             print(f"--router needs a workload routed by a softmax over logits; {wl.name} is {wl.routing}",
                   file=sys.stderr)
@@ -145,26 +213,50 @@ def main():
             moe.experts_forward_from_logits(x, logits, k, w, swiglu_limit=wl.swiglu_limit, out=out,
                                             top_k_index=r_ids, top_k_weights=r_w, workspace=ws)
 
-    if args.only:
-        return only_gemm(args, wl, inp, w, dev)
-
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
+    log(f"[bench] warmup {warmup}")
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    log(f"[bench] timing {args.steps} steps")
+    log(f"[bench] timing {steps} steps")
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     ev1.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    ms = ev0.elapsed_time(ev1) / args.steps
-    log(f"[bench] {ms:.3f} ms/step (wall {1e3 * t_wall / args.steps:.3f} ms/step)")
+    ms = ev0.elapsed_time(ev1) / steps
+    log(f"[bench] {ms:.3f} ms/step (wall {1e3 * t_wall / steps:.3f} ms/step)")
+    extra = {}
+    if cold:
+        # one forward at a time, each bracketed by its own events: warm (back to
+        # back) and cold (a 1 GiB fill between forwards evicts the 256 MB
+        # last-level cache, so weights and inputs come from HBM)
+        n_it = 200
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_it)]
+        for a, b in evs:
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        warm = [a.elapsed_time(b) for a, b in evs]
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        for i, (a, b) in enumerate(evs):
+            scratch.fill_(i & 0xFF)
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        cold_t = [a.elapsed_time(b) for a, b in evs]
+        del scratch
+        extra["warm"] = _percentiles(warm)
+        extra["cold"] = dict(_percentiles(cold_t), evict_bytes_between=1 << 30)
+        extra["cold"]["hbm_gbs_algorithmic_median"] = round(alg_bytes / (np.median(cold_t) * 1e-3) / 1e9, 1)
+        extra["cold"]["hbm_frac_median"] = round(alg_bytes / (np.median(cold_t) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        log(f"[bench] per forward: warm median {np.median(warm) * 1e3:.1f} us, cold median {np.median(cold_t) * 1e3:.1f} us")
     router_us = None
     if logits is not None:
         # the router + route sort launch(es) alone, as moe_route_topk enqueues them
@@ -183,11 +275,11 @@ def main():
             route()
         torch.cuda.synchronize()
         ev0.record(stream)
-        for _ in range(args.steps):
+        for _ in range(steps):
             route()
         ev1.record(stream)
         torch.cuda.synchronize()
-        router_us = ev0.elapsed_time(ev1) / args.steps * 1e3
+        router_us = ev0.elapsed_time(ev1) / steps * 1e3
         log(f"[bench] router + route sort {router_us:.1f} us")
 
     # ---- dominant kernel: gate_up grouped GEMM with the SwiGLU + h-quant epilogue,
@@ -206,11 +298,11 @@ def main():
         l1()
     torch.cuda.synchronize()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         l1()
     ev1.record(stream)
     torch.cuda.synchronize()
-    l1_ms = ev0.elapsed_time(ev1) / args.steps
+    l1_ms = ev0.elapsed_time(ev1) / steps
     l1_tflops = flop_l1 / (l1_ms * 1e-3) / 1e12
     act_b = 2 if wl.fmt == W.FMT_BF16 else 1  # bytes per activation / h element
     l1_bytes = int(len(touched) * w13_bytes + (T * H + S_v * I) * act_b)  # weights + A in + h out
@@ -230,32 +322,29 @@ def main():
                 "frac": round(l1_gbs / PEAK_HBM_GBS, 4)}
 
     tflops = flop_total / (ms * 1e-3) / 1e12
+    config = {
+        "workload": wl.name, "tokens": T, "hidden": H, "intermediate": I, "experts": E, "top_k": k,
+        "format": {W.FMT_FP8_B128: "fp8 e4m3, fp32 scales 1x128 act / 128x128 weight",
+                   W.FMT_MX: "e4m3 act x e2m1 weight, UE8M0 per 1x32",
+                   W.FMT_BF16: "bf16 act x bf16 weight, no quantization"}[wl.fmt],
+        "routing": wl.routing, "skipped_slot_prob": wl.skip, "swiglu_limit": wl.swiglu_limit,
+        "valid_slots": S_v, "active_tflop": round(flop_total / 1e12, 4),
+        "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "pct_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2),
+        "pct_mxfp4_peak": round(100.0 * tflops / PEAK_MXFP4_TFLOPS, 2),
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "hbm_gbs_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "algorithmic_bytes": int(alg_bytes),
+    }
+    if logits is not None:
+        config["router"] = "fp32 logits N(0,1): softmax, top-k (lower id on ties), renormalised"
+        config["router_sort_us"] = round(router_us, 2)
     result = {
-        "metric": METRIC,
-        "value": round(tflops, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
+        "tflops": round(tflops, 2),
         "dtype": {W.FMT_FP8_B128: "fp8e4m3", W.FMT_MX: "fp8e4m3 x fp4e2m1", W.FMT_BF16: "bf16"}[wl.fmt],
-        "data": "synthetic",
-        "config": {
-            "workload": wl.name, "tokens": T, "hidden": H, "intermediate": I, "experts": E, "top_k": k,
-            "format": {W.FMT_FP8_B128: "fp8 e4m3, fp32 scales 1x128 act / 128x128 weight",
-                       W.FMT_MX: "e4m3 act x e2m1 weight, UE8M0 per 1x32",
-                       W.FMT_BF16: "bf16 act x bf16 weight, no quantization"}[wl.fmt],
-            "routing": wl.routing, "skipped_slot_prob": wl.skip, "swiglu_limit": wl.swiglu_limit,
-            "valid_slots": S_v, "active_tflop": round(flop_total / 1e12, 4),
-            "tokens_per_s": round(T / (ms * 1e-3), 1),
-            "pct_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2),
-            "pct_mxfp4_peak": round(100.0 * tflops / PEAK_MXFP4_TFLOPS, 2),
-            "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-            "hbm_gbs_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
-        },
+        "config": config,
         "roofline": dict(roof, **{
             "traffic": traffic_record(wl),
             "kernel": f"gate_up grouped GEMM + SwiGLU + h quantization ({kname}, MOE_EPI_SWIGLU_QUANT)",
@@ -265,13 +354,12 @@ def main():
             "pct_mxfp4_peak": round(100.0 * l1_tflops / PEAK_MXFP4_TFLOPS, 2),
         }),
     }
-
-    if logits is not None:
-        result["config"]["router"] = "fp32 logits N(0,1): softmax, top-k (lower id on ties), renormalised"
-        result["config"]["router_sort_us"] = round(router_us, 2)
+    result.update(extra)
+    del w, ws, out, h_codes, h_scales, a_codes
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, inp, cpu_seconds)
+    del inp
+    return result
 
 
 def traffic_record(wl):
@@ -405,7 +493,18 @@ def cpu_baseline(wl, inp, seconds):
     log(f"[bench] oracle: {sample.size} tokens in {dt:.1f} s on {threads} threads")
     return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{sample.size} of {wl.T} tokens (seeded), {s_v} valid slots, {dt:.1f} s",
-            "tokens_per_s": round(sample.size / dt, 2)}
+            "tokens_per_s": round(sample.size / dt, 2), "cpu_model": _cpu_model(),
+            "host_logical_cpus": os.cpu_count()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":
