@@ -15,7 +15,7 @@ roofline its arithmetic intensity binds (MFMA at the FP8 peak, or HBM);
 `per_config` repeats the measurement for the other workloads (the tiny layer,
 the Qwen3-MoE-shaped decode batch, the DeepSeek-V3-shaped layer and the
 Mega-MoE-style FP8 x FP4 layer), each with its own roofline and oracle sample;
-the decode batch is also timed cold (a 1 GiB write between forwards evicts the
+the decode batch is also timed cold (a 1 GiB read between forwards evicts the
 256 MB last-level cache) and warm, per forward.
 """
 from __future__ import annotations
@@ -114,7 +114,8 @@ def main():
         w = moe.prepare_weights(inp["w13"], inp["s13"], inp["w2"], inp["s2"], fmt=wl.fmt)
         return only_gemm(args, wl, inp, w, dev)
 
-    result = measure(args.workload, args, dev, args.steps, args.warmup, args.cpu_seconds, router=args.router)
+    result = measure(args.workload, args, dev, args.steps, args.warmup, args.cpu_seconds, router=args.router,
+                     cold=args.workload == DECODE)
     line = {
         "metric": METRIC,
         "value": result.pop("tflops"),
@@ -133,6 +134,7 @@ def main():
     }
     if "cpu_baseline" in result:
         line["cpu_baseline"] = result.pop("cpu_baseline")
+    line.update(result)  # per-forward warm / cold timings of the decode batch
     if not args.no_per_config and args.workload == "mixtral_8x7b" and not args.router:
         # the other workloads, measured the same way after the headline (outside
         # its timed region); each drops its inputs before the next is generated
@@ -233,8 +235,10 @@ def measure(name, args, dev, steps, warmup, cpu_seconds, router=False, cold=Fals
     extra = {}
     if cold:
         # one forward at a time, each bracketed by its own events: warm (back to
-        # back) and cold (a 1 GiB fill between forwards evicts the 256 MB
-        # last-level cache, so weights and inputs come from HBM)
+        # back) and cold (a 1 GiB read between forwards evicts the 256 MB
+        # last-level cache, so weights and inputs come from HBM; a read, not a
+        # fill, so that the cache holds clean lines, as after a layer that
+        # streamed its own weights, and no write-back lands on the forward)
         n_it = 200
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_it)]
         for a, b in evs:
@@ -243,9 +247,10 @@ def measure(name, args, dev, steps, warmup, cpu_seconds, router=False, cold=Fals
             b.record(stream)
         torch.cuda.synchronize()
         warm = [a.elapsed_time(b) for a, b in evs]
-        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        total = torch.empty((), dtype=torch.float32, device=dev)
         for i, (a, b) in enumerate(evs):
-            scratch.fill_(i & 0xFF)
+            torch.sum(scratch, dim=0, out=total)
             a.record(stream)
             step()
             b.record(stream)
@@ -253,7 +258,7 @@ def measure(name, args, dev, steps, warmup, cpu_seconds, router=False, cold=Fals
         cold_t = [a.elapsed_time(b) for a, b in evs]
         del scratch
         extra["warm"] = _percentiles(warm)
-        extra["cold"] = dict(_percentiles(cold_t), evict_bytes_between=1 << 30)
+        extra["cold"] = dict(_percentiles(cold_t), evict_read_bytes_between=1 << 30)
         extra["cold"]["hbm_gbs_algorithmic_median"] = round(alg_bytes / (np.median(cold_t) * 1e-3) / 1e9, 1)
         extra["cold"]["hbm_frac_median"] = round(alg_bytes / (np.median(cold_t) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         log(f"[bench] per forward: warm median {np.median(warm) * 1e3:.1f} us, cold median {np.median(cold_t) * 1e3:.1f} us")
