@@ -154,3 +154,49 @@ def test_forward_static_equal_to_dynamic_scales_is_the_dynamic_forward():
                             act_scales=torch.from_numpy(dyn).to(DEV))
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_e4m3_encoder_over_the_fp32_range():
+    """The device's e4m3 encoding (the hardware conversion after a clamp to
+    +-448, the step every quantization in the library ends with) against the
+    oracle's nearest-even encoder, on fp32 quotients x / s spread over every
+    exponent that matters: saturating (|q| >= 448, up to 2^40), normal, e4m3
+    subnormal (below 2^-6) and underflowing to zero (below 2^-10), plus
+    quotients within an fp32 ulp of every e4m3 rounding midpoint.  The static
+    scheme hands the device arbitrary block scales, so x / s can be any fp32
+    value; the quotient itself is the IEEE one on both sides (checked on the
+    host), so a code mismatch can only come from the encoding."""
+    rng = np.random.default_rng(123)
+    rows, H = 8192, 1024
+    B = 128
+    nb = rows * (H // B)
+    # x: bf16 values with exponents in [-12, 12], random signs and mantissas
+    x = np.ldexp(rng.uniform(1, 2, size=(rows, H)), rng.integers(-12, 13, size=(rows, H)))
+    x *= np.where(rng.random((rows, H)) < 0.5, -1, 1)
+    xb = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+    xv = xb.double().numpy()
+    # per-block scales: log-uniform over a range that puts x / s anywhere from 2^-30 to 2^40
+    sc = np.exp2(rng.uniform(-52, 28, size=(rows, H // B))).astype(np.float32)
+    # a quarter of the blocks: scale = x0 / m0 with m0 an e4m3 rounding midpoint, so
+    # that x0 / s sits within an fp32 ulp of it
+    v = torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    mids = (v[1:] + v[:-1]) / 2
+    blocks = xv.reshape(nb, B)
+    sflat = sc.reshape(nb)
+    pick = rng.random(nb) < 0.25
+    m0 = rng.choice(mids, size=int(pick.sum()))
+    sflat[pick] = (np.abs(blocks[pick, 0]) / m0).astype(np.float32)
+    sc = sflat.reshape(rows, H // B)
+    x_bits = xb.view(torch.int16).numpy().view(np.uint16)
+    codes, _ = moe.quant_act_static(xb.to(DEV), torch.from_numpy(sc).to(DEV), FP8)
+    torch.cuda.synchronize()
+    o_codes = oracle.quant_rows_bf16_static(x_bits, FP8, sc)
+    g = _rowmajor_codes(codes)
+    q = np.abs(xv / np.repeat(sc.astype(np.float64), B, axis=1))
+    cover = {"saturating": np.mean(q >= 448), "normal": np.mean((q >= 2 ** -6) & (q < 448)),
+             "subnormal": np.mean((q >= 2 ** -10) & (q < 2 ** -6)), "zero": np.mean(q < 2 ** -10)}
+    say("  quotient coverage: " + ", ".join(f"{k} {100 * v:.1f}%" for k, v in cover.items()) +
+        f"; log2|q| from {np.log2(q[q > 0].min()):.0f} to {np.log2(q.max()):.0f}")
+    assert all(v > 0.02 for v in cover.values())
+    mism = np.argwhere(g != o_codes)
+    assert mism.size == 0, f"{len(mism)} code mismatches, first at {mism[:5]}"
