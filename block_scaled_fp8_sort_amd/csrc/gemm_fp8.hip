@@ -197,12 +197,15 @@ __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nx
   v8i af = lds_frag_w(cur->w, wn * 8, lane);
 #pragma unroll
   for (int ni = 0; ni <= 8; ++ni) {
-    // the DMAs of block kb + STAGES - 1 go out spread over the sub-tiles: issued
-    // all at once they queue in the texture addresser and hold every wave back
-    // from its MFMAs; between MFMAs they drain in the background
+    // the DMAs of block kb + STAGES - 1 go out spread over the first six of the
+    // eight sub-tiles: issued all at once they queue in the texture addresser
+    // and hold every wave back from its MFMAs, between MFMAs they drain in the
+    // background; spread over all eight, the last ones have too little of the
+    // step left to land before the next step's wait (six: the gate_up GEMM 1-3%
+    // faster than eight; five and seven about the same as six, four slower)
 #pragma unroll
     for (int idx = 0; idx < LOADS; ++idx)
-      if (idx * 8 / LOADS == ni) issue_part<BM>(nxt, src, kb_dma, wave, lane, idx);
+      if (idx * 6 / LOADS == ni) issue_part<BM>(nxt, src, kb_dma, wave, lane, idx);
     v8i af_next = af;
     if (ni < 7) af_next = lds_frag_w(cur->w, wn * 8 + ni + 1, lane);
     const int pn = ni - 1;
