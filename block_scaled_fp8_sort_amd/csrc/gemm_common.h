@@ -80,6 +80,7 @@ __device__ __forceinline__ int build_tile_table(const int32_t* offsets, int E, i
 
 struct TileCoord {
   int e, n_tile, m0, m_end;
+  int half;  // two-phase table with split phase-1 tiles: which 128 weight rows of the n-tile, else -1
 };
 
 // Order of an expert's mt x NT tiles: groups of up to kTileGroupM m-tiles, m
@@ -109,6 +110,7 @@ __device__ __forceinline__ TileCoord locate_tile(int t, int E, int BM, int NT, c
     if (tp[mid] <= t) lo = mid; else hi = mid;
   }
   TileCoord c;
+  c.half = -1;
   c.e = __builtin_amdgcn_readfirstlane(lo);
   const int m_begin = __builtin_amdgcn_readfirstlane(off[c.e]);
   c.m_end = __builtin_amdgcn_readfirstlane(off[c.e + 1]);
@@ -133,14 +135,15 @@ __device__ __forceinline__ TileCoord locate_tile(int t, int E, int BM, int NT, c
 //   off[e]  expert offsets (E + 1)
 //   tp[e]   first phase-0 tile of expert e; tp[E] = phase-0 total
 //   cnt[e]  experts before e that have a phase-1 tile; expert e's phase-1 tiles
-//           are [cnt[e] NT, cnt[e] NT + NT)
+//           are [cnt[e] NT, cnt[e] NT + NT), or with SPLIT = 2 the two 128-row
+//           halves of each n-tile, [2 cnt[e] NT, 2 cnt[e] NT + 2 NT)
 // Returns the total tile count.  All threads of the block must call it.
 __device__ __forceinline__ int has_short_tile(int rows) {
   return rows > 256 && (rows % 256) > 0 && (rows % 256) <= 128;
 }
 __device__ __forceinline__ int full_m_tiles(int rows) { return (rows + 255) / 256 - has_short_tile(rows); }
 
-template <int THREADS>
+template <int THREADS, int SPLIT = 1>
 __device__ __forceinline__ int build_tile_table2(const int32_t* offsets, int E, int NT, int* off, int* tp,
                                                  uint16_t* cnt, int2* scan) {
   const int tid = threadIdx.x;
@@ -168,15 +171,17 @@ __device__ __forceinline__ int build_tile_table2(const int32_t* offsets, int E, 
     cnt[E] = (uint16_t)tot1;
   }
   __syncthreads();
-  return tp[E] + (int)cnt[E] * NT;
+  return tp[E] + (int)cnt[E] * NT * SPLIT;
 }
 
 // Tile t of the two-phase table -> (expert, n-tile, first sorted row, end of
-// the expert's rows), made wave-uniform.
+// the expert's rows, half), made wave-uniform.
+template <int SPLIT = 1>
 __device__ __forceinline__ TileCoord locate_tile2(int t, int E, int NT, const int* off, const int* tp,
                                                   const uint16_t* cnt) {
   const int total0 = __builtin_amdgcn_readfirstlane(tp[E]);
   TileCoord c;
+  c.half = -1;
   int lo = 0, hi = E;
   if (t < total0) {
     while (hi - lo > 1) {
@@ -193,7 +198,7 @@ __device__ __forceinline__ TileCoord locate_tile2(int t, int E, int NT, const in
     c.m0 = m_begin + m_idx * 256;
   } else {
     const int t1 = t - total0;
-    const int j = t1 / NT;  // the j-th expert that has a phase-1 tile
+    const int j = t1 / (NT * SPLIT);  // the j-th expert that has a phase-1 tile
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if ((int)cnt[mid] <= j) lo = mid; else hi = mid;
@@ -201,7 +206,9 @@ __device__ __forceinline__ TileCoord locate_tile2(int t, int E, int NT, const in
     c.e = __builtin_amdgcn_readfirstlane(lo);
     const int m_begin = __builtin_amdgcn_readfirstlane(off[c.e]);
     c.m_end = __builtin_amdgcn_readfirstlane(off[c.e + 1]);
-    c.n_tile = t1 - j * NT;
+    const int loc = t1 - j * NT * SPLIT;
+    c.n_tile = loc / SPLIT;
+    if (SPLIT == 2) c.half = loc - c.n_tile * 2;
     c.m0 = m_begin + ((c.m_end - m_begin) / 256) * 256;
   }
   return c;
@@ -285,29 +292,34 @@ __device__ __forceinline__ int xcd_virtual_block() {
 constexpr int kOutPitch = 528;  // bytes per staged row: 512 + 16 (fewer bank conflicts)
 
 // Second half of the staged scatter: ROWS staged rows (bf16, pitch
-// kOutPitch) leave as 512-byte row segments to slot_out[srow[r]][256 n_tile ...];
+// kOutPitch) leave as COLS * 2-byte row segments to slot_out[srow[r]][col0 ...];
 // rows with srow < 0 are skipped.  Staging must be complete (barrier) on entry.
-template <int ROWS>
+template <int ROWS, int COLS = 256>
 __device__ __forceinline__ void copy_out_staged_rows(const GemmParams& p, const uint8_t* area, const int* srow,
-                                                     int n_tile, int tid) {
+                                                     int col0, int tid) {
+  constexpr int LPR = COLS / 8;        // lanes per row, 8 columns each
+  constexpr int RPP = 8 * 64 / LPR;    // rows per pass of the 8 waves
   const int wave = tid >> 6, lane = tid & 63;
   const int N = p.N;
-  // wave w, pass j: tile row 16 j + 2 w + (lane / 32), 8 columns per lane
-  const int n0 = n_tile * 256 + (lane & 31) * 8;
+  // wave w, pass j: tile row RPP j + (64 / LPR) w + lane / LPR
+  const int n0 = col0 + (lane % LPR) * 8;
 #pragma unroll 4
-  for (int j = 0; j < ROWS / 16; ++j) {
-    const int tr = 16 * j + 2 * wave + (lane >> 5);
+  for (int j = 0; j < ROWS / RPP; ++j) {
+    const int tr = RPP * j + (64 / LPR) * wave + lane / LPR;
     const int slot = srow[tr];
     if (slot >= 0 && n0 < N) {
-      const int4 v = *(const int4*)(area + tr * kOutPitch + (lane & 31) * 16);
+      const int4 v = *(const int4*)(area + tr * kOutPitch + (lane % LPR) * 16);
       *(int4*)(p.slot_out + (size_t)slot * N + n0) = v;
     }
   }
 }
 
-template <int BM, typename V>
+// The weighted scatter of a tile's outputs: NW 16-column groups per wave (8: a
+// 256-column n-tile, the two waves of a token quarter 128 columns each; 4: one
+// 128-column half, starting at column col0 of the output).
+template <int BM, int NW = 8, typename V>
 __device__ __forceinline__ void scatter_rows_staged(const GemmParams& p, uint8_t* area, int* srow,
-                                                    const V (&acc)[8][BM / 64], int n_tile, int m0, int m_end,
+                                                    const V (&acc)[NW][BM / 64], int col0, int m0, int m_end,
                                                     int tid) {
   constexpr int WM = BM / 4, TS = WM / 16;
   const int wave = tid >> 6, lane = tid & 63;
@@ -320,16 +332,16 @@ __device__ __forceinline__ void scatter_rows_staged(const GemmParams& p, uint8_t
     const int r = m0 + tr;
     const float w = r < m_end ? p.top_k_weights[p.slot_of_row[r]] : 0.0f;
 #pragma unroll
-    for (int ni = 0; ni < 8; ++ni) {
+    for (int ni = 0; ni < NW; ++ni) {
       const V v = acc[ni][ti] * w;
       uint2 o;
       o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
       o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-      *(uint2*)(area + tr * kOutPitch + (wn * 128 + ni * 16 + 4 * g) * 2) = o;
+      *(uint2*)(area + tr * kOutPitch + (wn * NW * 16 + ni * 16 + 4 * g) * 2) = o;
     }
   }
   __syncthreads();
-  copy_out_staged_rows<BM>(p, area, srow, n_tile, tid);
+  copy_out_staged_rows<BM, NW * 32>(p, area, srow, col0, tid);
 }
 
 // SwiGLU epilogues: a tile's h codes are BM sorted rows x 128 bytes of one

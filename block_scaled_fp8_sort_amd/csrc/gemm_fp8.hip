@@ -36,7 +36,10 @@
 //    table in LDS (per expert, groups of up to 8 m-tiles, m fastest inside a
 //    group, then n; the short remainder tiles of large experts after all the
 //    rest, so they fill the last round), and walks tiles with a stride of the
-//    grid size.
+//    grid size.  Without the gate/up pairing those remainder tiles run as two
+//    128-row halves of each n-tile: the last round then has twice the tiles to
+//    spread over the CUs, and each half streams its weights through four or
+//    five stages instead of three.
 //    Workgroup ids are remapped so that consecutive tiles land on the same XCD
 //    (dispatch is round-robin over the 8 XCDs): a weight tile is shared by the
 //    group's m-tiles in that XCD's L2, and the group's activation rows stay
@@ -65,14 +68,14 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxE = 512;
 
-// One pipeline stage in LDS: the 256 weight rows and BM activation rows of one
-// 128-wide K block, and the scales of that block (one 256-byte DMA per wave:
-// slots [0, BM) are the activation scales in the order the MFMA lanes read
-// them, slots BM and BM + 1 the two weight-block scales).  Each stage is its
-// own __shared__ object.
-template <int BM>
+// One pipeline stage in LDS: the WR weight rows (256, or one 128-row half of
+// an n-tile) and BM activation rows of one 128-wide K block, and the scales of
+// that block (one 256-byte DMA per wave: slots [0, BM) are the activation
+// scales in the order the MFMA lanes read them, slots BM and BM + 1 the two
+// weight-block scales).
+template <int BM, int WR = BN>
 struct StageBuf {
-  uint8_t w[BN * BK];
+  uint8_t w[WR * BK];
   uint8_t a[BM * BK];
   float s[kWaves * 64];
 };
@@ -93,13 +96,15 @@ struct Misc {
 
 // LDS shared by the pipeline stages of every tile height: three stages of the
 // 128-row layout, which also hold two of the 256-row one and three of the
-// 64-row one.
+// 64-row one, and four or five of the half-width (128 weight rows) ones.
 constexpr int kStageArea = 3 * (int)sizeof(StageBuf<128>);
-template <int BM>
+template <int BM, int WR = BN>
 constexpr int stages_for() {
-  return kStageArea / (int)sizeof(StageBuf<BM>) < 4 ? kStageArea / (int)sizeof(StageBuf<BM>) : 4;
+  return kStageArea / (int)sizeof(StageBuf<BM, WR>) < 5 ? kStageArea / (int)sizeof(StageBuf<BM, WR>) : 5;
 }
-static_assert(stages_for<256>() >= 2 && stages_for<64>() >= 3, "stage area");
+static_assert(stages_for<256>() >= 2 && stages_for<64>() >= 3 && stages_for<128, 128>() >= 4 &&
+                  stages_for<64, 128>() >= 5,
+              "stage area");
 
 // The 32 bytes lane group g of an MFMA operand holds: K bytes [16 g, 16 g + 16)
 // and [64 + 16 g, 64 + 16 g + 16) of its row (logical chunks g and 4 + g).
@@ -123,7 +128,7 @@ __device__ __forceinline__ v8i lds_frag_w(const uint8_t* region, int grp, int la
 template <int BM>
 struct TileSrc {
   static constexpr int A_LOADS = BM / 64;  // 1 KB activation DMAs per wave per stage
-  const uint8_t* w_tile;   // tiled weights of (expert, n-tile), K block 0 (uniform)
+  const uint8_t* w_tile;   // tiled weights of (expert, n-tile[, half]), K block 0 (uniform)
   const uint8_t* a_codes;  // activation planes (uniform)
   size_t a_plane;          // bytes of one 128-wide K plane of activation codes
   uint32_t a_off[A_LOADS]; // per-lane byte offset of the gathered row chunk
@@ -131,32 +136,35 @@ struct TileSrc {
   uint32_t s_stride;       // per-lane scale advance per K block, in floats
 };
 
-// DMA instruction idx (0 .. LOADS - 1) of the stage for block kb: 0-3 the
-// weights (wave w copies the 4 KB of tile rows [32 w, 32 w + 32), contiguous),
-// then BM / 64 activation gathers (wave w gathers rows [w BM/8, (w+1) BM/8) of
-// the tile), last the scales.  idx is a compile-time constant after unrolling.
-template <int BM>
-__device__ __forceinline__ void issue_part(StageBuf<BM>* st, const TileSrc<BM>& src, int kb, int wave, int lane,
-                                           int idx) {
+// DMA instruction idx (0 .. LOADS - 1) of the stage for block kb: first WR / 64
+// for the weights (wave w copies the WR / 8 rows [w WR/8, (w+1) WR/8) of the
+// stage, contiguous in the tiled layout), then BM / 64 activation gathers (wave
+// w gathers rows [w BM/8, (w+1) BM/8) of the tile), last the scales.  idx is a
+// compile-time constant after unrolling.
+template <int BM, int WR>
+__device__ __forceinline__ void issue_part(StageBuf<BM, WR>* st, const TileSrc<BM>& src, int kb, int wave,
+                                           int lane, int idx) {
+  constexpr int W_LOADS = WR / 64, WB = WR * BK / kWaves;  // per wave: 1 KB DMAs, bytes
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(st));
   const uint32_t w = __builtin_amdgcn_readfirstlane(wave);
-  if (idx < 4) {
-    const uint8_t* wsrc = src.w_tile + (size_t)kb * (BN * BK) + w * 4096;
-    lds_dma16_s(wsrc + idx * 1024, lane * 16, base + w * 4096 + idx * 1024);
-  } else if (idx < 4 + TileSrc<BM>::A_LOADS) {
-    const int q = idx - 4;
+  if (idx < W_LOADS) {
+    const uint8_t* wsrc = src.w_tile + (size_t)kb * (BN * BK) + w * WB;
+    lds_dma16_s(wsrc + idx * 1024, lane * 16, base + w * WB + idx * 1024);
+  } else if (idx < W_LOADS + TileSrc<BM>::A_LOADS) {
+    const int q = idx - W_LOADS;
     const uint8_t* plane = src.a_codes + (size_t)kb * src.a_plane;
-    lds_dma16_s(plane, src.a_off[q], base + BN * BK + (w * (BM / 8) + 8 * q) * BK);
+    lds_dma16_s(plane, src.a_off[q], base + WR * BK + (w * (BM / 8) + 8 * q) * BK);
   } else {
-    lds_dma4(src.s_base + (size_t)kb * src.s_stride, base + (BN + BM) * BK + w * 256);
+    lds_dma4(src.s_base + (size_t)kb * src.s_stride, base + (WR + BM) * BK + w * 256);
   }
 }
 
-template <int BM>
-__device__ __forceinline__ void issue_stage(StageBuf<BM>* st, const TileSrc<BM>& src, int kb, int wave, int lane) {
-  constexpr int LOADS = 4 + BM / 64 + 1;
+template <int BM, int WR>
+__device__ __forceinline__ void issue_stage(StageBuf<BM, WR>* st, const TileSrc<BM>& src, int kb, int wave,
+                                            int lane) {
+  constexpr int LOADS = WR / 64 + BM / 64 + 1;
 #pragma unroll
-  for (int idx = 0; idx < LOADS; ++idx) issue_part<BM>(st, src, kb, wave, lane, idx);
+  for (int idx = 0; idx < LOADS; ++idx) issue_part<BM, WR>(st, src, kb, wave, lane, idx);
 }
 
 // One K block: wait for stage `cur`, then accumulate the block from `cur` while
@@ -165,18 +173,20 @@ __device__ __forceinline__ void issue_stage(StageBuf<BM>* st, const TileSrc<BM>&
 // Past the last block the DMA repeats block KB - 1 into a stage nobody reads,
 // which keeps the number of DMAs in flight, and so this wait, the same on every
 // step.
-template <int BM, bool PAIRED, int STAGES>
-__device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nxt, const TileSrc<BM>& src, int kb,
-                                       int KB, int wave, int lane, v4f (&acc)[8][BM / 64]) {
+template <int BM, bool PAIRED, int STAGES, int WR>
+__device__ __forceinline__ void k_step(const StageBuf<BM, WR>* cur, StageBuf<BM, WR>* nxt, const TileSrc<BM>& src,
+                                       int kb, int KB, int wave, int lane, v4f (&acc)[WR / 32][BM / 64]) {
   constexpr int WM = BM / 4;
   constexpr int TS = WM / 16;
-  constexpr int LOADS = 4 + BM / 64 + 1;  // DMA instructions per wave per stage
+  constexpr int NW = WR / 32;                    // 16-row weight groups per wave
+  constexpr int LOADS = WR / 64 + BM / 64 + 1;  // DMA instructions per wave per stage
   const int wn = wave & 1, wt = wave >> 1;
   const int g = lane >> 4, l16 = lane & 15;
   wait_vmcnt<LOADS * (STAGES - 2)>();  // this wave's DMAs of stage kb have landed
   raw_barrier();  // ... and every other wave's; all waves are done with block kb - 1
   const int kb_dma = min(kb + STAGES - 1, KB - 1);
-  const float swg = cur->s[PAIRED ? BM : BM + wn];
+  // a half tile's 128 rows lie in one 128-row weight-scale block
+  const float swg = cur->s[PAIRED || WR == 128 ? BM : BM + wn];
   const float swu = cur->s[BM + 1];
   typedef float vts __attribute__((ext_vector_type(TS)));
   const vts sav = *(const vts*)(cur->s + (wt * 16 + l16) * TS);
@@ -194,9 +204,9 @@ __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nx
   // ni - 1) into the accumulators, and the weight fragment of sub-tile ni + 1 is
   // read from LDS meanwhile.  sched_barrier(0) keeps this program order.
   v4f part[2][TS];
-  v8i af = lds_frag_w(cur->w, wn * 8, lane);
+  v8i af = lds_frag_w(cur->w, wn * NW, lane);
 #pragma unroll
-  for (int ni = 0; ni <= 8; ++ni) {
+  for (int ni = 0; ni <= NW; ++ni) {
     // the DMAs of block kb + STAGES - 1 go out spread over the first six of the
     // eight sub-tiles: issued all at once they queue in the texture addresser
     // and hold every wave back from its MFMAs, between MFMAs they drain in the
@@ -205,14 +215,14 @@ __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nx
     // faster than eight; five and seven about the same as six, four slower)
 #pragma unroll
     for (int idx = 0; idx < LOADS; ++idx)
-      if (idx * 6 / LOADS == ni) issue_part<BM>(nxt, src, kb_dma, wave, lane, idx);
+      if (idx * (NW * 3 / 4) / LOADS == ni) issue_part<BM, WR>(nxt, src, kb_dma, wave, lane, idx);
     v8i af_next = af;
-    if (ni < 7) af_next = lds_frag_w(cur->w, wn * 8 + ni + 1, lane);
+    if (ni < NW - 1) af_next = lds_frag_w(cur->w, wn * NW + ni + 1, lane);
     const int pn = ni - 1;
     const bool up = PAIRED && (pn & 1);
 #pragma unroll
     for (int ti = 0; ti < TS; ++ti) {
-      if (ni < 8)
+      if (ni < NW)
         part[ni & 1][ti] =
             __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[ti], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
       if (ni > 0) acc[pn][ti] += part[pn & 1][ti] * (up ? fu[ti] : fg[ti]);
@@ -223,16 +233,20 @@ __device__ __forceinline__ void k_step(const StageBuf<BM>* cur, StageBuf<BM>* nx
 }
 
 // One tile of BM sorted rows [m0, min(m0 + BM, m_end)) of expert e against
-// n-tile n_tile: the K loop through a ring of STAGES LDS stages carved out of
-// `area`, then the epilogue.
-template <int BM, int EPI, bool PAIRED>
+// n-tile n_tile (WR = 256), or against its 128 weight rows [128 half, 128 half +
+// 128) (WR = 128, unpaired only): the K loop through a ring of STAGES LDS
+// stages carved out of `area`, then the epilogue.  A half tile streams half the
+// weights per stage, so more stages fit and more bytes are in flight per CU.
+template <int BM, int EPI, bool PAIRED, int WR = BN>
 __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Misc& misc, int e, int n_tile, int m0,
-                                         int m_end) {
-  constexpr int STAGES = stages_for<BM>();
+                                         int m_end, int half = 0) {
+  constexpr int STAGES = stages_for<BM, WR>();
   constexpr int WM = BM / 4;   // tokens per wave
   constexpr int TS = WM / 16;  // 16-token sub-tiles per wave
+  constexpr int NW = WR / 32;  // 16-row weight groups per wave
   static_assert(TS >= 1 && BM + 2 <= kWaves * 64, "64 <= BM <= 256");
-  StageBuf<BM>* st = reinterpret_cast<StageBuf<BM>*>(area);
+  static_assert(WR == BN || (WR == 128 && !PAIRED), "half tiles are unpaired");
+  StageBuf<BM, WR>* st = reinterpret_cast<StageBuf<BM, WR>*>(area);
 
   // the thread id is made opaque per tile so that the per-lane address math of
   // each tile height stays inside its tile instead of being hoisted out of the
@@ -250,7 +264,7 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Mis
 
   // ---- per-lane DMA sources
   TileSrc<BM> src;
-  src.w_tile = p.b_codes + ((size_t)e * NT + n_tile) * (size_t)KB * (BN * BK);
+  src.w_tile = p.b_codes + ((size_t)e * NT + n_tile) * (size_t)KB * (BN * BK) + (WR == 128 ? half * (128 * BK) : 0);
   src.a_codes = p.a_codes;
   src.a_plane = (size_t)p.a_rows * BK;
 #pragma unroll
@@ -265,6 +279,7 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Mis
     if (slot == BM || slot == BM + 1) {
       int nb;
       if constexpr (PAIRED) nb = slot == BM ? n_tile : I / 128 + n_tile;
+      else if constexpr (WR == 128) nb = min(n_tile * 2 + half, NB - 1);
       else nb = min(n_tile * 2 + (slot - BM), NB - 1);
       src.s_base = bsc + ((size_t)e * NB + nb) * KB;
       src.s_stride = 1;
@@ -284,20 +299,20 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Mis
     }
   }
 
-  v4f acc[8][TS];
+  v4f acc[NW][TS];
 #pragma unroll
-  for (int ni = 0; ni < 8; ++ni)
+  for (int ni = 0; ni < NW; ++ni)
 #pragma unroll
     for (int ti = 0; ti < TS; ++ti) acc[ni][ti] = v4f{0.f, 0.f, 0.f, 0.f};
 
   __syncthreads();  // the previous tile's LDS readers are done
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) issue_stage<BM>(&st[s], src, min(s, KB - 1), wave, lane);
+  for (int s = 0; s < STAGES - 1; ++s) issue_stage<BM, WR>(&st[s], src, min(s, KB - 1), wave, lane);
   for (int kb = 0; kb < KB; kb += STAGES) {
 #pragma unroll
     for (int j = 0; j < STAGES; ++j)
       if (kb + j < KB)
-        k_step<BM, PAIRED, STAGES>(&st[j], &st[(j + STAGES - 1) % STAGES], src, kb + j, KB, wave, lane, acc);
+        k_step<BM, PAIRED, STAGES, WR>(&st[j], &st[(j + STAGES - 1) % STAGES], src, kb + j, KB, wave, lane, acc);
   }
   wait_vmcnt<0>();  // the trailing repeat DMAs land before the stages are reused
 
@@ -308,13 +323,13 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Mis
       const int r = m0 + wt * WM + ti * 16 + l16;
       if (r < m_end) {
 #pragma unroll
-        for (int ni = 0; ni < 8; ++ni) {
+        for (int ni = 0; ni < NW; ++ni) {
           int n;
           if constexpr (PAIRED) {
             const int h = n_tile * 128 + 16 * (wn * 4 + (ni >> 1)) + 4 * g;
             n = (ni & 1) ? I + h : h;
           } else {
-            n = n_tile * BN + wn * 128 + ni * 16 + 4 * g;
+            n = n_tile * BN + (WR == 128 ? half * 128 : 0) + wn * NW * 16 + ni * 16 + 4 * g;
           }
           if (n < N) *(v4f*)(p.c_f32 + (size_t)r * N + n) = acc[ni][ti];
         }
@@ -370,7 +385,8 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Mis
     copy_out_h_codes<BM>(p, area, n_tile, m0, m_end, tid);
   } else {  // kEpiWeightedScatter
     static_assert(BM * kOutPitch <= kStageArea, "output staging");
-    scatter_rows_staged<BM>(p, area, reinterpret_cast<int*>(&misc.amax[0][0]), acc, n_tile, m0, m_end, tid);
+    scatter_rows_staged<BM, NW>(p, area, reinterpret_cast<int*>(&misc.amax[0][0]), acc,
+                                n_tile * BN + (WR == 128 ? half * 128 : 0), m0, m_end, tid);
   }
 }
 
@@ -384,11 +400,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p
   __shared__ __attribute__((aligned(16))) Misc misc;
   const int E = p.E, N = p.N;
   const int NT = PAIRED ? (N / 2) / 128 : (N + BN - 1) / BN;
-  const int total = build_tile_table2<kThreads>(p.offsets, E, NT, misc.off, misc.tp, misc.cnt, misc.scan);
+  // unpaired: the short remainder tiles (at most 128 rows, run last) go as two
+  // 128-row halves each
+  constexpr int SPLIT = PAIRED ? 1 : 2;
+  const int total = build_tile_table2<kThreads, SPLIT>(p.offsets, E, NT, misc.off, misc.tp, misc.cnt, misc.scan);
   const int G = gridDim.x;
   auto run = [&](int t) {
-    const TileCoord tc = locate_tile2(t, E, NT, misc.off, misc.tp, misc.cnt);
+    const TileCoord tc = locate_tile2<SPLIT>(t, E, NT, misc.off, misc.tp, misc.cnt);
     const int left = tc.m_end - tc.m0;
+    if constexpr (!PAIRED) {
+      if (tc.half >= 0) {  // uniform
+        if (left > 64)
+          run_tile<128, EPI, PAIRED, 128>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end, tc.half);
+        else
+          run_tile<64, EPI, PAIRED, 128>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end, tc.half);
+        return;
+      }
+    }
     if (left > 128)
       run_tile<256, EPI, PAIRED>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end);
     else if (left > 64)

@@ -305,7 +305,7 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, int
           *(const uint32_t*)(sstage + tid * 4);
   } else {  // kEpiWeightedScatter
     static_assert(BM * kOutPitch <= kStageArea, "output staging");
-    scatter_rows_staged<BM>(p, area, srow, acc, n_tile, m0, m_end, tid);
+    scatter_rows_staged<BM>(p, area, srow, acc, n_tile * 256, m0, m_end, tid);
   }
 }
 

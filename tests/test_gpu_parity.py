@@ -249,6 +249,20 @@ def test_grouped_gemm_few_rows_one_heavy_expert(which):
     _gemm_vs_oracle(FP8, which, E, 512, 384, ids, k, seed=77)
 
 
+@pytest.mark.parametrize("H", [512, 640])
+def test_grouped_gemm_half_width_tail_tiles(H):
+    """The unpaired GEMM runs an expert's short remainder tile (at most 128 rows
+    past its full 256-row tiles) as two 128-row halves of each n-tile: rows
+    counts with remainders of 1, 40, 64, 65, 100 and 128 rows (both half
+    heights), an expert with no remainder and one with fewer than 256 rows;
+    H = 640 leaves the second half of the last n-tile past N."""
+    say(f"gemm half-width tail tiles H={H}")
+    counts = [256 + 40, 512 + 100, 256 + 128, 300, 256 + 1, 512, 200, 256 + 64, 256 + 65]
+    ids = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
+    ids = np.random.default_rng(90).permutation(ids).reshape(-1, 1)
+    _gemm_vs_oracle(FP8, 1, len(counts), H, 256, ids, 1, seed=90)
+
+
 @pytest.mark.parametrize("fmt", [FP8, MX])
 def test_grouped_gemm_tile_order_and_counters(fmt):
     """The fixed round-robin tile order (no counters) and the dynamic dispensers
@@ -338,6 +352,10 @@ SMALL = [
     _small_workload("k16_fp8", FP8, T=96, H=256, I=128, E=32, k=16, routing="zipf", skip=0.1, seed=24),
     _small_workload("k64_fp8", FP8, T=20, H=256, I=128, E=128, k=64, routing="zipf", skip=0.1, seed=25),
     _small_workload("k24_mx", MX, T=40, H=256, I=128, E=48, k=24, routing="zipf", skip=0.1, limit=7.0, seed=26),
+    # the down GEMM's half-width tail tiles: experts of 303-339 rows (remainders
+    # of 47 to 83 past one 256-row tile: both half heights), H = 640 (a partial
+    # last n-tile)
+    _small_workload("tail_halves_fp8", FP8, T=640, H=640, I=256, E=4, k=2, seed=29),
     # 16384 slots and more: the multi-workgroup sort; the activation scales are
     # then copied by sorted row (sorted_slot / k) for the gate_up GEMM
     _small_workload("multiblock_fp8", FP8, T=2100, H=384, I=256, E=64, k=8, routing="zipf", skip=0.05, seed=27),
