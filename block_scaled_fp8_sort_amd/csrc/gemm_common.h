@@ -219,57 +219,114 @@ __device__ __forceinline__ TileCoord locate_tile2(int t, int E, int NT, const in
 // w % 8, so each XCD gets a fair slice of the whole sequence (its short tail
 // included) while the tiles that share a weight or activation tile still run
 // together on one XCD, whose workgroups (dispatch puts block b on XCD b % 8)
-// take them in order from an atomic counter.  Counter x lives at
-// counters[x * 32] (own 128-byte line).  Each workgroup makes exactly one failed
-// grab, so the grab that returns count + workgroups - 1 is the dispenser's last;
-// it resets the counter to 0, and the counters are zero again when the launch
-// ends.  With a grid that is not a multiple of 8, one dispenser hands out the
-// plain sequence.
+// take them in order from the front of its dispenser.  Equal tile counts are
+// not equal work (tiles of different heights, skewed experts), so a workgroup
+// whose own dispenser is exhausted takes tiles from the back of the dispenser
+// with the most left: the tail of that XCD's share, away from the tiles its own
+// workgroups run (and share their L2 with) at the front.  A dispenser is one
+// 64-bit counter, taken from the front in its low half and from the back in its
+// high half; a take with old halves (f, b) is valid iff f + b < count, and then
+// hands out index f (front) or count - 1 - b (back), so every index goes out
+// exactly once.  Dispenser x's counter is at counters[x * 32] (own 128-byte
+// line), the count of retired workgroups at counters[2]; the last workgroup to
+// retire zeroes them, so the counters are zero again when the launch ends.
+// With a grid that is not a multiple of 8, one dispenser hands out the plain
+// sequence.
 constexpr int kWindow = 32;
 constexpr int kCounterStride = 32;  // ints between counters: 128 bytes
 
 struct Dispenser {
-  int32_t* ctr;  // this workgroup's counter
-  int x, nd;     // dispenser index, number of dispensers
-  int count;     // tiles it hands out
-  int last;      // value of its final grab
+  int32_t* base;  // the counters
+  int x, y, nd;   // own dispenser, the one taken from, number of dispensers
+  int back;       // taking from the back of dispenser y (after the own one ran out)
+  int total;      // tiles in the sequence
 };
+
+// Tiles that dispenser x hands out.
+__device__ __forceinline__ int dispenser_count(int x, int nd, int total) {
+  if (nd == 1) return total;
+  const int nwin = (total + kWindow - 1) / kWindow;
+  const int owned = x < nwin ? (nwin - 1 - x) / 8 + 1 : 0;
+  int count = owned * kWindow;
+  if (nwin > 0 && (nwin - 1) % 8 == x) count -= nwin * kWindow - total;
+  return count;
+}
 
 __device__ __forceinline__ Dispenser make_dispenser(int32_t* counters, int total, int G) {
   Dispenser d;
   d.nd = (G % 8 == 0) ? 8 : 1;
-  d.x = (int)blockIdx.x % d.nd;
-  if (d.nd == 1) {
-    d.count = total;
-  } else {
-    const int nwin = (total + kWindow - 1) / kWindow;
-    const int owned = d.x < nwin ? (nwin - 1 - d.x) / 8 + 1 : 0;
-    d.count = owned * kWindow;
-    if (nwin > 0 && (nwin - 1) % 8 == d.x) d.count -= nwin * kWindow - total;
-  }
-  d.last = d.count + G / d.nd - 1;
-  d.ctr = counters + d.x * kCounterStride;
+  d.x = d.y = (int)blockIdx.x % d.nd;
+  d.back = 0;
+  d.base = counters;
+  d.total = total;
   return d;
 }
 
-// The tile of the dispenser's v-th grab (>= total once it is exhausted).
-__device__ __forceinline__ int dispensed_tile(const Dispenser& d, int v) {
-  if (d.nd == 1) return v;
-  return ((v / kWindow) * 8 + d.x) * kWindow + (v % kWindow);
+// The tile of dispenser y's index i.
+__device__ __forceinline__ int dispensed_tile(int y, int nd, int i) {
+  if (nd == 1) return i;
+  return ((i / kWindow) * 8 + y) * kWindow + (i % kWindow);
 }
 
-// One grab (call from a single thread).  The counter address is taken through
-// a VGPR so the atomic is a vector memory atomic.
-__device__ __forceinline__ int grab_tile(const Dispenser& d) {
-  int zero;
+__device__ __forceinline__ unsigned long long* dispenser_word(const Dispenser& d, int y) {
+  int zero;  // the address goes through a VGPR, so the atomics are vector memory atomics
   asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
-  return atomicAdd(d.ctr + zero, 1);
+  return reinterpret_cast<unsigned long long*>(d.base + y * kCounterStride + zero);
 }
 
-__device__ __forceinline__ void reset_dispenser(const Dispenser& d) {
+// One take from dispenser y, from the front or the back (single thread); the
+// old counter word comes back, take_tile decodes it.
+__device__ __forceinline__ unsigned long long grab_tile(const Dispenser& d) {
+  return atomicAdd(dispenser_word(d, d.y), d.back ? 1ull << 32 : 1ull);
+}
+
+// The tile of a take whose old counter word was `old`, or, once that dispenser
+// is exhausted, a tile from the back of the dispenser with the most left; -1
+// when every dispenser is exhausted (single thread).
+__device__ __forceinline__ int take_tile(Dispenser& d, unsigned long long old) {
+  {
+    const int f = (int)(uint32_t)old, b = (int)(uint32_t)(old >> 32);
+    const int count = dispenser_count(d.y, d.nd, d.total);
+    if (f >= 0 && b >= 0 && f + b < count) return dispensed_tile(d.y, d.nd, d.back ? count - 1 - b : f);
+  }
+  // a take that fails leaves its dispenser out of every later look, so at most
+  // nd looks find work; the bound also ends the search on counters that were
+  // not zero at the launch (negative halves count as empty)
+  for (int look = 0; look < 2 * 8; ++look) {
+    int best = -1, most = 0;
+    unsigned long long seen[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      seen[j] = j < d.nd ? __hip_atomic_load(dispenser_word(d, j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int f = (int)(uint32_t)seen[j], b = (int)(uint32_t)(seen[j] >> 32);
+      const int left = j < d.nd && f >= 0 && b >= 0 ? dispenser_count(j, d.nd, d.total) - f - b : 0;
+      if (left > most) {
+        most = left;
+        best = j;
+      }
+    }
+    if (best < 0) return -1;
+    d.y = best;
+    d.back = 1;
+    const unsigned long long w = grab_tile(d);
+    const int f = (int)(uint32_t)w, b = (int)(uint32_t)(w >> 32);
+    const int count = dispenser_count(best, d.nd, d.total);
+    if (f >= 0 && b >= 0 && f + b < count) return dispensed_tile(best, d.nd, count - 1 - b);
+  }
+  return -1;
+}
+
+// After a workgroup's last take (single thread): the last to retire zeroes the
+// counters for the next launch.
+__device__ __forceinline__ void retire(const Dispenser& d, int G) {
   int zero;
   asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
-  atomicExch(d.ctr + zero, 0);
+  if (atomicAdd(d.base + 2 + zero, 1) == G - 1) {
+    for (int j = 0; j < d.nd; ++j) atomicExch(dispenser_word(d, j), 0ull);
+    atomicExch(d.base + 2 + zero, 0);
+  }
 }
 
 // Workgroup id remap for the persistent tile loop: dispatch places block b on

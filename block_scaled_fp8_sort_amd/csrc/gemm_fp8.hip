@@ -426,31 +426,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p
   };
   // tiles come from the per-XCD dispensers when counters are given (the next
   // tile is grabbed at the start of the current one and handed to every wave
-  // through LDS after it), else in the fixed round-robin order
+  // through LDS after it; a workgroup whose dispenser is exhausted takes from
+  // another XCD's), else in the fixed round-robin order
   const bool dyn = p.sched != nullptr;
   const int tid = threadIdx.x;
   Dispenser d{};
-  int v = 0;
+  int td = 0;
   if (dyn) {
     d = make_dispenser(p.sched, total, G);
-    if (tid == 0) misc.next[0] = grab_tile(d);
+    if (tid == 0) misc.next[0] = take_tile(d, grab_tile(d));
     __syncthreads();
-    v = __builtin_amdgcn_readfirstlane(misc.next[0]);  // the same in every lane
+    td = __builtin_amdgcn_readfirstlane(misc.next[0]);  // the same in every lane
   }
   const int vb = xcd_virtual_block();
   for (int i = 1;; ++i) {
-    const int t = dyn ? dispensed_tile(d, v) : vb + (i - 1) * G;
-    if (t < 0 || t >= total) {  // (t < 0 only from counters that were not zeroed)
-      if (dyn && tid == 0 && v == d.last) reset_dispenser(d);
+    const int t = dyn ? td : vb + (i - 1) * G;
+    if (t < 0 || t >= total) {
+      if (dyn && tid == 0) retire(d, G);
       break;
     }
-    int v_next = 0;
+    unsigned long long v_next = 0;
     if (dyn && tid == 0) v_next = grab_tile(d);
     run(t);
     if (dyn) {
-      if (tid == 0) misc.next[i & 1] = v_next;
+      if (tid == 0) misc.next[i & 1] = take_tile(d, v_next);
       __syncthreads();
-      v = __builtin_amdgcn_readfirstlane(misc.next[i & 1]);
+      td = __builtin_amdgcn_readfirstlane(misc.next[i & 1]);
     }
   }
 }

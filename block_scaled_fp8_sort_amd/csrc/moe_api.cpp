@@ -197,6 +197,8 @@ moe_status validate_gemm(const moe_gemm_args* a) {
     default:
       return fail(MOE_ERR_UNSUPPORTED, "unknown epilogue %d", (int)a->epilogue);
   }
+  if ((uintptr_t)a->tile_counters % 8)
+    return fail(MOE_ERR_SHAPE, "tile_counters must be 8-byte aligned (64-bit counters)");
   // the epilogue's outputs must not alias what the launch reads
   const void* outs[] = {a->epilogue == MOE_EPI_STORE_F32 ? (const void*)a->c_f32 : nullptr,
                         a->epilogue == MOE_EPI_SWIGLU_QUANT ? (const void*)a->h_codes : nullptr,

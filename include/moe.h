@@ -288,7 +288,8 @@ typedef struct moe_gemm_args {
   const float* top_k_weights;
   const int32_t* slot_of_row;
   /* May be NULL (tiles are then taken in a fixed round-robin order).  Else
-   * device memory of MOE_TILE_COUNTERS_BYTES, all zero before the launch:
+   * device memory of MOE_TILE_COUNTERS_BYTES, 8-byte aligned (MOE_ERR_SHAPE
+   * otherwise), all zero before the launch:
    * workgroups then take tiles dynamically from atomic counters in it, and the
    * launch leaves it zero again.  Two launches in flight at once must not share
    * it. */

@@ -249,6 +249,9 @@ def test_gemm_refusals(lib):
     a.epilogue = 9
     assert lib.moe_grouped_gemm(ctypes.byref(a), None) == UNSUP
     a.epilogue = moe.EPI_STORE_F32
+    a.tile_counters = 4100  # the dispensers are 64-bit counters
+    assert lib.moe_grouped_gemm(ctypes.byref(a), None) == SHAPE
+    a.tile_counters = None
     a.max_rows = 0
     assert lib.moe_grouped_gemm(ctypes.byref(a), None) == OK  # nothing to do
     bad = _weights(H=100)
