@@ -131,21 +131,30 @@ __device__ __forceinline__ TileCoord locate_tile(int t, int E, int BM, int NT, c
 // first, so with round-robin assignment the short remainders fill the last
 // round instead of lengthening it; an expert whose only m-tile is short keeps
 // its place in phase 0, where its weight-streaming tiles interleave with the
-// MFMA-bound ones of the large experts.
+// MFMA-bound ones of the large experts.  With two_phase false every tile is
+// in phase 0: a remainder tile then runs beside its expert's other m-tiles and
+// reads their weight tile from L2 instead of streaming it again at the end
+// (launches with many rounds of tiles, where the last round is a small part).
 //   off[e]  expert offsets (E + 1)
 //   tp[e]   first phase-0 tile of expert e; tp[E] = phase-0 total
 //   cnt[e]  experts before e that have a phase-1 tile; expert e's phase-1 tiles
 //           are [cnt[e] NT, cnt[e] NT + NT), or with SPLIT = 2 the two 128-row
 //           halves of each n-tile, [2 cnt[e] NT, 2 cnt[e] NT + 2 NT)
 // Returns the total tile count.  All threads of the block must call it.
-__device__ __forceinline__ int has_short_tile(int rows) {
-  return rows > 256 && (rows % 256) > 0 && (rows % 256) <= 128;
+// Unpaired FP8 launches with fewer rounds of tiles than this (tiles per
+// workgroup, from the host's upper bound) run the remainder tiles last.
+constexpr long kTwoPhaseMaxRounds = 4;
+
+__device__ __forceinline__ int has_short_tile(int rows, bool two_phase) {
+  return two_phase && rows > 256 && (rows % 256) > 0 && (rows % 256) <= 128;
 }
-__device__ __forceinline__ int full_m_tiles(int rows) { return (rows + 255) / 256 - has_short_tile(rows); }
+__device__ __forceinline__ int full_m_tiles(int rows, bool two_phase) {
+  return (rows + 255) / 256 - has_short_tile(rows, two_phase);
+}
 
 template <int THREADS, int SPLIT = 1>
 __device__ __forceinline__ int build_tile_table2(const int32_t* offsets, int E, int NT, int* off, int* tp,
-                                                 uint16_t* cnt, int2* scan) {
+                                                 uint16_t* cnt, int2* scan, bool two_phase) {
   const int tid = threadIdx.x;
   for (int e = tid; e <= E; e += THREADS) off[e] = offsets[e];
   __syncthreads();
@@ -154,8 +163,8 @@ __device__ __forceinline__ int build_tile_table2(const int32_t* offsets, int E, 
   int2 mine = make_int2(0, 0);
   for (int e = e_lo; e < e_hi; ++e) {
     const int rows = off[e + 1] - off[e];
-    mine.x += full_m_tiles(rows) * NT;
-    mine.y += has_short_tile(rows);
+    mine.x += full_m_tiles(rows, two_phase) * NT;
+    mine.y += has_short_tile(rows, two_phase);
   }
   int run0, run1, tot0, tot1;
   block_scan2<THREADS>(mine.x, mine.y, reinterpret_cast<int*>(scan), run0, run1, tot0, tot1);
@@ -163,8 +172,8 @@ __device__ __forceinline__ int build_tile_table2(const int32_t* offsets, int E, 
     const int rows = off[e + 1] - off[e];
     tp[e] = run0;
     cnt[e] = (uint16_t)run1;
-    run0 += full_m_tiles(rows) * NT;
-    run1 += has_short_tile(rows);
+    run0 += full_m_tiles(rows, two_phase) * NT;
+    run1 += has_short_tile(rows, two_phase);
   }
   if (tid == 0) {
     tp[E] = tot0;
@@ -178,7 +187,7 @@ __device__ __forceinline__ int build_tile_table2(const int32_t* offsets, int E, 
 // the expert's rows, half), made wave-uniform.
 template <int SPLIT = 1>
 __device__ __forceinline__ TileCoord locate_tile2(int t, int E, int NT, const int* off, const int* tp,
-                                                  const uint16_t* cnt) {
+                                                  const uint16_t* cnt, bool two_phase) {
   const int total0 = __builtin_amdgcn_readfirstlane(tp[E]);
   TileCoord c;
   c.half = -1;
@@ -193,7 +202,7 @@ __device__ __forceinline__ TileCoord locate_tile2(int t, int E, int NT, const in
     c.m_end = __builtin_amdgcn_readfirstlane(off[c.e + 1]);
     const int loc = t - __builtin_amdgcn_readfirstlane(tp[c.e]);
     int m_idx, n_idx;
-    tile_position(loc, full_m_tiles(c.m_end - m_begin), NT, m_idx, n_idx);
+    tile_position(loc, full_m_tiles(c.m_end - m_begin, two_phase), NT, m_idx, n_idx);
     c.n_tile = n_idx;
     c.m0 = m_begin + m_idx * 256;
   } else {

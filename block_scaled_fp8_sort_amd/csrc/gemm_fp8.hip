@@ -403,10 +403,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p
   // unpaired: the short remainder tiles (at most 128 rows, run last) go as two
   // 128-row halves each
   constexpr int SPLIT = PAIRED ? 1 : 2;
-  const int total = build_tile_table2<kThreads, SPLIT>(p.offsets, E, NT, misc.off, misc.tp, misc.cnt, misc.scan);
+  const int total = build_tile_table2<kThreads, SPLIT>(p.offsets, E, NT, misc.off, misc.tp, misc.cnt, misc.scan,
+                                                                 p.two_phase != 0);
   const int G = gridDim.x;
   auto run = [&](int t) {
-    const TileCoord tc = locate_tile2<SPLIT>(t, E, NT, misc.off, misc.tp, misc.cnt);
+    const TileCoord tc = locate_tile2<SPLIT>(t, E, NT, misc.off, misc.tp, misc.cnt, p.two_phase != 0);
     const int left = tc.m_end - tc.m0;
     if constexpr (!PAIRED) {
       if (tc.half >= 0) {  // uniform
@@ -464,7 +465,13 @@ hipError_t launch_one(const GemmParams& p, int num_cus, hipStream_t stream) {
   long grid = bound < num_cus ? bound : num_cus;
   if (grid >= 8) grid = grid / 8 * 8;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  // the remainder tiles run last (in halves) on launches with few rounds; on
+  // the unpaired GEMM with many rounds they stay beside their expert's other
+  // m-tiles (DeepSeek-V3's down GEMM 3% faster); the gate_up GEMM gained
+  // nothing measurable either way
+  GemmParams q = p;
+  q.two_phase = PAIRED || bound < kTwoPhaseMaxRounds * grid ? 1 : 0;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, stream, q);
   return hipGetLastError();
 }
 

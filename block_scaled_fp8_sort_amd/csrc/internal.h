@@ -35,6 +35,11 @@ struct GemmParams {
   // (FP8) or [K/128][max_rows][4] bytes (MX), read instead of a_scales at the
   // gathered rows (tiled FP8 and MX kernels)
   const void* a_scales_sorted;
+  // tiled FP8 and MX kernels: nonzero = the short remainder tiles of large
+  // experts run last (phase 1 of the tile table), set by the launcher when a
+  // launch has few rounds of tiles; zero = they stay beside their expert's
+  // other m-tiles, whose weight tiles they then read from L2
+  int32_t two_phase;
 };
 
 enum Epilogue { kEpiStoreF32 = 0, kEpiSwiGLUQuant = 1, kEpiWeightedScatter = 2 };
