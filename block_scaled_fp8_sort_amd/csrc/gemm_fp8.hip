@@ -8,6 +8,11 @@
 // experts forward ("grouped_mm experts dispatch does not support
 // activation_scheme='static'", sections "What it means" and "Source"), with the
 // token-row gather (rows picked by perm // k) folded into the operand loads.
+// The same tiles also run the unquantized bf16 experts (the pages' grouped_mm
+// fallback, "DeepGEMM experts selected on a model spanning multiple CUDA
+// devices", the record's source): bf16 rows are tiled as rows of 2K bytes, and
+// only the K step (two bf16 MFMAs per 128-byte block, no scales) and the SwiGLU
+// store (h in bf16) differ.
 //
 // Design (gfx950, wave64):
 //  * MFMA A operand = weight rows (output features n), MFMA B operand = the
@@ -60,6 +65,7 @@ namespace moe {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i_t __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int BN = kTileN;
@@ -129,8 +135,8 @@ template <int BM>
 struct TileSrc {
   static constexpr int A_LOADS = BM / 64;  // 1 KB activation DMAs per wave per stage
   const uint8_t* w_tile;   // tiled weights of (expert, n-tile[, half]), K block 0 (uniform)
-  const uint8_t* a_codes;  // activation planes (uniform)
-  size_t a_plane;          // bytes of one 128-wide K plane of activation codes
+  const uint8_t* a_codes;  // activations (uniform)
+  size_t a_plane;          // byte step of A per K block: one K-block plane (FP8), 128 (bf16 rows)
   uint32_t a_off[A_LOADS]; // per-lane byte offset of the gathered row chunk
   const float* s_base;     // per-lane scale address of K block 0
   uint32_t s_stride;       // per-lane scale advance per K block, in floats
@@ -141,7 +147,7 @@ struct TileSrc {
 // stage, contiguous in the tiled layout), then BM / 64 activation gathers (wave
 // w gathers rows [w BM/8, (w+1) BM/8) of the tile), last the scales.  idx is a
 // compile-time constant after unrolling.
-template <int BM, int WR>
+template <int BM, int WR, bool BF>
 __device__ __forceinline__ void issue_part(StageBuf<BM, WR>* st, const TileSrc<BM>& src, int kb, int wave,
                                            int lane, int idx) {
   constexpr int W_LOADS = WR / 64, WB = WR * BK / kWaves;  // per wave: 1 KB DMAs, bytes
@@ -154,17 +160,24 @@ __device__ __forceinline__ void issue_part(StageBuf<BM, WR>* st, const TileSrc<B
     const int q = idx - W_LOADS;
     const uint8_t* plane = src.a_codes + (size_t)kb * src.a_plane;
     lds_dma16_s(plane, src.a_off[q], base + WR * BK + (w * (BM / 8) + 8 * q) * BK);
-  } else {
+  } else if constexpr (!BF) {
     lds_dma4(src.s_base + (size_t)kb * src.s_stride, base + (WR + BM) * BK + w * 256);
   }
 }
 
-template <int BM, int WR>
+// DMA instructions per wave per stage: weights, activations, and the scales
+// (none for bf16 operands)
+template <int BM, int WR, bool BF>
+constexpr int stage_loads() {
+  return WR / 64 + BM / 64 + (BF ? 0 : 1);
+}
+
+template <int BM, int WR, bool BF>
 __device__ __forceinline__ void issue_stage(StageBuf<BM, WR>* st, const TileSrc<BM>& src, int kb, int wave,
                                             int lane) {
-  constexpr int LOADS = WR / 64 + BM / 64 + 1;
+  constexpr int LOADS = stage_loads<BM, WR, BF>();
 #pragma unroll
-  for (int idx = 0; idx < LOADS; ++idx) issue_part<BM, WR>(st, src, kb, wave, lane, idx);
+  for (int idx = 0; idx < LOADS; ++idx) issue_part<BM, WR, BF>(st, src, kb, wave, lane, idx);
 }
 
 // One K block: wait for stage `cur`, then accumulate the block from `cur` while
@@ -179,7 +192,7 @@ __device__ __forceinline__ void k_step(const StageBuf<BM, WR>* cur, StageBuf<BM,
   constexpr int WM = BM / 4;
   constexpr int TS = WM / 16;
   constexpr int NW = WR / 32;                    // 16-row weight groups per wave
-  constexpr int LOADS = WR / 64 + BM / 64 + 1;  // DMA instructions per wave per stage
+  constexpr int LOADS = stage_loads<BM, WR, false>();
   const int wn = wave & 1, wt = wave >> 1;
   const int g = lane >> 4, l16 = lane & 15;
   wait_vmcnt<LOADS * (STAGES - 2)>();  // this wave's DMAs of stage kb have landed
@@ -215,7 +228,7 @@ __device__ __forceinline__ void k_step(const StageBuf<BM, WR>* cur, StageBuf<BM,
     // faster than eight; five and seven about the same as six, four slower)
 #pragma unroll
     for (int idx = 0; idx < LOADS; ++idx)
-      if (idx * (NW * 3 / 4) / LOADS == ni) issue_part<BM, WR>(nxt, src, kb_dma, wave, lane, idx);
+      if (idx * (NW * 3 / 4) / LOADS == ni) issue_part<BM, WR, false>(nxt, src, kb_dma, wave, lane, idx);
     v8i af_next = af;
     if (ni < NW - 1) af_next = lds_frag_w(cur->w, wn * NW + ni + 1, lane);
     const int pn = ni - 1;
@@ -232,12 +245,63 @@ __device__ __forceinline__ void k_step(const StageBuf<BM, WR>* cur, StageBuf<BM,
   }
 }
 
+// The same K step for bf16 operands.  A 128-byte K block holds 64 bf16, and
+// the fragments the FP8 step reads (chunks g and 4 + g of a row, for both
+// operands) are exactly the operands of two v_mfma_f32_16x16x32_bf16: chunk g
+// covers K elements [8 g, 8 g + 8) of the block's first 32, chunk 4 + g the same
+// of its last 32.  The products accumulate in the MFMA itself (no scales, no
+// promotion); the two MFMAs of one accumulator are split by the tile's other
+// token sub-tiles.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8 frag_lo(const v8i& v) {
+  return __builtin_bit_cast(bf16x8, v4i_t{v[0], v[1], v[2], v[3]});
+}
+__device__ __forceinline__ bf16x8 frag_hi(const v8i& v) {
+  return __builtin_bit_cast(bf16x8, v4i_t{v[4], v[5], v[6], v[7]});
+}
+
+template <int BM, int STAGES, int WR>
+__device__ __forceinline__ void k_step_bf16(const StageBuf<BM, WR>* cur, StageBuf<BM, WR>* nxt,
+                                            const TileSrc<BM>& src, int kb, int KB, int wave, int lane,
+                                            v4f (&acc)[WR / 32][BM / 64]) {
+  constexpr int WM = BM / 4;
+  constexpr int TS = WM / 16;
+  constexpr int NW = WR / 32;
+  constexpr int LOADS = stage_loads<BM, WR, true>();
+  const int wn = wave & 1, wt = wave >> 1;
+  const int g = lane >> 4, l16 = lane & 15;
+  wait_vmcnt<LOADS * (STAGES - 2)>();  // this wave's DMAs of stage kb have landed
+  raw_barrier();  // ... and every other wave's; all waves are done with block kb - 1
+  const int kb_dma = min(kb + STAGES - 1, KB - 1);
+  v8i bf[TS];
+#pragma unroll
+  for (int ti = 0; ti < TS; ++ti) bf[ti] = lds_frag_a(cur->a, wt * WM + ti * 16 + l16, g);
+  v8i af = lds_frag_w(cur->w, wn * NW, lane);
+#pragma unroll
+  for (int ni = 0; ni < NW; ++ni) {
+    // the next block's DMAs spread over the first six sub-tiles, as in k_step
+#pragma unroll
+    for (int idx = 0; idx < LOADS; ++idx)
+      if (idx * (NW * 3 / 4) / LOADS == ni) issue_part<BM, WR, true>(nxt, src, kb_dma, wave, lane, idx);
+    v8i af_next = af;
+    if (ni < NW - 1) af_next = lds_frag_w(cur->w, wn * NW + ni + 1, lane);
+#pragma unroll
+    for (int ti = 0; ti < TS; ++ti)
+      acc[ni][ti] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag_lo(af), frag_lo(bf[ti]), acc[ni][ti], 0, 0, 0);
+#pragma unroll
+    for (int ti = 0; ti < TS; ++ti)
+      acc[ni][ti] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag_hi(af), frag_hi(bf[ti]), acc[ni][ti], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    af = af_next;
+  }
+}
+
 // One tile of BM sorted rows [m0, min(m0 + BM, m_end)) of expert e against
 // n-tile n_tile (WR = 256), or against its 128 weight rows [128 half, 128 half +
 // 128) (WR = 128, unpaired only): the K loop through a ring of STAGES LDS
 // stages carved out of `area`, then the epilogue.  A half tile streams half the
 // weights per stage, so more stages fit and more bytes are in flight per CU.
-template <int BM, int EPI, bool PAIRED, int WR = BN>
+template <int BM, int EPI, bool PAIRED, bool BF, int WR = BN>
 __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Misc& misc, int e, int n_tile, int m0,
                                          int m_end, int half = 0) {
   constexpr int STAGES = stages_for<BM, WR>();
@@ -256,7 +320,8 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Mis
   const int wave = tid >> 6, lane = tid & 63;
   const int wn = wave & 1, wt = wave >> 1;
   const int g = lane >> 4, l16 = lane & 15;
-  const int N = p.N, KB = p.K / BK;
+  const int N = p.N;
+  const int KB = BF ? p.K * 2 / BK : p.K / BK;  // 128-byte K blocks
   const int I = N / 2;
   const int NB = N / 128;
   const int NT = PAIRED ? I / 128 : (N + BN - 1) / BN;
@@ -266,15 +331,18 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Mis
   TileSrc<BM> src;
   src.w_tile = p.b_codes + ((size_t)e * NT + n_tile) * (size_t)KB * (BN * BK) + (WR == 128 ? half * (128 * BK) : 0);
   src.a_codes = p.a_codes;
-  src.a_plane = (size_t)p.a_rows * BK;
+  // FP8 codes are K-block-major ([K/128][rows][128]); bf16 rows are row-major
+  // [rows][K] (the host keeps them under 4 GiB, so byte offsets fit 32 bits)
+  src.a_plane = BF ? (size_t)BK : (size_t)p.a_rows * BK;
+  const uint32_t a_pitch = BF ? (uint32_t)p.K * 2 : (uint32_t)BK;
 #pragma unroll
   for (int q = 0; q < TileSrc<BM>::A_LOADS; ++q) {
     const int tr = wave * (BM / 8) + 8 * q + (lane >> 3);
     const int r = min(m0 + tr, m_end - 1);
     const int arow = p.a_row_index ? p.a_row_index[r] / p.a_row_div : r;
-    src.a_off[q] = (uint32_t)arow * BK + (uint32_t)(((lane & 7) ^ swz(tr)) << 4);
+    src.a_off[q] = (uint32_t)arow * a_pitch + (uint32_t)(((lane & 7) ^ swz(tr)) << 4);
   }
-  {
+  if constexpr (!BF) {
     const int slot = 64 * wave + lane;
     if (slot == BM || slot == BM + 1) {
       int nb;
@@ -307,12 +375,16 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Mis
 
   __syncthreads();  // the previous tile's LDS readers are done
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) issue_stage<BM, WR>(&st[s], src, min(s, KB - 1), wave, lane);
+  for (int s = 0; s < STAGES - 1; ++s) issue_stage<BM, WR, BF>(&st[s], src, min(s, KB - 1), wave, lane);
   for (int kb = 0; kb < KB; kb += STAGES) {
 #pragma unroll
     for (int j = 0; j < STAGES; ++j)
-      if (kb + j < KB)
-        k_step<BM, PAIRED, STAGES, WR>(&st[j], &st[(j + STAGES - 1) % STAGES], src, kb + j, KB, wave, lane, acc);
+      if (kb + j < KB) {
+        if constexpr (BF)
+          k_step_bf16<BM, STAGES, WR>(&st[j], &st[(j + STAGES - 1) % STAGES], src, kb + j, KB, wave, lane, acc);
+        else
+          k_step<BM, PAIRED, STAGES, WR>(&st[j], &st[(j + STAGES - 1) % STAGES], src, kb + j, KB, wave, lane, acc);
+      }
   }
   wait_vmcnt<0>();  // the trailing repeat DMAs land before the stages are reused
 
@@ -335,6 +407,30 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Mis
         }
       }
     }
+  } else if constexpr (EPI == kEpiSwiGLUQuant && BF) {
+    static_assert(PAIRED, "SwiGLU needs the paired gate/up layout");
+    // h rounded once to bf16, row-major [rows][I] (the down GEMM's operand)
+    auto store_h = [&](auto lim) {
+      constexpr bool LIM = decltype(lim)::value;
+#pragma unroll
+      for (int ti = 0; ti < TS; ++ti) {
+        const int r = m0 + wt * WM + ti * 16 + l16;
+        if (r >= m_end) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int h = n_tile * 128 + 16 * (wn * 4 + q) + 4 * g;
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = swiglu<LIM>(acc[2 * q][ti][i], acc[2 * q + 1][ti][i], p.limit);
+          uint2 o;
+          o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+          o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+          *(uint2*)((uint16_t*)p.h_codes + (size_t)r * I + h) = o;
+        }
+      }
+    };
+    if (p.has_limit) store_h(std::true_type{});
+    else store_h(std::false_type{});
   } else if constexpr (EPI == kEpiSwiGLUQuant) {
     static_assert(PAIRED, "SwiGLU needs the paired gate/up layout");
     // h of pair q, sub-tile ti, element i, computed once into the gate's
@@ -393,11 +489,10 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Mis
 // Persistent kernel.  An expert's rows are cut into 256-row m-tiles; the last,
 // partial one runs at the smallest height of {64, 128, 256} that covers it, so
 // little MFMA work goes to padding rows while the number of tiles stays that of
-// 256-row tiles.  Tiles come from the two-phase table (longest first).
-template <int EPI, bool PAIRED>
-__global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t area[kStageArea];
-  __shared__ __attribute__((aligned(16))) Misc misc;
+// 256-row tiles.  Tiles come from the two-phase table (longest first).  The
+// body serves both operand types; each has a kernel of its own below.
+template <int EPI, bool PAIRED, bool BF>
+__device__ __forceinline__ void tiled_gemm(const GemmParams& p, uint8_t* area, Misc& misc) {
   const int E = p.E, N = p.N;
   const int NT = PAIRED ? (N / 2) / 128 : (N + BN - 1) / BN;
   // unpaired: the short remainder tiles (at most 128 rows, run last) go as two
@@ -412,18 +507,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p
     if constexpr (!PAIRED) {
       if (tc.half >= 0) {  // uniform
         if (left > 64)
-          run_tile<128, EPI, PAIRED, 128>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end, tc.half);
+          run_tile<128, EPI, PAIRED, BF, 128>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end, tc.half);
         else
-          run_tile<64, EPI, PAIRED, 128>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end, tc.half);
+          run_tile<64, EPI, PAIRED, BF, 128>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end, tc.half);
         return;
       }
     }
     if (left > 128)
-      run_tile<256, EPI, PAIRED>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end);
+      run_tile<256, EPI, PAIRED, BF>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end);
     else if (left > 64)
-      run_tile<128, EPI, PAIRED>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end);
+      run_tile<128, EPI, PAIRED, BF>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end);
     else
-      run_tile<64, EPI, PAIRED>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end);
+      run_tile<64, EPI, PAIRED, BF>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end);
   };
   // tiles come from the per-XCD dispensers when counters are given (the next
   // tile is grabbed at the start of the current one and handed to every wave
@@ -458,8 +553,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p
 }
 
 template <int EPI, bool PAIRED>
+__global__ __launch_bounds__(kThreads, 1) void gemm_fp8_b128_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t area[kStageArea];
+  __shared__ __attribute__((aligned(16))) Misc misc;
+  tiled_gemm<EPI, PAIRED, false>(p, area, misc);
+}
+
+// bf16 x bf16 with fp32 accumulation: the unquantized experts (weights tiled
+// the same way, two bytes per element, so a 128-byte K block is 64 of them).
+template <int EPI, bool PAIRED>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_tiled_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t area[kStageArea];
+  __shared__ __attribute__((aligned(16))) Misc misc;
+  tiled_gemm<EPI, PAIRED, true>(p, area, misc);
+}
+
+template <int EPI, bool PAIRED, bool BF>
 hipError_t launch_one(const GemmParams& p, int num_cus, hipStream_t stream) {
-  auto kern = gemm_fp8_b128_kernel<EPI, PAIRED>;
+  auto kern = BF ? gemm_bf16_tiled_kernel<EPI, PAIRED> : gemm_fp8_b128_kernel<EPI, PAIRED>;
   const int NT = PAIRED ? (p.N / 2) / 128 : (p.N + BN - 1) / BN;
   const long bound = ((long)(p.max_rows + kMaxBM - 1) / kMaxBM + p.E) * NT;
   long grid = bound < num_cus ? bound : num_cus;
@@ -478,10 +589,17 @@ hipError_t launch_one(const GemmParams& p, int num_cus, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_gemm_fp8_b128(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream) {
-  if (epi == kEpiSwiGLUQuant) return launch_one<kEpiSwiGLUQuant, true>(p, num_cus, stream);
-  if (epi == kEpiWeightedScatter) return launch_one<kEpiWeightedScatter, false>(p, num_cus, stream);
-  if (paired) return launch_one<kEpiStoreF32, true>(p, num_cus, stream);
-  return launch_one<kEpiStoreF32, false>(p, num_cus, stream);
+  if (epi == kEpiSwiGLUQuant) return launch_one<kEpiSwiGLUQuant, true, false>(p, num_cus, stream);
+  if (epi == kEpiWeightedScatter) return launch_one<kEpiWeightedScatter, false, false>(p, num_cus, stream);
+  if (paired) return launch_one<kEpiStoreF32, true, false>(p, num_cus, stream);
+  return launch_one<kEpiStoreF32, false, false>(p, num_cus, stream);
+}
+
+hipError_t launch_gemm_bf16(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream) {
+  if (epi == kEpiSwiGLUQuant) return launch_one<kEpiSwiGLUQuant, true, true>(p, num_cus, stream);
+  if (epi == kEpiWeightedScatter) return launch_one<kEpiWeightedScatter, false, true>(p, num_cus, stream);
+  if (paired) return launch_one<kEpiStoreF32, true, true>(p, num_cus, stream);
+  return launch_one<kEpiStoreF32, false, true>(p, num_cus, stream);
 }
 
 }  // namespace moe

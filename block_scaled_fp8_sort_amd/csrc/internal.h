@@ -109,8 +109,9 @@ hipError_t launch_gemm_fp8_b128(const GemmParams& p, int epi, bool paired, int n
 // registers, 16 rows per tile.
 hipError_t launch_gemm_fp8_skinny(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream);
 hipError_t launch_gemm_mx(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream);
-// The unquantized bf16 grouped GEMM (A and B bf16, B stored [E, N, K]; the
-// SwiGLU epilogue writes h as bf16 [max_rows, N/2] into h_codes).
+// The unquantized bf16 grouped GEMM on the same tiles (A bf16 rows [a_rows][K],
+// B bf16 tiled as in tile_layout.h with 2K-byte rows; the SwiGLU epilogue writes
+// h as bf16 [max_rows, N/2] into h_codes).
 hipError_t launch_gemm_bf16(const GemmParams& p, int epi, bool paired, int num_cus, hipStream_t stream);
 hipError_t launch_combine(const uint16_t* slot_out, const int32_t* ids, int32_t T, int32_t k, int32_t H, int32_t E,
                           int32_t expert_begin, uint16_t* out, hipStream_t stream);
@@ -122,10 +123,10 @@ hipError_t launch_tile_weight_fp8(const uint8_t* src, bool nn, bool paired, int3
 // the MX layout of tile_layout.h (codes and scales each get their own array).
 hipError_t launch_tile_weight_mx(const uint8_t* codes, const uint8_t* scales, bool paired, int32_t E, int32_t N,
                                  int32_t K, uint8_t* dst_codes, uint8_t* dst_scales, hipStream_t stream);
-// bf16 weights [E, N, K] (N % 16 == 0, K % 64 == 0) into the operand order of
-// the bf16 grouped GEMM (see gemm_bf16.hip).
-hipError_t launch_tile_weight_bf16(const uint16_t* src, bool nn, int32_t E, int32_t N, int32_t K, uint16_t* dst,
-                                   hipStream_t stream);
+// bf16 weights [E, N, K] (nt) or [E, K, N] (nn) into the layout of
+// tile_layout.h, each row taken as 2K bytes (K % 64 == 0).
+hipError_t launch_tile_weight_bf16(const uint16_t* src, bool nn, bool paired, int32_t E, int32_t N, int32_t K,
+                                   uint16_t* dst, hipStream_t stream);
 hipError_t launch_transpose_u8(const uint8_t* in, uint8_t* out, int32_t batch, int32_t rows, int32_t cols,
                                hipStream_t stream);
 hipError_t launch_transpose_f32(const float* in, float* out, int32_t batch, int32_t rows, int32_t cols,

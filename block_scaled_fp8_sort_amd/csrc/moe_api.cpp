@@ -625,7 +625,8 @@ size_t moe_prepared_weights_size(moe_format fmt, int32_t E, int32_t H, int32_t I
   if (!valid_fmt(fmt) || E < 1 || H <= 0 || I <= 0 || H % 128 || I % 128) return 0;
   const size_t A = 256;
   const size_t e = (size_t)E, h = (size_t)H, i = (size_t)I;
-  if (fmt == MOE_FMT_BF16) return align_up(e * 2 * i * h * 2, A) + align_up(e * h * i * 2, A);
+  if (fmt == MOE_FMT_BF16)  // down weight rows padded to whole 256-row tiles
+    return align_up(e * 2 * i * h * 2, A) + align_up(e * ((h + 255) / 256 * 256) * i * 2, A);
   if (fmt == MOE_FMT_FP8_B128) {
     const size_t nt2 = (h + 255) / 256;
     return align_up(e * 2 * i * h, A) + align_up(4 * e * (2 * i / 128) * (h / 128), A) +
@@ -668,14 +669,15 @@ moe_status moe_prepare_weights(moe_format fmt, moe_layout layout, int32_t E, int
   const size_t A = 256;
   const size_t e = E, h = H, i = I;
   if (bf) {
-    // bf16 weights in the bf16 GEMM's operand order
+    // bf16 weights tiled like the FP8 codes, two bytes per element
     uint8_t* q13 = (uint8_t*)prepared;
     uint8_t* q2 = q13 + align_up(e * 2 * i * h * 2, A);
     hipError_t he;
     const bool nn = layout == MOE_LAYOUT_NN;
-    if ((he = moe::launch_tile_weight_bf16((const uint16_t*)gate_up, nn, E, 2 * I, H, (uint16_t*)q13, stream)) !=
-            hipSuccess ||
-        (he = moe::launch_tile_weight_bf16((const uint16_t*)down, nn, E, H, I, (uint16_t*)q2, stream)) != hipSuccess)
+    if ((he = moe::launch_tile_weight_bf16((const uint16_t*)gate_up, nn, true, E, 2 * I, H, (uint16_t*)q13,
+                                           stream)) != hipSuccess ||
+        (he = moe::launch_tile_weight_bf16((const uint16_t*)down, nn, false, E, H, I, (uint16_t*)q2, stream)) !=
+            hipSuccess)
       return hip_status(he, "weight tiling");
     moe_weights w{};
     w.fmt = fmt;

@@ -35,12 +35,13 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
 // One thread per 16-byte piece of the tiled destination [E][NT][KB][32 KB]:
 // find the tile row tr and logical chunk c the piece holds (the MFMA operand
 // order of tile_layout.h), copy the source row's 16 K-bytes there, or zeros for
-// a padding row.
-template <bool PAIRED>
+// a padding row.  ESZ is the element size: 1 for FP8 codes, 2 for bf16, whose
+// rows are tiled as rows of 2K bytes (a 128-byte K block is 64 elements).
+template <bool PAIRED, int ESZ>
 __global__ __launch_bounds__(256) void tile_weight_kernel(const uint8_t* __restrict__ src, int nn, int32_t N,
                                                           int32_t K, int32_t NT, int64_t n_chunks,
                                                           uint8_t* __restrict__ dst) {
-  const int KB = K / kBlockK;
+  const int KB = K * ESZ / kBlockK;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < n_chunks; d += stride) {
     const int piece = (int)(d & 2047);  // 16-byte piece inside the 32 KB block
@@ -55,13 +56,20 @@ __global__ __launch_bounds__(256) void tile_weight_kernel(const uint8_t* __restr
     const int row = tile_src_row<PAIRED>(nt, tr, N);
     uint4 v = make_uint4(0, 0, 0, 0);
     if (row >= 0) {
-      const int64_t k0 = (int64_t)kb * kBlockK + c * 16;
+      const int64_t k0 = (int64_t)kb * kBlockK + c * 16;  // byte offset in the row
       if (!nn) {
-        v = *(const uint4*)(src + (e * N + row) * (int64_t)K + k0);
-      } else {  // [E][K][N]: gather 16 bytes down a column
+        v = *(const uint4*)(src + (e * N + row) * (int64_t)K * ESZ + k0);
+      } else if constexpr (ESZ == 1) {  // [E][K][N]: gather 16 bytes down a column
         uint8_t b[16];
         for (int j = 0; j < 16; ++j) b[j] = src[(e * K + k0 + j) * (int64_t)N + row];
         v = *(const uint4*)b;
+      } else {  // bf16 [E][K][N]: 8 elements down a column
+        const uint16_t* s16 = reinterpret_cast<const uint16_t*>(src);
+        uint32_t w[4];
+        for (int j = 0; j < 4; ++j)
+          w[j] = (uint32_t)s16[(e * K + k0 / 2 + 2 * j) * (int64_t)N + row] |
+                 ((uint32_t)s16[(e * K + k0 / 2 + 2 * j + 1) * (int64_t)N + row] << 16);
+        v = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
     *(uint4*)(dst + d * 16) = v;
@@ -127,20 +135,36 @@ hipError_t launch_t(const T* in, T* out, int32_t batch, int32_t rows, int32_t co
 
 }  // namespace
 
-hipError_t launch_tile_weight_fp8(const uint8_t* src, bool nn, bool paired, int32_t E, int32_t N, int32_t K,
-                                  uint8_t* dst, hipStream_t stream) {
+namespace {
+
+template <int ESZ>
+hipError_t launch_tile_weight(const uint8_t* src, bool nn, bool paired, int32_t E, int32_t N, int32_t K, uint8_t* dst,
+                              hipStream_t stream) {
   const int32_t NT = paired ? (N / 2) / 128 : (N + kTileN - 1) / kTileN;
-  const int64_t n_chunks = (int64_t)E * NT * (K / kBlockK) * kTileN * 8;
+  const int64_t n_chunks = (int64_t)E * NT * (K * ESZ / kBlockK) * kTileN * 8;
   if (n_chunks == 0) return hipSuccess;
   const int64_t want = (n_chunks + 255) / 256;
   const int blocks = (int)(want < 65536 ? want : 65536);
   if (paired)
-    hipLaunchKernelGGL(tile_weight_kernel<true>, dim3(blocks), dim3(256), 0, stream, src, nn ? 1 : 0, N, K, NT,
-                       n_chunks, dst);
+    hipLaunchKernelGGL((tile_weight_kernel<true, ESZ>), dim3(blocks), dim3(256), 0, stream, src, nn ? 1 : 0, N, K,
+                       NT, n_chunks, dst);
   else
-    hipLaunchKernelGGL(tile_weight_kernel<false>, dim3(blocks), dim3(256), 0, stream, src, nn ? 1 : 0, N, K, NT,
-                       n_chunks, dst);
+    hipLaunchKernelGGL((tile_weight_kernel<false, ESZ>), dim3(blocks), dim3(256), 0, stream, src, nn ? 1 : 0, N, K,
+                       NT, n_chunks, dst);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_tile_weight_fp8(const uint8_t* src, bool nn, bool paired, int32_t E, int32_t N, int32_t K,
+                                  uint8_t* dst, hipStream_t stream) {
+  return launch_tile_weight<1>(src, nn, paired, E, N, K, dst, stream);
+}
+
+hipError_t launch_tile_weight_bf16(const uint16_t* src, bool nn, bool paired, int32_t E, int32_t N, int32_t K,
+                                   uint16_t* dst, hipStream_t stream) {
+  return launch_tile_weight<2>(reinterpret_cast<const uint8_t*>(src), nn, paired, E, N, K,
+                               reinterpret_cast<uint8_t*>(dst), stream);
 }
 
 hipError_t launch_tile_weight_mx(const uint8_t* codes, const uint8_t* scales, bool paired, int32_t E, int32_t N,
@@ -165,49 +189,6 @@ hipError_t launch_tile_weight_mx(const uint8_t* codes, const uint8_t* scales, bo
   else
     hipLaunchKernelGGL(tile_scale_mx_kernel<false>, dim3(blocks), dim3(256), 0, stream, scales, N, K, NT, n_entries,
                        (uint32_t*)dst_scales);
-  return hipGetLastError();
-}
-
-namespace {
-
-// bf16 weights [E, N, K] (nt) or [E, K, N] (nn) -> MFMA operand order for the
-// bf16 grouped GEMM: for each 16-row group and 64-element K stage, a 2 KB block
-// holding the two 32-element sub-steps, each as the 64 lanes' 16-byte fragments
-// in lane order (lane = 16 * (k % 32 / 8) + row % 16), so one wave-wide load
-// reads 1 KB contiguous.  One thread fills one 16-byte chunk (8 consecutive k of
-// one row n): one load from an nt row, eight 2-byte loads down an nn column.
-__global__ __launch_bounds__(256) void tile_weight_bf16_kernel(const uint16_t* __restrict__ src, int nn, int32_t N,
-                                                               int32_t K, int64_t chunks, uint4* __restrict__ dst) {
-  const int64_t kc = K / 8;  // chunks per row
-  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks; c += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t row = c / kc;  // e * N + n
-    const int k0 = (int)(c - row * kc) * 8;
-    const int64_t e = row / N;
-    const int n = (int)(row - e * N);
-    const int stage = k0 / 64, ks = (k0 % 64) / 32, g = (k0 % 32) / 8;
-    const int64_t block = (e * (N / 16) + n / 16) * (K / 64) + stage;
-    uint4 v;
-    if (!nn) {
-      v = reinterpret_cast<const uint4*>(src)[c];
-    } else {
-      const uint16_t* col = src + (e * K + k0) * (int64_t)N + n;
-      uint32_t w[4];
-      for (int j = 0; j < 4; ++j) w[j] = (uint32_t)col[(2 * j) * (int64_t)N] | ((uint32_t)col[(2 * j + 1) * (int64_t)N] << 16);
-      v = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-    dst[block * 128 + ks * 64 + g * 16 + n % 16] = v;
-  }
-}
-
-}  // namespace
-
-hipError_t launch_tile_weight_bf16(const uint16_t* src, bool nn, int32_t E, int32_t N, int32_t K, uint16_t* dst,
-                                   hipStream_t stream) {
-  const int64_t chunks = (int64_t)E * N * (K / 8);
-  int64_t blocks = (chunks + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(tile_weight_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src, nn ? 1 : 0, N, K,
-                     chunks, (uint4*)dst);
   return hipGetLastError();
 }
 

@@ -401,9 +401,10 @@ def test_workspace_sized_for_next_power_of_two():
 
 
 def test_bf16_format_on_the_host(lib):
-    # prepared size: the two bf16 weights in operand order, each rounded up to 256 bytes
+    # prepared size: the two bf16 weights tiled, each rounded up to 256 bytes; the
+    # down weight's rows (H) padded to whole 256-row tiles
     assert lib.moe_prepared_weights_size(2, 4, 256, 128) == 4 * 256 * 256 * 2 + 4 * 256 * 128 * 2
-    assert lib.moe_prepared_weights_size(2, 3, 384, 128) == 3 * 256 * 384 * 2 + 3 * 384 * 128 * 2
+    assert lib.moe_prepared_weights_size(2, 3, 384, 128) == 3 * 256 * 384 * 2 + 3 * 512 * 128 * 2
     desc = moe.MoeWeights()
     p = ctypes.c_void_p(4096)
     # the nn layout is refused for MX only; bf16 scale pointers may be NULL (with
