@@ -48,7 +48,7 @@ GATE_UP_KERNELS = {
     "fp8_tiled": ("gemm_fp8_b128_kernel", [_CSRC + "gemm_fp8.hip"] + _COMMON),
     "fp8_skinny": ("gemm_fp8_skinny_kernel", [_CSRC + "gemm_fp8_skinny.hip"] + _COMMON),
     "mx": ("gemm_mx_kernel", [_CSRC + "gemm_mx.hip"] + _COMMON),
-    "bf16": ("gemm_bf16_kernel", [_CSRC + "gemm_bf16.hip"] + _COMMON),
+    "bf16": ("gemm_bf16_tiled_kernel", [_CSRC + "gemm_fp8.hip"] + _COMMON),
 }
 
 
