@@ -45,10 +45,10 @@ SKINNY_ROWS_PER_EXPERT = 8
 _CSRC = "block_scaled_fp8_sort_amd/csrc/"
 _COMMON = [_CSRC + "gemm_common.h", _CSRC + "tile_layout.h", _CSRC + "device_common.h"]
 GATE_UP_KERNELS = {
-    "fp8_tiled": ("gemm_fp8_b128_kernel", [_CSRC + "gemm_fp8.hip"] + _COMMON),
+    "fp8_tiled": ("gemm_fp8_b128_kernel", [_CSRC + "gemm_tiled.hip"] + _COMMON),
     "fp8_skinny": ("gemm_fp8_skinny_kernel", [_CSRC + "gemm_fp8_skinny.hip"] + _COMMON),
     "mx": ("gemm_mx_kernel", [_CSRC + "gemm_mx.hip"] + _COMMON),
-    "bf16": ("gemm_bf16_tiled_kernel", [_CSRC + "gemm_fp8.hip"] + _COMMON),
+    "bf16": ("gemm_bf16_tiled_kernel", [_CSRC + "gemm_tiled.hip"] + _COMMON),
 }
 
 

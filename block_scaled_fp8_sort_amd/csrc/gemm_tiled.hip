@@ -1,5 +1,6 @@
-// Grouped GEMM over expert-sorted rows, FP8 e4m3 x e4m3 with fp32 block scales
-// (1x128 on the activations, 128x128 on the weights), for gfx950.
+// Tiled grouped GEMM over expert-sorted rows for gfx950: FP8 e4m3 x e4m3 with
+// fp32 block scales (1x128 on the activations, 128x128 on the weights), and on
+// the same tiles bf16 x bf16.
 //
 // What it computes: for expert e and sorted row r of its range,
 // C[r, n] = sum_i A[a_row(r), i] * B[e, n, i] with dequantized operands (code
