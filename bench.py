@@ -85,6 +85,9 @@ def parse():
                          "(workloads with softmax routing only)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="time a plain device-to-device copy of this many bytes (counter calibration)")
+    ap.add_argument("--mfma-probe", type=int, default=0, metavar="ITERS",
+                    help="measure the matrix cores' issue rate for each MFMA form the GEMMs use (register "
+                         "operands, ITERS rounds of 16 MFMAs per wave) and print one JSON line")
     return ap.parse_args()
 
 
@@ -105,6 +108,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.copy_bytes:
         return copy_calibration(args, dev)
+    if args.mfma_probe:
+        return mfma_probe(args, dev)
     if args.only:
         import block_scaled_fp8_sort_amd as moe
         import workloads as W
@@ -468,6 +473,28 @@ def copy_calibration(args, dev):
     ms = e0.elapsed_time(e1) / args.steps
     print(json.dumps({"mode": "copy", "bytes": n, "ms_per_copy": round(ms, 4),
                       "GB/s (read+write)": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
+def mfma_probe(args, dev):
+    """The MFMA issue rate of each form the grouped GEMMs use (moe_probe_mfma_rate),
+    against the published dense peak of its operand type and against that peak
+    scaled to the shader clock the probe ran at (published peaks assume 2.4 GHz)."""
+    import block_scaled_fp8_sort_amd as moe
+
+    peaks = {0: PEAK_FP8_TFLOPS, 1: PEAK_FP8_TFLOPS, 2: PEAK_MXFP4_TFLOPS, 3: PEAK_BF16_TFLOPS, 4: PEAK_FP8_TFLOPS}
+    peak_names = {0: "fp8", 1: "fp8 (also reported against mxfp4)", 2: "mxfp4", 3: "bf16", 4: "fp8"}
+    rows = {}
+    for kind in sorted(moe.PROBE_KINDS):
+        tf, ghz = moe.probe_mfma_rate(kind, args.mfma_probe, dev)
+        peak = peaks[kind]
+        row = {"form": moe.PROBE_KINDS[kind], "tflops": round(tf, 1), "sclk_ghz": round(ghz, 3),
+               "peak": peak, "peak_of": peak_names[kind], "frac_of_peak": round(tf / peak, 4),
+               "frac_of_peak_at_this_clock": round(tf / (peak * ghz / 2.4), 4) if ghz > 0 else None}
+        if kind == 1:
+            row["frac_of_mxfp4_peak"] = round(tf / PEAK_MXFP4_TFLOPS, 4)
+        rows[str(kind)] = row
+        log(f"[bench] mfma probe kind {kind} ({moe.PROBE_KINDS[kind]}): {tf:.0f} TFLOP/s at {ghz:.2f} GHz")
+    print(json.dumps({"mode": "mfma probe", "iters_per_wave": args.mfma_probe, "kinds": rows}), flush=True)
 
 
 def cpu_baseline(wl, inp, seconds):

@@ -25,7 +25,7 @@ __all__ = [
     "prepare_weights",
     "grouped_gemm", "experts_forward", "experts_forward_from_logits", "experts_forward_noalloc",
     "forward_workspace_bytes", "NOALLOC_SCRATCH_BYTES", "Weights",
-    "TILE_COUNTERS_INTS",
+    "TILE_COUNTERS_INTS", "probe_mfma_rate", "PROBE_KINDS",
 ]
 
 FMT_FP8_B128 = 0
@@ -126,6 +126,9 @@ def load_library():
     lib.moe_experts_forward_noalloc.restype = ctypes.c_int
     lib.moe_experts_forward_noalloc.argtypes = [ctypes.POINTER(MoeWeights), _P, _P, _P, _I32, _I32,
                                                 ctypes.POINTER(MoeOptions), _P, _P]
+    lib.moe_probe_mfma_rate.restype = ctypes.c_int
+    lib.moe_probe_mfma_rate.argtypes = [_I32, _I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                        _P]
     lib.moe_experts_forward_from_logits.restype = ctypes.c_int
     lib.moe_experts_forward_from_logits.argtypes = [ctypes.POINTER(MoeWeights), _P, _P, _I32, _I32, _I32, _I32,
                                                     ctypes.POINTER(MoeOptions), _P, _P, _P, _P, _SZ, _P]
@@ -622,3 +625,24 @@ def experts_forward_noalloc(hidden_states: torch.Tensor, top_k_index: torch.Tens
     _check(lib.moe_experts_forward_noalloc(ctypes.byref(weights.desc), _ptr(hidden_states), _ptr(top_k_index),
                                            _ptr(top_k_weights), T, k, ctypes.byref(opt), _ptr(out), _stream(dev)))
     return out
+
+
+# The MFMA forms moe_probe_mfma_rate measures, by kind.
+PROBE_KINDS = {
+    0: "e4m3 x e4m3 16x16x128",
+    1: "e2m1 x e4m3 16x16x128, UE8M0 scales (the MX GEMM's form)",
+    2: "e2m1 x e2m1 16x16x128, UE8M0 scales",
+    3: "bf16 16x16x32",
+    4: "e4m3 x e4m3 16x16x128 + fp32 promotion (the FP8 GEMM's form)",
+}
+
+
+def probe_mfma_rate(kind: int, iters: int = 20000, device: Optional[torch.device] = None):
+    """The matrix cores' issue rate for one MFMA form (moe_probe_mfma_rate): random
+    operands in registers, 8 waves on every CU.  Returns (TFLOP/s, mean shader
+    clock in GHz).  A measurement utility; blocks until the probe has run."""
+    lib = load_library()
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    tf, ghz = ctypes.c_double(), ctypes.c_double()
+    _check(lib.moe_probe_mfma_rate(int(kind), int(iters), ctypes.byref(tf), ctypes.byref(ghz), _stream(dev)))
+    return tf.value, ghz.value

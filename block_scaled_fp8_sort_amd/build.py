@@ -28,7 +28,7 @@ FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
-SOURCES = ["route_sort.hip", "quant_act.hip", "gemm_tiled.hip", "gemm_fp8_skinny.hip", "gemm_mx.hip", "combine.hip",
+SOURCES = ["route_sort.hip", "quant_act.hip", "gemm_tiled.hip", "gemm_fp8_skinny.hip", "gemm_mx.hip", "combine.hip", "probe.hip",
            "prepare.hip", "moe_api.cpp"]
 
 

@@ -138,6 +138,13 @@ hipError_t launch_tile_weight_bf16(const uint16_t* src, bool nn, bool paired, in
                                    uint16_t* dst, hipStream_t stream);
 hipError_t launch_transpose_u8(const uint8_t* in, uint8_t* out, int32_t batch, int32_t rows, int32_t cols,
                                hipStream_t stream);
+// The matrix-core issue-rate probe (probe.hip): one workgroup of
+// probe_threads() threads per CU; sink holds grid * probe_threads() floats,
+// clk 2 * grid counters (shader-clock and 100 MHz ticks per workgroup).
+int probe_threads();
+int64_t probe_flops_per_mfma(int kind);
+hipError_t launch_mfma_probe(int kind, int iters, int grid, float* sink, unsigned long long* clk,
+                             hipStream_t stream);
 hipError_t launch_transpose_f32(const float* in, float* out, int32_t batch, int32_t rows, int32_t cols,
                                 hipStream_t stream);
 

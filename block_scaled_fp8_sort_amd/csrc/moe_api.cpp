@@ -20,6 +20,7 @@
 #include <mutex>
 #include <utility>
 #include <string>
+#include <vector>
 
 #include "internal.h"
 #include "moe.h"
@@ -818,6 +819,49 @@ moe_status moe_experts_forward_noalloc(const moe_weights* w, const uint16_t* hid
   if ((st = scratch_address(dev, &ws)) != MOE_OK) return st;
   return forward_impl(w, hidden_states, nullptr, top_k_index, top_k_weights, T, k, opt, out, ws,
                       MOE_NOALLOC_SCRATCH_BYTES, stream, true);
+}
+
+moe_status moe_probe_mfma_rate(int32_t kind, int32_t iters, double* tflops, double* sclk_ghz, hipStream_t stream) {
+  if (!tflops || !sclk_ghz) return fail(MOE_ERR_NULL, "tflops / sclk_ghz are NULL");
+  if (kind < 0 || kind > 4) return fail(MOE_ERR_UNSUPPORTED, "probe kind %d outside [0, 4]", (int)kind);
+  if (iters < 1 || iters > (1 << 24)) return fail(MOE_ERR_SHAPE, "iters=%d outside [1, 2^24]", (int)iters);
+  int dev, cus;
+  moe_status st = check_device(stream, &dev, &cus);
+  if (st != MOE_OK) return st;
+  const int grid = cus, threads = moe::probe_threads();
+  float* sink = nullptr;
+  unsigned long long* clk = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  std::vector<unsigned long long> h_clk(2 * (size_t)grid);
+  float ms = 0.0f;
+  hipError_t he = hipMalloc(&sink, sizeof(float) * (size_t)grid * threads);
+  if (he == hipSuccess) he = hipMalloc(&clk, sizeof(unsigned long long) * 2 * (size_t)grid);
+  if (he == hipSuccess) he = hipEventCreate(&e0);
+  if (he == hipSuccess) he = hipEventCreate(&e1);
+  // a short warm-up launch, then the timed one
+  if (he == hipSuccess) he = moe::launch_mfma_probe(kind, iters / 8 + 1, grid, sink, clk, stream);
+  if (he == hipSuccess) he = hipEventRecord(e0, stream);
+  if (he == hipSuccess) he = moe::launch_mfma_probe(kind, iters, grid, sink, clk, stream);
+  if (he == hipSuccess) he = hipEventRecord(e1, stream);
+  if (he == hipSuccess) he = hipEventSynchronize(e1);
+  if (he == hipSuccess) he = hipEventElapsedTime(&ms, e0, e1);
+  if (he == hipSuccess)
+    he = hipMemcpy(h_clk.data(), clk, sizeof(unsigned long long) * h_clk.size(), hipMemcpyDeviceToHost);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (sink) (void)hipFree(sink);
+  if (clk) (void)hipFree(clk);
+  if (he != hipSuccess) return hip_status(he, "mfma probe");
+  if (!(ms > 0.0f)) return fail(MOE_ERR_HIP, "mfma probe: no elapsed time");
+  double shader = 0.0, real = 0.0;
+  for (int b = 0; b < grid; ++b) {
+    shader += (double)h_clk[2 * b];
+    real += (double)h_clk[2 * b + 1];
+  }
+  const double flops = (double)grid * (threads / 64) * (double)iters * 16.0 * (double)moe::probe_flops_per_mfma(kind);
+  *tflops = flops / ((double)ms * 1e-3) / 1e12;
+  *sclk_ghz = real > 0.0 ? shader / real * 0.1 : 0.0;  // the real-time counter ticks at 100 MHz
+  return ok();
 }
 
 moe_status moe_experts_forward_from_logits(const moe_weights* w, const uint16_t* hidden_states,

@@ -1,0 +1,125 @@
+// Matrix-core issue-rate probe for gfx950 (a measurement utility, not a step
+// of the forward).
+//
+// The grouped GEMMs are priced against the MFMA rate of their own operand
+// types.  The published peaks give FP8 and FP4 rates for matching operands,
+// but the MX experts multiply e2m1 weights by e4m3 activations, and the FP8
+// experts add an fp32 promotion per 128-wide K block; this kernel measures
+// the rate each form the GEMMs use actually issues at, with random operands
+// held in registers (no memory traffic), eight waves on every CU, and reads
+// the shader clock it ran at.
+#include "device_common.h"
+#include "internal.h"
+
+namespace moe {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kProbeWaves = 8;
+
+// 32-bit mixing function (the xorshift-multiply finalizer of a counter hash):
+// operand bits that toggle like real data
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352dU;
+  x ^= x >> 15;
+  x *= 0x846ca68bU;
+  x ^= x >> 16;
+  return x;
+}
+
+// KIND: 0 e4m3 x e4m3 accumulating in the MFMA, 1 e2m1 x e4m3 and 2 e2m1 x e2m1
+// with per-lane UE8M0 scales (the MX GEMM's form), 3 bf16 16x16x32, 4 e4m3 x
+// e4m3 with a fresh accumulator and the fp32 promotion acc += P * s (the FP8
+// GEMM's form).  Every wave runs iters rounds of 16 independent MFMAs, the
+// operands rotating each round.
+template <int KIND>
+__global__ __launch_bounds__(kProbeWaves * 64, 1) void mfma_rate_kernel(int iters, float* sink,
+                                                                         unsigned long long* clk) {
+  const int tid = threadIdx.x;
+  const uint32_t seed = (uint32_t)(blockIdx.x * blockDim.x + tid) * 128u;
+  // e4m3 bytes with the exponent's top bit cleared (no NaN code), bf16 values
+  // likewise finite; e2m1 has no special codes
+  const uint32_t mask = KIND == 3 ? 0xBFFFBFFFu : (KIND == 0 || KIND == 4) ? 0xBFBFBFBFu : 0xFFFFFFFFu;
+  const uint32_t mask_b = KIND == 1 ? 0xBFBFBFBFu : mask;
+  v8i A[4], B[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      A[j][i] = (int)(mix32(seed + j * 16 + i) & mask);
+      B[j][i] = (int)(mix32(seed + 64 + j * 16 + i) & mask_b);
+    }
+  int sc;  // UE8M0 1.0 in a VGPR, as the MX GEMM passes its per-lane scales
+  asm volatile("v_mov_b32 %0, 127" : "=v"(sc));
+  const float s = 1e-3f * (float)(tid + 1);
+  v4f acc[4][4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[n][t] = v4f{0.f, 0.f, 0.f, 0.f};
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+    const int o = it & 3;
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const v8i a = A[(n + o) & 3], b = B[(t + o) & 3];
+        if constexpr (KIND == 0) {
+          acc[n][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[n][t], 0, 0, 0, 0, 0, 0);
+        } else if constexpr (KIND == 1) {
+          acc[n][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(v8i{a[0], a[1], a[2], a[3], 0, 0, 0, 0}, b,
+                                                                       acc[n][t], 4, 0, 0, sc, 0, sc);
+        } else if constexpr (KIND == 2) {
+          acc[n][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              v8i{a[0], a[1], a[2], a[3], 0, 0, 0, 0}, v8i{b[0], b[1], b[2], b[3], 0, 0, 0, 0}, acc[n][t], 4, 4, 0, sc,
+              0, sc);
+        } else if constexpr (KIND == 3) {
+          acc[n][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v4i{a[0], a[1], a[2], a[3]}),
+                                                              __builtin_bit_cast(bf16x8, v4i{b[0], b[1], b[2], b[3]}),
+                                                              acc[n][t], 0, 0, 0);
+        } else {
+          const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+          acc[n][t] += p * s;
+        }
+      }
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  float sum = 0.f;
+#pragma unroll
+  for (int n = 0; n < 4; ++n)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sum += acc[n][t][0] + acc[n][t][1] + acc[n][t][2] + acc[n][t][3];
+  sink[blockIdx.x * blockDim.x + tid] = sum;
+  if (tid == 0) {
+    clk[2 * blockIdx.x] = t1 - t0;
+    clk[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
+}  // namespace
+
+int probe_threads() { return kProbeWaves * 64; }
+
+int64_t probe_flops_per_mfma(int kind) { return kind == 3 ? 16 * 16 * 32 * 2 : 16 * 16 * 128 * 2; }
+
+hipError_t launch_mfma_probe(int kind, int iters, int grid, float* sink, unsigned long long* clk,
+                             hipStream_t stream) {
+  const dim3 g((unsigned)grid), b(kProbeWaves * 64);
+  switch (kind) {
+    case 0: hipLaunchKernelGGL(mfma_rate_kernel<0>, g, b, 0, stream, iters, sink, clk); break;
+    case 1: hipLaunchKernelGGL(mfma_rate_kernel<1>, g, b, 0, stream, iters, sink, clk); break;
+    case 2: hipLaunchKernelGGL(mfma_rate_kernel<2>, g, b, 0, stream, iters, sink, clk); break;
+    case 3: hipLaunchKernelGGL(mfma_rate_kernel<3>, g, b, 0, stream, iters, sink, clk); break;
+    default: hipLaunchKernelGGL(mfma_rate_kernel<4>, g, b, 0, stream, iters, sink, clk); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -397,6 +397,27 @@ moe_status moe_experts_forward_from_logits(const moe_weights* w, const uint16_t*
                                            float* top_k_weights, uint16_t* out, void* ws, size_t ws_bytes,
                                            hipStream_t stream);
 
+/* ------------------------------------------------------ measurement utility --
+ * Not a step of the forward: the rate at which the matrix cores issue the MFMA
+ * forms the grouped GEMMs use, with random operands held in registers (no
+ * memory traffic), one workgroup of 8 waves on every CU, each wave running
+ * `iters` rounds of 16 independent MFMAs.  It exists so that each GEMM can be
+ * priced against the rate its own operand types reach on the device; the
+ * published peaks give FP8 and FP4 rates for matching operands only.
+ *  kind 0: e4m3 x e4m3 16x16x128, accumulating in the MFMA;
+ *  kind 1: e2m1 x e4m3 16x16x128 with per-lane UE8M0 scales (the MX GEMM's form);
+ *  kind 2: e2m1 x e2m1 16x16x128 with per-lane UE8M0 scales;
+ *  kind 3: bf16 16x16x32;
+ *  kind 4: e4m3 x e4m3 16x16x128 into a fresh accumulator, then the fp32
+ *          promotion acc += P * s (the FP8 GEMM's form).
+ * Outputs (host): *tflops, the achieved dense TFLOP/s (2 flops per MAC), and
+ * *sclk_ghz, the mean shader clock the probe ran at (shader-clock ticks over
+ * the 100 MHz real-time counter, per workgroup).  Allocates and frees its own
+ * device scratch and waits for the stream (a blocking call).  Errors:
+ * MOE_ERR_NULL (NULL output), MOE_ERR_UNSUPPORTED (kind outside 0..4),
+ * MOE_ERR_SHAPE (iters outside [1, 2^24]), device and HIP errors as elsewhere. */
+moe_status moe_probe_mfma_rate(int32_t kind, int32_t iters, double* tflops, double* sclk_ghz, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,7 @@ def lib():
 def test_library_exports_every_declared_function(lib):
     names = _declared_functions()
     assert "moe_experts_forward" in names and "moe_grouped_gemm" in names
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
 
@@ -447,3 +447,15 @@ def test_noalloc_forward_host_refusals(lib):
     assert lib.moe_experts_forward_noalloc(ctypes.byref(small), p, p, p, 8, 0, None, ctypes.c_void_p(32), None) == SHAPE
     assert lib.moe_experts_forward_noalloc(ctypes.byref(_weights(H=100)), p, p, p, 8, 2, None, ctypes.c_void_p(32),
                                            None) == SHAPE
+
+
+def test_mfma_probe_host_refusals(lib):
+    """The matrix-core rate probe refuses bad arguments on the host, before
+    touching the GPU (its kinds are the MFMA forms the GEMMs use)."""
+    d = ctypes.c_double()
+    assert lib.moe_probe_mfma_rate(0, 100, None, ctypes.byref(d), None) == NULL
+    assert lib.moe_probe_mfma_rate(5, 100, ctypes.byref(d), ctypes.byref(d), None) == UNSUP
+    assert lib.moe_probe_mfma_rate(-1, 100, ctypes.byref(d), ctypes.byref(d), None) == UNSUP
+    assert lib.moe_probe_mfma_rate(0, 0, ctypes.byref(d), ctypes.byref(d), None) == SHAPE
+    assert lib.moe_probe_mfma_rate(0, (1 << 24) + 1, ctypes.byref(d), ctypes.byref(d), None) == SHAPE
+    assert sorted(moe.PROBE_KINDS) == [0, 1, 2, 3, 4]
