@@ -143,6 +143,7 @@ hipError_t launch_transpose_u8(const uint8_t* in, uint8_t* out, int32_t batch, i
 // clk 2 * grid counters (shader-clock and 100 MHz ticks per workgroup).
 int probe_threads();
 int64_t probe_flops_per_mfma(int kind);
+int probe_mfmas_per_round(int kind);
 hipError_t launch_mfma_probe(int kind, int iters, int grid, float* sink, unsigned long long* clk,
                              hipStream_t stream);
 hipError_t launch_transpose_f32(const float* in, float* out, int32_t batch, int32_t rows, int32_t cols,

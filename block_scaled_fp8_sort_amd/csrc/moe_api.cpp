@@ -829,6 +829,7 @@ moe_status moe_probe_mfma_rate(int32_t kind, int32_t iters, double* tflops, doub
   moe_status st = check_device(stream, &dev, &cus);
   if (st != MOE_OK) return st;
   const int grid = cus, threads = moe::probe_threads();
+  iters = (iters + 1) & ~1;  // the probe runs its rounds in pairs
   float* sink = nullptr;
   unsigned long long* clk = nullptr;
   hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -858,7 +859,8 @@ moe_status moe_probe_mfma_rate(int32_t kind, int32_t iters, double* tflops, doub
     shader += (double)h_clk[2 * b];
     real += (double)h_clk[2 * b + 1];
   }
-  const double flops = (double)grid * (threads / 64) * (double)iters * 16.0 * (double)moe::probe_flops_per_mfma(kind);
+  const double flops = (double)grid * (threads / 64) * (double)iters * (double)moe::probe_mfmas_per_round(kind) *
+                       (double)moe::probe_flops_per_mfma(kind);
   *tflops = flops / ((double)ms * 1e-3) / 1e12;
   *sclk_ghz = real > 0.0 ? shader / real * 0.1 : 0.0;  // the real-time counter ticks at 100 MHz
   return ok();

@@ -36,8 +36,9 @@ __device__ __forceinline__ uint32_t mix32(uint32_t x) {
 // KIND: 0 e4m3 x e4m3 accumulating in the MFMA, 1 e2m1 x e4m3 and 2 e2m1 x e2m1
 // with per-lane UE8M0 scales (the MX GEMM's form), 3 bf16 16x16x32, 4 e4m3 x
 // e4m3 with a fresh accumulator and the fp32 promotion acc += P * s (the FP8
-// GEMM's form).  Every wave runs iters rounds of 16 independent MFMAs, the
-// operands rotating each round.
+// GEMM's form, pipelined as the GEMM does it).  Every wave runs iters (even)
+// rounds of probe_mfmas_per_round(KIND) independent MFMAs, the operands
+// rotating each round.
 template <int KIND>
 __global__ __launch_bounds__(kProbeWaves * 64, 1) void mfma_rate_kernel(int iters, float* sink,
                                                                          unsigned long long* clk) {
@@ -47,9 +48,14 @@ __global__ __launch_bounds__(kProbeWaves * 64, 1) void mfma_rate_kernel(int iter
   // likewise finite; e2m1 has no special codes
   const uint32_t mask = KIND == 3 ? 0xBFFFBFFFu : (KIND == 0 || KIND == 4) ? 0xBFBFBFBFu : 0xFFFFFFFFu;
   const uint32_t mask_b = KIND == 1 ? 0xBFBFBFBFu : mask;
-  v8i A[4], B[4];
+  // four operand sets rotated through, as a K step's four token sub-tiles and
+  // changing weight fragments are; the promotion form runs 4 x 2 outputs per
+  // round (its partials take the registers of the other eight)
+  constexpr int NOPS = 4;
+  constexpr int TN = KIND == 4 ? 2 : 4;
+  v8i A[NOPS], B[NOPS];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < NOPS; ++j)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       A[j][i] = (int)(mix32(seed + j * 16 + i) & mask);
@@ -58,19 +64,20 @@ __global__ __launch_bounds__(kProbeWaves * 64, 1) void mfma_rate_kernel(int iter
   int sc;  // UE8M0 1.0 in a VGPR, as the MX GEMM passes its per-lane scales
   asm volatile("v_mov_b32 %0, 127" : "=v"(sc));
   const float s = 1e-3f * (float)(tid + 1);
-  v4f acc[4][4];
+  v4f acc[4][TN], pa[4][TN], pb[4][TN];
 #pragma unroll
   for (int n = 0; n < 4; ++n)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[n][t] = v4f{0.f, 0.f, 0.f, 0.f};
-  const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
-  for (int it = 0; it < iters; ++it) {
-    const int o = it & 3;
+    for (int t = 0; t < TN; ++t) acc[n][t] = pa[n][t] = pb[n][t] = v4f{0.f, 0.f, 0.f, 0.f};
+  // one round: an MFMA per output; the promotion form writes this round's
+  // partials into `wr` while folding the previous round's, in `rd`, into the
+  // accumulators (the FP8 GEMM's pipeline: no FMA waits on the MFMA before it)
+  auto round = [&](int o, v4f(&wr)[4][TN], v4f(&rd)[4][TN]) {
 #pragma unroll
     for (int n = 0; n < 4; ++n)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const v8i a = A[(n + o) & 3], b = B[(t + o) & 3];
+      for (int t = 0; t < TN; ++t) {
+        const v8i a = A[(n + o) % NOPS], b = B[(t + o) % NOPS];
         if constexpr (KIND == 0) {
           acc[n][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[n][t], 0, 0, 0, 0, 0, 0);
         } else if constexpr (KIND == 1) {
@@ -85,17 +92,25 @@ __global__ __launch_bounds__(kProbeWaves * 64, 1) void mfma_rate_kernel(int iter
                                                               __builtin_bit_cast(bf16x8, v4i{b[0], b[1], b[2], b[3]}),
                                                               acc[n][t], 0, 0, 0);
         } else {
-          const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-          acc[n][t] += p * s;
+          wr[n][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+          acc[n][t] += rd[n][t] * s;
         }
       }
+  };
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; it += 2) {  // iters is even
+    round(it & 3, pa, pb);
+    round((it + 1) & 3, pb, pa);
   }
   const unsigned long long t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
   float sum = 0.f;
 #pragma unroll
   for (int n = 0; n < 4; ++n)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) sum += acc[n][t][0] + acc[n][t][1] + acc[n][t][2] + acc[n][t][3];
+    for (int t = 0; t < TN; ++t) {
+      const v4f v = acc[n][t] + pa[n][t] + pb[n][t];
+      sum += v[0] + v[1] + v[2] + v[3];
+    }
   sink[blockIdx.x * blockDim.x + tid] = sum;
   if (tid == 0) {
     clk[2 * blockIdx.x] = t1 - t0;
@@ -108,6 +123,8 @@ __global__ __launch_bounds__(kProbeWaves * 64, 1) void mfma_rate_kernel(int iter
 int probe_threads() { return kProbeWaves * 64; }
 
 int64_t probe_flops_per_mfma(int kind) { return kind == 3 ? 16 * 16 * 32 * 2 : 16 * 16 * 128 * 2; }
+
+int probe_mfmas_per_round(int kind) { return kind == 4 ? 8 : 16; }
 
 hipError_t launch_mfma_probe(int kind, int iters, int grid, float* sink, unsigned long long* clk,
                              hipStream_t stream) {

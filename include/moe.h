@@ -401,7 +401,8 @@ moe_status moe_experts_forward_from_logits(const moe_weights* w, const uint16_t*
  * Not a step of the forward: the rate at which the matrix cores issue the MFMA
  * forms the grouped GEMMs use, with random operands held in registers (no
  * memory traffic), one workgroup of 8 waves on every CU, each wave running
- * `iters` rounds of 16 independent MFMAs.  It exists so that each GEMM can be
+ * `iters` rounds of 16 independent MFMAs (8 for kind 4), over four rotating
+ * operand sets.  It exists so that each GEMM can be
  * priced against the rate its own operand types reach on the device; the
  * published peaks give FP8 and FP4 rates for matching operands only.
  *  kind 0: e4m3 x e4m3 16x16x128, accumulating in the MFMA;
