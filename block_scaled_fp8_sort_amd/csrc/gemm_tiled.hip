@@ -28,9 +28,10 @@
 //    interleaved in program order, so the matrix core and the VALU overlap.
 //  * Workgroup tile 256 (n) x BM (tokens) x 128 (K), eight waves as 2 (n) x 4
 //    (tokens), two per SIMD, each 128 n x BM/4 tokens.  BM is 256 for full
-//    m-tiles and 64, 128 or 256 for an expert's last, partial one, chosen per
-//    tile.  Two LDS stages at BM = 256, three at smaller BM (more bytes in
-//    flight per CU, which is what streaming weights at decode sizes needs).
+//    m-tiles and 64, 128, 192 or 256 for an expert's last, partial one, chosen
+//    per tile.  Two LDS stages at BM = 192 and 256, three at smaller BM (more
+//    bytes in flight per CU, which is what streaming weights at decode sizes
+//    needs).
 //  * Operands move global -> LDS by LDS-DMA (global_load_lds_dwordx4, 16 bytes
 //    per lane).  Weights are pre-tiled in MFMA operand order (tile_layout.h), so
 //    each DMA instruction copies one contiguous 1 KB and each fragment read is
@@ -202,8 +203,18 @@ __device__ __forceinline__ void k_step(const StageBuf<BM, WR>* cur, StageBuf<BM,
   // a half tile's 128 rows lie in one 128-row weight-scale block
   const float swg = cur->s[PAIRED || WR == 128 ? BM : BM + wn];
   const float swu = cur->s[BM + 1];
-  typedef float vts __attribute__((ext_vector_type(TS)));
-  const vts sav = *(const vts*)(cur->s + (wt * 16 + l16) * TS);
+  // the lane's TS activation scales are consecutive slots: one vector read
+  // (three single reads at TS = 3, whose slots are not 16-byte aligned)
+  float sav[TS];
+  if constexpr (TS == 3) {
+#pragma unroll
+    for (int ti = 0; ti < TS; ++ti) sav[ti] = cur->s[(wt * 16 + l16) * TS + ti];
+  } else {
+    typedef float vts __attribute__((ext_vector_type(TS)));
+    const vts v = *(const vts*)(cur->s + (wt * 16 + l16) * TS);
+#pragma unroll
+    for (int ti = 0; ti < TS; ++ti) sav[ti] = v[ti];
+  }
   v8i bf[TS];
 #pragma unroll
   for (int ti = 0; ti < TS; ++ti) bf[ti] = lds_frag_a(cur->a, wt * WM + ti * 16 + l16, g);
@@ -488,7 +499,7 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Mis
 }
 
 // Persistent kernel.  An expert's rows are cut into 256-row m-tiles; the last,
-// partial one runs at the smallest height of {64, 128, 256} that covers it, so
+// partial one runs at the smallest height of {64, 128, 192, 256} that covers it, so
 // little MFMA work goes to padding rows while the number of tiles stays that of
 // 256-row tiles.  Tiles come from the two-phase table (longest first).  The
 // body serves both operand types; each has a kernel of its own below.
@@ -514,8 +525,10 @@ __device__ __forceinline__ void tiled_gemm(const GemmParams& p, uint8_t* area, M
         return;
       }
     }
-    if (left > 128)
+    if (left > 192)
       run_tile<256, EPI, PAIRED, BF>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end);
+    else if (left > 128)
+      run_tile<192, EPI, PAIRED, BF>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end);
     else if (left > 64)
       run_tile<128, EPI, PAIRED, BF>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end);
     else

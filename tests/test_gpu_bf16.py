@@ -114,6 +114,25 @@ def test_bf16_forward_parity(wl):
     assert_out_close(host(out), ref, wl.name)
 
 
+def test_bf16_forward_every_tile_height():
+    """Experts whose last m-tile runs at each height the tiled kernel picks
+    (64, 128, 192, 256), at both ends of each range."""
+    counts = [1, 64, 65, 128, 129, 150, 192, 193, 255, 256, 256 + 129, 256 + 192, 512 + 170, 256 + 64]
+    wl = _wl("bf16_tile_heights", T=sum(counts), H=256, I=256, E=len(counts), k=1, seed=59)
+    say(f"bf16 forward {wl.name}")
+    inp = W.inputs(wl, DEV)
+    ids = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
+    inp["ids"] = torch.from_numpy(np.random.default_rng(59).permutation(ids).reshape(-1, 1)).to(DEV)
+    w = moe.prepare_weights(inp["w13"], None, inp["w2"], None, fmt=BF16)
+    dbg = {}
+    out = moe.experts_forward(inp["x"], inp["ids"], inp["w"], w, debug=dbg)
+    torch.cuda.synchronize()
+    n = {k_: host(v) for k_, v in inp.items()}
+    assert np.array_equal(host(dbg["expert_offsets"]), np.concatenate([[0], np.cumsum(counts)]))
+    ref = oracle.forward(BF16, n["w13"], None, n["w2"], None, n["x"], n["ids"], n["w"])
+    assert_out_close(host(out), ref, wl.name)
+
+
 def test_bf16_forward_invariants():
     wl = SMALL[1]
     inp = W.inputs(wl, DEV)

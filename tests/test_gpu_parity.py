@@ -263,6 +263,27 @@ def test_grouped_gemm_half_width_tail_tiles(H):
     _gemm_vs_oracle(FP8, 1, len(counts), H, 256, ids, 1, seed=90)
 
 
+# rows per expert whose last m-tile takes each height the tiled GEMMs choose
+# from (64, 128, 192, 256) at both ends of its range, alone and past one or two
+# full 256-row m-tiles
+TILE_HEIGHT_COUNTS = [1, 64, 65, 128, 129, 150, 192, 193, 255, 256, 256 + 129, 256 + 192, 512 + 170, 256 + 64]
+
+
+def _ids_with_counts(counts, seed):
+    ids = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
+    return np.random.default_rng(seed).permutation(ids).reshape(-1, 1)
+
+
+@pytest.mark.parametrize("fmt", [FP8, MX])
+@pytest.mark.parametrize("which", [0, 1])
+def test_grouped_gemm_every_tile_height(fmt, which):
+    """Both GEMMs (paired and unpaired) on experts whose last m-tile runs at
+    each height, 64 to 256 rows, including the 192-row one."""
+    say(f"gemm every tile height fmt={fmt} which={which}")
+    counts = TILE_HEIGHT_COUNTS
+    _gemm_vs_oracle(fmt, which, len(counts), 384, 256, _ids_with_counts(counts, 95 + which), 1, seed=95)
+
+
 @pytest.mark.parametrize("fmt", [FP8, MX])
 def test_grouped_gemm_tile_order_and_counters(fmt):
     """The fixed round-robin tile order (no counters) and the dynamic dispensers
@@ -378,6 +399,24 @@ def test_forward_parity_small(wl):
     o_codes, o_scales = oracle.quant_rows_bf16(n["x"], wl.fmt)
     assert np.array_equal(rowmajor_codes(dbg["act_codes"]), o_codes)
     assert np.array_equal(rowmajor_scales(dbg["act_scales"]).view(np.uint8), o_scales.view(np.uint8))
+    assert_forward_parity(wl.name, got, ref,
+                          flip_explainer(wl.fmt, wl.T, wl.k, wl.H, wl.I, n, got, dbg, swiglu_limit=wl.swiglu_limit))
+
+
+@pytest.mark.parametrize("fmt", [FP8, MX])
+def test_forward_every_tile_height(fmt):
+    """The forward (SwiGLU and h quantization, the weighted scatter, the
+    combine) over experts whose last m-tile runs at each height, 64 to 256
+    rows."""
+    counts = TILE_HEIGHT_COUNTS
+    wl = _small_workload(f"tile_heights_{fmt}", fmt, T=sum(counts), H=256, I=256, E=len(counts), k=1,
+                         limit=7.0 if fmt == MX else None, seed=96)
+    say(f"forward every tile height {wl.name}")
+    inp = W.inputs(wl, DEV)
+    inp["ids"] = torch.from_numpy(_ids_with_counts(counts, 96)).to(DEV)
+    got, ref, dbg, n, inv = _forward_case(wl, inp, debug=True)
+    assert np.array_equal(host(dbg["expert_offsets"]), np.concatenate([[0], np.cumsum(counts)]))
+    assert inv == 0
     assert_forward_parity(wl.name, got, ref,
                           flip_explainer(wl.fmt, wl.T, wl.k, wl.H, wl.I, n, got, dbg, swiglu_limit=wl.swiglu_limit))
 
