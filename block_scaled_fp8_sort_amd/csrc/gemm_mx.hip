@@ -16,8 +16,9 @@
 // [32 g, 32 g + 32) as 32 nibbles; an FP8 lane of group g holds K elements
 // [16 g, 16 g + 16) in bytes 0-15 and [64 + 16 g, 64 + 16 g + 16) in bytes 16-31;
 // the scale byte of lane group g applies to K elements [32 g, 32 g + 32).
-// Tiles: 256 weight rows x BM tokens x 128 K (BM = 256, or 64 / 128 / 192 / 256
-// for an expert's last, partial m-tile), eight waves (2 x 4), three or four LDS stages
+// Tiles: 256 weight rows x BM tokens x 128 K (BM = 256, or 64 / 128 / 256 for an
+// expert's last, partial m-tile, 192 for a gate_up expert's only one), eight
+// waves (2 x 4), three or four LDS stages
 // fed by LDS-DMA from the tiled weights (64-byte rows) and the K-block-major
 // activations; persistent XCD-aware tile walk and staged, whole-row epilogue
 // stores as in the FP8 kernel.
@@ -310,7 +311,8 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, int
 }
 
 // Persistent kernel; the last, partial m-tile of an expert runs at the
-// smallest height of {64, 128, 192, 256} that covers it, and tiles come from the
+// smallest height of {64, 128, 256} that covers it (on the gate_up GEMM an
+// expert's only m-tile at 192 rows when that covers it), and tiles come from the
 // two-phase, longest-first table (as in the FP8 kernel).
 template <int EPI, bool PAIRED>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmParams p) {
@@ -325,10 +327,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmParams p) {
   auto run = [&](int t) {
     const TileCoord tc = locate_tile2(t, E, NT, misc.off, misc.tp, misc.cnt, p.two_phase != 0);
     const int left = tc.m_end - tc.m0;
-    if (left > 192)
+    if constexpr (PAIRED) {
+      // an expert whose only m-tile has 129-192 rows: 192-row tile (not the
+      // last m-tile of an expert with full ones, which would run ahead of its
+      // group's 256-row tiles and make them fetch its weight tile again)
+      if (left > 128 && left <= 192 && tc.m0 == __builtin_amdgcn_readfirstlane(misc.off[tc.e])) {
+        run_tile<192, EPI, PAIRED>(p, area, srow, tc.e, tc.n_tile, tc.m0, tc.m_end);
+        return;
+      }
+    }
+    if (left > 128)
       run_tile<256, EPI, PAIRED>(p, area, srow, tc.e, tc.n_tile, tc.m0, tc.m_end);
-    else if (left > 128)
-      run_tile<192, EPI, PAIRED>(p, area, srow, tc.e, tc.n_tile, tc.m0, tc.m_end);
     else if (left > 64)
       run_tile<128, EPI, PAIRED>(p, area, srow, tc.e, tc.n_tile, tc.m0, tc.m_end);
     else

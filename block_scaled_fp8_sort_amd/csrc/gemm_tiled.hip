@@ -28,10 +28,10 @@
 //    interleaved in program order, so the matrix core and the VALU overlap.
 //  * Workgroup tile 256 (n) x BM (tokens) x 128 (K), eight waves as 2 (n) x 4
 //    (tokens), two per SIMD, each 128 n x BM/4 tokens.  BM is 256 for full
-//    m-tiles and 64, 128, 192 or 256 for an expert's last, partial one, chosen
-//    per tile.  Two LDS stages at BM = 192 and 256, three at smaller BM (more
-//    bytes in flight per CU, which is what streaming weights at decode sizes
-//    needs).
+//    m-tiles and 64, 128 or 256 for an expert's last, partial one (192 on the
+//    gate_up GEMM for an expert whose only m-tile has 129-192 rows), chosen per
+//    tile.  Two LDS stages at BM = 192 and 256, three at smaller BM (more bytes
+//    in flight per CU, which is what streaming weights at decode sizes needs).
 //  * Operands move global -> LDS by LDS-DMA (global_load_lds_dwordx4, 16 bytes
 //    per lane).  Weights are pre-tiled in MFMA operand order (tile_layout.h), so
 //    each DMA instruction copies one contiguous 1 KB and each fragment read is
@@ -499,9 +499,10 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, uint8_t* area, Mis
 }
 
 // Persistent kernel.  An expert's rows are cut into 256-row m-tiles; the last,
-// partial one runs at the smallest height of {64, 128, 192, 256} that covers it, so
-// little MFMA work goes to padding rows while the number of tiles stays that of
-// 256-row tiles.  Tiles come from the two-phase table (longest first).  The
+// partial one runs at the smallest height of {64, 128, 256} that covers it (and
+// on the gate_up GEMM an expert's only m-tile at 192 rows when that covers it),
+// so little MFMA work goes to padding rows while the number of tiles stays that
+// of 256-row tiles.  Tiles come from the two-phase table (longest first).  The
 // body serves both operand types; each has a kernel of its own below.
 template <int EPI, bool PAIRED, bool BF>
 __device__ __forceinline__ void tiled_gemm(const GemmParams& p, uint8_t* area, Misc& misc) {
@@ -525,10 +526,18 @@ __device__ __forceinline__ void tiled_gemm(const GemmParams& p, uint8_t* area, M
         return;
       }
     }
-    if (left > 192)
+    if constexpr (PAIRED) {
+      // an expert whose only m-tile has 129-192 rows: 192-row tile.  Not for
+      // the last m-tile of an expert with full ones: being shorter it runs
+      // ahead of its group's 256-row tiles through the K loop, and they fetch
+      // the weight tile it streamed again (Mega-MoE's gate_up L2 misses +34%)
+      if (left > 128 && left <= 192 && tc.m0 == __builtin_amdgcn_readfirstlane(misc.off[tc.e])) {
+        run_tile<192, EPI, PAIRED, BF>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end);
+        return;
+      }
+    }
+    if (left > 128)
       run_tile<256, EPI, PAIRED, BF>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end);
-    else if (left > 128)
-      run_tile<192, EPI, PAIRED, BF>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end);
     else if (left > 64)
       run_tile<128, EPI, PAIRED, BF>(p, area, misc, tc.e, tc.n_tile, tc.m0, tc.m_end);
     else

@@ -116,7 +116,8 @@ def test_bf16_forward_parity(wl):
 
 def test_bf16_forward_every_tile_height():
     """Experts whose last m-tile runs at each height the tiled kernel picks
-    (64, 128, 192, 256), at both ends of each range."""
+    (64, 128, 256, and 192 on the gate_up GEMM for an expert whose only m-tile
+    has 129-192 rows), at both ends of each range."""
     counts = [1, 64, 65, 128, 129, 150, 192, 193, 255, 256, 256 + 129, 256 + 192, 512 + 170, 256 + 64]
     wl = _wl("bf16_tile_heights", T=sum(counts), H=256, I=256, E=len(counts), k=1, seed=59)
     say(f"bf16 forward {wl.name}")

@@ -264,8 +264,9 @@ def test_grouped_gemm_half_width_tail_tiles(H):
 
 
 # rows per expert whose last m-tile takes each height the tiled GEMMs choose
-# from (64, 128, 192, 256) at both ends of its range, alone and past one or two
-# full 256-row m-tiles
+# from at both ends of its range, alone and past one or two full 256-row
+# m-tiles: 64, 128, 256, and on the gate_up GEMM 192 for an expert whose only
+# m-tile has 129-192 rows
 TILE_HEIGHT_COUNTS = [1, 64, 65, 128, 129, 150, 192, 193, 255, 256, 256 + 129, 256 + 192, 512 + 170, 256 + 64]
 
 
@@ -278,7 +279,7 @@ def _ids_with_counts(counts, seed):
 @pytest.mark.parametrize("which", [0, 1])
 def test_grouped_gemm_every_tile_height(fmt, which):
     """Both GEMMs (paired and unpaired) on experts whose last m-tile runs at
-    each height, 64 to 256 rows, including the 192-row one."""
+    each height, 64 to 256 rows (the paired one's 192-row tiles included)."""
     say(f"gemm every tile height fmt={fmt} which={which}")
     counts = TILE_HEIGHT_COUNTS
     _gemm_vs_oracle(fmt, which, len(counts), 384, 256, _ids_with_counts(counts, 95 + which), 1, seed=95)
