@@ -124,7 +124,7 @@ __device__ __forceinline__ TileCoord locate_tile(int t, int E, int BM, int NT, c
 }
 
 // Two-phase tile table of the tiled GEMMs (256-row m-tiles, an expert's last,
-// partial m-tile run at 64, 128 or 256 rows).  Phase 1 holds the short
+// partial m-tile run at 64, 128, 192 or 256 rows).  Phase 1 holds the short
 // remainder tiles (at most 128 rows) of experts that also have full m-tiles, NT
 // per such expert; phase 0 holds every other tile, in expert order and
 // tile_position order inside an expert, and comes first.  The long tiles go
