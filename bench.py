@@ -231,13 +231,17 @@ def measure(name, args, dev, steps, warmup, cpu_seconds, router=False, cold=Fals
     log(f"[bench] timing {steps} steps")
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
+    # clock stamps just outside the timed region: the mean shader clock over it
+    clk0 = moe.clock_stamp(1024, dev)
     ev0.record(stream)
     for _ in range(steps):
         step()
     ev1.record(stream)
+    clk1 = moe.clock_stamp(1024, dev)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms = ev0.elapsed_time(ev1) / steps
+    fwd_sclk = _sclk_summary(moe.shader_clock_ghz(clk0, clk1))
     log(f"[bench] {ms:.3f} ms/step (wall {1e3 * t_wall / steps:.3f} ms/step)")
     extra = {}
     if cold:
@@ -309,12 +313,15 @@ def measure(name, args, dev, steps, warmup, cpu_seconds, router=False, cold=Fals
     for _ in range(max(2, warmup)):  # past the clock ramp after the host-side preparation above
         l1()
     torch.cuda.synchronize()
+    clk0 = moe.clock_stamp(1024, dev)
     ev0.record(stream)
     for _ in range(steps):
         l1()
     ev1.record(stream)
+    clk1 = moe.clock_stamp(1024, dev)
     torch.cuda.synchronize()
     l1_ms = ev0.elapsed_time(ev1) / steps
+    l1_sclk = _sclk_summary(moe.shader_clock_ghz(clk0, clk1))
     l1_tflops = flop_l1 / (l1_ms * 1e-3) / 1e12
     act_b = 2 if wl.fmt == W.FMT_BF16 else 1  # bytes per activation / h element
     l1_bytes = int(len(touched) * w13_bytes + (T * H + S_v * I) * act_b)  # weights + A in + h out
@@ -355,6 +362,7 @@ def measure(name, args, dev, steps, warmup, cpu_seconds, router=False, cold=Fals
     result = {
         "ms_per_step": round(ms, 4),
         "tflops": round(tflops, 2),
+        "sclk_ghz": fwd_sclk,
         "dtype": {W.FMT_FP8_B128: "fp8e4m3", W.FMT_MX: "fp8e4m3 x fp4e2m1", W.FMT_BF16: "bf16"}[wl.fmt],
         "config": config,
         "roofline": dict(roof, **{
@@ -364,6 +372,11 @@ def measure(name, args, dev, steps, warmup, cpu_seconds, router=False, cold=Fals
             "algorithmic_flop_per_launch": flop_l1, "tflops": round(l1_tflops, 2), "gbs": round(l1_gbs, 1),
             "pct_fp8_peak": round(100.0 * l1_tflops / PEAK_FP8_TFLOPS, 2),
             "pct_mxfp4_peak": round(100.0 * l1_tflops / PEAK_MXFP4_TFLOPS, 2),
+            # the shader clock over the timed launches (published peaks assume
+            # 2.4 GHz), and the fraction of the peak scaled to that clock
+            "sclk_ghz": l1_sclk,
+            "frac_at_sclk": (round(roof["frac"] * 2.4 / l1_sclk["mean"], 4)
+                             if roof["bound"] == "mfma" and l1_sclk["mean"] else None),
         }),
     }
     result.update(extra)
@@ -372,6 +385,14 @@ def measure(name, args, dev, steps, warmup, cpu_seconds, router=False, cold=Fals
         result["cpu_baseline"] = cpu_baseline(wl, inp, cpu_seconds)
     del inp
     return result
+
+
+def _sclk_summary(per_xcd):
+    """Mean, lowest and highest per-XCD shader clock (GHz) of a bracketed span."""
+    v = list(per_xcd.values())
+    if not v:
+        return {"mean": None, "min": None, "max": None, "xcds": 0}
+    return {"mean": round(sum(v) / len(v), 3), "min": round(min(v), 3), "max": round(max(v), 3), "xcds": len(v)}
 
 
 def traffic_record(wl):

@@ -126,6 +126,8 @@ def load_library():
     lib.moe_experts_forward_noalloc.restype = ctypes.c_int
     lib.moe_experts_forward_noalloc.argtypes = [ctypes.POINTER(MoeWeights), _P, _P, _P, _I32, _I32,
                                                 ctypes.POINTER(MoeOptions), _P, _P]
+    lib.moe_clock_stamp.restype = ctypes.c_int
+    lib.moe_clock_stamp.argtypes = [ctypes.c_void_p, _I32, ctypes.c_void_p]
     lib.moe_probe_mfma_rate.restype = ctypes.c_int
     lib.moe_probe_mfma_rate.argtypes = [_I32, _I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                         _P]
@@ -635,6 +637,41 @@ PROBE_KINDS = {
     3: "bf16 16x16x32",
     4: "e4m3 x e4m3 16x16x128 + fp32 promotion (the FP8 GEMM's form)",
 }
+
+
+def clock_stamp(n: int = 1024, device: Optional[torch.device] = None) -> torch.Tensor:
+    """Enqueue one set of clock stamps (moe_clock_stamp) on the current stream:
+    an int64 device tensor [n, 3] of (compute unit: XCD id * 256 + its SE / array
+    / CU ids, that unit's shader-clock counter, 100 MHz real-time counter), one
+    row per one-wave workgroup.  Two stamps bracket the work enqueued between
+    them (shader_clock_ghz)."""
+    lib = load_library()
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    out = torch.empty((int(n), 3), dtype=torch.int64, device=dev)
+    _check(lib.moe_clock_stamp(out.data_ptr(), int(n), _stream(dev)))
+    return out
+
+
+def shader_clock_ghz(before: torch.Tensor, after: torch.Tensor) -> dict:
+    """Mean shader clock per XCD (GHz) between two clock_stamp results: for each
+    compute unit stamped in both, its shader-clock ticks over the 100 MHz
+    real-time ticks (the counters of different units are not aligned); per
+    XCD, the mean over its units.  Synchronizes with the device."""
+    a, b = before.cpu(), after.cpu()
+
+    def first(t):
+        d = {}
+        for u, clk, real in t.tolist():
+            d.setdefault(int(u), (clk, real))
+        return d
+
+    fa, fb = first(a), first(b)
+    per_xcd = {}
+    for u in sorted(set(fa) & set(fb)):
+        dt, dr = fb[u][0] - fa[u][0], fb[u][1] - fa[u][1]
+        if dr > 0:
+            per_xcd.setdefault(u // 256, []).append(dt / dr * 0.1)
+    return {x: sum(v) / len(v) for x, v in per_xcd.items()}
 
 
 def probe_mfma_rate(kind: int, iters: int = 20000, device: Optional[torch.device] = None):

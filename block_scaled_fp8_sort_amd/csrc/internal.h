@@ -146,6 +146,7 @@ int64_t probe_flops_per_mfma(int kind);
 int probe_mfmas_per_round(int kind);
 hipError_t launch_mfma_probe(int kind, int iters, int grid, float* sink, unsigned long long* clk,
                              hipStream_t stream);
+hipError_t launch_clock_stamp(unsigned long long* out, int n, hipStream_t stream);
 hipError_t launch_transpose_f32(const float* in, float* out, int32_t batch, int32_t rows, int32_t cols,
                                 hipStream_t stream);
 

@@ -50,6 +50,7 @@ bool valid_fmt(int f) { return f == MOE_FMT_FP8_B128 || f == MOE_FMT_MXFP8A_MXFP
 
 constexpr int kMaxE = 512;
 constexpr int kMaxK = 64;
+constexpr int kMaxClockStamps = 4096;
 
 // ------------------------------------------------------------ device checks
 struct DeviceInfo {
@@ -863,6 +864,18 @@ moe_status moe_probe_mfma_rate(int32_t kind, int32_t iters, double* tflops, doub
                        (double)moe::probe_flops_per_mfma(kind);
   *tflops = flops / ((double)ms * 1e-3) / 1e12;
   *sclk_ghz = real > 0.0 ? shader / real * 0.1 : 0.0;  // the real-time counter ticks at 100 MHz
+  return ok();
+}
+
+moe_status moe_clock_stamp(uint64_t* stamps, int32_t n, hipStream_t stream) {
+  if (!stamps) return fail(MOE_ERR_NULL, "stamps is NULL");
+  if (n < 1 || n > kMaxClockStamps) return fail(MOE_ERR_SHAPE, "n=%d outside [1, %d]", (int)n, kMaxClockStamps);
+  int dev, cus;
+  moe_status st = check_device(stream, &dev, &cus);
+  if (st != MOE_OK) return st;
+  if ((st = check_ptr(stamps, dev, "stamps")) != MOE_OK) return st;
+  const hipError_t he = moe::launch_clock_stamp(reinterpret_cast<unsigned long long*>(stamps), n, stream);
+  if (he != hipSuccess) return hip_status(he, "clock stamp");
   return ok();
 }
 

@@ -1,5 +1,5 @@
-// Matrix-core issue-rate probe for gfx950 (a measurement utility, not a step
-// of the forward).
+// Matrix-core issue-rate probe and clock stamps for gfx950 (measurement
+// utilities, not steps of the forward).
 //
 // The grouped GEMMs are priced against the MFMA rate of their own operand
 // types.  The published peaks give FP8 and FP4 rates for matching operands,
@@ -118,7 +118,29 @@ __global__ __launch_bounds__(kProbeWaves * 64, 1) void mfma_rate_kernel(int iter
   }
 }
 
+// One stamp per workgroup: the compute unit it runs on (XCD id x 256 + the
+// shader engine, array and CU ids of the hardware-id register, bits 8-15), that
+// unit's shader-clock counter and the 100 MHz real-time counter.  Two stamps on
+// one stream bracket the work enqueued between them; the shader-clock counters
+// of different units are not aligned, so spans are measured per unit.
+__global__ __launch_bounds__(64) void clock_stamp_kernel(unsigned long long* out) {
+  if (threadIdx.x != 0) return;
+  unsigned xcc, hw;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(xcc));
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID, 8, 8)" : "=s"(hw));
+  const unsigned long long t = __builtin_amdgcn_s_memtime();
+  const unsigned long long r = __builtin_amdgcn_s_memrealtime();
+  out[3 * blockIdx.x] = (unsigned long long)(xcc * 256u + hw);
+  out[3 * blockIdx.x + 1] = t;
+  out[3 * blockIdx.x + 2] = r;
+}
+
 }  // namespace
+
+hipError_t launch_clock_stamp(unsigned long long* out, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(clock_stamp_kernel, dim3((unsigned)n), dim3(64), 0, stream, out);
+  return hipGetLastError();
+}
 
 int probe_threads() { return kProbeWaves * 64; }
 

@@ -419,6 +419,25 @@ moe_status moe_experts_forward_from_logits(const moe_weights* w, const uint16_t*
  * MOE_ERR_SHAPE (iters outside [1, 2^24]), device and HIP errors as elsewhere. */
 moe_status moe_probe_mfma_rate(int32_t kind, int32_t iters, double* tflops, double* sclk_ghz, hipStream_t stream);
 
+/* Clock stamps (a measurement utility, not a step of the forward): enqueues on
+ * `stream` n one-wave workgroups; workgroup i writes three uint64 values to
+ * stamps[3 i], stamps[3 i + 1], stamps[3 i + 2]: the compute unit it ran on
+ * (XCD id * 256 + bits 8-15 of the hardware-id register: the shader engine,
+ * array and CU ids), that unit's shader-clock counter and the device's 100 MHz
+ * real-time counter.  Two calls on one stream bracket the work enqueued
+ * between them: for a unit stamped in both, the difference of its shader-clock
+ * counters over the difference of the real-time counters, times 0.1 GHz, is
+ * its mean shader clock over that span (the clock the GEMMs ran at under the
+ * chip's power limit).  The counters of different units are not aligned, and
+ * they follow the actual clock, which drops to its idle level while there is
+ * no work, so a span should hold back-to-back kernels only.  stamps: device
+ * memory of 3 n uint64 on the stream's device, written asynchronously (read
+ * it once the stream has passed the call).  n: 1..4096; 1024 stamp most units
+ * of the 256-CU part.  Allocates nothing and does not block.  Errors: MOE_ERR_NULL
+ * (stamps NULL), MOE_ERR_SHAPE (n out of range), MOE_ERR_DEVICE (stamps not on
+ * the stream's device), HIP errors as elsewhere. */
+moe_status moe_clock_stamp(uint64_t* stamps, int32_t n, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

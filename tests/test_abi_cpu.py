@@ -33,7 +33,7 @@ def lib():
 def test_library_exports_every_declared_function(lib):
     names = _declared_functions()
     assert "moe_experts_forward" in names and "moe_grouped_gemm" in names
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
 
@@ -459,3 +459,13 @@ def test_mfma_probe_host_refusals(lib):
     assert lib.moe_probe_mfma_rate(0, 0, ctypes.byref(d), ctypes.byref(d), None) == SHAPE
     assert lib.moe_probe_mfma_rate(0, (1 << 24) + 1, ctypes.byref(d), ctypes.byref(d), None) == SHAPE
     assert sorted(moe.PROBE_KINDS) == [0, 1, 2, 3, 4]
+
+
+def test_clock_stamp_host_refusals(lib):
+    """The clock stamps refuse a NULL output and a stamp count outside
+    [1, 4096] on the host, before touching the GPU."""
+    dummy = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails first
+    assert lib.moe_clock_stamp(None, 64, None) == NULL
+    assert lib.moe_clock_stamp(dummy, 0, None) == SHAPE
+    assert lib.moe_clock_stamp(dummy, 4097, None) == SHAPE
+    assert lib.moe_clock_stamp(dummy, -1, None) == SHAPE
