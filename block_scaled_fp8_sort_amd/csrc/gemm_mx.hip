@@ -61,7 +61,8 @@ struct Misc {
 
 // LDS shared by the pipeline stages of every tile height: three stages of the
 // 256-row layout (with the tile table, 159.8 of the 160 KiB), which also
-// hold four of the 128-row and of the 64-row one.  A third 256-row stage (two
+// hold three of the 192-row one and four of the 128-row and of the 64-row
+// one.  A third 256-row stage (two
 // before) took Mega-MoE's gate_up GEMM from 3.32 to 3.28 ms.
 constexpr int kStageArea = 3 * (int)sizeof(StageBuf<256>);
 template <int BM>

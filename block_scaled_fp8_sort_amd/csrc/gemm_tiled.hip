@@ -103,8 +103,9 @@ struct Misc {
 };
 
 // LDS shared by the pipeline stages of every tile height: three stages of the
-// 128-row layout, which also hold two of the 256-row one and three of the
-// 64-row one, and four or five of the half-width (128 weight rows) ones.
+// 128-row layout, which also hold two of the 256-row and of the 192-row one,
+// three of the 64-row one, and four or five of the half-width (128 weight
+// rows) ones.
 constexpr int kStageArea = 3 * (int)sizeof(StageBuf<128>);
 template <int BM, int WR = BN>
 constexpr int stages_for() {
