@@ -89,8 +89,12 @@ struct TileCoord {
 // while all n-tiles pass over them and each weight tile is fetched once per
 // group.  With m fastest over a whole large expert instead, its activation rows
 // (more than the last-level cache holds at large token counts) would come back
-// from HBM once per n-tile.
-constexpr int kTileGroupM = 8;
+// from HBM once per n-tile.  A window of 32 consecutive tiles (one XCD's
+// share, see the dispensers) then spans 4 m-tiles x 8 n-tiles, whose activation
+// and weight tiles together are the least bytes when a weight tile is at most
+// the size of an activation tile (equal for FP8, half for FP4 weights): on
+// Mega-MoE's gate_up GEMM, 4 gave 13% fewer L2 misses and 0.8% less time than 8.
+constexpr int kTileGroupM = 4;
 
 // (m index, n index) of tile loc (0-based within its expert).
 __device__ __forceinline__ void tile_position(int loc, int mt, int NT, int& m_idx, int& n_idx) {

@@ -40,7 +40,7 @@
 //    128-byte chunks by per-lane address (the gather is free) without the
 //    same-L2-channel aliasing that 4 KB-strided rows suffer.
 //  * Persistent grid: each workgroup reads the expert offsets, builds the tile
-//    table in LDS (per expert, groups of up to 8 m-tiles, m fastest inside a
+//    table in LDS (per expert, groups of up to 4 m-tiles, m fastest inside a
 //    group, then n; the short remainder tiles of large experts after all the
 //    rest, so they fill the last round), and walks tiles with a stride of the
 //    grid size.  Without the gate/up pairing those remainder tiles run as two
