@@ -5,8 +5,10 @@ for the whole output, with one documented exception path: the quantized SwiGLU
 output h is an integer decided by floating point (an e4m3 code), computed on the
 GPU from fp32 accumulators and in the oracle from fp64 sums, so a code may round
 to its neighbour; at the top of e4m3's range a neighbour is 1/14 of the block
-maximum away, and one such flip moves every output of that slot.  Where the
-max-norm bar is exceeded, the test must show that such flips are all there is:
+maximum away, and one such flip moves every output of that slot (with a few
+tokens, one flip among a thousand h codes moves the relative L2 past 5e-3 as
+well).  Where either bar is exceeded, the test must show that such flips are
+all there is:
 (1) the rest of the path, run by the oracle on the GPU's own h codes, matches
 the GPU's output within the rounding the GPU does after h, and (2) every h code
 that differs from the oracle's is a neighbouring e4m3 value.
@@ -135,16 +137,15 @@ def check_h_codes(fmt, hq, hs, slots, o_codes, o_scales, I):
 
 
 def assert_forward_parity(what, got_bits, ref_bits, explain=None):
-    """The forward's tolerance; beyond the max-norm bar, `explain` must show
-    that only h-code rounding flips are at play (module docstring)."""
+    """The forward's tolerance; beyond either bar, `explain` must show that
+    only h-code rounding flips are at play (module docstring)."""
     g, r, max_rel, rel_l2 = norms(got_bits, ref_bits)
     assert np.all(np.isfinite(g)), f"{what}: non-finite output"
     say(f"  {what}: max|err| / max|ref| = {max_rel:.2e}, rel L2 = {rel_l2:.2e}")
-    assert rel_l2 <= 5e-3, f"{what}: rel L2 {rel_l2}"
-    if max_rel <= 1e-2:
+    if max_rel <= 1e-2 and rel_l2 <= 5e-3:
         return
-    assert explain is not None, f"{what}: max|err| / max|ref| {max_rel:.3e} > 1e-2"
-    say(f"  {what}: past the max-norm bar; checking that h-code rounding flips explain it")
+    assert explain is not None, f"{what}: max|err| / max|ref| {max_rel:.3e}, rel L2 {rel_l2:.3e}: past the bar"
+    say(f"  {what}: past the bar; checking that h-code rounding flips explain it")
     explain()
 
 

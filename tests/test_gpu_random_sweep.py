@@ -54,6 +54,15 @@ def _cases(n=36, seed=2024, large=False):
 
 CASES = _cases() + _cases(n=15, seed=2025, large=True)
 
+# Two 3-token FP8 layers of a wider sweep (seed 9090) whose outputs pass the
+# bars only through the h-flip explanation: one of 1152 h codes (r54) and five
+# of 2304 (r96) round to the neighbouring e4m3 value, which moves the few
+# outputs by 6.6e-3 and 6.1e-3 in relative L2.
+FLIP_CASES = [c for c in _cases(n=150, seed=9090)
+              if c[0] in ("r54_fp8_T3_H640_I384_E40_k1_b0", "r96_fp8_T3_H640_I384_E2_k2_b3")]
+assert len(FLIP_CASES) == 2
+CASES = CASES + FLIP_CASES
+
 
 @pytest.mark.parametrize("name,wl,begin", CASES, ids=[c[0] for c in CASES])
 def test_random_layer_parity(name, wl, begin):
