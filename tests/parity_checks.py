@@ -101,16 +101,31 @@ def _e4m3_step(v):
     return 2.0 ** (np.floor(np.log2(a)) - 3)
 
 
-def check_h_codes(fmt, hq, hs, slots, o_codes, o_scales, I):
+def h_tolerance(o_gu, I, limit=None):
+    """Per element, how far h = silu(g) u can move when the gate/up sums move by
+    the grouped GEMM's own parity bound, 1e-4 of the largest |g|, |u| of the
+    call (test_grouped_gemm_store_f32): |dh| <= d (1.1 |u| + |silu(g)|), as
+    |silu'| <= 1.1 and the clamp only shrinks the change.  o_gu: the oracle's
+    gate (first I) and up (last I) sums per row."""
+    gu = o_gu.astype(np.float64)
+    d = 1e-4 * float(np.max(np.abs(gu))) if gu.size else 0.0
+    g, u = gu[:, :I], gu[:, I:]
+    if limit is not None:
+        g, u = np.minimum(g, limit), np.clip(u, -limit, limit)
+    with np.errstate(over="ignore"):
+        silu = g / (1.0 + np.exp(-g))
+    return d * (1.1 * np.abs(u) + np.abs(silu))
+
+
+def check_h_codes(fmt, hq, hs, slots, o_codes, o_scales, I, o_gu, limit=None):
     """The GPU's h (by sorted row) against the oracle's (by flat slot): scales
     within 1e-3 (FP8) or one exponent step (MX), and every differing code a
     neighbouring e4m3 value of the oracle's, compared as values (code times
     block scale, so an MX block whose scale byte moved by one is judged by its
-    values).  The two h differ by the gate/up sums' accumulation error, which
-    is absolute (a fraction of the row's largest products, not of each
-    element), so near zero, where e4m3 steps are finest, a difference of
-    2e-4 of the block's largest magnitude (0.09 of a code unit at 448) is
-    accepted too."""
+    values), give or take how far h itself can move under the gate/up GEMM's
+    accumulation error (h_tolerance; it matters near zero, where e4m3 steps
+    are finest, since that error is a fraction of the largest sums, not of
+    each element)."""
     oc, osc = o_codes[slots], o_scales[slots]
     B = 128 if fmt == FP8 else 32
     if fmt == FP8:
@@ -128,11 +143,12 @@ def check_h_codes(fmt, hq, hs, slots, o_codes, o_scales, I):
     diff = hq != oc
     du = np.abs(ug - uo)
     one_step = 1.0001 * np.maximum(_e4m3_step(ug), _e4m3_step(uo)) + np.abs(ug) * np.abs(ratio - 1)
-    ok = (du <= one_step) | (du <= 2e-4 * 448.0)
+    moved = h_tolerance(o_gu[slots], I, limit) / so  # h's own movement, in code units
+    ok = du <= one_step + moved
     multi = diff & (du > one_step)
     say(f"  h codes: {np.count_nonzero(diff)} of {diff.size} differ ({100 * np.mean(diff):.3f}%); "
-        f"{np.count_nonzero(multi)} by more than one e4m3 step, all within "
-        f"{np.max(du[multi]) / 448.0 if multi.any() else 0:.1e} of the block maximum")
+        f"{np.count_nonzero(multi)} by more than one e4m3 step, each within "
+        f"{np.max((du - one_step)[multi] / np.maximum(moved[multi], 1e-300)) if multi.any() else 0:.2f} of its bound")
     assert np.all(ok | ~diff), "an h code differs from the oracle's by more than its rounding allows"
 
 
@@ -158,5 +174,5 @@ def flip_explainer(fmt, T, k, H, I, n, out_bits, dbg, swiglu_limit=None, act_sca
         _, odbg = oracle.forward(fmt, n["w13"], n["s13"], n["w2"], n["s2"], n["x"], n["ids"], n["w"],
                                  swiglu_limit=swiglu_limit, expert_begin=expert_begin, debug=True,
                                  act_scales=act_scales, act_scales_row_stride=act_stride)
-        check_h_codes(fmt, hq, hs, slots, odbg["h_codes"], odbg["h_scales"], I)
+        check_h_codes(fmt, hq, hs, slots, odbg["h_codes"], odbg["h_scales"], I, odbg["gu"], swiglu_limit)
     return run

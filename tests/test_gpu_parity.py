@@ -446,7 +446,7 @@ def test_forward_down_half_from_the_gpus_own_h(name):
     hq, hs, slots = check_down_half(wl.fmt, wl.T, wl.k, wl.H, wl.I, n, host(out), dbg)
     _, odbg = oracle.forward(wl.fmt, n["w13"], n["s13"], n["w2"], n["s2"], n["x"], n["ids"], n["w"],
                              swiglu_limit=wl.swiglu_limit, debug=True)
-    check_h_codes(wl.fmt, hq, hs, slots, odbg["h_codes"], odbg["h_scales"], wl.I)
+    check_h_codes(wl.fmt, hq, hs, slots, odbg["h_codes"], odbg["h_scales"], wl.I, odbg["gu"], wl.swiglu_limit)
 
 DUP_CASES = [
     _small_workload("dup_garbage_fp8", FP8, T=200, H=384, I=256, E=10, k=4, seed=40),

@@ -13,6 +13,7 @@ stays well under its 5e-3 bar.  The GPU parity tests therefore accept a
 max-norm breach only when the flips are shown to be all there is
 (tests/parity_checks.py)."""
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -48,3 +49,60 @@ def test_fp32_level_gate_up_noise_alone_reaches_the_max_norm_bar():
     assert 1e-3 < flips < 2e-2
     assert max_rel > 0.8e-2  # as large as the bar itself, from flips alone
     assert rel_l2 < 4e-3
+
+
+def _study_layer():
+    wl = W.Workload("flip_check", T=600, H=384, I=256, E=16, k=4, fmt=W.FMT_FP8_B128, routing="zipf",
+                    zipf_s=1.1, skip=0.05, seed=29)
+    inp = W.inputs(wl, "cpu")
+    n = {k: W.to_numpy(v) for k, v in inp.items()}
+    _, d = oracle.forward(wl.fmt, n["w13"], n["s13"], n["w2"], n["s2"], n["x"], n["ids"], n["w"], debug=True)
+    ss, off, _, _ = oracle.route_sort(n["ids"], wl.E)
+    nv = int(off[-1])
+    return wl, d, ss[:nv]
+
+
+def _requantized_h(wl, d, slots, noise, seed):
+    """h from the oracle's gate/up sums moved by uniform noise of `noise` times
+    their largest magnitude, quantized with the oracle's rule (by sorted row)."""
+    gu = d["gu"][slots].astype(np.float64)
+    I = wl.I
+    rng = np.random.default_rng(seed)
+    gu = gu + noise * np.max(np.abs(gu)) * rng.uniform(-1, 1, gu.shape)
+    g, u = gu[:, :I], gu[:, I:]
+    h = (g / (1 + np.exp(-g)) * u).astype(np.float32)
+    return oracle.quant_rows_f32(h, wl.fmt)
+
+
+def test_h_check_accepts_gate_up_error_within_the_gemm_bound():
+    """The h-code check of the GPU parity tests (parity_checks.check_h_codes)
+    accepts every h the gate/up GEMM's own tolerance allows: sums moved by up
+    to 1e-4 of the largest |g|, |u|, requantized."""
+    from parity_checks import check_h_codes
+    wl, d, slots = _study_layer()
+    hq, hs = _requantized_h(wl, d, slots, 1e-4, 1)
+    assert np.mean(hq != d["h_codes"][slots]) > 1e-3  # the noise does flip codes
+    check_h_codes(wl.fmt, hq, hs, slots, d["h_codes"], d["h_scales"], wl.I, d["gu"])
+
+
+def test_h_check_rejects_misplaced_or_wrong_h():
+    """... and rejects what a bug would leave: two sorted rows' h swapped, one
+    large code three e4m3 steps off, or h computed from sums moved by ten times
+    the GEMM's tolerance."""
+    from parity_checks import check_h_codes
+    wl, d, slots = _study_layer()
+    hq, hs = _requantized_h(wl, d, slots, 0.0, 1)
+    check_h_codes(wl.fmt, hq, hs, slots, d["h_codes"], d["h_scales"], wl.I, d["gu"])  # exact h passes
+    bad = hq.copy()
+    bad[[3, 7]] = bad[[7, 3]]
+    with pytest.raises(AssertionError):
+        check_h_codes(wl.fmt, bad, hs, slots, d["h_codes"], d["h_scales"], wl.I, d["gu"])
+    bad = hq.copy()
+    r, c = np.unravel_index(np.argmax(np.where(hq & 0x7F < 0x70, hq & 0x7F, 0)), hq.shape)
+    bad[r, c] = hq[r, c] + 3  # three steps up in magnitude, same sign
+    with pytest.raises(AssertionError):
+        check_h_codes(wl.fmt, bad, hs, slots, d["h_codes"], d["h_scales"], wl.I, d["gu"])
+    hq10, hs10 = _requantized_h(wl, d, slots, 1e-3, 2)
+    with pytest.raises(AssertionError):
+        check_h_codes(wl.fmt, hq10, hs10, slots, d["h_codes"], d["h_scales"], wl.I, d["gu"])
+
