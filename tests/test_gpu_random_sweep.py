@@ -4,10 +4,11 @@ Each case draws its shape (T, H, I, E, k), format, routing, skipped slots,
 clamp and expert_begin from a fixed seed, so the sweep reaches combinations
 the hand-picked cases do not (both FP8 GEMM paths and their switch-over, the
 half-width tail tiles, the tile dispensers' stealing on small grids, MX and
-bf16 experts).  Checked: the route sort bit-exact; the activation codes and
-scales bit-exact (quantized formats); the forward within the parity bar
-(max|err| <= 1e-2 max|ref|, relative L2 <= 5e-3), a max-norm breach accepted
-only with the h-flip explanation of parity_checks.
+bf16 experts), and a set of extreme shapes (up to 512 experts, top-64, half
+the slots skipped).  Checked: the route sort bit-exact; the activation codes
+and scales bit-exact (quantized formats); the forward within the parity bar
+(max|err| <= 1e-2 max|ref|, relative L2 <= 5e-3), a breach accepted only with
+the h-flip explanation of parity_checks.
 """
 import numpy as np
 import pytest
@@ -52,7 +53,33 @@ def _cases(n=36, seed=2024, large=False):
     return out
 
 
-CASES = _cases() + _cases(n=15, seed=2025, large=True)
+def _wide_cases(n=40, seed=777):
+    """Extreme shapes: up to 512 experts, top-64, hidden up to 2048 and
+    intermediate up to 1024 (one to sixteen and one to eight 128-wide blocks),
+    half the slots skipped, ids offset by 100; the oracle's work capped."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        i = len(out)
+        fmt = FMTS[i % 3]
+        E = int(rng.choice([1, 2, 4, 7, 16, 33, 64, 128, 256, 512]))
+        k = int(rng.integers(1, min(64, E) + 1)) if rng.random() < 0.3 else int(rng.integers(1, min(8, E) + 1))
+        T = int(rng.choice([1, 2, int(rng.integers(3, 32)), int(rng.integers(32, 512)), int(rng.integers(512, 4000))]))
+        H = 128 * int(rng.integers(1, 17))
+        I = 128 * int(rng.integers(1, 9))
+        if T * k * H * I > 4e9:
+            continue
+        routing = "zipf" if rng.random() < 0.5 else "uniform"
+        skip = float(rng.choice([0.0, 0.1, 0.5]))
+        limit = None if rng.random() < 0.5 else (7.0 if fmt == W.FMT_MX else float(rng.choice([0.05, 1.0, 7.0])))
+        begin = int(rng.choice([0, 0, 3, 100]))
+        out.append((f"w{i:02d}_{FMT_NAME[fmt]}_T{T}_H{H}_I{I}_E{E}_k{k}_b{begin}_s{skip}",
+                    W.Workload(f"wide{i}", T=T, H=H, I=I, E=E, k=k, fmt=fmt, routing=routing, zipf_s=1.1,
+                               skip=skip, swiglu_limit=limit, seed=5000 + i), begin))
+    return out
+
+
+CASES = _cases() + _cases(n=15, seed=2025, large=True) + _wide_cases()
 
 # Two 3-token FP8 layers of a wider sweep (seed 9090) whose outputs pass the
 # bars only through the h-flip explanation: one of 1152 h codes (r54) and five
