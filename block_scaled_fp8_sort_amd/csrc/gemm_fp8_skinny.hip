@@ -7,17 +7,17 @@
 // "Source").
 //
 // Why a second kernel: with a handful of rows per expert the work is streaming
-// the expert weights from HBM, and the rate is set by the bytes each CU keeps in
-// flight (HBM latency under load is several microseconds).  LDS stages cap that
-// at two or three 40 KB stages.  Here no weight goes through LDS: each of the 8
+// the expert weights from HBM.  Here no weight goes through LDS: each of the 8
 // waves of a workgroup owns 32 rows of the 256-row prepared weight tile and
-// loads its MFMA fragments straight into VGPRs, D K-blocks ahead, in a ring of
-// register slots (one slot holds a K block's 4 KB of weight fragments and the
-// activation fragment of a wave, about 28 VGPRs; D = 8 keeps 256 KB of weights
-// per CU in flight within the 256 VGPRs of a wave).  The ring runs on into
-// the workgroup's next tile, so consecutive tiles do not drain the pipeline.
-// The loads are ordinary ones, so the compiler tracks them and waits exactly
-// for the slot it consumes.
+// loads its MFMA fragments straight into VGPRs, in a ring of D register slots
+// (one slot holds a K block's 4 KB of weight fragments and the activation
+// fragment of a wave).  The ring runs on into the workgroup's next tile, so
+// consecutive tiles do not drain the pipeline, and its loads are ordinary ones,
+// so the compiler tracks them and waits exactly for the slot it consumes.  The
+// launcher runs one slot (one K block ahead per wave) and one workgroup per
+// CU: deeper rings (2 to 8 blocks, up to 256 KB of weights in flight per CU)
+// were 2-5% slower on decode layers, and two or three workgroups per CU
+// 10-16% slower; fewer concurrent streams stream faster on this part.
 //
 // Tile: 16 sorted rows x 256 weight rows.  MFMA A operand = 16 weight rows,
 // B operand = the 16 gathered activation rows; each lane ends with 4
@@ -319,19 +319,10 @@ hipError_t launch_d(const GemmParams& p, int num_cus, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// D (K blocks in flight per wave) divides K / 128, so a tile ends on a ring
-// boundary and the next tile starts at slot 0.
+// One K block in flight per wave (D = 1 divides every K / 128, so a tile ends
+// on a ring boundary): measured faster than every deeper ring.
 template <int EPI, bool PAIRED>
 hipError_t launch_epi(const GemmParams& p, int num_cus, hipStream_t stream) {
-  const int KB = p.K / BK;
-  // 8 slots fit in registers with the SwiGLU epilogue too, but measured slower
-  // there (the wave's 72 loads in flight exceed what vmcnt counts)
-  if constexpr (EPI != kEpiSwiGLUQuant)
-    if (KB % 8 == 0) return launch_d<EPI, PAIRED, 8>(p, num_cus, stream);
-  if (KB % 6 == 0) return launch_d<EPI, PAIRED, 6>(p, num_cus, stream);
-  if (KB % 4 == 0) return launch_d<EPI, PAIRED, 4>(p, num_cus, stream);
-  if (KB % 3 == 0) return launch_d<EPI, PAIRED, 3>(p, num_cus, stream);
-  if (KB % 2 == 0) return launch_d<EPI, PAIRED, 2>(p, num_cus, stream);
   return launch_d<EPI, PAIRED, 1>(p, num_cus, stream);
 }
 

@@ -141,7 +141,7 @@ def test_quant_act_all_bf16_values(fmt):
 @pytest.mark.parametrize("E,H,I,T,k", [
     (3, 256, 128, 40, 2), (5, 640, 384, 700, 3), (2, 384, 1024, 300, 1),
     # at most 8 rows per expert on average: the FP8 path streams weights
-    # through registers; K / 128 = 5, 3, 16, 4, 2 give ring depths 1, 3, 4, 4, 2
+    # through registers one K block ahead; K / 128 = 5, 3, 16, 4, 2
     (12, 640, 384, 10, 3), (16, 2048, 512, 24, 4), (20, 256, 256, 30, 2),
 ])
 def test_grouped_gemm_store_f32(fmt, which, E, H, I, T, k):
