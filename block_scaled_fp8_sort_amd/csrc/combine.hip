@@ -83,7 +83,11 @@ hipError_t launch_combine(const uint16_t* slot_out, const int32_t* ids, int32_t 
   if (n == 0) return hipSuccess;
   const int threads = 256;
   const int64_t want = (n + threads - 1) / threads;
-  const int blocks = (int)(want < 256 * 32 ? want : 256 * 32);
+  // one chunk per thread (a grid-stride loop only past 2^22 workgroups, which
+  // keeps the launch under 2^32 work-items): against 8192 workgroups, the
+  // DeepSeek-V3 combine took 197.6 instead of 202.5 us, Mega-MoE's 408 instead
+  // of 420 us
+  const int blocks = (int)(want < (1 << 22) ? want : (1 << 22));
   hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(threads), 0, stream, (const uint4*)slot_out, ids, T, k,
                      H / 8, E, expert_begin, (uint4*)out);
   return hipGetLastError();
