@@ -9,7 +9,11 @@
 // added in ascending j in fp32 and rounded once to bf16.  Skipped slots add
 // nothing: their rows were never written, and whatever they hold (NaN included)
 // is dropped by a select before the sum.  HBM-bound at large sizes (16-byte
-// loads and stores, 8 bf16 per lane), latency-bound at decode sizes.
+// loads and stores, 8 bf16 per lane), latency-bound at decode sizes.  The slot
+// rows, read once, are loaded with the nontemporal hint (DeepSeek-V3's combine
+// 169 instead of 200 us, Mega-MoE's 348 instead of 406 us); with the hint on
+// the output stores as well the combine ran 4-9% slower than with it on the
+// loads alone.
 #include "device_common.h"
 #include "internal.h"
 
@@ -17,6 +21,7 @@ namespace moe {
 
 namespace {
 
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 // Sum of one token's valid slot rows at 8 columns (one 16-byte chunk).  Every
 // slot's load is issued before any is used (one memory round trip, which is
@@ -35,7 +40,8 @@ __device__ __forceinline__ void combine_chunk(const uint4* __restrict__ slot_out
       const int j = min(j0 + u, k - 1);
       const int64_t local = (int64_t)ids[t * k + j] - expert_begin;
       ok[u] = j0 + u < k && local >= 0 && local < E;
-      v[u] = slot_out[(t * k + j) * H8 + col];
+      const v4u x = __builtin_nontemporal_load((const v4u*)&slot_out[(t * k + j) * H8 + col]);
+      v[u] = make_uint4(x.x, x.y, x.z, x.w);
     }
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
