@@ -39,9 +39,9 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "MoE-layer active-expert TFLOP/s + tokens/s at 1 GPU; % of FP8/MXFP4 MFMA peak"
 
 # The gate_up GEMM kernel the library launches for a workload: the register-
-# streaming FP8 kernel when there are at most 8 rows per expert on average (the
+# streaming FP8 kernel when there are at most 12 rows per expert on average (the
 # library's own rule), else the LDS-tiled FP8 kernel, or the MX kernel.
-SKINNY_ROWS_PER_EXPERT = 8
+SKINNY_ROWS_PER_EXPERT = 12
 _CSRC = "block_scaled_fp8_sort_amd/csrc/"
 _COMMON = [_CSRC + "gemm_common.h", _CSRC + "tile_layout.h", _CSRC + "device_common.h"]
 GATE_UP_KERNELS = {

@@ -243,8 +243,14 @@ moe::GemmParams to_params(const moe_gemm_args* a) {
 }
 
 // At most this many rows per expert on average (decode batches): the FP8 GEMM
-// streams the weights through registers instead of LDS tiles.
-constexpr int64_t kSkinnyRowsPerExpert = 8;
+// streams the weights through registers instead of LDS tiles.  Forward times
+// (uniform routing) of the register-streaming against the tiled kernel: on the
+// Qwen3-MoE shape 124 against 153 us at 10 rows, 131 against 156 at 12, 135
+// against 156 at 14, 154 against 157 at 16; on the DeepSeek-V3 shape 1.85
+// against 1.97 ms at 10 rows, 1.99 against 2.00 at 12, but 2.24 against 2.01
+// at 14 and 2.66 against 2.03 at 16 (past 16 rows an expert needs a second
+// 16-row tile, whose weights stream again).
+constexpr int64_t kSkinnyRowsPerExpert = 12;
 // Bytes of the gate_up weight read ahead during a decode batch's sort (the
 // Qwen3-shaped decode forward: 16 MB 1 us faster, 24 MB the same warm and
 // slower cold, 40 MB slower: more outlasts the sorting workgroup).

@@ -140,7 +140,7 @@ def test_quant_act_all_bf16_values(fmt):
 @pytest.mark.parametrize("which", [0, 1])
 @pytest.mark.parametrize("E,H,I,T,k", [
     (3, 256, 128, 40, 2), (5, 640, 384, 700, 3), (2, 384, 1024, 300, 1),
-    # at most 8 rows per expert on average: the FP8 path streams weights
+    # at most 12 rows per expert on average: the FP8 path streams weights
     # through registers one K block ahead; K / 128 = 5, 3, 16, 4, 2
     (12, 640, 384, 10, 3), (16, 2048, 512, 24, 4), (20, 256, 256, 30, 2),
 ])
@@ -357,7 +357,7 @@ SMALL = [
     _small_workload("ragged_fp8_clamp", FP8, T=517, H=384, I=256, E=12, k=4, routing="zipf", skip=0.05,
                     limit=0.05, seed=12),
     _small_workload("k1_one_expert", FP8, T=129, H=256, I=128, E=1, k=1, seed=13),
-    # decode-like: at most 8 rows per expert on average
+    # decode-like: at most 12 rows per expert on average
     _small_workload("decode_fp8", FP8, T=24, H=512, I=256, E=16, k=4, seed=17),
     _small_workload("decode_fp8_ragged_clamp", FP8, T=16, H=640, I=384, E=32, k=8, routing="zipf", skip=0.1,
                     limit=0.05, seed=18),
