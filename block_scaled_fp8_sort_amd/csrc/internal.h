@@ -65,15 +65,6 @@ struct StaticScales {
   int32_t stride;
 };
 
-// Bytes the small-batch sort + quantization launch reads ahead (one 4-byte load
-// per 128-byte line) from the start of the next GEMM's weights while its one
-// sorting workgroup runs, so that those lines come from the last-level cache
-// when the GEMM starts.  base == NULL: none.
-struct Prefetch {
-  const uint8_t* base;
-  int64_t bytes;
-};
-
 size_t route_sort_lds_bytes(int32_t E);
 // Device workspace the sort of S slots needs (0 for the one-workgroup path).
 size_t route_sort_ws_bytes(int32_t S, int32_t E);
@@ -100,7 +91,7 @@ hipError_t launch_route_sort_and_quant(const RouterArgs* router, const int32_t* 
                                       int32_t* invalid_count, void* sort_ws, const uint16_t* x, int32_t rows,
                                       int32_t H, int fmt, uint8_t* codes, void* scales, int32_t* zero,
                                       int32_t n_zero, hipStream_t stream, void* sorted_scales = nullptr,
-                                      const StaticScales* static_scales = nullptr, Prefetch prefetch = {});
+                                      const StaticScales* static_scales = nullptr);
 // The router alone (no sort).
 hipError_t launch_router_only(const RouterArgs& router, int32_t T, int32_t k, hipStream_t stream);
 // static_scales non-NULL: the caller's block scales instead of the amax rule.

@@ -251,10 +251,6 @@ moe::GemmParams to_params(const moe_gemm_args* a) {
 // at 14 and 2.66 against 2.03 at 16 (past 16 rows an expert needs a second
 // 16-row tile, whose weights stream again).
 constexpr int64_t kSkinnyRowsPerExpert = 12;
-// Bytes of the gate_up weight read ahead during a decode batch's sort (the
-// Qwen3-shaped decode forward: 16 MB 1 us faster, 24 MB the same warm and
-// slower cold, 40 MB slower: more outlasts the sorting workgroup).
-constexpr int64_t kDecodePrefetchBytes = 16 << 20;
 
 hipError_t launch_gemm(const moe::GemmParams& p, int fmt, int epi, bool paired, int num_cus, hipStream_t stream) {
   if (fmt == MOE_FMT_BF16) return moe::launch_gemm_bf16(p, epi, paired, num_cus, stream);
@@ -396,18 +392,11 @@ moe_status forward_impl(const moe_weights* w, const uint16_t* hidden_states, con
                                      2 * MOE_TILE_COUNTERS_BYTES / 4, stream);
   else {
     const moe::StaticScales sts{stat ? opt->act_scales : nullptr, stat ? opt->act_scales_row_stride : 0};
-    // decode batches (the register-streaming FP8 GEMM): the start of the
-    // gate_up weight is read ahead while the sort runs
-    moe::Prefetch pf{};
-    if (w->fmt == MOE_FMT_FP8_B128 && (int64_t)T * k <= kSkinnyRowsPerExpert * E) {
-      const int64_t w13_bytes = (int64_t)E * 2 * I * H;
-      pf = moe::Prefetch{w->w13, w13_bytes < kDecodePrefetchBytes ? w13_bytes : kDecodePrefetchBytes};
-    }
     he = moe::launch_route_sort_and_quant(router, top_k_index, T, k, E, expert_begin, sorted_slot, offsets,
                                           opt ? opt->invalid_count : nullptr, base + L.sort_ws, hidden_states, T, H,
                                           w->fmt, act_codes, act_scales, sched, 2 * MOE_TILE_COUNTERS_BYTES / 4,
                                           stream, L.sorted_scales ? base + L.act_scales_sorted : nullptr,
-                                          stat ? &sts : nullptr, pf);
+                                          stat ? &sts : nullptr);
   }
   if (he != hipSuccess) return hip_status(he, "route sort / quant launch");
 

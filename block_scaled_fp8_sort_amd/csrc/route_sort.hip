@@ -444,32 +444,23 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(const RouterAr
 // Small batches: the sort and the activation quantization are independent and
 // each too small to fill the chip, so one launch runs both: workgroup 0 sorts,
 // the next q_blocks quantize (a grid-stride loop whose stride is a multiple of
-// the lanes of one quantization block), and any workgroups after those read
-// the start of the next GEMM's weights into the last-level cache while the
-// sorting workgroup, the launch's long pole, runs.
+// the lanes of one quantization block).  Workgroups that read the start of the
+// next GEMM's weights into the last-level cache while the sorting workgroup
+// runs saved 1 us of the Qwen3-MoE decode forward while that GEMM's weight
+// loads were plain; with the nontemporal hint on them the read-ahead cost
+// 0.4-0.7 us instead, so there is none.
 template <int BLOCK, bool STATIC>
 __global__ __launch_bounds__(kSortThreads) void route_quant_kernel(
     const RouterArgs router, const int32_t* ids, int32_t T, int32_t k, int32_t E, int32_t expert_begin,
     int32_t* __restrict__ sorted_slot,
     int32_t* __restrict__ offsets, int32_t* __restrict__ invalid_count, const uint4* __restrict__ x,
     int64_t n_chunks, int32_t rows, int32_t H, uint8_t* __restrict__ codes, void* __restrict__ scales,
-    int32_t* __restrict__ zero, int32_t n_zero, StaticScales st, int32_t q_blocks, Prefetch pf) {
+    int32_t* __restrict__ zero, int32_t n_zero, StaticScales st, int32_t q_blocks) {
   if (blockIdx.x == 1 || gridDim.x == 1)
     for (int i = threadIdx.x; i < n_zero; i += blockDim.x) zero[i] = 0;
   if (blockIdx.x == 0) {
     router_in_workgroup(router, T, k);
     sort_one_workgroup(ids, T * k, E, expert_begin, sorted_slot, offsets, nullptr, invalid_count);
-    return;
-  }
-  if (blockIdx.x > q_blocks) {
-    // one 4-byte load per 128-byte line; the value feeds nothing but an empty
-    // asm statement, which keeps the loads (and waits for them before exit)
-    const int64_t lines = pf.bytes / 128;
-    const int64_t pstride = (int64_t)(gridDim.x - 1 - q_blocks) * blockDim.x;
-    uint32_t v = 0;
-    for (int64_t l = (int64_t)(blockIdx.x - 1 - q_blocks) * blockDim.x + threadIdx.x; l < lines; l += pstride)
-      v ^= *(const uint32_t*)(pf.base + l * 128);
-    asm volatile("" ::"v"(v));
     return;
   }
   const int64_t stride = (int64_t)q_blocks * blockDim.x;
@@ -576,7 +567,7 @@ hipError_t launch_route_sort_and_quant(const RouterArgs* router, const int32_t* 
                                       int32_t* invalid_count, void* sort_ws, const uint16_t* x, int32_t rows,
                                       int32_t H, int fmt, uint8_t* codes, void* scales, int32_t* zero,
                                       int32_t n_zero, hipStream_t stream, void* sorted_scales,
-                                      const StaticScales* static_scales, Prefetch prefetch) {
+                                      const StaticScales* static_scales) {
   if (router && !router->logits) router = nullptr;
   const int32_t S = T * k;
   const int64_t n_chunks = (int64_t)rows * H / 8;
@@ -597,19 +588,13 @@ hipError_t launch_route_sort_and_quant(const RouterArgs* router, const int32_t* 
   const RouterArgs r = fuse ? *router : kNoRouter;
   const int64_t want = (n_chunks + kSortThreads - 1) / kSortThreads;
   const int q_blocks = (int)(want < 256 * 16 ? want : 256 * 16);
-  int pf_blocks = 0;
-  if (prefetch.base && prefetch.bytes >= 128) {
-    const int64_t lines = prefetch.bytes / 128;
-    const int64_t pb = (lines + kSortThreads - 1) / kSortThreads;
-    pf_blocks = (int)(pb < 256 ? pb : 256);
-  }
-  const int blocks = 1 + q_blocks + pf_blocks;
+  const int blocks = 1 + q_blocks;
   const StaticScales st = static_scales ? *static_scales : StaticScales{nullptr, 0};
   auto kern = fmt == 0 ? (static_scales ? route_quant_kernel<128, true> : route_quant_kernel<128, false>)
                        : (static_scales ? route_quant_kernel<32, true> : route_quant_kernel<32, false>);
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(kSortThreads), route_sort_lds_bytes(E), stream, r, ids, T, k, E,
                      expert_begin, sorted_slot, offsets, invalid_count, (const uint4*)x, n_chunks, rows, H, codes,
-                     scales, zero, n_zero, st, q_blocks, prefetch);
+                     scales, zero, n_zero, st, q_blocks);
   return hipGetLastError();
 }
 
