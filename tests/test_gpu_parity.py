@@ -373,6 +373,11 @@ SMALL = [
     # more than 8 slots per token (the combine's wide path), up to the largest k
     _small_workload("k16_fp8", FP8, T=96, H=256, I=128, E=32, k=16, routing="zipf", skip=0.1, seed=24),
     _small_workload("k64_fp8", FP8, T=20, H=256, I=128, E=128, k=64, routing="zipf", skip=0.1, seed=25),
+    # both sides of the switch between the FP8 GEMMs: 12 slots per expert on
+    # average streams weights through registers (skewed, so some experts span
+    # several 16-row tiles), 13 takes the LDS-tiled kernel
+    _small_workload("switch_12_rows_fp8", FP8, T=96, H=512, I=256, E=32, k=4, routing="zipf", skip=0.05, seed=41),
+    _small_workload("switch_13_rows_fp8", FP8, T=104, H=512, I=256, E=32, k=4, routing="zipf", skip=0.05, seed=42),
     _small_workload("k24_mx", MX, T=40, H=256, I=128, E=48, k=24, routing="zipf", skip=0.1, limit=7.0, seed=26),
     # the down GEMM's half-width tail tiles: experts of 303-339 rows (remainders
     # of 47 to 83 past one 256-row tile: both half heights), H = 640 (a partial
